@@ -1,0 +1,88 @@
+/*
+ * Oracle for the gated, grouped, depthwise causal FIR convolution
+ *     y = q (.) (h * (k (.) v))
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no code, header or constant with the HIP
+ * library.
+ *
+ * What it computes, written out as the plain definition (no blocking, no
+ * Toeplitz split, no reordering beyond the sum's natural index order):
+ *
+ *   Page "04. hardware-aware convolution kernels" (StripedHyena 2 explainer),
+ *   section 1, first equation: a causal FIR filter h of length l_h applied to
+ *   an input x of length l gives  y_t = sum_{j=0..t} h_{t-j} x_j,  with
+ *   h_i = 0 for i < 0 or i >= l_h.
+ *
+ *   Same page, section 4 (Algorithm 1): the output chunk is gated by q after
+ *   the convolution, and k is loaded beside v; the convolution input is read
+ *   here as x = k (.) v, the reading under which the loaded k has a role.
+ *
+ *   Same page, section 4, first bullet list: all channels of a group share
+ *   one filter; channel d uses filter floor(d / group_size).
+ *
+ * Arithmetic is fp64 on the exact values the caller passes (bf16 or fp32
+ * inputs are widened to fp64 by the caller, which is lossless).  Each batch
+ * row starts with zero history (x_t = 0 for t < 0).
+ *
+ * Layout: q, k, v, y are [B, L, D] row-major (D contiguous); h is
+ * [D / group_size, l_h] row-major (taps contiguous).
+ */
+#include <stddef.h>
+#include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Return codes: 0 ok, -1 null pointer, -2 bad shape, -3 bad group size,
+ * -4 bad filter length. */
+int hyena_ref_fwd_f64(const double *q, const double *k, const double *v,
+                      const double *h, int64_t B, int64_t L, int64_t D,
+                      int64_t group_size, int64_t l_h, double *y)
+{
+    if (!q || !k || !v || !h || !y)
+        return -1;
+    if (B < 0 || L < 0 || D < 0)
+        return -2;
+    if (group_size < 1 || (D % group_size) != 0)
+        return -3;
+    if (l_h < 1)
+        return -4;
+    if (B == 0 || L == 0 || D == 0)
+        return 0;
+
+    const int64_t rows = B * L;
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < rows; ++row) {
+        const int64_t b = row / L;
+        const int64_t t = row % L;
+        const size_t batch0 = (size_t)b * (size_t)L * (size_t)D;
+        for (int64_t d = 0; d < D; ++d) {
+            const double *hg = h + (size_t)(d / group_size) * (size_t)l_h;
+            /* only j with 0 <= t - j < l_h contribute */
+            int64_t j0 = t - (l_h - 1);
+            if (j0 < 0)
+                j0 = 0;
+            double z = 0.0;
+            for (int64_t j = j0; j <= t; ++j) {
+                const size_t o = batch0 + (size_t)j * (size_t)D + (size_t)d;
+                const double x = k[o] * v[o];
+                z += hg[t - j] * x;
+            }
+            const size_t oy = batch0 + (size_t)t * (size_t)D + (size_t)d;
+            y[oy] = q[oy] * z;
+        }
+    }
+    return 0;
+}
+
+/* Number of OpenMP threads a call above uses (1 without OpenMP). */
+int hyena_ref_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

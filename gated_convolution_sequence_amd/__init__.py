@@ -1,0 +1,132 @@
+"""MI355X (gfx950) Hyena-SE / Hyena-MR forward: y = q (.) (h * (k (.) v)).
+
+A thin Python binding of the C ABI in ``include/hyena_conv.h``.  It only
+checks and marshals arguments (device pointers, sizes, the current HIP
+stream); every step of the computation runs in the HIP kernels of
+``libhyena_conv.so``.  There is no fallback: if the library is missing or
+rejects a call, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhyena_conv.so")
+
+BLOCK_LEN = 64
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+STATUS = {
+    0: "HYENA_OK", -1: "HYENA_ERR_NULL", -2: "HYENA_ERR_SHAPE", -3: "HYENA_ERR_GROUP",
+    -4: "HYENA_ERR_FILTER_LEN", -5: "HYENA_ERR_ALIGN", -6: "HYENA_ERR_ALIAS",
+    -7: "HYENA_ERR_UNSUPPORTED", -8: "HYENA_ERR_LAUNCH", -9: "HYENA_ERR_DTYPE",
+}
+
+# Every symbol include/hyena_conv.h declares.
+EXPORTS = ("hyena_conv_fwd", "hyena_conv_fwd_f32", "hyena_conv_fwd_ex", "hyena_conv_plan",
+           "hyena_conv_strerror", "hyena_conv_block_len")
+
+
+class HyenaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, strerror(status), STATUS.get(status, status)))
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libhyena_conv.so is not built (expected at %s); run "
+                "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        fwd_args = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp]
+        for name in ("hyena_conv_fwd", "hyena_conv_fwd_f32"):
+            fn = getattr(L, name)
+            fn.argtypes = fwd_args
+            fn.restype = ctypes.c_int
+        L.hyena_conv_fwd_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp,
+                                        ctypes.c_int, i64, vp]
+        L.hyena_conv_fwd_ex.restype = ctypes.c_int
+        L.hyena_conv_plan.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, i64,
+                                      ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.hyena_conv_plan.restype = ctypes.c_int
+        L.hyena_conv_strerror.argtypes = [ctypes.c_int]
+        L.hyena_conv_strerror.restype = ctypes.c_char_p
+        L.hyena_conv_block_len.argtypes = []
+        L.hyena_conv_block_len.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().hyena_conv_strerror(int(status)).decode()
+
+
+def plan(B: int, L: int, D: int, group_size: int, l_h: int, dtype: int = DTYPE_BF16,
+         span_chunks: int = 0):
+    """(chunks per workgroup, workgroup count) the library would launch."""
+    span = ctypes.c_int64()
+    wgs = ctypes.c_int64()
+    st = lib().hyena_conv_plan(B, L, D, group_size, l_h, dtype, span_chunks,
+                               ctypes.byref(span), ctypes.byref(wgs))
+    if st != 0:
+        raise HyenaError(st, "hyena_conv_plan")
+    return span.value, wgs.value
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return DTYPE_BF16
+    if t == torch.float32:
+        return DTYPE_F32
+    raise TypeError("q, k, v, h must be bfloat16 or float32, got %s" % t)
+
+
+def conv_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Tensor,
+             group_size: int, out: Optional[torch.Tensor] = None, span_chunks: int = 0,
+             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """y = q (.) (h * (k (.) v)) on the GPU, enqueued on ``stream`` (default: current).
+
+    q, k, v: [B, L, D] contiguous device tensors (bf16 or fp32, all alike);
+    h: [D // group_size, l_h] of the same dtype.  Returns ``out`` ([B, L, D]).
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("h", h)):
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, q has %s" % (name, t.dtype, q.dtype))
+    code = _dtype_code(q.dtype)
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share one [B, L, D] shape")
+    if h.dim() != 2:
+        raise ValueError("h must be [D // group_size, l_h]")
+    B, L, D = q.shape
+    if group_size < 1 or D % group_size != 0 or h.shape[0] != D // group_size:
+        raise ValueError("h has %d filters; D=%d, group_size=%d" % (h.shape[0], D, group_size))
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous GPU tensor like q")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        st = lib().hyena_conv_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(),
+                                     B, L, D, group_size, h.shape[1], out.data_ptr(), code,
+                                     span_chunks, stream.cuda_stream)
+    if st != 0:
+        raise HyenaError(st, "hyena_conv_fwd_ex")
+    return out

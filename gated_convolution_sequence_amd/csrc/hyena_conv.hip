@@ -1,0 +1,516 @@
+// Hyena-SE / Hyena-MR forward for MI355X (gfx950):
+//     y = q (.) (h * (k (.) v)),  grouped depthwise causal FIR, l_h <= 128.
+//
+// Method (StripedHyena 2 explainer, page "04. hardware-aware convolution
+// kernels"):
+//   * section 1: the convolution is a product with a lower-triangular
+//     Toeplitz matrix whose entry (row, column) is the tap h[row - column];
+//   * section 3: split time into chunks of l_b rows; output chunk n is
+//     H0 X_n + H1 X_{n-1} (+ H2 X_{n-2} once l_h > l_b + 1), X_{<0} = 0;
+//   * section 4: the blocks are the same for every chunk and for every
+//     channel of a group, so each group's products become dense GEMMs on the
+//     matrix cores, with the blocks resident on chip; Algorithm 1 gates the
+//     convolved chunk with q;
+//   * section 6: the chunk direction is parallel (preload the blocks, load the
+//     chunks, GEMM, write back);
+//   * section 7: a Toeplitz tile is never stored in memory; each entry is
+//     gathered from the filter by the difference of its row and column index.
+//
+// gfx950 mapping (l_b = 64 rows, one 16-channel group per wave):
+//   * A workgroup of 4 waves owns a slab of 64 channels (4 groups of 16) and a
+//     span of consecutive 64-row chunks of one batch row.  It first walks the
+//     32*KH rows before the span (the history the first chunk needs), then
+//     the span.
+//   * k and v arrive through 16-byte buffer loads, coalesced along channels;
+//     x = k*v is formed in fp32, rounded to bf16 and written to an XOR-swizzled
+//     LDS tile, which each wave re-reads time-major as the MFMA operand.
+//   * Each wave computes Y^T (16 channels x 64 times) = X^T H^T with
+//     v_mfma_f32_16x16x32_bf16: A = X^T (channel x input time), B = H^T
+//     (input time x output time).  For an output tile of 16 rows and an input
+//     step of 32 rows the Toeplitz operand depends only on their distance
+//     e = nt - 2*kappa (in units of 16 rows), so a group needs 4 + 2*KH
+//     distinct B fragments, built once per workgroup from the filter and kept
+//     in registers.  Fragments whose taps all fall outside [0, l_h) are
+//     skipped (the zero blocks of section 2).
+//   * The previous chunks' X^T fragments stay in registers, so every input
+//     row is read from HBM once per span.
+//   * The epilogue multiplies the fp32 accumulators by q (loaded in the
+//     accumulator layout: 4 consecutive channels per lane), rounds to bf16
+//     and stores 8 bytes per lane.
+//   * Buffer resources bound every access: rows before the batch start or
+//     past the span, and channels past D, read as zero and are never
+//     written.  That supplies X_{-1} = 0, ragged last chunks and partial slabs.
+// The fp32 path has the same structure with v_mfma_f32_16x16x4_f32 (one
+// input row per lane and step) and fp32 data in LDS.
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "hyena_conv.h"
+
+namespace {
+
+constexpr int kChunk = 64;               // l_b: rows per chunk
+constexpr int kTile = 16;                // channels per wave (MFMA M)
+constexpr int kWaves = 4;                // waves per workgroup
+constexpr int kSlab = kTile * kWaves;    // channels per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxTaps = 2 * kChunk;     // l_h <= 2 l_b
+constexpr int kHOff = 64;                // filter staging: index = tap + kHOff
+constexpr int kHLen = 256;               // staged taps per wave: [-64, 192)
+constexpr uint32_t kOOB = 0x80000000u;   // a buffer offset past every range
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+struct Params {
+    const void *q, *k, *v, *h;
+    void *y;
+    int64_t L;          // rows per batch
+    int32_t D;          // channels (row pitch, elements)
+    int32_t group_size;
+    int32_t l_h;
+    int32_t span;       // chunks per workgroup
+    int32_t n_spans;    // spans per batch row
+    int32_t n_slabs;    // 64-channel slabs
+};
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    // Raw buffer (stride 0): an offset >= bytes reads 0 and drops writes.
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             (int)bytes, 0x00020000);
+}
+
+__device__ inline float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ inline uint32_t pack_bf16(float a, float b) {
+    bf16x2_t r = {(__bf16)a, (__bf16)b};  // round to nearest even
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Element-type traits: the I/O width and the LDS tile geometry.
+template <bool F32> struct Tr;
+template <> struct Tr<false> {           // bf16 I/O
+    static constexpr int EB = 2;         // bytes per element
+    static constexpr int VEC = 8;        // elements per 16-byte access
+    static constexpr int PITCH = kSlab * 2;          // LDS bytes per row
+    static constexpr int TPR = PITCH / 16;           // threads per row (8)
+    static constexpr int RPL = kThreads / TPR;       // rows per load (32)
+    static constexpr int NLD = kChunk / RPL;         // loads per tensor per chunk (2)
+    // XOR swizzle of the 16-byte segment index by row (conflict-free
+    // time-major reads of 16 channels x 4 row groups).
+    __device__ static int swz(int row) { return ((row >> 3) & 3) << 1; }
+};
+template <> struct Tr<true> {            // fp32 I/O
+    static constexpr int EB = 4;
+    static constexpr int VEC = 4;
+    static constexpr int PITCH = kSlab * 4;
+    static constexpr int TPR = PITCH / 16;           // 16
+    static constexpr int RPL = kThreads / TPR;       // 16
+    static constexpr int NLD = kChunk / RPL;         // 4
+    __device__ static int swz(int row) { return (row & 3) << 2; }
+};
+
+template <bool F32, int KH>
+__global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
+    using T = Tr<F32>;
+    constexpr int HROWS = 32 * KH;                    // history rows before a span
+    constexpr int C0 = -((HROWS + kChunk - 1) / kChunk);  // first (history) chunk
+
+    __shared__ __attribute__((aligned(16))) unsigned char xs[2][kChunk * T::PITCH];
+    __shared__ float hs[kWaves][kHLen];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;           // wave = 16-channel tile of the slab
+    const int l = tid & 63;
+    const int n16 = l & 15;
+    const int q4 = l >> 4;
+
+    int bid = blockIdx.x;
+    const int slab = bid % p.n_slabs;
+    bid /= p.n_slabs;
+    const int spn = bid % p.n_spans;
+    const int b = bid / p.n_spans;
+
+    const int64_t t_begin = (int64_t)spn * p.span * kChunk;
+    const int64_t t_stop = min(p.L, t_begin + (int64_t)p.span * kChunk);
+    const int nck = (int)((t_stop - t_begin + kChunk - 1) / kChunk);
+    const int64_t base_row = max((int64_t)0, t_begin - HROWS);
+    const int c_begin = slab * kSlab;
+    const int row_bytes = p.D * T::EB;
+
+    // Byte window [base, base + nrec) of this workgroup: rows base_row ..
+    // t_stop-1 of batch b, starting at channel c_begin.  The host keeps it
+    // below 2^31 bytes, so a negative (earlier) row offset is out of range.
+    const size_t base_off = ((size_t)b * (size_t)p.L + (size_t)base_row) * (size_t)row_bytes +
+                            (size_t)c_begin * T::EB;
+    const uint32_t nrec = (uint32_t)((t_stop - base_row) * row_bytes - c_begin * T::EB);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc((char *)p.y + base_off, nrec);
+    const int row0 = (int)(t_begin - base_row);       // window row of chunk 0
+
+    // ---- stage this wave's filter (zero outside [0, l_h)) -----------------
+    const bool tile_ok = c_begin + w * kTile < p.D;
+    {
+        const int g = tile_ok ? (c_begin + w * kTile) / p.group_size : 0;
+        for (int i = l; i < kHLen; i += 64) {
+            const int tap = i - kHOff;
+            float hv = 0.0f;
+            if (tile_ok && tap >= 0 && tap < p.l_h) {
+                if constexpr (F32)
+                    hv = ((const float *)p.h)[(size_t)g * p.l_h + tap];
+                else
+                    hv = bf_lo(((const uint16_t *)p.h)[(size_t)g * p.l_h + tap]);
+            }
+            hs[w][i] = hv;
+        }
+    }
+
+    // ---- cooperative k, v loads: thread -> (row, 16-byte segment) ----------
+    const int ld_row = tid / T::TPR;
+    const int ld_seg = tid % T::TPR;
+    const bool seg_ok = c_begin + ld_seg * T::VEC < p.D;
+    auto kv_off = [&](int c, int i) -> uint32_t {
+        const int r = row0 + c * kChunk + i * T::RPL + ld_row;
+        return seg_ok ? (uint32_t)(r * row_bytes + ld_seg * 16) : kOOB;
+    };
+
+    u32x4_t kr[T::NLD], vr[T::NLD];
+    auto load_kv = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const uint32_t o = kv_off(c, i);
+            kr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+            vr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+        }
+    };
+    // x = k*v for this thread's rows of chunk c -> LDS buffer `buf`.
+    auto store_x = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const int row = i * T::RPL + ld_row;
+            u32x4_t xv;
+            if constexpr (F32) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xv[e] = __float_as_uint(__uint_as_float(kr[i][e]) * __uint_as_float(vr[i][e]));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xv[e] = pack_bf16(bf_lo(kr[i][e]) * bf_lo(vr[i][e]),
+                                      bf_hi(kr[i][e]) * bf_hi(vr[i][e]));
+            }
+            const int off = row * T::PITCH + ((ld_seg ^ T::swz(row)) << 4);
+            *(u32x4_t *)(&xs[buf][off]) = xv;
+        }
+    };
+
+    // ---- epilogue geometry: lane holds times 16nt + n16, channels 4q4..4q4+3
+    const int ep_col = (w * kTile + 4 * q4) * T::EB;
+    auto ep_off = [&](int c, int nt) -> uint32_t {
+        const int r = row0 + c * kChunk + nt * 16 + n16;
+        return tile_ok ? (uint32_t)(r * row_bytes + ep_col) : kOOB;
+    };
+
+    __syncthreads();  // filters staged
+
+    if constexpr (!F32) {
+        // ================= bf16: v_mfma_f32_16x16x32_bf16 ==================
+        constexpr int NE = 4 + 2 * KH;  // Toeplitz fragments, e = 0 .. 3 + 2 KH
+        constexpr int NX = KH + 2;      // X^T fragments, kappa = -KH .. 1
+        bf16x8_t F[NE];
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                // B = H^T: row k = 8 q4 + j (input time), column n16 (output time)
+                const int tap = 16 * e + n16 - 8 * q4 - j;
+                F[e][j] = (__bf16)hs[w][tap + kHOff];
+            }
+        }
+        bf16x8_t X[NX];
+#pragma unroll
+        for (int i = 0; i < NX; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) X[i][j] = (__bf16)0.0f;
+
+        // Time-major LDS read address of this lane: channel 16w + n16, rows
+        // 8 q4 + j (+ 32 kappa); the swizzle of those rows is 2 q4.
+        const int ch = w * kTile + n16;
+        const int rd_base = (8 * q4) * T::PITCH + ((((ch >> 3) ^ (2 * q4))) << 4) + ((ch & 7) << 1);
+
+        u32x2_t qc[4], qn[4];
+        auto load_q = [&](int c, u32x2_t *dst) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                dst[nt] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rq, ep_off(c, nt), 0, 0));
+        };
+
+        load_kv(C0);
+        if (C0 == 0) load_q(0, qc);
+        for (int c = C0; c < nck; ++c) {
+            const int buf = (c - C0) & 1;
+            store_x(buf);
+            if (c + 1 < nck) {
+                if (c + 1 >= 0) load_q(c + 1, qn);
+                load_kv(c + 1);
+            }
+            __syncthreads();
+            const unsigned char *xb = xs[buf];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint16_t raw = *(const uint16_t *)(xb + rd_base + (32 * kk + j) * T::PITCH);
+                    X[KH + kk][j] = __builtin_bit_cast(__bf16, raw);
+                }
+            }
+            if (c >= 0) {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int kk = 0; kk < NX; ++kk) {
+                        const int kappa = kk - KH;
+                        const int e = nt - 2 * kappa;
+                        if (e < 0 || e >= NE) continue;
+                        if (16 * e - 31 >= p.l_h) continue;  // every tap past the filter
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(X[kk], F[e], acc, 0, 0, 0);
+                    }
+                    const u32x2_t qv = qc[nt];
+                    u32x2_t yv;
+                    yv[0] = pack_bf16(bf_lo(qv[0]) * acc[0], bf_hi(qv[0]) * acc[1]);
+                    yv[1] = pack_bf16(bf_lo(qv[1]) * acc[2], bf_hi(qv[1]) * acc[3]);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, yv), ry, ep_off(c, nt), 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < KH; ++i) X[i] = X[i + 2];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) qc[nt] = qn[nt];
+        }
+    } else {
+        // ================= fp32: v_mfma_f32_16x16x4_f32 ====================
+        constexpr int H4 = HROWS / 4;   // history steps of 4 rows
+        constexpr int NX = H4 + 16;     // kappa4 = -H4 .. 15
+        constexpr int NE = 16 + H4;     // e4 = -3 .. 12 + H4
+        float F[NE];
+#pragma unroll
+        for (int i = 0; i < NE; ++i) {
+            const int e4 = i - 3;
+            // B = H^T: row k = q4 (input time), column n16 (output time)
+            F[i] = hs[w][4 * e4 + n16 - q4 + kHOff];
+        }
+        float X[NX];
+#pragma unroll
+        for (int i = 0; i < NX; ++i) X[i] = 0.0f;
+        const int ch = w * kTile + n16;
+        const int rd_base = q4 * T::PITCH + ((((ch >> 2) ^ (4 * q4))) << 4) + ((ch & 3) << 2);
+
+        u32x4_t qc[4], qn[4];
+        auto load_q = [&](int c, u32x4_t *dst) {
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                dst[nt] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, ep_off(c, nt), 0, 0));
+        };
+
+        load_kv(C0);
+        if (C0 == 0) load_q(0, qc);
+        for (int c = C0; c < nck; ++c) {
+            const int buf = (c - C0) & 1;
+            store_x(buf);
+            if (c + 1 < nck) {
+                if (c + 1 >= 0) load_q(c + 1, qn);
+                load_kv(c + 1);
+            }
+            __syncthreads();
+            const unsigned char *xb = xs[buf];
+#pragma unroll
+            for (int s = 0; s < 16; ++s)
+                X[H4 + s] = *(const float *)(xb + rd_base + (4 * s) * T::PITCH);
+            if (c >= 0) {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int kk = 0; kk < NX; ++kk) {
+                        const int kappa4 = kk - H4;
+                        const int e4 = 4 * nt - kappa4;
+                        if (e4 < -3 || e4 + 3 >= NE) continue;
+                        if (4 * e4 - 3 >= p.l_h) continue;
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[kk], F[e4 + 3], acc, 0, 0, 0);
+                    }
+                    const u32x4_t qv = qc[nt];
+                    u32x4_t yv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) yv[e] = __float_as_uint(__uint_as_float(qv[e]) * acc[e]);
+                    __builtin_amdgcn_raw_buffer_store_b128(yv, ry, ep_off(c, nt), 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < H4; ++i) X[i] = X[i + 16];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) qc[nt] = qn[nt];
+        }
+    }
+}
+
+typedef void (*KernelFn)(Params);
+
+template <bool F32>
+KernelFn pick_kernel(int kh) {
+    switch (kh) {
+    case 0: return hyena_fwd_kernel<F32, 0>;
+    case 1: return hyena_fwd_kernel<F32, 1>;
+    case 2: return hyena_fwd_kernel<F32, 2>;
+    case 3: return hyena_fwd_kernel<F32, 3>;
+    default: return hyena_fwd_kernel<F32, 4>;
+    }
+}
+
+// Workgroups the automatic split aims for: 256 CUs x 2 resident workgroups.
+constexpr int64_t kTargetWorkgroups = 512;
+constexpr int64_t kMaxWindowBytes = (int64_t)1 << 31;
+
+struct Plan {
+    int64_t span, n_spans, n_slabs, n_chunks, workgroups;
+    int kh;
+};
+
+int check_sizes(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, int dtype) {
+    if (dtype != HYENA_DTYPE_BF16 && dtype != HYENA_DTYPE_F32) return HYENA_ERR_DTYPE;
+    if (B < 0 || L < 0 || D < 0) return HYENA_ERR_SHAPE;
+    if (group_size < 1 || D % group_size != 0) return HYENA_ERR_GROUP;
+    if (l_h < 1 || l_h > kMaxTaps) return HYENA_ERR_FILTER_LEN;
+    // element count must fit comfortably in 63 bits
+    if (B > 0 && L > 0 && D > 0) {
+        const int64_t lim = INT64_MAX / 8;
+        if (L > lim / D || B > lim / (L * D)) return HYENA_ERR_SHAPE;
+    }
+    return HYENA_OK;
+}
+
+int make_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, int dtype,
+              int64_t span_req, Plan *pl) {
+    (void)group_size;
+    const int64_t eb = dtype == HYENA_DTYPE_F32 ? 4 : 2;
+    pl->kh = (int)((l_h - 1 + 31) / 32);
+    pl->n_chunks = (L + kChunk - 1) / kChunk;
+    pl->n_slabs = (D + kSlab - 1) / kSlab;
+    if (group_size % kTile != 0) return HYENA_ERR_UNSUPPORTED;
+    if (D > INT32_MAX / 16) return HYENA_ERR_UNSUPPORTED;
+    int64_t span = span_req;
+    if (span <= 0) {
+        const int64_t total = pl->n_chunks * pl->n_slabs * B;
+        span = (total + kTargetWorkgroups - 1) / kTargetWorkgroups;
+    }
+    if (span < 1) span = 1;
+    if (span > pl->n_chunks) span = pl->n_chunks;
+    // the workgroup's byte window (span + history rows) must stay below 2^31
+    while (span > 1 && (span * kChunk + 32 * pl->kh + kChunk) * D * eb >= kMaxWindowBytes) span = (span + 1) / 2;
+    if ((span * kChunk + 32 * pl->kh + kChunk) * D * eb >= kMaxWindowBytes) return HYENA_ERR_UNSUPPORTED;
+    pl->span = span;
+    pl->n_spans = (pl->n_chunks + span - 1) / span;
+    pl->workgroups = pl->n_spans * pl->n_slabs * B;
+    if (pl->workgroups > INT32_MAX || pl->n_spans > INT32_MAX) return HYENA_ERR_UNSUPPORTED;
+    return HYENA_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hyena_conv_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, int dtype,
+                    int64_t span_chunks, int64_t *span_out, int64_t *workgroups_out) {
+    int st = check_sizes(B, L, D, group_size, l_h, dtype);
+    if (st != HYENA_OK) return st;
+    if (B == 0 || L == 0 || D == 0) {
+        if (span_out) *span_out = 0;
+        if (workgroups_out) *workgroups_out = 0;
+        return HYENA_OK;
+    }
+    Plan pl;
+    st = make_plan(B, L, D, group_size, l_h, dtype, span_chunks, &pl);
+    if (st != HYENA_OK) return st;
+    if (span_out) *span_out = pl.span;
+    if (workgroups_out) *workgroups_out = pl.workgroups;
+    return HYENA_OK;
+}
+
+int hyena_conv_fwd_ex(const void *q, const void *k, const void *v, const void *h, int64_t B,
+                      int64_t L, int64_t D, int64_t group_size, int64_t l_h, void *out, int dtype,
+                      int64_t span_chunks, void *stream) {
+    int st = check_sizes(B, L, D, group_size, l_h, dtype);
+    if (st != HYENA_OK) return st;
+    if (B == 0 || L == 0 || D == 0) return HYENA_OK;
+    if (!q || !k || !v || !h || !out) return HYENA_ERR_NULL;
+    const size_t eb = dtype == HYENA_DTYPE_F32 ? 4 : 2;
+    const uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out;
+    if (mis & 15u) return HYENA_ERR_ALIGN;
+    if ((uintptr_t)h & (eb - 1)) return HYENA_ERR_ALIGN;
+    const size_t nbytes = (size_t)B * (size_t)L * (size_t)D * eb;
+    const size_t hbytes = (size_t)(D / group_size) * (size_t)l_h * eb;
+    if (overlaps(out, nbytes, q, nbytes) || overlaps(out, nbytes, k, nbytes) ||
+        overlaps(out, nbytes, v, nbytes) || overlaps(out, nbytes, h, hbytes))
+        return HYENA_ERR_ALIAS;
+    Plan pl;
+    st = make_plan(B, L, D, group_size, l_h, dtype, span_chunks, &pl);
+    if (st != HYENA_OK) return st;
+
+    Params p;
+    p.q = q; p.k = k; p.v = v; p.h = h; p.y = out;
+    p.L = L;
+    p.D = (int32_t)D;
+    p.group_size = (int32_t)group_size;
+    p.l_h = (int32_t)l_h;
+    p.span = (int32_t)pl.span;
+    p.n_spans = (int32_t)pl.n_spans;
+    p.n_slabs = (int32_t)pl.n_slabs;
+    KernelFn fn = dtype == HYENA_DTYPE_F32 ? pick_kernel<true>(pl.kh) : pick_kernel<false>(pl.kh);
+    hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(kThreads), 0, (hipStream_t)stream, p);
+    if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+    return HYENA_OK;
+}
+
+int hyena_conv_fwd(const void *q, const void *k, const void *v, const void *h, int64_t B, int64_t L,
+                   int64_t D, int64_t group_size, int64_t l_h, void *out, void *stream) {
+    return hyena_conv_fwd_ex(q, k, v, h, B, L, D, group_size, l_h, out, HYENA_DTYPE_BF16, 0, stream);
+}
+
+int hyena_conv_fwd_f32(const void *q, const void *k, const void *v, const void *h, int64_t B,
+                       int64_t L, int64_t D, int64_t group_size, int64_t l_h, void *out,
+                       void *stream) {
+    return hyena_conv_fwd_ex(q, k, v, h, B, L, D, group_size, l_h, out, HYENA_DTYPE_F32, 0, stream);
+}
+
+const char *hyena_conv_strerror(int status) {
+    switch (status) {
+    case HYENA_OK: return "ok";
+    case HYENA_ERR_NULL: return "a required pointer is NULL";
+    case HYENA_ERR_SHAPE: return "B, L or D is negative or the sizes overflow";
+    case HYENA_ERR_GROUP: return "group_size must be >= 1 and divide D";
+    case HYENA_ERR_FILTER_LEN: return "l_h must be in [1, 128]";
+    case HYENA_ERR_ALIGN: return "q, k, v and out must be 16-byte aligned; h element aligned";
+    case HYENA_ERR_ALIAS: return "out overlaps an input";
+    case HYENA_ERR_UNSUPPORTED: return "group_size must be a multiple of 16 (or the shape is too large to address)";
+    case HYENA_ERR_LAUNCH: return "kernel launch failed";
+    case HYENA_ERR_DTYPE: return "unknown dtype code";
+    default: return "unknown status";
+    }
+}
+
+int hyena_conv_block_len(void) { return kChunk; }
+
+}  // extern "C"

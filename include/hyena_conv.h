@@ -1,0 +1,114 @@
+/*
+ * hyena_conv.h -- C ABI of the MI355X (gfx950) Hyena-SE / Hyena-MR forward
+ * operator
+ *
+ *     y[b,t,d] = q[b,t,d] * sum_{s=0}^{min(t, l_h-1)} h[d / group_size, s] * k[b,t-s,d] * v[b,t-s,d]
+ *
+ * i.e. y = q (.) (h * (k (.) v)): a gated, grouped, depthwise causal FIR
+ * convolution.  Sources (the StripedHyena 2 explainer pages):
+ *   - page "04. hardware-aware convolution kernels", section 1, first
+ *     equation: the causal FIR sum y_t = sum_j h_{t-j} x_j, h zero outside
+ *     [0, l_h);
+ *   - same page, section 3: the chunked (block-Toeplitz) form with chunk
+ *     length l_b, Y_n = H0 X_n + H1 X_{n-1}, X_{-1} = 0;
+ *   - same page, section 4, Algorithm 1: q gates the convolved chunk; k is
+ *     loaded beside v and taken here as the pre-convolution gate, x = k (.) v;
+ *   - same page, section 4, first bullet list: the channels of a group share
+ *     one filter; channel d uses filter d / group_size.
+ *
+ * The library computes this with its own chunk length of 64 rows (the
+ * value every workload here uses); the chunk length changes only the order
+ * of the fp32 additions, never which terms are summed.  Filters may be up to
+ * 2 * 64 = 128 taps long.  Where l_h > 65 the output chunk also reaches into
+ * chunk n-2 (Y_n = H0 X_n + H1 X_{n-1} + H2 X_{n-2}); the library includes
+ * that term, so the result is the convolution above for every l_h <= 128.
+ *
+ * Layout (all row-major, no strides):
+ *   q, k, v, out : [B, L, D], D contiguous.
+ *   h            : [D / group_size, l_h], taps contiguous.
+ * Precision:
+ *   hyena_conv_fwd      : bf16 in, bf16 out.  k*v is formed in fp32 and
+ *                         rounded once to bf16 (round to nearest even) as the
+ *                         matrix-core operand; taps are bf16; sums are fp32;
+ *                         the gated result is rounded once to bf16.
+ *   hyena_conv_fwd_f32  : fp32 in, fp32 out, fp32 products and sums.
+ *
+ * Ownership and asynchrony: every pointer is a DEVICE pointer owned by the
+ * caller.  The library allocates no device memory and keeps no state between
+ * calls except a per-process cache of device properties.  Work is enqueued on
+ * `stream` (a hipStream_t; NULL means the default stream) and the call
+ * returns without waiting; the result is valid once the caller synchronises
+ * that stream.  Calls on distinct streams are independent.
+ *
+ * Errors: integer status codes only -- nothing is printed, thrown or
+ * aborted.  Argument checks run on the host before any HIP call, so a
+ * rejected call touches no device state.  The output must not overlap any
+ * input (other workgroups still read the inputs around an output row).
+ */
+#ifndef HYENA_CONV_H
+#define HYENA_CONV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum hyena_status {
+    HYENA_OK = 0,
+    HYENA_ERR_NULL = -1,        /* a required pointer is NULL */
+    HYENA_ERR_SHAPE = -2,       /* B, L or D negative, or sizes overflow */
+    HYENA_ERR_GROUP = -3,       /* group_size < 1 or D % group_size != 0 */
+    HYENA_ERR_FILTER_LEN = -4,  /* l_h outside [1, 128] */
+    HYENA_ERR_ALIGN = -5,       /* q, k, v or out not 16-byte aligned, h not element aligned */
+    HYENA_ERR_ALIAS = -6,       /* out overlaps q, k, v or h */
+    HYENA_ERR_UNSUPPORTED = -7, /* group_size not a multiple of 16, or a shape the kernel cannot address */
+    HYENA_ERR_LAUNCH = -8,      /* the HIP runtime reported an error at launch */
+    HYENA_ERR_DTYPE = -9        /* unknown element-type code */
+};
+
+enum hyena_dtype {
+    HYENA_DTYPE_BF16 = 0,
+    HYENA_DTYPE_F32 = 1
+};
+
+/* bf16 forward (see the top of this file).  B, L, D >= 0; an empty problem
+ * (B == 0, L == 0 or D == 0) is a no-op that returns HYENA_OK. */
+int hyena_conv_fwd(const void *q, const void *k, const void *v, const void *h,
+                   int64_t B, int64_t L, int64_t D, int64_t group_size,
+                   int64_t l_h, void *out, void *stream);
+
+/* fp32 forward: same arguments and layout, every buffer float32. */
+int hyena_conv_fwd_f32(const void *q, const void *k, const void *v,
+                       const void *h, int64_t B, int64_t L, int64_t D,
+                       int64_t group_size, int64_t l_h, void *out,
+                       void *stream);
+
+/* Either forward with an explicit work split: `dtype` is a hyena_dtype and
+ * `span_chunks` is the number of consecutive 64-row chunks one workgroup
+ * walks (0 = the library's choice, clamped to [1, ceil(L/64)]).  The result
+ * does not depend on `span_chunks`; it exists for tuning and for tests that
+ * cover spans which do not divide the chunk count. */
+int hyena_conv_fwd_ex(const void *q, const void *k, const void *v,
+                      const void *h, int64_t B, int64_t L, int64_t D,
+                      int64_t group_size, int64_t l_h, void *out, int dtype,
+                      int64_t span_chunks, void *stream);
+
+/* The work split hyena_conv_fwd_ex would use: writes the chunks per
+ * workgroup and the workgroup count.  Host only; runs the same argument
+ * checks on the sizes (pointers are not inspected).  Returns a status. */
+int hyena_conv_plan(int64_t B, int64_t L, int64_t D, int64_t group_size,
+                    int64_t l_h, int dtype, int64_t span_chunks,
+                    int64_t *span_out, int64_t *workgroups_out);
+
+/* Static English text for a status code (never NULL). */
+const char *hyena_conv_strerror(int status);
+
+/* The library's chunk length l_b (64). */
+int hyena_conv_block_len(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYENA_CONV_H */

@@ -1,0 +1,121 @@
+"""C-ABI contract checks that run without a GPU.
+
+The library must load, export every function ``include/hyena_conv.h``
+declares, and reject bad arguments on the host before any HIP call (so these
+calls are safe on a machine with no GPU: rejected calls never reach the
+runtime).  Pointers below are fake, non-dereferenced addresses.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_convolution_sequence_amd as hc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hyena_conv.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(hc.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return hc.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hyena_conv_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_python_export_list():
+    assert _declared_functions() == sorted(hc.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(hc.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_block_len_and_strerror():
+    assert hc.lib().hyena_conv_block_len() == 64 == hc.BLOCK_LEN
+    for code in list(hc.STATUS) + [-100, 7]:
+        assert isinstance(hc.strerror(code), str) and hc.strerror(code)
+    assert hc.strerror(0) == "ok"
+
+
+A = 1 << 20  # fake 16-byte-aligned device addresses, far apart
+P = dict(q=A, k=2 * A << 8, v=3 * A << 8, h=4 * A << 8, out=5 * A << 8)
+
+
+def _call(q=P["q"], k=P["k"], v=P["v"], h=P["h"], B=1, L=128, D=64, gs=16, l_h=7,
+          out=P["out"], dtype=hc.DTYPE_BF16, span=0):
+    return hc.lib().hyena_conv_fwd_ex(q, k, v, h, B, L, D, gs, l_h, out, dtype, span, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(h=None), -1),
+    (dict(out=None), -1),
+    (dict(B=-1), -2), (dict(L=-5), -2), (dict(D=-16), -2),
+    (dict(L=1 << 40, D=1 << 30), -2),
+    (dict(gs=0), -3), (dict(D=64, gs=48), -3),
+    (dict(l_h=0), -4), (dict(l_h=129), -4), (dict(l_h=-3), -4),
+    (dict(q=P["q"] + 8), -5), (dict(out=P["out"] + 2), -5), (dict(h=P["h"] + 1), -5),
+    (dict(dtype=hc.DTYPE_F32, h=P["h"] + 2), -5),
+    (dict(out=P["q"]), -6), (dict(out=P["k"] + 64), -6), (dict(out=P["v"] - 16), -6),
+    (dict(out=P["h"] - 64), -6),
+    (dict(D=64, gs=8), -7), (dict(D=24, gs=1), -7), (dict(D=96, gs=24), -7),
+    (dict(dtype=2), -9), (dict(dtype=-1), -9),
+])
+def test_host_validation_rejects_before_any_gpu_call(kw, code):
+    assert _call(**kw) == code
+
+
+def test_empty_problems_are_noops_even_with_null_pointers():
+    for B, L, D in [(0, 10, 16), (1, 0, 16), (1, 10, 0)]:
+        assert _call(q=None, k=None, v=None, h=None, out=None, B=B, L=L, D=D) == 0
+
+
+def test_error_precedence_shape_checks_come_first():
+    # sizes are judged before pointers: a bad l_h with NULL pointers reports l_h
+    assert _call(q=None, l_h=0) == -4
+    assert _call(q=None, gs=3, D=64) == -3
+
+
+def test_binding_raises_with_status():
+    with pytest.raises(hc.HyenaError) as ei:
+        hc.plan(1, 128, 64, 8, 7)
+    assert ei.value.status == -7
+
+
+@pytest.mark.parametrize("B,L,D,l_h,dtype,span,expect_span", [
+    (1, 8192, 4096, 7, 0, 0, 16), (1, 8192, 4096, 128, 0, 0, 16),
+    (4, 32768, 4096, 128, 0, 0, 256), (1, 1024, 256, 7, 1, 0, 1),
+    (1, 1000, 64, 7, 0, 3, 3), (1, 100, 64, 7, 0, 50, 2),
+    (1, 1 << 20, 4096, 128, 0, 0, 2048),
+])
+def test_plan_split(B, L, D, l_h, dtype, span, expect_span):
+    s, wgs = hc.plan(B, L, D, 16, l_h, dtype, span)
+    assert s == expect_span
+    chunks = -(-L // 64)
+    assert wgs == B * (-(-D // 64)) * (-(-chunks // s))
+
+
+def test_plan_keeps_the_window_addressable():
+    # a very wide row forces short spans: (span*64 + history + 64) * D * 2 < 2^31
+    D = 1 << 20
+    s, _ = hc.plan(1, 1 << 16, D, 16, 128, hc.DTYPE_BF16, 0)
+    assert (s * 64 + 128 + 64) * D * 2 < 1 << 31
+    with pytest.raises(hc.HyenaError):
+        hc.plan(1, 64, 1 << 24, 16, 128, hc.DTYPE_F32, 0)
+
+
+def test_binding_validates_tensors_on_host():
+    import torch
+    q = torch.zeros(1, 8, 16)
+    with pytest.raises(ValueError):
+        hc.conv_fwd(q, q, q, torch.zeros(1, 3), 16)  # CPU tensors are refused

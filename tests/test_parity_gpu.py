@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every test here runs hyena_conv_fwd_ex on cuda:0 via the Python binding and
+compares with oracle.conv_fwd_ref on the very same inputs, using the bar in
+tests/gpu_util.py (spec gate plus an elementwise rounding bound), or
+bitwise where every intermediate is exactly representable.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_convolution_sequence_amd as hc
+import oracle
+from gpu_util import DEV, check, log, nan_like, ref_and_envelope, to_np
+from workloads import WORKLOADS, gaussian_inputs, integer_inputs, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    hc.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run(q, k, v, h, gs, span=0, pad=16):
+    """Run the library into a NaN-filled output with canaries on both sides."""
+    n = q.numel()
+    big = torch.full((n + 2 * pad,), 7.0, dtype=q.dtype, device=q.device)
+    out = big[pad:pad + n].view(q.shape)
+    out.fill_(float("nan"))
+    hc.conv_fwd(q, k, v, h, gs, out=out, span_chunks=span)
+    torch.cuda.synchronize()
+    assert torch.all(big[:pad] == 7.0) and torch.all(big[pad + n:] == 7.0), "write outside out"
+    return out
+
+
+# ---------------------------------------------------------------------------
+# shapes: ragged L, partial slabs, every history depth, spans that do not
+# divide the chunk count, several groups per slab and groups wider than 16
+# ---------------------------------------------------------------------------
+EDGE = [
+    # B, L, D, group_size, l_h, span
+    (1, 1, 16, 16, 1, 0),
+    (1, 6, 16, 16, 4, 0),
+    (1, 63, 16, 16, 7, 0),
+    (1, 64, 64, 16, 65, 0),
+    (1, 65, 48, 16, 7, 0),
+    (2, 127, 80, 16, 33, 1),
+    (1, 129, 16, 16, 34, 1),
+    (1, 1000, 64, 32, 128, 3),
+    (3, 333, 96, 48, 65, 2),
+    (1, 640, 128, 64, 66, 4),
+    (1, 257, 16, 16, 97, 1),
+    (1, 300, 32, 16, 98, 2),
+    (2, 100, 32, 16, 2, 0),
+    (1, 4096, 256, 16, 128, 7),
+    (1, 2048, 1024, 16, 127, 0),
+    (1, 515, 208, 16, 32, 5),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h,span", EDGE)
+def test_edge_shapes_gaussian(dt, B, L, D, gs, l_h, span):
+    log("edge %s B=%d L=%d D=%d gs=%d l_h=%d span=%d" % (dt, B, L, D, gs, l_h, span))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B * 1000 + L + l_h)
+    y = run(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), gs, span)
+    ref, env = ref_and_envelope(q, k, v, h, gs)
+    check(to_np(y), ref, env, l_h, dtype, "edge")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h,span", [
+    (1, 6, 16, 16, 4, 0), (1, 1000, 64, 16, 128, 0), (2, 777, 96, 32, 7, 3),
+    (1, 2049, 128, 16, 66, 1), (1, 4096, 4096, 16, 128, 0), (3, 130, 16, 16, 33, 1),
+])
+def test_integer_inputs_are_bitwise_exact(dt, B, L, D, gs, l_h, span):
+    """q, k, v in {-1,0,1}, taps in {-2..2}: every partial sum is a small integer."""
+    log("integer %s B=%d L=%d D=%d gs=%d l_h=%d span=%d" % (dt, B, L, D, gs, l_h, span))
+    dtype = DTYPES[dt]
+    q, k, v, h = integer_inputs(B, L, D, gs, l_h, dtype, seed=L + D)
+    y = run(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), gs, span)
+    ref = oracle.conv_fwd_ref(to_np(q), to_np(k), to_np(v), to_np(h), gs)
+    assert np.array_equal(to_np(y), ref)
+
+
+def test_worked_example_shape_matches_two_stage_blocks():
+    """l = 6, l_h = 4 (the worked example's sizes) on 16 channels of one group."""
+    log("worked example on GPU")
+    L, l_h = 6, 4
+    h = torch.tensor([[1.0, 2.0, 4.0, 8.0]], dtype=torch.bfloat16)
+    v = torch.zeros(1, L, 16, dtype=torch.bfloat16)
+    for d in range(16):
+        v[0, d % L, d] = 1.0 + (d // L)  # channel d: impulse at time d % 6
+    ones = torch.ones_like(v)
+    y = to_np(run(ones.to(DEV), ones.to(DEV), v.to(DEV), h.to(DEV), 16))
+    for d in range(16):
+        t0, a = d % L, 1.0 + (d // L)
+        expect = np.zeros(L)
+        n = min(l_h, L - t0)
+        expect[t0:t0 + n] = a * np.array([1.0, 2.0, 4.0, 8.0])[:n]
+        assert np.array_equal(y[0, :, d], expect), d
+
+
+@pytest.mark.parametrize("l_h", [1, 7, 64, 65, 66, 127, 128])
+def test_impulses_on_chunk_seams_reproduce_the_filter(l_h):
+    L, D = 600, 64
+    seams = [0, 1, 63, 64, 65, 127, 128, 191, 192, 255, 256, 383, 384, 511, 512, L - 1]
+    rng = np.random.default_rng(l_h)
+    h = torch.tensor(rng.standard_normal((D // 16, l_h)), dtype=torch.bfloat16)
+    v = torch.zeros(1, L, D, dtype=torch.bfloat16)
+    for d in range(D):
+        v[0, seams[d % len(seams)], d] = 1.0
+    ones = torch.ones_like(v)
+    for span in (0, 1, 3):
+        log("impulses l_h=%d span=%d" % (l_h, span))
+        y = to_np(run(ones.to(DEV), ones.to(DEV), v.to(DEV), h.to(DEV), 16, span))
+        ref = oracle.conv_fwd_ref(to_np(ones), to_np(ones), to_np(v), to_np(h), 16)
+        assert np.array_equal(y, ref)
+
+
+def test_mr_last_tap_and_flat_filters():
+    """A kernel missing the chunk n-2 block fails both by O(1)."""
+    B, L, D, l_h = 1, 1024, 128, 128
+    q, k, v, _ = gaussian_inputs(B, L, D, 16, l_h, torch.bfloat16, seed=5)
+    last = torch.zeros(D // 16, l_h, dtype=torch.bfloat16)
+    last[:, l_h - 1] = 1.0
+    flat = torch.ones(D // 16, l_h, dtype=torch.bfloat16)
+    ones = torch.ones_like(q)
+    log("mr last tap")
+    y = to_np(run(ones.to(DEV), ones.to(DEV), v.to(DEV), last.to(DEV), 16))
+    ref = oracle.conv_fwd_ref(to_np(ones), to_np(ones), to_np(v), to_np(last), 16)
+    assert np.array_equal(y, ref)  # a single exact term per output
+    log("mr flat")
+    y = to_np(run(q.to(DEV), k.to(DEV), v.to(DEV), flat.to(DEV), 16))
+    ref, env = ref_and_envelope(q, k, v, flat, 16)
+    check(y, ref, env, l_h, torch.bfloat16, "flat")
+
+
+def test_deterministic_and_span_independent_rounding():
+    """Bitwise identical across reruns; any span gives the same bits (same sum order)."""
+    q, k, v, h = gaussian_inputs(2, 3000, 256, 16, 128, torch.bfloat16, seed=11)
+    q, k, v, h = q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV)
+    log("determinism")
+    y0 = run(q, k, v, h, 16).clone()
+    for span in (0, 0, 1, 2, 5, 47):
+        y1 = run(q, k, v, h, 16, span)
+        assert torch.equal(y0, y1), span
+
+
+def test_batch_rows_and_causality():
+    B, L, D, l_h = 3, 700, 64, 100
+    q, k, v, h = gaussian_inputs(B, L, D, 16, l_h, torch.bfloat16, seed=12)
+    k[1] = 0
+    q, k, v, h = q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV)
+    log("batch isolation and causality")
+    y0 = run(q, k, v, h, 16).clone()
+    assert torch.all(y0[1] == 0)
+    t0 = 301
+    v2 = v.clone()
+    v2[:, t0] += 3.0
+    y1 = run(q, k, v2, h, 16)
+    assert torch.equal(y0[:, :t0], y1[:, :t0])
+    assert torch.equal(y0[:, t0 + l_h:], y1[:, t0 + l_h:])
+
+
+def test_stream_argument_is_honoured():
+    q, k, v, h = gaussian_inputs(1, 512, 64, 16, 7, torch.bfloat16, seed=13)
+    q, k, v, h = q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV)
+    s = torch.cuda.Stream()
+    out = nan_like(q)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        hc.conv_fwd(q, k, v, h, 16, out=out)
+    s.synchronize()
+    ref, env = ref_and_envelope(q.cpu(), k.cpu(), v.cpu(), h.cpu(), 16)
+    check(to_np(out), ref, env, 7, torch.bfloat16, "stream")
+
+
+# ---------------------------------------------------------------------------
+# The workloads at full size
+# ---------------------------------------------------------------------------
+
+def test_tiny_se_fp32_full():
+    w = WORKLOADS["tiny_se"]
+    log("tiny_se full")
+    q, k, v, h = make_inputs(w, "cpu")
+    y = run(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), w.group_size)
+    ref, env = ref_and_envelope(q, k, v, h, w.group_size)
+    rel = check(to_np(y), ref, env, w.l_h, w.torch_dtype, "tiny_se")
+    log("tiny_se rel err %.3e" % rel)
+
+
+@pytest.mark.parametrize("name", ["se", "mr"])
+def test_full_workload_every_element(name):
+    w = WORKLOADS[name]
+    log("%s full: generate" % name)
+    q, k, v, h = make_inputs(w, DEV)
+    y = run(q, k, v, h, w.group_size)
+    log("%s full: oracle" % name)
+    ref, env = ref_and_envelope(q, k, v, h, w.group_size)
+    rel = check(to_np(y), ref, env, w.l_h, w.torch_dtype, name)
+    log("%s rel err %.3e" % (name, rel))
+
+
+def _window_check(q, k, v, h, y, w, b, t0, t1, c0, c1):
+    """Exact sub-problem: rows [t0, t1) of channels [c0, c1) need l_h-1 rows of history."""
+    gs = w.group_size
+    s = max(0, t0 - (w.l_h - 1))
+    sl = lambda a: a[b:b + 1, s:t1, c0:c1]
+    hh = h[c0 // gs:c1 // gs]
+    ref, env = ref_and_envelope(sl(q), sl(k), sl(v), hh, gs)
+    got = to_np(sl(y))
+    off = t0 - s
+    check(got[:, off:], ref[:, off:], env[:, off:], w.l_h, w.torch_dtype,
+          "%s b=%d t=[%d,%d) c=[%d,%d)" % (w.name, b, t0, t1, c0, c1))
+
+
+def _sampled_checks(w, q, k, v, h, y, n_groups, seed):
+    L, D = w.L, w.D
+    mid = (1 << 31) // D  # the row where the element index reaches 2^31
+    windows = [(0, 256), (L // 2 - 100, L // 2 + 37), (L - 256, L)]
+    if mid + 128 <= L:
+        windows.append((mid - 128, mid + 128))
+    for b in sorted({0, w.B - 1}):
+        for t0, t1 in windows:
+            log("  window b=%d [%d,%d)" % (b, t0, t1))
+            _window_check(q, k, v, h, y, w, b, t0, t1, 0, D)
+    rng = np.random.default_rng(seed)
+    groups = sorted({0, w.G - 1, *rng.choice(w.G, size=n_groups, replace=False).tolist()})
+    for g in groups:
+        b = int(rng.integers(w.B))
+        log("  full-length group %d b=%d" % (g, b))
+        _window_check(q, k, v, h, y, w, b, 0, L, g * w.group_size, (g + 1) * w.group_size)
+
+
+def test_mr_b4_sampled():
+    w = WORKLOADS["mr_b4"]
+    log("mr_b4: generate")
+    q, k, v, h = make_inputs(w, DEV)
+    y = run(q, k, v, h, w.group_size)
+    _sampled_checks(w, q, k, v, h, y, n_groups=4, seed=4)
+
+
+def test_long_stripe_sampled():
+    """SE layer then MR layer at L = 2^20 (2^32 elements per tensor), one stream."""
+    outs = []
+    for name in ("long_se", "long_mr"):
+        w = WORKLOADS[name]
+        log("%s: generate" % name)
+        q, k, v, h = make_inputs(w, DEV)
+        y = nan_like(q)
+        hc.conv_fwd(q, k, v, h, w.group_size, out=y)
+        outs.append((w, q, k, v, h, y))
+    torch.cuda.synchronize()
+    for w, q, k, v, h, y in outs:
+        log("%s: sampled checks" % w.name)
+        assert not torch.isnan(y[0, -1]).any()
+        _sampled_checks(w, q, k, v, h, y, n_groups=2, seed=5)
+        del q, k, v, h, y

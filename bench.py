@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Throughput of the Hyena-SE / Hyena-MR forward on one MI355X.
+
+One step = one pass of the whole forward path over one batch of synthetic
+input: a Hyena-SE layer (l_h = 7) and then a Hyena-MR layer (l_h = 128), each
+y = q (.) (h * (k (.) v)) at B = 1, L = 8192, D = 4096, 16 channels per
+filter group, bf16 I/O with fp32 accumulation, with independent seeded inputs
+per layer (the two layers of a striped block at the 8K pretraining context).
+``--workload`` selects another shape for exploration (se, mr, mr_b4,
+long_stripe); the default line is the stripe.
+
+Reported (one JSON line):
+  value        whole-step throughput, G(token*channel)/s = 2 * B*L*D / step time
+               (both layers count), inputs resident in HBM;
+  roofline     the MR kernel (the longer of the two): algorithmic bytes per
+               launch (q, k, v read once, y written once: 8 B per
+               token*channel) / its mean launch time from HIP events on the
+               launch stream, against the 8 TB/s HBM3E peak; `traffic` is the
+               measured HBM bytes per launch from the committed rocprofv3
+               counter summary, or null if the kernel source changed since;
+  layers       the same figures for each layer's kernel;
+  cpu_baseline the fp64 oracle on the host cores over the full step's inputs;
+  naive_conv1d the same step written with torch's depthwise F.conv1d (bf16),
+               with and without the layout permutes.
+Input sets rotate over ``--sets`` copies per layer so that no launch finds its
+operands in the 256 MB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Hyena-SE/MR fwd: G(token·channel)/s and % of HBM-bandwidth roofline, D=4096"
+UNIT = "G(token·channel)/s"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "gated_convolution_sequence_amd", "csrc", "hyena_conv.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+WORKLOAD_LAYERS = {
+    "stripe_8k": ["se", "mr"],
+    "se": ["se"],
+    "mr": ["mr"],
+    "mr_b4": ["mr_b4"],
+    "long_stripe": ["long_se", "long_mr"],
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="stripe_8k", choices=sorted(WORKLOAD_LAYERS))
+    ap.add_argument("--sets", type=int, default=4, help="input copies per layer (cache rotation)")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-naive", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="rough CPU budget of the oracle baseline")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="instead of the step, run a plain device copy of this many MiB "
+                         "(reference point for the HBM byte counters)")
+    return ap.parse_args()
+
+
+def calibrate_copy(mib: int, reps: int = 10):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE give the counter scale."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "reps": reps}), flush=True)
+
+
+def source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(layer: str):
+    """HBM bytes per launch from the committed counter summary, if still current."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != source_digest():
+        return None
+    entry = t.get("layers", {}).get(layer)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this operator is benchmarked on a single MI355X; "
+              "--gpus %d is not supported (the multi-GPU split is described in DESIGN.md)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
+
+    import torch
+    import gated_convolution_sequence_amd as hc
+    from workloads import WORKLOADS, make_inputs
+
+    if not os.path.exists(hc.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    layer_names = WORKLOAD_LAYERS[args.workload]
+    layers = [WORKLOADS[n] for n in layer_names]
+
+    # ---- inputs: set 0 from the seeds, further sets are copies -------------
+    t_gen = time.time()
+    sets = []
+    for w in layers:
+        q, k, v, h = make_inputs(w, dev)
+        n_sets = args.sets if w.elems * 8 * args.sets <= (64 << 30) else 1
+        per = [(q, k, v, h, torch.empty_like(q))]
+        for _ in range(n_sets - 1):
+            per.append((q.clone(), k.clone(), v.clone(), h, torch.empty_like(q)))
+        sets.append(per)
+    torch.cuda.synchronize()
+    print("inputs ready in %.1fs" % (time.time() - t_gen), file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None):
+        for li, w in enumerate(layers):
+            q, k, v, h, y = sets[li][i % len(sets[li])]
+            if events is not None:
+                events[li][0].record(stream)
+            hc.conv_fwd(q, k, v, h, w.group_size, out=y, stream=stream)
+            if events is not None:
+                events[li][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps ------------------------------------
+    K = args.steps
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+           for _ in layers] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+
+    elems_step = sum(w.elems for w in layers)
+    value = elems_step / (wall / K) / 1e9
+
+    layer_stats = {}
+    for li, w in enumerate(layers):
+        ms = [ev[i][li][0].elapsed_time(ev[i][li][1]) for i in range(K)]
+        mean_ms = sum(ms) / len(ms)
+        alg_bytes = w.elems * (4 * (2 if w.dtype == "bf16" else 4))
+        achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
+        span, wgs = hc.plan(w.B, w.L, w.D, w.group_size, w.l_h,
+                            hc.DTYPE_BF16 if w.dtype == "bf16" else hc.DTYPE_F32)
+        layer_stats[w.name] = {
+            "B": w.B, "L": w.L, "D": w.D, "l_h": w.l_h, "kernel_KH": (w.l_h - 1 + 31) // 32,
+            "mean_us": round(mean_ms * 1e3, 2), "median_us": round(statistics.median(ms) * 1e3, 2),
+            "p10_us": round(sorted(ms)[len(ms) // 10] * 1e3, 2),
+            "p90_us": round(sorted(ms)[(9 * len(ms)) // 10] * 1e3, 2),
+            "G_tok_ch_per_s": round(w.elems / (mean_ms * 1e-3) / 1e9, 2),
+            "alg_bytes": alg_bytes, "achieved_GBs": round(achieved, 1),
+            "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+            "span_chunks": span, "workgroups": wgs,
+        }
+    dom = max(layer_stats, key=lambda n: layer_stats[n]["mean_us"])
+    d = layer_stats[dom]
+    traffic = measured_traffic(dom)
+    roofline = {"bound": "hbm", "achieved": d["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(d["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "hyena_fwd_kernel<bf16, KH=%d> (%s layer)" % (d["kernel_KH"], dom),
+                "alg_bytes_per_launch": d["alg_bytes"], "mean_launch_us": d["mean_us"]}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": UNIT, "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if layers[0].dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) q,k,v; Gaussian SE taps, decaying MR taps)",
+        "config": {"workload": "%s: %s" % (args.workload, " then ".join(
+            "%s(B=%d,L=%d,D=%d,group_size=%d,l_h=%d)" % (w.name, w.B, w.L, w.D, w.group_size, w.l_h)
+            for w in layers)), "l_b": 64, "input_sets_rotated": len(sets[0])},
+        "roofline": roofline,
+        "layers": layer_stats,
+    }
+
+    # ---- naive baseline: torch depthwise conv1d ---------------------------
+    if not args.skip_naive:
+        out["naive_conv1d"] = naive_conv1d(layers, sets, stream, max(5, K // 10))
+
+    # ---- CPU baseline: the oracle on the host -----------------------------
+    if not args.skip_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(layers, sets, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def naive_conv1d(layers, sets, stream, reps):
+    """The step as a user would write it with torch ops (MIOpen depthwise conv)."""
+    import torch
+    import torch.nn.functional as F
+
+    def layer_fn(w, q, k, v, h, permute):
+        weight = torch.repeat_interleave(h, w.group_size, dim=0).flip(-1)[:, None, :].contiguous()
+        if permute:
+            x = (k * v).transpose(1, 2)  # [B, D, L]
+            z = F.conv1d(x, weight, padding=w.l_h - 1, groups=w.D)[..., :w.L]
+            return q * z.transpose(1, 2)
+        return F.conv1d(k, weight, padding=w.l_h - 1, groups=w.D)[..., :w.L]
+
+    res = {}
+    try:
+        for permute in (True, False):
+            for i in range(2):
+                for li, w in enumerate(layers):
+                    q, k, v, h, _ = sets[li][i % len(sets[li])]
+                    kk = k if permute else k.view(w.B, w.D, w.L)
+                    layer_fn(w, q, kk, v, h, permute)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(reps):
+                for li, w in enumerate(layers):
+                    q, k, v, h, _ = sets[li][i % len(sets[li])]
+                    kk = k if permute else k.view(w.B, w.D, w.L)
+                    layer_fn(w, q, kk, v, h, permute)
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / reps
+            key = "with_permutes_and_gating" if permute else "conv1d_only"
+            res[key] = {"ms_per_step": round(dt * 1e3, 4),
+                        "value": round(sum(w.elems for w in layers) / dt / 1e9, 2), "unit": UNIT}
+    except Exception as e:  # report, do not hide, a failing baseline
+        res["error"] = repr(e)
+    return res
+
+
+def cpu_baseline(layers, sets, budget_s):
+    """fp64 oracle over the step's inputs on the host cores (bounded sample)."""
+    import torch
+
+    import oracle
+
+    per_layer = []
+    t_total, elems_total = 0.0, 0
+    sample_desc = []
+    for li, w in enumerate(layers):
+        q, k, v, h, _ = sets[li][0]
+        # bounded sample: whole sequences of the first `ch` channels
+        rate_probe_ch = min(w.D, 64)
+        cols = lambda a, c: a[:, :, :c].to("cpu", dtype=torch.float64).numpy()
+        hq = h[: rate_probe_ch // w.group_size].to("cpu", dtype=torch.float64).numpy()
+        t0 = time.perf_counter()
+        oracle.conv_fwd_ref(cols(q, rate_probe_ch), cols(k, rate_probe_ch), cols(v, rate_probe_ch),
+                            hq, w.group_size)
+        probe = time.perf_counter() - t0
+        per_elem = probe / (w.B * w.L * rate_probe_ch)
+        share = budget_s / len(layers)
+        ch = int(min(w.D, max(rate_probe_ch, share / (per_elem * w.B * w.L))))
+        ch = max(w.group_size, (ch // w.group_size) * w.group_size)
+        hq = h[: ch // w.group_size].to("cpu", dtype=torch.float64).numpy()
+        qa, ka, va = cols(q, ch), cols(k, ch), cols(v, ch)
+        t0 = time.perf_counter()
+        oracle.conv_fwd_ref(qa, ka, va, hq, w.group_size)
+        dt = time.perf_counter() - t0
+        n = w.B * w.L * ch
+        per_layer.append({"layer": w.name, "channels": ch, "seconds": round(dt, 3),
+                          "G_tok_ch_per_s": round(n / dt / 1e9, 5)})
+        sample_desc.append("%s: all %d rows x first %d of %d channels" % (w.name, w.B * w.L, ch, w.D))
+        # the step's time at this rate: every layer's full size
+        t_total += dt * (w.elems / n)
+        elems_total += w.elems
+    return {"value": round(elems_total / t_total / 1e9, 5), "unit": UNIT,
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "; ".join(sample_desc) + " (rate scaled to the full step)",
+            "cpu_count": os.cpu_count(), "layers": per_layer}
+
+
+if __name__ == "__main__":
+    main()

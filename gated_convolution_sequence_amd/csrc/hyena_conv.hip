@@ -47,6 +47,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "hyena_conv.h"
 
 namespace {
@@ -74,7 +76,6 @@ struct Params {
     int32_t D;          // channels (row pitch, elements)
     int32_t group_size;
     int32_t l_h;
-    int32_t span;       // chunks per workgroup
     int32_t n_spans;    // spans per batch row
     int32_t n_slabs;    // 64-channel slabs
 };
@@ -116,13 +117,22 @@ template <> struct Tr<true> {            // fp32 I/O
     __device__ static int swz(int row) { return (row & 3) << 2; }
 };
 
-template <bool F32, int KH>
+// Kernel: F32 selects the element type, KH the 32-row history steps
+// (KH = ceil((l_h - 1) / 32)), PF the chunks of k, v and q kept in flight,
+// S the chunks of one span.  The walk over the span is fully unrolled: the
+// prefetched registers are then never loop-carried, so the compiler's
+// memory-counter waits are exact and no in-flight load is copied.
+template <bool F32, int KH, int PF, int S>
 __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     using T = Tr<F32>;
-    constexpr int HROWS = 32 * KH;                    // history rows before a span
+    constexpr int HROWS = 32 * KH;                        // history rows before a span
     constexpr int C0 = -((HROWS + kChunk - 1) / kChunk);  // first (history) chunk
+    constexpr int ST_PITCH = kSlab * 4;                   // fp32 staging row, bytes
 
-    __shared__ __attribute__((aligned(16))) unsigned char xs[2][kChunk * T::PITCH];
+    // x = k*v of the current chunk (row-major, swizzled), the fp32
+    // accumulators of the current chunk (row-major, swizzled) and the filters.
+    __shared__ __attribute__((aligned(16))) unsigned char xs[kChunk * T::PITCH];
+    __shared__ __attribute__((aligned(16))) unsigned char st[kChunk * ST_PITCH];
     __shared__ float hs[kWaves][kHLen];
 
     const int tid = threadIdx.x;
@@ -137,16 +147,16 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     const int spn = bid % p.n_spans;
     const int b = bid / p.n_spans;
 
-    const int64_t t_begin = (int64_t)spn * p.span * kChunk;
-    const int64_t t_stop = min(p.L, t_begin + (int64_t)p.span * kChunk);
-    const int nck = (int)((t_stop - t_begin + kChunk - 1) / kChunk);
+    const int64_t t_begin = (int64_t)spn * S * kChunk;
+    const int64_t t_stop = min(p.L, t_begin + (int64_t)S * kChunk);
     const int64_t base_row = max((int64_t)0, t_begin - HROWS);
     const int c_begin = slab * kSlab;
     const int row_bytes = p.D * T::EB;
 
     // Byte window [base, base + nrec) of this workgroup: rows base_row ..
     // t_stop-1 of batch b, starting at channel c_begin.  The host keeps it
-    // below 2^31 bytes, so a negative (earlier) row offset is out of range.
+    // below 2^31 bytes, so a negative (earlier) row offset is out of range,
+    // as is every row at or past t_stop.
     const size_t base_off = ((size_t)b * (size_t)p.L + (size_t)base_row) * (size_t)row_bytes +
                             (size_t)c_begin * T::EB;
     const uint32_t nrec = (uint32_t)((t_stop - base_row) * row_bytes - c_begin * T::EB);
@@ -173,26 +183,37 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
         }
     }
 
-    // ---- cooperative k, v loads: thread -> (row, 16-byte segment) ----------
+    // ---- cooperative row-major access: thread -> (row, 16-byte segment) ----
+    // q, k, v and y all use it: 16 bytes per lane, whole 128/256-byte rows.
     const int ld_row = tid / T::TPR;
     const int ld_seg = tid % T::TPR;
     const bool seg_ok = c_begin + ld_seg * T::VEC < p.D;
-    auto kv_off = [&](int c, int i) -> uint32_t {
-        const int r = row0 + c * kChunk + i * T::RPL + ld_row;
-        return seg_ok ? (uint32_t)(r * row_bytes + ld_seg * 16) : kOOB;
+    const int ld_base = ld_row * row_bytes + ld_seg * 16;
+    // Offsets of chunk c, load i; chunks past the span fall outside the byte
+    // window (no traffic, no store), and history chunks (c < 0) never touch q
+    // or y.
+    auto io_off = [&](int c, int i, bool need) -> uint32_t {
+        const int r = (row0 + c * kChunk + i * T::RPL) * row_bytes + ld_base;
+        return (seg_ok && need) ? (uint32_t)r : kOOB;
     };
 
-    u32x4_t kr[T::NLD], vr[T::NLD];
-    auto load_kv = [&](int c) {
+    u32x4_t kr[PF][T::NLD], vr[PF][T::NLD], qr[PF][T::NLD];
+
+    auto load_kv = [&](int c, u32x4_t *kd, u32x4_t *vd) {
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
-            const uint32_t o = kv_off(c, i);
-            kr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
-            vr[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+            const uint32_t o = io_off(c, i, true);
+            kd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+            vd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
         }
     };
-    // x = k*v for this thread's rows of chunk c -> LDS buffer `buf`.
-    auto store_x = [&](int buf) {
+    auto load_q = [&](int c, u32x4_t *qd) {
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i)
+            qd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, io_off(c, i, c >= 0), 0, 0));
+    };
+    // x = k*v for this thread's rows -> xs.
+    auto store_x = [&](const u32x4_t *kd, const u32x4_t *vd) {
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
             const int row = i * T::RPL + ld_row;
@@ -200,24 +221,53 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
             if constexpr (F32) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    xv[e] = __float_as_uint(__uint_as_float(kr[i][e]) * __uint_as_float(vr[i][e]));
+                    xv[e] = __float_as_uint(__uint_as_float(kd[i][e]) * __uint_as_float(vd[i][e]));
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    xv[e] = pack_bf16(bf_lo(kr[i][e]) * bf_lo(vr[i][e]),
-                                      bf_hi(kr[i][e]) * bf_hi(vr[i][e]));
+                    xv[e] = pack_bf16(bf_lo(kd[i][e]) * bf_lo(vd[i][e]),
+                                      bf_hi(kd[i][e]) * bf_hi(vd[i][e]));
             }
-            const int off = row * T::PITCH + ((ld_seg ^ T::swz(row)) << 4);
-            *(u32x4_t *)(&xs[buf][off]) = xv;
+            *(u32x4_t *)(&xs[row * T::PITCH + ((ld_seg ^ T::swz(row)) << 4)]) = xv;
         }
     };
-
-    // ---- epilogue geometry: lane holds times 16nt + n16, channels 4q4..4q4+3
-    const int ep_col = (w * kTile + 4 * q4) * T::EB;
-    auto ep_off = [&](int c, int nt) -> uint32_t {
-        const int r = row0 + c * kChunk + nt * 16 + n16;
-        return tile_ok ? (uint32_t)(r * row_bytes + ep_col) : kOOB;
+    // Accumulator staging: row t_out, 16-byte segment (4 fp32 channels) XOR
+    // (row & 15), so 16 lanes writing one segment column of 16 rows, and the
+    // row-major readers, hit distinct banks.
+    auto st_addr = [&](int row, int seg) -> int { return row * ST_PITCH + ((seg ^ (row & 15)) << 4); };
+    // Epilogue: y = q * acc for this thread's rows, coalesced 16-byte stores.
+    auto epilogue = [&](int c, u32x4_t *qd) {
+        u32x4_t yv[T::NLD];
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const int row = i * T::RPL + ld_row;
+            if constexpr (F32) {
+                const f32x4_t a = *(const f32x4_t *)(&st[st_addr(row, ld_seg)]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) yv[i][e] = __float_as_uint(__uint_as_float(qd[i][e]) * a[e]);
+            } else {
+                const f32x4_t a0 = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg)]);
+                const f32x4_t a1 = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg + 1)]);
+                yv[i][0] = pack_bf16(bf_lo(qd[i][0]) * a0[0], bf_hi(qd[i][0]) * a0[1]);
+                yv[i][1] = pack_bf16(bf_lo(qd[i][1]) * a0[2], bf_hi(qd[i][1]) * a0[3]);
+                yv[i][2] = pack_bf16(bf_lo(qd[i][2]) * a1[0], bf_hi(qd[i][2]) * a1[1]);
+                yv[i][3] = pack_bf16(bf_lo(qd[i][3]) * a1[2], bf_hi(qd[i][3]) * a1[3]);
+            }
+        }
+        // refill q before storing y, so y never shares registers with q
+        load_q(c + PF, qd);
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(yv[i], ry, io_off(c, i, c >= 0), 0, 0);
     };
+
+    // Prologue: the first PF chunks in flight.  Each step then consumes the
+    // oldest slot and refills it with the chunk PF ahead.
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+        load_kv(C0 + s, kr[s], vr[s]);
+        load_q(C0 + s, qr[s]);
+    }
 
     __syncthreads();  // filters staged
 
@@ -246,56 +296,39 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
         const int ch = w * kTile + n16;
         const int rd_base = (8 * q4) * T::PITCH + ((((ch >> 3) ^ (2 * q4))) << 4) + ((ch & 7) << 1);
 
-        u32x2_t qc[4], qn[4];
-        auto load_q = [&](int c, u32x2_t *dst) {
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-                dst[nt] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rq, ep_off(c, nt), 0, 0));
-        };
-
-        load_kv(C0);
-        if (C0 == 0) load_q(0, qc);
-        for (int c = C0; c < nck; ++c) {
-            const int buf = (c - C0) & 1;
-            store_x(buf);
-            if (c + 1 < nck) {
-                if (c + 1 >= 0) load_q(c + 1, qn);
-                load_kv(c + 1);
-            }
+        auto step = [&](int c, u32x4_t *kd, u32x4_t *vd, u32x4_t *qd) {
+            store_x(kd, vd);
+            load_kv(c + PF, kd, vd);
             __syncthreads();
-            const unsigned char *xb = xs[buf];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const uint16_t raw = *(const uint16_t *)(xb + rd_base + (32 * kk + j) * T::PITCH);
+                    const uint16_t raw = *(const uint16_t *)(&xs[rd_base + (32 * kk + j) * T::PITCH]);
                     X[KH + kk][j] = __builtin_bit_cast(__bf16, raw);
                 }
             }
-            if (c >= 0) {
 #pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int nt = 0; nt < 4; ++nt) {
+                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int kk = 0; kk < NX; ++kk) {
-                        const int kappa = kk - KH;
-                        const int e = nt - 2 * kappa;
-                        if (e < 0 || e >= NE) continue;
-                        if (16 * e - 31 >= p.l_h) continue;  // every tap past the filter
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(X[kk], F[e], acc, 0, 0, 0);
-                    }
-                    const u32x2_t qv = qc[nt];
-                    u32x2_t yv;
-                    yv[0] = pack_bf16(bf_lo(qv[0]) * acc[0], bf_hi(qv[0]) * acc[1]);
-                    yv[1] = pack_bf16(bf_lo(qv[1]) * acc[2], bf_hi(qv[1]) * acc[3]);
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, yv), ry, ep_off(c, nt), 0, 0);
+                for (int kk = 0; kk < NX; ++kk) {
+                    const int e = nt - 2 * (kk - KH);
+                    if (e < 0) continue;  // strictly above the diagonal: all zero
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(X[kk], F[e], acc, 0, 0, 0);
                 }
+                // lane holds output time 16 nt + n16, channels 4 q4 .. 4 q4 + 3
+                *(f32x4_t *)(&st[st_addr(16 * nt + n16, 4 * w + q4)]) = acc;
             }
+            __syncthreads();
+            epilogue(c, qd);
 #pragma unroll
             for (int i = 0; i < KH; ++i) X[i] = X[i + 2];
+        };
+        // Chunks past t_stop (a short last span) run on zeros and store
+        // nothing: their rows are outside the byte window.
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) qc[nt] = qn[nt];
-        }
+        for (int c = C0; c < S; ++c) step(c, kr[(c - C0) % PF], vr[(c - C0) % PF], qr[(c - C0) % PF]);
     } else {
         // ================= fp32: v_mfma_f32_16x16x4_f32 ====================
         constexpr int H4 = HROWS / 4;   // history steps of 4 rows
@@ -314,64 +347,66 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
         const int ch = w * kTile + n16;
         const int rd_base = q4 * T::PITCH + ((((ch >> 2) ^ (4 * q4))) << 4) + ((ch & 3) << 2);
 
-        u32x4_t qc[4], qn[4];
-        auto load_q = [&](int c, u32x4_t *dst) {
+        auto step = [&](int c, u32x4_t *kd, u32x4_t *vd, u32x4_t *qd) {
+            store_x(kd, vd);
+            load_kv(c + PF, kd, vd);
+            __syncthreads();
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-                dst[nt] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, ep_off(c, nt), 0, 0));
-        };
-
-        load_kv(C0);
-        if (C0 == 0) load_q(0, qc);
-        for (int c = C0; c < nck; ++c) {
-            const int buf = (c - C0) & 1;
-            store_x(buf);
-            if (c + 1 < nck) {
-                if (c + 1 >= 0) load_q(c + 1, qn);
-                load_kv(c + 1);
+            for (int s4 = 0; s4 < 16; ++s4)
+                X[H4 + s4] = *(const float *)(&xs[rd_base + (4 * s4) * T::PITCH]);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kk = 0; kk < NX; ++kk) {
+                    const int e4 = 4 * nt - (kk - H4);
+                    if (e4 < -3 || e4 + 3 >= NE) continue;
+                    if (4 * e4 - 3 >= p.l_h) continue;  // every tap past the filter
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[kk], F[e4 + 3], acc, 0, 0, 0);
+                }
+                *(f32x4_t *)(&st[st_addr(16 * nt + n16, 4 * w + q4)]) = acc;
             }
             __syncthreads();
-            const unsigned char *xb = xs[buf];
-#pragma unroll
-            for (int s = 0; s < 16; ++s)
-                X[H4 + s] = *(const float *)(xb + rd_base + (4 * s) * T::PITCH);
-            if (c >= 0) {
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int kk = 0; kk < NX; ++kk) {
-                        const int kappa4 = kk - H4;
-                        const int e4 = 4 * nt - kappa4;
-                        if (e4 < -3 || e4 + 3 >= NE) continue;
-                        if (4 * e4 - 3 >= p.l_h) continue;
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[kk], F[e4 + 3], acc, 0, 0, 0);
-                    }
-                    const u32x4_t qv = qc[nt];
-                    u32x4_t yv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) yv[e] = __float_as_uint(__uint_as_float(qv[e]) * acc[e]);
-                    __builtin_amdgcn_raw_buffer_store_b128(yv, ry, ep_off(c, nt), 0, 0);
-                }
-            }
+            epilogue(c, qd);
 #pragma unroll
             for (int i = 0; i < H4; ++i) X[i] = X[i + 16];
+        };
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) qc[nt] = qn[nt];
-        }
+        for (int c = C0; c < S; ++c) step(c, kr[(c - C0) % PF], vr[(c - C0) % PF], qr[(c - C0) % PF]);
     }
 }
 
 typedef void (*KernelFn)(Params);
 
+// Chunks of k, v and q in flight per workgroup.  The fp32 path (twice the
+// bytes per element, one row per MFMA step) keeps two to stay spill-free.
+template <bool F32> constexpr int kPrefetch = F32 ? 2 : 3;
+
+// Spans (chunks per workgroup) with a compiled kernel; a requested span is
+// rounded down to one of these.  fp32 stops at 8 (register budget).
+constexpr int kSpans[] = {1, 2, 4, 8, 16, 32};
+constexpr int kNumSpans = sizeof(kSpans) / sizeof(kSpans[0]);
+template <bool F32> constexpr int kNumSpansFor = F32 ? 4 : kNumSpans;
+
+template <bool F32, int KH, int... Ss>
+KernelFn span_table_entry(int si, std::integer_sequence<int, Ss...>) {
+    static constexpr KernelFn fns[] = {hyena_fwd_kernel<F32, KH, kPrefetch<F32>, kSpans[Ss]>...};
+    return fns[si];
+}
+
+template <bool F32, int KH>
+KernelFn pick_span(int si) {
+    return span_table_entry<F32, KH>(si, std::make_integer_sequence<int, kNumSpansFor<F32>>{});
+}
+
 template <bool F32>
-KernelFn pick_kernel(int kh) {
+KernelFn pick_kernel(int kh, int si) {
     switch (kh) {
-    case 0: return hyena_fwd_kernel<F32, 0>;
-    case 1: return hyena_fwd_kernel<F32, 1>;
-    case 2: return hyena_fwd_kernel<F32, 2>;
-    case 3: return hyena_fwd_kernel<F32, 3>;
-    default: return hyena_fwd_kernel<F32, 4>;
+    case 0: return pick_span<F32, 0>(si);
+    case 1: return pick_span<F32, 1>(si);
+    case 2: return pick_span<F32, 2>(si);
+    case 3: return pick_span<F32, 3>(si);
+    default: return pick_span<F32, 4>(si);
     }
 }
 
@@ -381,7 +416,7 @@ constexpr int64_t kMaxWindowBytes = (int64_t)1 << 31;
 
 struct Plan {
     int64_t span, n_spans, n_slabs, n_chunks, workgroups;
-    int kh;
+    int kh, span_index;
 };
 
 int check_sizes(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, int dtype) {
@@ -399,25 +434,31 @@ int check_sizes(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h
 
 int make_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, int dtype,
               int64_t span_req, Plan *pl) {
-    (void)group_size;
     const int64_t eb = dtype == HYENA_DTYPE_F32 ? 4 : 2;
     pl->kh = (int)((l_h - 1 + 31) / 32);
     pl->n_chunks = (L + kChunk - 1) / kChunk;
     pl->n_slabs = (D + kSlab - 1) / kSlab;
     if (group_size % kTile != 0) return HYENA_ERR_UNSUPPORTED;
     if (D > INT32_MAX / 16) return HYENA_ERR_UNSUPPORTED;
-    int64_t span = span_req;
-    if (span <= 0) {
+    int64_t want = span_req;
+    if (want <= 0) {
         const int64_t total = pl->n_chunks * pl->n_slabs * B;
-        span = (total + kTargetWorkgroups - 1) / kTargetWorkgroups;
+        want = (total + kTargetWorkgroups - 1) / kTargetWorkgroups;
     }
-    if (span < 1) span = 1;
-    if (span > pl->n_chunks) span = pl->n_chunks;
-    // the workgroup's byte window (span + history rows) must stay below 2^31
-    while (span > 1 && (span * kChunk + 32 * pl->kh + kChunk) * D * eb >= kMaxWindowBytes) span = (span + 1) / 2;
-    if ((span * kChunk + 32 * pl->kh + kChunk) * D * eb >= kMaxWindowBytes) return HYENA_ERR_UNSUPPORTED;
-    pl->span = span;
-    pl->n_spans = (pl->n_chunks + span - 1) / span;
+    if (want > pl->n_chunks) want = pl->n_chunks;
+    // largest compiled span <= want whose byte window (history + span +
+    // one chunk of slack) stays below 2^31
+    int si = -1;
+    const int n_spans_compiled = dtype == HYENA_DTYPE_F32 ? kNumSpansFor<true> : kNumSpansFor<false>;
+    for (int i = 0; i < n_spans_compiled; ++i) {
+        const int64_t win = ((int64_t)kSpans[i] * kChunk + 32 * pl->kh + kChunk) * D * eb;
+        if (win >= kMaxWindowBytes) break;
+        if (i == 0 || kSpans[i] <= want) si = i;
+    }
+    if (si < 0) return HYENA_ERR_UNSUPPORTED;
+    pl->span_index = si;
+    pl->span = kSpans[si];
+    pl->n_spans = (pl->n_chunks + pl->span - 1) / pl->span;
     pl->workgroups = pl->n_spans * pl->n_slabs * B;
     if (pl->workgroups > INT32_MAX || pl->n_spans > INT32_MAX) return HYENA_ERR_UNSUPPORTED;
     return HYENA_OK;
@@ -475,10 +516,10 @@ int hyena_conv_fwd_ex(const void *q, const void *k, const void *v, const void *h
     p.D = (int32_t)D;
     p.group_size = (int32_t)group_size;
     p.l_h = (int32_t)l_h;
-    p.span = (int32_t)pl.span;
     p.n_spans = (int32_t)pl.n_spans;
     p.n_slabs = (int32_t)pl.n_slabs;
-    KernelFn fn = dtype == HYENA_DTYPE_F32 ? pick_kernel<true>(pl.kh) : pick_kernel<false>(pl.kh);
+    KernelFn fn = dtype == HYENA_DTYPE_F32 ? pick_kernel<true>(pl.kh, pl.span_index)
+                                           : pick_kernel<false>(pl.kh, pl.span_index);
     hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(kThreads), 0, (hipStream_t)stream, p);
     if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
     return HYENA_OK;

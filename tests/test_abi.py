@@ -94,9 +94,10 @@ def test_binding_raises_with_status():
 
 @pytest.mark.parametrize("B,L,D,l_h,dtype,span,expect_span", [
     (1, 8192, 4096, 7, 0, 0, 16), (1, 8192, 4096, 128, 0, 0, 16),
-    (4, 32768, 4096, 128, 0, 0, 256), (1, 1024, 256, 7, 1, 0, 1),
-    (1, 1000, 64, 7, 0, 3, 3), (1, 100, 64, 7, 0, 50, 2),
-    (1, 1 << 20, 4096, 128, 0, 0, 2048),
+    (4, 32768, 4096, 128, 0, 0, 32), (1, 1024, 256, 7, 1, 0, 1),
+    (1, 1000, 64, 7, 0, 3, 2), (1, 1000, 64, 7, 0, 7, 4), (1, 100, 64, 7, 0, 50, 2),
+    (1, 1 << 20, 4096, 128, 0, 0, 32), (1, 1 << 20, 4096, 128, 1, 0, 8),
+    (1, 1 << 20, 4096, 128, 0, 1000, 32), (1, 130, 64, 7, 0, 0, 1),
 ])
 def test_plan_split(B, L, D, l_h, dtype, span, expect_span):
     s, wgs = hc.plan(B, L, D, 16, l_h, dtype, span)

@@ -69,7 +69,75 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="instead of the step, run a plain device copy of this many MiB "
                          "(reference point for the HBM byte counters)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
+                    "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE output of this bench and of "
+                         "--calibrate-copy-mib into profiles/traffic.json")
     return ap.parse_args()
+
+
+def _counter_means(d):
+    """{kernel name: mean Counter_Value} over the dispatches in a rocprofv3 --pmc output dir."""
+    import csv
+    import glob
+    sums, counts = {}, {}
+    for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = r["Kernel_Name"]
+                sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+                counts[k] = counts.get(k, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib=1024):
+    """HBM bytes per launch of each layer's kernel, scaled by a plain copy's counters.
+
+    FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  The copy of ``copy_mib``
+    MiB reads and writes exactly that many bytes; the ratio of that figure to
+    its counter readings scales the kernel's readings to bytes.
+    """
+    import re
+    copy_bytes = copy_mib << 20
+
+    def copy_reading(d):
+        m = _counter_means(d)
+        k = [n for n in m if "copyBuffer" in n or "copy" in n.lower()]
+        return max(m[n] for n in k) * 1024.0
+
+    f_scale = copy_bytes / copy_reading(copy_fetch_dir)
+    w_scale = copy_bytes / copy_reading(copy_write_dir)
+    fetch, write = _counter_means(fetch_dir), _counter_means(write_dir)
+    layers = {}
+    for name, kib in fetch.items():
+        m = re.search(r"hyena_fwd_kernel<false, (\d+), (\d+), (\d+)>", name)
+        if not m:
+            continue
+        kh = int(m.group(1))
+        layer = {1: "se", 4: "mr"}.get(kh)
+        if layer is None:
+            continue
+        fb = kib * 1024.0 * f_scale
+        wb = write.get(name, float("nan")) * 1024.0 * w_scale
+        layers[layer] = {"kernel": name.split("(")[0].strip(), "fetch_bytes": round(fb),
+                         "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb),
+                         "fetch_counter_KiB": round(kib, 1),
+                         "write_counter_KiB": round(write.get(name, float("nan")), 1)}
+    out = {"kernel_source_sha256": source_digest(),
+           "scale": {"fetch": round(f_scale, 4), "write": round(w_scale, 4),
+                     "copy_bytes": copy_bytes},
+           "layers": layers,
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- "
+               "python3 bench.py --steps 8 --warmup 2 --skip-cpu-baseline --skip-naive",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- "
+               "python3 bench.py --steps 8 --warmup 2 --skip-cpu-baseline --skip-naive",
+               "rocprofv3 --pmc FETCH_SIZE ... -- python3 bench.py --calibrate-copy-mib %d" % copy_mib,
+               "rocprofv3 --pmc WRITE_SIZE ... -- python3 bench.py --calibrate-copy-mib %d" % copy_mib]}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def calibrate_copy(mib: int, reps: int = 10):
@@ -112,6 +180,9 @@ def main():
 
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
 
     import torch
@@ -164,8 +235,10 @@ def main():
     t0 = time.perf_counter()
     for i in range(K):
         step(i, ev[i])
+    t_issued = time.perf_counter()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    host_issue_us = (t_issued - t0) * 1e6 / K
     ms_per_step = wall * 1e3 / K
 
     elems_step = sum(w.elems for w in layers)
@@ -207,6 +280,7 @@ def main():
             for w in layers)), "l_b": 64, "input_sets_rotated": len(sets[0])},
         "roofline": roofline,
         "layers": layer_stats,
+        "host_issue_us_per_step": round(host_issue_us, 2),
     }
 
     # ---- naive baseline: torch depthwise conv1d ---------------------------

@@ -18,6 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhyena_conv.so")
 
 BLOCK_LEN = 64
+SLAB = 128  # channels per workgroup of the library's kernels
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 
@@ -102,31 +103,39 @@ def conv_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Tensor,
     q, k, v: [B, L, D] contiguous device tensors (bf16 or fp32, all alike);
     h: [D // group_size, l_h] of the same dtype.  Returns ``out`` ([B, L, D]).
     """
+    dt = q.dtype
+    dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("h", h)):
-        if not t.is_cuda:
-            raise ValueError("%s must be a GPU tensor" % name)
+        if t.dtype != dt:
+            raise TypeError("%s has dtype %s, q has %s" % (name, t.dtype, dt))
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError("%s must be a tensor on q's GPU" % name)
         if not t.is_contiguous():
             raise ValueError("%s must be contiguous" % name)
-        if t.dtype != q.dtype:
-            raise TypeError("%s has dtype %s, q has %s" % (name, t.dtype, q.dtype))
-    code = _dtype_code(q.dtype)
-    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape:
+    code = _dtype_code(dt)
+    shape = q.shape
+    if len(shape) != 3 or k.shape != shape or v.shape != shape:
         raise ValueError("q, k, v must share one [B, L, D] shape")
     if h.dim() != 2:
         raise ValueError("h must be [D // group_size, l_h]")
-    B, L, D = q.shape
-    if group_size < 1 or D % group_size != 0 or h.shape[0] != D // group_size:
-        raise ValueError("h has %d filters; D=%d, group_size=%d" % (h.shape[0], D, group_size))
+    B, L, D = shape
+    G, l_h = h.shape
+    if group_size < 1 or D % group_size != 0 or G != D // group_size:
+        raise ValueError("h has %d filters; D=%d, group_size=%d" % (G, D, group_size))
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or not out.is_cuda:
-        raise ValueError("out must be a contiguous GPU tensor like q")
+    elif out.shape != shape or out.dtype != dt or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
     if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    with torch.cuda.device(q.device):
-        st = lib().hyena_conv_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(),
-                                     B, L, D, group_size, h.shape[1], out.data_ptr(), code,
-                                     span_chunks, stream.cuda_stream)
+        stream = torch.cuda.current_stream(dev)
+    fn = lib().hyena_conv_fwd_ex
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(), B, L, D, group_size, l_h,
+            out.data_ptr(), code, span_chunks, stream.cuda_stream)
+    if dev.index == torch.cuda.current_device():
+        st = fn(*args)
+    else:
+        with torch.cuda.device(dev):
+            st = fn(*args)
     if st != 0:
         raise HyenaError(st, "hyena_conv_fwd_ex")
     return out

@@ -53,9 +53,12 @@
 
 namespace {
 
+#ifndef HYENA_WAVES
+#define HYENA_WAVES 8
+#endif
 constexpr int kChunk = 64;               // l_b: rows per chunk
 constexpr int kTile = 16;                // channels per wave (MFMA M)
-constexpr int kWaves = 4;                // waves per workgroup
+constexpr int kWaves = HYENA_WAVES;      // waves per workgroup
 constexpr int kSlab = kTile * kWaves;    // channels per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxTaps = 2 * kChunk;     // l_h <= 2 l_b
@@ -106,6 +109,7 @@ template <> struct Tr<false> {           // bf16 I/O
     // XOR swizzle of the 16-byte segment index by row (conflict-free
     // time-major reads of 16 channels x 4 row groups).
     __device__ static int swz(int row) { return ((row >> 3) & 3) << 1; }
+    static_assert(NLD * RPL == kChunk, "loads must tile the chunk");
 };
 template <> struct Tr<true> {            // fp32 I/O
     static constexpr int EB = 4;
@@ -115,6 +119,7 @@ template <> struct Tr<true> {            // fp32 I/O
     static constexpr int RPL = kThreads / TPR;       // 16
     static constexpr int NLD = kChunk / RPL;         // 4
     __device__ static int swz(int row) { return (row & 3) << 2; }
+    static_assert(NLD * RPL == kChunk, "loads must tile the chunk");
 };
 
 // Kernel: F32 selects the element type, KH the 32-row history steps
@@ -410,8 +415,6 @@ KernelFn pick_kernel(int kh, int si) {
     }
 }
 
-// Workgroups the automatic split aims for: 256 CUs x 2 resident workgroups.
-constexpr int64_t kTargetWorkgroups = 512;
 constexpr int64_t kMaxWindowBytes = (int64_t)1 << 31;
 
 struct Plan {
@@ -440,11 +443,12 @@ int make_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, 
     pl->n_slabs = (D + kSlab - 1) / kSlab;
     if (group_size % kTile != 0) return HYENA_ERR_UNSUPPORTED;
     if (D > INT32_MAX / 16) return HYENA_ERR_UNSUPPORTED;
+    // Default span: long enough that the 32*KH history rows a workgroup
+    // re-reads stay a small share of its rows (2*KH chunks: 1/4 at most),
+    // short enough that many workgroups balance the CUs.  Measured on
+    // MI355X at B=1, L=8192, D=4096: SE best at 2 chunks, MR at 8.
     int64_t want = span_req;
-    if (want <= 0) {
-        const int64_t total = pl->n_chunks * pl->n_slabs * B;
-        want = (total + kTargetWorkgroups - 1) / kTargetWorkgroups;
-    }
+    if (want <= 0) want = pl->kh <= 1 ? 2 : 2 * pl->kh;
     if (want > pl->n_chunks) want = pl->n_chunks;
     // largest compiled span <= want whose byte window (history + span +
     // one chunk of slack) stays below 2^31

@@ -283,6 +283,9 @@ def main():
         "host_issue_us_per_step": round(host_issue_us, 2),
     }
 
+    # ---- attainable streaming rate on this GPU (same bytes, no convolution)
+    out["stream_reference"] = stream_reference(layers[-1], sets[-1], stream, max(10, K // 4))
+
     # ---- naive baseline: torch depthwise conv1d ---------------------------
     if not args.skip_naive:
         out["naive_conv1d"] = naive_conv1d(layers, sets, stream, max(5, K // 10))
@@ -293,6 +296,35 @@ def main():
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def stream_reference(w, per, stream, reps):
+    """What plain streaming kernels reach on the same tensors and rotation.
+
+    torch.addcmul(q, k, v, out=y) reads three [B, L, D] tensors and writes one
+    (the operator's 8 bytes per token*channel in one fused elementwise kernel);
+    a device copy reads one and writes one.  Timed with HIP events around
+    ``reps`` back-to-back launches.
+    """
+    import torch
+    res = {}
+    for name, fn, nbytes in (
+            ("addcmul_read3_write1", lambda s: torch.addcmul(s[0], s[1], s[2], out=s[4]), 4),
+            ("copy_read1_write1", lambda s: s[4].copy_(s[0]), 2)):
+        for i in range(3):
+            fn(per[i % len(per)])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(per[i % len(per)])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        moved = w.elems * (2 if w.dtype == "bf16" else 4) * nbytes
+        res[name] = {"us": round(us, 2), "GBs": round(moved / (us * 1e-6) / 1e9, 1),
+                     "frac_of_peak": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    return res
 
 
 def naive_conv1d(layers, sets, stream, reps):

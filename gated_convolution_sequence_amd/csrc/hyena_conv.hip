@@ -65,6 +65,16 @@ constexpr int kMaxTaps = 2 * kChunk;     // l_h <= 2 l_b
 constexpr int kHOff = 64;                // filter staging: index = tap + kHOff
 constexpr int kHLen = 256;               // staged taps per wave: [-64, 192)
 constexpr uint32_t kOOB = 0x80000000u;   // a buffer offset past every range
+#ifndef HYENA_LOAD_POLICY
+#define HYENA_LOAD_POLICY 2
+#endif
+#ifndef HYENA_STORE_POLICY
+#define HYENA_STORE_POLICY 2
+#endif
+// Cache-policy bits of the streaming buffer loads and stores (gfx950: 1 = sc0,
+// 2 = nt, 16 = sc1).
+constexpr int kLoadPolicy = HYENA_LOAD_POLICY;
+constexpr int kStorePolicy = HYENA_STORE_POLICY;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -122,16 +132,44 @@ template <> struct Tr<true> {            // fp32 I/O
     static_assert(NLD * RPL == kChunk, "loads must tile the chunk");
 };
 
+// Matrix-core step of each element type: the MFMA operand fragment, the input
+// rows one fragment covers (the MFMA K) and the fragments per 64-row chunk.
+template <bool F32> struct Mma;
+template <> struct Mma<false> {
+    typedef bf16x8_t frag;               // v_mfma_f32_16x16x32_bf16: 8 rows per lane
+    static constexpr int ROWS = 32;
+    static constexpr int FPC = kChunk / ROWS;
+};
+template <> struct Mma<true> {
+    typedef float frag;                  // v_mfma_f32_16x16x4_f32: 1 row per lane
+    static constexpr int ROWS = 4;
+    static constexpr int FPC = kChunk / ROWS;
+};
+
 // Kernel: F32 selects the element type, KH the 32-row history steps
 // (KH = ceil((l_h - 1) / 32)), PF the chunks of k, v and q kept in flight,
 // S the chunks of one span.  The walk over the span is fully unrolled: the
 // prefetched registers are then never loop-carried, so the compiler's
 // memory-counter waits are exact and no in-flight load is copied.
+//
+// Walk order.  A span first ingests its own S chunks.  The first ND chunks
+// need rows from before the span (the history); their operand fragments are
+// kept and their outputs deferred.  The history rows are ingested last: at
+// that time the workgroup of the preceding span (same slab, same XCD under
+// the round-robin dispatch, launched together) is reading the same rows as
+// its own last chunks, so they come from L2 instead of HBM.  Then the
+// deferred chunks are computed.
 template <bool F32, int KH, int PF, int S>
 __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     using T = Tr<F32>;
+    using M = Mma<F32>;
+    using frag = typename M::frag;
     constexpr int HROWS = 32 * KH;                        // history rows before a span
-    constexpr int C0 = -((HROWS + kChunk - 1) / kChunk);  // first (history) chunk
+    constexpr int H = (HROWS + kChunk - 1) / kChunk;      // history chunks
+    constexpr int ND = (KH + 1) / 2 < S ? (KH + 1) / 2 : S;  // deferred chunks
+    constexpr int NI = S + H;                             // ingested chunks
+    constexpr int NH = HROWS / M::ROWS;                   // history fragments
+    constexpr int NX = NH + M::FPC;                       // fragments one chunk reads
     constexpr int ST_PITCH = kSlab * 4;                   // fp32 staging row, bytes
 
     // x = k*v of the current chunk (row-major, swizzled), the fp32
@@ -189,33 +227,50 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     }
 
     // ---- cooperative row-major access: thread -> (row, 16-byte segment) ----
-    // q, k, v and y all use it: 16 bytes per lane, whole 128/256-byte rows.
+    // q, k, v and y all use it: 16 bytes per lane, whole 256-byte rows.
     const int ld_row = tid / T::TPR;
     const int ld_seg = tid % T::TPR;
     const bool seg_ok = c_begin + ld_seg * T::VEC < p.D;
     const int ld_base = ld_row * row_bytes + ld_seg * 16;
-    // Offsets of chunk c, load i; chunks past the span fall outside the byte
-    // window (no traffic, no store), and history chunks (c < 0) never touch q
-    // or y.
+    // Offset of chunk c (relative to the span start), load i.  Rows past the
+    // span or before the history fall outside the byte window (no traffic,
+    // no store); `need` = false sends the access outside it too.
     auto io_off = [&](int c, int i, bool need) -> uint32_t {
         const int r = (row0 + c * kChunk + i * T::RPL) * row_bytes + ld_base;
         return (seg_ok && need) ? (uint32_t)r : kOOB;
     };
+    // chunk of ingest item i: the span's chunks, then the history chunks
+    auto item_chunk = [](int i) -> int { return i < S ? i : -H + (i - S); };
+    // chunk of compute item j: the non-deferred chunks, then the deferred ones
+    auto comp_chunk = [](int j) -> int { return j < S - ND ? ND + j : j - (S - ND); };
 
     u32x4_t kr[PF][T::NLD], vr[PF][T::NLD], qr[PF][T::NLD];
 
-    auto load_kv = [&](int c, u32x4_t *kd, u32x4_t *vd) {
+    // The last H chunks of a span are the next span's history: they are
+    // loaded with the default (L2-allocating) policy so that the neighbour's
+    // history read hits; every other row is read once and streams past L2.
+    auto load_kv = [&](int item, u32x4_t *kd, u32x4_t *vd) {
+        const bool need = item < NI;
+        const int c = need ? item_chunk(item) : S;
+        const bool keep = need && item < S && item >= S - H;
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
-            const uint32_t o = io_off(c, i, true);
-            kd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
-            vd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+            const uint32_t o = io_off(c, i, need);
+            if (keep) {
+                kd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+                vd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+            } else {
+                kd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadPolicy));
+                vd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kLoadPolicy));
+            }
         }
     };
-    auto load_q = [&](int c, u32x4_t *qd) {
+    auto load_q = [&](int j, u32x4_t *qd) {
+        const bool need = j < S;
+        const int c = need ? comp_chunk(j) : S;
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i)
-            qd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, io_off(c, i, c >= 0), 0, 0));
+            qd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, io_off(c, i, need), 0, kLoadPolicy));
     };
     // x = k*v for this thread's rows -> xs.
     auto store_x = [&](const u32x4_t *kd, const u32x4_t *vd) {
@@ -240,8 +295,85 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     // (row & 15), so 16 lanes writing one segment column of 16 rows, and the
     // row-major readers, hit distinct banks.
     auto st_addr = [&](int row, int seg) -> int { return row * ST_PITCH + ((seg ^ (row & 15)) << 4); };
-    // Epilogue: y = q * acc for this thread's rows, coalesced 16-byte stores.
-    auto epilogue = [&](int c, u32x4_t *qd) {
+
+    // Prologue: the first PF ingest items and the first PF compute items in
+    // flight.  Each ingest then refills its slot with the item PF ahead, and
+    // each compute the q slot with the compute item PF ahead.
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+        load_kv(s, kr[s], vr[s]);
+        load_q(s, qr[s]);
+    }
+
+    __syncthreads();  // filters staged
+
+    // ---- Toeplitz operand fragments and the time-major operand read --------
+    // B = H^T: lane (n16 = output time within a 16-row tile, q4 = input-row
+    // group), element j = input row.  The operand of output tile nt and input
+    // step kappa depends only on their distance: bf16 e = nt - 2 kappa (units
+    // of 16 rows), fp32 e4 = 4 nt - kappa (units of 4 rows).
+    constexpr int NE = F32 ? 16 + NH : 4 + 2 * KH;
+    frag F[NE];
+    const int ch = w * kTile + n16;
+    int rd_base;
+    if constexpr (F32) {
+#pragma unroll
+        for (int i = 0; i < NE; ++i) F[i] = hs[w][4 * (i - 3) + n16 - q4 + kHOff];
+        rd_base = q4 * T::PITCH + ((((ch >> 2) ^ (4 * q4))) << 4) + ((ch & 3) << 2);
+    } else {
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) F[e][j] = (__bf16)hs[w][16 * e + n16 - 8 * q4 - j + kHOff];
+        // channel 16w + n16, rows 8 q4 + j (+ 32 kappa); their swizzle is 2 q4
+        rd_base = (8 * q4) * T::PITCH + ((((ch >> 3) ^ (2 * q4))) << 4) + ((ch & 7) << 1);
+    }
+    // This chunk's FPC operand fragments from xs (A = X^T: lane n16 = channel).
+    auto read_frags = [&](frag *dst) {
+        if constexpr (F32) {
+#pragma unroll
+            for (int s4 = 0; s4 < M::FPC; ++s4)
+                dst[s4] = *(const float *)(&xs[rd_base + (4 * s4) * T::PITCH]);
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < M::FPC; ++kk)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    dst[kk][j] = __builtin_bit_cast(__bf16, *(const uint16_t *)(&xs[rd_base + (32 * kk + j) * T::PITCH]));
+        }
+    };
+    // ingest item i: k*v -> xs, refill its slot, and read its fragments
+    auto ingest = [&](int i, frag *dst) {
+        store_x(kr[i % PF], vr[i % PF]);
+        load_kv(i + PF, kr[i % PF], vr[i % PF]);
+        __syncthreads();
+        read_frags(dst);
+    };
+    // compute item j (chunk c) from its NX fragments Xc (history first)
+    auto compute = [&](int j, const frag *Xc) {
+        const int c = comp_chunk(j);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < NX; ++kk) {
+                if constexpr (F32) {
+                    const int e4 = 4 * nt - (kk - NH);
+                    if (e4 < -3 || e4 + 3 >= NE) continue;
+                    if (4 * e4 - 3 >= p.l_h) continue;  // every tap past the filter
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Xc[kk], F[e4 + 3], acc, 0, 0, 0);
+                } else {
+                    const int e = nt - 2 * (kk - NH);
+                    if (e < 0) continue;  // strictly above the diagonal: all zero
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Xc[kk], F[e], acc, 0, 0, 0);
+                }
+            }
+            // lane holds output time 16 nt + n16, channels 4 q4 .. 4 q4 + 3
+            *(f32x4_t *)(&st[st_addr(16 * nt + n16, 4 * w + q4)]) = acc;
+        }
+        __syncthreads();
+        // epilogue: y = q * acc for this thread's rows, 16-byte stores
+        u32x4_t *qd = qr[j % PF];
         u32x4_t yv[T::NLD];
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
@@ -260,124 +392,53 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
             }
         }
         // refill q before storing y, so y never shares registers with q
-        load_q(c + PF, qd);
+        load_q(j + PF, qd);
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i)
-            __builtin_amdgcn_raw_buffer_store_b128(yv[i], ry, io_off(c, i, c >= 0), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(yv[i], ry, io_off(c, i, true), 0, kStorePolicy);
     };
 
-    // Prologue: the first PF chunks in flight.  Each step then consumes the
-    // oldest slot and refills it with the chunk PF ahead.
+    // ---- phase 1: the span's own chunks ------------------------------------
+    // X holds the NX fragments chunk c reads: NH history fragments, then its
+    // own FPC.  Chunks before ND keep their fragments for phase 3.
+    frag X[NX];
+    frag Xsave[ND * M::FPC > 0 ? ND * M::FPC : 1];
 #pragma unroll
-    for (int s = 0; s < PF; ++s) {
-        load_kv(C0 + s, kr[s], vr[s]);
-        load_q(C0 + s, qr[s]);
+    for (int c = 0; c < S; ++c) {
+        ingest(c, &X[NH]);
+        if (c >= ND) {
+            compute(c - ND, X);
+        } else {
+#pragma unroll
+            for (int f = 0; f < M::FPC; ++f) Xsave[c * M::FPC + f] = X[NH + f];
+            __syncthreads();  // xs is rewritten by the next ingest
+        }
+#pragma unroll
+        for (int i = 0; i < NH; ++i) X[i] = X[i + M::FPC];
     }
-
-    __syncthreads();  // filters staged
-
-    if constexpr (!F32) {
-        // ================= bf16: v_mfma_f32_16x16x32_bf16 ==================
-        constexpr int NE = 4 + 2 * KH;  // Toeplitz fragments, e = 0 .. 3 + 2 KH
-        constexpr int NX = KH + 2;      // X^T fragments, kappa = -KH .. 1
-        bf16x8_t F[NE];
+    if constexpr (ND > 0) {
+        // ---- phase 2: the history rows before the span ---------------------
+        frag Hst[H * M::FPC];
 #pragma unroll
-        for (int e = 0; e < NE; ++e) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                // B = H^T: row k = 8 q4 + j (input time), column n16 (output time)
-                const int tap = 16 * e + n16 - 8 * q4 - j;
-                F[e][j] = (__bf16)hs[w][tap + kHOff];
-            }
+        for (int i = S; i < NI; ++i) {
+            ingest(i, &Hst[(i - S) * M::FPC]);
+            __syncthreads();  // xs is rewritten by the next ingest
         }
-        bf16x8_t X[NX];
+        // ---- phase 3: the deferred chunks ----------------------------------
+        // fragment g (input step relative to the span start) of chunk c's
+        // window: history if g < 0 (Hst ends at step -1), else saved
+        constexpr int HF = H * M::FPC;
 #pragma unroll
-        for (int i = 0; i < NX; ++i)
+        for (int c = 0; c < ND; ++c) {
+            if (c > 0) __syncthreads();  // st is rewritten by this compute
+            frag Xc[NX];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) X[i][j] = (__bf16)0.0f;
-
-        // Time-major LDS read address of this lane: channel 16w + n16, rows
-        // 8 q4 + j (+ 32 kappa); the swizzle of those rows is 2 q4.
-        const int ch = w * kTile + n16;
-        const int rd_base = (8 * q4) * T::PITCH + ((((ch >> 3) ^ (2 * q4))) << 4) + ((ch & 7) << 1);
-
-        auto step = [&](int c, u32x4_t *kd, u32x4_t *vd, u32x4_t *qd) {
-            store_x(kd, vd);
-            load_kv(c + PF, kd, vd);
-            __syncthreads();
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint16_t raw = *(const uint16_t *)(&xs[rd_base + (32 * kk + j) * T::PITCH]);
-                    X[KH + kk][j] = __builtin_bit_cast(__bf16, raw);
-                }
+            for (int kk = 0; kk < NX; ++kk) {
+                const int g = c * M::FPC + kk - NH;
+                Xc[kk] = g < 0 ? Hst[HF + g] : Xsave[g];
             }
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int kk = 0; kk < NX; ++kk) {
-                    const int e = nt - 2 * (kk - KH);
-                    if (e < 0) continue;  // strictly above the diagonal: all zero
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(X[kk], F[e], acc, 0, 0, 0);
-                }
-                // lane holds output time 16 nt + n16, channels 4 q4 .. 4 q4 + 3
-                *(f32x4_t *)(&st[st_addr(16 * nt + n16, 4 * w + q4)]) = acc;
-            }
-            __syncthreads();
-            epilogue(c, qd);
-#pragma unroll
-            for (int i = 0; i < KH; ++i) X[i] = X[i + 2];
-        };
-        // Chunks past t_stop (a short last span) run on zeros and store
-        // nothing: their rows are outside the byte window.
-#pragma unroll
-        for (int c = C0; c < S; ++c) step(c, kr[(c - C0) % PF], vr[(c - C0) % PF], qr[(c - C0) % PF]);
-    } else {
-        // ================= fp32: v_mfma_f32_16x16x4_f32 ====================
-        constexpr int H4 = HROWS / 4;   // history steps of 4 rows
-        constexpr int NX = H4 + 16;     // kappa4 = -H4 .. 15
-        constexpr int NE = 16 + H4;     // e4 = -3 .. 12 + H4
-        float F[NE];
-#pragma unroll
-        for (int i = 0; i < NE; ++i) {
-            const int e4 = i - 3;
-            // B = H^T: row k = q4 (input time), column n16 (output time)
-            F[i] = hs[w][4 * e4 + n16 - q4 + kHOff];
+            compute(S - ND + c, Xc);
         }
-        float X[NX];
-#pragma unroll
-        for (int i = 0; i < NX; ++i) X[i] = 0.0f;
-        const int ch = w * kTile + n16;
-        const int rd_base = q4 * T::PITCH + ((((ch >> 2) ^ (4 * q4))) << 4) + ((ch & 3) << 2);
-
-        auto step = [&](int c, u32x4_t *kd, u32x4_t *vd, u32x4_t *qd) {
-            store_x(kd, vd);
-            load_kv(c + PF, kd, vd);
-            __syncthreads();
-#pragma unroll
-            for (int s4 = 0; s4 < 16; ++s4)
-                X[H4 + s4] = *(const float *)(&xs[rd_base + (4 * s4) * T::PITCH]);
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int kk = 0; kk < NX; ++kk) {
-                    const int e4 = 4 * nt - (kk - H4);
-                    if (e4 < -3 || e4 + 3 >= NE) continue;
-                    if (4 * e4 - 3 >= p.l_h) continue;  // every tap past the filter
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[kk], F[e4 + 3], acc, 0, 0, 0);
-                }
-                *(f32x4_t *)(&st[st_addr(16 * nt + n16, 4 * w + q4)]) = acc;
-            }
-            __syncthreads();
-            epilogue(c, qd);
-#pragma unroll
-            for (int i = 0; i < H4; ++i) X[i] = X[i + 16];
-        };
-#pragma unroll
-        for (int c = C0; c < S; ++c) step(c, kr[(c - C0) % PF], vr[(c - C0) % PF], qr[(c - C0) % PF]);
     }
 }
 
@@ -388,10 +449,10 @@ typedef void (*KernelFn)(Params);
 template <bool F32> constexpr int kPrefetch = F32 ? 2 : 3;
 
 // Spans (chunks per workgroup) with a compiled kernel; a requested span is
-// rounded down to one of these.  fp32 stops at 8 (register budget).
+// rounded down to one of these.  fp32 stops at 4 (register budget).
 constexpr int kSpans[] = {1, 2, 4, 8, 16, 32};
 constexpr int kNumSpans = sizeof(kSpans) / sizeof(kSpans[0]);
-template <bool F32> constexpr int kNumSpansFor = F32 ? 4 : kNumSpans;
+template <bool F32> constexpr int kNumSpansFor = F32 ? 3 : kNumSpans;
 
 template <bool F32, int KH, int... Ss>
 KernelFn span_table_entry(int si, std::integer_sequence<int, Ss...>) {

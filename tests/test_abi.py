@@ -96,8 +96,8 @@ def test_binding_raises_with_status():
     (1, 8192, 4096, 7, 0, 0, 2), (1, 8192, 4096, 128, 0, 0, 8),
     (4, 32768, 4096, 128, 0, 0, 8), (1, 1024, 256, 7, 1, 0, 2),
     (1, 1000, 64, 7, 0, 3, 2), (1, 1000, 64, 7, 0, 7, 4), (1, 100, 64, 7, 0, 50, 2),
-    (1, 1 << 20, 4096, 128, 0, 0, 8), (1, 1 << 20, 4096, 128, 1, 0, 8),
-    (1, 1 << 20, 4096, 128, 0, 1000, 32), (1, 1 << 20, 4096, 128, 1, 1000, 8),
+    (1, 1 << 20, 4096, 128, 0, 0, 8), (1, 1 << 20, 4096, 128, 1, 0, 4),
+    (1, 1 << 20, 4096, 128, 0, 1000, 32), (1, 1 << 20, 4096, 128, 1, 1000, 4),
     (1, 130, 64, 7, 0, 0, 2), (1, 60, 64, 128, 0, 0, 1), (1, 8192, 4096, 66, 0, 0, 4),
     (1, 8192, 4096, 1, 0, 0, 2),
 ])

@@ -215,13 +215,15 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(i, events=None):
+        # events[0] before the first layer, events[li + 1] after layer li:
+        # one timestamp per kernel boundary
+        if events is not None:
+            events[0].record(stream)
         for li, w in enumerate(layers):
             q, k, v, h, y = sets[li][i % len(sets[li])]
-            if events is not None:
-                events[li][0].record(stream)
             hc.conv_fwd(q, k, v, h, w.group_size, out=y, stream=stream)
             if events is not None:
-                events[li][1].record(stream)
+                events[li + 1].record(stream)
 
     for i in range(args.warmup):
         step(i)
@@ -229,8 +231,7 @@ def main():
 
     # ---- timed region: exactly K steps ------------------------------------
     K = args.steps
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-           for _ in layers] for _ in range(K)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(layers) + 1)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -246,7 +247,7 @@ def main():
 
     layer_stats = {}
     for li, w in enumerate(layers):
-        ms = [ev[i][li][0].elapsed_time(ev[i][li][1]) for i in range(K)]
+        ms = [ev[i][li].elapsed_time(ev[i][li + 1]) for i in range(K)]
         mean_ms = sum(ms) / len(ms)
         alg_bytes = w.elems * (4 * (2 if w.dtype == "bf16" else 4))
         achieved = alg_bytes / (mean_ms * 1e-3) / 1e9

@@ -29,8 +29,8 @@ STATUS = {
 }
 
 # Every symbol include/hyena_conv.h declares.
-EXPORTS = ("hyena_conv_fwd", "hyena_conv_fwd_f32", "hyena_conv_fwd_ex", "hyena_conv_plan",
-           "hyena_conv_strerror", "hyena_conv_block_len")
+EXPORTS = ("hyena_conv_fwd", "hyena_conv_fwd_f32", "hyena_conv_fwd_ex", "hyena_conv_fwd_halo",
+           "hyena_conv_plan", "hyena_conv_strerror", "hyena_conv_block_len")
 
 
 class HyenaError(RuntimeError):
@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
         L.hyena_conv_fwd_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp,
                                         ctypes.c_int, i64, vp]
         L.hyena_conv_fwd_ex.restype = ctypes.c_int
+        L.hyena_conv_fwd_halo.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                          vp, ctypes.c_int, i64, vp]
+        L.hyena_conv_fwd_halo.restype = ctypes.c_int
         L.hyena_conv_plan.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, i64,
                                       ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.hyena_conv_plan.restype = ctypes.c_int
@@ -97,11 +100,14 @@ def _dtype_code(t: torch.dtype) -> int:
 
 def conv_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Tensor,
              group_size: int, out: Optional[torch.Tensor] = None, span_chunks: int = 0,
-             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+             stream: Optional[torch.cuda.Stream] = None, k_prev: Optional[torch.Tensor] = None,
+             v_prev: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = q (.) (h * (k (.) v)) on the GPU, enqueued on ``stream`` (default: current).
 
     q, k, v: [B, L, D] contiguous device tensors (bf16 or fp32, all alike);
     h: [D // group_size, l_h] of the same dtype.  Returns ``out`` ([B, L, D]).
+    k_prev, v_prev ([B, P, D]): the rows that precede row 0 (a shard of a
+    longer sequence); without them the history before row 0 is zero.
     """
     dt = q.dtype
     dev = q.device
@@ -122,20 +128,36 @@ def conv_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Tensor,
     G, l_h = h.shape
     if group_size < 1 or D % group_size != 0 or G != D // group_size:
         raise ValueError("h has %d filters; D=%d, group_size=%d" % (G, D, group_size))
+    P = 0
+    if (k_prev is None) != (v_prev is None):
+        raise ValueError("pass both k_prev and v_prev, or neither")
+    if k_prev is not None:
+        for name, t in (("k_prev", k_prev), ("v_prev", v_prev)):
+            if t.dtype != dt or t.device != dev or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous tensor like q" % name)
+            if t.dim() != 3 or t.shape[0] != B or t.shape[2] != D or t.shape != k_prev.shape:
+                raise ValueError("%s must be [B, P, D]" % name)
+        P = k_prev.shape[1]
     if out is None:
         out = torch.empty_like(q)
     elif out.shape != shape or out.dtype != dt or out.device != dev or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    fn = lib().hyena_conv_fwd_ex
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(), B, L, D, group_size, l_h,
-            out.data_ptr(), code, span_chunks, stream.cuda_stream)
+    if P == 0:
+        fn = lib().hyena_conv_fwd_ex
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(), B, L, D, group_size, l_h,
+                out.data_ptr(), code, span_chunks, stream.cuda_stream)
+    else:
+        fn = lib().hyena_conv_fwd_halo
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(), k_prev.data_ptr(),
+                v_prev.data_ptr(), P, B, L, D, group_size, l_h, out.data_ptr(), code,
+                span_chunks, stream.cuda_stream)
     if dev.index == torch.cuda.current_device():
         st = fn(*args)
     else:
         with torch.cuda.device(dev):
             st = fn(*args)
     if st != 0:
-        raise HyenaError(st, "hyena_conv_fwd_ex")
+        raise HyenaError(st, fn.__name__)
     return out

@@ -85,12 +85,14 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 struct Params {
     const void *q, *k, *v, *h;
     void *y;
+    const void *kp, *vp; // rows before row 0 of each batch row ([B, P, D]), or null
     int64_t L;          // rows per batch
     int32_t D;          // channels (row pitch, elements)
     int32_t group_size;
     int32_t l_h;
     int32_t n_spans;    // spans per batch row
-    int32_t n_slabs;    // 64-channel slabs
+    int32_t n_slabs;    // channel slabs
+    int32_t P;          // prefix rows in kp / vp (0: the history before row 0 is zero)
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -208,6 +210,13 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + base_off, nrec);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc((char *)p.y + base_off, nrec);
     const int row0 = (int)(t_begin - base_row);       // window row of chunk 0
+    // The caller's prefix rows (the P rows before row 0 of batch row b), read
+    // instead of zeros by history chunks that lie before row 0.  With P = 0
+    // the window is empty and every such read returns zero.
+    const size_t pre_off = (size_t)b * (size_t)p.P * (size_t)row_bytes + (size_t)c_begin * T::EB;
+    const uint32_t nrec_p = p.P > 0 ? (uint32_t)(p.P * row_bytes - c_begin * T::EB) : 0u;
+    const __amdgpu_buffer_rsrc_t rkp = make_rsrc(p.P > 0 ? (const char *)p.kp + pre_off : (const char *)p.k, nrec_p);
+    const __amdgpu_buffer_rsrc_t rvp = make_rsrc(p.P > 0 ? (const char *)p.vp + pre_off : (const char *)p.v, nrec_p);
 
     // ---- stage this wave's filter (zero outside [0, l_h)) -----------------
     const bool tile_ok = c_begin + w * kTile < p.D;
@@ -253,15 +262,23 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
         const bool need = item < NI;
         const int c = need ? item_chunk(item) : S;
         const bool keep = need && item < S && item >= S - H;
+        // a chunk lies wholly before or wholly after row 0 (spans start on
+        // chunk boundaries); before it, read the prefix rows P + t
+        const int64_t t0c = t_begin + (int64_t)c * kChunk;
+        const bool pre = t0c < 0;
+        const __amdgpu_buffer_rsrc_t sk = pre ? rkp : rk;
+        const __amdgpu_buffer_rsrc_t sv = pre ? rvp : rv;
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
-            const uint32_t o = io_off(c, i, need);
+            const int rp = (int)(p.P + t0c) + i * T::RPL;
+            const uint32_t o = pre ? (seg_ok ? (uint32_t)(rp * row_bytes + ld_base) : kOOB)
+                                   : io_off(c, i, need);
             if (keep) {
-                kd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
-                vd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+                kd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sk, o, 0, 0));
+                vd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sv, o, 0, 0));
             } else {
-                kd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadPolicy));
-                vd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kLoadPolicy));
+                kd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sk, o, 0, kLoadPolicy));
+                vd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(sv, o, 0, kLoadPolicy));
             }
         }
     };
@@ -555,15 +572,19 @@ int hyena_conv_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t
     return HYENA_OK;
 }
 
-int hyena_conv_fwd_ex(const void *q, const void *k, const void *v, const void *h, int64_t B,
-                      int64_t L, int64_t D, int64_t group_size, int64_t l_h, void *out, int dtype,
-                      int64_t span_chunks, void *stream) {
+// Shared by every forward entry point: host checks, plan, launch.
+static int fwd_launch(const void *q, const void *k, const void *v, const void *h, const void *kp,
+                      const void *vp, int64_t P, int64_t B, int64_t L, int64_t D, int64_t group_size,
+                      int64_t l_h, void *out, int dtype, int64_t span_chunks, void *stream) {
     int st = check_sizes(B, L, D, group_size, l_h, dtype);
     if (st != HYENA_OK) return st;
+    if (P < 0) return HYENA_ERR_SHAPE;
     if (B == 0 || L == 0 || D == 0) return HYENA_OK;
     if (!q || !k || !v || !h || !out) return HYENA_ERR_NULL;
+    if (P > 0 && (!kp || !vp)) return HYENA_ERR_NULL;
     const size_t eb = dtype == HYENA_DTYPE_F32 ? 4 : 2;
-    const uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out;
+    uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out;
+    if (P > 0) mis |= (uintptr_t)kp | (uintptr_t)vp;
     if (mis & 15u) return HYENA_ERR_ALIGN;
     if ((uintptr_t)h & (eb - 1)) return HYENA_ERR_ALIGN;
     const size_t nbytes = (size_t)B * (size_t)L * (size_t)D * eb;
@@ -571,23 +592,46 @@ int hyena_conv_fwd_ex(const void *q, const void *k, const void *v, const void *h
     if (overlaps(out, nbytes, q, nbytes) || overlaps(out, nbytes, k, nbytes) ||
         overlaps(out, nbytes, v, nbytes) || overlaps(out, nbytes, h, hbytes))
         return HYENA_ERR_ALIAS;
+    if (P > 0) {
+        if (P > INT32_MAX / 4 || P * D * (int64_t)eb >= kMaxWindowBytes) return HYENA_ERR_UNSUPPORTED;
+        const size_t pbytes = (size_t)B * (size_t)P * (size_t)D * eb;
+        if (overlaps(out, nbytes, kp, pbytes) || overlaps(out, nbytes, vp, pbytes)) return HYENA_ERR_ALIAS;
+    }
     Plan pl;
     st = make_plan(B, L, D, group_size, l_h, dtype, span_chunks, &pl);
     if (st != HYENA_OK) return st;
 
     Params p;
     p.q = q; p.k = k; p.v = v; p.h = h; p.y = out;
+    p.kp = P > 0 ? kp : nullptr;
+    p.vp = P > 0 ? vp : nullptr;
     p.L = L;
     p.D = (int32_t)D;
     p.group_size = (int32_t)group_size;
     p.l_h = (int32_t)l_h;
     p.n_spans = (int32_t)pl.n_spans;
     p.n_slabs = (int32_t)pl.n_slabs;
+    p.P = (int32_t)P;
     KernelFn fn = dtype == HYENA_DTYPE_F32 ? pick_kernel<true>(pl.kh, pl.span_index)
                                            : pick_kernel<false>(pl.kh, pl.span_index);
     hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(kThreads), 0, (hipStream_t)stream, p);
     if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
     return HYENA_OK;
+}
+
+int hyena_conv_fwd_ex(const void *q, const void *k, const void *v, const void *h, int64_t B,
+                      int64_t L, int64_t D, int64_t group_size, int64_t l_h, void *out, int dtype,
+                      int64_t span_chunks, void *stream) {
+    return fwd_launch(q, k, v, h, nullptr, nullptr, 0, B, L, D, group_size, l_h, out, dtype,
+                      span_chunks, stream);
+}
+
+int hyena_conv_fwd_halo(const void *q, const void *k, const void *v, const void *h,
+                        const void *k_prev, const void *v_prev, int64_t P, int64_t B, int64_t L,
+                        int64_t D, int64_t group_size, int64_t l_h, void *out, int dtype,
+                        int64_t span_chunks, void *stream) {
+    return fwd_launch(q, k, v, h, k_prev, v_prev, P, B, L, D, group_size, l_h, out, dtype,
+                      span_chunks, stream);
 }
 
 int hyena_conv_fwd(const void *q, const void *k, const void *v, const void *h, int64_t B, int64_t L,

@@ -35,7 +35,7 @@
  *
  * Ownership and asynchrony: every pointer is a DEVICE pointer owned by the
  * caller.  The library allocates no device memory and keeps no state between
- * calls except a per-process cache of device properties.  Work is enqueued on
+ * calls.  Work is enqueued on
  * `stream` (a hipStream_t; NULL means the default stream) and the call
  * returns without waiting; the result is valid once the caller synchronises
  * that stream.  Calls on distinct streams are independent.
@@ -61,7 +61,7 @@ enum hyena_status {
     HYENA_ERR_GROUP = -3,       /* group_size < 1 or D % group_size != 0 */
     HYENA_ERR_FILTER_LEN = -4,  /* l_h outside [1, 128] */
     HYENA_ERR_ALIGN = -5,       /* q, k, v or out not 16-byte aligned, h not element aligned */
-    HYENA_ERR_ALIAS = -6,       /* out overlaps q, k, v or h */
+    HYENA_ERR_ALIAS = -6,       /* out overlaps an input (q, k, v, h, k_prev, v_prev) */
     HYENA_ERR_UNSUPPORTED = -7, /* group_size not a multiple of 16, or a shape the kernel cannot address */
     HYENA_ERR_LAUNCH = -8,      /* the HIP runtime reported an error at launch */
     HYENA_ERR_DTYPE = -9        /* unknown element-type code */
@@ -93,6 +93,22 @@ int hyena_conv_fwd_ex(const void *q, const void *k, const void *v,
                       const void *h, int64_t B, int64_t L, int64_t D,
                       int64_t group_size, int64_t l_h, void *out, int dtype,
                       int64_t span_chunks, void *stream);
+
+/* Forward of one shard of a longer sequence (context parallelism, point to
+ * point): the history before row 0 of each batch row is not zero but the P
+ * rows the caller passes, k_prev and v_prev ([B, P, D], same layout, dtype
+ * and alignment as k, v; row P-1 immediately precedes row 0).  Only the last
+ * l_h - 1 of them are read; if P < l_h - 1 the rows before those are zero.
+ * P = 0 is hyena_conv_fwd_ex (k_prev, v_prev may then be NULL).  The result
+ * equals rows [P, P + L) of the forward over the concatenated sequence
+ * [prefix; q, k, v] (StripedHyena 2 explainer, page "01. overview", section
+ * 5: context parallelism with point-to-point exchange; the operator itself is
+ * the one at the top of this file).  out must not overlap k_prev or v_prev. */
+int hyena_conv_fwd_halo(const void *q, const void *k, const void *v,
+                        const void *h, const void *k_prev, const void *v_prev,
+                        int64_t P, int64_t B, int64_t L, int64_t D,
+                        int64_t group_size, int64_t l_h, void *out, int dtype,
+                        int64_t span_chunks, void *stream);
 
 /* The work split hyena_conv_fwd_ex would use: writes the chunks per
  * workgroup and the workgroup count.  Host only; runs the same argument

@@ -122,3 +122,26 @@ def test_binding_validates_tensors_on_host():
     q = torch.zeros(1, 8, 16)
     with pytest.raises(ValueError):
         hc.conv_fwd(q, q, q, torch.zeros(1, 3), 16)  # CPU tensors are refused
+
+
+def _halo(kp=P["k"] + (64 << 20), vp=P["v"] + (64 << 20), Pn=127, out=P["out"], **kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], h=P["h"], B=1, L=128, D=64, gs=16, l_h=7,
+             dtype=hc.DTYPE_BF16, span=0)
+    a.update(kw)
+    return hc.lib().hyena_conv_fwd_halo(a["q"], a["k"], a["v"], a["h"], kp, vp, Pn, a["B"], a["L"],
+                                        a["D"], a["gs"], a["l_h"], out, a["dtype"], a["span"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Pn=-1), -2), (dict(kp=None), -1), (dict(vp=None), -1),
+    (dict(kp=P["k"] + (64 << 20) + 8), -5), (dict(vp=P["v"] + (64 << 20) + 4), -5),
+    (dict(out=P["k"] + (64 << 20)), -6), (dict(out=P["v"] + (64 << 20) - 16), -6),
+    (dict(l_h=200), -4), (dict(gs=8), -7),
+])
+def test_halo_entry_validates_its_prefix_on_host(kw, code):
+    assert _halo(**kw) == code
+
+
+def test_halo_entry_without_prefix_needs_no_prefix_pointers():
+    # P = 0: same checks as the plain entry point; still rejected before launch
+    assert _halo(kp=None, vp=None, Pn=0, q=None) == -1

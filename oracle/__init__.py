@@ -9,7 +9,10 @@ The arithmetic lives in ``hyena_ref.c`` (plain C, fp64, OpenMP over output
 rows): the causal FIR definition from the page "04. hardware-aware convolution
 kernels" (StripedHyena 2 explainer), section 1, first equation, gated as in
 that page's Algorithm 1 (section 4), with one filter per channel group
-(section 4, first bullet list).  See the C file for the exact statement.
+(section 4, first bullet list); and its backward, the chain rule of that
+definition term by term (the filter gradient being the global sum over
+positions that the same page's section 7 describes).  See the C file for the
+exact statements.
 
 Every pin that ties this oracle to something other than itself lives in
 ``tests/test_oracle.py``; nothing here is left "parity unpinned".
@@ -50,6 +53,8 @@ def _load():
         i64 = ctypes.c_int64
         lib.hyena_ref_fwd_f64.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, i64, dp]
         lib.hyena_ref_fwd_f64.restype = ctypes.c_int
+        lib.hyena_ref_bwd_f64.argtypes = [dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, dp, dp, dp, dp]
+        lib.hyena_ref_bwd_f64.restype = ctypes.c_int
         lib.hyena_ref_num_threads.argtypes = []
         lib.hyena_ref_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -88,3 +93,28 @@ def conv_fwd_ref(q, k, v, h, group_size: int) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle rejected the arguments (code %d)" % rc)
     return y
+
+
+def conv_bwd_ref(q, k, v, h, dy, group_size: int):
+    """(dq, dk, dv, dh) of y = q (.) (h * (k (.) v)) for upstream gradient dy, fp64.
+
+    dq, dk, dv: [B, L, D]; dh: [D // group_size, l_h].
+    """
+    q, k, v, h, dy = _f64(q), _f64(k), _f64(v), _f64(h), _f64(dy)
+    if q.ndim != 3 or any(a.shape != q.shape for a in (k, v, dy)):
+        raise ValueError("q, k, v, dy must share one [B, L, D] shape")
+    B, L, D = q.shape
+    if h.ndim != 2:
+        raise ValueError("h must be [D // group_size, l_h]")
+    G, l_h = h.shape
+    if group_size < 1 or D % group_size != 0 or G != D // group_size:
+        raise ValueError("h has %d filters; D=%d, group_size=%d" % (G, D, group_size))
+    dq, dk, dv = np.empty_like(q), np.empty_like(q), np.empty_like(q)
+    dh = np.empty_like(h)
+    dp = ctypes.POINTER(ctypes.c_double)
+    P = lambda a: a.ctypes.data_as(dp)
+    rc = _load().hyena_ref_bwd_f64(P(q), P(k), P(v), P(h), P(dy), B, L, D, group_size, l_h,
+                                   P(dq), P(dk), P(dv), P(dh))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments (code %d)" % rc)
+    return dq, dk, dv, dh

@@ -86,3 +86,102 @@ int hyena_ref_num_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Backward of the same operator: given dy = dLoss/dy, the gradients of
+ *     y[b,t,d] = q[b,t,d] * z[b,t,d],   z[b,t,d] = sum_{s<l_h, s<=t} h[g,s] x[b,t-s,d],
+ *     x = k (.) v,   g = d / group_size,
+ * written out by the chain rule, term by term, in fp64:
+ *     dq[b,t,d] = dy[b,t,d] * z[b,t,d]
+ *     dz[b,t,d] = dy[b,t,d] * q[b,t,d]
+ *     dx[b,j,d] = sum_{s<l_h, j+s<L} h[g,s] dz[b,j+s,d]      (x[b,j,d] enters z at t = j+s)
+ *     dk = dx (.) v,   dv = dx (.) k
+ *     dh[g,s]   = sum_{b, d in g, t>=s} dz[b,t,d] x[b,t-s,d]
+ * The page "04. hardware-aware convolution kernels", section 7, states that
+ * the filter gradient is a global accumulation over every position; here it
+ * is that sum, in one fp64 accumulator per (g, s).  dh is [G, l_h]; every
+ * other array is [B, L, D].  Any of dq, dk, dv, dh may be NULL (skipped).
+ * Return codes as hyena_ref_fwd_f64.
+ */
+int hyena_ref_bwd_f64(const double *q, const double *k, const double *v,
+                      const double *h, const double *dy, int64_t B, int64_t L,
+                      int64_t D, int64_t group_size, int64_t l_h, double *dq,
+                      double *dk, double *dv, double *dh)
+{
+    if (!q || !k || !v || !h || !dy)
+        return -1;
+    if (B < 0 || L < 0 || D < 0)
+        return -2;
+    if (group_size < 1 || (D % group_size) != 0)
+        return -3;
+    if (l_h < 1)
+        return -4;
+    const int64_t G = D / group_size;
+    if (dh) {
+        for (int64_t i = 0; i < G * l_h; ++i)
+            dh[i] = 0.0;
+    }
+    if (B == 0 || L == 0 || D == 0)
+        return 0;
+    const int64_t rows = B * L;
+
+    if (dq) {
+#pragma omp parallel for schedule(static)
+        for (int64_t row = 0; row < rows; ++row) {
+            const int64_t b = row / L, t = row % L;
+            const size_t batch0 = (size_t)b * (size_t)L * (size_t)D;
+            for (int64_t d = 0; d < D; ++d) {
+                const double *hg = h + (size_t)(d / group_size) * (size_t)l_h;
+                int64_t j0 = t - (l_h - 1);
+                if (j0 < 0)
+                    j0 = 0;
+                double z = 0.0;
+                for (int64_t j = j0; j <= t; ++j) {
+                    const size_t o = batch0 + (size_t)j * (size_t)D + (size_t)d;
+                    z += hg[t - j] * (k[o] * v[o]);
+                }
+                const size_t oy = batch0 + (size_t)t * (size_t)D + (size_t)d;
+                dq[oy] = dy[oy] * z;
+            }
+        }
+    }
+    if (dk || dv) {
+#pragma omp parallel for schedule(static)
+        for (int64_t row = 0; row < rows; ++row) {
+            const int64_t b = row / L, j = row % L;
+            const size_t batch0 = (size_t)b * (size_t)L * (size_t)D;
+            for (int64_t d = 0; d < D; ++d) {
+                const double *hg = h + (size_t)(d / group_size) * (size_t)l_h;
+                double dx = 0.0;
+                for (int64_t s = 0; s < l_h && j + s < L; ++s) {
+                    const size_t o = batch0 + (size_t)(j + s) * (size_t)D + (size_t)d;
+                    dx += hg[s] * (dy[o] * q[o]);
+                }
+                const size_t ox = batch0 + (size_t)j * (size_t)D + (size_t)d;
+                if (dk)
+                    dk[ox] = dx * v[ox];
+                if (dv)
+                    dv[ox] = dx * k[ox];
+            }
+        }
+    }
+    if (dh) {
+        const int64_t pairs = G * l_h;
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t gs_ = 0; gs_ < pairs; ++gs_) {
+            const int64_t g = gs_ / l_h, s = gs_ % l_h;
+            double acc = 0.0;
+            for (int64_t b = 0; b < B; ++b) {
+                const size_t batch0 = (size_t)b * (size_t)L * (size_t)D;
+                for (int64_t t = s; t < L; ++t) {
+                    const size_t rt = batch0 + (size_t)t * (size_t)D;
+                    const size_t rx = batch0 + (size_t)(t - s) * (size_t)D;
+                    for (int64_t d = g * group_size; d < (g + 1) * group_size; ++d)
+                        acc += (dy[rt + d] * q[rt + d]) * (k[rx + d] * v[rx + d]);
+                }
+            }
+            dh[gs_] = acc;
+        }
+    }
+    return 0;
+}

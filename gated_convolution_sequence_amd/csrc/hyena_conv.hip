@@ -86,6 +86,8 @@ struct Params {
     const void *q, *k, *v, *h;
     void *y;
     const void *kp, *vp; // rows before row 0 of each batch row ([B, P, D]), or null
+    const void *g2;     // second gate (two-output form), or null
+    void *y2;           // second output (two-output form), or null
     int64_t L;          // rows per batch
     int32_t D;          // channels (row pitch, elements)
     int32_t group_size;
@@ -161,7 +163,12 @@ template <> struct Mma<true> {
 // the round-robin dispatch, launched together) is reading the same rows as
 // its own last chunks, so they come from L2 instead of HBM.  Then the
 // deferred chunks are computed.
-template <bool F32, int KH, int PF, int S>
+//
+// REV walks time backwards: logical row t is physical row L-1-t, so the same
+// causal filter applied in the walk's order computes sum_s h[s] x[t+s] (the
+// input gradient of the operator).  DUAL gates the one convolution with two
+// tensors into two outputs (y = q acc, y2 = g2 acc).
+template <bool F32, int KH, int PF, int S, bool REV = false, bool DUAL = false>
 __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     using T = Tr<F32>;
     using M = Mma<F32>;
@@ -202,13 +209,19 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     // t_stop-1 of batch b, starting at channel c_begin.  The host keeps it
     // below 2^31 bytes, so a negative (earlier) row offset is out of range,
     // as is every row at or past t_stop.
-    const size_t base_off = ((size_t)b * (size_t)p.L + (size_t)base_row) * (size_t)row_bytes +
+    // Under REV the window holds the same logical rows, at physical rows
+    // L - t_stop .. L - 1 - base_row, in decreasing order.
+    const int nwin = (int)(t_stop - base_row);
+    const size_t first_phys = REV ? (size_t)(p.L - t_stop) : (size_t)base_row;
+    const size_t base_off = ((size_t)b * (size_t)p.L + first_phys) * (size_t)row_bytes +
                             (size_t)c_begin * T::EB;
-    const uint32_t nrec = (uint32_t)((t_stop - base_row) * row_bytes - c_begin * T::EB);
+    const uint32_t nrec = (uint32_t)(nwin * row_bytes - c_begin * T::EB);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + base_off, nrec);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + base_off, nrec);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + base_off, nrec);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc((char *)p.y + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rg2 = make_rsrc(DUAL ? (const char *)p.g2 + base_off : (const char *)p.q, DUAL ? nrec : 0u);
+    const __amdgpu_buffer_rsrc_t ry2 = make_rsrc(DUAL ? (char *)p.y2 + base_off : (char *)p.y, DUAL ? nrec : 0u);
     const int row0 = (int)(t_begin - base_row);       // window row of chunk 0
     // The caller's prefix rows (the P rows before row 0 of batch row b), read
     // instead of zeros by history chunks that lie before row 0.  With P = 0
@@ -240,12 +253,13 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     const int ld_row = tid / T::TPR;
     const int ld_seg = tid % T::TPR;
     const bool seg_ok = c_begin + ld_seg * T::VEC < p.D;
-    const int ld_base = ld_row * row_bytes + ld_seg * 16;
+    const int ld_base = (REV ? -ld_row : ld_row) * row_bytes + ld_seg * 16;
     // Offset of chunk c (relative to the span start), load i.  Rows past the
     // span or before the history fall outside the byte window (no traffic,
     // no store); `need` = false sends the access outside it too.
     auto io_off = [&](int c, int i, bool need) -> uint32_t {
-        const int r = (row0 + c * kChunk + i * T::RPL) * row_bytes + ld_base;
+        const int lr = row0 + c * kChunk + i * T::RPL;  // logical window row (+ ld_row)
+        const int r = (REV ? nwin - 1 - lr : lr) * row_bytes + ld_base;
         return (seg_ok && need) ? (uint32_t)r : kOOB;
     };
     // chunk of ingest item i: the span's chunks, then the history chunks
@@ -253,7 +267,8 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     // chunk of compute item j: the non-deferred chunks, then the deferred ones
     auto comp_chunk = [](int j) -> int { return j < S - ND ? ND + j : j - (S - ND); };
 
-    u32x4_t kr[PF][T::NLD], vr[PF][T::NLD], qr[PF][T::NLD];
+    constexpr int NG = DUAL ? 2 : 1;  // gates per row
+    u32x4_t kr[PF][T::NLD], vr[PF][T::NLD], qr[PF][NG][T::NLD];
 
     // The last H chunks of a span are the next span's history: they are
     // loaded with the default (L2-allocating) policy so that the neighbour's
@@ -282,12 +297,15 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
             }
         }
     };
-    auto load_q = [&](int j, u32x4_t *qd) {
+    auto load_q = [&](int j, u32x4_t (*qd)[T::NLD]) {
         const bool need = j < S;
         const int c = need ? comp_chunk(j) : S;
 #pragma unroll
-        for (int i = 0; i < T::NLD; ++i)
-            qd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, io_off(c, i, need), 0, kLoadPolicy));
+        for (int i = 0; i < T::NLD; ++i) {
+            qd[0][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, io_off(c, i, need), 0, kLoadPolicy));
+            if constexpr (DUAL)
+                qd[NG - 1][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rg2, io_off(c, i, need), 0, kLoadPolicy));
+        }
     };
     // x = k*v for this thread's rows -> xs.
     auto store_x = [&](const u32x4_t *kd, const u32x4_t *vd) {
@@ -389,30 +407,44 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
             *(f32x4_t *)(&st[st_addr(16 * nt + n16, 4 * w + q4)]) = acc;
         }
         __syncthreads();
-        // epilogue: y = q * acc for this thread's rows, 16-byte stores
-        u32x4_t *qd = qr[j % PF];
-        u32x4_t yv[T::NLD];
+        // epilogue: y = q * acc (and y2 = g2 * acc) for this thread's rows,
+        // 16-byte stores.  LDS tiles are in walk order; io_off maps the
+        // thread's walk row to its physical row (REV: backwards) for the
+        // gate load and the store alike.
+        u32x4_t (*qd)[T::NLD] = qr[j % PF];
+        u32x4_t yv[NG][T::NLD];
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
             const int row = i * T::RPL + ld_row;
+            f32x4_t a[2];
             if constexpr (F32) {
-                const f32x4_t a = *(const f32x4_t *)(&st[st_addr(row, ld_seg)]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) yv[i][e] = __float_as_uint(__uint_as_float(qd[i][e]) * a[e]);
+                a[0] = *(const f32x4_t *)(&st[st_addr(row, ld_seg)]);
             } else {
-                const f32x4_t a0 = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg)]);
-                const f32x4_t a1 = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg + 1)]);
-                yv[i][0] = pack_bf16(bf_lo(qd[i][0]) * a0[0], bf_hi(qd[i][0]) * a0[1]);
-                yv[i][1] = pack_bf16(bf_lo(qd[i][1]) * a0[2], bf_hi(qd[i][1]) * a0[3]);
-                yv[i][2] = pack_bf16(bf_lo(qd[i][2]) * a1[0], bf_hi(qd[i][2]) * a1[1]);
-                yv[i][3] = pack_bf16(bf_lo(qd[i][3]) * a1[2], bf_hi(qd[i][3]) * a1[3]);
+                a[0] = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg)]);
+                a[1] = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg + 1)]);
+            }
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const u32x4_t gq = qd[gi][i];
+                if constexpr (F32) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) yv[gi][i][e] = __float_as_uint(__uint_as_float(gq[e]) * a[0][e]);
+                } else {
+                    yv[gi][i][0] = pack_bf16(bf_lo(gq[0]) * a[0][0], bf_hi(gq[0]) * a[0][1]);
+                    yv[gi][i][1] = pack_bf16(bf_lo(gq[1]) * a[0][2], bf_hi(gq[1]) * a[0][3]);
+                    yv[gi][i][2] = pack_bf16(bf_lo(gq[2]) * a[1][0], bf_hi(gq[2]) * a[1][1]);
+                    yv[gi][i][3] = pack_bf16(bf_lo(gq[3]) * a[1][2], bf_hi(gq[3]) * a[1][3]);
+                }
             }
         }
         // refill q before storing y, so y never shares registers with q
         load_q(j + PF, qd);
 #pragma unroll
-        for (int i = 0; i < T::NLD; ++i)
-            __builtin_amdgcn_raw_buffer_store_b128(yv[i], ry, io_off(c, i, true), 0, kStorePolicy);
+        for (int i = 0; i < T::NLD; ++i) {
+            __builtin_amdgcn_raw_buffer_store_b128(yv[0][i], ry, io_off(c, i, true), 0, kStorePolicy);
+            if constexpr (DUAL)
+                __builtin_amdgcn_raw_buffer_store_b128(yv[NG - 1][i], ry2, io_off(c, i, true), 0, kStorePolicy);
+        }
     };
 
     // ---- phase 1: the span's own chunks ------------------------------------
@@ -459,6 +491,193 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Filter gradient, pass 1 (page "04. hardware-aware convolution kernels",
+// section 7: block-local partial filter gradients written coalesced, then a
+// reduction).  With dz = dy q and x = k v,
+//     dh[g, s] = sum_{b, t, d in g} dz[b, t, d] x[b, t - s, d].
+// For one 16-channel tile the products dz[t, :] . x[u, :] over the tile's
+// channels are a GEMM (rows t of a chunk by rows u of the chunk and its
+// history) with the channels as the contraction, so both MFMA operands are
+// read row-major: no transpose.  dh[s] sums that product along the diagonal
+// t - u = s.  For a 16-row output tile a and input tile b = a - delta, the
+// accumulator element (lane n16, q4, i) always has lag 16 delta + 4 q4 + i -
+// n16, so every tile pair on one diagonal accumulates into one register tile
+// P[delta]; the lags are sorted out once per span.  Each workgroup writes
+// its partial dh (one row of l_h floats per 16-channel tile) to ws.
+// ---------------------------------------------------------------------------
+struct DhParams {
+    const void *q, *k, *v, *dy;
+    float *ws;          // [B * n_spans][D / 16][l_h] partial sums
+    int64_t L;
+    int32_t D, l_h, n_spans, n_slabs;
+};
+
+template <bool F32, int KH, int S>
+__global__ __launch_bounds__(kThreads) void hyena_bwd_dh_kernel(DhParams p) {
+    using T = Tr<F32>;
+    constexpr int PF = 2;
+    constexpr int HROWS = 32 * KH;
+    constexpr int H = (HROWS + kChunk - 1) / kChunk;      // history chunks
+    constexpr int RING = H + 1;                           // x chunks resident
+    constexpr int NDL = 2 * KH + 1;                       // diagonals (16-row units)
+    constexpr int PITCH = kSlab * T::EB;
+
+    __shared__ __attribute__((aligned(16))) unsigned char xr[RING][kChunk * PITCH];
+    __shared__ __attribute__((aligned(16))) unsigned char dzs[kChunk * PITCH];
+    __shared__ float acc_s[kWaves][256];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int l = tid & 63;
+    const int n16 = l & 15;
+    const int q4 = l >> 4;
+
+    int bid = blockIdx.x;
+    const int slab = bid % p.n_slabs;
+    bid /= p.n_slabs;
+    const int spn = bid % p.n_spans;
+    const int b = bid / p.n_spans;
+
+    const int64_t t_begin = (int64_t)spn * S * kChunk;
+    const int64_t t_stop = min(p.L, t_begin + (int64_t)S * kChunk);
+    const int64_t base_row = max((int64_t)0, t_begin - HROWS);
+    const int c_begin = slab * kSlab;
+    const int row_bytes = p.D * T::EB;
+    const size_t base_off = ((size_t)b * (size_t)p.L + (size_t)base_row) * (size_t)row_bytes +
+                            (size_t)c_begin * T::EB;
+    const uint32_t nrec = (uint32_t)((t_stop - base_row) * row_bytes - c_begin * T::EB);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.dy + base_off, nrec);
+    const int row0 = (int)(t_begin - base_row);
+
+    const int ld_row = tid / T::TPR;
+    const int ld_seg = tid % T::TPR;
+    const bool seg_ok = c_begin + ld_seg * T::VEC < p.D;
+    const int ld_base = ld_row * row_bytes + ld_seg * 16;
+    auto off = [&](int c, int i, bool need) -> uint32_t {
+        const int r = (row0 + c * kChunk + i * T::RPL) * row_bytes + ld_base;
+        return (seg_ok && need) ? (uint32_t)r : kOOB;
+    };
+    // Row-major LDS tiles, 16-byte segment XOR (row & 15): 16 lanes reading
+    // the same channels of 16 consecutive rows hit distinct banks.
+    auto lds_addr = [&](int row, int byte) -> int {
+        return row * PITCH + ((((byte >> 4) ^ (row & 15))) << 4) + (byte & 15);
+    };
+
+    u32x4_t kr[PF][T::NLD], vr[PF][T::NLD], qr[PF][T::NLD], dr[PF][T::NLD];
+    // chunks -H .. S-1 in order; history chunks need no q, dy
+    auto load = [&](int c, int slot) {
+        const bool need = c < S;
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const uint32_t o = off(c, i, need);
+            const uint32_t og = off(c, i, need && c >= 0);
+            kr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadPolicy));
+            vr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kLoadPolicy));
+            qr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, og, 0, kLoadPolicy));
+            dr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rd, og, 0, kLoadPolicy));
+        }
+    };
+    // elementwise product of two 16-byte vectors -> LDS tile (bf16: rounded)
+    auto put = [&](unsigned char *tile, const u32x4_t *a, const u32x4_t *b2) {
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const int row = i * T::RPL + ld_row;
+            u32x4_t xv;
+            if constexpr (F32) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xv[e] = __float_as_uint(__uint_as_float(a[i][e]) * __uint_as_float(b2[i][e]));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xv[e] = pack_bf16(bf_lo(a[i][e]) * bf_lo(b2[i][e]), bf_hi(a[i][e]) * bf_hi(b2[i][e]));
+            }
+            *(u32x4_t *)(&tile[lds_addr(row, ld_seg * 16)]) = xv;
+        }
+    };
+
+    f32x4_t P[NDL];
+#pragma unroll
+    for (int d = 0; d < NDL; ++d) P[d] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // this lane's 4 channels of the wave's tile (K of the MFMA)
+    const int kbyte = (w * kTile + 4 * q4) * T::EB;
+
+#pragma unroll
+    for (int s = 0; s < PF; ++s) load(-H + s, s);
+#pragma unroll
+    for (int c = -H; c < S; ++c) {
+        const int slot = (c + H) % PF;
+        unsigned char *xt = xr[(c + H) % RING];
+        put(xt, kr[slot], vr[slot]);
+        if (c >= 0) put(dzs, dr[slot], qr[slot]);
+        load(c + PF, slot);
+        __syncthreads();
+        if (c >= 0) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                // A: dz rows 16a + n16 (as M), channels 4 q4 .. +3 (as K)
+                const int ra = 16 * a + n16;
+#pragma unroll
+                for (int d = 0; d < NDL; ++d) {
+                    const int bt = a - d;                         // input tile, may be < 0
+                    const int cb = c + (bt < 0 ? -((-bt + 3) / 4) : 0);  // its chunk
+                    const int rb = 16 * (bt - 4 * (cb - c)) + n16;       // its row in that chunk
+                    const unsigned char *xt2 = xr[(cb + H + 4 * RING) % RING];
+                    if constexpr (F32) {
+                        const f32x4_t av = *(const f32x4_t *)(&dzs[lds_addr(ra, kbyte)]);
+                        const f32x4_t bv = *(const f32x4_t *)(&xt2[lds_addr(rb, kbyte)]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            P[d] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[e], bv[e], P[d], 0, 0, 0);
+                    } else {
+                        typedef short s16x4_t __attribute__((ext_vector_type(4)));
+                        const s16x4_t av = *(const s16x4_t *)(&dzs[lds_addr(ra, kbyte)]);
+                        const s16x4_t bv = *(const s16x4_t *)(&xt2[lds_addr(rb, kbyte)]);
+                        P[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, P[d], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        __syncthreads();  // dzs and the oldest x chunk are rewritten next
+    }
+    // lags: element i of lane (n16, q4) in P[d] is lag 16 d + 4 q4 + i - n16
+    for (int i = l; i < 256; i += 64) acc_s[w][i] = 0.0f;
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < NDL; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int lag = 16 * d + 4 * q4 + i - n16;
+            if (lag >= 0 && lag < p.l_h) atomicAdd(&acc_s[w][lag], P[d][i]);
+        }
+    __syncthreads();
+    const int tile = slab * kWaves + w;
+    if (c_begin + w * kTile < p.D) {
+        float *dst = p.ws + ((size_t)(b * p.n_spans + spn) * (size_t)(p.D / kTile) + tile) * p.l_h;
+        for (int i = l; i < p.l_h; i += 64) dst[i] = acc_s[w][i];
+    }
+}
+
+// Pass 2: dh[g, s] = sum over partial rows and over the group's tiles.
+// Consecutive threads read consecutive taps of one partial row.
+__global__ __launch_bounds__(256) void hyena_bwd_dh_reduce_kernel(const float *ws, float *dh,
+                                                                  int rows, int tiles, int tiles_per_group,
+                                                                  int l_h, int G) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= G * l_h) return;
+    const int g = idx / l_h, s = idx % l_h;
+    float acc = 0.0f;
+    for (int r = 0; r < rows; ++r) {
+        const float *row = ws + (size_t)r * tiles * l_h;
+        for (int t = 0; t < tiles_per_group; ++t) acc += row[(size_t)(g * tiles_per_group + t) * l_h + s];
+    }
+    dh[idx] = acc;
+}
+
 typedef void (*KernelFn)(Params);
 
 // Chunks of k, v and q in flight per workgroup.  The fp32 path (twice the
@@ -471,25 +690,40 @@ constexpr int kSpans[] = {1, 2, 4, 8, 16, 32};
 constexpr int kNumSpans = sizeof(kSpans) / sizeof(kSpans[0]);
 template <bool F32> constexpr int kNumSpansFor = F32 ? 3 : kNumSpans;
 
-template <bool F32, int KH, int... Ss>
-KernelFn span_table_entry(int si, std::integer_sequence<int, Ss...>) {
-    static constexpr KernelFn fns[] = {hyena_fwd_kernel<F32, KH, kPrefetch<F32>, kSpans[Ss]>...};
+// Kernel families and their compiled span counts (indices into kSpans).
+enum Family { kFwd = 0, kRevDual = 1, kDh = 2 };
+template <bool F32, int Fam> constexpr int kSpanCount =
+    Fam == kFwd ? kNumSpansFor<F32> : Fam == kRevDual ? (F32 ? 2 : 4) : (F32 ? 3 : 5);
+
+typedef void (*DhFn)(DhParams);
+template <bool F32, int Fam> struct FnType { typedef KernelFn type; };
+template <bool F32> struct FnType<F32, kDh> { typedef DhFn type; };
+
+template <bool F32, int Fam, int KH, int Sp>
+constexpr typename FnType<F32, Fam>::type kernel_of() {
+    if constexpr (Fam == kFwd)
+        return hyena_fwd_kernel<F32, KH, kPrefetch<F32>, Sp, false, false>;
+    else if constexpr (Fam == kRevDual)
+        return hyena_fwd_kernel<F32, KH, kPrefetch<F32>, Sp, true, true>;
+    else
+        return hyena_bwd_dh_kernel<F32, KH, Sp>;
+}
+
+template <bool F32, int Fam, int KH, int... Ss>
+typename FnType<F32, Fam>::type span_table_entry(int si, std::integer_sequence<int, Ss...>) {
+    static constexpr typename FnType<F32, Fam>::type fns[] = {kernel_of<F32, Fam, KH, kSpans[Ss]>()...};
     return fns[si];
 }
 
-template <bool F32, int KH>
-KernelFn pick_span(int si) {
-    return span_table_entry<F32, KH>(si, std::make_integer_sequence<int, kNumSpansFor<F32>>{});
-}
-
-template <bool F32>
-KernelFn pick_kernel(int kh, int si) {
+template <bool F32, int Fam>
+typename FnType<F32, Fam>::type pick_kernel(int kh, int si) {
+    constexpr int n = kSpanCount<F32, Fam>;
     switch (kh) {
-    case 0: return pick_span<F32, 0>(si);
-    case 1: return pick_span<F32, 1>(si);
-    case 2: return pick_span<F32, 2>(si);
-    case 3: return pick_span<F32, 3>(si);
-    default: return pick_span<F32, 4>(si);
+    case 0: return span_table_entry<F32, Fam, 0>(si, std::make_integer_sequence<int, n>{});
+    case 1: return span_table_entry<F32, Fam, 1>(si, std::make_integer_sequence<int, n>{});
+    case 2: return span_table_entry<F32, Fam, 2>(si, std::make_integer_sequence<int, n>{});
+    case 3: return span_table_entry<F32, Fam, 3>(si, std::make_integer_sequence<int, n>{});
+    default: return span_table_entry<F32, Fam, 4>(si, std::make_integer_sequence<int, n>{});
     }
 }
 
@@ -514,7 +748,7 @@ int check_sizes(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h
 }
 
 int make_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, int dtype,
-              int64_t span_req, Plan *pl) {
+              int64_t span_req, Plan *pl, int family = kFwd) {
     const int64_t eb = dtype == HYENA_DTYPE_F32 ? 4 : 2;
     pl->kh = (int)((l_h - 1 + 31) / 32);
     pl->n_chunks = (L + kChunk - 1) / kChunk;
@@ -527,11 +761,17 @@ int make_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, 
     // MI355X at B=1, L=8192, D=4096: SE best at 2 chunks, MR at 8.
     int64_t want = span_req;
     if (want <= 0) want = pl->kh <= 1 ? 2 : 2 * pl->kh;
+    // the filter-gradient kernel writes one partial row per span: longer
+    if (family == kDh && span_req <= 0) want = 16;
     if (want > pl->n_chunks) want = pl->n_chunks;
     // largest compiled span <= want whose byte window (history + span +
     // one chunk of slack) stays below 2^31
     int si = -1;
-    const int n_spans_compiled = dtype == HYENA_DTYPE_F32 ? kNumSpansFor<true> : kNumSpansFor<false>;
+    const bool f32 = dtype == HYENA_DTYPE_F32;
+    const int n_spans_compiled =
+        family == kFwd ? (f32 ? kSpanCount<true, kFwd> : kSpanCount<false, kFwd>)
+        : family == kRevDual ? (f32 ? kSpanCount<true, kRevDual> : kSpanCount<false, kRevDual>)
+                             : (f32 ? kSpanCount<true, kDh> : kSpanCount<false, kDh>);
     for (int i = 0; i < n_spans_compiled; ++i) {
         const int64_t win = ((int64_t)kSpans[i] * kChunk + 32 * pl->kh + kChunk) * D * eb;
         if (win >= kMaxWindowBytes) break;
@@ -612,10 +852,22 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
     p.n_spans = (int32_t)pl.n_spans;
     p.n_slabs = (int32_t)pl.n_slabs;
     p.P = (int32_t)P;
-    KernelFn fn = dtype == HYENA_DTYPE_F32 ? pick_kernel<true>(pl.kh, pl.span_index)
-                                           : pick_kernel<false>(pl.kh, pl.span_index);
+    p.g2 = nullptr;
+    p.y2 = nullptr;
+    KernelFn fn = dtype == HYENA_DTYPE_F32 ? pick_kernel<true, kFwd>(pl.kh, pl.span_index)
+                                           : pick_kernel<false, kFwd>(pl.kh, pl.span_index);
     hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(kThreads), 0, (hipStream_t)stream, p);
     if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+    return HYENA_OK;
+}
+
+// Partial-row count of the filter-gradient pass 1 (one row per span per
+// batch row), for the workspace size.
+static int dh_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, int dtype,
+                   Plan *pl, int64_t *ws_bytes) {
+    int st = make_plan(B, L, D, group_size, l_h, dtype, 0, pl, kDh);
+    if (st != HYENA_OK) return st;
+    *ws_bytes = B * pl->n_spans * (D / kTile) * l_h * (int64_t)sizeof(float);
     return HYENA_OK;
 }
 
@@ -632,6 +884,114 @@ int hyena_conv_fwd_halo(const void *q, const void *k, const void *v, const void 
                         int64_t span_chunks, void *stream) {
     return fwd_launch(q, k, v, h, k_prev, v_prev, P, B, L, D, group_size, l_h, out, dtype,
                       span_chunks, stream);
+}
+
+int hyena_conv_bwd_workspace(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h,
+                             int dtype, int64_t *bytes_out) {
+    int st = check_sizes(B, L, D, group_size, l_h, dtype);
+    if (st != HYENA_OK) return st;
+    if (!bytes_out) return HYENA_ERR_NULL;
+    if (B == 0 || L == 0 || D == 0) {
+        *bytes_out = 0;
+        return HYENA_OK;
+    }
+    Plan pl;
+    return dh_plan(B, L, D, group_size, l_h, dtype, &pl, bytes_out);
+}
+
+int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, const void *dy,
+                   int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, void *dq,
+                   void *dk, void *dv, float *dh, void *workspace, int64_t workspace_bytes,
+                   int dtype, void *stream) {
+    int st = check_sizes(B, L, D, group_size, l_h, dtype);
+    if (st != HYENA_OK) return st;
+    if (!q || !k || !v || !h || !dy) return HYENA_ERR_NULL;
+    if ((dk == nullptr) != (dv == nullptr)) return HYENA_ERR_NULL;
+    const size_t eb = dtype == HYENA_DTYPE_F32 ? 4 : 2;
+    const size_t nbytes = (size_t)B * (size_t)L * (size_t)D * eb;
+    const size_t hbytes = (size_t)(D / group_size) * (size_t)l_h * eb;
+    const size_t dhbytes = (size_t)(D / group_size) * (size_t)l_h * sizeof(float);
+    uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)dy;
+    if (dq) mis |= (uintptr_t)dq;
+    if (dk) mis |= (uintptr_t)dk | (uintptr_t)dv;
+    if (mis & 15u) return HYENA_ERR_ALIGN;
+    if (((uintptr_t)h & (eb - 1)) || ((uintptr_t)dh & 3u) || ((uintptr_t)workspace & 15u))
+        return HYENA_ERR_ALIGN;
+    // every output and the workspace are disjoint from every input and
+    // from each other
+    const void *in[5] = {q, k, v, dy, h};
+    const size_t in_n[5] = {nbytes, nbytes, nbytes, nbytes, hbytes};
+    Plan dpl;
+    int64_t ws_need = 0;
+    if (B > 0 && L > 0 && D > 0) {
+        st = dh_plan(B, L, D, group_size, l_h, dtype, &dpl, &ws_need);
+        if (st != HYENA_OK) return st;
+    }
+    const void *out[5] = {dq, dk, dv, dh, dh ? workspace : nullptr};
+    const size_t out_n[5] = {nbytes, nbytes, nbytes, dhbytes, (size_t)ws_need};
+    for (int i = 0; i < 5; ++i) {
+        if (!out[i]) continue;
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(out[i], out_n[i], in[j], in_n[j])) return HYENA_ERR_ALIAS;
+        for (int j = i + 1; j < 5; ++j)
+            if (out[j] && overlaps(out[i], out_n[i], out[j], out_n[j])) return HYENA_ERR_ALIAS;
+    }
+    if (dh && (!workspace || workspace_bytes < ws_need)) return HYENA_ERR_WORKSPACE;
+    if (B == 0 || L == 0 || D == 0) {
+        if (dh) return hipMemsetAsync(dh, 0, dhbytes, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_LAUNCH;
+        return HYENA_OK;
+    }
+    if (group_size % kTile != 0) return HYENA_ERR_UNSUPPORTED;
+    const bool f32 = dtype == HYENA_DTYPE_F32;
+
+    // dq = dy * (h * (k v)): the forward with dy as the gate
+    if (dq) {
+        st = fwd_launch(dy, k, v, h, nullptr, nullptr, 0, B, L, D, group_size, l_h, dq, dtype, 0, stream);
+        if (st != HYENA_OK) return st;
+    }
+    // dk = v * dx, dv = k * dx with dx = h applied to dz = dy q at later rows:
+    // the forward walked backwards in time, x = dy q, gates v and k
+    if (dk) {
+        Plan pl;
+        st = make_plan(B, L, D, group_size, l_h, dtype, 0, &pl, kRevDual);
+        if (st != HYENA_OK) return st;
+        Params p;
+        p.q = v; p.k = dy; p.v = q; p.h = h; p.y = dk;
+        p.g2 = k; p.y2 = dv;
+        p.kp = nullptr; p.vp = nullptr; p.P = 0;
+        p.L = L;
+        p.D = (int32_t)D;
+        p.group_size = (int32_t)group_size;
+        p.l_h = (int32_t)l_h;
+        p.n_spans = (int32_t)pl.n_spans;
+        p.n_slabs = (int32_t)pl.n_slabs;
+        KernelFn fn = f32 ? pick_kernel<true, kRevDual>(pl.kh, pl.span_index)
+                          : pick_kernel<false, kRevDual>(pl.kh, pl.span_index);
+        hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(kThreads), 0, (hipStream_t)stream, p);
+        if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+    }
+    // dh: partial sums per span (pass 1), then their reduction (pass 2)
+    if (dh) {
+        DhParams p;
+        p.q = q; p.k = k; p.v = v; p.dy = dy;
+        p.ws = (float *)workspace;
+        p.L = L;
+        p.D = (int32_t)D;
+        p.l_h = (int32_t)l_h;
+        p.n_spans = (int32_t)dpl.n_spans;
+        p.n_slabs = (int32_t)dpl.n_slabs;
+        DhFn fn = f32 ? pick_kernel<true, kDh>(dpl.kh, dpl.span_index)
+                      : pick_kernel<false, kDh>(dpl.kh, dpl.span_index);
+        hipLaunchKernelGGL(fn, dim3((unsigned)dpl.workgroups), dim3(kThreads), 0, (hipStream_t)stream, p);
+        if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+        const int G = (int)(D / group_size);
+        const int n = G * (int)l_h;
+        hipLaunchKernelGGL(hyena_bwd_dh_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           (hipStream_t)stream, (const float *)workspace, dh, (int)(B * dpl.n_spans),
+                           (int)(D / kTile), (int)(group_size / kTile), (int)l_h, G);
+        if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+    }
+    return HYENA_OK;
 }
 
 int hyena_conv_fwd(const void *q, const void *k, const void *v, const void *h, int64_t B, int64_t L,
@@ -657,6 +1017,7 @@ const char *hyena_conv_strerror(int status) {
     case HYENA_ERR_UNSUPPORTED: return "group_size must be a multiple of 16 (or the shape is too large to address)";
     case HYENA_ERR_LAUNCH: return "kernel launch failed";
     case HYENA_ERR_DTYPE: return "unknown dtype code";
+    case HYENA_ERR_WORKSPACE: return "workspace missing or smaller than hyena_conv_bwd_workspace reports";
     default: return "unknown status";
     }
 }

@@ -1,6 +1,6 @@
 /*
- * hyena_conv.h -- C ABI of the MI355X (gfx950) Hyena-SE / Hyena-MR forward
- * operator
+ * hyena_conv.h -- C ABI of the MI355X (gfx950) Hyena-SE / Hyena-MR operator
+ * (forward, and its backward further down)
  *
  *     y[b,t,d] = q[b,t,d] * sum_{s=0}^{min(t, l_h-1)} h[d / group_size, s] * k[b,t-s,d] * v[b,t-s,d]
  *
@@ -64,7 +64,8 @@ enum hyena_status {
     HYENA_ERR_ALIAS = -6,       /* out overlaps an input (q, k, v, h, k_prev, v_prev) */
     HYENA_ERR_UNSUPPORTED = -7, /* group_size not a multiple of 16, or a shape the kernel cannot address */
     HYENA_ERR_LAUNCH = -8,      /* the HIP runtime reported an error at launch */
-    HYENA_ERR_DTYPE = -9        /* unknown element-type code */
+    HYENA_ERR_DTYPE = -9,       /* unknown element-type code */
+    HYENA_ERR_WORKSPACE = -10   /* workspace missing or too small */
 };
 
 enum hyena_dtype {
@@ -109,6 +110,35 @@ int hyena_conv_fwd_halo(const void *q, const void *k, const void *v,
                         int64_t P, int64_t B, int64_t L, int64_t D,
                         int64_t group_size, int64_t l_h, void *out, int dtype,
                         int64_t span_chunks, void *stream);
+
+/* Backward of the forward above for an upstream gradient dy ([B, L, D]):
+ *     dq = dy (.) (h * (k (.) v)),         dz = dy (.) q,
+ *     dx[t] = sum_{s < l_h, t+s < L} h[g, s] dz[t + s],
+ *     dk = dx (.) v,   dv = dx (.) k,
+ *     dh[g, s] = sum_{b, t, d in g} dz[b, t, d] x[b, t - s, d],  x = k (.) v.
+ * (StripedHyena 2 explainer, page "04. hardware-aware convolution kernels",
+ * section 7: the filter gradient is a global accumulation over positions,
+ * computed in two back-to-back passes -- block-local partial gradients
+ * written coalesced to `workspace`, then a vectorised reduction.)
+ * dq, dk, dv are [B, L, D] in `dtype` (16-byte aligned); dh is float32
+ * [D / group_size, l_h] (4-byte aligned) for either dtype.  Any of dq, dh
+ * may be NULL (not computed); dk and dv are both given or both NULL.  With dh
+ * the caller passes `workspace`, at least the size hyena_conv_bwd_workspace
+ * reports (16-byte aligned, contents need not be initialised); it is
+ * overwritten.  Outputs and workspace must not overlap the inputs or each
+ * other.  bf16 precision as the forward: dz and x are rounded once to bf16
+ * as matrix-core operands, sums are fp32, outputs rounded once. */
+int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h,
+                   const void *dy, int64_t B, int64_t L, int64_t D,
+                   int64_t group_size, int64_t l_h, void *dq, void *dk,
+                   void *dv, float *dh, void *workspace,
+                   int64_t workspace_bytes, int dtype, void *stream);
+
+/* Bytes of workspace hyena_conv_bwd needs to compute dh for these sizes
+ * (written to *bytes_out).  Host only.  Returns a status. */
+int hyena_conv_bwd_workspace(int64_t B, int64_t L, int64_t D,
+                             int64_t group_size, int64_t l_h, int dtype,
+                             int64_t *bytes_out);
 
 /* The work split hyena_conv_fwd_ex would use: writes the chunks per
  * workgroup and the workgroup count.  Host only; runs the same argument

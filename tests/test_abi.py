@@ -145,3 +145,32 @@ def test_halo_entry_validates_its_prefix_on_host(kw, code):
 def test_halo_entry_without_prefix_needs_no_prefix_pointers():
     # P = 0: same checks as the plain entry point; still rejected before launch
     assert _halo(kp=None, vp=None, Pn=0, q=None) == -1
+
+
+def _bwd(q=P["q"], k=P["k"], v=P["v"], h=P["h"], dy=P["out"] + (64 << 20), B=1, L=128, D=64,
+         gs=16, l_h=7, dq=P["out"], dk=P["out"] + (16 << 20), dv=P["out"] + (32 << 20),
+         dh=P["out"] + (48 << 20), ws=P["out"] + (96 << 20), ws_n=1 << 20, dtype=hc.DTYPE_BF16):
+    return hc.lib().hyena_conv_bwd(q, k, v, h, dy, B, L, D, gs, l_h, dq, dk, dv, dh, ws, ws_n,
+                                   dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dy=None), -1), (dict(q=None), -1), (dict(dk=None), -1), (dict(dv=None), -1),
+    (dict(dh=P["out"] + (48 << 20) + 2), -5), (dict(dq=P["out"] + 8), -5),
+    (dict(ws=P["out"] + (96 << 20) + 4), -5),
+    (dict(dq=P["q"]), -6), (dict(dk=P["out"]), -6), (dict(dh=P["k"] + 64), -6),
+    (dict(ws=P["v"]), -6), (dict(ws=P["out"] + (16 << 20)), -6),
+    (dict(ws=None), -10), (dict(ws_n=16), -10),
+    (dict(l_h=0), -4), (dict(gs=8), -7), (dict(dtype=5), -9),
+])
+def test_backward_validates_on_host(kw, code):
+    assert _bwd(**kw) == code
+
+
+def test_backward_workspace_size():
+    # one float per (batch row, span of the filter-gradient pass, 16-channel tile, tap)
+    n = hc.bwd_workspace_bytes(1, 8192, 4096, 16, 128)
+    assert n == 1 * (8192 // (64 * 16)) * (4096 // 16) * 128 * 4
+    assert hc.bwd_workspace_bytes(0, 8192, 4096, 16, 128) == 0
+    with pytest.raises(hc.HyenaError):
+        hc.bwd_workspace_bytes(1, 64, 64, 16, 300)

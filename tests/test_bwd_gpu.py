@@ -1,0 +1,167 @@
+"""GPU parity of the backward (hyena_conv_bwd) against the fp64 backward oracle.
+
+The bar, per gradient, from the rounding the library does (dz = dy q and
+x = k v rounded once to bf16 as matrix-core operands, fp32 sums, one output
+rounding), with env the same gradient computed on magnitudes:
+  dq, dk, dv (bf16): |e| <= 2^-8 |ref| + (2^-8 (1 + 2^-8) + l_h 2^-23) env
+  dq, dk, dv (fp32): |e| <= 2^-24 |ref| + (l_h + 4) 2^-23 env
+  dh (fp32 output):  |e| <= (u_in + (R + 256) 2^-24) env,  u_in = 2^-7 + 2^-14
+                     (bf16 inputs) or 4 * 2^-24 (fp32), R = partial rows summed
+plus the gate max|e| <= 1e-2 max|ref| (bf16) / 1e-5 max|ref| (fp32).
+Integer inputs are exact in every intermediate, so they must match bitwise.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_convolution_sequence_amd as hc
+import oracle
+from gpu_util import DEV, check, log, to_np
+from workloads import WORKLOADS, gaussian_inputs, integer_inputs, make_inputs, normal_activation
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    hc.lib()
+
+
+def _bwd_gpu(q, k, v, h, dy, gs):
+    out = hc.conv_bwd(q, k, v, h, dy, gs)
+    torch.cuda.synchronize()
+    return out
+
+
+def _refs(q, k, v, h, dy, gs):
+    a = [to_np(t) for t in (q, k, v, h, dy)]
+    ref = oracle.conv_bwd_ref(*a, gs)
+    env = oracle.conv_bwd_ref(*[np.abs(x) for x in a], gs)
+    return ref, env
+
+
+def _check_dh(got, ref, env, dtype, rows, what):
+    got = to_np(got)
+    assert np.all(np.isfinite(got)), what
+    err = np.abs(got - ref)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    gate = (1e-2 if dtype == torch.bfloat16 else 1e-5) * scale
+    u_in = 2.0 ** -7 + 2.0 ** -14 if dtype == torch.bfloat16 else 4 * 2.0 ** -24
+    bound = (u_in + (rows + 256) * 2.0 ** -24) * env + 1e-30
+    assert float(np.max(err)) <= gate, "%s: dh max err %.3e > gate %.3e" % (what, np.max(err), gate)
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, "%s: dh bound broken at %s" % (what, bad[0])
+
+
+def _check_all(grads, ref, env, l_h, dtype, rows, what):
+    names = ("dq", "dk", "dv")
+    for name, g, r, e in zip(names, grads[:3], ref[:3], env[:3]):
+        check(to_np(g), r, e, l_h, dtype, "%s %s" % (what, name))
+    _check_dh(grads[3], ref[3], env[3], dtype, rows, what)
+
+
+def _rows(B, L, D, gs, l_h, dtype):
+    n = hc.bwd_workspace_bytes(B, L, D, gs, l_h, hc.DTYPE_BF16 if dtype == torch.bfloat16 else hc.DTYPE_F32)
+    return max(1, n // ((D // 16) * l_h * 4))
+
+
+BWD_SHAPES = [
+    # B, L, D, group_size, l_h
+    (1, 1, 16, 16, 1), (1, 6, 16, 16, 4), (1, 63, 32, 16, 7), (2, 130, 48, 16, 33),
+    (1, 700, 64, 32, 128), (3, 257, 128, 16, 65), (1, 1000, 96, 48, 97), (1, 2048, 256, 16, 128),
+    (2, 515, 208, 16, 2),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h", BWD_SHAPES)
+def test_backward_gaussian(dt, B, L, D, gs, l_h):
+    log("bwd %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=7 * L + l_h)
+    dy = normal_activation((B, L, D), dtype, "cpu", seed=L + 1)
+    dev = [t.to(DEV) for t in (q, k, v, h, dy)]
+    grads = _bwd_gpu(*dev, gs)
+    ref, env = _refs(q, k, v, h, dy, gs)
+    _check_all(grads, ref, env, l_h, dtype, _rows(B, L, D, gs, l_h, dtype), "bwd")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h", [(1, 6, 16, 16, 4), (2, 777, 96, 32, 7),
+                                          (1, 1000, 64, 16, 128), (3, 130, 16, 16, 66)])
+def test_backward_integer_inputs_bitwise(dt, B, L, D, gs, l_h):
+    log("bwd integer %s B=%d L=%d D=%d l_h=%d" % (dt, B, L, D, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = integer_inputs(B, L, D, gs, l_h, dtype, seed=L + 3)
+    dy = integer_inputs(B, L, D, gs, 1, dtype, seed=L + 4)[0]
+    grads = _bwd_gpu(*[t.to(DEV) for t in (q, k, v, h, dy)], gs)
+    ref = oracle.conv_bwd_ref(*[to_np(t) for t in (q, k, v, h, dy)], gs)
+    for name, g, r in zip(("dq", "dk", "dv", "dh"), grads, ref):
+        assert np.array_equal(to_np(g), r), name
+
+
+def test_backward_deterministic():
+    q, k, v, h = gaussian_inputs(2, 1500, 256, 16, 128, torch.bfloat16, seed=21)
+    dy = normal_activation((2, 1500, 256), torch.bfloat16, "cpu", seed=22)
+    dev = [t.to(DEV) for t in (q, k, v, h, dy)]
+    a = _bwd_gpu(*dev, 16)
+    b = _bwd_gpu(*dev, 16)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_autograd_function_matches_the_oracle():
+    log("autograd wrapper")
+    B, L, D, gs, l_h = 1, 500, 64, 16, 100
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, torch.bfloat16, seed=31)
+    dy = normal_activation((B, L, D), torch.bfloat16, "cpu", seed=32)
+    tq, tk, tv, th = (t.to(DEV).requires_grad_(True) for t in (q, k, v, h))
+    y = hc.HyenaConv.apply(tq, tk, tv, th, gs)
+    y.backward(dy.to(DEV))
+    ref, env = _refs(q, k, v, h, dy, gs)
+    for name, t, r, e in zip(("dq", "dk", "dv"), (tq, tk, tv), ref, env):
+        check(to_np(t.grad), r, e, l_h, torch.bfloat16, "autograd " + name)
+    # dh comes back in h's dtype (bf16): one more rounding
+    got = to_np(th.grad)
+    assert np.max(np.abs(got - ref[3])) <= 1e-2 * np.max(np.abs(ref[3]))
+
+
+@pytest.mark.parametrize("name", ["se", "mr"])
+def test_backward_full_workload(name):
+    w = WORKLOADS[name]
+    log("bwd %s full: generate" % name)
+    q, k, v, h = make_inputs(w, DEV)
+    dy = normal_activation((w.B, w.L, w.D), w.torch_dtype, DEV, seed=w.seed + 9)
+    grads = _bwd_gpu(q, k, v, h, dy, w.group_size)
+    log("bwd %s full: oracle" % name)
+    ref, env = _refs(q, k, v, h, dy, w.group_size)
+    _check_all(grads, ref, env, w.l_h, w.torch_dtype, _rows(w.B, w.L, w.D, w.group_size, w.l_h,
+                                                            w.torch_dtype), name)
+
+
+def test_backward_mr_b4_sampled():
+    """dq, dk, dv on exact windows; dh of whole groups (it sums every row)."""
+    w = WORKLOADS["mr_b4"]
+    log("bwd mr_b4: generate")
+    q, k, v, h = make_inputs(w, DEV)
+    dy = normal_activation((w.B, w.L, w.D), w.torch_dtype, DEV, seed=w.seed + 9)
+    dq, dk, dv, dh = _bwd_gpu(q, k, v, h, dy, w.group_size)
+    gs, lh = w.group_size, w.l_h
+    for b, t0, t1 in ((0, 0, 256), (3, w.L // 2 - 100, w.L // 2 + 37), (3, w.L - 256, w.L)):
+        log("  window b=%d [%d,%d)" % (b, t0, t1))
+        s, e = max(0, t0 - (lh - 1)), min(w.L, t1 + lh - 1)  # past for dq, future for dk, dv
+        sl = lambda a: a[b:b + 1, s:e]
+        ref, env = _refs(sl(q), sl(k), sl(v), h, sl(dy), gs)
+        o0, o1 = t0 - s, t1 - s
+        for nm, g, r, en in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, env):
+            check(to_np(g[b:b + 1, t0:t1]), r[:, o0:o1], en[:, o0:o1], lh, w.torch_dtype, "mr_b4 " + nm)
+    for g in (0, 77, w.G - 1):
+        log("  dh group %d" % g)
+        c = slice(g * gs, (g + 1) * gs)
+        ref, env = _refs(q[:, :, c].contiguous(), k[:, :, c].contiguous(), v[:, :, c].contiguous(),
+                         h[g:g + 1], dy[:, :, c].contiguous(), gs)
+        _check_dh(dh[g:g + 1], ref[3], env[3], w.torch_dtype,
+                  _rows(w.B, w.L, w.D, gs, lh, w.torch_dtype), "mr_b4 dh")

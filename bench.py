@@ -64,6 +64,7 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="input copies per layer (cache rotation)")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-naive", action="store_true")
+    ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough CPU budget of the oracle baseline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -284,6 +285,10 @@ def main():
         "host_issue_us_per_step": round(host_issue_us, 2),
     }
 
+    # ---- backward of each layer (outside the forward step's timed region)
+    if not args.skip_backward:
+        out["backward"] = backward_rates(layers, sets, stream, max(5, K // 8))
+
     # ---- attainable streaming rate on this GPU (same bytes, no convolution)
     out["stream_reference"] = stream_reference(layers[-1], sets[-1], stream, max(10, K // 4))
 
@@ -297,6 +302,56 @@ def main():
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def backward_rates(layers, sets, stream, reps):
+    """Time hyena_conv_bwd (dq, dk, dv, dh) per layer on rotated inputs.
+
+    Minimal traffic of the backward is 14 B per token*channel in bf16 (q, k,
+    v, dy read once; dq, dk, dv written once); the library's three kernels
+    move 28 B (dq kernel: dy, k, v -> dq; reversed kernel: dy, q, v, k ->
+    dk, dv; filter-gradient pass: q, k, v, dy).
+    """
+    import torch
+    import gated_convolution_sequence_amd as hc
+    from workloads import normal_activation
+    res = {}
+    for li, w in enumerate(layers):
+        per = sets[li]
+        dys = [normal_activation((w.B, w.L, w.D), w.torch_dtype, per[0][0].device, w.seed + 9 + i)
+               for i in range(len(per))]
+        code = hc.DTYPE_BF16 if w.dtype == "bf16" else hc.DTYPE_F32
+        dq, dk, dv = (torch.empty_like(per[0][0]) for _ in range(3))
+        dh = torch.empty((w.G, w.l_h), dtype=torch.float32, device=per[0][0].device)
+        ws_n = hc.bwd_workspace_bytes(w.B, w.L, w.D, w.group_size, w.l_h, code)
+        ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=per[0][0].device)
+        fn = hc.lib().hyena_conv_bwd
+
+        def call(i):
+            q, k, v, h, _ = per[i % len(per)]
+            st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(), dys[i % len(per)].data_ptr(),
+                    w.B, w.L, w.D, w.group_size, w.l_h, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    dh.data_ptr(), ws.data_ptr(), ws_n, code, stream.cuda_stream)
+            if st != 0:
+                raise hc.HyenaError(st, "hyena_conv_bwd")
+        for i in range(3):
+            call(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            call(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        eb = 2 if w.dtype == "bf16" else 4
+        res[w.name] = {"us": round(us, 2), "G_tok_ch_per_s": round(w.elems / (us * 1e-6) / 1e9, 2),
+                       "min_bytes": 7 * eb * w.elems, "moved_bytes": 14 * eb * w.elems,
+                       "GBs_vs_min_bytes": round(7 * eb * w.elems / (us * 1e-6) / 1e9, 1),
+                       "GBs_moved": round(14 * eb * w.elems / (us * 1e-6) / 1e9, 1),
+                       "kernels": 4, "workspace_bytes": ws_n}
+        del dys
+    return res
 
 
 def stream_reference(w, per, stream, reps):

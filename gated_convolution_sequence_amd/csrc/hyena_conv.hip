@@ -47,6 +47,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "hyena_conv.h"
@@ -690,10 +691,231 @@ constexpr int kSpans[] = {1, 2, 4, 8, 16, 32};
 constexpr int kNumSpans = sizeof(kSpans) / sizeof(kSpans[0]);
 template <bool F32> constexpr int kNumSpansFor = F32 ? 3 : kNumSpans;
 
+// ---------------------------------------------------------------------------
+// Chunk-direction forward, for group sizes that are not a multiple of 16
+// (down to one filter per channel).  Page "04. hardware-aware convolution
+// kernels", section 6: without grouping the GEMM is formed along the chunk
+// direction -- the blocks of one channel's filter are shared by every chunk
+// of that channel.  Here, per channel, the MFMA's 16 rows are 16 consecutive
+// sub-chunks of 16 rows (a 256-row block) and its 16 columns the output rows
+// of a sub-chunk: Y^T[sub-chunk][t_out] = X^T[sub-chunk][t_in] H^T[t_in][t_out]
+// with t_in running over the sub-chunk and the l_h - 1 rows before it.  The
+// B operand (this channel's Toeplitz fragment per input step) is shared by the
+// 16 sub-chunks; it is rebuilt from the staged taps channel by channel.
+//
+// A workgroup (8 waves) owns 64 channels (fp32: 32) and a span of NB
+// blocks; each wave takes 8 (fp32: 4) channels in turn.  x = k v of the block and of 32 KH history rows
+// lives in a 384-row LDS ring; the fp32 results are staged row-major in LDS
+// for the q gating and the 16-byte stores.
+// ---------------------------------------------------------------------------
+constexpr int kCdBlock = 256;    // rows per block (16 sub-chunks of 16)
+constexpr int kCdRing = 384;     // x rows resident: a block + 128 history rows
+constexpr int kCdTapOff = 32;    // tap staging: index = tap + 32, taps -31 .. 159
+constexpr int kCdTaps = 192;
+
+template <bool F32> struct CdTr {
+    static constexpr int EB = F32 ? 4 : 2;
+    static constexpr int SLAB = F32 ? 32 : 64;           // channels per workgroup (LDS budget)
+    static constexpr int VEC = 16 / EB;                  // channels per 16-byte access
+    static constexpr int PITCH = SLAB * EB;              // LDS bytes per x row
+    static constexpr int TPR = PITCH / 16;               // threads per row
+    static constexpr int RPL = kThreads / TPR;           // rows per load
+    static constexpr int NLD = kCdBlock / RPL;           // loads per tensor per block
+    static constexpr int SEGS = PITCH / 16;
+};
+
+template <bool F32, int KH, int NB>
+__global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
+    using T = CdTr<F32>;
+    constexpr int kCdSlab = T::SLAB;
+    constexpr int HROWS = 32 * KH;
+    constexpr int ST_PITCH = kCdSlab * 4;
+    typedef typename std::conditional<F32, float, uint16_t>::type tap_t;
+    __shared__ __attribute__((aligned(16))) unsigned char xr[kCdRing * T::PITCH];
+    __shared__ __attribute__((aligned(16))) unsigned char st[kCdBlock * ST_PITCH];
+    __shared__ tap_t hsd[kCdSlab][kCdTaps];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int l = tid & 63;
+    const int n16 = l & 15;
+    const int q4 = l >> 4;
+
+    int bid = blockIdx.x;
+    const int slab = bid % p.n_slabs;
+    bid /= p.n_slabs;
+    const int spn = bid % p.n_spans;
+    const int b = bid / p.n_spans;
+
+    const int64_t t_begin = (int64_t)spn * NB * kCdBlock;
+    const int64_t t_stop = min(p.L, t_begin + (int64_t)NB * kCdBlock);
+    const int64_t base_row = max((int64_t)0, t_begin - HROWS);
+    const int c_begin = slab * kCdSlab;
+    const int row_bytes = p.D * T::EB;
+    const size_t base_off = ((size_t)b * (size_t)p.L + (size_t)base_row) * (size_t)row_bytes +
+                            (size_t)c_begin * T::EB;
+    const uint32_t nrec = (uint32_t)((t_stop - base_row) * row_bytes - c_begin * T::EB);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc((char *)p.y + base_off, nrec);
+    const int row0 = (int)(t_begin - base_row);  // window row of the span start
+
+    // taps of the slab's 64 channels, zero outside [0, l_h)
+    for (int i = tid; i < kCdSlab * kCdTaps; i += kThreads) {
+        const int dl = i / kCdTaps, tap = i % kCdTaps - kCdTapOff;
+        tap_t hv = 0;
+        if (c_begin + dl < p.D && tap >= 0 && tap < p.l_h) {
+            const size_t o = (size_t)((c_begin + dl) / p.group_size) * p.l_h + tap;
+            hv = ((const tap_t *)p.h)[o];
+        }
+        hsd[dl][i % kCdTaps] = hv;
+    }
+
+    const int ld_row = tid / T::TPR;
+    const int ld_seg = tid % T::TPR;
+    const bool seg_ok = c_begin + ld_seg * T::VEC < p.D;
+    // window-relative rows r (r < 0: before the span's history window)
+    auto off = [&](int r, bool need) -> uint32_t {
+        return (seg_ok && need) ? (uint32_t)(r * row_bytes + ld_seg * 16) : kOOB;
+    };
+    // x ring: row t (relative to the span start) at ring row (t + 128) mod 384,
+    // 16-byte segment XOR ((row >> 4) & 7) so the 16 sub-chunk rows one
+    // operand read touches spread over the banks
+    auto ring_addr = [&](int t, int byte) -> int {
+        const int rr = (t + 128 + 4 * kCdRing) % kCdRing;
+        return rr * T::PITCH + ((((byte >> 4) ^ ((rr >> 4) & 7)) & (T::SEGS - 1)) << 4) + (byte & 15);
+    };
+    constexpr int QUADS = kCdSlab / 4;  // 16-byte fp32 quads per staging row
+    auto st_addr = [&](int row, int quad) -> int { return row * ST_PITCH + ((quad ^ (row & (QUADS - 1))) << 4); };
+    // rows t >= t_end are not written (the history pre-load must not touch
+    // the ring rows of block 0, which other threads write)
+    auto put_x = [&](int t0, const u32x4_t *kd, const u32x4_t *vd, int n, int t_end) {
+        for (int i = 0; i < n; ++i) {
+            const int t = t0 + i * T::RPL + ld_row;
+            if (t >= t_end) continue;
+            u32x4_t xv;
+            if constexpr (F32) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xv[e] = __float_as_uint(__uint_as_float(kd[i][e]) * __uint_as_float(vd[i][e]));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    xv[e] = pack_bf16(bf_lo(kd[i][e]) * bf_lo(vd[i][e]), bf_hi(kd[i][e]) * bf_hi(vd[i][e]));
+            }
+            *(u32x4_t *)(&xr[ring_addr(t, ld_seg * 16)]) = xv;
+        }
+    };
+
+    // The bf16 steps read 32 input rows, so the last sub-chunks of a block
+    // also read the 16 rows after it (with zero taps).  After the first block
+    // those ring rows hold earlier x; before it they are the rows of t in
+    // [-128, -112): give every ring row below the history a finite value.
+    for (int i = tid; i < (128 - HROWS) * T::TPR; i += kThreads)
+        *(u32x4_t *)(&xr[ring_addr(-128 + i / T::TPR, (i % T::TPR) * 16)]) = u32x4_t{0u, 0u, 0u, 0u};
+
+    // history rows before the span: HROWS rows, in loads of RPL rows
+    if constexpr (HROWS > 0) {
+        constexpr int NHL = (HROWS + T::RPL - 1) / T::RPL;
+        u32x4_t hk[NHL], hv[NHL];
+#pragma unroll
+        for (int i = 0; i < NHL; ++i) {
+            const int r = row0 - HROWS + i * T::RPL + ld_row;
+            const uint32_t o = off(r, i * T::RPL + ld_row < HROWS);
+            hk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+            hv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+        }
+        put_x(-HROWS, hk, hv, NHL, 0);
+    }
+
+    u32x4_t kr[2][T::NLD], vr[2][T::NLD], qr[2][T::NLD];
+    auto load_block = [&](int blk, int slot) {
+        const bool need = blk < NB;
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const uint32_t o = off(row0 + blk * kCdBlock + i * T::RPL + ld_row, need);
+            kr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadPolicy));
+            vr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kLoadPolicy));
+            qr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, kLoadPolicy));
+        }
+    };
+    load_block(0, 0);
+
+    using M = Mma<F32>;
+    using frag = typename M::frag;
+    constexpr int NK = (HROWS + 16 + M::ROWS - 1) / M::ROWS;  // input steps: rows -HROWS .. 15
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+        const int slot = blk & 1;
+        const int tb = blk * kCdBlock;  // block start relative to the span start
+        put_x(tb, kr[slot], vr[slot], T::NLD, 1 << 30);
+        load_block(blk + 1, slot ^ 1);
+        __syncthreads();
+        // ---- per channel: 16 sub-chunks x 16 output rows ------------------
+        for (int cl = 0; cl < kCdSlab / kWaves; ++cl) {
+            const int dl = w * (kCdSlab / kWaves) + cl;
+            if (c_begin + dl >= p.D) break;
+            f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            const int cbyte = dl * T::EB;
+#pragma unroll
+            for (int ks = 0; ks < NK; ++ks) {
+                // input rows of this step, relative to the sub-chunk start
+                const int tin0 = -HROWS + ks * M::ROWS;
+                frag A, Bf;
+                if constexpr (F32) {
+                    // A: lane (n16 = sub-chunk, q4 = input row); B: lane (n16 = output row, q4)
+                    A = *(const float *)(&xr[ring_addr(tb + 16 * n16 + tin0 + q4, cbyte)]);
+                    Bf = hsd[dl][n16 - (tin0 + q4) + kCdTapOff];  // fp32 taps
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A, Bf, acc, 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int tin = tin0 + 8 * q4 + j;
+                        A[j] = __builtin_bit_cast(__bf16, *(const uint16_t *)(&xr[ring_addr(tb + 16 * n16 + tin, cbyte)]));
+                        Bf[j] = __builtin_bit_cast(__bf16, (uint16_t)hsd[dl][n16 - tin + kCdTapOff]);
+                    }
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bf, acc, 0, 0, 0);
+                }
+            }
+            // lane holds output row n16 of sub-chunks 4 q4 .. 4 q4 + 3
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * (4 * q4 + i) + n16;
+                *(float *)(&st[st_addr(row, dl >> 2) + 4 * (dl & 3)]) = acc[i];
+            }
+        }
+        __syncthreads();
+        // ---- epilogue: y = q * acc, row-major, 16-byte stores --------------
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const int row = i * T::RPL + ld_row;
+            u32x4_t yv;
+            const u32x4_t gq = qr[slot][i];
+            if constexpr (F32) {
+                const f32x4_t a = *(const f32x4_t *)(&st[st_addr(row, ld_seg)]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) yv[e] = __float_as_uint(__uint_as_float(gq[e]) * a[e]);
+            } else {
+                const f32x4_t a0 = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg)]);
+                const f32x4_t a1 = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg + 1)]);
+                yv[0] = pack_bf16(bf_lo(gq[0]) * a0[0], bf_hi(gq[0]) * a0[1]);
+                yv[1] = pack_bf16(bf_lo(gq[1]) * a0[2], bf_hi(gq[1]) * a0[3]);
+                yv[2] = pack_bf16(bf_lo(gq[2]) * a1[0], bf_hi(gq[2]) * a1[1]);
+                yv[3] = pack_bf16(bf_lo(gq[3]) * a1[2], bf_hi(gq[3]) * a1[3]);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(yv, ry, off(row0 + tb + row, true), 0, kStorePolicy);
+        }
+        __syncthreads();  // st and the oldest ring rows are rewritten next
+    }
+}
+
 // Kernel families and their compiled span counts (indices into kSpans).
-enum Family { kFwd = 0, kRevDual = 1, kDh = 2 };
+enum Family { kFwd = 0, kRevDual = 1, kDh = 2, kCd = 3 };
+// chunk-direction kernels: spans of 1, 2 or 4 blocks of 256 rows
+constexpr int kCdSpans[] = {1, 2, 4};
 template <bool F32, int Fam> constexpr int kSpanCount =
-    Fam == kFwd ? kNumSpansFor<F32> : Fam == kRevDual ? (F32 ? 2 : 4) : (F32 ? 3 : 5);
+    Fam == kFwd ? kNumSpansFor<F32> : Fam == kRevDual ? (F32 ? 2 : 4) : Fam == kDh ? (F32 ? 3 : 5) : 3;
 
 typedef void (*DhFn)(DhParams);
 template <bool F32, int Fam> struct FnType { typedef KernelFn type; };
@@ -705,13 +927,16 @@ constexpr typename FnType<F32, Fam>::type kernel_of() {
         return hyena_fwd_kernel<F32, KH, kPrefetch<F32>, Sp, false, false>;
     else if constexpr (Fam == kRevDual)
         return hyena_fwd_kernel<F32, KH, kPrefetch<F32>, Sp, true, true>;
-    else
+    else if constexpr (Fam == kDh)
         return hyena_bwd_dh_kernel<F32, KH, Sp>;
+    else
+        return hyena_fwd_cd_kernel<F32, KH, Sp>;
 }
 
 template <bool F32, int Fam, int KH, int... Ss>
 typename FnType<F32, Fam>::type span_table_entry(int si, std::integer_sequence<int, Ss...>) {
-    static constexpr typename FnType<F32, Fam>::type fns[] = {kernel_of<F32, Fam, KH, kSpans[Ss]>()...};
+    static constexpr typename FnType<F32, Fam>::type fns[] = {
+        kernel_of<F32, Fam, KH, (Fam == kCd ? kCdSpans[Ss] : kSpans[Ss])>()...};
     return fns[si];
 }
 
@@ -786,6 +1011,38 @@ int make_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, 
     return HYENA_OK;
 }
 
+// Plan of the chunk-direction kernel (group sizes not a multiple of 16):
+// workgroups own CdTr::SLAB channels and spans of 1, 2 or 4 blocks of 256
+// rows; `span` is reported in 64-row chunks, `span_req` read in chunks too.
+int cd_plan(int64_t B, int64_t L, int64_t D, int64_t l_h, int dtype, int64_t span_req, Plan *pl) {
+    const bool f32 = dtype == HYENA_DTYPE_F32;
+    const int64_t eb = f32 ? 4 : 2;
+    const int64_t slab = f32 ? CdTr<true>::SLAB : CdTr<false>::SLAB;
+    if ((D * eb) % 16 != 0) return HYENA_ERR_UNSUPPORTED;  // 16-byte row segments
+    if (D > INT32_MAX / 16) return HYENA_ERR_UNSUPPORTED;
+    pl->kh = (int)((l_h - 1 + 31) / 32);
+    pl->n_chunks = (L + kChunk - 1) / kChunk;
+    const int64_t n_blocks = (L + kCdBlock - 1) / kCdBlock;
+    pl->n_slabs = (D + slab - 1) / slab;
+    // the 32 KH history rows are re-read once per span: longer spans for
+    // longer filters
+    int64_t want = span_req > 0 ? (span_req * kChunk + kCdBlock - 1) / kCdBlock : (pl->kh <= 1 ? 1 : 4);
+    if (want > n_blocks) want = n_blocks;
+    int si = -1;
+    for (int i = 0; i < 3; ++i) {
+        const int64_t win = ((int64_t)kCdSpans[i] * kCdBlock + 32 * pl->kh) * D * eb;
+        if (win >= kMaxWindowBytes) break;
+        if (i == 0 || kCdSpans[i] <= want) si = i;
+    }
+    if (si < 0) return HYENA_ERR_UNSUPPORTED;
+    pl->span_index = si;
+    pl->span = (int64_t)kCdSpans[si] * (kCdBlock / kChunk);
+    pl->n_spans = (n_blocks + kCdSpans[si] - 1) / kCdSpans[si];
+    pl->workgroups = pl->n_spans * pl->n_slabs * B;
+    if (pl->workgroups > INT32_MAX || pl->n_spans > INT32_MAX) return HYENA_ERR_UNSUPPORTED;
+    return HYENA_OK;
+}
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
@@ -805,7 +1062,8 @@ int hyena_conv_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t
         return HYENA_OK;
     }
     Plan pl;
-    st = make_plan(B, L, D, group_size, l_h, dtype, span_chunks, &pl);
+    st = group_size % kTile != 0 ? cd_plan(B, L, D, l_h, dtype, span_chunks, &pl)
+                                 : make_plan(B, L, D, group_size, l_h, dtype, span_chunks, &pl);
     if (st != HYENA_OK) return st;
     if (span_out) *span_out = pl.span;
     if (workgroups_out) *workgroups_out = pl.workgroups;
@@ -837,8 +1095,11 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
         const size_t pbytes = (size_t)B * (size_t)P * (size_t)D * eb;
         if (overlaps(out, nbytes, kp, pbytes) || overlaps(out, nbytes, vp, pbytes)) return HYENA_ERR_ALIAS;
     }
+    const bool chunk_dir = group_size % kTile != 0;
+    if (chunk_dir && P > 0) return HYENA_ERR_UNSUPPORTED;  // history prefix: grouped path only
     Plan pl;
-    st = make_plan(B, L, D, group_size, l_h, dtype, span_chunks, &pl);
+    st = chunk_dir ? cd_plan(B, L, D, l_h, dtype, span_chunks, &pl)
+                   : make_plan(B, L, D, group_size, l_h, dtype, span_chunks, &pl);
     if (st != HYENA_OK) return st;
 
     Params p;
@@ -854,8 +1115,11 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
     p.P = (int32_t)P;
     p.g2 = nullptr;
     p.y2 = nullptr;
-    KernelFn fn = dtype == HYENA_DTYPE_F32 ? pick_kernel<true, kFwd>(pl.kh, pl.span_index)
-                                           : pick_kernel<false, kFwd>(pl.kh, pl.span_index);
+    const bool f32 = dtype == HYENA_DTYPE_F32;
+    KernelFn fn = chunk_dir ? (f32 ? pick_kernel<true, kCd>(pl.kh, pl.span_index)
+                                   : pick_kernel<false, kCd>(pl.kh, pl.span_index))
+                            : (f32 ? pick_kernel<true, kFwd>(pl.kh, pl.span_index)
+                                   : pick_kernel<false, kFwd>(pl.kh, pl.span_index));
     hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(kThreads), 0, (hipStream_t)stream, p);
     if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
     return HYENA_OK;
@@ -1014,7 +1278,7 @@ const char *hyena_conv_strerror(int status) {
     case HYENA_ERR_FILTER_LEN: return "l_h must be in [1, 128]";
     case HYENA_ERR_ALIGN: return "q, k, v and out must be 16-byte aligned; h element aligned";
     case HYENA_ERR_ALIAS: return "out overlaps an input";
-    case HYENA_ERR_UNSUPPORTED: return "group_size must be a multiple of 16 (or the shape is too large to address)";
+    case HYENA_ERR_UNSUPPORTED: return "unsupported case (backward and history prefix need group_size a multiple of 16; rows must be a multiple of 16 bytes; or the shape is too large to address)";
     case HYENA_ERR_LAUNCH: return "kernel launch failed";
     case HYENA_ERR_DTYPE: return "unknown dtype code";
     case HYENA_ERR_WORKSPACE: return "workspace missing or smaller than hyena_conv_bwd_workspace reports";

@@ -23,6 +23,16 @@
  * chunk n-2 (Y_n = H0 X_n + H1 X_{n-1} + H2 X_{n-2}); the library includes
  * that term, so the result is the convolution above for every l_h <= 128.
  *
+ * Grouping: any group_size that divides D, down to one filter per channel.
+ * When group_size is a multiple of 16 the channels of a group form the
+ * matrix-core dimension (section 4 of the page above: one filter per group
+ * lets the Toeplitz factors be shared across its channels).  Otherwise the
+ * work is laid out along the chunk direction instead (same page, section 6):
+ * per channel, 16 consecutive 16-row sub-chunks share each Toeplitz block.
+ * That second layout needs D * element size to be a multiple of 16 bytes,
+ * and covers the plain forward only: the history-prefix forward and the
+ * backward return HYENA_ERR_UNSUPPORTED unless group_size % 16 == 0.
+ *
  * Layout (all row-major, no strides):
  *   q, k, v, out : [B, L, D], D contiguous.
  *   h            : [D / group_size, l_h], taps contiguous.
@@ -62,7 +72,7 @@ enum hyena_status {
     HYENA_ERR_FILTER_LEN = -4,  /* l_h outside [1, 128] */
     HYENA_ERR_ALIGN = -5,       /* q, k, v or out not 16-byte aligned, h not element aligned */
     HYENA_ERR_ALIAS = -6,       /* out overlaps an input (q, k, v, h, k_prev, v_prev) */
-    HYENA_ERR_UNSUPPORTED = -7, /* group_size not a multiple of 16, or a shape the kernel cannot address */
+    HYENA_ERR_UNSUPPORTED = -7, /* a case outside the kernels' reach (see "Grouping"), or a shape they cannot address */
     HYENA_ERR_LAUNCH = -8,      /* the HIP runtime reported an error at launch */
     HYENA_ERR_DTYPE = -9,       /* unknown element-type code */
     HYENA_ERR_WORKSPACE = -10   /* workspace missing or too small */
@@ -87,7 +97,9 @@ int hyena_conv_fwd_f32(const void *q, const void *k, const void *v,
 
 /* Either forward with an explicit work split: `dtype` is a hyena_dtype and
  * `span_chunks` is the number of consecutive 64-row chunks one workgroup
- * walks (0 = the library's choice, clamped to [1, ceil(L/64)]).  The result
+ * walks (0 = the library's choice, clamped to [1, ceil(L/64)]; when
+ * group_size % 16 != 0 the walk is in 256-row blocks of 1, 2 or 4, and the
+ * request is rounded to one of those).  The result
  * does not depend on `span_chunks`; it exists for tuning and for tests that
  * cover spans which do not divide the chunk count. */
 int hyena_conv_fwd_ex(const void *q, const void *k, const void *v,

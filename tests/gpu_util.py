@@ -17,6 +17,7 @@ import sys
 import numpy as np
 import torch
 
+import gated_convolution_sequence_amd as hc
 import oracle
 
 DEV = torch.device("cuda:0")
@@ -65,3 +66,15 @@ def check(y: np.ndarray, ref: np.ndarray, env: np.ndarray, l_h: int, dtype: torc
         raise AssertionError("%s: elementwise bound broken at %s: y=%r ref=%r env=%r" % (
             what, tuple(i), y[tuple(i)], ref[tuple(i)], env[tuple(i)]))
     return emax / scale if scale > 0 else 0.0
+
+
+def run(q, k, v, h, gs, span=0, pad=16):
+    """Forward through the C ABI into a NaN-filled output with canaries on both sides."""
+    n = q.numel()
+    big = torch.full((n + 2 * pad,), 7.0, dtype=q.dtype, device=q.device)
+    out = big[pad:pad + n].view(q.shape)
+    out.fill_(float("nan"))
+    hc.conv_fwd(q, k, v, h, gs, out=out, span_chunks=span)
+    torch.cuda.synchronize()
+    assert torch.all(big[:pad] == 7.0) and torch.all(big[pad + n:] == 7.0), "write outside out"
+    return out

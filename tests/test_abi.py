@@ -68,7 +68,8 @@ def _call(q=P["q"], k=P["k"], v=P["v"], h=P["h"], B=1, L=128, D=64, gs=16, l_h=7
     (dict(dtype=hc.DTYPE_F32, h=P["h"] + 2), -5),
     (dict(out=P["q"]), -6), (dict(out=P["k"] + 64), -6), (dict(out=P["v"] - 16), -6),
     (dict(out=P["h"] - 64), -6),
-    (dict(D=64, gs=8), -7), (dict(D=24, gs=1), -7), (dict(D=96, gs=24), -7),
+    # group sizes that are not a multiple of 16 need 16-byte rows
+    (dict(D=12, gs=1), -7), (dict(D=36, gs=4), -7), (dict(D=6, gs=3, dtype=hc.DTYPE_F32), -7),
     (dict(dtype=2), -9), (dict(dtype=-1), -9),
 ])
 def test_host_validation_rejects_before_any_gpu_call(kw, code):
@@ -88,7 +89,7 @@ def test_error_precedence_shape_checks_come_first():
 
 def test_binding_raises_with_status():
     with pytest.raises(hc.HyenaError) as ei:
-        hc.plan(1, 128, 64, 8, 7)
+        hc.plan(1, 128, 12, 1, 7)
     assert ei.value.status == -7
 
 
@@ -106,6 +107,30 @@ def test_plan_split(B, L, D, l_h, dtype, span, expect_span):
     assert s == expect_span
     chunks = -(-L // 64)
     assert wgs == B * (-(-D // hc.SLAB)) * (-(-chunks // s))
+
+
+@pytest.mark.parametrize("B,L,D,gs,l_h,dtype,span,expect_span", [
+    # group sizes off the 16-channel tile: walks of 1, 2 or 4 blocks of 256
+    # rows (4, 8 or 16 chunks), one block for short filters, four for long
+    (1, 8192, 4096, 1, 7, 0, 0, 4), (1, 8192, 4096, 1, 128, 0, 0, 16),
+    (1, 8192, 4096, 8, 33, 1, 0, 4), (1, 8192, 4096, 8, 34, 1, 0, 16), (2, 1000, 96, 3, 7, 1, 3, 4),
+    (1, 1000, 64, 1, 7, 0, 9, 8), (1, 100, 64, 1, 128, 0, 0, 4),
+    (1, 1000, 72, 24, 65, 0, 0, 16), (1, 1 << 20, 4096, 2, 2, 0, 1000, 16),
+])
+def test_plan_split_chunk_direction(B, L, D, gs, l_h, dtype, span, expect_span):
+    s, wgs = hc.plan(B, L, D, gs, l_h, dtype, span)
+    assert s == expect_span
+    slab = 32 if dtype == hc.DTYPE_F32 else 64
+    blocks = -(-L // 256)
+    assert wgs == B * (-(-D // slab)) * (-(-blocks // (s // 4)))
+
+
+def test_plan_chunk_direction_keeps_the_window_addressable():
+    # (blocks * 256 + history) * D * 2 < 2^31: four blocks no longer fit
+    s, _ = hc.plan(1, 1 << 16, 1 << 20, 1, 128, hc.DTYPE_BF16, 0)
+    assert s == 8 and (2 * 256 + 128) * (1 << 20) * 2 < 1 << 31
+    with pytest.raises(hc.HyenaError):
+        hc.plan(1, 256, 1 << 22, 2, 7, hc.DTYPE_F32, 0)
 
 
 def test_plan_keeps_the_window_addressable():

@@ -1,0 +1,151 @@
+"""GPU parity of the chunk-direction forward (group sizes off the 16-channel tile).
+
+A group_size that is not a multiple of 16 -- down to one filter per channel
+-- is computed with the sub-chunks of one channel as the matrix-core
+dimension instead of the channels of a group.  These tests run it through
+the same C ABI (hyena_conv_fwd_ex via the binding) and hold it to the same
+bar as the grouped path (tests/gpu_util.py): the gate plus the elementwise
+rounding bound against the fp64 oracle, bitwise on integer inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_convolution_sequence_amd as hc
+import oracle
+from gpu_util import DEV, check, log, ref_and_envelope, run, to_np
+from workloads import WORKLOADS, gaussian_inputs, integer_inputs, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    hc.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+# B, L, D, group_size, l_h, span (chunks of 64; rounded to 1, 2 or 4 blocks
+# of 256).  Ragged L against the 256-row block and the 16-row sub-chunk,
+# partial channel slabs (64 channels bf16, 32 fp32), every history depth.
+CD_EDGE = [
+    (1, 1, 8, 1, 1, 0),
+    (1, 6, 8, 2, 4, 0),
+    (1, 63, 24, 3, 7, 0),
+    (1, 256, 64, 1, 33, 0),
+    (1, 257, 72, 8, 34, 0),
+    (2, 255, 72, 24, 65, 4),
+    (1, 1000, 64, 1, 128, 0),
+    (1, 1000, 128, 4, 128, 8),
+    (3, 333, 96, 3, 100, 16),
+    (1, 1100, 40, 5, 2, 4),
+    (1, 2048, 200, 8, 127, 0),
+    (1, 513, 8, 8, 97, 8),
+    (2, 700, 48, 1, 66, 16),
+    (1, 4096, 256, 2, 128, 0),
+    (1, 17, 16, 1, 16, 0),
+    (1, 272, 32, 2, 17, 4),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h,span", CD_EDGE)
+def test_chunk_direction_edge_shapes_gaussian(dt, B, L, D, gs, l_h, span):
+    log("cd %s B=%d L=%d D=%d gs=%d l_h=%d span=%d" % (dt, B, L, D, gs, l_h, span))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B * 7000 + L + 3 * l_h + gs)
+    y = run(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), gs, span)
+    ref, env = ref_and_envelope(q, k, v, h, gs)
+    check(to_np(y), ref, env, l_h, dtype, "cd edge")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h,span", [
+    (1, 6, 8, 1, 4, 0), (1, 1000, 64, 1, 128, 0), (2, 777, 96, 3, 7, 4),
+    (1, 2049, 128, 8, 66, 8), (3, 130, 24, 24, 33, 0), (1, 4096, 512, 2, 128, 16),
+])
+def test_chunk_direction_integer_inputs_bitwise(dt, B, L, D, gs, l_h, span):
+    log("cd integer %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = integer_inputs(B, L, D, gs, l_h, dtype, seed=L + D + gs)
+    y = run(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), gs, span)
+    ref = oracle.conv_fwd_ref(to_np(q), to_np(k), to_np(v), to_np(h), gs)
+    assert np.array_equal(to_np(y), ref)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_paired_filters_match_the_grouped_path(dt):
+    """group_size 8 with equal filters in each pair is group_size 16: on integer
+    inputs the chunk-direction and grouped kernels must agree bit for bit."""
+    dtype = DTYPES[dt]
+    B, L, D, l_h = 2, 1500, 128, 128
+    q, k, v, h16 = integer_inputs(B, L, D, 16, l_h, dtype, seed=77)
+    h8 = torch.repeat_interleave(h16, 2, dim=0).contiguous()
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    log("paired filters %s" % dt)
+    y16 = run(q, k, v, h16.to(DEV), 16).clone()
+    y8 = run(q, k, v, h8.to(DEV), 8)
+    assert torch.equal(y8, y16)
+
+
+@pytest.mark.parametrize("l_h", [1, 16, 17, 33, 64, 65, 128])
+def test_impulses_on_block_and_sub_chunk_seams_reproduce_the_filter(l_h):
+    L, D = 1100, 64
+    seams = [0, 1, 15, 16, 17, 255, 256, 257, 271, 272, 511, 512, 767, 768, 1023, 1024, L - 1]
+    rng = np.random.default_rng(l_h + 1)
+    h = torch.tensor(rng.standard_normal((D, l_h)), dtype=torch.bfloat16)
+    v = torch.zeros(1, L, D, dtype=torch.bfloat16)
+    for d in range(D):
+        v[0, seams[d % len(seams)], d] = 1.0
+    ones = torch.ones_like(v)
+    for span in (0, 4, 8, 16):
+        log("cd impulses l_h=%d span=%d" % (l_h, span))
+        y = to_np(run(ones.to(DEV), ones.to(DEV), v.to(DEV), h.to(DEV), 1, span))
+        ref = oracle.conv_fwd_ref(to_np(ones), to_np(ones), to_np(v), to_np(h), 1)
+        assert np.array_equal(y, ref)
+
+
+def test_chunk_direction_span_independent_and_causal():
+    """Any walk length gives the same bits (same sums in the same order);
+    changing row t0 changes only rows t0 .. t0 + l_h - 1."""
+    B, L, D, gs, l_h = 2, 3000, 192, 1, 128
+    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(B, L, D, gs, l_h, torch.bfloat16, seed=19))
+    log("cd span independence")
+    y0 = run(q, k, v, h, gs).clone()
+    for span in (4, 8, 16, 1000):
+        assert torch.equal(y0, run(q, k, v, h, gs, span)), span
+    t0 = 767
+    v2 = v.clone()
+    v2[:, t0] += 2.0
+    y1 = run(q, k, v2, h, gs)
+    assert torch.equal(y0[:, :t0], y1[:, :t0])
+    assert torch.equal(y0[:, t0 + l_h:], y1[:, t0 + l_h:])
+    assert not torch.equal(y0[:, t0], y1[:, t0])
+
+
+@pytest.mark.parametrize("name", ["se", "mr"])
+def test_one_filter_per_channel_at_full_size(name):
+    """B=1, L=8192, D=4096 with group_size 1 (4096 filters), whole output."""
+    w = WORKLOADS[name].with_(group_size=1)
+    log("cd full %s gs=1: generate" % name)
+    q, k, v, h = make_inputs(w, DEV)
+    y = run(q, k, v, h, 1)
+    log("cd full %s gs=1: oracle" % name)
+    ref, env = ref_and_envelope(q.cpu(), k.cpu(), v.cpu(), h.cpu(), 1)
+    rel = check(to_np(y), ref, env, w.l_h, w.torch_dtype, "cd full " + name)
+    log("cd full %s rel err %.3e" % (name, rel))
+
+
+def test_halo_and_backward_stay_on_the_grouped_path():
+    """The history-prefix forward and the backward reject off-tile groups."""
+    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(1, 128, 64, 8, 7, torch.bfloat16, seed=3))
+    with pytest.raises(hc.HyenaError) as ei:
+        hc.conv_fwd(q, k, v, h, 8, k_prev=k[:, :6].contiguous(), v_prev=v[:, :6].contiguous())
+    assert ei.value.status == -7
+    with pytest.raises(hc.HyenaError) as ei:
+        hc.conv_bwd(q, k, v, h, q, 8)
+    assert ei.value.status == -7

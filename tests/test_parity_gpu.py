@@ -11,7 +11,7 @@ import torch
 
 import gated_convolution_sequence_amd as hc
 import oracle
-from gpu_util import DEV, check, log, nan_like, ref_and_envelope, to_np
+from gpu_util import DEV, check, log, nan_like, ref_and_envelope, run, to_np
 from workloads import WORKLOADS, gaussian_inputs, integer_inputs, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -25,18 +25,6 @@ def gpu():
     hc.lib()
     yield
     torch.cuda.synchronize()
-
-
-def run(q, k, v, h, gs, span=0, pad=16):
-    """Run the library into a NaN-filled output with canaries on both sides."""
-    n = q.numel()
-    big = torch.full((n + 2 * pad,), 7.0, dtype=q.dtype, device=q.device)
-    out = big[pad:pad + n].view(q.shape)
-    out.fill_(float("nan"))
-    hc.conv_fwd(q, k, v, h, gs, out=out, span_chunks=span)
-    torch.cuda.synchronize()
-    assert torch.all(big[:pad] == 7.0) and torch.all(big[pad + n:] == 7.0), "write outside out"
-    return out
 
 
 # ---------------------------------------------------------------------------

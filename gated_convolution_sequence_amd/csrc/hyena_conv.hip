@@ -694,46 +694,57 @@ template <bool F32> constexpr int kNumSpansFor = F32 ? 3 : kNumSpans;
 // ---------------------------------------------------------------------------
 // Chunk-direction forward, for group sizes that are not a multiple of 16
 // (down to one filter per channel).  Page "04. hardware-aware convolution
-// kernels", section 6: without grouping the GEMM is formed along the chunk
-// direction -- the blocks of one channel's filter are shared by every chunk
-// of that channel.  Here, per channel, the MFMA's 16 rows are 16 consecutive
-// sub-chunks of 16 rows (a 256-row block) and its 16 columns the output rows
-// of a sub-chunk: Y^T[sub-chunk][t_out] = X^T[sub-chunk][t_in] H^T[t_in][t_out]
-// with t_in running over the sub-chunk and the l_h - 1 rows before it.  The
-// B operand (this channel's Toeplitz fragment per input step) is shared by the
-// 16 sub-chunks; it is rebuilt from the staged taps channel by channel.
+// kernels", section 6: without grouping, the GEMM is formed along the chunk
+// direction, since the Toeplitz blocks of one channel's filter are the same
+// for every chunk of that channel.  Here, per channel, a 256-row block is
+// cut into 16 sub-chunks of 16 rows, and
+//     Y[t_out][sub-chunk] = H[t_out][t_in] X[t_in][sub-chunk]
+// with t_out the 16 rows of a sub-chunk and t_in the sub-chunk's rows and
+// the l_h - 1 rows before it, in steps of 32 rows (the MFMA's K).  The
+// Toeplitz operand H is shared by all 16 sub-chunks.
 //
-// A workgroup (8 waves) owns 64 channels (fp32: 32) and a span of NB
-// blocks; each wave takes 8 (fp32: 4) channels in turn.  x = k v of the block and of 32 KH history rows
-// lives in a 384-row LDS ring; the fp32 results are staged row-major in LDS
-// for the q gating and the 16-byte stores.
+// A workgroup (8 waves) owns 64 channels (fp32: 32) and a span of NB blocks;
+// wave w takes channels 8w .. 8w + 7 (fp32: 4w .. 4w + 3).  In LDS every
+// channel is a row of times:
+//   * x = k v of the block and the 128 rows before it, in a 384-entry ring,
+//     so that one 16-byte read is 8 (fp32: 4) consecutive times of the B
+//     operand;
+//   * q of the block, overwritten in place by y = q acc, so the gate is
+//     applied in the MFMA's own layout (lane: 4 consecutive times of one
+//     sub-chunk);
+//   * the taps as a table of pairs (h[m], h[m-1]) (fp32: single taps), so an
+//     A operand register is one 4-byte read.
+// Global loads give a thread 4 consecutive rows of 8 (fp32: 4) channels; the
+// thread writes them to LDS per channel, 4 times at once, and the epilogue
+// reads them back the same way, so every global access is a 16-byte row
+// segment.  LDS rows are in 16-byte units XOR-swizzled by the channel's row
+// segment, so the 8 segments of a row land in distinct banks.
 // ---------------------------------------------------------------------------
 constexpr int kCdBlock = 256;    // rows per block (16 sub-chunks of 16)
-constexpr int kCdRing = 384;     // x rows resident: a block + 128 history rows
-constexpr int kCdTapOff = 32;    // tap staging: index = tap + 32, taps -31 .. 159
-constexpr int kCdTaps = 192;
+constexpr int kCdRing = 384;     // ring entries per channel: a block + 128 history rows
+constexpr int kCdTapOff = 32;    // tap tables: entry m + 32 holds tap (pair) m
 
 template <bool F32> struct CdTr {
     static constexpr int EB = F32 ? 4 : 2;
-    static constexpr int SLAB = F32 ? 32 : 64;           // channels per workgroup (LDS budget)
-    static constexpr int VEC = 16 / EB;                  // channels per 16-byte access
-    static constexpr int PITCH = SLAB * EB;              // LDS bytes per x row
-    static constexpr int TPR = PITCH / 16;               // threads per row
-    static constexpr int RPL = kThreads / TPR;           // rows per load
-    static constexpr int NLD = kCdBlock / RPL;           // loads per tensor per block
-    static constexpr int SEGS = PITCH / 16;
+    static constexpr int SLAB = F32 ? 32 : 64;           // channels per workgroup
+    static constexpr int VEC = 16 / EB;                  // channels (or times) per 16 bytes
+    static constexpr int CPW = SLAB / kWaves;            // channels per wave
+    static constexpr int RING_B = kCdRing * EB;          // LDS bytes per channel ring
+    static constexpr int QY_B = kCdBlock * EB;           // LDS bytes per channel gate row
+    static_assert(CPW == VEC, "a wave's channels are one row segment (one swizzle key)");
+    static_assert(SLAB / VEC * (kCdBlock / 4) == kThreads, "4 rows x 16 bytes per thread tile a block");
 };
 
 template <bool F32, int KH, int NB>
 __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
     using T = CdTr<F32>;
-    constexpr int kCdSlab = T::SLAB;
+    constexpr int SLAB = T::SLAB;
     constexpr int HROWS = 32 * KH;
-    constexpr int ST_PITCH = kCdSlab * 4;
-    typedef typename std::conditional<F32, float, uint16_t>::type tap_t;
-    __shared__ __attribute__((aligned(16))) unsigned char xr[kCdRing * T::PITCH];
-    __shared__ __attribute__((aligned(16))) unsigned char st[kCdBlock * ST_PITCH];
-    __shared__ tap_t hsd[kCdSlab][kCdTaps];
+    constexpr int PTN = HROWS + 48;      // tap-table entries per channel
+    constexpr int NPT = (SLAB * PTN + kThreads - 1) / kThreads;
+    __shared__ __attribute__((aligned(16))) unsigned char xr[SLAB * T::RING_B];
+    __shared__ __attribute__((aligned(16))) unsigned char qy[SLAB * T::QY_B];
+    __shared__ uint32_t pt[SLAB * PTN];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -750,7 +761,7 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
     const int64_t t_begin = (int64_t)spn * NB * kCdBlock;
     const int64_t t_stop = min(p.L, t_begin + (int64_t)NB * kCdBlock);
     const int64_t base_row = max((int64_t)0, t_begin - HROWS);
-    const int c_begin = slab * kCdSlab;
+    const int c_begin = slab * SLAB;
     const int row_bytes = p.D * T::EB;
     const size_t base_off = ((size_t)b * (size_t)p.L + (size_t)base_row) * (size_t)row_bytes +
                             (size_t)c_begin * T::EB;
@@ -761,80 +772,55 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
     const __amdgpu_buffer_rsrc_t ry = make_rsrc((char *)p.y + base_off, nrec);
     const int row0 = (int)(t_begin - base_row);  // window row of the span start
 
-    // taps of the slab's 64 channels, zero outside [0, l_h)
-    for (int i = tid; i < kCdSlab * kCdTaps; i += kThreads) {
-        const int dl = i / kCdTaps, tap = i % kCdTaps - kCdTapOff;
-        tap_t hv = 0;
-        if (c_begin + dl < p.D && tap >= 0 && tap < p.l_h) {
-            const size_t o = (size_t)((c_begin + dl) / p.group_size) * p.l_h + tap;
-            hv = ((const tap_t *)p.h)[o];
+    // I/O tile of this thread: rows 4 g4 .. 4 g4 + 3 of a block, channels
+    // VEC sg .. VEC sg + VEC - 1 (one 16-byte row segment).
+    const int sg = tid & 7;
+    const int g4 = tid >> 3;
+    const bool seg_ok = c_begin + sg * T::VEC < p.D;
+    auto off = [&](int r, bool need) -> uint32_t {
+        return (seg_ok && need) ? (uint32_t)(r * row_bytes + sg * 16) : kOOB;
+    };
+    // LDS byte address of time index r in channel ch's row (pitch rb)
+    auto pos = [&](int ch, int r, int rb) -> int {
+        return ch * rb + ((((r / T::VEC) ^ ((ch / T::VEC) & 7))) << 4) + (r % T::VEC) * T::EB;
+    };
+
+    // taps: issued first, so that waiting for them does not wait for the
+    // block loads issued after them
+    uint32_t tap_lo[NPT], tap_hi[NPT];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const int i = tid + j * kThreads;
+        const int dl = i / PTN, m = i % PTN - kCdTapOff;
+        const int ch = c_begin + dl;
+        const bool chok = i < SLAB * PTN && ch < p.D;
+        const size_t hrow = chok ? (size_t)(ch / p.group_size) * p.l_h : 0;
+        if constexpr (F32) {
+            tap_lo[j] = (chok && m >= 0 && m < p.l_h) ? ((const uint32_t *)p.h)[hrow + m] : 0u;
+            tap_hi[j] = 0u;
+        } else {
+            tap_lo[j] = (chok && m >= 0 && m < p.l_h) ? ((const uint16_t *)p.h)[hrow + m] : 0u;
+            tap_hi[j] = (chok && m >= 1 && m <= p.l_h) ? ((const uint16_t *)p.h)[hrow + m - 1] : 0u;
         }
-        hsd[dl][i % kCdTaps] = hv;
     }
 
-    const int ld_row = tid / T::TPR;
-    const int ld_seg = tid % T::TPR;
-    const bool seg_ok = c_begin + ld_seg * T::VEC < p.D;
-    // window-relative rows r (r < 0: before the span's history window)
-    auto off = [&](int r, bool need) -> uint32_t {
-        return (seg_ok && need) ? (uint32_t)(r * row_bytes + ld_seg * 16) : kOOB;
-    };
-    // x ring: row t (relative to the span start) at ring row (t + 128) mod 384,
-    // 16-byte segment XOR ((row >> 4) & 7) so the 16 sub-chunk rows one
-    // operand read touches spread over the banks
-    auto ring_addr = [&](int t, int byte) -> int {
-        const int rr = (t + 128 + 4 * kCdRing) % kCdRing;
-        return rr * T::PITCH + ((((byte >> 4) ^ ((rr >> 4) & 7)) & (T::SEGS - 1)) << 4) + (byte & 15);
-    };
-    constexpr int QUADS = kCdSlab / 4;  // 16-byte fp32 quads per staging row
-    auto st_addr = [&](int row, int quad) -> int { return row * ST_PITCH + ((quad ^ (row & (QUADS - 1))) << 4); };
-    // rows t >= t_end are not written (the history pre-load must not touch
-    // the ring rows of block 0, which other threads write)
-    auto put_x = [&](int t0, const u32x4_t *kd, const u32x4_t *vd, int n, int t_end) {
-        for (int i = 0; i < n; ++i) {
-            const int t = t0 + i * T::RPL + ld_row;
-            if (t >= t_end) continue;
-            u32x4_t xv;
-            if constexpr (F32) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    xv[e] = __float_as_uint(__uint_as_float(kd[i][e]) * __uint_as_float(vd[i][e]));
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    xv[e] = pack_bf16(bf_lo(kd[i][e]) * bf_lo(vd[i][e]), bf_hi(kd[i][e]) * bf_hi(vd[i][e]));
-            }
-            *(u32x4_t *)(&xr[ring_addr(t, ld_seg * 16)]) = xv;
-        }
-    };
-
-    // The bf16 steps read 32 input rows, so the last sub-chunks of a block
-    // also read the 16 rows after it (with zero taps).  After the first block
-    // those ring rows hold earlier x; before it they are the rows of t in
-    // [-128, -112): give every ring row below the history a finite value.
-    for (int i = tid; i < (128 - HROWS) * T::TPR; i += kThreads)
-        *(u32x4_t *)(&xr[ring_addr(-128 + i / T::TPR, (i % T::TPR) * 16)]) = u32x4_t{0u, 0u, 0u, 0u};
-
-    // history rows before the span: HROWS rows, in loads of RPL rows
+    // history: the HROWS rows before the span, in the first HROWS / 4 row groups
+    u32x4_t hk[4], hv[4];
+    const bool hist = g4 < HROWS / 4;
     if constexpr (HROWS > 0) {
-        constexpr int NHL = (HROWS + T::RPL - 1) / T::RPL;
-        u32x4_t hk[NHL], hv[NHL];
 #pragma unroll
-        for (int i = 0; i < NHL; ++i) {
-            const int r = row0 - HROWS + i * T::RPL + ld_row;
-            const uint32_t o = off(r, i * T::RPL + ld_row < HROWS);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t o = off(row0 - HROWS + 4 * g4 + i, hist);
             hk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
             hv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
         }
-        put_x(-HROWS, hk, hv, NHL, 0);
     }
-
-    u32x4_t kr[2][T::NLD], vr[2][T::NLD], qr[2][T::NLD];
+    u32x4_t kr[2][4], vr[2][4], qr[2][4];
     auto load_block = [&](int blk, int slot) {
         const bool need = blk < NB;
 #pragma unroll
-        for (int i = 0; i < T::NLD; ++i) {
-            const uint32_t o = off(row0 + blk * kCdBlock + i * T::RPL + ld_row, need);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t o = off(row0 + blk * kCdBlock + 4 * g4 + i, need);
             kr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadPolicy));
             vr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kLoadPolicy));
             qr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, kLoadPolicy));
@@ -842,71 +828,147 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
     };
     load_block(0, 0);
 
-    using M = Mma<F32>;
-    using frag = typename M::frag;
-    constexpr int NK = (HROWS + 16 + M::ROWS - 1) / M::ROWS;  // input steps: rows -HROWS .. 15
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+        const int i = tid + j * kThreads;
+        if (i < SLAB * PTN) pt[i] = tap_lo[j] | (tap_hi[j] << 16);
+    }
+
+    // x = k v of rows 4 g4 .. 4 g4 + 3 -> ring index r (a multiple of 4)
+    auto put_x = [&](int r, const u32x4_t *kd, const u32x4_t *vd) {
+#pragma unroll
+        for (int e = 0; e < T::VEC; ++e) {
+            const int ch = sg * T::VEC + e;
+            if constexpr (F32) {
+                u32x4_t xv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xv[i] = __float_as_uint(__uint_as_float(kd[i][e]) * __uint_as_float(vd[i][e]));
+                *(u32x4_t *)(&xr[pos(ch, r, T::RING_B)]) = xv;
+            } else {
+                const int d = e >> 1;
+                float x4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    x4[i] = (e & 1) ? bf_hi(kd[i][d]) * bf_hi(vd[i][d]) : bf_lo(kd[i][d]) * bf_lo(vd[i][d]);
+                const u32x2_t xv = {pack_bf16(x4[0], x4[1]), pack_bf16(x4[2], x4[3])};
+                *(u32x2_t *)(&xr[pos(ch, r, T::RING_B)]) = xv;
+            }
+        }
+    };
+    // q of rows 4 g4 .. 4 g4 + 3 -> the gate rows (time 4 g4 of the block)
+    auto put_q = [&](const u32x4_t *qd) {
+#pragma unroll
+        for (int e = 0; e < T::VEC; ++e) {
+            const int ch = sg * T::VEC + e;
+            if constexpr (F32) {
+                const u32x4_t qv = {qd[0][e], qd[1][e], qd[2][e], qd[3][e]};
+                *(u32x4_t *)(&qy[pos(ch, 4 * g4, T::QY_B)]) = qv;
+            } else {
+                const int d = e >> 1;
+                uint32_t h4[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) h4[i] = (e & 1) ? (qd[i][d] >> 16) : (qd[i][d] & 0xffffu);
+                const u32x2_t qv = {h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16)};
+                *(u32x2_t *)(&qy[pos(ch, 4 * g4, T::QY_B)]) = qv;
+            }
+        }
+    };
+    auto ring_of = [](int t) -> int { return (t + 128 + 4 * kCdRing) % kCdRing; };
+
+    if constexpr (HROWS > 0) {
+        if (hist) put_x(ring_of(-HROWS + 4 * g4), hk, hv);
+    }
+
+    // MFMA lane roles: A = taps (row n16 = output row of a sub-chunk),
+    // B = x (column n16 = sub-chunk); the accumulator holds output rows
+    // 4 q4 .. 4 q4 + 3 of sub-chunk n16.
+    const int lane_t8 = 16 * n16 + 8 * q4;  // B rows of a K = 32 step (times)
+    const int lane_t4 = 16 * n16 + 4 * q4;  // accumulator rows (fp32: B rows of a group)
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
         const int slot = blk & 1;
         const int tb = blk * kCdBlock;  // block start relative to the span start
-        put_x(tb, kr[slot], vr[slot], T::NLD, 1 << 30);
+        put_x(ring_of(tb + 4 * g4), kr[slot], vr[slot]);
+        put_q(qr[slot]);
         load_block(blk + 1, slot ^ 1);
         __syncthreads();
-        // ---- per channel: 16 sub-chunks x 16 output rows ------------------
-        for (int cl = 0; cl < kCdSlab / kWaves; ++cl) {
-            const int dl = w * (kCdSlab / kWaves) + cl;
+#pragma unroll
+        for (int cl = 0; cl < T::CPW; ++cl) {
+            const int dl = w * T::CPW + cl;
             if (c_begin + dl >= p.D) break;
+            const uint32_t *ptc = pt + dl * PTN;
             f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-            const int cbyte = dl * T::EB;
+            if constexpr (F32) {
+                // groups of 16 input rows, 4 MFMAs each; in MFMA s lane q4
+                // takes input row 4 q4 + s of the group
 #pragma unroll
-            for (int ks = 0; ks < NK; ++ks) {
-                // input rows of this step, relative to the sub-chunk start
-                const int tin0 = -HROWS + ks * M::ROWS;
-                frag A, Bf;
-                if constexpr (F32) {
-                    // A: lane (n16 = sub-chunk, q4 = input row); B: lane (n16 = output row, q4)
-                    A = *(const float *)(&xr[ring_addr(tb + 16 * n16 + tin0 + q4, cbyte)]);
-                    Bf = hsd[dl][n16 - (tin0 + q4) + kCdTapOff];  // fp32 taps
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A, Bf, acc, 0, 0, 0);
-                } else {
+                for (int gi = 0; gi <= 2 * KH; ++gi) {
+                    const int tg = -HROWS + 16 * gi;
+                    int r = lane_t4 + ring_of(tb + tg);
+                    if (r >= kCdRing) r -= kCdRing;
+                    const f32x4_t xv = *(const f32x4_t *)(&xr[pos(dl, r, T::RING_B)]);
+                    const int c = n16 - 4 * q4 - tg + kCdTapOff;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int tin = tin0 + 8 * q4 + j;
-                        A[j] = __builtin_bit_cast(__bf16, *(const uint16_t *)(&xr[ring_addr(tb + 16 * n16 + tin, cbyte)]));
-                        Bf[j] = __builtin_bit_cast(__bf16, (uint16_t)hsd[dl][n16 - tin + kCdTapOff]);
-                    }
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bf, acc, 0, 0, 0);
+                    for (int s = 0; s < 4; ++s)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(ptc[c - s]), xv[s], acc, 0, 0, 0);
+                }
+            } else {
+                // steps of 32 input rows; the last (ks = KH) covers rows
+                // 0 .. 31 of the sub-chunk, of which 16 .. 31 have zero taps:
+                // lanes q4 >= 2 then read rows 0 .. 15 again (finite values
+                // inside the block) instead of rows past it
+#pragma unroll
+                for (int ks = 0; ks <= KH; ++ks) {
+                    const int tin0 = -HROWS + 32 * ks;
+                    int r = (ks == KH ? lane_t8 - ((q4 & 2) << 3) : lane_t8) + ring_of(tb + tin0);
+                    if (r >= kCdRing) r -= kCdRing;
+                    const u32x4_t xv = *(const u32x4_t *)(&xr[pos(dl, r, T::RING_B)]);
+                    const int c = n16 - 8 * q4 - tin0 + kCdTapOff;
+                    const u32x4_t hv4 = {ptc[c], ptc[c - 2], ptc[c - 4], ptc[c - 6]};
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hv4),
+                                                                  __builtin_bit_cast(bf16x8_t, xv), acc, 0, 0, 0);
                 }
             }
-            // lane holds output row n16 of sub-chunks 4 q4 .. 4 q4 + 3
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = 16 * (4 * q4 + i) + n16;
-                *(float *)(&st[st_addr(row, dl >> 2) + 4 * (dl & 3)]) = acc[i];
+            // y = q acc in place of q
+            const int qa = pos(dl, lane_t4, T::QY_B);
+            if constexpr (F32) {
+                const f32x4_t qv = *(const f32x4_t *)(&qy[qa]);
+                *(f32x4_t *)(&qy[qa]) = qv * acc;
+            } else {
+                const u32x2_t qv = *(const u32x2_t *)(&qy[qa]);
+                const u32x2_t yv = {pack_bf16(bf_lo(qv[0]) * acc[0], bf_hi(qv[0]) * acc[1]),
+                                    pack_bf16(bf_lo(qv[1]) * acc[2], bf_hi(qv[1]) * acc[3])};
+                *(u32x2_t *)(&qy[qa]) = yv;
             }
         }
         __syncthreads();
-        // ---- epilogue: y = q * acc, row-major, 16-byte stores --------------
+        // ---- epilogue: rows 4 g4 .. 4 g4 + 3 back to row-major, 16-byte stores
+        u32x4_t yrow[4];
+        if constexpr (F32) {
 #pragma unroll
-        for (int i = 0; i < T::NLD; ++i) {
-            const int row = i * T::RPL + ld_row;
-            u32x4_t yv;
-            const u32x4_t gq = qr[slot][i];
-            if constexpr (F32) {
-                const f32x4_t a = *(const f32x4_t *)(&st[st_addr(row, ld_seg)]);
+            for (int e = 0; e < 4; ++e) {
+                const u32x4_t cv = *(const u32x4_t *)(&qy[pos(sg * 4 + e, 4 * g4, T::QY_B)]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) yv[e] = __float_as_uint(__uint_as_float(gq[e]) * a[e]);
-            } else {
-                const f32x4_t a0 = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg)]);
-                const f32x4_t a1 = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg + 1)]);
-                yv[0] = pack_bf16(bf_lo(gq[0]) * a0[0], bf_hi(gq[0]) * a0[1]);
-                yv[1] = pack_bf16(bf_lo(gq[1]) * a0[2], bf_hi(gq[1]) * a0[3]);
-                yv[2] = pack_bf16(bf_lo(gq[2]) * a1[0], bf_hi(gq[2]) * a1[1]);
-                yv[3] = pack_bf16(bf_lo(gq[3]) * a1[2], bf_hi(gq[3]) * a1[3]);
+                for (int i = 0; i < 4; ++i) yrow[i][e] = cv[i];
             }
-            __builtin_amdgcn_raw_buffer_store_b128(yv, ry, off(row0 + tb + row, true), 0, kStorePolicy);
+        } else {
+            u32x2_t cv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) cv[e] = *(const u32x2_t *)(&qy[pos(sg * 8 + e, 4 * g4, T::QY_B)]);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const u32x2_t a = cv[2 * d], c = cv[2 * d + 1];
+                yrow[0][d] = (a[0] & 0xffffu) | (c[0] << 16);
+                yrow[1][d] = (a[0] >> 16) | (c[0] & 0xffff0000u);
+                yrow[2][d] = (a[1] & 0xffffu) | (c[1] << 16);
+                yrow[3][d] = (a[1] >> 16) | (c[1] & 0xffff0000u);
+            }
         }
-        __syncthreads();  // st and the oldest ring rows are rewritten next
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(yrow[i], ry, off(row0 + tb + 4 * g4 + i, true), 0, kStorePolicy);
+        __syncthreads();  // the gate rows and the oldest ring entries are rewritten next
     }
 }
 

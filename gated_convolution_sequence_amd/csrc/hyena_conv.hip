@@ -96,6 +96,7 @@ struct Params {
     int32_t n_spans;    // spans per batch row
     int32_t n_slabs;    // channel slabs
     int32_t P;          // prefix rows in kp / vp (0: the history before row 0 is zero)
+    int32_t span_blocks; // chunk-direction kernel: 256-row blocks per span
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -735,7 +736,7 @@ template <bool F32> struct CdTr {
     static_assert(SLAB / VEC * (kCdBlock / 4) == kThreads, "4 rows x 16 bytes per thread tile a block");
 };
 
-template <bool F32, int KH, int NB>
+template <bool F32, int KH>
 __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
     using T = CdTr<F32>;
     constexpr int SLAB = T::SLAB;
@@ -758,19 +759,25 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
     const int spn = bid % p.n_spans;
     const int b = bid / p.n_spans;
 
-    const int64_t t_begin = (int64_t)spn * NB * kCdBlock;
-    const int64_t t_stop = min(p.L, t_begin + (int64_t)NB * kCdBlock);
-    const int64_t base_row = max((int64_t)0, t_begin - HROWS);
+    const int64_t t_begin = (int64_t)spn * p.span_blocks * kCdBlock;
+    const int64_t t_stop = min(p.L, t_begin + (int64_t)p.span_blocks * kCdBlock);
+    const int nb = (int)((t_stop - t_begin + kCdBlock - 1) / kCdBlock);  // blocks of this span
     const int c_begin = slab * SLAB;
     const int row_bytes = p.D * T::EB;
-    const size_t base_off = ((size_t)b * (size_t)p.L + (size_t)base_row) * (size_t)row_bytes +
-                            (size_t)c_begin * T::EB;
-    const uint32_t nrec = (uint32_t)((t_stop - base_row) * row_bytes - c_begin * T::EB);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + base_off, nrec);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + base_off, nrec);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + base_off, nrec);
-    const __amdgpu_buffer_rsrc_t ry = make_rsrc((char *)p.y + base_off, nrec);
-    const int row0 = (int)(t_begin - base_row);  // window row of the span start
+    const size_t batch_off = (size_t)b * (size_t)p.L * (size_t)row_bytes + (size_t)c_begin * T::EB;
+    // Buffer window of `rows` rows of this slab from row r0 (r0 >= 0,
+    // rows >= 0): an offset at or past its end reads 0 and drops writes.  An
+    // empty window (the history of a span at row 0) has no records at all:
+    // its size must not go negative, or the out-of-bounds offset kOOB would
+    // land inside it.  Base and size are made wave-uniform explicitly, so the
+    // descriptor lives in scalar registers.
+    auto window = [&](const void *base, int64_t r0, int rows) {
+        const int n = rows * row_bytes - c_begin * T::EB;
+        const uint64_t a = (uint64_t)((const char *)base + batch_off + (size_t)r0 * (size_t)row_bytes);
+        const uint64_t au = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+        return make_rsrc((const void *)au, (uint32_t)__builtin_amdgcn_readfirstlane(n > 0 ? n : 0));
+    };
 
     // I/O tile of this thread: rows 4 g4 .. 4 g4 + 3 of a block, channels
     // VEC sg .. VEC sg + VEC - 1 (one 16-byte row segment).
@@ -785,8 +792,42 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
         return ch * rb + ((((r / T::VEC) ^ ((ch / T::VEC) & 7))) << 4) + (r % T::VEC) * T::EB;
     };
 
-    // taps: issued first, so that waiting for them does not wait for the
-    // block loads issued after them
+    u32x4_t k0[4], v0[4], q0[4], k1[4], v1[4], q1[4];
+    auto load_block = [&](int blk, u32x4_t *kd, u32x4_t *vd, u32x4_t *qd) {
+        const int64_t r0 = t_begin + (int64_t)blk * kCdBlock;
+        const int rows = min(kCdBlock, (int)(t_stop - r0));
+        const __amdgpu_buffer_rsrc_t rq = window(p.q, r0, rows);
+        const __amdgpu_buffer_rsrc_t rk = window(p.k, r0, rows);
+        const __amdgpu_buffer_rsrc_t rv = window(p.v, r0, rows);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t o = off(4 * g4 + i, true);
+            kd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadPolicy));
+            vd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kLoadPolicy));
+            qd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, kLoadPolicy));
+        }
+    };
+    // HBM requests first: the first block, then the history rows before the
+    // span (in the first HROWS / 4 row groups), then the taps (L2-resident)
+    load_block(0, k0, v0, q0);
+    u32x4_t hk[4], hv[4];
+    const bool hist = g4 < HROWS / 4;
+    if constexpr (HROWS > 0) {
+        const int64_t hr0 = max((int64_t)0, t_begin - HROWS);
+        const __amdgpu_buffer_rsrc_t rk = window(p.k, hr0, (int)(t_begin - hr0));
+        const __amdgpu_buffer_rsrc_t rv = window(p.v, hr0, (int)(t_begin - hr0));
+        const int rel = (int)(t_begin - HROWS - hr0);  // <= 0: rows before 0 read as zero
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = rel + 4 * g4 + i;
+            const uint32_t o = off(r, hist && r >= 0);
+            hk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+            hv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+        }
+    }
+    // Every tap load is issued unconditionally (an index outside the filter
+    // reads element 0 and is then replaced by zero), so all of them are in
+    // flight together.
     uint32_t tap_lo[NPT], tap_hi[NPT];
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
@@ -795,39 +836,21 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
         const int ch = c_begin + dl;
         const bool chok = i < SLAB * PTN && ch < p.D;
         const size_t hrow = chok ? (size_t)(ch / p.group_size) * p.l_h : 0;
+        const bool lo_ok = chok && m >= 0 && m < p.l_h;
+        const size_t ilo = lo_ok ? hrow + m : 0;
         if constexpr (F32) {
-            tap_lo[j] = (chok && m >= 0 && m < p.l_h) ? ((const uint32_t *)p.h)[hrow + m] : 0u;
+            const uint32_t vlo = ((const uint32_t *)p.h)[ilo];
+            tap_lo[j] = lo_ok ? vlo : 0u;
             tap_hi[j] = 0u;
         } else {
-            tap_lo[j] = (chok && m >= 0 && m < p.l_h) ? ((const uint16_t *)p.h)[hrow + m] : 0u;
-            tap_hi[j] = (chok && m >= 1 && m <= p.l_h) ? ((const uint16_t *)p.h)[hrow + m - 1] : 0u;
+            const bool hi_ok = chok && m >= 1 && m <= p.l_h;
+            const size_t ihi = hi_ok ? hrow + m - 1 : 0;
+            const uint32_t vlo = ((const uint16_t *)p.h)[ilo];
+            const uint32_t vhi = ((const uint16_t *)p.h)[ihi];
+            tap_lo[j] = lo_ok ? vlo : 0u;
+            tap_hi[j] = hi_ok ? vhi : 0u;
         }
     }
-
-    // history: the HROWS rows before the span, in the first HROWS / 4 row groups
-    u32x4_t hk[4], hv[4];
-    const bool hist = g4 < HROWS / 4;
-    if constexpr (HROWS > 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t o = off(row0 - HROWS + 4 * g4 + i, hist);
-            hk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
-            hv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
-        }
-    }
-    u32x4_t kr[2][4], vr[2][4], qr[2][4];
-    auto load_block = [&](int blk, int slot) {
-        const bool need = blk < NB;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t o = off(row0 + blk * kCdBlock + 4 * g4 + i, need);
-            kr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadPolicy));
-            vr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kLoadPolicy));
-            qr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, kLoadPolicy));
-        }
-    };
-    load_block(0, 0);
-
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
         const int i = tid + j * kThreads;
@@ -874,24 +897,31 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
             }
         }
     };
-    auto ring_of = [](int t) -> int { return (t + 128 + 4 * kCdRing) % kCdRing; };
-
+    // ring index of time t (relative to the block start) for a block whose
+    // start sits at ring index rb0: (rb0 + t) mod 384, t in [-128, 384)
+    auto wrap = [](int r) -> int {
+        r = r >= kCdRing ? r - kCdRing : r;
+        return r >= kCdRing ? r - kCdRing : r;
+    };
     if constexpr (HROWS > 0) {
-        if (hist) put_x(ring_of(-HROWS + 4 * g4), hk, hv);
+        if (hist) put_x(128 - HROWS + 4 * g4, hk, hv);  // times -HROWS .. -1 of block 0
     }
 
     // MFMA lane roles: A = taps (row n16 = output row of a sub-chunk),
     // B = x (column n16 = sub-chunk); the accumulator holds output rows
     // 4 q4 .. 4 q4 + 3 of sub-chunk n16.
-    const int lane_t8 = 16 * n16 + 8 * q4;  // B rows of a K = 32 step (times)
+    const int lane_t8 = 16 * n16 + 8 * q4;  // B rows of a 32-row step (times)
     const int lane_t4 = 16 * n16 + 4 * q4;  // accumulator rows (fp32: B rows of a group)
-#pragma unroll
-    for (int blk = 0; blk < NB; ++blk) {
-        const int slot = blk & 1;
-        const int tb = blk * kCdBlock;  // block start relative to the span start
-        put_x(ring_of(tb + 4 * g4), kr[slot], vr[slot]);
-        put_q(qr[slot]);
-        load_block(blk + 1, slot ^ 1);
+
+    // One block: stage x and q, prefetch the next block, contract, gate,
+    // write back.  Blocks alternate between the two register sets.
+    auto process = [&](int blk, const u32x4_t *kd, const u32x4_t *vd, const u32x4_t *qd,
+                       u32x4_t *kn, u32x4_t *vn, u32x4_t *qn) {
+        const int rb0 = (blk % 3) * 256 + 128 >= kCdRing ? (blk % 3) * 256 + 128 - kCdRing
+                                                         : (blk % 3) * 256 + 128;  // (256 blk + 128) mod 384
+        put_x(wrap(rb0 + 4 * g4), kd, vd);
+        put_q(qd);
+        if (blk + 1 < nb) load_block(blk + 1, kn, vn, qn);
         __syncthreads();
 #pragma unroll
         for (int cl = 0; cl < T::CPW; ++cl) {
@@ -905,8 +935,7 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
 #pragma unroll
                 for (int gi = 0; gi <= 2 * KH; ++gi) {
                     const int tg = -HROWS + 16 * gi;
-                    int r = lane_t4 + ring_of(tb + tg);
-                    if (r >= kCdRing) r -= kCdRing;
+                    const int r = wrap(rb0 + kCdRing + tg + lane_t4);
                     const f32x4_t xv = *(const f32x4_t *)(&xr[pos(dl, r, T::RING_B)]);
                     const int c = n16 - 4 * q4 - tg + kCdTapOff;
 #pragma unroll
@@ -921,8 +950,7 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
 #pragma unroll
                 for (int ks = 0; ks <= KH; ++ks) {
                     const int tin0 = -HROWS + 32 * ks;
-                    int r = (ks == KH ? lane_t8 - ((q4 & 2) << 3) : lane_t8) + ring_of(tb + tin0);
-                    if (r >= kCdRing) r -= kCdRing;
+                    const int r = wrap(rb0 + kCdRing + tin0 + (ks == KH ? lane_t8 - ((q4 & 2) << 3) : lane_t8));
                     const u32x4_t xv = *(const u32x4_t *)(&xr[pos(dl, r, T::RING_B)]);
                     const int c = n16 - 8 * q4 - tin0 + kCdTapOff;
                     const u32x4_t hv4 = {ptc[c], ptc[c - 2], ptc[c - 4], ptc[c - 6]};
@@ -965,19 +993,25 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
                 yrow[3][d] = (a[1] >> 16) | (c[1] & 0xffff0000u);
             }
         }
+        const int64_t r0 = t_begin + (int64_t)blk * kCdBlock;
+        const __amdgpu_buffer_rsrc_t ry = window(p.y, r0, min(kCdBlock, (int)(t_stop - r0)));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_buffer_store_b128(yrow[i], ry, off(row0 + tb + 4 * g4 + i, true), 0, kStorePolicy);
+            __builtin_amdgcn_raw_buffer_store_b128(yrow[i], ry, off(4 * g4 + i, true), 0, kStorePolicy);
         __syncthreads();  // the gate rows and the oldest ring entries are rewritten next
+    };
+    for (int blk = 0; blk < nb; blk += 2) {
+        process(blk, k0, v0, q0, k1, v1, q1);
+        if (blk + 1 >= nb) break;
+        process(blk + 1, k1, v1, q1, k0, v0, q0);
     }
 }
 
 // Kernel families and their compiled span counts (indices into kSpans).
 enum Family { kFwd = 0, kRevDual = 1, kDh = 2, kCd = 3 };
-// chunk-direction kernels: spans of 1, 2 or 4 blocks of 256 rows
-constexpr int kCdSpans[] = {1, 2, 4};
+// (the chunk-direction kernel takes its span at run time: one entry)
 template <bool F32, int Fam> constexpr int kSpanCount =
-    Fam == kFwd ? kNumSpansFor<F32> : Fam == kRevDual ? (F32 ? 2 : 4) : Fam == kDh ? (F32 ? 3 : 5) : 3;
+    Fam == kFwd ? kNumSpansFor<F32> : Fam == kRevDual ? (F32 ? 2 : 4) : Fam == kDh ? (F32 ? 3 : 5) : 1;
 
 typedef void (*DhFn)(DhParams);
 template <bool F32, int Fam> struct FnType { typedef KernelFn type; };
@@ -992,13 +1026,12 @@ constexpr typename FnType<F32, Fam>::type kernel_of() {
     else if constexpr (Fam == kDh)
         return hyena_bwd_dh_kernel<F32, KH, Sp>;
     else
-        return hyena_fwd_cd_kernel<F32, KH, Sp>;
+        return hyena_fwd_cd_kernel<F32, KH>;
 }
 
 template <bool F32, int Fam, int KH, int... Ss>
 typename FnType<F32, Fam>::type span_table_entry(int si, std::integer_sequence<int, Ss...>) {
-    static constexpr typename FnType<F32, Fam>::type fns[] = {
-        kernel_of<F32, Fam, KH, (Fam == kCd ? kCdSpans[Ss] : kSpans[Ss])>()...};
+    static constexpr typename FnType<F32, Fam>::type fns[] = {kernel_of<F32, Fam, KH, kSpans[Ss]>()...};
     return fns[si];
 }
 
@@ -1073,35 +1106,34 @@ int make_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, 
     return HYENA_OK;
 }
 
-// Plan of the chunk-direction kernel (group sizes not a multiple of 16):
-// workgroups own CdTr::SLAB channels and spans of 1, 2 or 4 blocks of 256
-// rows; `span` is reported in 64-row chunks, `span_req` read in chunks too.
+// Plan of the chunk-direction kernel (group sizes not a multiple of 16).
+// A workgroup owns CdTr::SLAB channels of one batch row and a span of
+// 256-row blocks; it needs most of a CU's LDS, so one runs per CU.  By
+// default the spans are as long as it takes to make about one workgroup per
+// CU (kCdWorkgroups), which reads the history rows and stages the taps once
+// per span; `span_req` (in 64-row chunks) overrides.  `span` is reported in
+// chunks.  Buffer windows are per block, so spans have no length limit.
+constexpr int64_t kCdWorkgroups = 256;
+
 int cd_plan(int64_t B, int64_t L, int64_t D, int64_t l_h, int dtype, int64_t span_req, Plan *pl) {
     const bool f32 = dtype == HYENA_DTYPE_F32;
     const int64_t eb = f32 ? 4 : 2;
     const int64_t slab = f32 ? CdTr<true>::SLAB : CdTr<false>::SLAB;
     if ((D * eb) % 16 != 0) return HYENA_ERR_UNSUPPORTED;  // 16-byte row segments
-    if (D > INT32_MAX / 16) return HYENA_ERR_UNSUPPORTED;
+    if (D > INT32_MAX / 16 || (kCdBlock + 128) * D * eb >= kMaxWindowBytes) return HYENA_ERR_UNSUPPORTED;
     pl->kh = (int)((l_h - 1 + 31) / 32);
     pl->n_chunks = (L + kChunk - 1) / kChunk;
     const int64_t n_blocks = (L + kCdBlock - 1) / kCdBlock;
     pl->n_slabs = (D + slab - 1) / slab;
-    // the 32 KH history rows are re-read once per span: longer spans for
-    // longer filters
-    int64_t want = span_req > 0 ? (span_req * kChunk + kCdBlock - 1) / kCdBlock : (pl->kh <= 1 ? 1 : 4);
-    if (want > n_blocks) want = n_blocks;
-    int si = -1;
-    for (int i = 0; i < 3; ++i) {
-        const int64_t win = ((int64_t)kCdSpans[i] * kCdBlock + 32 * pl->kh) * D * eb;
-        if (win >= kMaxWindowBytes) break;
-        if (i == 0 || kCdSpans[i] <= want) si = i;
-    }
-    if (si < 0) return HYENA_ERR_UNSUPPORTED;
-    pl->span_index = si;
-    pl->span = (int64_t)kCdSpans[si] * (kCdBlock / kChunk);
-    pl->n_spans = (n_blocks + kCdSpans[si] - 1) / kCdSpans[si];
+    int64_t sb = span_req > 0 ? (span_req * kChunk + kCdBlock - 1) / kCdBlock
+                              : (n_blocks * pl->n_slabs * B + kCdWorkgroups - 1) / kCdWorkgroups;
+    sb = max((int64_t)1, min(sb, n_blocks));
+    pl->span_index = 0;
+    pl->span = sb * (kCdBlock / kChunk);
+    pl->n_spans = (n_blocks + sb - 1) / sb;
     pl->workgroups = pl->n_spans * pl->n_slabs * B;
-    if (pl->workgroups > INT32_MAX || pl->n_spans > INT32_MAX) return HYENA_ERR_UNSUPPORTED;
+    if (pl->workgroups > INT32_MAX || pl->n_spans > INT32_MAX || sb > INT32_MAX / kCdBlock)
+        return HYENA_ERR_UNSUPPORTED;
     return HYENA_OK;
 }
 
@@ -1175,6 +1207,7 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
     p.n_spans = (int32_t)pl.n_spans;
     p.n_slabs = (int32_t)pl.n_slabs;
     p.P = (int32_t)P;
+    p.span_blocks = (int32_t)(pl.span / (kCdBlock / kChunk));
     p.g2 = nullptr;
     p.y2 = nullptr;
     const bool f32 = dtype == HYENA_DTYPE_F32;
@@ -1284,7 +1317,7 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
         Params p;
         p.q = v; p.k = dy; p.v = q; p.h = h; p.y = dk;
         p.g2 = k; p.y2 = dv;
-        p.kp = nullptr; p.vp = nullptr; p.P = 0;
+        p.kp = nullptr; p.vp = nullptr; p.P = 0; p.span_blocks = 0;
         p.L = L;
         p.D = (int32_t)D;
         p.group_size = (int32_t)group_size;

@@ -110,12 +110,13 @@ def test_plan_split(B, L, D, l_h, dtype, span, expect_span):
 
 
 @pytest.mark.parametrize("B,L,D,gs,l_h,dtype,span,expect_span", [
-    # group sizes off the 16-channel tile: walks of 1, 2 or 4 blocks of 256
-    # rows (4, 8 or 16 chunks), one block for short filters, four for long
-    (1, 8192, 4096, 1, 7, 0, 0, 4), (1, 8192, 4096, 1, 128, 0, 0, 16),
-    (1, 8192, 4096, 8, 33, 1, 0, 4), (1, 8192, 4096, 8, 34, 1, 0, 16), (2, 1000, 96, 3, 7, 1, 3, 4),
-    (1, 1000, 64, 1, 7, 0, 9, 8), (1, 100, 64, 1, 128, 0, 0, 4),
-    (1, 1000, 72, 24, 65, 0, 0, 16), (1, 1 << 20, 4096, 2, 2, 0, 1000, 16),
+    # group sizes off the 16-channel tile: spans of whole 256-row blocks (4
+    # chunks each), by default long enough for about one workgroup per CU
+    (1, 8192, 4096, 1, 7, 0, 0, 32), (1, 8192, 4096, 1, 128, 0, 0, 32),
+    (1, 8192, 4096, 8, 33, 1, 0, 64), (4, 32768, 4096, 2, 128, 0, 0, 512),
+    (2, 1000, 96, 3, 7, 1, 3, 4), (1, 1000, 64, 1, 7, 0, 9, 12), (1, 100, 64, 1, 128, 0, 0, 4),
+    (1, 1000, 72, 24, 65, 0, 0, 4), (1, 1 << 20, 4096, 2, 2, 0, 1000, 1000),
+    (1, 1 << 20, 4096, 1, 128, 0, 0, 4096), (1, 3000, 64, 1, 7, 0, 10 ** 6, 48),
 ])
 def test_plan_split_chunk_direction(B, L, D, gs, l_h, dtype, span, expect_span):
     s, wgs = hc.plan(B, L, D, gs, l_h, dtype, span)
@@ -125,10 +126,11 @@ def test_plan_split_chunk_direction(B, L, D, gs, l_h, dtype, span, expect_span):
     assert wgs == B * (-(-D // slab)) * (-(-blocks // (s // 4)))
 
 
-def test_plan_chunk_direction_keeps_the_window_addressable():
-    # (blocks * 256 + history) * D * 2 < 2^31: four blocks no longer fit
+def test_plan_chunk_direction_window():
+    # buffer windows are per block: any span length; only a row of 384
+    # rows x D elements must stay below 2^31 bytes
     s, _ = hc.plan(1, 1 << 16, 1 << 20, 1, 128, hc.DTYPE_BF16, 0)
-    assert s == 8 and (2 * 256 + 128) * (1 << 20) * 2 < 1 << 31
+    assert s == (1 << 16) // 64
     with pytest.raises(hc.HyenaError):
         hc.plan(1, 256, 1 << 22, 2, 7, hc.DTYPE_F32, 0)
 

@@ -43,6 +43,7 @@ if ROOT not in sys.path:
 METRIC = "Hyena-SE/MR fwd: G(token·channel)/s and % of HBM-bandwidth roofline, D=4096"
 UNIT = "G(token·channel)/s"
 HBM_PEAK_GBS = 8000.0
+EVENT_EVERY = 5          # per-kernel events in every 5th timed step (coprime with the input sets)
 KERNEL_SRC = os.path.join(ROOT, "gated_convolution_sequence_amd", "csrc", "hyena_conv.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -65,6 +66,7 @@ def parse():
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-naive", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
+    ap.add_argument("--skip-chunk-direction", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough CPU budget of the oracle baseline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -219,24 +221,31 @@ def main():
         # events[0] before the first layer, events[li + 1] after layer li:
         # one timestamp per kernel boundary
         if events is not None:
-            events[0].record(stream)
+            hip_ev.record(events[0], stream)
         for li, w in enumerate(layers):
             q, k, v, h, y = sets[li][i % len(sets[li])]
             hc.conv_fwd(q, k, v, h, w.group_size, out=y, stream=stream)
             if events is not None:
-                events[li + 1].record(stream)
+                hip_ev.record(events[li + 1], stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     # ---- timed region: exactly K steps ------------------------------------
+    # Every EVENT_EVERY-th step records one HIP event per kernel boundary on
+    # the launch stream (the per-kernel durations of the roofline).  The
+    # events skip the system-scope fence: a default event writes back and
+    # invalidates the caches, which costs about 2 us per record here and
+    # lengthens the kernels it brackets.
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(layers) + 1)] for _ in range(K)]
+    sampled = list(range(0, K, EVENT_EVERY))
+    hip_ev = HipEvents()
+    ev = {i: [hip_ev.create() for _ in range(len(layers) + 1)] for i in sampled}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(i, ev[i])
+        step(i, ev.get(i))
     t_issued = time.perf_counter()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -248,7 +257,7 @@ def main():
 
     layer_stats = {}
     for li, w in enumerate(layers):
-        ms = [ev[i][li].elapsed_time(ev[i][li + 1]) for i in range(K)]
+        ms = [hip_ev.elapsed_ms(ev[i][li], ev[i][li + 1]) for i in sampled]
         mean_ms = sum(ms) / len(ms)
         alg_bytes = w.elems * (4 * (2 if w.dtype == "bf16" else 4))
         achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
@@ -262,7 +271,7 @@ def main():
             "G_tok_ch_per_s": round(w.elems / (mean_ms * 1e-3) / 1e9, 2),
             "alg_bytes": alg_bytes, "achieved_GBs": round(achieved, 1),
             "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
-            "span_chunks": span, "workgroups": wgs,
+            "span_chunks": span, "workgroups": wgs, "event_samples": len(sampled),
         }
     dom = max(layer_stats, key=lambda n: layer_stats[n]["mean_us"])
     d = layer_stats[dom]
@@ -284,6 +293,10 @@ def main():
         "layers": layer_stats,
         "host_issue_us_per_step": round(host_issue_us, 2),
     }
+
+    # ---- one filter per channel (chunk-direction kernel), same layers -------
+    if not args.skip_chunk_direction:
+        out["chunk_direction"] = chunk_direction_rates(layers, sets, stream, max(10, K // 4))
 
     # ---- backward of each layer (outside the forward step's timed region)
     if not args.skip_backward:
@@ -351,6 +364,83 @@ def backward_rates(layers, sets, stream, reps):
                        "GBs_moved": round(14 * eb * w.elems / (us * 1e-6) / 1e9, 1),
                        "kernels": 4, "workspace_bytes": ws_n}
         del dys
+    return res
+
+
+class HipEvents:
+    """HIP timing events without the system-scope fence (hipEventDisableSystemFence),
+    created in the HIP runtime this process already loaded (the one torch and the
+    library use, so torch's stream handles are valid).  Only timestamps are
+    read, after a device synchronisation."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        self.ct = ctypes
+        self.lib = ctypes.CDLL(path)
+        self.events = []
+
+    def create(self):
+        e = self.ct.c_void_p()
+        rc = self.lib.hipEventCreateWithFlags(self.ct.byref(e), self.ct.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags: %d" % rc)
+        self.events.append(e)
+        return e
+
+    def record(self, e, stream):
+        rc = self.lib.hipEventRecord(e, self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord: %d" % rc)
+
+    def elapsed_ms(self, a, b):
+        f = self.ct.c_float()
+        rc = self.lib.hipEventElapsedTime(self.ct.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime: %d" % rc)
+        return f.value
+
+
+def chunk_direction_rates(layers, sets, stream, reps):
+    """Each layer with group_size 1: every channel its own filter (its group's
+    taps repeated, so the result is the grouped layer's), which runs the
+    chunk-direction kernel.  Timed back to back on the rotated inputs."""
+    import torch
+    import gated_convolution_sequence_amd as hc
+    res = {}
+    for li, w in enumerate(layers):
+        per = sets[li]
+        h1 = torch.repeat_interleave(per[0][3], w.group_size, dim=0).contiguous()
+
+        def call(i):
+            q, k, v, _, y = per[i % len(per)]
+            hc.conv_fwd(q, k, v, h1, 1, out=y, stream=stream)
+        for i in range(3):
+            call(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            call(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        alg = w.elems * (8 if w.dtype == "bf16" else 16)
+        span, wgs = hc.plan(w.B, w.L, w.D, 1, w.l_h, hc.DTYPE_BF16 if w.dtype == "bf16" else hc.DTYPE_F32)
+        res[w.name + "_gs1"] = {"group_size": 1, "us": round(us, 2),
+                                "G_tok_ch_per_s": round(w.elems / (us * 1e-6) / 1e9, 2),
+                                "achieved_GBs": round(alg / (us * 1e-6) / 1e9, 1),
+                                "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "span_chunks": span, "workgroups": wgs}
     return res
 
 

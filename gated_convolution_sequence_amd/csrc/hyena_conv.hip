@@ -794,7 +794,7 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
 
     u32x4_t k0[4], v0[4], q0[4], k1[4], v1[4], q1[4];
     auto load_block = [&](int blk, u32x4_t *kd, u32x4_t *vd, u32x4_t *qd) {
-        const int64_t r0 = t_begin + (int64_t)blk * kCdBlock;
+        const int64_t r0 = min(t_begin + (int64_t)blk * kCdBlock, t_stop);  // past the span: empty
         const int rows = min(kCdBlock, (int)(t_stop - r0));
         const __amdgpu_buffer_rsrc_t rq = window(p.q, r0, rows);
         const __amdgpu_buffer_rsrc_t rk = window(p.k, r0, rows);
@@ -915,13 +915,18 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
 
     // One block: stage x and q, prefetch the next block, contract, gate,
     // write back.  Blocks alternate between the two register sets.
+    // The next block's loads go out before this block is staged (its
+    // register set was freed by the previous block), so a block's loads are
+    // always in flight.  They are issued unconditionally: past the span the
+    // window is empty and they read nothing.  (Behind a branch, the
+    // compiler's wait for this block's data would also wait for them.)
     auto process = [&](int blk, const u32x4_t *kd, const u32x4_t *vd, const u32x4_t *qd,
                        u32x4_t *kn, u32x4_t *vn, u32x4_t *qn) {
         const int rb0 = (blk % 3) * 256 + 128 >= kCdRing ? (blk % 3) * 256 + 128 - kCdRing
                                                          : (blk % 3) * 256 + 128;  // (256 blk + 128) mod 384
+        load_block(blk + 1, kn, vn, qn);
         put_x(wrap(rb0 + 4 * g4), kd, vd);
         put_q(qd);
-        if (blk + 1 < nb) load_block(blk + 1, kn, vn, qn);
         __syncthreads();
 #pragma unroll
         for (int cl = 0; cl < T::CPW; ++cl) {

@@ -31,8 +31,9 @@ STATUS = {
 
 # Every symbol include/hyena_conv.h declares.
 EXPORTS = ("hyena_conv_fwd", "hyena_conv_fwd_f32", "hyena_conv_fwd_ex", "hyena_conv_fwd_halo",
-           "hyena_conv_bwd", "hyena_conv_bwd_workspace", "hyena_conv_plan",
-           "hyena_conv_strerror", "hyena_conv_block_len")
+           "hyena_conv_bwd", "hyena_conv_bwd_workspace", "hyena_conv_fwd_long",
+           "hyena_conv_fwd_long_workspace", "hyena_conv_plan", "hyena_conv_strerror",
+           "hyena_conv_block_len")
 
 
 class HyenaError(RuntimeError):
@@ -71,6 +72,12 @@ def lib() -> ctypes.CDLL:
         L.hyena_conv_bwd_workspace.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                                ctypes.POINTER(i64)]
         L.hyena_conv_bwd_workspace.restype = ctypes.c_int
+        L.hyena_conv_fwd_long.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, ctypes.c_int,
+                                          vp, i64, vp]
+        L.hyena_conv_fwd_long.restype = ctypes.c_int
+        L.hyena_conv_fwd_long_workspace.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
+                                                    ctypes.POINTER(i64)]
+        L.hyena_conv_fwd_long_workspace.restype = ctypes.c_int
         L.hyena_conv_plan.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, i64,
                                       ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.hyena_conv_plan.restype = ctypes.c_int
@@ -223,6 +230,60 @@ def conv_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Tensor,
     if st != 0:
         raise HyenaError(st, "hyena_conv_bwd")
     return dq, dk, dv, dh
+
+
+def long_workspace_bytes(B: int, L: int, D: int, group_size: int, l_h: int,
+                         dtype: int = DTYPE_BF16) -> int:
+    """Workspace bytes hyena_conv_fwd_long needs (FFT work area and filter spectra)."""
+    n = ctypes.c_int64()
+    st = lib().hyena_conv_fwd_long_workspace(B, L, D, group_size, l_h, dtype, ctypes.byref(n))
+    if st != 0:
+        raise HyenaError(st, "hyena_conv_fwd_long_workspace")
+    return n.value
+
+
+def conv_fwd_long(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Tensor,
+                  group_size: int, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None,
+                  stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """y = q (.) (h * (k (.) v)) by FFT convolution, for filters of any length.
+
+    Same tensors as conv_fwd; h is [D // group_size, l_h] with any l_h >= 1.
+    ``workspace`` (uint8, on q's device) is allocated here if not given.
+    """
+    dt, dev = q.dtype, q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("h", h)):
+        if t.dtype != dt or t.device != dev or dev.type != "cuda" or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor like q" % name)
+    if q.dim() != 3 or k.shape != q.shape or v.shape != q.shape or h.dim() != 2:
+        raise ValueError("q, k, v must be [B, L, D]; h [D // group_size, l_h]")
+    code = _dtype_code(dt)
+    B, L, D = q.shape
+    G, l_h = h.shape
+    if group_size < 1 or D % group_size != 0 or G != D // group_size:
+        raise ValueError("h has %d filters; D=%d, group_size=%d" % (G, D, group_size))
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != dt or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    ws_n = long_workspace_bytes(B, L, D, group_size, l_h, code)
+    if workspace is None:
+        workspace = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
+        raise ValueError("workspace must hold %d bytes on q's device" % ws_n)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(), B, L, D, group_size, l_h,
+            out.data_ptr(), code, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            stream.cuda_stream)
+    if dev.index == torch.cuda.current_device():
+        st = lib().hyena_conv_fwd_long(*args)
+    else:
+        with torch.cuda.device(dev):
+            st = lib().hyena_conv_fwd_long(*args)
+    if st != 0:
+        raise HyenaError(st, "hyena_conv_fwd_long")
+    return out
 
 
 class HyenaConv(torch.autograd.Function):

@@ -6,7 +6,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "hyena_conv.hip")
+SOURCES = [os.path.join(PKG, "csrc", name) for name in ("hyena_conv.hip", "hyena_fft.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhyena_conv.so")
 
@@ -24,9 +24,9 @@ def hipcc() -> str:
 
 
 def build_library(verbose: bool = False) -> str:
-    """Compile csrc/hyena_conv.hip into libhyena_conv.so next to this file."""
+    """Compile the csrc/*.hip sources into libhyena_conv.so next to this file."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I" + INCLUDE, "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I" + INCLUDE, "-o", tmp, *SOURCES]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)

@@ -152,6 +152,34 @@ int hyena_conv_bwd_workspace(int64_t B, int64_t L, int64_t D,
                              int64_t group_size, int64_t l_h, int dtype,
                              int64_t *bytes_out);
 
+/* Long-filter forward by FFT convolution, for filters of any length l_h >= 1
+ * (Hyena-LI with a given filter).  Same operator, layout and dtypes as
+ * hyena_conv_fwd_ex; taps past row L - 1 never contribute.  Computed as
+ *     z = IFFT( FFT(h) * FFT(k (.) v) )[0, L),   y = q (.) z
+ * with zero padding to N >= L + min(l_h, L) - 1 (a power of two, at most
+ * 2^23), so the circular convolution equals the causal one (StripedHyena 2
+ * explainer: page "01. overview", section 2, long convolutions through the
+ * FFT in O(N log N); page "04. hardware-aware convolution kernels", section
+ * 1, long filters are FFT-based).  The transforms are fp32 for both dtypes;
+ * the error is that of an fp32 FFT (it is spread over the sequence, not
+ * bounded per element by the direct sum's terms).  `workspace` (16-byte
+ * aligned, at least hyena_conv_fwd_long_workspace bytes, contents need not be
+ * initialised) receives the filter spectra and the transform work area.  D
+ * must be even (channels are transformed in pairs), else
+ * HYENA_ERR_UNSUPPORTED.  Inputs, output and workspace must not overlap.  The
+ * filter spectra are recomputed on every call. */
+int hyena_conv_fwd_long(const void *q, const void *k, const void *v,
+                        const void *h, int64_t B, int64_t L, int64_t D,
+                        int64_t group_size, int64_t l_h, void *out, int dtype,
+                        void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace hyena_conv_fwd_long needs (written to *bytes_out):
+ * 8 N (max(B D/2, G'/2) + G'), N the transform length and G' the filter
+ * count rounded up to even.  Host only.  Returns a status. */
+int hyena_conv_fwd_long_workspace(int64_t B, int64_t L, int64_t D,
+                                  int64_t group_size, int64_t l_h, int dtype,
+                                  int64_t *bytes_out);
+
 /* The work split hyena_conv_fwd_ex would use: writes the chunks per
  * workgroup and the workgroup count.  Host only; runs the same argument
  * checks on the sizes (pointers are not inspected).  Returns a status. */

@@ -201,3 +201,34 @@ def test_backward_workspace_size():
     assert hc.bwd_workspace_bytes(0, 8192, 4096, 16, 128) == 0
     with pytest.raises(hc.HyenaError):
         hc.bwd_workspace_bytes(1, 64, 64, 16, 300)
+
+
+def _long(q=P["q"], k=P["k"], v=P["v"], h=P["h"], B=1, L=128, D=64, gs=16, l_h=1000,
+          out=P["out"], dtype=hc.DTYPE_BF16, ws=P["out"] + (64 << 20), ws_n=1 << 30):
+    return hc.lib().hyena_conv_fwd_long(q, k, v, h, B, L, D, gs, l_h, out, dtype, ws, ws_n, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(h=None), -1), (dict(out=None), -1),
+    (dict(B=-1), -2), (dict(gs=0), -3), (dict(D=64, gs=48), -3), (dict(l_h=0), -4),
+    (dict(D=63, gs=1), -7), (dict(L=1 << 23), -7),
+    (dict(q=P["q"] + 8), -5), (dict(h=P["h"] + 1), -5), (dict(ws=P["out"] + (64 << 20) + 4), -5),
+    (dict(out=P["k"]), -6), (dict(ws=P["v"]), -6), (dict(ws=P["out"]), -6),
+    (dict(ws=None), -10), (dict(ws_n=1024), -10), (dict(dtype=3), -9),
+])
+def test_long_filter_entry_validates_on_host(kw, code):
+    assert _long(**kw) == code
+
+
+def test_long_filter_workspace_size():
+    # N = 2^ceil(log2(L + min(l_h, L) - 1)); 8 N (max(B D/2, G'/2) + G') bytes
+    def expect(B, L, D, gs, l_h):
+        n = 1 << max(2, (L + min(l_h, L) - 2).bit_length())
+        G = D // gs
+        Gp = G + (G & 1)
+        return 8 * n * (max(B * D // 2, Gp // 2) + Gp)
+    for args in [(1, 8192, 4096, 16, 8192), (2, 1000, 64, 1, 37), (1, 5, 6, 3, 1000), (3, 1, 2, 1, 1)]:
+        assert hc.long_workspace_bytes(*args) == expect(*args), args
+    assert hc.long_workspace_bytes(0, 8192, 4096, 16, 8192) == 0
+    with pytest.raises(hc.HyenaError):
+        hc.long_workspace_bytes(1, 100, 7, 1, 10)  # odd D

@@ -101,7 +101,9 @@ def test_worked_example_two_stage_reproduces_output():
 
 @pytest.mark.parametrize("L,D,gs,l_h,seed", [
     (1, 3, 1, 1, 0), (6, 2, 2, 4, 1), (100, 8, 4, 7, 2), (257, 6, 3, 128, 3),
-    (300, 16, 16, 65, 4), (64, 4, 1, 64, 5), (65, 2, 1, 66, 6)])
+    (300, 16, 16, 65, 4), (64, 4, 1, 64, 5), (65, 2, 1, 66, 6),
+    # long filters (the FFT path's regime): as long as the sequence, and longer
+    (300, 4, 2, 300, 7), (200, 2, 1, 500, 8)])
 def test_matches_numpy_convolve_exactly_on_integers(L, D, gs, l_h, seed):
     rng = np.random.default_rng(seed)
     v = rng.integers(-3, 4, size=(1, L, D)).astype(np.float64)
@@ -114,7 +116,8 @@ def test_matches_numpy_convolve_exactly_on_integers(L, D, gs, l_h, seed):
 
 
 @pytest.mark.parametrize("B,L,D,gs,l_h,seed", [
-    (1, 512, 16, 16, 7, 10), (2, 333, 32, 16, 128, 11), (3, 129, 8, 2, 100, 12)])
+    (1, 512, 16, 16, 7, 10), (2, 333, 32, 16, 128, 11), (3, 129, 8, 2, 100, 12),
+    (1, 1000, 4, 1, 1000, 13), (2, 700, 6, 3, 1500, 14)])
 def test_matches_fft_convolution(B, L, D, gs, l_h, seed):
     rng = np.random.default_rng(seed)
     q, k, v = (rng.standard_normal((B, L, D)) for _ in range(3))

@@ -30,7 +30,7 @@
 // spectra; equal filters make the second term vanish).  The filter spectra
 // come from the same two kernels run on the filters (pairs of filters,
 // separated the same way), once per call.
-// Inner transforms are radix-2 Stockham (self-sorting) in LDS with twiddles
+// Inner transforms are radix-4 Stockham (self-sorting) in LDS with twiddles
 // tabulated per workgroup; arithmetic is fp32 for both I/O types.
 
 #include <hip/hip_runtime.h>
@@ -41,10 +41,9 @@
 
 namespace {
 
-constexpr int kFftThreads = 512;
-constexpr int kFftLds = 8192;        // complex values per LDS buffer (64 KiB)
-constexpr int kFftMaxM = 4096;       // largest inner transform
-constexpr int kFftMaxLogN = 23;      // N <= 2^23
+constexpr int kFftThreads = 256;
+constexpr int kFftMaxLogN = 22;      // N <= 2^22
+constexpr int kFftMaxLdsBytes = 160 * 1024;
 
 struct FftParams {
     const void *q, *k, *v, *h;
@@ -57,7 +56,7 @@ struct FftParams {
     int32_t Gp;          // filters, rounded up to even
     int32_t G, group_size, l_h;
     int32_t N1, N2, log1, log2;
-    int32_t P, n_tiles;  // pairs per workgroup, pair tiles
+    int32_t logP, n_tiles;  // pairs per workgroup (log2), pair tiles, of the kernel launched
 };
 
 __device__ inline float2 cmul(float2 a, float2 b) {
@@ -65,7 +64,7 @@ __device__ inline float2 cmul(float2 a, float2 b) {
 }
 __device__ inline float2 cconj(float2 a) { return make_float2(a.x, -a.y); }
 
-// exp(-2 pi i m / n) for 0 <= m < n, n a power of two <= 2^23 (2m/n is
+// exp(-2 pi i m / n) for 0 <= m < n, n a power of two <= 2^22 (2m/n is
 // exact in fp32, and sincospif reduces it exactly).
 __device__ inline float2 twiddle(int64_t m, int64_t n) {
     float s, c;
@@ -73,35 +72,83 @@ __device__ inline float2 twiddle(int64_t m, int64_t n) {
     return make_float2(c, -s);
 }
 
-// Twiddle table tw[m] = exp(-2 pi i m / M), m < M/2.
-__device__ inline void fill_twiddles(float2 *tw, int M) {
-    for (int m = threadIdx.x; m < M / 2; m += blockDim.x) tw[m] = twiddle(m, M);
+// Work item of this workgroup.  Workgroups are dispatched to the 8 XCDs in
+// turn (workgroup i to XCD i mod 8), each with its own L2.  Consecutive work
+// items (neighbouring pair tiles, which share 128-byte lines) are given to
+// consecutive workgroups of one XCD: XCD x takes one contiguous run of items.
+__device__ inline int xcd_item() {
+    const int n = gridDim.x, bid = blockIdx.x;
+    const int per = n >> 3, rem = n & 7, x = bid & 7;
+    return x * per + min(x, rem) + (bid >> 3);
 }
 
-// In-LDS M-point transform of P interleaved sequences (element j of
-// sequence p at x[j P + p]), radix-2 Stockham: stage s combines
-// sub-transforms of Ns = 2^s points into 2 Ns points,
-//     y[(j - k) 2 + k] = a + w b,  y[(j - k) 2 + k + Ns] = a - w b,
-// with a = x[j], b = x[j + M/2], k = j mod Ns, w = W_(2 Ns)^k (conjugated
-// for the inverse).  Output in natural order; returns the buffer holding it.
+// Twiddle table tw[m] = exp(-2 pi i m / M), m < M.
+__device__ inline void fill_twiddles(float2 *tw, int M) {
+    for (int m = threadIdx.x; m < M; m += blockDim.x) tw[m] = twiddle(m, M);
+}
+
+// In-LDS M-point transform of P = 2^logP interleaved sequences (element j
+// of sequence p at x[j P + p]), Stockham (self-sorting), radix 4 with one
+// radix-2 stage when log2 M is odd.  A radix-R stage combines R
+// sub-transforms of Ns points into R Ns points: for j < M/R, k = j mod Ns,
+//     v_r = x[j + r M/R] W_(R Ns)^(r k),   V = DFT_R(v),
+//     y[(j - k) R + k + r Ns] = V_r,
+// with W conjugated (and DFT_R inverted) for the inverse transform.  tw[m] =
+// W_M^m for m < M.  Output in natural order; returns the buffer holding it.
 // Callers synchronise before (x written) and the routine ends synchronised.
-__device__ float2 *lds_fft(float2 *x, float2 *y, const float2 *tw, int M, int logM, int P, bool inverse) {
-    const int half = M >> 1;
-    const int n = half * P;
-    for (int s = 0; s < logM; ++s) {
-        const int Ns = 1 << s;
-        const int tstride = half >> s;  // W_(2 Ns)^k = W_M^(k M / (2 Ns))
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
-            const int j = i / P;
-            const int p = i - j * P;
-            const int k = j & (Ns - 1);
-            const float2 a = x[i];
-            float2 w = tw[k * tstride];
-            if (inverse) w.y = -w.y;
-            const float2 b = cmul(x[i + n], w);
-            const int d = ((j - k) << 1) + k;
-            y[d * P + p] = make_float2(a.x + b.x, a.y + b.y);
-            y[(d + Ns) * P + p] = make_float2(a.x - b.x, a.y - b.y);
+__device__ float2 *lds_fft(float2 *x, float2 *y, const float2 *tw, int M, int logM, int logP, bool inverse) {
+    const int pmask = (1 << logP) - 1;
+    int Ns = 1, logNs = 0;
+    while (logNs < logM) {
+        if (logM - logNs >= 2) {
+            const int quarter = M >> 2;
+            const int n = quarter << logP;
+            const int tstride = quarter >> logNs;  // W_(4 Ns)^k = W_M^(k M / (4 Ns))
+            for (int i = threadIdx.x; i < n; i += kFftThreads) {
+                const int j = i >> logP;
+                const int p = i & pmask;
+                const int k = j & (Ns - 1);
+                float2 v0 = x[i], v1 = x[i + n], v2 = x[i + 2 * n], v3 = x[i + 3 * n];
+                float2 w1 = tw[k * tstride], w2 = tw[2 * k * tstride], w3 = tw[3 * k * tstride];
+                if (inverse) {
+                    w1.y = -w1.y;
+                    w2.y = -w2.y;
+                    w3.y = -w3.y;
+                }
+                v1 = cmul(v1, w1);
+                v2 = cmul(v2, w2);
+                v3 = cmul(v3, w3);
+                // DFT_4: W_4 = -i (forward), +i (inverse)
+                const float2 s02 = make_float2(v0.x + v2.x, v0.y + v2.y), d02 = make_float2(v0.x - v2.x, v0.y - v2.y);
+                const float2 s13 = make_float2(v1.x + v3.x, v1.y + v3.y), d13 = make_float2(v1.x - v3.x, v1.y - v3.y);
+                // -i d13 = (d13.y, -d13.x)
+                const float2 jd = inverse ? make_float2(-d13.y, d13.x) : make_float2(d13.y, -d13.x);
+                const int d = ((j - k) << 2) + k;
+                y[(d << logP) + p] = make_float2(s02.x + s13.x, s02.y + s13.y);
+                y[((d + Ns) << logP) + p] = make_float2(d02.x + jd.x, d02.y + jd.y);
+                y[((d + 2 * Ns) << logP) + p] = make_float2(s02.x - s13.x, s02.y - s13.y);
+                y[((d + 3 * Ns) << logP) + p] = make_float2(d02.x - jd.x, d02.y - jd.y);
+            }
+            Ns <<= 2;
+            logNs += 2;
+        } else {
+            const int half = M >> 1;
+            const int n = half << logP;
+            const int tstride = half >> logNs;  // W_(2 Ns)^k = W_M^(k M / (2 Ns))
+            for (int i = threadIdx.x; i < n; i += kFftThreads) {
+                const int j = i >> logP;
+                const int p = i & pmask;
+                const int k = j & (Ns - 1);
+                const float2 a = x[i];
+                float2 w = tw[k * tstride];
+                if (inverse) w.y = -w.y;
+                const float2 bb = cmul(x[i + n], w);
+                const int d = ((j - k) << 1) + k;
+                y[(d << logP) + p] = make_float2(a.x + bb.x, a.y + bb.y);
+                y[((d + Ns) << logP) + p] = make_float2(a.x - bb.x, a.y - bb.y);
+            }
+            Ns <<= 1;
+            logNs += 1;
         }
         __syncthreads();
         float2 *t = x;
@@ -111,62 +158,89 @@ __device__ float2 *lds_fft(float2 *x, float2 *y, const float2 *tw, int M, int lo
     return x;
 }
 
-// Input pair j at row t: (x[2j], x[2j+1]) with x = k v (SRC = 0, the
-// sequence of batch row b) or (h[2j][t], h[2j+1][t]) (SRC = 1, the filters);
-// zero past the end of either.
-template <bool F32, int SRC>
-__device__ inline float2 load_pair(const FftParams &p, int b, int64_t t, int j) {
-    if (t >= p.L) return make_float2(0.0f, 0.0f);
-    if constexpr (SRC == 0) {
-        const size_t o = ((size_t)b * (size_t)p.L + (size_t)t) * (size_t)p.D + 2 * (size_t)j;
-        if constexpr (F32) {
-            const float2 kk = *(const float2 *)((const float *)p.k + o);
-            const float2 vv = *(const float2 *)((const float *)p.v + o);
-            return make_float2(kk.x * vv.x, kk.y * vv.y);
-        } else {
-            const uint32_t kk = *(const uint32_t *)((const uint16_t *)p.k + o);
-            const uint32_t vv = *(const uint32_t *)((const uint16_t *)p.v + o);
-            return make_float2(__uint_as_float(kk << 16) * __uint_as_float(vv << 16),
-                               __uint_as_float(kk & 0xffff0000u) * __uint_as_float(vv & 0xffff0000u));
+// Global -> LDS staging of n values, kBatch per thread at a time: the loads
+// of a batch are issued together (indices clamped into range, so none is
+// conditional) and waited for once.
+constexpr int kBatch = 8;
+template <typename Load>
+__device__ inline void stage_in(float2 *dst, int n, Load load) {
+    for (int base = 0; base < n; base += kBatch * kFftThreads) {
+        float2 r[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) r[u] = load(min(base + u * kFftThreads + (int)threadIdx.x, n - 1));
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = base + u * kFftThreads + (int)threadIdx.x;
+            if (i < n) dst[i] = r[u];
         }
-    } else {
-        const int g0 = 2 * j, g1 = 2 * j + 1;
-        float a = 0.0f, c = 0.0f;
-        if constexpr (F32) {
-            a = ((const float *)p.h)[(size_t)g0 * p.l_h + t];
-            if (g1 < p.G) c = ((const float *)p.h)[(size_t)g1 * p.l_h + t];
-        } else {
-            a = __uint_as_float((uint32_t)((const uint16_t *)p.h)[(size_t)g0 * p.l_h + t] << 16);
-            if (g1 < p.G) c = __uint_as_float((uint32_t)((const uint16_t *)p.h)[(size_t)g1 * p.l_h + t] << 16);
-        }
-        return make_float2(a, c);
     }
 }
 
+// Input pair j at row t, zero past the end of the sequence or the pairs:
+// (x[2j], x[2j+1]) with x = k v (SRC = 0, batch row b), or (h[2j][t],
+// h[2j+1][t]) (SRC = 1, the filters; zero for a filter past the last).  The
+// loads always go to a valid address (row 0, pair 0 when out of range) and
+// the value is then replaced by zero.
+template <bool F32, int SRC>
+__device__ inline float2 load_pair(const FftParams &p, int b, int64_t t, int j) {
+    const bool ok = t < p.L && j < p.np;
+    const int64_t tc = ok ? t : 0;
+    const int jc = ok ? j : 0;
+    float a, c;
+    if constexpr (SRC == 0) {
+        const size_t o = ((size_t)b * (size_t)p.L + (size_t)tc) * (size_t)p.D + 2 * (size_t)jc;
+        if constexpr (F32) {
+            const float2 kk = *(const float2 *)((const float *)p.k + o);
+            const float2 vv = *(const float2 *)((const float *)p.v + o);
+            a = kk.x * vv.x;
+            c = kk.y * vv.y;
+        } else {
+            const uint32_t kk = *(const uint32_t *)((const uint16_t *)p.k + o);
+            const uint32_t vv = *(const uint32_t *)((const uint16_t *)p.v + o);
+            a = __uint_as_float(kk << 16) * __uint_as_float(vv << 16);
+            c = __uint_as_float(kk & 0xffff0000u) * __uint_as_float(vv & 0xffff0000u);
+        }
+    } else {
+        const int g0 = 2 * jc, g1 = min(2 * jc + 1, p.G - 1);
+        const size_t o0 = (size_t)g0 * p.l_h + tc, o1 = (size_t)g1 * p.l_h + tc;
+        if constexpr (F32) {
+            a = ((const float *)p.h)[o0];
+            c = ((const float *)p.h)[o1];
+        } else {
+            a = __uint_as_float((uint32_t)((const uint16_t *)p.h)[o0] << 16);
+            c = __uint_as_float((uint32_t)((const uint16_t *)p.h)[o1] << 16);
+        }
+        if (2 * jc + 1 >= p.G) c = 0.0f;
+    }
+    return ok ? make_float2(a, c) : make_float2(0.0f, 0.0f);
+}
+
 // Kernel 1: forward transform along t2 for one t1, then the twiddle.
+// LDS (dynamic): two buffers of N2 P values, the N2 inner twiddles and the
+// N2 inter-step twiddles W_N^(t1 f2) of this t1.
 template <bool F32, int SRC>
 __global__ __launch_bounds__(kFftThreads) void fft_rows_kernel(FftParams p) {
-    __shared__ float2 buf[2][kFftLds];
-    __shared__ float2 tw[kFftMaxM / 2];
-    const int tile = blockIdx.x % p.n_tiles;
-    const int t1 = (blockIdx.x / p.n_tiles) % p.N1;
-    const int b = blockIdx.x / (p.n_tiles * p.N1);
-    const int P = p.P, N1 = p.N1, N2 = p.N2;
+    extern __shared__ float2 lds[];
+    const int item = xcd_item();
+    const int tile = item % p.n_tiles;
+    const int t1 = (item / p.n_tiles) % p.N1;
+    const int b = item / (p.n_tiles * p.N1);
+    const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1, N2 = p.N2;
+    const int NP = N2 << logP;
     const int64_t N = (int64_t)N1 * N2;
+    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + 2 * NP, *wt = tw + N2;
+    stage_in(buf0, NP, [&](int i) {
+        return load_pair<F32, SRC>(p, b, t1 + (int64_t)N1 * (i >> logP), (tile << logP) + (i & pmask));
+    });
     fill_twiddles(tw, N2);
-    for (int i = threadIdx.x; i < N2 * P; i += blockDim.x) {
-        const int t2 = i / P, pp = i - t2 * P;
-        const int j = tile * P + pp;
-        buf[0][i] = j < p.np ? load_pair<F32, SRC>(p, b, t1 + (int64_t)N1 * t2, j) : make_float2(0.0f, 0.0f);
-    }
+    for (int f2 = threadIdx.x; f2 < N2; f2 += kFftThreads) wt[f2] = twiddle(((int64_t)t1 * f2) & (N - 1), N);
     __syncthreads();
-    const float2 *X = lds_fft(buf[0], buf[1], tw, N2, p.log2, P, false);
-    for (int i = threadIdx.x; i < N2 * P; i += blockDim.x) {
-        const int f2 = i / P, pp = i - f2 * P;
-        const int j = tile * P + pp;
+    const float2 *X = lds_fft(buf0, buf1, tw, N2, p.log2, logP, false);
+    for (int i = threadIdx.x; i < NP; i += kFftThreads) {
+        const int f2 = i >> logP;
+        const int j = (tile << logP) + (i & pmask);
         if (j >= p.np) continue;
-        const float2 w = twiddle(((int64_t)t1 * f2) & (N - 1), N);
-        p.ws[(((int64_t)b * N2 + f2) * N1 + t1) * p.np + j] = cmul(X[i], w);
+        p.ws[(((int64_t)b * N2 + f2) * N1 + t1) * p.np + j] = cmul(X[i], wt[f2]);
     }
 }
 
@@ -174,109 +248,121 @@ __global__ __launch_bounds__(kFftThreads) void fft_rows_kernel(FftParams p) {
 // MODE 0 (filters): separate each pair's packed spectrum into the two
 // filters' spectra and store them in hs.  MODE 1 (sequence): multiply by the
 // filter spectra, inverse transform along f1, twiddle, store in place.
+// The two columns are interleaved in LDS -- element (t1, col, pair) at
+// (2 t1 + col) P + pair -- so one transform of 2P sequences covers both.  A
+// self-paired column (f2 = 0 or N2/2) is staged twice and stored once.
+// LDS (dynamic): two buffers of 2 N1 P values, the N1 inner twiddles and,
+// per column, the N1 inter-step twiddles W_N^(-t1 f2).
 template <int MODE>
 __global__ __launch_bounds__(kFftThreads) void fft_cols_kernel(FftParams p) {
-    __shared__ float2 buf[4][kFftLds / 2];
-    __shared__ float2 tw[kFftMaxM / 2];
-    const int tile = blockIdx.x % p.n_tiles;
-    const int c = (blockIdx.x / p.n_tiles) % (p.N2 / 2 + 1);
-    const int b = blockIdx.x / (p.n_tiles * (p.N2 / 2 + 1));
-    const int P = p.P, N1 = p.N1, N2 = p.N2;
+    extern __shared__ float2 lds[];
+    const int item = xcd_item();
+    const int tile = item % p.n_tiles;
+    const int c = (item / p.n_tiles) % (p.N2 / 2 + 1);
+    const int b = item / (p.n_tiles * (p.N2 / 2 + 1));
+    const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1, N2 = p.N2;
+    const int lP2 = logP + 1;
+    const int NP2 = N1 << lP2;
     const int64_t N = (int64_t)N1 * N2;
     const int fa = c, fb = (N2 - c) & (N2 - 1);
     const bool self = fa == fb;
-    const int ncol = self ? 1 : 2;
+    float2 *bufA = lds, *bufB = lds + NP2, *tw = lds + 2 * NP2;
+    float2 *wt[2] = {tw + N1, tw + 2 * N1};
+    stage_in(bufA, NP2, [&](int i) {
+        const int col = (i >> logP) & 1;
+        const int j = (tile << logP) + (i & pmask);
+        const bool ok = j < p.np;
+        const float2 v = p.ws[(((int64_t)b * N2 + (col ? fb : fa)) * N1 + (i >> lP2)) * p.np + (ok ? j : 0)];
+        return ok ? v : make_float2(0.0f, 0.0f);
+    });
     fill_twiddles(tw, N1);
-    for (int col = 0; col < ncol; ++col) {
-        const int f2 = col ? fb : fa;
-        for (int i = threadIdx.x; i < N1 * P; i += blockDim.x) {
-            const int t1 = i / P, pp = i - t1 * P;
-            const int j = tile * P + pp;
-            buf[2 * col][i] = j < p.np ? p.ws[(((int64_t)b * N2 + f2) * N1 + t1) * p.np + j] : make_float2(0.0f, 0.0f);
+    if constexpr (MODE == 1) {
+        for (int i = threadIdx.x; i < 2 * N1; i += kFftThreads) {
+            const int col = i >= N1 ? 1 : 0, t1 = i - col * N1;
+            wt[col][t1] = cconj(twiddle(((int64_t)t1 * (col ? fb : fa)) & (N - 1), N));
         }
     }
     __syncthreads();
-    float2 *S[2];
-    S[0] = lds_fft(buf[0], buf[1], tw, N1, p.log1, P, false);
-    S[1] = self ? S[0] : lds_fft(buf[2], buf[3], tw, N1, p.log1, P, false);
-    // the other buffer of each pair receives the product
-    float2 *Z[2] = {S[0] == buf[0] ? buf[1] : buf[0], S[1] == buf[2] ? buf[3] : buf[2]};
-    for (int col = 0; col < ncol; ++col) {
-        const int f2 = col ? fb : fa;
-        const float2 *Sp = S[col], *Sm = S[col ^ (self ? 0 : 1)];
-        for (int i = threadIdx.x; i < N1 * P; i += blockDim.x) {
-            const int f1 = i / P, pp = i - f1 * P;
-            const int j = tile * P + pp;
-            // -(N2 f1 + f2) mod N = N2 f1m + (N2 - f2) mod N2: the partner column
+    float2 *S = lds_fft(bufA, bufB, tw, N1, p.log1, lP2, false);
+    float2 *Z = S == bufA ? bufB : bufA;
+    for (int base = 0; base < NP2; base += kBatch * kFftThreads) {
+        float2 h0[kBatch], h1[kBatch];
+        if constexpr (MODE == 1) {
+            // filter spectra of this batch, all loads in flight together
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int i = min(base + u * kFftThreads + (int)threadIdx.x, NP2 - 1);
+                const int f2 = ((i >> logP) & 1) ? fb : fa;
+                const int j = min((tile << logP) + (i & pmask), p.np - 1);
+                const size_t o = ((size_t)f2 * N1 + (i >> lP2)) * p.Gp;
+                h0[u] = p.hs[o + (2 * j) / p.group_size];
+                h1[u] = p.hs[o + (2 * j + 1) / p.group_size];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = base + u * kFftThreads + (int)threadIdx.x;
+            if (i >= NP2) continue;
+            const int f1 = i >> lP2, col = (i >> logP) & 1, pp = i & pmask;
+            const int f2 = col ? fb : fa;
+            const int j = (tile << logP) + pp;
+            // -(N2 f1 + f2) mod N = N2 f1m + (N2 - f2) mod N2: the other column
             const int f1m = (N1 - f1 - (f2 > 0 ? 1 : 0)) & (N1 - 1);
-            const float2 a = Sp[i];
-            const float2 m = cconj(Sm[f1m * P + pp]);
+            const float2 a = S[i];
+            const float2 m = cconj(S[(((f1m << 1) | (col ^ 1)) << logP) + pp]);
             if constexpr (MODE == 0) {
                 // filters 2j and 2j + 1: (a + m)/2 and (a - m)/(2i)
-                if (j < p.np) {
+                if (j < p.np && !(self && col)) {
                     const size_t o = ((size_t)f2 * N1 + f1) * p.Gp + 2 * (size_t)j;
                     p.hs[o] = make_float2(0.5f * (a.x + m.x), 0.5f * (a.y + m.y));
                     p.hs[o + 1] = make_float2(0.5f * (a.y - m.y), -0.5f * (a.x - m.x));
                 }
             } else {
-                float2 z = make_float2(0.0f, 0.0f);
-                if (j < p.np) {
-                    const int g0 = (2 * j) / p.group_size;
-                    const int g1 = min(2 * j + 1, p.D - 1) / p.group_size;
-                    const size_t o = ((size_t)f2 * N1 + f1) * p.Gp;
-                    const float2 h0 = p.hs[o + g0];
-                    if (g1 == g0) {
-                        z = cmul(h0, a);
-                    } else {
-                        const float2 h1 = p.hs[o + g1];
-                        const float2 s = make_float2(0.5f * (h0.x + h1.x), 0.5f * (h0.y + h1.y));
-                        const float2 d = make_float2(0.5f * (h0.x - h1.x), 0.5f * (h0.y - h1.y));
-                        const float2 u = cmul(s, a), v = cmul(d, m);
-                        z = make_float2(u.x + v.x, u.y + v.y);
-                    }
-                }
-                Z[col][i] = z;
+                // (H0 + H1)/2 P[f] + (H0 - H1)/2 conj(P[-f])
+                const float2 sm = make_float2(0.5f * (h0[u].x + h1[u].x), 0.5f * (h0[u].y + h1[u].y));
+                const float2 df = make_float2(0.5f * (h0[u].x - h1[u].x), 0.5f * (h0[u].y - h1[u].y));
+                const float2 pu = cmul(sm, a), pv = cmul(df, m);
+                Z[i] = j < p.np ? make_float2(pu.x + pv.x, pu.y + pv.y) : make_float2(0.0f, 0.0f);
             }
         }
     }
     if constexpr (MODE == 1) {
         __syncthreads();
-        for (int col = 0; col < ncol; ++col) {
-            const int f2 = col ? fb : fa;
-            float2 *other = col ? (Z[1] == buf[2] ? buf[3] : buf[2]) : (Z[0] == buf[0] ? buf[1] : buf[0]);
-            const float2 *U = lds_fft(Z[col], other, tw, N1, p.log1, P, true);
-            for (int i = threadIdx.x; i < N1 * P; i += blockDim.x) {
-                const int t1 = i / P, pp = i - t1 * P;
-                const int j = tile * P + pp;
-                if (j >= p.np) continue;
-                const float2 w = cconj(twiddle(((int64_t)t1 * f2) & (N - 1), N));
-                p.ws[(((int64_t)b * N2 + f2) * N1 + t1) * p.np + j] = cmul(U[i], w);
-            }
+        const float2 *U = lds_fft(Z, S, tw, N1, p.log1, lP2, true);
+        for (int i = threadIdx.x; i < NP2; i += kFftThreads) {
+            const int t1 = i >> lP2, col = (i >> logP) & 1;
+            const int j = (tile << logP) + (i & pmask);
+            if (j >= p.np || (self && col)) continue;
+            p.ws[(((int64_t)b * N2 + (col ? fb : fa)) * N1 + t1) * p.np + j] = cmul(U[i], wt[col][t1]);
         }
     }
 }
 
 // Kernel 3: inverse transform along f2 for one t1, scale, gate, store.
+// LDS (dynamic): two buffers of N2 P values and the N2 inner twiddles.
 template <bool F32>
 __global__ __launch_bounds__(kFftThreads) void fft_out_kernel(FftParams p) {
-    __shared__ float2 buf[2][kFftLds];
-    __shared__ float2 tw[kFftMaxM / 2];
-    const int tile = blockIdx.x % p.n_tiles;
-    const int t1 = (blockIdx.x / p.n_tiles) % p.N1;
-    const int b = blockIdx.x / (p.n_tiles * p.N1);
-    const int P = p.P, N1 = p.N1, N2 = p.N2;
+    extern __shared__ float2 lds[];
+    const int item = xcd_item();
+    const int tile = item % p.n_tiles;
+    const int t1 = (item / p.n_tiles) % p.N1;
+    const int b = item / (p.n_tiles * p.N1);
+    const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1, N2 = p.N2;
+    const int NP = N2 << logP;
     const float scale = 1.0f / ((float)N1 * (float)N2);
+    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + 2 * NP;
+    stage_in(buf0, NP, [&](int i) {
+        const int j = (tile << logP) + (i & pmask);
+        const bool ok = j < p.np;
+        const float2 v = p.ws[(((int64_t)b * N2 + (i >> logP)) * N1 + t1) * p.np + (ok ? j : 0)];
+        return ok ? v : make_float2(0.0f, 0.0f);
+    });
     fill_twiddles(tw, N2);
-    for (int i = threadIdx.x; i < N2 * P; i += blockDim.x) {
-        const int f2 = i / P, pp = i - f2 * P;
-        const int j = tile * P + pp;
-        buf[0][i] = j < p.np ? p.ws[(((int64_t)b * N2 + f2) * N1 + t1) * p.np + j] : make_float2(0.0f, 0.0f);
-    }
     __syncthreads();
-    const float2 *z = lds_fft(buf[0], buf[1], tw, N2, p.log2, P, true);
-    for (int i = threadIdx.x; i < N2 * P; i += blockDim.x) {
-        const int t2 = i / P, pp = i - t2 * P;
-        const int j = tile * P + pp;
+    const float2 *z = lds_fft(buf0, buf1, tw, N2, p.log2, logP, true);
+    for (int i = threadIdx.x; i < NP; i += kFftThreads) {
+        const int t2 = i >> logP;
+        const int j = (tile << logP) + (i & pmask);
         const int64_t t = t1 + (int64_t)N1 * t2;
         if (j >= p.np || t >= p.L) continue;
         const size_t o = ((size_t)b * (size_t)p.L + (size_t)t) * (size_t)p.D + 2 * (size_t)j;
@@ -296,8 +382,24 @@ __global__ __launch_bounds__(kFftThreads) void fft_out_kernel(FftParams p) {
 
 struct FftPlan {
     int64_t N, ws_pairs, hs_bytes, ws_bytes;
-    int N1, N2, log1, log2, P;
+    int N1, N2, log1, log2;
+    int P_rows, P_cols;        // pairs per workgroup of the row and column kernels
+    int lds_rows, lds_cols;    // their LDS bytes
 };
+
+// Pairs per workgroup: LDS of about kFftBudget complex values (several
+// workgroups per CU), at most 64 pairs, no more than the pairs there are; a
+// single pair when even that exceeds the budget (the largest transforms).
+#ifndef HYENA_FFT_BUDGET
+#define HYENA_FFT_BUDGET 4096
+#endif
+constexpr int kFftBudget = HYENA_FFT_BUDGET;
+int pick_pairs(int M, int buffers, int64_t pairs) {
+    int P = 64;
+    while (P > 1 && (int64_t)buffers * M * P > kFftBudget) P >>= 1;
+    while (P > 1 && P / 2 >= pairs) P >>= 1;
+    return P;
+}
 
 int ilog2(int64_t n) {
     int r = 0;
@@ -321,14 +423,13 @@ int fft_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, i
     pl->log2 = logN / 2;
     pl->N1 = 1 << pl->log1;
     pl->N2 = 1 << pl->log2;
-    // pairs per workgroup: the column kernel holds 4 buffers of N1 P values,
-    // the row kernels 2 of N2 P
-    int P = 64;
-    while (P > 1 && (pl->N1 * P > kFftLds / 2 || pl->N2 * P > kFftLds)) P >>= 1;
-    const int64_t pairs = D / 2;
-    while (P > 1 && P / 2 >= pairs) P >>= 1;
-    pl->P = P;
     const int64_t G = D / group_size;
+    const int64_t pairs = D / 2 > (G + 1) / 2 ? D / 2 : (G + 1) / 2;
+    pl->P_rows = pick_pairs(pl->N2, 2, pairs);
+    pl->P_cols = pick_pairs(pl->N1, 4, pairs);
+    pl->lds_rows = (2 * pl->N2 * pl->P_rows + 2 * pl->N2) * (int)sizeof(float2);
+    pl->lds_cols = (4 * pl->N1 * pl->P_cols + 3 * pl->N1) * (int)sizeof(float2);
+    if (pl->lds_rows > kFftMaxLdsBytes || pl->lds_cols > kFftMaxLdsBytes) return HYENA_ERR_UNSUPPORTED;
     const int64_t Gp = G + (G & 1);
     pl->ws_pairs = B * (D / 2) > Gp / 2 ? B * (D / 2) : Gp / 2;
     pl->hs_bytes = pl->N * Gp * (int64_t)sizeof(float2);
@@ -387,33 +488,44 @@ int hyena_conv_fwd_long(const void *q, const void *k, const void *v, const void 
     p.group_size = (int32_t)group_size;
     p.l_h = (int32_t)l_h;
     p.N1 = pl.N1; p.N2 = pl.N2; p.log1 = pl.log1; p.log2 = pl.log2;
-    p.P = pl.P;
     const bool f32 = dtype == HYENA_DTYPE_F32;
     hipStream_t s = (hipStream_t)stream;
 
-    // filter spectra: the filters as one sequence of G channels, l_h rows
+    // One launch: pair tile, grid (batch rows x units x tiles), dynamic LDS.
+    auto launch = [&](const void *fn, FftParams q_, int P, int64_t units, int64_t nb, int lds) -> int {
+        q_.logP = 0;
+        while ((1 << q_.logP) < P) ++q_.logP;
+        q_.n_tiles = (q_.np + P - 1) / P;
+        const int64_t grid = nb * units * q_.n_tiles;
+        if (grid > INT32_MAX) return HYENA_ERR_UNSUPPORTED;
+        if (lds > 64 * 1024 &&
+            hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+            return HYENA_ERR_LAUNCH;
+        void *args[] = {&q_};
+        if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kFftThreads), args, (size_t)lds, s) != hipSuccess)
+            return HYENA_ERR_LAUNCH;
+        return HYENA_OK;
+    };
+    const int64_t cols = pl.N2 / 2 + 1;
+
+    // filter spectra: the filters as one sequence of G channels, min(l_h, L) rows
     FftParams ph = p;
     ph.L = l_h < L ? l_h : L;
     ph.np = p.Gp / 2;
-    ph.n_tiles = (ph.np + p.P - 1) / p.P;
-    const int64_t g_rows = (int64_t)ph.n_tiles * pl.N1;
-    const int64_t g_cols = (int64_t)ph.n_tiles * (pl.N2 / 2 + 1);
-    if (f32) hipLaunchKernelGGL((fft_rows_kernel<true, 1>), dim3((unsigned)g_rows), dim3(kFftThreads), 0, s, ph);
-    else hipLaunchKernelGGL((fft_rows_kernel<false, 1>), dim3((unsigned)g_rows), dim3(kFftThreads), 0, s, ph);
-    hipLaunchKernelGGL((fft_cols_kernel<0>), dim3((unsigned)g_cols), dim3(kFftThreads), 0, s, ph);
-
+    st = launch(f32 ? (const void *)fft_rows_kernel<true, 1> : (const void *)fft_rows_kernel<false, 1>, ph,
+                pl.P_rows, pl.N1, 1, pl.lds_rows);
+    if (st == HYENA_OK) st = launch((const void *)fft_cols_kernel<0>, ph, pl.P_cols, cols, 1, pl.lds_cols);
     // the sequence
     p.L = L;
     p.np = (int32_t)(D / 2);
-    p.n_tiles = (p.np + p.P - 1) / p.P;
-    const int64_t rows = B * p.n_tiles * (int64_t)pl.N1;
-    const int64_t cols = B * p.n_tiles * (int64_t)(pl.N2 / 2 + 1);
-    if (rows > INT32_MAX || cols > INT32_MAX || g_rows > INT32_MAX) return HYENA_ERR_UNSUPPORTED;
-    if (f32) hipLaunchKernelGGL((fft_rows_kernel<true, 0>), dim3((unsigned)rows), dim3(kFftThreads), 0, s, p);
-    else hipLaunchKernelGGL((fft_rows_kernel<false, 0>), dim3((unsigned)rows), dim3(kFftThreads), 0, s, p);
-    hipLaunchKernelGGL((fft_cols_kernel<1>), dim3((unsigned)cols), dim3(kFftThreads), 0, s, p);
-    if (f32) hipLaunchKernelGGL((fft_out_kernel<true>), dim3((unsigned)rows), dim3(kFftThreads), 0, s, p);
-    else hipLaunchKernelGGL((fft_out_kernel<false>), dim3((unsigned)rows), dim3(kFftThreads), 0, s, p);
+    if (st == HYENA_OK)
+        st = launch(f32 ? (const void *)fft_rows_kernel<true, 0> : (const void *)fft_rows_kernel<false, 0>, p,
+                    pl.P_rows, pl.N1, B, pl.lds_rows);
+    if (st == HYENA_OK) st = launch((const void *)fft_cols_kernel<1>, p, pl.P_cols, cols, B, pl.lds_cols);
+    if (st == HYENA_OK)
+        st = launch(f32 ? (const void *)fft_out_kernel<true> : (const void *)fft_out_kernel<false>, p, pl.P_rows,
+                    pl.N1, B, pl.lds_rows);
+    if (st != HYENA_OK) return st;
     if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
     return HYENA_OK;
 }

@@ -157,7 +157,7 @@ int hyena_conv_bwd_workspace(int64_t B, int64_t L, int64_t D,
  * hyena_conv_fwd_ex; taps past row L - 1 never contribute.  Computed as
  *     z = IFFT( FFT(h) * FFT(k (.) v) )[0, L),   y = q (.) z
  * with zero padding to N >= L + min(l_h, L) - 1 (a power of two, at most
- * 2^23), so the circular convolution equals the causal one (StripedHyena 2
+ * 2^22), so the circular convolution equals the causal one (StripedHyena 2
  * explainer: page "01. overview", section 2, long convolutions through the
  * FFT in O(N log N); page "04. hardware-aware convolution kernels", section
  * 1, long filters are FFT-based).  The transforms are fp32 for both dtypes;

@@ -67,6 +67,7 @@ def parse():
     ap.add_argument("--skip-naive", action="store_true")
     ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--skip-chunk-direction", action="store_true")
+    ap.add_argument("--skip-long-filter", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough CPU budget of the oracle baseline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -298,6 +299,10 @@ def main():
     if not args.skip_chunk_direction:
         out["chunk_direction"] = chunk_direction_rates(layers, sets, stream, max(10, K // 4))
 
+    # ---- a long filter (FFT convolution path), at the first layer's shape --
+    if not args.skip_long_filter:
+        out["long_filter"] = long_filter_rates(layers[0], stream, max(5, K // 20))
+
     # ---- backward of each layer (outside the forward step's timed region)
     if not args.skip_backward:
         out["backward"] = backward_rates(layers, sets, stream, max(5, K // 8))
@@ -441,6 +446,44 @@ def chunk_direction_rates(layers, sets, stream, reps):
                                 "achieved_GBs": round(alg / (us * 1e-6) / 1e9, 1),
                                 "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                                 "span_chunks": span, "workgroups": wgs}
+    return res
+
+
+def long_filter_rates(w, stream, reps):
+    """hyena_conv_fwd_long at the layer's B, L, D and group size with a filter
+    as long as the sequence (l_h = L, an LI-length filter), seeded inputs.
+
+    Bytes the three transform kernels move per token*channel (N = 2L, bf16
+    I/O, fp32 complex work area of one value per channel pair and point):
+    rows 4 (k, v) + 8, columns 8 + 8, output 8 + 4 (q, y): 40 B, plus the
+    filter pass.  The operator's own minimum is 8 B (q, k, v read, y written).
+    """
+    import torch
+    import gated_convolution_sequence_amd as hc
+    from workloads import make_inputs
+    lw = w.with_(l_h=w.L, filt="se", seed=w.seed + 50)
+    q, k, v, h = make_inputs(lw, stream.device)
+    y = torch.empty_like(q)
+    code = hc.DTYPE_BF16 if lw.dtype == "bf16" else hc.DTYPE_F32
+    ws_n = hc.long_workspace_bytes(lw.B, lw.L, lw.D, lw.group_size, lw.l_h, code)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
+    for _ in range(2):
+        hc.conv_fwd_long(q, k, v, h, lw.group_size, out=y, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        hc.conv_fwd_long(q, k, v, h, lw.group_size, out=y, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    moved = 40 * lw.elems
+    res = {"B": lw.B, "L": lw.L, "D": lw.D, "group_size": lw.group_size, "l_h": lw.l_h,
+           "us": round(us, 1), "G_tok_ch_per_s": round(lw.elems / (us * 1e-6) / 1e9, 2),
+           "moved_bytes_model": moved, "GBs_moved": round(moved / (us * 1e-6) / 1e9, 1),
+           "frac_of_peak_moved": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+           "workspace_bytes": ws_n, "kernels": 5}
+    del q, k, v, h, y, ws
     return res
 
 

@@ -114,7 +114,7 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cop
     fetch, write = _counter_means(fetch_dir), _counter_means(write_dir)
     layers = {}
     for name, kib in fetch.items():
-        m = re.search(r"hyena_fwd_kernel<false, (\d+), (\d+), (\d+)>", name)
+        m = re.search(r"hyena_fwd_kernel<false, (\d+), (\d+), (\d+)(?:, false, false)?>", name)
         if not m:
             continue
         kh = int(m.group(1))
@@ -123,7 +123,7 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cop
             continue
         fb = kib * 1024.0 * f_scale
         wb = write.get(name, float("nan")) * 1024.0 * w_scale
-        layers[layer] = {"kernel": name.split("(")[0].strip(), "fetch_bytes": round(fb),
+        layers[layer] = {"kernel": m.group(0), "fetch_bytes": round(fb),
                          "write_bytes": round(wb), "hbm_bytes_per_launch": round(fb + wb),
                          "fetch_counter_KiB": round(kib, 1),
                          "write_counter_KiB": round(write.get(name, float("nan")), 1)}

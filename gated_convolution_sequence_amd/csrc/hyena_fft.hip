@@ -42,6 +42,9 @@
 namespace {
 
 constexpr int kFftThreads = 256;
+// with at most 64 pairs per tile, 2P divides the thread count: a thread keeps
+// one channel pair (and one column) across all its strided iterations
+static_assert(kFftThreads % 128 == 0, "pair tiles of up to 64 pairs");
 constexpr int kFftMaxLogN = 22;      // N <= 2^22
 constexpr int kFftMaxLdsBytes = 160 * 1024;
 
@@ -285,27 +288,32 @@ __global__ __launch_bounds__(kFftThreads) void fft_cols_kernel(FftParams p) {
     __syncthreads();
     float2 *S = lds_fft(bufA, bufB, tw, N1, p.log1, lP2, false);
     float2 *Z = S == bufA ? bufB : bufA;
+    // 2P divides the thread count, so a thread always has the same column
+    // and channel pair: its filter spectra rows are fixed
+    const int my_col = (threadIdx.x >> logP) & 1, my_pp = threadIdx.x & pmask;
+    const int my_f2 = my_col ? fb : fa;
+    const int my_j = (tile << logP) + my_pp;
+    const int jc = min(my_j, p.np - 1);
+    const float2 *hrow0 = p.hs + (size_t)my_f2 * N1 * p.Gp + (2 * jc) / p.group_size;
+    const float2 *hrow1 = p.hs + (size_t)my_f2 * N1 * p.Gp + (2 * jc + 1) / p.group_size;
     for (int base = 0; base < NP2; base += kBatch * kFftThreads) {
         float2 h0[kBatch], h1[kBatch];
         if constexpr (MODE == 1) {
             // filter spectra of this batch, all loads in flight together
 #pragma unroll
             for (int u = 0; u < kBatch; ++u) {
-                const int i = min(base + u * kFftThreads + (int)threadIdx.x, NP2 - 1);
-                const int f2 = ((i >> logP) & 1) ? fb : fa;
-                const int j = min((tile << logP) + (i & pmask), p.np - 1);
-                const size_t o = ((size_t)f2 * N1 + (i >> lP2)) * p.Gp;
-                h0[u] = p.hs[o + (2 * j) / p.group_size];
-                h1[u] = p.hs[o + (2 * j + 1) / p.group_size];
+                const int f1 = min(base + u * kFftThreads + (int)threadIdx.x, NP2 - 1) >> lP2;
+                h0[u] = hrow0[(size_t)f1 * p.Gp];
+                h1[u] = hrow1[(size_t)f1 * p.Gp];
             }
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int i = base + u * kFftThreads + (int)threadIdx.x;
             if (i >= NP2) continue;
-            const int f1 = i >> lP2, col = (i >> logP) & 1, pp = i & pmask;
-            const int f2 = col ? fb : fa;
-            const int j = (tile << logP) + pp;
+            const int f1 = i >> lP2, col = my_col, pp = my_pp;
+            const int f2 = my_f2;
+            const int j = my_j;
             // -(N2 f1 + f2) mod N = N2 f1m + (N2 - f2) mod N2: the other column
             const int f1m = (N1 - f1 - (f2 > 0 ? 1 : 0)) & (N1 - 1);
             const float2 a = S[i];

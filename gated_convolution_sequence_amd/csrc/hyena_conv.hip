@@ -1,5 +1,7 @@
-// Hyena-SE / Hyena-MR forward for MI355X (gfx950):
-//     y = q (.) (h * (k (.) v)),  grouped depthwise causal FIR, l_h <= 128.
+// Hyena-SE / Hyena-MR for MI355X (gfx950):
+//     y = q (.) (h * (k (.) v)),  grouped depthwise causal FIR, l_h <= 128,
+// its backward, and the chunk-direction forward for group sizes that are not
+// a multiple of 16.  (Filters of any length: hyena_fft.hip.)
 //
 // Method (StripedHyena 2 explainer, page "04. hardware-aware convolution
 // kernels"):
@@ -17,10 +19,10 @@
 //     gathered from the filter by the difference of its row and column index.
 //
 // gfx950 mapping (l_b = 64 rows, one 16-channel group per wave):
-//   * A workgroup of 4 waves owns a slab of 64 channels (4 groups of 16) and a
-//     span of consecutive 64-row chunks of one batch row.  It first walks the
-//     32*KH rows before the span (the history the first chunk needs), then
-//     the span.
+//   * A workgroup of 8 waves owns a slab of 128 channels (8 groups of 16)
+//     and a span of consecutive 64-row chunks of one batch row, plus the
+//     32*KH rows before the span (the history its first chunks need), which
+//     it reads last (see the walk order below).
 //   * k and v arrive through 16-byte buffer loads, coalesced along channels;
 //     x = k*v is formed in fp32, rounded to bf16 and written to an XOR-swizzled
 //     LDS tile, which each wave re-reads time-major as the MFMA operand.
@@ -34,9 +36,9 @@
 //     skipped (the zero blocks of section 2).
 //   * The previous chunks' X^T fragments stay in registers, so every input
 //     row is read from HBM once per span.
-//   * The epilogue multiplies the fp32 accumulators by q (loaded in the
-//     accumulator layout: 4 consecutive channels per lane), rounds to bf16
-//     and stores 8 bytes per lane.
+//   * The epilogue stages the fp32 accumulators (4 consecutive channels per
+//     lane) through a swizzled LDS tile, reads them row-major, multiplies by
+//     q, rounds to bf16 and writes 16 bytes per lane.
 //   * Buffer resources bound every access: rows before the batch start or
 //     past the span, and channels past D, read as zero and are never
 //     written.  That supplies X_{-1} = 0, ragged last chunks and partial slabs.
@@ -704,7 +706,7 @@ template <bool F32> constexpr int kNumSpansFor = F32 ? 3 : kNumSpans;
 // the l_h - 1 rows before it, in steps of 32 rows (the MFMA's K).  The
 // Toeplitz operand H is shared by all 16 sub-chunks.
 //
-// A workgroup (8 waves) owns 64 channels (fp32: 32) and a span of NB blocks;
+// A workgroup (8 waves) owns 64 channels (fp32: 32) and a span of blocks;
 // wave w takes channels 8w .. 8w + 7 (fp32: 4w .. 4w + 3).  In LDS every
 // channel is a row of times:
 //   * x = k v of the block and the 128 rows before it, in a 384-entry ring,

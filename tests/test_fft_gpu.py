@@ -115,6 +115,28 @@ def test_impulse_reproduces_the_filter(t0):
     assert np.max(np.abs(y[0] - expect)) <= 1e-5 * np.max(np.abs(expect))
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_largest_transform_impulse(dt):
+    """L = l_h = 2^21 (N = 2^22, the largest transform): an impulse at t0 on
+    every channel returns the filter shifted by t0, checked on all rows."""
+    dtype = DTYPES[dt]
+    B, L, D, gs = 1, 1 << 21, 4, 2
+    t0 = 12345
+    g = torch.Generator().manual_seed(21)
+    h = (torch.randn(D // gs, L, generator=g) / math.sqrt(L)).to(dtype)
+    v = torch.zeros(B, L, D, dtype=dtype)
+    v[0, t0, :] = 1.0
+    ones = torch.ones_like(v)
+    log("largest transform %s" % dt)
+    y = run_long(ones.to(DEV), ones.to(DEV), v.to(DEV), h.to(DEV), gs)[0].float().cpu()
+    expect = torch.zeros(L, D)
+    expect[t0:, :] = torch.repeat_interleave(h.float(), gs, dim=0).T[:L - t0]
+    scale = float(expect.abs().max())
+    tol = (1e-2 if dtype == torch.bfloat16 else 1e-5) * scale
+    assert float((y - expect).abs().max()) <= tol
+    assert float(y[:t0].abs().max()) <= tol  # nothing before the impulse
+
+
 def test_matches_the_direct_kernel_for_short_filters():
     """l_h <= 128: the FFT path and the direct grouped kernel agree within their bars."""
     B, L, D, gs, l_h = 2, 5000, 256, 16, 128

@@ -59,6 +59,7 @@ struct FftParams {
     int32_t Gp;          // filters, rounded up to even
     int32_t G, group_size, l_h;
     int32_t N1, N2, log1, log2;
+    int32_t N3, log3;    // third factor (1 for the two-level split)
     int32_t logP, n_tiles;  // pairs per workgroup (log2), pair tiles, of the kernel launched
 };
 
@@ -261,21 +262,25 @@ __global__ __launch_bounds__(kFftThreads) void fft_cols_kernel(FftParams p) {
     extern __shared__ float2 lds[];
     const int item = xcd_item();
     const int tile = item % p.n_tiles;
-    const int c = (item / p.n_tiles) % (p.N2 / 2 + 1);
-    const int b = item / (p.n_tiles * (p.N2 / 2 + 1));
-    const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1, N2 = p.N2;
+    const int N2 = p.N2 * p.N3;  // columns (M of the three-level split)
+    const int c = (item / p.n_tiles) % (N2 / 2 + 1);
+    const int b = item / (p.n_tiles * (N2 / 2 + 1));
+    const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1;
     const int lP2 = logP + 1;
     const int NP2 = N1 << lP2;
     const int64_t N = (int64_t)N1 * N2;
     const int fa = c, fb = (N2 - c) & (N2 - 1);
     const bool self = fa == fb;
+    // work-area position of column f: (f mod N3) N2 + f / N3 (the identity
+    // for the two-level split), so the middle passes work in place
+    auto cpos = [&](int f) -> int64_t { return (int64_t)(f & (p.N3 - 1)) * p.N2 + (f >> p.log3); };
     float2 *bufA = lds, *bufB = lds + NP2, *tw = lds + 2 * NP2;
     float2 *wt[2] = {tw + N1, tw + 2 * N1};
     stage_in(bufA, NP2, [&](int i) {
         const int col = (i >> logP) & 1;
         const int j = (tile << logP) + (i & pmask);
         const bool ok = j < p.np;
-        const float2 v = p.ws[(((int64_t)b * N2 + (col ? fb : fa)) * N1 + (i >> lP2)) * p.np + (ok ? j : 0)];
+        const float2 v = p.ws[(((int64_t)b * N2 + cpos(col ? fb : fa)) * N1 + (i >> lP2)) * p.np + (ok ? j : 0)];
         return ok ? v : make_float2(0.0f, 0.0f);
     });
     fill_twiddles(tw, N1);
@@ -341,7 +346,123 @@ __global__ __launch_bounds__(kFftThreads) void fft_cols_kernel(FftParams p) {
             const int t1 = i >> lP2, col = (i >> logP) & 1;
             const int j = (tile << logP) + (i & pmask);
             if (j >= p.np || (self && col)) continue;
-            p.ws[(((int64_t)b * N2 + (col ? fb : fa)) * N1 + t1) * p.np + j] = cmul(U[i], wt[col][t1]);
+            p.ws[(((int64_t)b * N2 + cpos(col ? fb : fa)) * N1 + t1) * p.np + j] = cmul(U[i], wt[col][t1]);
+        }
+    }
+}
+
+// Three-level split (large N): N = N1 N2 N3, t = t1 + N1 t2 + N1 N2 t3.
+// The M = N2 N3 point transform along t2 + N2 t3 that the row kernel does
+// in one piece is done in two passes, as a four-step of its own:
+//   rows3 (per t1, t2):  N3-point FFT over t3, twiddle W_M^(t2 f3), store at
+//                        work-area position f3 N2 + t2;
+//   mid   (per t1, f3):  N2-point FFT over t2, twiddle W_N^(t1 c) with column
+//                        c = f3 + N3 f2, store at position f3 N2 + f2;
+// after which column c (position (c mod N3) N2 + c / N3) is what the column
+// kernel expects.  The inverse runs mid (inverse, twiddle conj W_M^(t2 f3))
+// and out3 (inverse N3-point FFT over f3, scale, gate, store).
+// LDS (dynamic) of either: two buffers of N3 P (N2 P) values, the inner
+// twiddles and the N3 (N2) inter-step twiddles.
+template <bool F32, int SRC>
+__global__ __launch_bounds__(kFftThreads) void fft_rows3_kernel(FftParams p) {
+    extern __shared__ float2 lds[];
+    const int item = xcd_item();
+    const int tile = item % p.n_tiles;
+    const int t2 = (item / p.n_tiles) % p.N2;
+    const int t1 = (item / (p.n_tiles * p.N2)) % p.N1;
+    const int b = item / (p.n_tiles * p.N2 * p.N1);
+    const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1, N2 = p.N2, N3 = p.N3;
+    const int NP = N3 << logP;
+    const int64_t M = (int64_t)N2 * N3;
+    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + 2 * NP, *wt = tw + N3;
+    stage_in(buf0, NP, [&](int i) {
+        return load_pair<F32, SRC>(p, b, t1 + (int64_t)N1 * (t2 + (int64_t)N2 * (i >> logP)),
+                                   (tile << logP) + (i & pmask));
+    });
+    fill_twiddles(tw, N3);
+    for (int f3 = threadIdx.x; f3 < N3; f3 += kFftThreads) wt[f3] = twiddle(((int64_t)t2 * f3) & (M - 1), M);
+    __syncthreads();
+    const float2 *X = lds_fft(buf0, buf1, tw, N3, p.log3, logP, false);
+    for (int i = threadIdx.x; i < NP; i += kFftThreads) {
+        const int f3 = i >> logP;
+        const int j = (tile << logP) + (i & pmask);
+        if (j >= p.np) continue;
+        p.ws[(((int64_t)b * M + (int64_t)f3 * N2 + t2) * N1 + t1) * p.np + j] = cmul(X[i], wt[f3]);
+    }
+}
+
+template <bool INV>
+__global__ __launch_bounds__(kFftThreads) void fft_mid_kernel(FftParams p) {
+    extern __shared__ float2 lds[];
+    const int item = xcd_item();
+    const int tile = item % p.n_tiles;
+    const int f3 = (item / p.n_tiles) % p.N3;
+    const int t1 = (item / (p.n_tiles * p.N3)) % p.N1;
+    const int b = item / (p.n_tiles * p.N3 * p.N1);
+    const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1, N2 = p.N2, N3 = p.N3;
+    const int NP = N2 << logP;
+    const int64_t M = (int64_t)N2 * N3;
+    const int64_t N = M * N1;
+    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + 2 * NP, *wt = tw + N2;
+    const int64_t row0 = (int64_t)b * M + (int64_t)f3 * N2;  // position of index 0 along t2 / f2
+    stage_in(buf0, NP, [&](int i) {
+        const int j = (tile << logP) + (i & pmask);
+        const bool ok = j < p.np;
+        const float2 v = p.ws[((row0 + (i >> logP)) * N1 + t1) * p.np + (ok ? j : 0)];
+        return ok ? v : make_float2(0.0f, 0.0f);
+    });
+    fill_twiddles(tw, N2);
+    for (int u = threadIdx.x; u < N2; u += kFftThreads)
+        wt[u] = INV ? cconj(twiddle(((int64_t)u * f3) & (M - 1), M))
+                    : twiddle(((int64_t)t1 * (f3 + (int64_t)N3 * u)) & (N - 1), N);
+    __syncthreads();
+    const float2 *X = lds_fft(buf0, buf1, tw, N2, p.log2, logP, INV);
+    for (int i = threadIdx.x; i < NP; i += kFftThreads) {
+        const int u = i >> logP;
+        const int j = (tile << logP) + (i & pmask);
+        if (j >= p.np) continue;
+        p.ws[((row0 + u) * N1 + t1) * p.np + j] = cmul(X[i], wt[u]);
+    }
+}
+
+template <bool F32>
+__global__ __launch_bounds__(kFftThreads) void fft_out3_kernel(FftParams p) {
+    extern __shared__ float2 lds[];
+    const int item = xcd_item();
+    const int tile = item % p.n_tiles;
+    const int t2 = (item / p.n_tiles) % p.N2;
+    const int t1 = (item / (p.n_tiles * p.N2)) % p.N1;
+    const int b = item / (p.n_tiles * p.N2 * p.N1);
+    const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1, N2 = p.N2, N3 = p.N3;
+    const int NP = N3 << logP;
+    const int64_t M = (int64_t)N2 * N3;
+    const float scale = 1.0f / ((float)N1 * (float)M);
+    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + 2 * NP;
+    stage_in(buf0, NP, [&](int i) {
+        const int j = (tile << logP) + (i & pmask);
+        const bool ok = j < p.np;
+        const float2 v = p.ws[(((int64_t)b * M + (int64_t)(i >> logP) * N2 + t2) * N1 + t1) * p.np + (ok ? j : 0)];
+        return ok ? v : make_float2(0.0f, 0.0f);
+    });
+    fill_twiddles(tw, N3);
+    __syncthreads();
+    const float2 *z = lds_fft(buf0, buf1, tw, N3, p.log3, logP, true);
+    for (int i = threadIdx.x; i < NP; i += kFftThreads) {
+        const int t3 = i >> logP;
+        const int j = (tile << logP) + (i & pmask);
+        const int64_t t = t1 + (int64_t)N1 * (t2 + (int64_t)N2 * t3);
+        if (j >= p.np || t >= p.L) continue;
+        const size_t o = ((size_t)b * (size_t)p.L + (size_t)t) * (size_t)p.D + 2 * (size_t)j;
+        const float z0 = z[i].x * scale, z1 = z[i].y * scale;
+        if constexpr (F32) {
+            const float2 qq = *(const float2 *)((const float *)p.q + o);
+            *(float2 *)((float *)p.y + o) = make_float2(qq.x * z0, qq.y * z1);
+        } else {
+            const uint32_t qq = *(const uint32_t *)((const uint16_t *)p.q + o);
+            const __bf16 y0 = (__bf16)(__uint_as_float(qq << 16) * z0);
+            const __bf16 y1 = (__bf16)(__uint_as_float(qq & 0xffff0000u) * z1);
+            *(uint32_t *)((uint16_t *)p.y + o) =
+                (uint32_t)__builtin_bit_cast(uint16_t, y0) | ((uint32_t)__builtin_bit_cast(uint16_t, y1) << 16);
         }
     }
 }
@@ -390,10 +511,15 @@ __global__ __launch_bounds__(kFftThreads) void fft_out_kernel(FftParams p) {
 
 struct FftPlan {
     int64_t N, ws_pairs, hs_bytes, ws_bytes;
-    int N1, N2, log1, log2;
-    int P_rows, P_cols;        // pairs per workgroup of the row and column kernels
-    int lds_rows, lds_cols;    // their LDS bytes
+    int N1, N2, N3, log1, log2, log3;
+    bool three;                      // three-level split (N3 > 1)
+    int P_rows, P_mid, P_cols;       // pairs per workgroup: row (rows3/out3), middle, column kernels
+    int lds_rows, lds_mid, lds_cols; // their LDS bytes
 };
+
+// Largest N done with the two-level split (columns of at most 256 points);
+// above it the three-level split keeps every transform at 256 points or less.
+constexpr int kFftTwoLevelMaxLogN = 16;
 
 // Pairs per workgroup: LDS of about kFftBudget complex values (several
 // workgroups per CU), at most 64 pairs, no more than the pairs there are; a
@@ -427,17 +553,30 @@ int fft_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, i
     if (logN > kFftMaxLogN) return HYENA_ERR_UNSUPPORTED;
     if (D > INT32_MAX / 2 || B > INT32_MAX) return HYENA_ERR_UNSUPPORTED;
     pl->N = (int64_t)1 << logN;
-    pl->log1 = (logN + 1) / 2;
-    pl->log2 = logN / 2;
+    pl->three = logN > kFftTwoLevelMaxLogN;
+    if (pl->three) {
+        pl->log1 = (logN + 2) / 3;
+        pl->log2 = (logN - pl->log1 + 1) / 2;
+        pl->log3 = logN - pl->log1 - pl->log2;
+    } else {
+        pl->log1 = (logN + 1) / 2;
+        pl->log2 = logN / 2;
+        pl->log3 = 0;
+    }
     pl->N1 = 1 << pl->log1;
     pl->N2 = 1 << pl->log2;
+    pl->N3 = 1 << pl->log3;
     const int64_t G = D / group_size;
     const int64_t pairs = D / 2 > (G + 1) / 2 ? D / 2 : (G + 1) / 2;
-    pl->P_rows = pick_pairs(pl->N2, 2, pairs);
+    const int Mr = pl->three ? pl->N3 : pl->N2;  // transform length of the row (and output) kernels
+    pl->P_rows = pick_pairs(Mr, 2, pairs);
+    pl->P_mid = pick_pairs(pl->N2, 2, pairs);
     pl->P_cols = pick_pairs(pl->N1, 4, pairs);
-    pl->lds_rows = (2 * pl->N2 * pl->P_rows + 2 * pl->N2) * (int)sizeof(float2);
+    pl->lds_rows = (2 * Mr * pl->P_rows + 2 * Mr) * (int)sizeof(float2);
+    pl->lds_mid = (2 * pl->N2 * pl->P_mid + 2 * pl->N2) * (int)sizeof(float2);
     pl->lds_cols = (4 * pl->N1 * pl->P_cols + 3 * pl->N1) * (int)sizeof(float2);
-    if (pl->lds_rows > kFftMaxLdsBytes || pl->lds_cols > kFftMaxLdsBytes) return HYENA_ERR_UNSUPPORTED;
+    if (pl->lds_rows > kFftMaxLdsBytes || pl->lds_cols > kFftMaxLdsBytes || pl->lds_mid > kFftMaxLdsBytes)
+        return HYENA_ERR_UNSUPPORTED;
     const int64_t Gp = G + (G & 1);
     pl->ws_pairs = B * (D / 2) > Gp / 2 ? B * (D / 2) : Gp / 2;
     pl->hs_bytes = pl->N * Gp * (int64_t)sizeof(float2);
@@ -496,6 +635,7 @@ int hyena_conv_fwd_long(const void *q, const void *k, const void *v, const void 
     p.group_size = (int32_t)group_size;
     p.l_h = (int32_t)l_h;
     p.N1 = pl.N1; p.N2 = pl.N2; p.log1 = pl.log1; p.log2 = pl.log2;
+    p.N3 = pl.N3; p.log3 = pl.log3;
     const bool f32 = dtype == HYENA_DTYPE_F32;
     hipStream_t s = (hipStream_t)stream;
 
@@ -514,25 +654,40 @@ int hyena_conv_fwd_long(const void *q, const void *k, const void *v, const void 
             return HYENA_ERR_LAUNCH;
         return HYENA_OK;
     };
-    const int64_t cols = pl.N2 / 2 + 1;
+    const int64_t M = (int64_t)pl.N2 * pl.N3;  // columns
+    const int64_t cols = M / 2 + 1;
+    const void *rows_seq, *rows_flt, *out_fn;
+    if (pl.three) {
+        rows_seq = f32 ? (const void *)fft_rows3_kernel<true, 0> : (const void *)fft_rows3_kernel<false, 0>;
+        rows_flt = f32 ? (const void *)fft_rows3_kernel<true, 1> : (const void *)fft_rows3_kernel<false, 1>;
+        out_fn = f32 ? (const void *)fft_out3_kernel<true> : (const void *)fft_out3_kernel<false>;
+    } else {
+        rows_seq = f32 ? (const void *)fft_rows_kernel<true, 0> : (const void *)fft_rows_kernel<false, 0>;
+        rows_flt = f32 ? (const void *)fft_rows_kernel<true, 1> : (const void *)fft_rows_kernel<false, 1>;
+        out_fn = f32 ? (const void *)fft_out_kernel<true> : (const void *)fft_out_kernel<false>;
+    }
+    // units per batch row of the row and output kernels: t1 (x t2 when three-level)
+    const int64_t row_units = pl.three ? (int64_t)pl.N1 * pl.N2 : pl.N1;
+    const int64_t mid_units = (int64_t)pl.N1 * pl.N3;
 
     // filter spectra: the filters as one sequence of G channels, min(l_h, L) rows
     FftParams ph = p;
     ph.L = l_h < L ? l_h : L;
     ph.np = p.Gp / 2;
-    st = launch(f32 ? (const void *)fft_rows_kernel<true, 1> : (const void *)fft_rows_kernel<false, 1>, ph,
-                pl.P_rows, pl.N1, 1, pl.lds_rows);
+    st = launch(rows_flt, ph, pl.P_rows, row_units, 1, pl.lds_rows);
+    if (st == HYENA_OK && pl.three)
+        st = launch((const void *)fft_mid_kernel<false>, ph, pl.P_mid, mid_units, 1, pl.lds_mid);
     if (st == HYENA_OK) st = launch((const void *)fft_cols_kernel<0>, ph, pl.P_cols, cols, 1, pl.lds_cols);
     // the sequence
     p.L = L;
     p.np = (int32_t)(D / 2);
-    if (st == HYENA_OK)
-        st = launch(f32 ? (const void *)fft_rows_kernel<true, 0> : (const void *)fft_rows_kernel<false, 0>, p,
-                    pl.P_rows, pl.N1, B, pl.lds_rows);
+    if (st == HYENA_OK) st = launch(rows_seq, p, pl.P_rows, row_units, B, pl.lds_rows);
+    if (st == HYENA_OK && pl.three)
+        st = launch((const void *)fft_mid_kernel<false>, p, pl.P_mid, mid_units, B, pl.lds_mid);
     if (st == HYENA_OK) st = launch((const void *)fft_cols_kernel<1>, p, pl.P_cols, cols, B, pl.lds_cols);
-    if (st == HYENA_OK)
-        st = launch(f32 ? (const void *)fft_out_kernel<true> : (const void *)fft_out_kernel<false>, p, pl.P_rows,
-                    pl.N1, B, pl.lds_rows);
+    if (st == HYENA_OK && pl.three)
+        st = launch((const void *)fft_mid_kernel<true>, p, pl.P_mid, mid_units, B, pl.lds_mid);
+    if (st == HYENA_OK) st = launch(out_fn, p, pl.P_rows, row_units, B, pl.lds_rows);
     if (st != HYENA_OK) return st;
     if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
     return HYENA_OK;

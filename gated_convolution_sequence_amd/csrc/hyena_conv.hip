@@ -727,24 +727,37 @@ constexpr int kCdBlock = 256;    // rows per block (16 sub-chunks of 16)
 constexpr int kCdRing = 384;     // ring entries per channel: a block + 128 history rows
 constexpr int kCdTapOff = 32;    // tap tables: entry m + 32 holds tap (pair) m
 
+// Waves per workgroup of the chunk-direction kernel; each wave owns one
+// 16-byte row segment of the slab.  Measured at B=1, L=8192, D=4096 on
+// MI355X: 8 waves (128-byte row segments, one workgroup per CU) 60 / 67 us
+// for SE / MR with one filter per channel; 4 waves (64-byte segments, two
+// or three workgroups per CU) 99 / 106 us.
+#ifndef HYENA_CD_WAVES
+#define HYENA_CD_WAVES 8
+#endif
+constexpr int kCdWaves = HYENA_CD_WAVES;
+constexpr int kCdThreads = 64 * kCdWaves;
+
 template <bool F32> struct CdTr {
     static constexpr int EB = F32 ? 4 : 2;
-    static constexpr int SLAB = F32 ? 32 : 64;           // channels per workgroup
     static constexpr int VEC = 16 / EB;                  // channels (or times) per 16 bytes
-    static constexpr int CPW = SLAB / kWaves;            // channels per wave
+    static constexpr int SLAB = VEC * kCdWaves;          // channels per workgroup (a wave: one row segment)
+    static constexpr int SEGS = SLAB / VEC;              // 16-byte segments per row of the slab
+    static constexpr int CPW = SLAB / kCdWaves;          // channels per wave
     static constexpr int RING_B = kCdRing * EB;          // LDS bytes per channel ring
     static constexpr int QY_B = kCdBlock * EB;           // LDS bytes per channel gate row
     static_assert(CPW == VEC, "a wave's channels are one row segment (one swizzle key)");
-    static_assert(SLAB / VEC * (kCdBlock / 4) == kThreads, "4 rows x 16 bytes per thread tile a block");
+    static_assert(SEGS * (kCdBlock / 4) == kCdThreads, "4 rows x 16 bytes per thread tile a block");
+    static_assert(SEGS <= 8, "swizzle keys 0..7");
 };
 
 template <bool F32, int KH>
-__global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
+__global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
     using T = CdTr<F32>;
     constexpr int SLAB = T::SLAB;
     constexpr int HROWS = 32 * KH;
     constexpr int PTN = HROWS + 48;      // tap-table entries per channel
-    constexpr int NPT = (SLAB * PTN + kThreads - 1) / kThreads;
+    constexpr int NPT = (SLAB * PTN + kCdThreads - 1) / kCdThreads;
     __shared__ __attribute__((aligned(16))) unsigned char xr[SLAB * T::RING_B];
     __shared__ __attribute__((aligned(16))) unsigned char qy[SLAB * T::QY_B];
     __shared__ uint32_t pt[SLAB * PTN];
@@ -755,7 +768,14 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
     const int n16 = l & 15;
     const int q4 = l >> 4;
 
-    int bid = blockIdx.x;
+    // Work item: workgroups are dealt to the 8 XCDs in turn, each with its
+    // own L2; consecutive items (neighbouring slabs, which share 128-byte
+    // lines) go to consecutive workgroups of one XCD.
+    int bid;
+    {
+        const int n = gridDim.x, g = blockIdx.x, per = n >> 3, rem = n & 7, x = g & 7;
+        bid = x * per + min(x, rem) + (g >> 3);
+    }
     const int slab = bid % p.n_slabs;
     bid /= p.n_slabs;
     const int spn = bid % p.n_spans;
@@ -783,8 +803,8 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
 
     // I/O tile of this thread: rows 4 g4 .. 4 g4 + 3 of a block, channels
     // VEC sg .. VEC sg + VEC - 1 (one 16-byte row segment).
-    const int sg = tid & 7;
-    const int g4 = tid >> 3;
+    const int sg = tid % T::SEGS;
+    const int g4 = tid / T::SEGS;
     const bool seg_ok = c_begin + sg * T::VEC < p.D;
     auto off = [&](int r, bool need) -> uint32_t {
         return (seg_ok && need) ? (uint32_t)(r * row_bytes + sg * 16) : kOOB;
@@ -833,7 +853,7 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
     uint32_t tap_lo[NPT], tap_hi[NPT];
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
-        const int i = tid + j * kThreads;
+        const int i = tid + j * kCdThreads;
         const int dl = i / PTN, m = i % PTN - kCdTapOff;
         const int ch = c_begin + dl;
         const bool chok = i < SLAB * PTN && ch < p.D;
@@ -855,7 +875,7 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_cd_kernel(Params p) {
     }
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
-        const int i = tid + j * kThreads;
+        const int i = tid + j * kCdThreads;
         if (i < SLAB * PTN) pt[i] = tap_lo[j] | (tap_hi[j] << 16);
     }
 
@@ -1115,12 +1135,12 @@ int make_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, 
 
 // Plan of the chunk-direction kernel (group sizes not a multiple of 16).
 // A workgroup owns CdTr::SLAB channels of one batch row and a span of
-// 256-row blocks; it needs most of a CU's LDS, so one runs per CU.  By
-// default the spans are as long as it takes to make about one workgroup per
-// CU (kCdWorkgroups), which reads the history rows and stages the taps once
-// per span; `span_req` (in 64-row chunks) overrides.  `span` is reported in
+// 256-row blocks.  By default the spans are as long as it takes to make
+// about as many workgroups as the CUs hold at once (kCdWorkgroups: 256 CUs,
+// one 8-wave workgroup each), which reads the history rows and stages the
+// taps once per span; `span_req` (in 64-row chunks) overrides.  `span` is reported in
 // chunks.  Buffer windows are per block, so spans have no length limit.
-constexpr int64_t kCdWorkgroups = 256;
+constexpr int64_t kCdWorkgroups = 256 * (8 / kCdWaves);
 
 int cd_plan(int64_t B, int64_t L, int64_t D, int64_t l_h, int dtype, int64_t span_req, Plan *pl) {
     const bool f32 = dtype == HYENA_DTYPE_F32;
@@ -1222,7 +1242,8 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
                                    : pick_kernel<false, kCd>(pl.kh, pl.span_index))
                             : (f32 ? pick_kernel<true, kFwd>(pl.kh, pl.span_index)
                                    : pick_kernel<false, kFwd>(pl.kh, pl.span_index));
-    hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(kThreads), 0, (hipStream_t)stream, p);
+    hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(chunk_dir ? kCdThreads : kThreads), 0,
+                       (hipStream_t)stream, p);
     if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
     return HYENA_OK;
 }

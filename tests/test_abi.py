@@ -121,7 +121,7 @@ def test_plan_split(B, L, D, l_h, dtype, span, expect_span):
 def test_plan_split_chunk_direction(B, L, D, gs, l_h, dtype, span, expect_span):
     s, wgs = hc.plan(B, L, D, gs, l_h, dtype, span)
     assert s == expect_span
-    slab = 32 if dtype == hc.DTYPE_F32 else 64
+    slab = 32 if dtype == hc.DTYPE_F32 else 64  # 8 waves x one 16-byte row segment each
     blocks = -(-L // 256)
     assert wgs == B * (-(-D // slab)) * (-(-blocks // (s // 4)))
 

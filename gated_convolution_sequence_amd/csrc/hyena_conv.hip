@@ -274,13 +274,15 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     constexpr int NG = DUAL ? 2 : 1;  // gates per row
     u32x4_t kr[PF][T::NLD], vr[PF][T::NLD], qr[PF][NG][T::NLD];
 
-    // The last H chunks of a span are the next span's history: they are
-    // loaded with the default (L2-allocating) policy so that the neighbour's
-    // history read hits; every other row is read once and streams past L2.
+    // The last H chunks of a span are the next span's history.  Both reads
+    // of those rows, as the span's own chunks and as the neighbour's history,
+    // use the default (L2-allocating) policy, so whichever workgroup comes
+    // second hits in L2 (measured: 2% faster for l_h = 128 than streaming
+    // the history reads).  Every other row is read once and streams past L2.
     auto load_kv = [&](int item, u32x4_t *kd, u32x4_t *vd) {
         const bool need = item < NI;
         const int c = need ? item_chunk(item) : S;
-        const bool keep = need && item < S && item >= S - H;
+        const bool keep = need && item >= S - H;
         // a chunk lies wholly before or wholly after row 0 (spans start on
         // chunk boundaries); before it, read the prefix rows P + t
         const int64_t t0c = t_begin + (int64_t)c * kChunk;

@@ -519,19 +519,28 @@ struct DhParams {
     int32_t D, l_h, n_spans, n_slabs;
 };
 
+// One chunk of q, k, v and dy in flight per workgroup, and at most 128
+// VGPRs (4 waves per SIMD): with its 72 KiB of LDS (bf16, l_h = 128) two
+// workgroups share a CU and overlap each other's loads, which measured
+// faster than two chunks in flight with one workgroup per CU.
 template <bool F32, int KH, int S>
-__global__ __launch_bounds__(kThreads) void hyena_bwd_dh_kernel(DhParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void hyena_bwd_dh_kernel(DhParams p) {
     using T = Tr<F32>;
-    constexpr int PF = 2;
+    constexpr int PF = 1;
     constexpr int HROWS = 32 * KH;
     constexpr int H = (HROWS + kChunk - 1) / kChunk;      // history chunks
     constexpr int RING = H + 1;                           // x chunks resident
     constexpr int NDL = 2 * KH + 1;                       // diagonals (16-row units)
     constexpr int PITCH = kSlab * T::EB;
+    constexpr int TILE_B = kChunk * PITCH;                // one row-major chunk tile
+    constexpr int WALK_B = (RING + 1) * TILE_B;           // x ring + dz tile
+    constexpr int LAG_B = kWaves * NDL * 256 * 4;         // every wave's P tiles
 
-    __shared__ __attribute__((aligned(16))) unsigned char xr[RING][kChunk * PITCH];
-    __shared__ __attribute__((aligned(16))) unsigned char dzs[kChunk * PITCH];
-    __shared__ float acc_s[kWaves][256];
+    // One LDS area: the x ring and the dz tile during the walk, then the P
+    // tiles for the lag sums.
+    __shared__ __attribute__((aligned(16))) unsigned char lds[WALK_B > LAG_B ? WALK_B : LAG_B];
+    auto xr = [&](int i) -> unsigned char * { return lds + i * TILE_B; };
+    unsigned char *const dzs = lds + RING * TILE_B;
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -617,7 +626,7 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dh_kernel(DhParams p) {
 #pragma unroll
     for (int c = -H; c < S; ++c) {
         const int slot = (c + H) % PF;
-        unsigned char *xt = xr[(c + H) % RING];
+        unsigned char *xt = xr((c + H) % RING);
         put(xt, kr[slot], vr[slot]);
         if (c >= 0) put(dzs, dr[slot], qr[slot]);
         load(c + PF, slot);
@@ -632,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dh_kernel(DhParams p) {
                     const int bt = a - d;                         // input tile, may be < 0
                     const int cb = c + (bt < 0 ? -((-bt + 3) / 4) : 0);  // its chunk
                     const int rb = 16 * (bt - 4 * (cb - c)) + n16;       // its row in that chunk
-                    const unsigned char *xt2 = xr[(cb + H + 4 * RING) % RING];
+                    const unsigned char *xt2 = xr((cb + H + 4 * RING) % RING);
                     if constexpr (F32) {
                         const f32x4_t av = *(const f32x4_t *)(&dzs[lds_addr(ra, kbyte)]);
                         const f32x4_t bv = *(const f32x4_t *)(&xt2[lds_addr(rb, kbyte)]);
@@ -650,21 +659,29 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dh_kernel(DhParams p) {
         }
         __syncthreads();  // dzs and the oldest x chunk are rewritten next
     }
-    // lags: element i of lane (n16, q4) in P[d] is lag 16 d + 4 q4 + i - n16
-    for (int i = l; i < 256; i += 64) acc_s[w][i] = 0.0f;
-    __syncthreads();
+    // Lags.  Element i of lane (n16, q4) of P[d] is row 4 q4 + i (a dz row)
+    // and column n16 (an x row) of a 16 x 16 tile on diagonal d: lag
+    // 16 d + 4 q4 + i - n16.  The tiles go to LDS, stored [d][column][row]
+    // (the walk's buffers are free after its last barrier), and each lane
+    // sums the tile diagonals of its lags in a fixed order: no atomics, and
+    // the same bits on every run.
+    float *const pt = (float *)lds + w * (NDL * 256);
 #pragma unroll
-    for (int d = 0; d < NDL; ++d)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int lag = 16 * d + 4 * q4 + i - n16;
-            if (lag >= 0 && lag < p.l_h) atomicAdd(&acc_s[w][lag], P[d][i]);
-        }
+    for (int d = 0; d < NDL; ++d) *(f32x4_t *)(&pt[d * 256 + n16 * 16 + 4 * q4]) = P[d];
     __syncthreads();
     const int tile = slab * kWaves + w;
     if (c_begin + w * kTile < p.D) {
         float *dst = p.ws + ((size_t)(b * p.n_spans + spn) * (size_t)(p.D / kTile) + tile) * p.l_h;
-        for (int i = l; i < p.l_h; i += 64) dst[i] = acc_s[w][i];
+        for (int lag = l; lag < p.l_h; lag += 64) {
+            float sum = 0.0f;
+            for (int d = 0; d < NDL; ++d) {
+                const int m = lag - 16 * d;  // row - column on tile d
+                if (m < -15 || m > 15) continue;
+                const int c0 = m < 0 ? -m : 0, c1 = m > 0 ? 15 - m : 15;
+                for (int col = c0; col <= c1; ++col) sum += pt[d * 256 + col * 17 + m];
+            }
+            dst[lag] = sum;
+        }
     }
 }
 

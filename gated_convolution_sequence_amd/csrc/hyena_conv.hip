@@ -515,8 +515,11 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
 struct DhParams {
     const void *q, *k, *v, *dy;
     float *ws;          // [B * n_spans][D / 16][l_h] partial sums
+    const void *h;      // filters (the fused dq form only)
+    void *dq;           // dq output (the fused dq form only)
     int64_t L;
     int32_t D, l_h, n_spans, n_slabs;
+    int32_t group_size; // (the fused dq form only)
 };
 
 // One chunk of q, k, v and dy in flight per workgroup, and at most 128
@@ -676,6 +679,246 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             float sum = 0.0f;
             for (int d = 0; d < NDL; ++d) {
                 const int m = lag - 16 * d;  // row - column on tile d
+                if (m < -15 || m > 15) continue;
+                const int c0 = m < 0 ? -m : 0, c1 = m > 0 ? 15 - m : 15;
+                for (int col = c0; col <= c1; ++col) sum += pt[d * 256 + col * 17 + m];
+            }
+            dst[lag] = sum;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dq and filter-gradient pass 1 in one walk (bf16).  dq = dy (h * x) is the
+// forward operator with dy as the gate, and the filter gradient pairs dz =
+// dy q with x = k v; both read the same rows of q, k, v and dy, so one pass
+// over them serves both (10 bytes per token-channel instead of 8 + 8).  The
+// walk is the filter-gradient kernel's (history chunks first, x chunks in an
+// LDS ring); the forward's Toeplitz GEMMs (page "04. hardware-aware
+// convolution kernels", sections 3-4) read their time-major operand
+// fragments from the same ring, keeping the previous chunks' fragments in
+// registers.  The ring's swizzle, 16-byte segment XOR (row & 15) ^ 4 (bit 4
+// of the row), is conflict-free for both reads: 16 consecutive rows at one
+// channel quad (the gradient's products) and 4 row groups of 8 at one
+// channel (the convolution's fragments).
+// ---------------------------------------------------------------------------
+template <int KH, int S, int PF>
+__global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
+    using T = Tr<false>;
+    using M = Mma<false>;
+    using frag = M::frag;
+    constexpr int HROWS = 32 * KH;
+    constexpr int H = (HROWS + kChunk - 1) / kChunk;      // history chunks
+    constexpr int RING = H + 1;                           // x chunks resident
+    constexpr int NDL = 2 * KH + 1;                       // diagonals (16-row units)
+    constexpr int NH = HROWS / M::ROWS;                   // history fragments
+    constexpr int NX = NH + M::FPC;                       // fragments one chunk reads
+    constexpr int NE = 4 + 2 * KH;                        // Toeplitz fragments
+    constexpr int PITCH = T::PITCH;
+    constexpr int TILE_B = kChunk * PITCH;
+    constexpr int ST_PITCH = kSlab * 4;                   // fp32 staging row, bytes
+    constexpr int WALK_B = (RING + 1) * TILE_B + kChunk * ST_PITCH;  // ring, dz, staging
+    constexpr int LAG_B = kWaves * NDL * 256 * 4;
+
+    __shared__ __attribute__((aligned(16))) unsigned char lds[WALK_B > LAG_B ? WALK_B : LAG_B];
+    __shared__ float hs[kWaves][kHLen];
+    auto xr = [&](int i) -> unsigned char * { return lds + i * TILE_B; };
+    unsigned char *const dzs = lds + RING * TILE_B;
+    unsigned char *const st = lds + (RING + 1) * TILE_B;
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int l = tid & 63;
+    const int n16 = l & 15;
+    const int q4 = l >> 4;
+
+    int bid = blockIdx.x;
+    const int slab = bid % p.n_slabs;
+    bid /= p.n_slabs;
+    const int spn = bid % p.n_spans;
+    const int b = bid / p.n_spans;
+
+    const int64_t t_begin = (int64_t)spn * S * kChunk;
+    const int64_t t_stop = min(p.L, t_begin + (int64_t)S * kChunk);
+    const int64_t base_row = max((int64_t)0, t_begin - HROWS);
+    const int c_begin = slab * kSlab;
+    const int row_bytes = p.D * T::EB;
+    const size_t base_off = ((size_t)b * (size_t)p.L + (size_t)base_row) * (size_t)row_bytes +
+                            (size_t)c_begin * T::EB;
+    const uint32_t nrec = (uint32_t)((t_stop - base_row) * row_bytes - c_begin * T::EB);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.dy + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rdq = make_rsrc((char *)p.dq + base_off, nrec);
+    const int row0 = (int)(t_begin - base_row);
+
+    // ---- stage this wave's filter (zero outside [0, l_h)) -----------------
+    const bool tile_ok = c_begin + w * kTile < p.D;
+    {
+        const int g = tile_ok ? (c_begin + w * kTile) / p.group_size : 0;
+        for (int i = l; i < kHLen; i += 64) {
+            const int tap = i - kHOff;
+            float hv = 0.0f;
+            if (tile_ok && tap >= 0 && tap < p.l_h) hv = bf_lo(((const uint16_t *)p.h)[(size_t)g * p.l_h + tap]);
+            hs[w][i] = hv;
+        }
+    }
+
+    const int ld_row = tid / T::TPR;
+    const int ld_seg = tid % T::TPR;
+    const bool seg_ok = c_begin + ld_seg * T::VEC < p.D;
+    const int ld_base = ld_row * row_bytes + ld_seg * 16;
+    auto off = [&](int c, int i, bool need) -> uint32_t {
+        const int r = (row0 + c * kChunk + i * T::RPL) * row_bytes + ld_base;
+        return (seg_ok && need) ? (uint32_t)r : kOOB;
+    };
+    auto lds_addr = [&](int row, int byte) -> int {
+        const int f = (row & 15) ^ (((row >> 4) & 1) << 2);
+        return row * PITCH + ((((byte >> 4) ^ f)) << 4) + (byte & 15);
+    };
+
+    u32x4_t kr[PF][T::NLD], vr[PF][T::NLD], qr[PF][T::NLD], dr[PF][T::NLD];
+    // chunks -H .. S-1 in order; history chunks need no q, dy
+    auto load = [&](int c, int slot) {
+        const bool need = c < S;
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const uint32_t o = off(c, i, need);
+            const uint32_t og = off(c, i, need && c >= 0);
+            kr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadPolicy));
+            vr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kLoadPolicy));
+            qr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, og, 0, kLoadPolicy));
+            dr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rd, og, 0, kLoadPolicy));
+        }
+    };
+    // elementwise product of two 16-byte vectors, rounded to bf16 -> LDS tile
+    auto put = [&](unsigned char *tile, const u32x4_t *a, const u32x4_t *b2) {
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const int row = i * T::RPL + ld_row;
+            u32x4_t xv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                xv[e] = pack_bf16(bf_lo(a[i][e]) * bf_lo(b2[i][e]), bf_hi(a[i][e]) * bf_hi(b2[i][e]));
+            *(u32x4_t *)(&tile[lds_addr(row, ld_seg * 16)]) = xv;
+        }
+    };
+    auto st_addr = [&](int row, int seg) -> int { return row * ST_PITCH + ((seg ^ (row & 15)) << 4); };
+
+#pragma unroll
+    for (int s = 0; s < PF; ++s) load(-H + s, s);
+    __syncthreads();  // filters staged
+
+    // Toeplitz operand fragments (B = H^T), as in the forward kernel.
+    frag F[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) F[e][j] = (__bf16)hs[w][16 * e + n16 - 8 * q4 - j + kHOff];
+    // Time-major fragment reads (A = X^T: lane n16 = channel 16 w + n16,
+    // element j = row 8 q4 + j of a 32-row step): the byte offsets of the
+    // eight rows within a tile, each lds_addr(row, 2 channel).
+    const int ch = w * kTile + n16;
+    const int gq = (8 * (q4 & 1)) ^ ((q4 >> 1) << 2);
+    int fr_off[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        fr_off[j] = (8 * q4 + j) * PITCH + ((((ch >> 3) ^ gq ^ j)) << 4) + ((ch & 7) << 1);
+    auto read_frags = [&](const unsigned char *tb, frag *dst) {
+#pragma unroll
+        for (int kk = 0; kk < M::FPC; ++kk)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                dst[kk][j] = __builtin_bit_cast(__bf16, *(const uint16_t *)(&tb[fr_off[j] + 32 * kk * PITCH]));
+    };
+
+    frag X[NX];
+#pragma unroll
+    for (int i = 0; i < NX; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) X[i][j] = (__bf16)0.0f;
+    f32x4_t P[NDL];
+#pragma unroll
+    for (int d = 0; d < NDL; ++d) P[d] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int kbyte = (w * kTile + 4 * q4) * T::EB;  // this lane's 4 channels (gradient K)
+
+#pragma unroll
+    for (int c = -H; c < S; ++c) {
+        const int slot = (c + H) % PF;
+        unsigned char *xt = xr((c + H) % RING);
+        put(xt, kr[slot], vr[slot]);
+        u32x4_t dyc[T::NLD];
+        if (c >= 0) {
+            put(dzs, dr[slot], qr[slot]);
+#pragma unroll
+            for (int i = 0; i < T::NLD; ++i) dyc[i] = dr[slot][i];
+        }
+        load(c + PF, slot);
+        __syncthreads();
+        read_frags(xt, &X[NH]);
+        if (c >= 0) {
+            // filter gradient: P[d] += dz rows (16 a + n16) . x rows 16 (a - d) + n16
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int ra = 16 * a + n16;
+                typedef short s16x4_t __attribute__((ext_vector_type(4)));
+                const s16x4_t av = *(const s16x4_t *)(&dzs[lds_addr(ra, kbyte)]);
+#pragma unroll
+                for (int d = 0; d < NDL; ++d) {
+                    const int bt = a - d;
+                    const int cb = c + (bt < 0 ? -((-bt + 3) / 4) : 0);
+                    const int rb = 16 * (bt - 4 * (cb - c)) + n16;
+                    const unsigned char *xt2 = xr((cb + H + 4 * RING) % RING);
+                    const s16x4_t bv = *(const s16x4_t *)(&xt2[lds_addr(rb, kbyte)]);
+                    P[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, P[d], 0, 0, 0);
+                }
+            }
+            // dq: the convolved chunk, 16 output rows per tile nt
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kk = 0; kk < NX; ++kk) {
+                    const int e = nt - 2 * (kk - NH);
+                    if (e < 0) continue;
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(X[kk], F[e], acc, 0, 0, 0);
+                }
+                *(f32x4_t *)(&st[st_addr(16 * nt + n16, 4 * w + q4)]) = acc;
+            }
+        }
+        __syncthreads();  // st complete; every read of dzs and of the oldest x chunk done
+        if (c >= 0) {
+#pragma unroll
+            for (int i = 0; i < T::NLD; ++i) {
+                const int row = i * T::RPL + ld_row;
+                const f32x4_t a0 = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg)]);
+                const f32x4_t a1 = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg + 1)]);
+                const u32x4_t g = dyc[i];
+                u32x4_t yv;
+                yv[0] = pack_bf16(bf_lo(g[0]) * a0[0], bf_hi(g[0]) * a0[1]);
+                yv[1] = pack_bf16(bf_lo(g[1]) * a0[2], bf_hi(g[1]) * a0[3]);
+                yv[2] = pack_bf16(bf_lo(g[2]) * a1[0], bf_hi(g[2]) * a1[1]);
+                yv[3] = pack_bf16(bf_lo(g[3]) * a1[2], bf_hi(g[3]) * a1[3]);
+                __builtin_amdgcn_raw_buffer_store_b128(yv, rdq, off(c, i, true), 0, kStorePolicy);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NH; ++i) X[i] = X[i + M::FPC];
+    }
+    __syncthreads();  // the staging tile is read; the lag tiles overwrite it
+    // Lags, as in the filter-gradient kernel.
+    float *const pt = (float *)lds + w * (NDL * 256);
+#pragma unroll
+    for (int d = 0; d < NDL; ++d) *(f32x4_t *)(&pt[d * 256 + n16 * 16 + 4 * q4]) = P[d];
+    __syncthreads();
+    const int tile = slab * kWaves + w;
+    if (tile_ok) {
+        float *dst = p.ws + ((size_t)(b * p.n_spans + spn) * (size_t)(p.D / kTile) + tile) * p.l_h;
+        for (int lag = l; lag < p.l_h; lag += 64) {
+            float sum = 0.0f;
+            for (int d = 0; d < NDL; ++d) {
+                const int m = lag - 16 * d;
                 if (m < -15 || m > 15) continue;
                 const int c0 = m < 0 ? -m : 0, c1 = m > 0 ? 15 - m : 15;
                 for (int col = c0; col <= c1; ++col) sum += pt[d * 256 + col * 17 + m];
@@ -1054,14 +1297,16 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
 }
 
 // Kernel families and their compiled span counts (indices into kSpans).
-enum Family { kFwd = 0, kRevDual = 1, kDh = 2, kCd = 3 };
+enum Family { kFwd = 0, kRevDual = 1, kDh = 2, kCd = 3, kDqDh = 4 };
 // (the chunk-direction kernel takes its span at run time: one entry)
 template <bool F32, int Fam> constexpr int kSpanCount =
-    Fam == kFwd ? kNumSpansFor<F32> : Fam == kRevDual ? (F32 ? 2 : 4) : Fam == kDh ? (F32 ? 3 : 5) : 1;
+    Fam == kFwd ? kNumSpansFor<F32> : Fam == kRevDual ? (F32 ? 2 : 4) : Fam == kDh ? (F32 ? 3 : 5)
+    : Fam == kDqDh ? 5 : 1;
 
 typedef void (*DhFn)(DhParams);
 template <bool F32, int Fam> struct FnType { typedef KernelFn type; };
 template <bool F32> struct FnType<F32, kDh> { typedef DhFn type; };
+template <bool F32> struct FnType<F32, kDqDh> { typedef DhFn type; };
 
 template <bool F32, int Fam, int KH, int Sp>
 constexpr typename FnType<F32, Fam>::type kernel_of() {
@@ -1071,6 +1316,8 @@ constexpr typename FnType<F32, Fam>::type kernel_of() {
         return hyena_fwd_kernel<F32, KH, kPrefetch<F32>, Sp, true, true>;
     else if constexpr (Fam == kDh)
         return hyena_bwd_dh_kernel<F32, KH, Sp>;
+    else if constexpr (Fam == kDqDh)
+        return hyena_bwd_dq_dh_kernel<KH, Sp, 1>;  // bf16 only
     else
         return hyena_fwd_cd_kernel<F32, KH>;
 }
@@ -1349,9 +1596,11 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
     }
     if (group_size % kTile != 0) return HYENA_ERR_UNSUPPORTED;
     const bool f32 = dtype == HYENA_DTYPE_F32;
+    // bf16 with both dq and dh: one kernel computes both (below)
+    const bool fused_dq = dq && dh && !f32;
 
     // dq = dy * (h * (k v)): the forward with dy as the gate
-    if (dq) {
+    if (dq && !fused_dq) {
         st = fwd_launch(dy, k, v, h, nullptr, nullptr, 0, B, L, D, group_size, l_h, dq, dtype, 0, stream);
         if (st != HYENA_OK) return st;
     }
@@ -1376,18 +1625,23 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
         hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(kThreads), 0, (hipStream_t)stream, p);
         if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
     }
-    // dh: partial sums per span (pass 1), then their reduction (pass 2)
+    // dh: partial sums per span (pass 1, with dq when fused), then their
+    // reduction (pass 2)
     if (dh) {
         DhParams p;
         p.q = q; p.k = k; p.v = v; p.dy = dy;
         p.ws = (float *)workspace;
+        p.h = h;
+        p.dq = fused_dq ? dq : nullptr;
         p.L = L;
         p.D = (int32_t)D;
         p.l_h = (int32_t)l_h;
         p.n_spans = (int32_t)dpl.n_spans;
         p.n_slabs = (int32_t)dpl.n_slabs;
-        DhFn fn = f32 ? pick_kernel<true, kDh>(dpl.kh, dpl.span_index)
-                      : pick_kernel<false, kDh>(dpl.kh, dpl.span_index);
+        p.group_size = (int32_t)group_size;
+        DhFn fn = fused_dq ? pick_kernel<false, kDqDh>(dpl.kh, dpl.span_index)
+                  : f32    ? pick_kernel<true, kDh>(dpl.kh, dpl.span_index)
+                           : pick_kernel<false, kDh>(dpl.kh, dpl.span_index);
         hipLaunchKernelGGL(fn, dim3((unsigned)dpl.workgroups), dim3(kThreads), 0, (hipStream_t)stream, p);
         if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
         const int G = (int)(D / group_size);

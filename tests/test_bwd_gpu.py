@@ -103,6 +103,33 @@ def test_backward_integer_inputs_bitwise(dt, B, L, D, gs, l_h):
         assert np.array_equal(to_np(g), r), name
 
 
+SUBSETS = [(True, False, False), (False, True, False), (False, False, True),
+           (True, False, True), (True, True, False), (False, True, True)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h", [(1, 6, 16, 16, 4), (2, 777, 96, 32, 7), (3, 257, 128, 16, 65),
+                                          (1, 1000, 96, 48, 97), (1, 2048, 256, 16, 128)])
+def test_output_subsets_match_the_full_call(dt, B, L, D, gs, l_h):
+    """Which gradients are requested decides which kernels run (bf16 dq with dh
+    is one fused pass; dq alone is the forward kernel, dh alone its own pass).
+    Every route sums in the same order, so each gradient has the same bits."""
+    dtype = DTYPES[dt]
+    log("bwd subsets %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B + L + l_h)
+    dy = normal_activation((B, L, D), dtype, "cpu", seed=L + 5)
+    dev = [t.to(DEV) for t in (q, k, v, h, dy)]
+    full = hc.conv_bwd(*dev, gs)
+    for need in SUBSETS:
+        part = hc.conv_bwd(*dev, gs, need_dq=need[0], need_dkv=need[1], need_dh=need[2])
+        torch.cuda.synchronize()
+        wanted = (need[0], need[1], need[1], need[2])
+        for name, want, f, g in zip(("dq", "dk", "dv", "dh"), wanted, full, part):
+            assert (g is not None) == want, (name, need)
+            if want:
+                assert torch.equal(f, g), (name, need)
+
+
 def test_backward_deterministic():
     q, k, v, h = gaussian_inputs(2, 1500, 256, 16, 128, torch.bfloat16, seed=21)
     dy = normal_activation((2, 1500, 256), torch.bfloat16, "cpu", seed=22)

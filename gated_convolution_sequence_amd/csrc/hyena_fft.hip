@@ -30,8 +30,9 @@
 // spectra; equal filters make the second term vanish).  The filter spectra
 // come from the same two kernels run on the filters (pairs of filters,
 // separated the same way), once per call.
-// Inner transforms are radix-4 Stockham (self-sorting) in LDS with twiddles
-// tabulated per workgroup; arithmetic is fp32 for both I/O types.
+// Inner transforms are Stockham (self-sorting) in LDS, radix 16 (two radix-4
+// levels in registers) per pass, with twiddles tabulated per workgroup;
+// arithmetic is fp32 for both I/O types.
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -91,69 +92,152 @@ __device__ inline void fill_twiddles(float2 *tw, int M) {
     for (int m = threadIdx.x; m < M; m += blockDim.x) tw[m] = twiddle(m, M);
 }
 
-// In-LDS M-point transform of P = 2^logP interleaved sequences (element j
-// of sequence p at x[j P + p]), Stockham (self-sorting), radix 4 with one
-// radix-2 stage when log2 M is odd.  A radix-R stage combines R
-// sub-transforms of Ns points into R Ns points: for j < M/R, k = j mod Ns,
+// cos(2 pi m / 16), m taken mod 16: the constant twiddles of the
+// in-register transforms (cos(pi/8), cos(pi/4), cos(3 pi/8), correctly
+// rounded to fp32).
+__host__ __device__ constexpr float cos16(int m) {
+    constexpr float c1 = 0.923879532511286756f, c2 = 0.707106781186547524f, c3 = 0.382683432365089772f;
+    switch (m & 15) {
+    case 0: return 1.0f;
+    case 1: return c1;
+    case 2: return c2;
+    case 3: return c3;
+    case 4: return 0.0f;
+    case 5: return -c3;
+    case 6: return -c2;
+    case 7: return -c1;
+    case 8: return -1.0f;
+    case 9: return -c1;
+    case 10: return -c2;
+    case 11: return -c3;
+    case 12: return 0.0f;
+    case 13: return c3;
+    case 14: return c2;
+    default: return c1;
+    }
+}
+__host__ __device__ constexpr float sin16(int m) { return cos16(m - 4); }
+
+// a W_R^m (INV: a W_R^-m) for a compile-time m, W_R = exp(-2 pi i / R),
+// R dividing 16; multiples of a quarter turn cost no multiply.
+template <int R, bool INV>
+__device__ __forceinline__ float2 wconst(float2 a, int m) {
+    const int e = (m * (16 / R)) & 15;
+    if (e == 0) return a;
+    if (e == 8) return make_float2(-a.x, -a.y);
+    const bool neg_i = (e == 4) != INV;  // multiply by -i, else by +i (e = 4 or 12)
+    if (e == 4 || e == 12) return neg_i ? make_float2(a.y, -a.x) : make_float2(-a.y, a.x);
+    const float c = cos16(e), s = INV ? -sin16(e) : sin16(e);
+    // a (c - i s)
+    return make_float2(a.x * c + a.y * s, a.y * c - a.x * s);
+}
+
+// In-register DFT of R = 2, 4, 8 or 16 points (INV: the unscaled inverse).
+template <int R, bool INV> __device__ __forceinline__ void dft(float2 *v);
+template <> __device__ __forceinline__ void dft<2, false>(float2 *v) {
+    const float2 a = v[0], b = v[1];
+    v[0] = make_float2(a.x + b.x, a.y + b.y);
+    v[1] = make_float2(a.x - b.x, a.y - b.y);
+}
+template <> __device__ __forceinline__ void dft<2, true>(float2 *v) { dft<2, false>(v); }
+template <bool INV> __device__ __forceinline__ void dft4(float2 *v) {
+    const float2 s02 = make_float2(v[0].x + v[2].x, v[0].y + v[2].y), d02 = make_float2(v[0].x - v[2].x, v[0].y - v[2].y);
+    const float2 s13 = make_float2(v[1].x + v[3].x, v[1].y + v[3].y), d13 = make_float2(v[1].x - v[3].x, v[1].y - v[3].y);
+    // W_4 d13 = -i d13 (forward), +i d13 (inverse)
+    const float2 jd = INV ? make_float2(-d13.y, d13.x) : make_float2(d13.y, -d13.x);
+    v[0] = make_float2(s02.x + s13.x, s02.y + s13.y);
+    v[1] = make_float2(d02.x + jd.x, d02.y + jd.y);
+    v[2] = make_float2(s02.x - s13.x, s02.y - s13.y);
+    v[3] = make_float2(d02.x - jd.x, d02.y - jd.y);
+}
+template <> __device__ __forceinline__ void dft<4, false>(float2 *v) { dft4<false>(v); }
+template <> __device__ __forceinline__ void dft<4, true>(float2 *v) { dft4<true>(v); }
+// R = A B by one Cooley-Tukey split: with n = B n1 + n2 and k = k1 + A k2,
+//     V[k1 + A k2] = sum_n2 W_B^(n2 k2) W_R^(n2 k1) sum_n1 v[B n1 + n2] W_A^(n1 k1).
+template <int A, int B, bool INV> __device__ __forceinline__ void dft_split(float2 *v) {
+    constexpr int R = A * B;
+    float2 a[B][A];
+#pragma unroll
+    for (int n2 = 0; n2 < B; ++n2) {
+        float2 t[A];
+#pragma unroll
+        for (int n1 = 0; n1 < A; ++n1) t[n1] = v[B * n1 + n2];
+        dft<A, INV>(t);
+#pragma unroll
+        for (int k1 = 0; k1 < A; ++k1) a[n2][k1] = wconst<R, INV>(t[k1], n2 * k1);
+    }
+#pragma unroll
+    for (int k1 = 0; k1 < A; ++k1) {
+        float2 t[B];
+#pragma unroll
+        for (int n2 = 0; n2 < B; ++n2) t[n2] = a[n2][k1];
+        dft<B, INV>(t);
+#pragma unroll
+        for (int k2 = 0; k2 < B; ++k2) v[k1 + A * k2] = t[k2];
+    }
+}
+template <> __device__ __forceinline__ void dft<8, false>(float2 *v) { dft_split<4, 2, false>(v); }
+template <> __device__ __forceinline__ void dft<8, true>(float2 *v) { dft_split<4, 2, true>(v); }
+template <> __device__ __forceinline__ void dft<16, false>(float2 *v) { dft_split<4, 4, false>(v); }
+template <> __device__ __forceinline__ void dft<16, true>(float2 *v) { dft_split<4, 4, true>(v); }
+
+// One Stockham (self-sorting) stage of radix R on M points of P = 2^logP
+// interleaved sequences (element j of sequence p at x[j P + p]): it combines
+// R sub-transforms of Ns points into R Ns points.  For j < M/R, k = j mod Ns,
 //     v_r = x[j + r M/R] W_(R Ns)^(r k),   V = DFT_R(v),
 //     y[(j - k) R + k + r Ns] = V_r,
 // with W conjugated (and DFT_R inverted) for the inverse transform.  tw[m] =
-// W_M^m for m < M.  Output in natural order; returns the buffer holding it.
-// Callers synchronise before (x written) and the routine ends synchronised.
-__device__ float2 *lds_fft(float2 *x, float2 *y, const float2 *tw, int M, int logM, int logP, bool inverse) {
+// W_M^m for m < M.
+template <int R, bool INV>
+__device__ __forceinline__ void fft_stage(const float2 *x, float2 *y, const float2 *tw, int M, int logP, int Ns,
+                                          int logNs) {
     const int pmask = (1 << logP) - 1;
+    const int n = (M / R) << logP;
+    const int tstride = (M / R) >> logNs;  // W_(R Ns)^k = W_M^(k M / (R Ns))
+    for (int i = threadIdx.x; i < n; i += kFftThreads) {
+        const int j = i >> logP;
+        const int p = i & pmask;
+        const int k = j & (Ns - 1);
+        float2 v[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) v[r] = x[i + r * n];
+        if (Ns > 1) {
+#pragma unroll
+            for (int r = 1; r < R; ++r) {
+                float2 w = tw[r * k * tstride];
+                if (INV) w.y = -w.y;
+                v[r] = cmul(v[r], w);
+            }
+        }
+        dft<R, INV>(v);
+        const int d = (j - k) * R + k;
+#pragma unroll
+        for (int r = 0; r < R; ++r) y[((d + r * Ns) << logP) + p] = v[r];
+    }
+}
+
+// In-LDS M-point transform of P = 2^logP interleaved sequences: radix-16
+// stages in registers while four or more bits of log2 M remain, then one of
+// radix 8, 4 or 2.  Output in natural order; returns the buffer holding it.
+// Callers synchronise before (x written) and the routine ends synchronised.
+__device__ __forceinline__ float2 *lds_fft(float2 *x, float2 *y, const float2 *tw, int M, int logM, int logP,
+                                         bool inverse) {
     int Ns = 1, logNs = 0;
     while (logNs < logM) {
-        if (logM - logNs >= 2) {
-            const int quarter = M >> 2;
-            const int n = quarter << logP;
-            const int tstride = quarter >> logNs;  // W_(4 Ns)^k = W_M^(k M / (4 Ns))
-            for (int i = threadIdx.x; i < n; i += kFftThreads) {
-                const int j = i >> logP;
-                const int p = i & pmask;
-                const int k = j & (Ns - 1);
-                float2 v0 = x[i], v1 = x[i + n], v2 = x[i + 2 * n], v3 = x[i + 3 * n];
-                float2 w1 = tw[k * tstride], w2 = tw[2 * k * tstride], w3 = tw[3 * k * tstride];
-                if (inverse) {
-                    w1.y = -w1.y;
-                    w2.y = -w2.y;
-                    w3.y = -w3.y;
-                }
-                v1 = cmul(v1, w1);
-                v2 = cmul(v2, w2);
-                v3 = cmul(v3, w3);
-                // DFT_4: W_4 = -i (forward), +i (inverse)
-                const float2 s02 = make_float2(v0.x + v2.x, v0.y + v2.y), d02 = make_float2(v0.x - v2.x, v0.y - v2.y);
-                const float2 s13 = make_float2(v1.x + v3.x, v1.y + v3.y), d13 = make_float2(v1.x - v3.x, v1.y - v3.y);
-                // -i d13 = (d13.y, -d13.x)
-                const float2 jd = inverse ? make_float2(-d13.y, d13.x) : make_float2(d13.y, -d13.x);
-                const int d = ((j - k) << 2) + k;
-                y[(d << logP) + p] = make_float2(s02.x + s13.x, s02.y + s13.y);
-                y[((d + Ns) << logP) + p] = make_float2(d02.x + jd.x, d02.y + jd.y);
-                y[((d + 2 * Ns) << logP) + p] = make_float2(s02.x - s13.x, s02.y - s13.y);
-                y[((d + 3 * Ns) << logP) + p] = make_float2(d02.x - jd.x, d02.y - jd.y);
-            }
-            Ns <<= 2;
-            logNs += 2;
+        const int lr = logM - logNs >= 4 ? 4 : logM - logNs;
+        if (inverse) {
+            if (lr == 4) fft_stage<16, true>(x, y, tw, M, logP, Ns, logNs);
+            else if (lr == 3) fft_stage<8, true>(x, y, tw, M, logP, Ns, logNs);
+            else if (lr == 2) fft_stage<4, true>(x, y, tw, M, logP, Ns, logNs);
+            else fft_stage<2, true>(x, y, tw, M, logP, Ns, logNs);
         } else {
-            const int half = M >> 1;
-            const int n = half << logP;
-            const int tstride = half >> logNs;  // W_(2 Ns)^k = W_M^(k M / (2 Ns))
-            for (int i = threadIdx.x; i < n; i += kFftThreads) {
-                const int j = i >> logP;
-                const int p = i & pmask;
-                const int k = j & (Ns - 1);
-                const float2 a = x[i];
-                float2 w = tw[k * tstride];
-                if (inverse) w.y = -w.y;
-                const float2 bb = cmul(x[i + n], w);
-                const int d = ((j - k) << 1) + k;
-                y[(d << logP) + p] = make_float2(a.x + bb.x, a.y + bb.y);
-                y[((d + Ns) << logP) + p] = make_float2(a.x - bb.x, a.y - bb.y);
-            }
-            Ns <<= 1;
-            logNs += 1;
+            if (lr == 4) fft_stage<16, false>(x, y, tw, M, logP, Ns, logNs);
+            else if (lr == 3) fft_stage<8, false>(x, y, tw, M, logP, Ns, logNs);
+            else if (lr == 2) fft_stage<4, false>(x, y, tw, M, logP, Ns, logNs);
+            else fft_stage<2, false>(x, y, tw, M, logP, Ns, logNs);
         }
+        Ns <<= lr;
+        logNs += lr;
         __syncthreads();
         float2 *t = x;
         x = y;

@@ -249,7 +249,10 @@ __device__ __forceinline__ float2 *lds_fft(float2 *x, float2 *y, const float2 *t
 // Global -> LDS staging of n values, kBatch per thread at a time: the loads
 // of a batch are issued together (indices clamped into range, so none is
 // conditional) and waited for once.
-constexpr int kBatch = 8;
+#ifndef HYENA_FFT_BATCH
+#define HYENA_FFT_BATCH 8
+#endif
+constexpr int kBatch = HYENA_FFT_BATCH;
 template <typename Load>
 __device__ inline void stage_in(float2 *dst, int n, Load load) {
     for (int base = 0; base < n; base += kBatch * kFftThreads) {

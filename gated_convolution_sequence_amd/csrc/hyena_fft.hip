@@ -615,9 +615,13 @@ constexpr int kFftTwoLevelMaxLogN = 16;
 #define HYENA_FFT_BUDGET 4096
 #endif
 constexpr int kFftBudget = HYENA_FFT_BUDGET;
-int pick_pairs(int M, int buffers, int64_t pairs) {
+#ifndef HYENA_FFT_COLS_BUDGET
+#define HYENA_FFT_COLS_BUDGET HYENA_FFT_BUDGET
+#endif
+constexpr int kFftColsBudget = HYENA_FFT_COLS_BUDGET;  // the column kernel's
+int pick_pairs(int M, int buffers, int64_t pairs, int budget = kFftBudget) {
     int P = 64;
-    while (P > 1 && (int64_t)buffers * M * P > kFftBudget) P >>= 1;
+    while (P > 1 && (int64_t)buffers * M * P > budget) P >>= 1;
     while (P > 1 && P / 2 >= pairs) P >>= 1;
     return P;
 }
@@ -658,7 +662,7 @@ int fft_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, i
     const int Mr = pl->three ? pl->N3 : pl->N2;  // transform length of the row (and output) kernels
     pl->P_rows = pick_pairs(Mr, 2, pairs);
     pl->P_mid = pick_pairs(pl->N2, 2, pairs);
-    pl->P_cols = pick_pairs(pl->N1, 4, pairs);
+    pl->P_cols = pick_pairs(pl->N1, 4, pairs, kFftColsBudget);
     pl->lds_rows = (2 * Mr * pl->P_rows + 2 * Mr) * (int)sizeof(float2);
     pl->lds_mid = (2 * pl->N2 * pl->P_mid + 2 * pl->N2) * (int)sizeof(float2);
     pl->lds_cols = (4 * pl->N1 * pl->P_cols + 3 * pl->N1) * (int)sizeof(float2);

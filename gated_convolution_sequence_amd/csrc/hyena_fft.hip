@@ -19,7 +19,8 @@
 //      N2-point FFT, twiddle W_N^(t1 f2), write the workspace [B][N2][N1][pairs];
 //   2. fft_cols: per (batch, column pair {f2, N2 - f2}, pair tile): N1-point
 //      FFT of both columns, multiply by the filter spectra, inverse N1-point
-//      FFT, twiddle W_N^(-t1 f2), write back in place;
+//      FFT, twiddle W_N^(-t1 f2), write back in place (fft_col1: one column
+//      at a time, when both channels of every pair share a filter);
 //   3. fft_out: per (batch, t1, pair tile): inverse N2-point FFT, scale 1/N,
 //      gate with q, store rows t1 + N1 t2 < L.
 // Two real channels travel as one complex sequence (re = channel 2j, im =
@@ -438,6 +439,69 @@ __global__ __launch_bounds__(kFftThreads) void fft_cols_kernel(FftParams p) {
     }
 }
 
+// Kernel 2, single-column form, for a sequence whose channel pairs each lie
+// inside one group (even group sizes): H0 = H1, so Z = H P[f] and a column
+// needs no partner.  Per (batch, column f2, pair tile): N1-point FFT, the
+// product with the group's filter spectrum, inverse N1-point FFT, twiddle
+// W_N^(-t1 f2), store in place.  Half the LDS of the paired form per pair,
+// so tiles are twice as wide (whole 128-byte work-area segments) and each
+// point reads one filter spectrum value.
+// LDS (dynamic): two buffers of N1 P values, the N1 inner twiddles and the N1
+// inter-step twiddles.
+__global__ __launch_bounds__(kFftThreads) void fft_col1_kernel(FftParams p) {
+    extern __shared__ float2 lds[];
+    const int item = xcd_item();
+    const int tile = item % p.n_tiles;
+    const int M = p.N2 * p.N3;  // columns
+    const int f2 = (item / p.n_tiles) % M;
+    const int b = item / (p.n_tiles * M);
+    const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1;
+    const int NP = N1 << logP;
+    const int64_t N = (int64_t)N1 * M;
+    // work-area row of (f2, t1 = 0): column position as in the paired form
+    const int64_t col0 = ((int64_t)b * M + (int64_t)(f2 & (p.N3 - 1)) * p.N2 + (f2 >> p.log3)) * N1;
+    float2 *bufA = lds, *bufB = lds + NP, *tw = lds + 2 * NP, *wt = tw + N1;
+    stage_in(bufA, NP, [&](int i) {
+        const int j = (tile << logP) + (i & pmask);
+        const bool ok = j < p.np;
+        const float2 v = p.ws[(col0 + (i >> logP)) * p.np + (ok ? j : 0)];
+        return ok ? v : make_float2(0.0f, 0.0f);
+    });
+    fill_twiddles(tw, N1);
+    for (int t1 = threadIdx.x; t1 < N1; t1 += kFftThreads)
+        wt[t1] = cconj(twiddle(((int64_t)t1 * f2) & (N - 1), N));
+    __syncthreads();
+    float2 *S = lds_fft(bufA, bufB, tw, N1, p.log1, logP, false);
+    float2 *Z = S == bufA ? bufB : bufA;
+    // P divides the thread count, so a thread always has the same pair and
+    // its filter spectrum row is fixed
+    const int my_j = (tile << logP) + (threadIdx.x & pmask);
+    const int jc = min(my_j, p.np - 1);
+    const float2 *hrow = p.hs + (size_t)f2 * N1 * p.Gp + (2 * jc) / p.group_size;
+    for (int base = 0; base < NP; base += kBatch * kFftThreads) {
+        float2 hh[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int f1 = min(base + u * kFftThreads + (int)threadIdx.x, NP - 1) >> logP;
+            hh[u] = hrow[(size_t)f1 * p.Gp];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = base + u * kFftThreads + (int)threadIdx.x;
+            if (i >= NP) continue;
+            Z[i] = my_j < p.np ? cmul(hh[u], S[i]) : make_float2(0.0f, 0.0f);
+        }
+    }
+    __syncthreads();
+    const float2 *U = lds_fft(Z, S, tw, N1, p.log1, logP, true);
+    for (int i = threadIdx.x; i < NP; i += kFftThreads) {
+        const int j = (tile << logP) + (i & pmask);
+        if (j >= p.np) continue;
+        const int t1 = i >> logP;
+        p.ws[(col0 + t1) * p.np + j] = cmul(U[i], wt[t1]);
+    }
+}
+
 // Three-level split (large N): N = N1 N2 N3, t = t1 + N1 t2 + N1 N2 t3.
 // The M = N2 N3 point transform along t2 + N2 t3 that the row kernel does
 // in one piece is done in two passes, as a four-step of its own:
@@ -600,8 +664,8 @@ struct FftPlan {
     int64_t N, ws_pairs, hs_bytes, ws_bytes;
     int N1, N2, N3, log1, log2, log3;
     bool three;                      // three-level split (N3 > 1)
-    int P_rows, P_mid, P_cols;       // pairs per workgroup: row (rows3/out3), middle, column kernels
-    int lds_rows, lds_mid, lds_cols; // their LDS bytes
+    int P_rows, P_mid, P_cols, P_col1;          // pairs per workgroup: row (rows3/out3), middle,
+    int lds_rows, lds_mid, lds_cols, lds_col1;  // column (paired, single) kernels; their LDS bytes
 };
 
 // Largest N done with the two-level split (columns of at most 256 points);
@@ -666,7 +730,10 @@ int fft_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, i
     pl->lds_rows = (2 * Mr * pl->P_rows + 2 * Mr) * (int)sizeof(float2);
     pl->lds_mid = (2 * pl->N2 * pl->P_mid + 2 * pl->N2) * (int)sizeof(float2);
     pl->lds_cols = (4 * pl->N1 * pl->P_cols + 3 * pl->N1) * (int)sizeof(float2);
-    if (pl->lds_rows > kFftMaxLdsBytes || pl->lds_cols > kFftMaxLdsBytes || pl->lds_mid > kFftMaxLdsBytes)
+    pl->P_col1 = pick_pairs(pl->N1, 2, pairs);
+    pl->lds_col1 = (2 * pl->N1 * pl->P_col1 + 2 * pl->N1) * (int)sizeof(float2);
+    if (pl->lds_rows > kFftMaxLdsBytes || pl->lds_cols > kFftMaxLdsBytes || pl->lds_mid > kFftMaxLdsBytes ||
+        pl->lds_col1 > kFftMaxLdsBytes)
         return HYENA_ERR_UNSUPPORTED;
     const int64_t Gp = G + (G & 1);
     pl->ws_pairs = B * (D / 2) > Gp / 2 ? B * (D / 2) : Gp / 2;
@@ -775,7 +842,10 @@ int hyena_conv_fwd_long(const void *q, const void *k, const void *v, const void 
     if (st == HYENA_OK) st = launch(rows_seq, p, pl.P_rows, row_units, B, pl.lds_rows);
     if (st == HYENA_OK && pl.three)
         st = launch((const void *)fft_mid_kernel<false>, p, pl.P_mid, mid_units, B, pl.lds_mid);
-    if (st == HYENA_OK) st = launch((const void *)fft_cols_kernel<1>, p, pl.P_cols, cols, B, pl.lds_cols);
+    // channel pairs inside one group (even group size): single columns
+    if (st == HYENA_OK)
+        st = group_size % 2 == 0 ? launch((const void *)fft_col1_kernel, p, pl.P_col1, M, B, pl.lds_col1)
+                                 : launch((const void *)fft_cols_kernel<1>, p, pl.P_cols, cols, B, pl.lds_cols);
     if (st == HYENA_OK && pl.three)
         st = launch((const void *)fft_mid_kernel<true>, p, pl.P_mid, mid_units, B, pl.lds_mid);
     if (st == HYENA_OK) st = launch(out_fn, p, pl.P_rows, row_units, B, pl.lds_rows);

@@ -150,6 +150,27 @@ def test_matches_the_direct_kernel_for_short_filters():
     assert float((y_fft - y_dir).abs().max()) <= 2e-5 * scale
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_single_and_paired_column_kernels_agree(dt):
+    """An even group size runs the single-column kernel, group size 1 the
+    paired one (the partner column separates the two channels' spectra).
+    With each channel given its group's filter the two compute the same
+    convolution; they agree within the FFT bar, and each matches the oracle."""
+    dtype = DTYPES[dt]
+    B, L, D, l_h = 2, 3000, 64, 3000
+    q, k, v, h2 = gaussian_inputs(B, L, D, 2, l_h, dtype, seed=41)
+    h1 = torch.repeat_interleave(h2, 2, dim=0).contiguous()
+    dev = [t.to(DEV) for t in (q, k, v)]
+    log("single vs paired columns %s" % dt)
+    y2 = run_long(*dev, h2.to(DEV), 2).clone()
+    y1 = run_long(*dev, h1.to(DEV), 1)
+    scale = float(y1.float().abs().max())
+    tol = (1e-2 if dtype == torch.bfloat16 else 1e-5) * scale
+    assert float((y1.float() - y2.float()).abs().max()) <= tol
+    check_long(y2, q, k, v, h2, 2, dtype, "single-column")
+    check_long(y1, q, k, v, h1, 1, dtype, "paired")
+
+
 def test_deterministic_and_workspace_reuse():
     B, L, D, gs, l_h = 1, 3000, 64, 2, 3000
     q, k, v, h = (t.to(DEV) for t in gaussian_inputs(B, L, D, gs, l_h, torch.bfloat16, seed=9))

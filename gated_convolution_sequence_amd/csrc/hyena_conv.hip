@@ -982,12 +982,10 @@ template <bool F32> constexpr int kNumSpansFor = F32 ? 3 : kNumSpans;
 // Global loads give a thread 4 consecutive rows of 8 (fp32: 4) channels; the
 // thread writes them to LDS per channel, 4 times at once, and the epilogue
 // reads them back the same way, so every global access is a 16-byte row
-// segment.  LDS rows are in 16-byte units XOR-swizzled by a key of the
-// channel (bf16: 4 ((ch / 8) mod 4), fp32: 8 ((ch / 4) mod 2)).  Every row is
-// a multiple of 256 bytes long, so all rows start on bank 0; the key spreads
-// one staging access of a wave (8 row segments x 8 row groups) over all 16
-// units of a bank cycle, and being below 16 it keeps each access inside its
-// own row (rows and the staged ranges are aligned to 16 units).
+// segment.  LDS rows are in 16-byte units XOR-swizzled by the channel's row
+// segment, so the 8 segments of a row land in distinct banks.  (A key that
+// spread one staging access over all 16 units of a bank cycle measured more
+// bank-conflict cycles on gfx950, and no faster.)
 // ---------------------------------------------------------------------------
 constexpr int kCdBlock = 256;    // rows per block (16 sub-chunks of 16)
 constexpr int kCdRing = 384;     // ring entries per channel: a block + 128 history rows
@@ -1014,7 +1012,7 @@ template <bool F32> struct CdTr {
     static constexpr int QY_B = kCdBlock * EB;           // LDS bytes per channel gate row
     static_assert(CPW == VEC, "a wave's channels are one row segment (one swizzle key)");
     static_assert(SEGS * (kCdBlock / 4) == kCdThreads, "4 rows x 16 bytes per thread tile a block");
-    static_assert(SEGS <= 8, "8 row segments per slab");
+    static_assert(SEGS <= 8, "swizzle keys 0..7");
 };
 
 template <bool F32, int KH>
@@ -1077,8 +1075,7 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
     };
     // LDS byte address of time index r in channel ch's row (pitch rb)
     auto pos = [&](int ch, int r, int rb) -> int {
-        const int key = F32 ? ((ch >> 2) & 1) << 3 : ((ch >> 3) & 3) << 2;
-        return ch * rb + ((((r / T::VEC) ^ key)) << 4) + (r % T::VEC) * T::EB;
+        return ch * rb + ((((r / T::VEC) ^ ((ch / T::VEC) & 7))) << 4) + (r % T::VEC) * T::EB;
     };
 
     u32x4_t k0[4], v0[4], q0[4], k1[4], v1[4], q1[4];

@@ -1137,10 +1137,12 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
             tap_hi[j] = hi_ok ? vhi : 0u;
         }
     }
+    // stored reversed (entry e of a channel at PTN - 1 - e), so the entries
+    // one MFMA operand takes, e, e - 2, e - 4, e - 6, lie at rising addresses
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
         const int i = tid + j * kCdThreads;
-        if (i < SLAB * PTN) pt[i] = tap_lo[j] | (tap_hi[j] << 16);
+        if (i < SLAB * PTN) pt[i - i % PTN + PTN - 1 - i % PTN] = tap_lo[j] | (tap_hi[j] << 16);
     }
 
     // x = k v of rows 4 g4 .. 4 g4 + 3 -> ring index r (a multiple of 4)
@@ -1213,41 +1215,58 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
         load_block(blk + 1, kn, vn, qn);
         put_x(wrap(rb0 + 4 * g4), kd, vd);
         put_q(qd);
+        // B-operand offsets of this lane within a channel's ring row, one per
+        // step: the wave's channels share the swizzle key (one row segment),
+        // so these serve all of them.  bf16: steps of 32 input rows; the last
+        // (ks = KH) covers rows 0 .. 31 of the sub-chunk, of which 16 .. 31
+        // have zero taps, so lanes q4 >= 2 then read rows 0 .. 15 again
+        // (finite values inside the block) instead of rows past it.  fp32:
+        // groups of 16 input rows, lane q4 taking row 4 q4 + s in MFMA s.
+        constexpr int NS = F32 ? 2 * KH + 1 : KH + 1;
+        int xoff[NS];
+#pragma unroll
+        for (int ks = 0; ks < NS; ++ks) {
+            const int tin0 = -HROWS + (F32 ? 16 : 32) * ks;
+            const int lane = F32 ? lane_t4 : (ks == KH ? lane_t8 - ((q4 & 2) << 3) : lane_t8);
+            const unsigned r = (unsigned)wrap(rb0 + kCdRing + tin0 + lane);  // in [0, 384)
+            xoff[ks] = (int)((((r / T::VEC) ^ (unsigned)(w & 7))) << 4) + (int)(r % T::VEC) * T::EB;
+        }
         __syncthreads();
 #pragma unroll
         for (int cl = 0; cl < T::CPW; ++cl) {
             const int dl = w * T::CPW + cl;
             if (c_begin + dl >= p.D) break;
-            const uint32_t *ptc = pt + dl * PTN;
+            const unsigned char *xrow = xr + dl * T::RING_B;
+            const uint32_t *ptr = pt + dl * PTN;  // reversed tap table of this channel
             f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
             if constexpr (F32) {
-                // groups of 16 input rows, 4 MFMAs each; in MFMA s lane q4
-                // takes input row 4 q4 + s of the group
+                f32x4_t xv[NS];
+                float tv[NS][4];
 #pragma unroll
-                for (int gi = 0; gi <= 2 * KH; ++gi) {
-                    const int tg = -HROWS + 16 * gi;
-                    const int r = wrap(rb0 + kCdRing + tg + lane_t4);
-                    const f32x4_t xv = *(const f32x4_t *)(&xr[pos(dl, r, T::RING_B)]);
-                    const int c = n16 - 4 * q4 - tg + kCdTapOff;
+                for (int gi = 0; gi < NS; ++gi) {
+                    xv[gi] = *(const f32x4_t *)(&xrow[xoff[gi]]);
+                    const int c = PTN - 1 - (n16 - 4 * q4 - (-HROWS + 16 * gi) + kCdTapOff);  // entry c - s at c + s
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) tv[gi][s] = __uint_as_float(ptr[c + s]);
+                }
+#pragma unroll
+                for (int gi = 0; gi < NS; ++gi)
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(ptc[c - s]), xv[s], acc, 0, 0, 0);
-                }
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tv[gi][s], xv[gi][s], acc, 0, 0, 0);
             } else {
-                // steps of 32 input rows; the last (ks = KH) covers rows
-                // 0 .. 31 of the sub-chunk, of which 16 .. 31 have zero taps:
-                // lanes q4 >= 2 then read rows 0 .. 15 again (finite values
-                // inside the block) instead of rows past it
+                u32x4_t xv[NS], hv[NS];
 #pragma unroll
-                for (int ks = 0; ks <= KH; ++ks) {
-                    const int tin0 = -HROWS + 32 * ks;
-                    const int r = wrap(rb0 + kCdRing + tin0 + (ks == KH ? lane_t8 - ((q4 & 2) << 3) : lane_t8));
-                    const u32x4_t xv = *(const u32x4_t *)(&xr[pos(dl, r, T::RING_B)]);
-                    const int c = n16 - 8 * q4 - tin0 + kCdTapOff;
-                    const u32x4_t hv4 = {ptc[c], ptc[c - 2], ptc[c - 4], ptc[c - 6]};
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hv4),
-                                                                  __builtin_bit_cast(bf16x8_t, xv), acc, 0, 0, 0);
+                for (int ks = 0; ks < NS; ++ks) {
+                    xv[ks] = *(const u32x4_t *)(&xrow[xoff[ks]]);
+                    // entries e, e - 2, e - 4, e - 6 of e = n16 - 8 q4 - tin0 + 32
+                    const int c = PTN - 1 - (n16 - 8 * q4 - (-HROWS + 32 * ks) + kCdTapOff);
+                    hv[ks] = u32x4_t{ptr[c], ptr[c + 2], ptr[c + 4], ptr[c + 6]};
                 }
+#pragma unroll
+                for (int ks = 0; ks < NS; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hv[ks]),
+                                                                  __builtin_bit_cast(bf16x8_t, xv[ks]), acc, 0, 0, 0);
             }
             // y = q acc in place of q
             const int qa = pos(dl, lane_t4, T::QY_B);

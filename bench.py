@@ -21,7 +21,8 @@ Reported (one JSON line):
   layers       the same figures for each layer's kernel;
   cpu_baseline the fp64 oracle on the host cores over the full step's inputs;
   naive_conv1d the same step written with torch's depthwise F.conv1d (bf16),
-               with and without the layout permutes.
+               with and without the layout permutes;
+  batched_mr   (with --batched) the MR layer at B=4, L=32768.
 Input sets rotate over ``--sets`` copies per layer so that no launch finds its
 operands in the 256 MB Infinity Cache.
 """
@@ -68,6 +69,10 @@ def parse():
     ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--skip-chunk-direction", action="store_true")
     ap.add_argument("--skip-long-filter", action="store_true")
+    ap.add_argument("--batched", action="store_true",
+                    help="also time the batched MR configuration (B=4, L=32768); off by default because "
+                         "its launches share the kernel instance of the B=1 MR layer, which would mix "
+                         "two shapes in a profiler's per-kernel statistics of the default command")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough CPU budget of the oracle baseline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -307,6 +312,10 @@ def main():
     if not args.skip_backward:
         out["backward"] = backward_rates(layers, sets, stream, max(5, K // 8))
 
+    # ---- the batched MR configuration (B=4, L=32768), outside the step ---
+    if args.batched:
+        out["batched_mr"] = batched_mr_rate(stream, max(10, K // 10))
+
     # ---- attainable streaming rate on this GPU (same bytes, no convolution)
     out["stream_reference"] = stream_reference(layers[-1], sets[-1], stream, max(10, K // 4))
 
@@ -416,6 +425,46 @@ class HipEvents:
         if rc != 0:
             raise RuntimeError("hipEventElapsedTime: %d" % rc)
         return f.value
+
+
+def batched_mr_rate(stream, reps):
+    """The MR layer at B=4, L=32768, D=4096 (4 GiB of q, k, v and y per input
+    set; two sets alternate): mean launch time from fence-free HIP events
+    around each launch, and its fraction of the HBM peak at 8 B per
+    token*channel."""
+    import torch
+    import gated_convolution_sequence_amd as hc
+    from workloads import WORKLOADS, make_inputs
+    w = WORKLOADS["mr_b4"]
+    q, k, v, h = make_inputs(w, torch.device("cuda:0"))
+    sets = [(q, k, v, torch.empty_like(q)), (q.clone(), k.clone(), v.clone(), torch.empty_like(q))]
+
+    def call(i):
+        a, b, c, y = sets[i % 2]
+        hc.conv_fwd(a, b, c, h, w.group_size, out=y, stream=stream)
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    marks = [(ev.create(), ev.create()) for _ in range(reps)]
+    for i, (e0, e1) in enumerate(marks):
+        ev.record(e0, stream)
+        call(i)
+        ev.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = [ev.elapsed_ms(e0, e1) for e0, e1 in marks]
+    mean_ms = sum(ms) / len(ms)
+    alg = 8 * w.elems
+    span, wgs = hc.plan(w.B, w.L, w.D, w.group_size, w.l_h, hc.DTYPE_BF16)
+    res = {"B": w.B, "L": w.L, "D": w.D, "group_size": w.group_size, "l_h": w.l_h,
+           "mean_us": round(mean_ms * 1e3, 1), "median_us": round(statistics.median(ms) * 1e3, 1),
+           "G_tok_ch_per_s": round(w.elems / (mean_ms * 1e-3) / 1e9, 2),
+           "achieved_GBs": round(alg / (mean_ms * 1e-3) / 1e9, 1),
+           "hbm_frac": round(alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "span_chunks": span, "workgroups": wgs, "launches": reps}
+    del sets, q, k, v, h
+    torch.cuda.empty_cache()
+    return res
 
 
 def chunk_direction_rates(layers, sets, stream, reps):

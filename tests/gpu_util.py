@@ -12,6 +12,7 @@ with env = |q| (|h| * |k v|), the same operator on magnitudes.
 fp32 I/O -- gate max|y - y_ref| <= 1e-5 * max|y_ref|; elementwise
     |y - y_ref| <= 2^-24 |y_ref| + (l_h + 4) 2^-23 * env + tiny.
 """
+import math
 import sys
 
 import numpy as np
@@ -78,3 +79,92 @@ def run(q, k, v, h, gs, span=0, pad=16):
     torch.cuda.synchronize()
     assert torch.all(big[:pad] == 7.0) and torch.all(big[pad + n:] == 7.0), "write outside out"
     return out
+
+
+# ---- backward --------------------------------------------------------------
+# dq, dk, dv use the forward's bar with the envelope of the backward oracle
+# on magnitudes; dh (fp32 output) |e| <= (u_in + (R + 256) 2^-24) env with
+# u_in = 2^-7 + 2^-14 (bf16 inputs: dz and x each rounded once) or 4 2^-24
+# (fp32), R the partial rows summed, plus the gate.
+
+def bwd_refs(q, k, v, h, dy, gs):
+    """(oracle gradients, the same on magnitudes) for CPU or GPU tensors."""
+    a = [to_np(t) for t in (q, k, v, h, dy)]
+    ref = oracle.conv_bwd_ref(*a, gs)
+    env = oracle.conv_bwd_ref(*[np.abs(x) for x in a], gs)
+    return ref, env
+
+
+def check_dh(got, ref, env, dtype, rows, what):
+    got = to_np(got)
+    assert np.all(np.isfinite(got)), what
+    err = np.abs(got - ref)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    gate = (1e-2 if dtype == torch.bfloat16 else 1e-5) * scale
+    u_in = 2.0 ** -7 + 2.0 ** -14 if dtype == torch.bfloat16 else 4 * 2.0 ** -24
+    bound = (u_in + (rows + 256) * 2.0 ** -24) * env + TINY
+    assert float(np.max(err)) <= gate, "%s: dh max err %.3e > gate %.3e" % (what, np.max(err), gate)
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, "%s: dh bound broken at %s" % (what, bad[0])
+
+
+def check_bwd(grads, ref, env, l_h, dtype, rows, what):
+    for name, g, r, e in zip(("dq", "dk", "dv"), grads[:3], ref[:3], env[:3]):
+        check(to_np(g), r, e, l_h, dtype, "%s %s" % (what, name))
+    check_dh(grads[3], ref[3], env[3], dtype, rows, what)
+
+
+def bwd_rows(B, L, D, gs, l_h, dtype):
+    """Partial rows the filter gradient sums (from the workspace size)."""
+    n = hc.bwd_workspace_bytes(B, L, D, gs, l_h, hc.DTYPE_BF16 if dtype == torch.bfloat16 else hc.DTYPE_F32)
+    return max(1, n // ((D // 16) * l_h * 4))
+
+
+# ---- long filters (FFT convolution) ------------------------------------------
+# The FFT path's rounding error is not local.  Per channel d of group g and
+# transform length N (fp32 transforms for both I/O types):
+#     |y - y_ref| <= r |y_ref| + |q| * 3 e sqrt(N) ||h_g||_2 ||x_d||_2,
+#     e = (log2 N + 2) * 7 * 2^-24,
+# r = 2^-8 (bf16 output rounding) or 2^-24 (fp32): the norm-wise error of a
+# radix-2 FFT (about 7 units of rounding per level with accurate twiddles,
+# log2 N levels plus the two twiddle passes of the split) through the forward
+# transforms of x and h, the product and the inverse.  The north-star gate is
+# applied as well.
+
+def transform_len(L, l_h):
+    n = L + min(l_h, L) - 1
+    return 1 << max(2, (n - 1).bit_length())
+
+
+def run_long(q, k, v, h, gs, pad=16):
+    n = q.numel()
+    big = torch.full((n + 2 * pad,), 7.0, dtype=q.dtype, device=q.device)
+    out = big[pad:pad + n].view(q.shape)
+    out.fill_(float("nan"))
+    hc.conv_fwd_long(q, k, v, h, gs, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(big[:pad] == 7.0) and torch.all(big[pad + n:] == 7.0), "write outside out"
+    return out
+
+
+def check_long(y, q, k, v, h, gs, dtype, what=""):
+    """Gate and the norm-wise FFT bound against the fp64 oracle (CPU tensors)."""
+    qn, kn, vn, hn = (to_np(t) for t in (q, k, v, h))
+    ref = oracle.conv_fwd_ref(qn, kn, vn, hn, gs)
+    y = to_np(y)
+    assert np.all(np.isfinite(y)), what
+    err = np.abs(y - ref)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    gate = (1e-2 if dtype == torch.bfloat16 else 1e-5) * scale
+    assert float(np.max(err)) <= gate, "%s: max err %.3e > gate %.3e" % (what, np.max(err), gate)
+    B, L, D = qn.shape
+    N = transform_len(L, hn.shape[1])
+    e = (math.log2(N) + 2) * 7 * 2.0 ** -24
+    x = kn * vn
+    xn = np.sqrt(np.sum(x * x, axis=1))                   # [B, D]
+    hnorm = np.sqrt(np.sum(hn * hn, axis=1))[np.arange(D) // gs]  # [D]
+    r = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -24
+    bound = r * np.abs(ref) + np.abs(qn) * (3 * e * math.sqrt(N) * hnorm[None, None, :] * xn[:, None, :]) + TINY
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, "%s: FFT bound broken at %s" % (what, bad[0])
+    return float(np.max(err)) / scale if scale else 0.0

@@ -16,7 +16,7 @@ import torch
 
 import gated_convolution_sequence_amd as hc
 import oracle
-from gpu_util import DEV, check, log, to_np
+from gpu_util import DEV, bwd_refs, bwd_rows, check, check_bwd, check_dh, log, to_np
 from workloads import WORKLOADS, gaussian_inputs, integer_inputs, make_inputs, normal_activation
 
 pytestmark = pytest.mark.gpu
@@ -36,36 +36,10 @@ def _bwd_gpu(q, k, v, h, dy, gs):
     return out
 
 
-def _refs(q, k, v, h, dy, gs):
-    a = [to_np(t) for t in (q, k, v, h, dy)]
-    ref = oracle.conv_bwd_ref(*a, gs)
-    env = oracle.conv_bwd_ref(*[np.abs(x) for x in a], gs)
-    return ref, env
-
-
-def _check_dh(got, ref, env, dtype, rows, what):
-    got = to_np(got)
-    assert np.all(np.isfinite(got)), what
-    err = np.abs(got - ref)
-    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
-    gate = (1e-2 if dtype == torch.bfloat16 else 1e-5) * scale
-    u_in = 2.0 ** -7 + 2.0 ** -14 if dtype == torch.bfloat16 else 4 * 2.0 ** -24
-    bound = (u_in + (rows + 256) * 2.0 ** -24) * env + 1e-30
-    assert float(np.max(err)) <= gate, "%s: dh max err %.3e > gate %.3e" % (what, np.max(err), gate)
-    bad = np.argwhere(err > bound)
-    assert bad.size == 0, "%s: dh bound broken at %s" % (what, bad[0])
-
-
-def _check_all(grads, ref, env, l_h, dtype, rows, what):
-    names = ("dq", "dk", "dv")
-    for name, g, r, e in zip(names, grads[:3], ref[:3], env[:3]):
-        check(to_np(g), r, e, l_h, dtype, "%s %s" % (what, name))
-    _check_dh(grads[3], ref[3], env[3], dtype, rows, what)
-
-
-def _rows(B, L, D, gs, l_h, dtype):
-    n = hc.bwd_workspace_bytes(B, L, D, gs, l_h, hc.DTYPE_BF16 if dtype == torch.bfloat16 else hc.DTYPE_F32)
-    return max(1, n // ((D // 16) * l_h * 4))
+_refs = bwd_refs
+_check_dh = check_dh
+_check_all = check_bwd
+_rows = bwd_rows
 
 
 BWD_SHAPES = [

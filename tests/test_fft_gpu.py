@@ -24,7 +24,7 @@ import torch
 
 import gated_convolution_sequence_amd as hc
 import oracle
-from gpu_util import DEV, log, nan_like, to_np
+from gpu_util import DEV, check_long, log, run_long, to_np
 from workloads import WORKLOADS, gaussian_inputs, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -38,45 +38,6 @@ def gpu():
     hc.lib()
     yield
     torch.cuda.synchronize()
-
-
-def transform_len(L, l_h):
-    n = L + min(l_h, L) - 1
-    return 1 << max(2, (n - 1).bit_length())
-
-
-def run_long(q, k, v, h, gs, pad=16):
-    n = q.numel()
-    big = torch.full((n + 2 * pad,), 7.0, dtype=q.dtype, device=q.device)
-    out = big[pad:pad + n].view(q.shape)
-    out.fill_(float("nan"))
-    hc.conv_fwd_long(q, k, v, h, gs, out=out)
-    torch.cuda.synchronize()
-    assert torch.all(big[:pad] == 7.0) and torch.all(big[pad + n:] == 7.0), "write outside out"
-    return out
-
-
-def check_long(y, q, k, v, h, gs, dtype, what=""):
-    """Gate and the norm-wise FFT bound against the fp64 oracle (CPU tensors)."""
-    qn, kn, vn, hn = (to_np(t) for t in (q, k, v, h))
-    ref = oracle.conv_fwd_ref(qn, kn, vn, hn, gs)
-    y = to_np(y)
-    assert np.all(np.isfinite(y)), what
-    err = np.abs(y - ref)
-    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
-    gate = (1e-2 if dtype == torch.bfloat16 else 1e-5) * scale
-    assert float(np.max(err)) <= gate, "%s: max err %.3e > gate %.3e" % (what, np.max(err), gate)
-    B, L, D = qn.shape
-    N = transform_len(L, hn.shape[1])
-    e = (math.log2(N) + 2) * 7 * 2.0 ** -24
-    x = kn * vn
-    xn = np.sqrt(np.sum(x * x, axis=1))                   # [B, D]
-    hnorm = np.sqrt(np.sum(hn * hn, axis=1))[np.arange(D) // gs]  # [D]
-    r = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -24
-    bound = r * np.abs(ref) + np.abs(qn) * (3 * e * math.sqrt(N) * hnorm[None, None, :] * xn[:, None, :]) + 1e-30
-    bad = np.argwhere(err > bound)
-    assert bad.size == 0, "%s: FFT bound broken at %s" % (what, bad[0])
-    return float(np.max(err)) / scale if scale else 0.0
 
 
 SHAPES = [

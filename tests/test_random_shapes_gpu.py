@@ -1,0 +1,116 @@
+"""Seeded random shapes through every entry point, against the fp64 oracle.
+
+The fixed edge lists of the other GPU suites pick the seams by hand (chunk,
+block and slab boundaries, history depths, spans).  Here a fixed-seed draw
+of shapes -- batch rows, ragged lengths, widths, group sizes, filter
+lengths, requested spans, both dtypes -- goes through the same C ABI and is
+held to the same bars (tests/gpu_util.py), so combinations the lists do not
+name are covered too.  The draw is fixed: the cases are the same on every
+run.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_convolution_sequence_amd as hc
+from gpu_util import (DEV, bwd_refs, bwd_rows, check, check_bwd, check_long, log, ref_and_envelope, run,
+                      run_long, to_np)
+from workloads import gaussian_inputs, normal_activation
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+N_CASES = 12
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    hc.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _draw(kind, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(N_CASES):
+        dt = str(rng.choice(["bf16", "f32"]))
+        B = int(rng.integers(1, 4))
+        L = int(rng.choice([rng.integers(1, 130), rng.integers(130, 3000)]))
+        if kind == "grouped":
+            gs = int(rng.choice([16, 32, 48, 64]))
+            D = gs * int(rng.integers(1, max(2, 384 // gs) + 1))
+            l_h = int(rng.integers(1, 129))
+            span = int(rng.choice([0, 1, 2, 4, 8, 16, 32]))
+            cases.append((dt, B, L, D, gs, l_h, span))
+        elif kind == "chunk_direction":
+            gs = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 12, 24]))
+            unit = np.lcm(gs, 8 if dt == "bf16" else 4)  # whole 16-byte rows
+            D = int(unit * rng.integers(1, max(2, 192 // unit) + 1))
+            l_h = int(rng.integers(1, 129))
+            span = int(rng.choice([0, 4, 8, 16]))
+            cases.append((dt, B, L, D, gs, l_h, span))
+        elif kind == "backward":
+            gs = int(rng.choice([16, 32, 48]))
+            D = gs * int(rng.integers(1, max(2, 192 // gs) + 1))
+            L = min(L, 1500)
+            l_h = int(rng.integers(1, 129))
+            cases.append((dt, B, L, D, gs, l_h, 0))
+        else:  # long filters
+            gs = int(rng.choice([1, 2, 3, 4, 8, 16]))
+            D = int(np.lcm(gs, 2) * rng.integers(1, max(2, 48 // np.lcm(gs, 2)) + 1))
+            l_h = int(rng.integers(1, 5000))
+            cases.append((dt, B, L, D, gs, l_h, 0))
+    return cases
+
+
+def _ids(cases):
+    return ["%s-B%d-L%d-D%d-gs%d-lh%d-s%d" % c for c in cases]
+
+
+GROUPED = _draw("grouped", 101)
+CHUNK_DIR = _draw("chunk_direction", 202)
+BACKWARD = _draw("backward", 303)
+LONG = _draw("long", 404)
+
+
+@pytest.mark.parametrize("dt,B,L,D,gs,l_h,span", GROUPED, ids=_ids(GROUPED))
+def test_random_grouped_forward(dt, B, L, D, gs, l_h, span):
+    log("random grouped %s B=%d L=%d D=%d gs=%d l_h=%d span=%d" % (dt, B, L, D, gs, l_h, span))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B * 100003 + L * 7 + D + l_h)
+    y = run(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), gs, span)
+    ref, env = ref_and_envelope(q, k, v, h, gs)
+    check(to_np(y), ref, env, l_h, dtype, "random grouped")
+
+
+@pytest.mark.parametrize("dt,B,L,D,gs,l_h,span", CHUNK_DIR, ids=_ids(CHUNK_DIR))
+def test_random_chunk_direction_forward(dt, B, L, D, gs, l_h, span):
+    log("random chunk-direction %s B=%d L=%d D=%d gs=%d l_h=%d span=%d" % (dt, B, L, D, gs, l_h, span))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B * 100019 + L * 11 + D + l_h)
+    y = run(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), gs, span)
+    ref, env = ref_and_envelope(q, k, v, h, gs)
+    check(to_np(y), ref, env, l_h, dtype, "random chunk-direction")
+
+
+@pytest.mark.parametrize("dt,B,L,D,gs,l_h,span", BACKWARD, ids=_ids(BACKWARD))
+def test_random_backward(dt, B, L, D, gs, l_h, span):
+    log("random backward %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B * 100043 + L * 13 + D + l_h)
+    dy = normal_activation((B, L, D), dtype, "cpu", seed=L + D + 3)
+    grads = hc.conv_bwd(*[t.to(DEV) for t in (q, k, v, h, dy)], gs)
+    torch.cuda.synchronize()
+    ref, env = bwd_refs(q, k, v, h, dy, gs)
+    check_bwd(grads, ref, env, l_h, dtype, bwd_rows(B, L, D, gs, l_h, dtype), "random backward")
+
+
+@pytest.mark.parametrize("dt,B,L,D,gs,l_h,span", LONG, ids=_ids(LONG))
+def test_random_long_filter(dt, B, L, D, gs, l_h, span):
+    log("random long filter %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B * 100057 + L * 17 + D + l_h)
+    y = run_long(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), gs)
+    check_long(y, q, k, v, h, gs, dtype, "random long filter")

@@ -641,10 +641,43 @@ def cpu_baseline(layers, sets, budget_s):
         # the step's time at this rate: every layer's full size
         t_total += dt * (w.elems / n)
         elems_total += w.elems
+    threads = oracle.num_threads()
+    # one thread: the same channels as above (the same row width, so the
+    # same cache behaviour), the first R rows only, R >= 2 l_h (rows before
+    # l_h have shorter sums), sized from the rate above for about 3 s per
+    # layer; scaled to the full step the same way
+    t_step_1, desc_1, secs_1 = 0.0, [], 0.0
+    oracle.set_num_threads(1)
+    try:
+        for li, w in enumerate(layers):
+            q, k, v, h, _ = sets[li][0]
+            ch = per_layer[li]["channels"]
+            per_elem_1 = per_layer[li]["seconds"] * threads / (w.B * w.L * ch)
+            R = int(min(w.L, max(2 * w.l_h, 3.0 / max(per_elem_1 * w.B * ch, 1e-12))))
+            rows = lambda a: a[:, :R, :ch].to("cpu", dtype=torch.float64).numpy()
+            hq = h[: ch // w.group_size].to("cpu", dtype=torch.float64).numpy()
+            qa, ka, va = rows(q), rows(k), rows(v)
+            t0 = time.perf_counter()
+            oracle.conv_fwd_ref(qa, ka, va, hq, w.group_size)
+            dt1 = time.perf_counter() - t0
+            secs_1 += dt1
+            t_step_1 += dt1 * (w.elems / (w.B * R * ch))
+            desc_1.append("%s: first %d of %d rows x first %d channels" % (w.name, R, w.L, ch))
+    finally:
+        oracle.set_num_threads(threads)
+    try:
+        import psutil
+        physical = psutil.cpu_count(logical=False)
+    except ImportError:
+        physical = None
     return {"value": round(elems_total / t_total / 1e9, 5), "unit": UNIT,
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": threads, "kind": "oracle",
             "sample": "; ".join(sample_desc) + " (rate scaled to the full step)",
-            "cpu_count": os.cpu_count(), "layers": per_layer}
+            "cpu_count": os.cpu_count(), "physical_cores": physical,
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"), "layers": per_layer,
+            "single_thread": {"value": round(elems_total / t_step_1 / 1e9, 6), "unit": UNIT,
+                              "sample": "; ".join(desc_1) + " (one thread; rate scaled to the full step)",
+                              "seconds": round(secs_1, 3)}}
 
 
 if __name__ == "__main__":

@@ -57,6 +57,8 @@ def _load():
         lib.hyena_ref_bwd_f64.restype = ctypes.c_int
         lib.hyena_ref_num_threads.argtypes = []
         lib.hyena_ref_num_threads.restype = ctypes.c_int
+        lib.hyena_ref_set_num_threads.argtypes = [ctypes.c_int]
+        lib.hyena_ref_set_num_threads.restype = None
         _lib = lib
     return _lib
 
@@ -64,6 +66,11 @@ def _load():
 def num_threads() -> int:
     """OpenMP threads one oracle call uses."""
     return int(_load().hyena_ref_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads later oracle calls use (for timing; results do not depend on it)."""
+    _load().hyena_ref_set_num_threads(int(n))
 
 
 def _f64(a) -> np.ndarray:

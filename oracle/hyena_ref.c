@@ -87,6 +87,17 @@ int hyena_ref_num_threads(void)
 #endif
 }
 
+/* Set the OpenMP threads later calls use (n >= 1); for timing the oracle
+ * on one core beside all of them.  No effect without OpenMP. */
+void hyena_ref_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * Backward of the same operator: given dy = dLoss/dy, the gradients of
  *     y[b,t,d] = q[b,t,d] * z[b,t,d],   z[b,t,d] = sum_{s<l_h, s<=t} h[g,s] x[b,t-s,d],

@@ -22,7 +22,9 @@ Reported (one JSON line):
   cpu_baseline the fp64 oracle on the host cores over the full step's inputs;
   naive_conv1d the same step written with torch's depthwise F.conv1d (bf16),
                with and without the layout permutes;
-  batched_mr   (with --batched) the MR layer at B=4, L=32768.
+  batched_mr   (with --batched) the MR layer at B=4, L=32768;
+  halo_shard   (with --halo) the second half of the MR layer through the
+               history-prefix entry point, beside the plain forward.
 Input sets rotate over ``--sets`` copies per layer so that no launch finds its
 operands in the 256 MB Infinity Cache.
 """
@@ -69,6 +71,10 @@ def parse():
     ap.add_argument("--skip-backward", action="store_true")
     ap.add_argument("--skip-chunk-direction", action="store_true")
     ap.add_argument("--skip-long-filter", action="store_true")
+    ap.add_argument("--halo", action="store_true",
+                    help="also time one shard of the MR layer through hyena_conv_fwd_halo (the second half "
+                         "of the sequence with its l_h - 1 prefix rows); off by default for the same "
+                         "reason as --batched")
     ap.add_argument("--batched", action="store_true",
                     help="also time the batched MR configuration (B=4, L=32768); off by default because "
                          "its launches share the kernel instance of the B=1 MR layer, which would mix "
@@ -315,6 +321,8 @@ def main():
     # ---- the batched MR configuration (B=4, L=32768), outside the step ---
     if args.batched:
         out["batched_mr"] = batched_mr_rate(stream, max(10, K // 10))
+    if args.halo:
+        out["halo_shard"] = halo_shard_rate(layers[-1], sets[-1], stream, max(20, K // 4))
 
     # ---- attainable streaming rate on this GPU (same bytes, no convolution)
     out["stream_reference"] = stream_reference(layers[-1], sets[-1], stream, max(10, K // 4))
@@ -425,6 +433,47 @@ class HipEvents:
         if rc != 0:
             raise RuntimeError("hipEventElapsedTime: %d" % rc)
         return f.value
+
+
+def halo_shard_rate(w, per, stream, reps):
+    """One shard of a layer as one of two GPUs would run it: rows [L/2, L)
+    through hyena_conv_fwd_halo with the l_h - 1 rows before L/2 as the
+    prefix, next to the plain forward of an L/2-row sequence (no prefix).
+    Mean launch times from fence-free HIP events; the input sets rotate."""
+    import torch
+    import gated_convolution_sequence_amd as hc
+    s, P = w.L // 2, w.l_h - 1
+    shards = []
+    for (q, k, v, h, _) in per:
+        sl = lambda a: a[:, s:].contiguous()
+        pre = lambda a: a[:, s - P:s].contiguous()
+        shards.append((sl(q), sl(k), sl(v), h, pre(k), pre(v), torch.empty_like(sl(q))))
+    ev = HipEvents()
+
+    def timed(with_prefix):
+        for i in range(3):
+            q, k, v, h, kp, vp, y = shards[i % len(shards)]
+            hc.conv_fwd(q, k, v, h, w.group_size, out=y, stream=stream,
+                        k_prev=kp if with_prefix else None, v_prev=vp if with_prefix else None)
+        torch.cuda.synchronize()
+        marks = [(ev.create(), ev.create()) for _ in range(reps)]
+        for i, (e0, e1) in enumerate(marks):
+            q, k, v, h, kp, vp, y = shards[i % len(shards)]
+            ev.record(e0, stream)
+            hc.conv_fwd(q, k, v, h, w.group_size, out=y, stream=stream,
+                        k_prev=kp if with_prefix else None, v_prev=vp if with_prefix else None)
+            ev.record(e1, stream)
+        torch.cuda.synchronize()
+        return sum(ev.elapsed_ms(e0, e1) for e0, e1 in marks) / reps
+    t_halo, t_plain = timed(True), timed(False)
+    alg = 8 * w.B * (w.L - s) * w.D
+    res = {"layer": w.name, "B": w.B, "rows": w.L - s, "prefix_rows": P, "D": w.D, "l_h": w.l_h,
+           "halo_us": round(t_halo * 1e3, 2), "plain_us": round(t_plain * 1e3, 2),
+           "halo_hbm_frac": round(alg / (t_halo * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "plain_hbm_frac": round(alg / (t_plain * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "launches": reps}
+    del shards
+    torch.cuda.empty_cache()
+    return res
 
 
 def batched_mr_rate(stream, reps):

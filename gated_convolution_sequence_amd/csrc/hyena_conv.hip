@@ -697,10 +697,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // LDS ring); the forward's Toeplitz GEMMs (page "04. hardware-aware
 // convolution kernels", sections 3-4) read their time-major operand
 // fragments from the same ring, keeping the previous chunks' fragments in
-// registers.  The ring's swizzle, 16-byte segment XOR (row & 15) ^ 4 (bit 4
-// of the row), is conflict-free for both reads: 16 consecutive rows at one
-// channel quad (the gradient's products) and 4 row groups of 8 at one
-// channel (the convolution's fragments).
+// registers.  One swizzle of the ring serves both reads (see lds_addr).
 // ---------------------------------------------------------------------------
 template <int KH, int S, int PF>
 __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
@@ -773,9 +770,18 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
         const int r = (row0 + c * kChunk + i * T::RPL) * row_bytes + ld_base;
         return (seg_ok && need) ? (uint32_t)r : kOOB;
     };
+    // Swizzle of the row-major tiles (LDS of 32 four-byte banks, 128 bytes
+    // per cycle): the 16-byte unit XOR U(row) and the 8-byte half XOR V(row),
+    //     U = (row & 7) ^ 2 ((row >> 3) & 3),   V = (row >> 3) & 1.
+    // 16 consecutive rows at one 8-byte channel quad (the gradient's
+    // operands, 16 lanes a cycle) land on 16 distinct 8-byte slots, and 4 row
+    // groups of 8 at 16 consecutive channels (the convolution's fragments)
+    // on 32 distinct banks.
+    auto swz_u = [](int row) -> int { return (row & 7) ^ (((row >> 3) & 3) << 1); };
+    auto swz_v = [](int row) -> int { return (row >> 3) & 1; };
     auto lds_addr = [&](int row, int byte) -> int {
-        const int f = (row & 15) ^ (((row >> 4) & 1) << 2);
-        return row * PITCH + ((((byte >> 4) ^ f)) << 4) + (byte & 15);
+        return row * PITCH + ((((byte >> 4) ^ swz_u(row))) << 4) + (((((byte >> 3) & 1) ^ swz_v(row))) << 3) +
+               (byte & 7);
     };
 
     u32x4_t kr[PF][T::NLD], vr[PF][T::NLD], qr[PF][T::NLD], dr[PF][T::NLD];
@@ -793,6 +799,7 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
         }
     };
     // elementwise product of two 16-byte vectors, rounded to bf16 -> LDS tile
+    // (one 16-byte write per unit, its 8-byte halves swapped where V = 1)
     auto put = [&](unsigned char *tile, const u32x4_t *a, const u32x4_t *b2) {
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
@@ -801,7 +808,8 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 xv[e] = pack_bf16(bf_lo(a[i][e]) * bf_lo(b2[i][e]), bf_hi(a[i][e]) * bf_hi(b2[i][e]));
-            *(u32x4_t *)(&tile[lds_addr(row, ld_seg * 16)]) = xv;
+            const u32x4_t wv = swz_v(row) ? u32x4_t{xv[2], xv[3], xv[0], xv[1]} : xv;
+            *(u32x4_t *)(&tile[row * PITCH + ((ld_seg ^ swz_u(row)) << 4)]) = wv;
         }
     };
     auto st_addr = [&](int row, int seg) -> int { return row * ST_PITCH + ((seg ^ (row & 15)) << 4); };
@@ -818,13 +826,11 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
         for (int j = 0; j < 8; ++j) F[e][j] = (__bf16)hs[w][16 * e + n16 - 8 * q4 - j + kHOff];
     // Time-major fragment reads (A = X^T: lane n16 = channel 16 w + n16,
     // element j = row 8 q4 + j of a 32-row step): the byte offsets of the
-    // eight rows within a tile, each lds_addr(row, 2 channel).
+    // eight rows within a tile (the swizzle repeats every 32 rows).
     const int ch = w * kTile + n16;
-    const int gq = (8 * (q4 & 1)) ^ ((q4 >> 1) << 2);
     int fr_off[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        fr_off[j] = (8 * q4 + j) * PITCH + ((((ch >> 3) ^ gq ^ j)) << 4) + ((ch & 7) << 1);
+    for (int j = 0; j < 8; ++j) fr_off[j] = lds_addr(8 * q4 + j, 2 * ch);
     auto read_frags = [&](const unsigned char *tb, frag *dst) {
 #pragma unroll
         for (int kk = 0; kk < M::FPC; ++kk)
@@ -978,7 +984,8 @@ template <bool F32> constexpr int kNumSpansFor = F32 ? 3 : kNumSpans;
 //     applied in the MFMA's own layout (lane: 4 consecutive times of one
 //     sub-chunk);
 //   * the taps as a table of pairs (h[m], h[m-1]) (fp32: single taps), so an
-//     A operand register is one 4-byte read.
+//     A operand register is one 4-byte read; stored in reverse, so the four
+//     pairs of one operand lie at rising addresses in operand order.
 // Global loads give a thread 4 consecutive rows of 8 (fp32: 4) channels; the
 // thread writes them to LDS per channel, 4 times at once, and the epilogue
 // reads them back the same way, so every global access is a 16-byte row

@@ -154,6 +154,14 @@ template <> struct Mma<true> {
     static constexpr int FPC = kChunk / ROWS;
 };
 
+// Staging buffers of the accumulator tile: two (each item's epilogue
+// overlaps the next item's matrix-core work) from this many history steps,
+// where registers already hold a CU to one workgroup; below, one, so that
+// two workgroups still fit a CU's LDS.
+#ifndef HYENA_ST2_MIN_KH
+#define HYENA_ST2_MIN_KH 2
+#endif
+
 // Kernel: F32 selects the element type, KH the 32-row history steps
 // (KH = ceil((l_h - 1) / 32)), PF the chunks of k, v and q kept in flight,
 // S the chunks of one span.  The walk over the span is fully unrolled: the
@@ -184,11 +192,12 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     constexpr int NH = HROWS / M::ROWS;                   // history fragments
     constexpr int NX = NH + M::FPC;                       // fragments one chunk reads
     constexpr int ST_PITCH = kSlab * 4;                   // fp32 staging row, bytes
+    constexpr int kStBufs = KH >= HYENA_ST2_MIN_KH ? 2 : 1;
 
     // x = k*v of the current chunk (row-major, swizzled), the fp32
     // accumulators of the current chunk (row-major, swizzled) and the filters.
     __shared__ __attribute__((aligned(16))) unsigned char xs[kChunk * T::PITCH];
-    __shared__ __attribute__((aligned(16))) unsigned char st[kChunk * ST_PITCH];
+    __shared__ __attribute__((aligned(16))) unsigned char st[kStBufs * kChunk * ST_PITCH];
     __shared__ float hs[kWaves][kHLen];
 
     const int tid = threadIdx.x;
@@ -390,33 +399,41 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
         __syncthreads();
         read_frags(dst);
     };
-    // compute item j (chunk c) from its NX fragments Xc (history first)
-    auto compute = [&](int j, const frag *Xc) {
-        const int c = comp_chunk(j);
+    // compute item j (chunk c) from its NX fragments Xc (history first):
+    // the four 16-row output tiles into registers
+    auto mma = [&](const frag *Xc, f32x4_t *acc) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kk = 0; kk < NX; ++kk) {
                 if constexpr (F32) {
                     const int e4 = 4 * nt - (kk - NH);
                     if (e4 < -3 || e4 + 3 >= NE) continue;
                     if (4 * e4 - 3 >= p.l_h) continue;  // every tap past the filter
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Xc[kk], F[e4 + 3], acc, 0, 0, 0);
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(Xc[kk], F[e4 + 3], acc[nt], 0, 0, 0);
                 } else {
                     const int e = nt - 2 * (kk - NH);
                     if (e < 0) continue;  // strictly above the diagonal: all zero
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Xc[kk], F[e], acc, 0, 0, 0);
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Xc[kk], F[e], acc[nt], 0, 0, 0);
                 }
             }
-            // lane holds output time 16 nt + n16, channels 4 q4 .. 4 q4 + 3
-            *(f32x4_t *)(&st[st_addr(16 * nt + n16, 4 * w + q4)]) = acc;
         }
-        __syncthreads();
-        // epilogue: y = q * acc (and y2 = g2 * acc) for this thread's rows,
-        // 16-byte stores.  LDS tiles are in walk order; io_off maps the
-        // thread's walk row to its physical row (REV: backwards) for the
-        // gate load and the store alike.
+    };
+    // the tiles of item j -> its staging buffer (lane: output time 16 nt +
+    // n16, channels 4 q4 .. 4 q4 + 3)
+    auto stage = [&](int j, const f32x4_t *acc) {
+        unsigned char *sb = st + (j % kStBufs) * (kChunk * ST_PITCH);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) *(f32x4_t *)(&sb[st_addr(16 * nt + n16, 4 * w + q4)]) = acc[nt];
+    };
+    // epilogue of item j, once its staging buffer is complete: y = q * acc
+    // (and y2 = g2 * acc) for this thread's rows, 16-byte stores.  LDS tiles
+    // are in walk order; io_off maps the thread's walk row to its physical
+    // row (REV: backwards) for the gate load and the store alike.
+    auto finish = [&](int j) {
+        const int c = comp_chunk(j);
+        const unsigned char *sb = st + (j % kStBufs) * (kChunk * ST_PITCH);
         u32x4_t (*qd)[T::NLD] = qr[j % PF];
         u32x4_t yv[NG][T::NLD];
 #pragma unroll
@@ -424,10 +441,10 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
             const int row = i * T::RPL + ld_row;
             f32x4_t a[2];
             if constexpr (F32) {
-                a[0] = *(const f32x4_t *)(&st[st_addr(row, ld_seg)]);
+                a[0] = *(const f32x4_t *)(&sb[st_addr(row, ld_seg)]);
             } else {
-                a[0] = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg)]);
-                a[1] = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg + 1)]);
+                a[0] = *(const f32x4_t *)(&sb[st_addr(row, 2 * ld_seg)]);
+                a[1] = *(const f32x4_t *)(&sb[st_addr(row, 2 * ld_seg + 1)]);
             }
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
@@ -451,6 +468,21 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
             if constexpr (DUAL)
                 __builtin_amdgcn_raw_buffer_store_b128(yv[NG - 1][i], ry2, io_off(c, i, true), 0, kStorePolicy);
         }
+    };
+    // compute item j.  With two staging buffers the previous item's
+    // epilogue runs here, while this item's MFMAs execute; its buffer was
+    // completed before the last barrier, and the buffer this item stages
+    // into was last read before it.  The last item's epilogue follows the
+    // walk.  With one buffer, each item's epilogue follows its own barrier.
+    auto compute = [&](int j, const frag *Xc) {
+        f32x4_t acc[4];
+        mma(Xc, acc);
+        if constexpr (kStBufs == 2) {
+            if (j > 0) finish(j - 1);
+        }
+        stage(j, acc);
+        __syncthreads();
+        if constexpr (kStBufs == 1) finish(j);
     };
 
     // ---- phase 1: the span's own chunks ------------------------------------
@@ -485,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
         constexpr int HF = H * M::FPC;
 #pragma unroll
         for (int c = 0; c < ND; ++c) {
-            if (c > 0) __syncthreads();  // st is rewritten by this compute
+            if (kStBufs == 1 && c > 0) __syncthreads();  // st is rewritten by this compute
             frag Xc[NX];
 #pragma unroll
             for (int kk = 0; kk < NX; ++kk) {
@@ -495,6 +527,7 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
             compute(S - ND + c, Xc);
         }
     }
+    if constexpr (kStBufs == 2) finish(S - 1);
 }
 
 // ---------------------------------------------------------------------------

@@ -344,10 +344,11 @@ def backward_rates(layers, sets, stream, reps):
 
     Minimal traffic of the backward is 14 B per token*channel in bf16 (q, k,
     v, dy read once; dq, dk, dv written once).  The library's bf16 backward
-    moves 22 B in two passes over the rows plus a small reduction: the fused
-    dq and filter-gradient pass (q, k, v, dy -> dq, partial dh) and the
-    reversed kernel (dy, q, v, k -> dk, dv).  fp32 runs dq separately: 28
-    element-widths (56 B).
+    is one pass over the rows that moves those bytes (q, k, v, dy -> dq, dk,
+    dv, partial dh), plus a small reduction of the partial dh; each span of
+    16 chunks also reads the 32*KH rows of k, v before it and of q, dy after
+    it, and reads k, v again as the dk, dv gates (mostly L2 hits).  fp32
+    runs dq, dk/dv and dh as separate passes: 14 element-widths (56 B).
     """
     import torch
     import gated_convolution_sequence_amd as hc
@@ -382,12 +383,12 @@ def backward_rates(layers, sets, stream, reps):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
         eb = 2 if w.dtype == "bf16" else 4
-        moved = (11 if w.dtype == "bf16" else 14) * eb * w.elems  # element accesses x width
+        moved = (7 if w.dtype == "bf16" else 14) * eb * w.elems  # element accesses x width
         res[w.name] = {"us": round(us, 2), "G_tok_ch_per_s": round(w.elems / (us * 1e-6) / 1e9, 2),
                        "min_bytes": 7 * eb * w.elems, "moved_bytes": moved,
                        "GBs_vs_min_bytes": round(7 * eb * w.elems / (us * 1e-6) / 1e9, 1),
                        "GBs_moved": round(moved / (us * 1e-6) / 1e9, 1),
-                       "kernels": 3 if w.dtype == "bf16" else 4, "workspace_bytes": ws_n}
+                       "kernels": 2 if w.dtype == "bf16" else 4, "workspace_bytes": ws_n}
         del dys
     return res
 

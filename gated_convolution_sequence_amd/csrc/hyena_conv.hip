@@ -548,11 +548,12 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
 struct DhParams {
     const void *q, *k, *v, *dy;
     float *ws;          // [B * n_spans][D / 16][l_h] partial sums
-    const void *h;      // filters (the fused dq form only)
-    void *dq;           // dq output (the fused dq form only)
+    const void *h;      // filters (the fused forms only)
+    void *dq;           // dq output (the fused forms only)
+    void *dk, *dv;      // dk, dv outputs (the whole-backward form only)
     int64_t L;
     int32_t D, l_h, n_spans, n_slabs;
-    int32_t group_size; // (the fused dq form only)
+    int32_t group_size; // (the fused forms only)
 };
 
 // One chunk of q, k, v and dy in flight per workgroup, and at most 128
@@ -731,8 +732,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // convolution kernels", sections 3-4) read their time-major operand
 // fragments from the same ring, keeping the previous chunks' fragments in
 // registers.  One swizzle of the ring serves both reads (see lds_addr).
+//
+// DKV adds dk = v dx and dv = k dx, dx[t] = sum_s h[s] dz[t + s], to the same
+// walk, so that q, k, v and dy are read once and dq, dk, dv written once (14
+// bytes per token-channel).  dz = dy q goes to a second ring; the walk runs
+// H chunks past the span (dz rows only) and completes chunk c - H at chunk
+// c, once dz is resident up to 32 KH rows past it.  Read backwards in time,
+// dx is the causal Toeplitz product again: the same operand fragments F, with
+// the dz fragments taken in reversed row order and the outputs staged in
+// reversed row order, in a second staging tile (the staged filter taps share
+// its memory: they are read before the walk's first barrier, the tile is
+// written after it), so the walk keeps two barriers per chunk in 160 KiB of
+// LDS.  Every product and its accumulation order is the one the forward
+// kernel walked backwards (REV) computes, so dk and dv equal it.
 // ---------------------------------------------------------------------------
-template <int KH, int S, int PF>
+template <int KH, int S, int PF, bool DKV>
 __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
     using T = Tr<false>;
     using M = Mma<false>;
@@ -740,6 +754,8 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
     constexpr int HROWS = 32 * KH;
     constexpr int H = (HROWS + kChunk - 1) / kChunk;      // history chunks
     constexpr int RING = H + 1;                           // x chunks resident
+    constexpr int NZ = DKV ? RING : 1;                    // dz chunks resident
+    constexpr int FH = DKV ? H : 0;                       // chunks walked past the span
     constexpr int NDL = 2 * KH + 1;                       // diagonals (16-row units)
     constexpr int NH = HROWS / M::ROWS;                   // history fragments
     constexpr int NX = NH + M::FPC;                       // fragments one chunk reads
@@ -747,14 +763,26 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
     constexpr int PITCH = T::PITCH;
     constexpr int TILE_B = kChunk * PITCH;
     constexpr int ST_PITCH = kSlab * 4;                   // fp32 staging row, bytes
-    constexpr int WALK_B = (RING + 1) * TILE_B + kChunk * ST_PITCH;  // ring, dz, staging
+    constexpr int NST = DKV ? 2 : 1;                      // staging tiles
+    constexpr int WALK_B = (RING + NZ) * TILE_B + NST * kChunk * ST_PITCH;  // rings, staging
     constexpr int LAG_B = kWaves * NDL * 256 * 4;
+    static_assert(!DKV || kWaves * kHLen * 4 <= kChunk * ST_PITCH, "taps fit the second staging tile");
 
     __shared__ __attribute__((aligned(16))) unsigned char lds[WALK_B > LAG_B ? WALK_B : LAG_B];
-    __shared__ float hs[kWaves][kHLen];
-    auto xr = [&](int i) -> unsigned char * { return lds + i * TILE_B; };
-    unsigned char *const dzs = lds + RING * TILE_B;
-    unsigned char *const st = lds + (RING + 1) * TILE_B;
+    // chunk c's x and dz tiles (x from chunk -H, dz from chunk 0)
+    auto xr = [&](int c) -> unsigned char * { return lds + ((c + H + 4 * RING) % RING) * TILE_B; };
+    auto zr = [&](int c) -> unsigned char * {
+        return lds + (RING + (DKV ? (c + H + 4 * RING) % RING : 0)) * TILE_B;
+    };
+    unsigned char *const st = lds + (RING + NZ) * TILE_B;
+    unsigned char *const st2 = st + (NST - 1) * kChunk * ST_PITCH;  // (DKV) dx staging
+    float *hsw;  // this wave's kHLen staged taps
+    if constexpr (DKV) {
+        hsw = (float *)st2 + (threadIdx.x >> 6) * kHLen;
+    } else {
+        __shared__ float hs[kWaves][kHLen];
+        hsw = hs[threadIdx.x >> 6];
+    }
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -776,11 +804,17 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
     const size_t base_off = ((size_t)b * (size_t)p.L + (size_t)base_row) * (size_t)row_bytes +
                             (size_t)c_begin * T::EB;
     const uint32_t nrec = (uint32_t)((t_stop - base_row) * row_bytes - c_begin * T::EB);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + base_off, nrec);
+    // q and dy: also the FH chunks past the span (the host keeps that window
+    // below 2^31 bytes too)
+    const int64_t t_fut = min(p.L, t_stop + (int64_t)FH * kChunk);
+    const uint32_t nrec_z = (uint32_t)((t_fut - base_row) * row_bytes - c_begin * T::EB);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + base_off, nrec_z);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + base_off, nrec);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + base_off, nrec);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.dy + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.dy + base_off, nrec_z);
     const __amdgpu_buffer_rsrc_t rdq = make_rsrc((char *)p.dq + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rdk = make_rsrc((char *)(DKV ? p.dk : p.dq) + base_off, nrec);
+    const __amdgpu_buffer_rsrc_t rdv = make_rsrc((char *)(DKV ? p.dv : p.dq) + base_off, nrec);
     const int row0 = (int)(t_begin - base_row);
 
     // ---- stage this wave's filter (zero outside [0, l_h)) -----------------
@@ -791,7 +825,7 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
             const int tap = i - kHOff;
             float hv = 0.0f;
             if (tile_ok && tap >= 0 && tap < p.l_h) hv = bf_lo(((const uint16_t *)p.h)[(size_t)g * p.l_h + tap]);
-            hs[w][i] = hv;
+            hsw[i] = hv;
         }
     }
 
@@ -818,15 +852,21 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
     };
 
     u32x4_t kr[PF][T::NLD], vr[PF][T::NLD], qr[PF][T::NLD], dr[PF][T::NLD];
-    // chunks -H .. S-1 in order; history chunks need no q, dy
+    // DKV reads k and v again FH chunks later, as the dk, dv gates: these
+    // first reads allocate in L2 so that the second mostly hits (measured:
+    // 131 -> 100 us for the SE backward, 137 -> 116 us for MR, with
+    // streaming first reads)
+    constexpr int kKvPolicy = DKV ? 0 : kLoadPolicy;
+    // chunks -H .. S-1+FH in order; history chunks need no q, dy, and the
+    // chunks past the span no k, v
     auto load = [&](int c, int slot) {
         const bool need = c < S;
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
             const uint32_t o = off(c, i, need);
-            const uint32_t og = off(c, i, need && c >= 0);
-            kr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadPolicy));
-            vr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kLoadPolicy));
+            const uint32_t og = off(c, i, c >= 0 && c < S + FH);
+            kr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kKvPolicy));
+            vr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kKvPolicy));
             qr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, og, 0, kLoadPolicy));
             dr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rd, og, 0, kLoadPolicy));
         }
@@ -856,7 +896,7 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
 #pragma unroll
     for (int e = 0; e < NE; ++e)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) F[e][j] = (__bf16)hs[w][16 * e + n16 - 8 * q4 - j + kHOff];
+        for (int j = 0; j < 8; ++j) F[e][j] = (__bf16)hsw[16 * e + n16 - 8 * q4 - j + kHOff];
     // Time-major fragment reads (A = X^T: lane n16 = channel 16 w + n16,
     // element j = row 8 q4 + j of a 32-row step): the byte offsets of the
     // eight rows within a tile (the swizzle repeats every 32 rows).
@@ -864,6 +904,12 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
     int fr_off[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) fr_off[j] = lds_addr(8 * q4 + j, 2 * ch);
+    // the same read backwards in time: element j = row 31 - 8 q4 - j
+    int fr_rev[DKV ? 8 : 1];
+    if constexpr (DKV) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fr_rev[j] = lds_addr(31 - 8 * q4 - j, 2 * ch);
+    }
     auto read_frags = [&](const unsigned char *tb, frag *dst) {
 #pragma unroll
         for (int kk = 0; kk < M::FPC; ++kk)
@@ -872,31 +918,51 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
                 dst[kk][j] = __builtin_bit_cast(__bf16, *(const uint16_t *)(&tb[fr_off[j] + 32 * kk * PITCH]));
     };
 
-    frag X[NX];
+    // the previous chunks' fragments in registers (DKV: read from the ring)
+    frag X[DKV ? 1 : NX];
+    if constexpr (!DKV) {
 #pragma unroll
-    for (int i = 0; i < NX; ++i)
+        for (int i = 0; i < NX; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) X[i][j] = (__bf16)0.0f;
+            for (int j = 0; j < 8; ++j) X[i][j] = (__bf16)0.0f;
+    }
     f32x4_t P[NDL];
 #pragma unroll
     for (int d = 0; d < NDL; ++d) P[d] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const int kbyte = (w * kTile + 4 * q4) * T::EB;  // this lane's 4 channels (gradient K)
 
-#pragma unroll
-    for (int c = -H; c < S; ++c) {
+    auto chunk_step = [&](const int c) {
         const int slot = (c + H) % PF;
-        unsigned char *xt = xr((c + H) % RING);
-        put(xt, kr[slot], vr[slot]);
+        const bool own = c >= 0 && c < S;  // a span chunk: dq and the dh products
+        const int cg = c - FH;             // the chunk whose dk, dv complete here
+        unsigned char *xt = xr(c);
+        if (c < S) put(xt, kr[slot], vr[slot]);
         u32x4_t dyc[T::NLD];
         if (c >= 0) {
-            put(dzs, dr[slot], qr[slot]);
+            put(zr(c), dr[slot], qr[slot]);
+            if (own) {
 #pragma unroll
-            for (int i = 0; i < T::NLD; ++i) dyc[i] = dr[slot][i];
+                for (int i = 0; i < T::NLD; ++i) dyc[i] = dr[slot][i];
+            }
+        }
+        // the gates of chunk cg, read again (L2 hits for the most part)
+        u32x4_t kg[DKV ? T::NLD : 1], vg[DKV ? T::NLD : 1];
+        if constexpr (DKV) {
+            if (cg >= 0) {
+#pragma unroll
+                for (int i = 0; i < T::NLD; ++i) {
+                    kg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off(cg, i, true), 0, kLoadPolicy));
+                    vg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off(cg, i, true), 0, kLoadPolicy));
+                }
+            }
         }
         load(c + PF, slot);
         __syncthreads();
-        read_frags(xt, &X[NH]);
-        if (c >= 0) {
+        if constexpr (!DKV) {
+            if (c < S) read_frags(xt, &X[NH]);
+        }
+        if (own) {
+            const unsigned char *dzs = zr(c);
             // filter gradient: P[d] += dz rows (16 a + n16) . x rows 16 (a - d) + n16
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
@@ -908,26 +974,77 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
                     const int bt = a - d;
                     const int cb = c + (bt < 0 ? -((-bt + 3) / 4) : 0);
                     const int rb = 16 * (bt - 4 * (cb - c)) + n16;
-                    const unsigned char *xt2 = xr((cb + H + 4 * RING) % RING);
+                    const unsigned char *xt2 = xr(cb);
                     const s16x4_t bv = *(const s16x4_t *)(&xt2[lds_addr(rb, kbyte)]);
                     P[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, P[d], 0, 0, 0);
                 }
             }
             // dq: the convolved chunk, 16 output rows per tile nt
+            if constexpr (DKV) {
+                // input step kappa = kk - NH: 32-row block kappa from the
+                // chunk's start (chunk c + floor(kappa / 2), half kappa & 1)
+                f32x4_t acc[4];
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int kk = 0; kk < NX; ++kk) {
-                    const int e = nt - 2 * (kk - NH);
-                    if (e < 0) continue;
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(X[kk], F[e], acc, 0, 0, 0);
+                    const int kap = kk - NH;
+                    const unsigned char *xt3 = xr(c + (kap >= 0 ? 0 : -((1 - kap) / 2))) + (kap & 1) * 32 * PITCH;
+                    frag xf;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) xf[j] = __builtin_bit_cast(__bf16, *(const uint16_t *)(&xt3[fr_off[j]]));
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        const int e = nt - 2 * kap;
+                        if (e < 0) continue;
+                        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf, F[e], acc[nt], 0, 0, 0);
+                    }
                 }
-                *(f32x4_t *)(&st[st_addr(16 * nt + n16, 4 * w + q4)]) = acc;
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) *(f32x4_t *)(&st[st_addr(16 * nt + n16, 4 * w + q4)]) = acc[nt];
+            } else {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int kk = 0; kk < NX; ++kk) {
+                        const int e = nt - 2 * (kk - NH);
+                        if (e < 0) continue;
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(X[kk], F[e], acc, 0, 0, 0);
+                    }
+                    *(f32x4_t *)(&st[st_addr(16 * nt + n16, 4 * w + q4)]) = acc;
+                }
             }
         }
-        __syncthreads();  // st complete; every read of dzs and of the oldest x chunk done
-        if (c >= 0) {
+        // dx of chunk cg, backwards in time, -> st2: output tile nt holds rows
+        // 63 - 16 nt - n16; input step kappa = kk - NH covers the 32-row
+        // block b = 1 - kappa counted from the chunk's start (chunk cg + b / 2,
+        // half b % 2), its rows in reverse
+        if constexpr (DKV) {
+            if (cg >= 0) {
+                f32x4_t ga[4];
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) ga[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kk = 0; kk < NX; ++kk) {
+                    const int blk = NH + 1 - kk;
+                    const unsigned char *zt = zr(cg + blk / 2) + (blk % 2) * 32 * PITCH;
+                    frag zf;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) zf[j] = __builtin_bit_cast(__bf16, *(const uint16_t *)(&zt[fr_rev[j]]));
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt) {
+                        const int e = nt - 2 * (kk - NH);
+                        if (e < 0) continue;
+                        ga[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(zf, F[e], ga[nt], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) *(f32x4_t *)(&st2[st_addr(63 - 16 * nt - n16, 4 * w + q4)]) = ga[nt];
+            }
+        }
+        __syncthreads();  // st, st2 complete; every read of the oldest x and dz chunks done
+        if (own) {
 #pragma unroll
             for (int i = 0; i < T::NLD; ++i) {
                 const int row = i * T::RPL + ld_row;
@@ -942,8 +1059,41 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
                 __builtin_amdgcn_raw_buffer_store_b128(yv, rdq, off(c, i, true), 0, kStorePolicy);
             }
         }
+        if constexpr (DKV) {
+            if (cg >= 0) {
 #pragma unroll
-        for (int i = 0; i < NH; ++i) X[i] = X[i + M::FPC];
+                for (int i = 0; i < T::NLD; ++i) {
+                    const int row = i * T::RPL + ld_row;
+                    const f32x4_t a0 = *(const f32x4_t *)(&st2[st_addr(row, 2 * ld_seg)]);
+                    const f32x4_t a1 = *(const f32x4_t *)(&st2[st_addr(row, 2 * ld_seg + 1)]);
+                    u32x4_t yk, yv2;
+                    yk[0] = pack_bf16(bf_lo(vg[i][0]) * a0[0], bf_hi(vg[i][0]) * a0[1]);
+                    yk[1] = pack_bf16(bf_lo(vg[i][1]) * a0[2], bf_hi(vg[i][1]) * a0[3]);
+                    yk[2] = pack_bf16(bf_lo(vg[i][2]) * a1[0], bf_hi(vg[i][2]) * a1[1]);
+                    yk[3] = pack_bf16(bf_lo(vg[i][3]) * a1[2], bf_hi(vg[i][3]) * a1[3]);
+                    yv2[0] = pack_bf16(bf_lo(kg[i][0]) * a0[0], bf_hi(kg[i][0]) * a0[1]);
+                    yv2[1] = pack_bf16(bf_lo(kg[i][1]) * a0[2], bf_hi(kg[i][1]) * a0[3]);
+                    yv2[2] = pack_bf16(bf_lo(kg[i][2]) * a1[0], bf_hi(kg[i][2]) * a1[1]);
+                    yv2[3] = pack_bf16(bf_lo(kg[i][3]) * a1[2], bf_hi(kg[i][3]) * a1[3]);
+                    __builtin_amdgcn_raw_buffer_store_b128(yk, rdk, off(cg, i, true), 0, kStorePolicy);
+                    __builtin_amdgcn_raw_buffer_store_b128(yv2, rdv, off(cg, i, true), 0, kStorePolicy);
+                }
+            }
+        }
+        // the next chunk writes st and st2 only after its first barrier
+        if constexpr (!DKV) {
+#pragma unroll
+            for (int i = 0; i < NH; ++i) X[i] = X[i + M::FPC];
+        }
+    };
+    if constexpr (DKV) {
+        // a loop at run time: unrolled, the walk's schedule needs more
+        // registers than a wave has
+#pragma unroll 1
+        for (int c = -H; c < S + FH; ++c) chunk_step(c);
+    } else {
+#pragma unroll
+        for (int c = -H; c < S; ++c) chunk_step(c);
     }
     __syncthreads();  // the staging tile is read; the lag tiles overwrite it
     // Lags, as in the filter-gradient kernel.
@@ -1358,16 +1508,17 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
 }
 
 // Kernel families and their compiled span counts (indices into kSpans).
-enum Family { kFwd = 0, kRevDual = 1, kDh = 2, kCd = 3, kDqDh = 4 };
+enum Family { kFwd = 0, kRevDual = 1, kDh = 2, kCd = 3, kDqDh = 4, kBwd = 5 };
 // (the chunk-direction kernel takes its span at run time: one entry)
 template <bool F32, int Fam> constexpr int kSpanCount =
     Fam == kFwd ? kNumSpansFor<F32> : Fam == kRevDual ? (F32 ? 2 : 4) : Fam == kDh ? (F32 ? 3 : 5)
-    : Fam == kDqDh ? 5 : 1;
+    : Fam == kDqDh || Fam == kBwd ? 5 : 1;
 
 typedef void (*DhFn)(DhParams);
 template <bool F32, int Fam> struct FnType { typedef KernelFn type; };
 template <bool F32> struct FnType<F32, kDh> { typedef DhFn type; };
 template <bool F32> struct FnType<F32, kDqDh> { typedef DhFn type; };
+template <bool F32> struct FnType<F32, kBwd> { typedef DhFn type; };
 
 template <bool F32, int Fam, int KH, int Sp>
 constexpr typename FnType<F32, Fam>::type kernel_of() {
@@ -1378,7 +1529,9 @@ constexpr typename FnType<F32, Fam>::type kernel_of() {
     else if constexpr (Fam == kDh)
         return hyena_bwd_dh_kernel<F32, KH, Sp>;
     else if constexpr (Fam == kDqDh)
-        return hyena_bwd_dq_dh_kernel<KH, Sp, 1>;  // bf16 only
+        return hyena_bwd_dq_dh_kernel<KH, Sp, 1, false>;  // bf16 only
+    else if constexpr (Fam == kBwd)
+        return hyena_bwd_dq_dh_kernel<KH, Sp, 1, true>;  // bf16 only
     else
         return hyena_fwd_cd_kernel<F32, KH>;
 }
@@ -1657,7 +1810,13 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
     }
     if (group_size % kTile != 0) return HYENA_ERR_UNSUPPORTED;
     const bool f32 = dtype == HYENA_DTYPE_F32;
-    // bf16 with both dq and dh: one kernel computes both (below)
+    // bf16 with all four gradients: one kernel computes dq, dk, dv and the
+    // partial dh, when its window (history, span, the dz rows past the span
+    // and a chunk of slack) stays below 2^31 bytes; else, with dq and dh, one
+    // kernel computes both (below)
+    const int64_t fut_rows = ((32 * (int64_t)dpl.kh + kChunk - 1) / kChunk) * kChunk;
+    const bool fused_all = dq && dk && dv && dh && !f32 &&
+                           (dpl.span * kChunk + 32 * dpl.kh + fut_rows + kChunk) * D * (int64_t)eb < kMaxWindowBytes;
     const bool fused_dq = dq && dh && !f32;
 
     // dq = dy * (h * (k v)): the forward with dy as the gate
@@ -1667,7 +1826,7 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
     }
     // dk = v * dx, dv = k * dx with dx = h applied to dz = dy q at later rows:
     // the forward walked backwards in time, x = dy q, gates v and k
-    if (dk) {
+    if (dk && !fused_all) {
         Plan pl;
         st = make_plan(B, L, D, group_size, l_h, dtype, 0, &pl, kRevDual);
         if (st != HYENA_OK) return st;
@@ -1694,13 +1853,16 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
         p.ws = (float *)workspace;
         p.h = h;
         p.dq = fused_dq ? dq : nullptr;
+        p.dk = fused_all ? dk : nullptr;
+        p.dv = fused_all ? dv : nullptr;
         p.L = L;
         p.D = (int32_t)D;
         p.l_h = (int32_t)l_h;
         p.n_spans = (int32_t)dpl.n_spans;
         p.n_slabs = (int32_t)dpl.n_slabs;
         p.group_size = (int32_t)group_size;
-        DhFn fn = fused_dq ? pick_kernel<false, kDqDh>(dpl.kh, dpl.span_index)
+        DhFn fn = fused_all  ? pick_kernel<false, kBwd>(dpl.kh, dpl.span_index)
+                  : fused_dq ? pick_kernel<false, kDqDh>(dpl.kh, dpl.span_index)
                   : f32    ? pick_kernel<true, kDh>(dpl.kh, dpl.span_index)
                            : pick_kernel<false, kDh>(dpl.kh, dpl.span_index);
         hipLaunchKernelGGL(fn, dim3((unsigned)dpl.workgroups), dim3(kThreads), 0, (hipStream_t)stream, p);

@@ -83,24 +83,42 @@ SUBSETS = [(True, False, False), (False, True, False), (False, False, True),
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("B,L,D,gs,l_h", [(1, 6, 16, 16, 4), (2, 777, 96, 32, 7), (3, 257, 128, 16, 65),
-                                          (1, 1000, 96, 48, 97), (1, 2048, 256, 16, 128)])
+                                          (1, 1000, 96, 48, 97), (1, 2048, 256, 16, 128),
+                                          (2, 768, 96, 32, 7), (3, 320, 48, 16, 65), (1, 1024, 128, 16, 128),
+                                          (1, 96, 32, 16, 1)])
 def test_output_subsets_match_the_full_call(dt, B, L, D, gs, l_h):
-    """Which gradients are requested decides which kernels run (bf16 dq with dh
-    is one fused pass; dq alone is the forward kernel, dh alone its own pass).
-    Every route sums in the same order, so each gradient has the same bits."""
+    """Which gradients are requested decides which kernels run (bf16 with all
+    four is one pass; bf16 dq with dh is one pass; dk and dv alone are the
+    forward kernel walked backwards in time; dq alone is the forward kernel,
+    dh alone its own pass).  dq and dh sum in the same order on every route,
+    so they have the same bits.  dk and dv sum each 32-row block of dz as one
+    matrix-core step: the backwards walk aligns its blocks to the sequence's
+    end, the one-pass walk to its start, so the two have the same bits when L
+    is a multiple of 32 and agree to the operands' rounding otherwise."""
     dtype = DTYPES[dt]
     log("bwd subsets %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
     q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B + L + l_h)
     dy = normal_activation((B, L, D), dtype, "cpu", seed=L + 5)
     dev = [t.to(DEV) for t in (q, k, v, h, dy)]
     full = hc.conv_bwd(*dev, gs)
+    same_blocks = dt == "f32" or L % 32 == 0
     for need in SUBSETS:
         part = hc.conv_bwd(*dev, gs, need_dq=need[0], need_dkv=need[1], need_dh=need[2])
         torch.cuda.synchronize()
         wanted = (need[0], need[1], need[1], need[2])
         for name, want, f, g in zip(("dq", "dk", "dv", "dh"), wanted, full, part):
             assert (g is not None) == want, (name, need)
-            if want:
+            if not want:
+                continue
+            if name in ("dk", "dv") and not same_blocks:
+                # fp32 sums of the same bf16 products, grouped differently,
+                # then one bf16 rounding each: within two bf16 ulps of the
+                # larger, plus the sums' own rounding (the products' scale,
+                # bounded loosely by 2^-10 of the largest output)
+                fa, ga = f.float(), g.float()
+                tol = 2.0 ** -7 * torch.maximum(fa.abs(), ga.abs()) + 2.0 ** -10 * fa.abs().max()
+                assert bool(((fa - ga).abs() <= tol).all()), (name, need)
+            else:
                 assert torch.equal(f, g), (name, need)
 
 

@@ -734,17 +734,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 // registers.  One swizzle of the ring serves both reads (see lds_addr).
 //
 // DKV adds dk = v dx and dv = k dx, dx[t] = sum_s h[s] dz[t + s], to the same
-// walk, so that q, k, v and dy are read once and dq, dk, dv written once (14
-// bytes per token-channel).  dz = dy q goes to a second ring; the walk runs
-// H chunks past the span (dz rows only) and completes chunk c - H at chunk
-// c, once dz is resident up to 32 KH rows past it.  Read backwards in time,
-// dx is the causal Toeplitz product again: the same operand fragments F, with
-// the dz fragments taken in reversed row order and the outputs staged in
-// reversed row order, in a second staging tile (the staged filter taps share
+// pass, so that q, k, v and dy are read once and dq, dk, dv written once (14
+// bytes per token-channel).  That walk runs backwards in time: walk row tau
+// is physical row L - 1 - tau, as in the forward kernel's REV form.  Then dx
+// is the causal product over dz and completes at each chunk, gated by k and
+// v still in registers, while dq runs against the walk.  dz goes to ring A
+// and x to a second ring B; the walk runs H chunks past the span (x rows
+// only) and completes dq of chunk c - H at chunk c, once x is resident up to
+// 32 KH rows past it in walk order.  dq reads the same Toeplitz fragments F,
+// with the x fragments taken in reversed row order and the outputs staged in
+// reversed row order in a second staging tile (the staged filter taps share
 // its memory: they are read before the walk's first barrier, the tile is
 // written after it), so the walk keeps two barriers per chunk in 160 KiB of
-// LDS.  Every product and its accumulation order is the one the forward
-// kernel walked backwards (REV) computes, so dk and dv equal it.
+// LDS.  dq's gate dy is read again then (one tensor; dk and dv late would
+// need both k and v again).  The dh products pair x of the chunk with dz
+// before it in walk order: the same lag.  dx and its accumulation order are
+// those of the forward kernel walked backwards, so dk and dv equal it.
 // ---------------------------------------------------------------------------
 template <int KH, int S, int PF, bool DKV>
 __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
@@ -753,8 +758,8 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
     using frag = M::frag;
     constexpr int HROWS = 32 * KH;
     constexpr int H = (HROWS + kChunk - 1) / kChunk;      // history chunks
-    constexpr int RING = H + 1;                           // x chunks resident
-    constexpr int NZ = DKV ? RING : 1;                    // dz chunks resident
+    constexpr int RING = H + 1;                           // ring A chunks resident
+    constexpr int NZ = DKV ? RING : 1;                    // ring B chunks resident
     constexpr int FH = DKV ? H : 0;                       // chunks walked past the span
     constexpr int NDL = 2 * KH + 1;                       // diagonals (16-row units)
     constexpr int NH = HROWS / M::ROWS;                   // history fragments
@@ -769,13 +774,13 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
     static_assert(!DKV || kWaves * kHLen * 4 <= kChunk * ST_PITCH, "taps fit the second staging tile");
 
     __shared__ __attribute__((aligned(16))) unsigned char lds[WALK_B > LAG_B ? WALK_B : LAG_B];
-    // chunk c's x and dz tiles (x from chunk -H, dz from chunk 0)
+    // chunk c's tiles in ring A (from chunk -H) and ring B (from chunk 0)
     auto xr = [&](int c) -> unsigned char * { return lds + ((c + H + 4 * RING) % RING) * TILE_B; };
     auto zr = [&](int c) -> unsigned char * {
         return lds + (RING + (DKV ? (c + H + 4 * RING) % RING : 0)) * TILE_B;
     };
     unsigned char *const st = lds + (RING + NZ) * TILE_B;
-    unsigned char *const st2 = st + (NST - 1) * kChunk * ST_PITCH;  // (DKV) dx staging
+    unsigned char *const st2 = st + (NST - 1) * kChunk * ST_PITCH;  // (DKV) dq staging
     float *hsw;  // this wave's kHLen staged taps
     if constexpr (DKV) {
         hsw = (float *)st2 + (threadIdx.x >> 6) * kHLen;
@@ -801,21 +806,24 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
     const int64_t base_row = max((int64_t)0, t_begin - HROWS);
     const int c_begin = slab * kSlab;
     const int row_bytes = p.D * T::EB;
-    const size_t base_off = ((size_t)b * (size_t)p.L + (size_t)base_row) * (size_t)row_bytes +
-                            (size_t)c_begin * T::EB;
-    const uint32_t nrec = (uint32_t)((t_stop - base_row) * row_bytes - c_begin * T::EB);
-    // q and dy: also the FH chunks past the span (the host keeps that window
-    // below 2^31 bytes too)
+    // Ring B's tensors are read FH chunks past the span too (the host keeps
+    // that window below 2^31 bytes).  DKV: walk row tau is physical row
+    // L - 1 - tau, and one window holds walk rows base_row .. t_fut - 1 at
+    // physical rows L - t_fut .. L - 1 - base_row for every tensor.
     const int64_t t_fut = min(p.L, t_stop + (int64_t)FH * kChunk);
+    const size_t base_off = ((size_t)b * (size_t)p.L + (size_t)(DKV ? p.L - t_fut : base_row)) * (size_t)row_bytes +
+                            (size_t)c_begin * T::EB;
     const uint32_t nrec_z = (uint32_t)((t_fut - base_row) * row_bytes - c_begin * T::EB);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + base_off, nrec_z);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + base_off, nrec);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + base_off, nrec);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.dy + base_off, nrec_z);
+    const uint32_t nrec = DKV ? nrec_z : (uint32_t)((t_stop - base_row) * row_bytes - c_begin * T::EB);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + base_off, DKV ? nrec : nrec_z);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + base_off, DKV ? nrec_z : nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + base_off, DKV ? nrec_z : nrec);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.dy + base_off, DKV ? nrec : nrec_z);
     const __amdgpu_buffer_rsrc_t rdq = make_rsrc((char *)p.dq + base_off, nrec);
     const __amdgpu_buffer_rsrc_t rdk = make_rsrc((char *)(DKV ? p.dk : p.dq) + base_off, nrec);
     const __amdgpu_buffer_rsrc_t rdv = make_rsrc((char *)(DKV ? p.dv : p.dq) + base_off, nrec);
     const int row0 = (int)(t_begin - base_row);
+    const int rowf = (int)(t_fut - 1 - t_begin);  // (DKV) offset rows of walk row t_begin
 
     // ---- stage this wave's filter (zero outside [0, l_h)) -----------------
     const bool tile_ok = c_begin + w * kTile < p.D;
@@ -832,9 +840,13 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
     const int ld_row = tid / T::TPR;
     const int ld_seg = tid % T::TPR;
     const bool seg_ok = c_begin + ld_seg * T::VEC < p.D;
-    const int ld_base = ld_row * row_bytes + ld_seg * 16;
+    const int ld_base = DKV ? ld_seg * 16 - ld_row * row_bytes : ld_row * row_bytes + ld_seg * 16;
+    // byte offset of this thread's row i of chunk c (DKV: counted backwards
+    // from the window's last row; a walk row past the window's last comes
+    // out negative, past every range)
     auto off = [&](int c, int i, bool need) -> uint32_t {
-        const int r = (row0 + c * kChunk + i * T::RPL) * row_bytes + ld_base;
+        const int r = DKV ? (rowf - c * kChunk - i * T::RPL) * row_bytes + ld_base
+                           : (row0 + c * kChunk + i * T::RPL) * row_bytes + ld_base;
         return (seg_ok && need) ? (uint32_t)r : kOOB;
     };
     // Swizzle of the row-major tiles (LDS of 32 four-byte banks, 128 bytes
@@ -851,24 +863,30 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
                (byte & 7);
     };
 
-    u32x4_t kr[PF][T::NLD], vr[PF][T::NLD], qr[PF][T::NLD], dr[PF][T::NLD];
-    // DKV reads k and v again FH chunks later, as the dk, dv gates: these
-    // first reads allocate in L2 so that the second mostly hits (measured:
-    // 131 -> 100 us for the SE backward, 137 -> 116 us for MR, with
-    // streaming first reads)
-    constexpr int kKvPolicy = DKV ? 0 : kLoadPolicy;
-    // chunks -H .. S-1+FH in order; history chunks need no q, dy, and the
-    // chunks past the span no k, v
+    // Ring A (xr) holds the operand of the products that complete at each
+    // chunk, ring B (zr) that of the products that complete FH chunks later:
+    // x = k v and dz = dy q in time order (dq with dh), dz and x walked
+    // backwards (DKV).  The gate of DKV's late product, dy, is read again
+    // then: its first read allocates in L2 so that the second mostly hits.
+    // (With dk and dv late instead, walking in time order, allocating first
+    // reads of k and v took the call from 131 to 100 us for SE and 137 to
+    // 116 us for MR; walking backwards, MR takes 112-117 us.)
+    const __amdgpu_buffer_rsrc_t rA1 = DKV ? rd : rk, rA2 = DKV ? rq : rv;
+    const __amdgpu_buffer_rsrc_t rB1 = DKV ? rk : rd, rB2 = DKV ? rv : rq;
+    constexpr int kPolA1 = DKV ? 0 : kLoadPolicy;  // k, or (DKV) dy
+    u32x4_t a1r[PF][T::NLD], a2r[PF][T::NLD], b1r[PF][T::NLD], b2r[PF][T::NLD];
+    // chunks -H .. S-1+FH in walk order; ring A needs chunks -H .. S-1 and
+    // ring B chunks 0 .. S-1+FH
     auto load = [&](int c, int slot) {
         const bool need = c < S;
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
             const uint32_t o = off(c, i, need);
             const uint32_t og = off(c, i, c >= 0 && c < S + FH);
-            kr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kKvPolicy));
-            vr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kKvPolicy));
-            qr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, og, 0, kLoadPolicy));
-            dr[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rd, og, 0, kLoadPolicy));
+            a1r[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA1, o, 0, kPolA1));
+            a2r[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rA2, o, 0, kLoadPolicy));
+            b2r[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB2, og, 0, kLoadPolicy));
+            b1r[slot][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB1, og, 0, kLoadPolicy));
         }
     };
     // elementwise product of two 16-byte vectors, rounded to bf16 -> LDS tile
@@ -886,6 +904,22 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
         }
     };
     auto st_addr = [&](int row, int seg) -> int { return row * ST_PITCH + ((seg ^ (row & 15)) << 4); };
+    // y = gate * (staged fp32 accumulators) for this thread's rows of chunk
+    // c, rounded to bf16 -> out
+    auto gate_store = [&](const unsigned char *tile, const u32x4_t *g, const __amdgpu_buffer_rsrc_t &out, int c) {
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const int row = i * T::RPL + ld_row;
+            const f32x4_t a0 = *(const f32x4_t *)(&tile[st_addr(row, 2 * ld_seg)]);
+            const f32x4_t a1 = *(const f32x4_t *)(&tile[st_addr(row, 2 * ld_seg + 1)]);
+            u32x4_t yv;
+            yv[0] = pack_bf16(bf_lo(g[i][0]) * a0[0], bf_hi(g[i][0]) * a0[1]);
+            yv[1] = pack_bf16(bf_lo(g[i][1]) * a0[2], bf_hi(g[i][1]) * a0[3]);
+            yv[2] = pack_bf16(bf_lo(g[i][2]) * a1[0], bf_hi(g[i][2]) * a1[1]);
+            yv[3] = pack_bf16(bf_lo(g[i][3]) * a1[2], bf_hi(g[i][3]) * a1[3]);
+            __builtin_amdgcn_raw_buffer_store_b128(yv, out, off(c, i, true), 0, kStorePolicy);
+        }
+    };
 
 #pragma unroll
     for (int s = 0; s < PF; ++s) load(-H + s, s);
@@ -933,27 +967,30 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
 
     auto chunk_step = [&](const int c) {
         const int slot = (c + H) % PF;
-        const bool own = c >= 0 && c < S;  // a span chunk: dq and the dh products
-        const int cg = c - FH;             // the chunk whose dk, dv complete here
+        const bool own = c >= 0 && c < S;  // a span chunk: its own products and the dh products
+        const int cg = c - FH;             // the chunk whose late products complete here
         unsigned char *xt = xr(c);
-        if (c < S) put(xt, kr[slot], vr[slot]);
-        u32x4_t dyc[T::NLD];
+        if (c < S) put(xt, a1r[slot], a2r[slot]);
+        // gates of chunk c's own products: dy, or (DKV) k and v
+        u32x4_t g1c[T::NLD], g2c[DKV ? T::NLD : 1];
         if (c >= 0) {
-            put(zr(c), dr[slot], qr[slot]);
+            put(zr(c), b1r[slot], b2r[slot]);
             if (own) {
 #pragma unroll
-                for (int i = 0; i < T::NLD; ++i) dyc[i] = dr[slot][i];
+                for (int i = 0; i < T::NLD; ++i) g1c[i] = b1r[slot][i];
+                if constexpr (DKV) {
+#pragma unroll
+                    for (int i = 0; i < T::NLD; ++i) g2c[i] = b2r[slot][i];
+                }
             }
         }
-        // the gates of chunk cg, read again (L2 hits for the most part)
-        u32x4_t kg[DKV ? T::NLD : 1], vg[DKV ? T::NLD : 1];
+        // (DKV) dy of chunk cg, dq's gate, read again (L2 hits for the most part)
+        u32x4_t dyg[DKV ? T::NLD : 1];
         if constexpr (DKV) {
             if (cg >= 0) {
 #pragma unroll
-                for (int i = 0; i < T::NLD; ++i) {
-                    kg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, off(cg, i, true), 0, kLoadPolicy));
-                    vg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, off(cg, i, true), 0, kLoadPolicy));
-                }
+                for (int i = 0; i < T::NLD; ++i)
+                    dyg[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rd, off(cg, i, true), 0, kLoadPolicy));
             }
         }
         load(c + PF, slot);
@@ -962,13 +999,16 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
             if (c < S) read_frags(xt, &X[NH]);
         }
         if (own) {
-            const unsigned char *dzs = zr(c);
-            // filter gradient: P[d] += dz rows (16 a + n16) . x rows 16 (a - d) + n16
+            const unsigned char *bt_c = zr(c);
+            // filter gradient: P[d] += ring B rows (16 a + n16) . ring A rows
+            // 16 (a - d) + n16 of this and the previous chunks: dz with x
+            // before it in time, or (DKV) x with dz before it in the walk,
+            // the same lag either way
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const int ra = 16 * a + n16;
                 typedef short s16x4_t __attribute__((ext_vector_type(4)));
-                const s16x4_t av = *(const s16x4_t *)(&dzs[lds_addr(ra, kbyte)]);
+                const s16x4_t av = *(const s16x4_t *)(&bt_c[lds_addr(ra, kbyte)]);
 #pragma unroll
                 for (int d = 0; d < NDL; ++d) {
                     const int bt = a - d;
@@ -979,7 +1019,8 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
                     P[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, P[d], 0, 0, 0);
                 }
             }
-            // dq: the convolved chunk, 16 output rows per tile nt
+            // the causal product over ring A for chunk c (dq, or (DKV) dx),
+            // 16 output rows per tile nt
             if constexpr (DKV) {
                 // input step kappa = kk - NH: 32-row block kappa from the
                 // chunk's start (chunk c + floor(kappa / 2), half kappa & 1)
@@ -1016,10 +1057,10 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
                 }
             }
         }
-        // dx of chunk cg, backwards in time, -> st2: output tile nt holds rows
-        // 63 - 16 nt - n16; input step kappa = kk - NH covers the 32-row
-        // block b = 1 - kappa counted from the chunk's start (chunk cg + b / 2,
-        // half b % 2), its rows in reverse
+        // (DKV) the product over ring B against the walk, dq of chunk cg, ->
+        // st2: output tile nt holds rows 63 - 16 nt - n16; input step kappa =
+        // kk - NH covers the 32-row block b = 1 - kappa counted from the
+        // chunk's start (chunk cg + b / 2, half b % 2), its rows in reverse
         if constexpr (DKV) {
             if (cg >= 0) {
                 f32x4_t ga[4];
@@ -1043,42 +1084,17 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
                 for (int nt = 0; nt < 4; ++nt) *(f32x4_t *)(&st2[st_addr(63 - 16 * nt - n16, 4 * w + q4)]) = ga[nt];
             }
         }
-        __syncthreads();  // st, st2 complete; every read of the oldest x and dz chunks done
+        __syncthreads();  // st, st2 complete; every read of the oldest ring chunks done
         if (own) {
-#pragma unroll
-            for (int i = 0; i < T::NLD; ++i) {
-                const int row = i * T::RPL + ld_row;
-                const f32x4_t a0 = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg)]);
-                const f32x4_t a1 = *(const f32x4_t *)(&st[st_addr(row, 2 * ld_seg + 1)]);
-                const u32x4_t g = dyc[i];
-                u32x4_t yv;
-                yv[0] = pack_bf16(bf_lo(g[0]) * a0[0], bf_hi(g[0]) * a0[1]);
-                yv[1] = pack_bf16(bf_lo(g[1]) * a0[2], bf_hi(g[1]) * a0[3]);
-                yv[2] = pack_bf16(bf_lo(g[2]) * a1[0], bf_hi(g[2]) * a1[1]);
-                yv[3] = pack_bf16(bf_lo(g[3]) * a1[2], bf_hi(g[3]) * a1[3]);
-                __builtin_amdgcn_raw_buffer_store_b128(yv, rdq, off(c, i, true), 0, kStorePolicy);
+            if constexpr (DKV) {
+                gate_store(st, g2c, rdk, c);  // dk = v dx
+                gate_store(st, g1c, rdv, c);  // dv = k dx
+            } else {
+                gate_store(st, g1c, rdq, c);  // dq = dy (h * x)
             }
         }
         if constexpr (DKV) {
-            if (cg >= 0) {
-#pragma unroll
-                for (int i = 0; i < T::NLD; ++i) {
-                    const int row = i * T::RPL + ld_row;
-                    const f32x4_t a0 = *(const f32x4_t *)(&st2[st_addr(row, 2 * ld_seg)]);
-                    const f32x4_t a1 = *(const f32x4_t *)(&st2[st_addr(row, 2 * ld_seg + 1)]);
-                    u32x4_t yk, yv2;
-                    yk[0] = pack_bf16(bf_lo(vg[i][0]) * a0[0], bf_hi(vg[i][0]) * a0[1]);
-                    yk[1] = pack_bf16(bf_lo(vg[i][1]) * a0[2], bf_hi(vg[i][1]) * a0[3]);
-                    yk[2] = pack_bf16(bf_lo(vg[i][2]) * a1[0], bf_hi(vg[i][2]) * a1[1]);
-                    yk[3] = pack_bf16(bf_lo(vg[i][3]) * a1[2], bf_hi(vg[i][3]) * a1[3]);
-                    yv2[0] = pack_bf16(bf_lo(kg[i][0]) * a0[0], bf_hi(kg[i][0]) * a0[1]);
-                    yv2[1] = pack_bf16(bf_lo(kg[i][1]) * a0[2], bf_hi(kg[i][1]) * a0[3]);
-                    yv2[2] = pack_bf16(bf_lo(kg[i][2]) * a1[0], bf_hi(kg[i][2]) * a1[1]);
-                    yv2[3] = pack_bf16(bf_lo(kg[i][3]) * a1[2], bf_hi(kg[i][3]) * a1[3]);
-                    __builtin_amdgcn_raw_buffer_store_b128(yk, rdk, off(cg, i, true), 0, kStorePolicy);
-                    __builtin_amdgcn_raw_buffer_store_b128(yv2, rdv, off(cg, i, true), 0, kStorePolicy);
-                }
-            }
+            if (cg >= 0) gate_store(st2, dyg, rdq, cg);  // dq = dy (h * x)
         }
         // the next chunk writes st and st2 only after its first barrier
         if constexpr (!DKV) {

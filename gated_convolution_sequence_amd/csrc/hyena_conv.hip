@@ -99,6 +99,7 @@ struct Params {
     int32_t n_slabs;    // channel slabs
     int32_t P;          // prefix rows in kp / vp (0: the history before row 0 is zero)
     int32_t span_blocks; // chunk-direction kernel: 256-row blocks per span
+    int32_t span_rows;  // short-filter direct kernel: rows per span
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -1523,6 +1524,147 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Short filters without the 16-channel grouping (page "04. hardware-aware
+// convolution kernels", section 6 gives the chunk-direction GEMM for this
+// case; for a few taps the plain sum is cheaper).  With l_h <= 8 taps a
+// channel's output needs 8 multiply-adds, far below the fp32 vector ridge, so
+// each lane computes the definition directly for 4 channels of one
+// row-major segment: x = k v of the last LH rows in registers (fp32, exact
+// for bf16 inputs), the channels' taps in registers, y = q * sum_s h[s]
+// x[t - s] in fp32, rounded once.  Every access is a coalesced row segment
+// (a wave covers 256 consecutive channels) and nothing is transposed, so the
+// kernel streams q, k, v and y at the rate of a plain elementwise kernel.
+// A wave walks one span of rows after reading the LH - 1 rows before it;
+// rows are loaded four at a time, the next four while these are computed.
+// Each output's sum runs over s = LH - 1 .. 0 whatever the span, so spans
+// give the same bits.
+// ---------------------------------------------------------------------------
+constexpr int kDirTaps = 8;                // longest filter of the direct kernel
+constexpr int kDirCh = 4;                  // channels per lane
+constexpr int kDirSlab = 64 * kDirCh;      // channels per wave (one workgroup)
+constexpr int kDirBatch = 4;               // rows per load batch
+
+template <bool F32, int LH>
+__global__ __launch_bounds__(64) void hyena_fwd_direct_kernel(Params p) {
+    constexpr int EB = F32 ? 4 : 2;
+    const int lane = threadIdx.x;
+    int bid = blockIdx.x;
+    const int slab = bid % p.n_slabs;
+    bid /= p.n_slabs;
+    const int spn = bid % p.n_spans;
+    const int b = bid / p.n_spans;
+    const int c0 = slab * kDirSlab + lane * kDirCh;
+    const bool ok = c0 < p.D;  // D % 4 == 0: the lane's 4 channels are all in range
+    const int64_t t0 = (int64_t)spn * p.span_rows;
+    const int64_t t1 = min(p.L, t0 + (int64_t)p.span_rows);
+    const int64_t r_lo = max((int64_t)0, t0 - (LH - 1));
+    const int row_bytes = p.D * EB;
+    // window: rows r_lo .. t1 - 1 of batch row b (the host keeps it below 2^31 bytes)
+    const size_t base = ((size_t)b * (size_t)p.L + (size_t)r_lo) * (size_t)row_bytes;
+    const uint32_t nrec = (uint32_t)((t1 - r_lo) * row_bytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + base, nrec);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + base, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + base, nrec);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc((char *)p.y + base, nrec);
+    const int rel0 = (int)(t0 - r_lo), nrows = (int)(t1 - t0);
+    // byte offset of span row i (i >= -(LH - 1)); rows past the span: out of range
+    auto off = [&](int i) -> uint32_t {
+        return (ok && i < nrows) ? (uint32_t)((rel0 + i) * row_bytes + c0 * EB) : kOOB;
+    };
+    typedef typename std::conditional<F32, u32x4_t, u32x2_t>::type seg_t;
+    // streaming loads; the history rows (read by the previous span too) with
+    // the default, L2-allocating policy
+    auto load = [&](const __amdgpu_buffer_rsrc_t &r, uint32_t o) -> seg_t {
+        if constexpr (F32)
+            return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, kLoadPolicy));
+        else
+            return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, kLoadPolicy));
+    };
+    auto load_keep = [&](const __amdgpu_buffer_rsrc_t &r, uint32_t o) -> seg_t {
+        if constexpr (F32)
+            return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+        else
+            return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0));
+    };
+    auto elem = [](const seg_t &a, int c) -> float {
+        if constexpr (F32) return __uint_as_float(a[c]);
+        else return (c & 1) ? bf_hi(a[c >> 1]) : bf_lo(a[c >> 1]);
+    };
+
+    // taps of the lane's channels (zero past l_h)
+    float hv[kDirCh][LH];
+#pragma unroll
+    for (int c = 0; c < kDirCh; ++c) {
+        const size_t hrow = ok ? (size_t)((c0 + c) / p.group_size) * p.l_h : 0;
+#pragma unroll
+        for (int s = 0; s < LH; ++s) {
+            float t = 0.0f;
+            if (ok && s < p.l_h) t = F32 ? ((const float *)p.h)[hrow + s] : bf_lo(((const uint16_t *)p.h)[hrow + s]);
+            hv[c][s] = t;
+        }
+    }
+    // xw[s][c] = x of row t - s while row t is computed; before the first
+    // row, row -j sits in xw[j - 1] (the first row's shift moves it to xw[j])
+    float xw[LH][kDirCh];
+#pragma unroll
+    for (int s = 0; s < LH; ++s)
+#pragma unroll
+        for (int c = 0; c < kDirCh; ++c) xw[s][c] = 0.0f;
+#pragma unroll
+    for (int j = 1; j < LH; ++j) {
+        if (t0 - j >= 0) {
+            const seg_t kk = load_keep(rk, off(-j)), vv = load_keep(rv, off(-j));
+#pragma unroll
+            for (int c = 0; c < kDirCh; ++c) xw[j - 1][c] = elem(kk, c) * elem(vv, c);
+        }
+    }
+    seg_t kb[2][kDirBatch], vb[2][kDirBatch], qb[2][kDirBatch];
+    auto load_batch = [&](int i0, int sl) {
+#pragma unroll
+        for (int u = 0; u < kDirBatch; ++u) {
+            const uint32_t o = off(i0 + u);
+            kb[sl][u] = load(rk, o);
+            vb[sl][u] = load(rv, o);
+            qb[sl][u] = load(rq, o);
+        }
+    };
+    load_batch(0, 0);
+    for (int i = 0; i < nrows; i += 2 * kDirBatch) {
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const int ib = i + sl * kDirBatch;
+            load_batch(ib + kDirBatch, sl ^ 1);
+#pragma unroll
+            for (int u = 0; u < kDirBatch; ++u) {
+#pragma unroll
+                for (int s = LH - 1; s > 0; --s)
+#pragma unroll
+                    for (int c = 0; c < kDirCh; ++c) xw[s][c] = xw[s - 1][c];
+                float yv[kDirCh];
+#pragma unroll
+                for (int c = 0; c < kDirCh; ++c) {
+                    xw[0][c] = elem(kb[sl][u], c) * elem(vb[sl][u], c);
+                    float a = 0.0f;
+#pragma unroll
+                    for (int s = LH - 1; s >= 0; --s) a = __builtin_fmaf(hv[c][s], xw[s][c], a);
+                    yv[c] = elem(qb[sl][u], c) * a;
+                }
+                seg_t out;
+                if constexpr (F32) {
+#pragma unroll
+                    for (int c = 0; c < kDirCh; ++c) out[c] = __float_as_uint(yv[c]);
+                    __builtin_amdgcn_raw_buffer_store_b128(out, ry, off(ib + u), 0, kStorePolicy);
+                } else {
+                    out[0] = pack_bf16(yv[0], yv[1]);
+                    out[1] = pack_bf16(yv[2], yv[3]);
+                    __builtin_amdgcn_raw_buffer_store_b64(out, ry, off(ib + u), 0, kStorePolicy);
+                }
+            }
+        }
+    }
+}
+
 // Kernel families and their compiled span counts (indices into kSpans).
 enum Family { kFwd = 0, kRevDual = 1, kDh = 2, kCd = 3, kDqDh = 4, kBwd = 5 };
 // (the chunk-direction kernel takes its span at run time: one entry)
@@ -1660,6 +1802,48 @@ int cd_plan(int64_t B, int64_t L, int64_t D, int64_t l_h, int dtype, int64_t spa
     return HYENA_OK;
 }
 
+// Plan of the short-filter direct kernel (group sizes off the 16-channel
+// tile, l_h <= kDirTaps).  One wave per 256-channel slab and span of rows;
+// spans of 256 rows, halved down to 64 while that leaves fewer than 1024
+// workgroups (four waves per CU) or a byte window (span + 8 rows) of 2^31
+// or more, or span_req chunks.  `kh` holds the compiled tap count (1, 2, 4 or
+// 8) and `span` the span in 64-row chunks.
+constexpr int64_t kDirWorkgroups = 1024;
+
+int dir_plan(int64_t B, int64_t L, int64_t D, int64_t l_h, int dtype, int64_t span_req, Plan *pl) {
+    const int64_t eb = dtype == HYENA_DTYPE_F32 ? 4 : 2;
+    if ((D * eb) % 16 != 0) return HYENA_ERR_UNSUPPORTED;  // same row rule as the chunk-direction kernel
+    if (D > INT32_MAX / 16) return HYENA_ERR_UNSUPPORTED;
+    pl->kh = l_h <= 1 ? 1 : l_h <= 2 ? 2 : l_h <= 4 ? 4 : 8;
+    pl->n_chunks = (L + kChunk - 1) / kChunk;
+    pl->n_slabs = (D + kDirSlab - 1) / kDirSlab;
+    int64_t rows;
+    if (span_req > 0) {
+        rows = min(span_req, pl->n_chunks) * kChunk;
+    } else {
+        rows = 256;
+        while (rows > kChunk && (B * pl->n_slabs * ((L + rows - 1) / rows) < kDirWorkgroups ||
+                                 (rows + kDirTaps) * D * eb >= kMaxWindowBytes))
+            rows /= 2;
+    }
+    if ((rows + kDirTaps) * D * eb >= kMaxWindowBytes) return HYENA_ERR_UNSUPPORTED;
+    pl->span_index = 0;
+    pl->span = rows / kChunk;
+    pl->n_spans = (L + rows - 1) / rows;
+    pl->workgroups = pl->n_spans * pl->n_slabs * B;
+    if (pl->workgroups > INT32_MAX || pl->n_spans > INT32_MAX) return HYENA_ERR_UNSUPPORTED;
+    return HYENA_OK;
+}
+
+template <bool F32> KernelFn pick_direct(int lh) {
+    switch (lh) {
+    case 1: return hyena_fwd_direct_kernel<F32, 1>;
+    case 2: return hyena_fwd_direct_kernel<F32, 2>;
+    case 4: return hyena_fwd_direct_kernel<F32, 4>;
+    default: return hyena_fwd_direct_kernel<F32, 8>;
+    }
+}
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
@@ -1679,8 +1863,9 @@ int hyena_conv_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t
         return HYENA_OK;
     }
     Plan pl;
-    st = group_size % kTile != 0 ? cd_plan(B, L, D, l_h, dtype, span_chunks, &pl)
-                                 : make_plan(B, L, D, group_size, l_h, dtype, span_chunks, &pl);
+    st = group_size % kTile == 0 ? make_plan(B, L, D, group_size, l_h, dtype, span_chunks, &pl)
+         : l_h <= kDirTaps       ? dir_plan(B, L, D, l_h, dtype, span_chunks, &pl)
+                                 : cd_plan(B, L, D, l_h, dtype, span_chunks, &pl);
     if (st != HYENA_OK) return st;
     if (span_out) *span_out = pl.span;
     if (workgroups_out) *workgroups_out = pl.workgroups;
@@ -1714,9 +1899,13 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
     }
     const bool chunk_dir = group_size % kTile != 0;
     if (chunk_dir && P > 0) return HYENA_ERR_UNSUPPORTED;  // history prefix: grouped path only
+    // off the 16-channel tile: a few taps are summed directly, longer
+    // filters take the chunk-direction GEMMs
+    const bool direct = chunk_dir && l_h <= kDirTaps;
     Plan pl;
-    st = chunk_dir ? cd_plan(B, L, D, l_h, dtype, span_chunks, &pl)
-                   : make_plan(B, L, D, group_size, l_h, dtype, span_chunks, &pl);
+    st = direct      ? dir_plan(B, L, D, l_h, dtype, span_chunks, &pl)
+         : chunk_dir ? cd_plan(B, L, D, l_h, dtype, span_chunks, &pl)
+                     : make_plan(B, L, D, group_size, l_h, dtype, span_chunks, &pl);
     if (st != HYENA_OK) return st;
 
     Params p;
@@ -1731,14 +1920,16 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
     p.n_slabs = (int32_t)pl.n_slabs;
     p.P = (int32_t)P;
     p.span_blocks = (int32_t)(pl.span / (kCdBlock / kChunk));
+    p.span_rows = (int32_t)(pl.span * kChunk);
     p.g2 = nullptr;
     p.y2 = nullptr;
     const bool f32 = dtype == HYENA_DTYPE_F32;
-    KernelFn fn = chunk_dir ? (f32 ? pick_kernel<true, kCd>(pl.kh, pl.span_index)
-                                   : pick_kernel<false, kCd>(pl.kh, pl.span_index))
-                            : (f32 ? pick_kernel<true, kFwd>(pl.kh, pl.span_index)
-                                   : pick_kernel<false, kFwd>(pl.kh, pl.span_index));
-    hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(chunk_dir ? kCdThreads : kThreads), 0,
+    KernelFn fn = direct      ? (f32 ? pick_direct<true>(pl.kh) : pick_direct<false>(pl.kh))
+                  : chunk_dir ? (f32 ? pick_kernel<true, kCd>(pl.kh, pl.span_index)
+                                     : pick_kernel<false, kCd>(pl.kh, pl.span_index))
+                              : (f32 ? pick_kernel<true, kFwd>(pl.kh, pl.span_index)
+                                     : pick_kernel<false, kFwd>(pl.kh, pl.span_index));
+    hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(direct ? 64 : chunk_dir ? kCdThreads : kThreads), 0,
                        (hipStream_t)stream, p);
     if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
     return HYENA_OK;
@@ -1849,7 +2040,7 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
         Params p;
         p.q = v; p.k = dy; p.v = q; p.h = h; p.y = dk;
         p.g2 = k; p.y2 = dv;
-        p.kp = nullptr; p.vp = nullptr; p.P = 0; p.span_blocks = 0;
+        p.kp = nullptr; p.vp = nullptr; p.P = 0; p.span_blocks = 0; p.span_rows = 0;
         p.L = L;
         p.D = (int32_t)D;
         p.group_size = (int32_t)group_size;

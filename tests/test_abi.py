@@ -110,13 +110,12 @@ def test_plan_split(B, L, D, l_h, dtype, span, expect_span):
 
 
 @pytest.mark.parametrize("B,L,D,gs,l_h,dtype,span,expect_span", [
-    # group sizes off the 16-channel tile: spans of whole 256-row blocks (4
-    # chunks each), by default long enough for about one workgroup per CU
-    (1, 8192, 4096, 1, 7, 0, 0, 32), (1, 8192, 4096, 1, 128, 0, 0, 32),
-    (1, 8192, 4096, 8, 33, 1, 0, 64), (4, 32768, 4096, 2, 128, 0, 0, 512),
-    (2, 1000, 96, 3, 7, 1, 3, 4), (1, 1000, 64, 1, 7, 0, 9, 12), (1, 100, 64, 1, 128, 0, 0, 4),
-    (1, 1000, 72, 24, 65, 0, 0, 4), (1, 1 << 20, 4096, 2, 2, 0, 1000, 1000),
-    (1, 1 << 20, 4096, 1, 128, 0, 0, 4096), (1, 3000, 64, 1, 7, 0, 10 ** 6, 48),
+    # group sizes off the 16-channel tile, filters longer than 8 taps (the
+    # chunk-direction GEMMs): spans of whole 256-row blocks (4 chunks each), by
+    # default long enough for about one workgroup per CU
+    (1, 8192, 4096, 1, 128, 0, 0, 32), (1, 8192, 4096, 8, 33, 1, 0, 64), (4, 32768, 4096, 2, 128, 0, 0, 512),
+    (1, 100, 64, 1, 128, 0, 0, 4), (1, 1000, 72, 24, 65, 0, 0, 4), (1, 1 << 20, 4096, 1, 128, 0, 0, 4096),
+    (1, 1000, 64, 1, 9, 0, 9, 12), (2, 1000, 96, 3, 9, 1, 3, 4),
 ])
 def test_plan_split_chunk_direction(B, L, D, gs, l_h, dtype, span, expect_span):
     s, wgs = hc.plan(B, L, D, gs, l_h, dtype, span)
@@ -126,13 +125,39 @@ def test_plan_split_chunk_direction(B, L, D, gs, l_h, dtype, span, expect_span):
     assert wgs == B * (-(-D // slab)) * (-(-blocks // (s // 4)))
 
 
+@pytest.mark.parametrize("B,L,D,gs,l_h,dtype,span,expect_span", [
+    # off the tile with at most 8 taps (the direct kernel): one 64-lane
+    # workgroup per 256 channels and span; spans of 256 rows halved (down to
+    # 64) while there are fewer than 1024 workgroups, or the requested chunks
+    # (at most the sequence)
+    (1, 8192, 4096, 1, 7, 0, 0, 2), (1, 8192, 4096, 1, 8, 1, 0, 2), (4, 32768, 4096, 2, 4, 0, 0, 4),
+    (1, 100, 64, 1, 7, 0, 0, 1), (1, 1 << 20, 4096, 2, 1, 0, 0, 4),
+    (2, 1000, 96, 3, 7, 1, 3, 3), (1, 1000, 64, 1, 7, 0, 9, 9), (1, 1 << 20, 4096, 2, 2, 0, 1000, 1000),
+    (1, 3000, 64, 1, 7, 0, 10 ** 6, 47),
+])
+def test_plan_split_direct(B, L, D, gs, l_h, dtype, span, expect_span):
+    s, wgs = hc.plan(B, L, D, gs, l_h, dtype, span)
+    assert s == expect_span
+    assert wgs == B * (-(-D // 256)) * (-(-L // (64 * s)))
+
+
 def test_plan_chunk_direction_window():
     # buffer windows are per block: any span length; only a row of 384
     # rows x D elements must stay below 2^31 bytes
     s, _ = hc.plan(1, 1 << 16, 1 << 20, 1, 128, hc.DTYPE_BF16, 0)
     assert s == (1 << 16) // 64
     with pytest.raises(hc.HyenaError):
-        hc.plan(1, 256, 1 << 22, 2, 7, hc.DTYPE_F32, 0)
+        hc.plan(1, 256, 1 << 22, 2, 65, hc.DTYPE_F32, 0)
+    # the direct kernel's window is a span plus 8 rows: default spans shrink
+    # (down to one chunk) to keep it below 2^31 bytes
+    s, _ = hc.plan(1, 256, 1 << 21, 2, 7, hc.DTYPE_F32, 0)
+    assert s == 2
+    s, _ = hc.plan(1, 256, 1 << 22, 2, 7, hc.DTYPE_F32, 0)
+    assert s == 1
+    with pytest.raises(hc.HyenaError):
+        hc.plan(1, 256, 1 << 24, 2, 7, hc.DTYPE_F32, 0)
+    with pytest.raises(hc.HyenaError):
+        hc.plan(1, 256, 1 << 22, 2, 7, hc.DTYPE_F32, 4)
 
 
 def test_plan_keeps_the_window_addressable():

@@ -1,11 +1,13 @@
-"""GPU parity of the chunk-direction forward (group sizes off the 16-channel tile).
+"""GPU parity of the forward for group sizes off the 16-channel tile.
 
 A group_size that is not a multiple of 16 -- down to one filter per channel
 -- is computed with the sub-chunks of one channel as the matrix-core
-dimension instead of the channels of a group.  These tests run it through
-the same C ABI (hyena_conv_fwd_ex via the binding) and hold it to the same
-bar as the grouped path (tests/gpu_util.py): the gate plus the elementwise
-rounding bound against the fp64 oracle, bitwise on integer inputs.
+dimension instead of the channels of a group (filters longer than 8 taps),
+or by the direct kernel's plain sums (8 taps or fewer).  These tests run
+both through the same C ABI (hyena_conv_fwd_ex via the binding) and hold
+them to the same bar as the grouped path (tests/gpu_util.py): the gate plus
+the elementwise rounding bound against the fp64 oracle, bitwise on integer
+inputs.
 """
 import numpy as np
 import pytest
@@ -138,6 +140,64 @@ def test_one_filter_per_channel_at_full_size(name):
     ref, env = ref_and_envelope(q.cpu(), k.cpu(), v.cpu(), h.cpu(), 1)
     rel = check(to_np(y), ref, env, w.l_h, w.torch_dtype, "cd full " + name)
     log("cd full %s rel err %.3e" % (name, rel))
+
+
+# The direct kernel (l_h <= 8): B, L, D, group_size, l_h, span (chunks of 64).
+# L below the filter, on and across span seams, partial 256-channel slabs,
+# every compiled tap count (1, 2, 4, 8) and the lengths padded up to them.
+DIRECT_EDGE = [
+    (1, 1, 8, 1, 1, 0),
+    (1, 5, 8, 1, 8, 0),
+    (1, 64, 16, 2, 3, 1),
+    (2, 65, 24, 3, 5, 1),
+    (1, 130, 264, 1, 8, 1),
+    (3, 333, 40, 5, 6, 2),
+    (1, 700, 512, 8, 7, 0),
+    (2, 1000, 96, 1, 4, 3),
+    (1, 2047, 256, 2, 2, 0),
+    (1, 4100, 1032, 4, 7, 0),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h,span", DIRECT_EDGE)
+def test_direct_short_filter_edge_shapes_gaussian(dt, B, L, D, gs, l_h, span):
+    log("direct %s B=%d L=%d D=%d gs=%d l_h=%d span=%d" % (dt, B, L, D, gs, l_h, span))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B * 9000 + L + 5 * l_h + gs)
+    y = run(*(t.to(DEV) for t in (q, k, v, h)), gs, span)
+    ref, env = ref_and_envelope(q, k, v, h, gs)
+    check(to_np(y), ref, env, l_h, dtype, "direct edge")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h,span", [(1, 6, 8, 1, 4, 0), (2, 777, 264, 3, 7, 2), (1, 300, 40, 5, 8, 1)])
+def test_direct_short_filter_integer_inputs_bitwise(dt, B, L, D, gs, l_h, span):
+    log("direct integer %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = integer_inputs(B, L, D, gs, l_h, dtype, seed=L + D + gs + 1)
+    y = run(*(t.to(DEV) for t in (q, k, v, h)), gs, span)
+    ref = oracle.conv_fwd_ref(*(to_np(t) for t in (q, k, v, h)), gs)
+    assert np.array_equal(to_np(y), ref)
+
+
+def test_direct_short_filter_span_independent_and_causal():
+    """The direct kernel sums each output over the taps in one fixed order,
+    so any span gives the same bits; changing row t0 changes only rows t0 ..
+    t0 + l_h - 1."""
+    B, L, D, gs, l_h = 2, 3000, 520, 1, 7
+    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(B, L, D, gs, l_h, torch.bfloat16, seed=23))
+    log("direct span independence")
+    y0 = run(q, k, v, h, gs).clone()
+    for span in (1, 2, 3, 5, 1000):
+        assert torch.equal(y0, run(q, k, v, h, gs, span)), span
+    t0 = 767
+    v2 = v.clone()
+    v2[:, t0] += 2.0
+    y1 = run(q, k, v2, h, gs)
+    assert torch.equal(y0[:, :t0], y1[:, :t0])
+    assert torch.equal(y0[:, t0 + l_h:], y1[:, t0 + l_h:])
+    assert not torch.equal(y0[:, t0], y1[:, t0])
 
 
 def test_halo_and_backward_stay_on_the_grouped_path():

@@ -520,7 +520,8 @@ def batched_mr_rate(stream, reps):
 def chunk_direction_rates(layers, sets, stream, reps):
     """Each layer with group_size 1: every channel its own filter (its group's
     taps repeated, so the result is the grouped layer's), which runs the
-    chunk-direction kernel.  Timed back to back on the rotated inputs."""
+    direct kernel (8 taps or fewer) or the chunk-direction kernel.  Timed back
+    to back on the rotated inputs."""
     import torch
     import gated_convolution_sequence_amd as hc
     res = {}
@@ -547,7 +548,8 @@ def chunk_direction_rates(layers, sets, stream, reps):
                                 "G_tok_ch_per_s": round(w.elems / (us * 1e-6) / 1e9, 2),
                                 "achieved_GBs": round(alg / (us * 1e-6) / 1e9, 1),
                                 "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                                "span_chunks": span, "workgroups": wgs}
+                                "span_chunks": span, "workgroups": wgs,
+                                "kernel": ("hyena_fwd_direct_kernel" if w.l_h <= 8 else "hyena_fwd_cd_kernel")}
     return res
 
 

@@ -1,7 +1,8 @@
 // Hyena-SE / Hyena-MR for MI355X (gfx950):
 //     y = q (.) (h * (k (.) v)),  grouped depthwise causal FIR, l_h <= 128,
-// its backward, and the chunk-direction forward for group sizes that are not
-// a multiple of 16.  (Filters of any length: hyena_fft.hip.)
+// its backward, and for group sizes that are not a multiple of 16 the
+// chunk-direction forward (or, for at most 8 taps, the direct forward).
+// (Filters of any length: hyena_fft.hip.)
 //
 // Method (StripedHyena 2 explainer, page "04. hardware-aware convolution
 // kernels"):

@@ -555,7 +555,8 @@ struct DhParams {
     void *dk, *dv;      // dk, dv outputs (the whole-backward form only)
     int64_t L;
     int32_t D, l_h, n_spans, n_slabs;
-    int32_t group_size; // (the fused forms only)
+    int32_t group_size; // (the fused forms and the direct form)
+    int32_t span_rows;  // (the direct form) rows per span
 };
 
 // One chunk of q, k, v and dy in flight per workgroup, and at most 128
@@ -1540,73 +1541,118 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
 // rows are loaded four at a time, the next four while these are computed.
 // Each output's sum runs over s = LH - 1 .. 0 whatever the span, so spans
 // give the same bits.
+//
+// REV walks time backwards (walk row tau is physical row L - 1 - tau), which
+// turns the backward's correlation dx[t] = sum_s h[s] dz[t + s] into the same
+// causal sum; DUAL gates that sum twice (y = q acc and y2 = g2 acc), as dk =
+// v dx and dv = k dx need.  Without REV the rows before row 0 may come from
+// a caller prefix (kp, vp: P rows per batch row).
 // ---------------------------------------------------------------------------
-constexpr int kDirTaps = 8;                // longest filter of the direct kernel
+constexpr int kDirTaps = 8;                // longest filter of the direct kernels
 constexpr int kDirCh = 4;                  // channels per lane
 constexpr int kDirSlab = 64 * kDirCh;      // channels per wave (one workgroup)
 constexpr int kDirBatch = 4;               // rows per load batch
 
-template <bool F32, int LH>
-__global__ __launch_bounds__(64) void hyena_fwd_direct_kernel(Params p) {
-    constexpr int EB = F32 ? 4 : 2;
-    const int lane = threadIdx.x;
-    int bid = blockIdx.x;
-    const int slab = bid % p.n_slabs;
-    bid /= p.n_slabs;
-    const int spn = bid % p.n_spans;
-    const int b = bid / p.n_spans;
-    const int c0 = slab * kDirSlab + lane * kDirCh;
-    const bool ok = c0 < p.D;  // D % 4 == 0: the lane's 4 channels are all in range
-    const int64_t t0 = (int64_t)spn * p.span_rows;
-    const int64_t t1 = min(p.L, t0 + (int64_t)p.span_rows);
-    const int64_t r_lo = max((int64_t)0, t0 - (LH - 1));
-    const int row_bytes = p.D * EB;
-    // window: rows r_lo .. t1 - 1 of batch row b (the host keeps it below 2^31 bytes)
-    const size_t base = ((size_t)b * (size_t)p.L + (size_t)r_lo) * (size_t)row_bytes;
-    const uint32_t nrec = (uint32_t)((t1 - r_lo) * row_bytes);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + base, nrec);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + base, nrec);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + base, nrec);
-    const __amdgpu_buffer_rsrc_t ry = make_rsrc((char *)p.y + base, nrec);
-    const int rel0 = (int)(t0 - r_lo), nrows = (int)(t1 - t0);
-    // byte offset of span row i (i >= -(LH - 1)); rows past the span: out of range
-    auto off = [&](int i) -> uint32_t {
-        return (ok && i < nrows) ? (uint32_t)((rel0 + i) * row_bytes + c0 * EB) : kOOB;
-    };
+// The direct kernels' shared pieces: the work item, the row window and its
+// byte offsets, the segment loads and the taps.
+template <bool F32, int LH, bool REV>
+struct DirWalk {
     typedef typename std::conditional<F32, u32x4_t, u32x2_t>::type seg_t;
-    // streaming loads; the history rows (read by the previous span too) with
-    // the default, L2-allocating policy
-    auto load = [&](const __amdgpu_buffer_rsrc_t &r, uint32_t o) -> seg_t {
+    static constexpr int EB = F32 ? 4 : 2;
+    int b, spn, c0, rel0, nrows, nwin, row_bytes;
+    bool ok;
+    int64_t t0;
+    size_t base;  // byte offset of the window's first physical row in a [B, L, D] tensor
+
+    __device__ DirWalk(int64_t L, int D, int n_slabs, int n_spans, int span_rows) {
+        int bid = blockIdx.x;
+        const int slab = bid % n_slabs;
+        bid /= n_slabs;
+        spn = bid % n_spans;
+        b = bid / n_spans;
+        c0 = slab * kDirSlab + (int)threadIdx.x * kDirCh;
+        ok = c0 < D;  // D % 4 == 0: the lane's 4 channels are all in range
+        t0 = (int64_t)spn * span_rows;
+        const int64_t t1 = min(L, t0 + (int64_t)span_rows);
+        const int64_t r_lo = max((int64_t)0, t0 - (LH - 1));
+        row_bytes = D * EB;
+        rel0 = (int)(t0 - r_lo);
+        nrows = (int)(t1 - t0);
+        nwin = (int)(t1 - r_lo);
+        // walk rows r_lo .. t1 - 1: physical rows r_lo .. t1 - 1, or (REV)
+        // L - t1 .. L - 1 - r_lo in decreasing order (the host keeps the
+        // window below 2^31 bytes)
+        base = ((size_t)b * (size_t)L + (size_t)(REV ? L - t1 : r_lo)) * (size_t)row_bytes;
+    }
+    __device__ uint32_t nrec() const { return (uint32_t)(nwin * row_bytes); }
+    // byte offset of the lane's segment in walk row t0 + i (i >= -(LH - 1));
+    // rows past the span: out of range
+    __device__ uint32_t off(int i) const {
+        const int w = rel0 + i;
+        return (ok && i < nrows) ? (uint32_t)((REV ? nwin - 1 - w : w) * row_bytes + c0 * EB) : kOOB;
+    }
+    template <int POLICY>
+    __device__ static seg_t load(const __amdgpu_buffer_rsrc_t &r, uint32_t o) {
         if constexpr (F32)
-            return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, kLoadPolicy));
+            return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, POLICY));
         else
-            return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, kLoadPolicy));
-    };
-    auto load_keep = [&](const __amdgpu_buffer_rsrc_t &r, uint32_t o) -> seg_t {
+            return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, POLICY));
+    }
+    __device__ static void store(const seg_t &v, const __amdgpu_buffer_rsrc_t &r, uint32_t o) {
         if constexpr (F32)
-            return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, o, 0, kStorePolicy);
         else
-            return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0));
-    };
-    auto elem = [](const seg_t &a, int c) -> float {
+            __builtin_amdgcn_raw_buffer_store_b64(v, r, o, 0, kStorePolicy);
+    }
+    __device__ static float elem(const seg_t &a, int c) {
         if constexpr (F32) return __uint_as_float(a[c]);
         else return (c & 1) ? bf_hi(a[c >> 1]) : bf_lo(a[c >> 1]);
-    };
-
+    }
+    __device__ static seg_t pack(const float *y) {
+        seg_t out;
+        if constexpr (F32) {
+#pragma unroll
+            for (int c = 0; c < kDirCh; ++c) out[c] = __float_as_uint(y[c]);
+        } else {
+            out[0] = pack_bf16(y[0], y[1]);
+            out[1] = pack_bf16(y[2], y[3]);
+        }
+        return out;
+    }
     // taps of the lane's channels (zero past l_h)
-    float hv[kDirCh][LH];
+    __device__ void taps(const void *h, int group_size, int l_h, float (*hv)[LH]) const {
 #pragma unroll
-    for (int c = 0; c < kDirCh; ++c) {
-        const size_t hrow = ok ? (size_t)((c0 + c) / p.group_size) * p.l_h : 0;
+        for (int c = 0; c < kDirCh; ++c) {
+            const size_t hrow = ok ? (size_t)((c0 + c) / group_size) * l_h : 0;
 #pragma unroll
-        for (int s = 0; s < LH; ++s) {
-            float t = 0.0f;
-            if (ok && s < p.l_h) t = F32 ? ((const float *)p.h)[hrow + s] : bf_lo(((const uint16_t *)p.h)[hrow + s]);
-            hv[c][s] = t;
+            for (int s = 0; s < LH; ++s) {
+                float t = 0.0f;
+                if (ok && s < l_h) t = F32 ? ((const float *)h)[hrow + s] : bf_lo(((const uint16_t *)h)[hrow + s]);
+                hv[c][s] = t;
+            }
         }
     }
+};
+
+template <bool F32, int LH, bool REV, bool DUAL>
+__global__ __launch_bounds__(64) void hyena_fwd_direct_kernel(Params p) {
+    using W = DirWalk<F32, LH, REV>;
+    using seg_t = typename W::seg_t;
+    const W wk(p.L, p.D, p.n_slabs, p.n_spans, p.span_rows);
+    const uint32_t nrec = wk.nrec();
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + wk.base, nrec);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + wk.base, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + wk.base, nrec);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc((char *)p.y + wk.base, nrec);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc((const char *)(DUAL ? p.g2 : p.q) + wk.base, nrec);
+    const __amdgpu_buffer_rsrc_t ry2 = make_rsrc((char *)(DUAL ? p.y2 : p.y) + wk.base, nrec);
+
+    float hv[kDirCh][LH];
+    wk.taps(p.h, p.group_size, p.l_h, hv);
     // xw[s][c] = x of row t - s while row t is computed; before the first
-    // row, row -j sits in xw[j - 1] (the first row's shift moves it to xw[j])
+    // row, row -j sits in xw[j - 1] (the first row's shift moves it to xw[j]).
+    // History rows (read by the previous span too) use the default,
+    // L2-allocating policy; rows before row 0 come from the prefix, if any.
     float xw[LH][kDirCh];
 #pragma unroll
     for (int s = 0; s < LH; ++s)
@@ -1614,24 +1660,39 @@ __global__ __launch_bounds__(64) void hyena_fwd_direct_kernel(Params p) {
         for (int c = 0; c < kDirCh; ++c) xw[s][c] = 0.0f;
 #pragma unroll
     for (int j = 1; j < LH; ++j) {
-        if (t0 - j >= 0) {
-            const seg_t kk = load_keep(rk, off(-j)), vv = load_keep(rv, off(-j));
+        seg_t kk, vv;
+        bool have = false;
+        if (wk.t0 - j >= 0) {
+            kk = W::template load<0>(rk, wk.off(-j));
+            vv = W::template load<0>(rv, wk.off(-j));
+            have = true;
+        } else if (!REV && p.P > 0 && p.P + wk.t0 - j >= 0) {
+            const size_t pb = (size_t)wk.b * (size_t)p.P * (size_t)wk.row_bytes;
+            const __amdgpu_buffer_rsrc_t rkp = make_rsrc((const char *)p.kp + pb, (uint32_t)(p.P * wk.row_bytes));
+            const __amdgpu_buffer_rsrc_t rvp = make_rsrc((const char *)p.vp + pb, (uint32_t)(p.P * wk.row_bytes));
+            const uint32_t o = wk.ok ? (uint32_t)((p.P + (int)wk.t0 - j) * wk.row_bytes + wk.c0 * W::EB) : kOOB;
+            kk = W::template load<0>(rkp, o);
+            vv = W::template load<0>(rvp, o);
+            have = true;
+        }
+        if (have) {
 #pragma unroll
-            for (int c = 0; c < kDirCh; ++c) xw[j - 1][c] = elem(kk, c) * elem(vv, c);
+            for (int c = 0; c < kDirCh; ++c) xw[j - 1][c] = W::elem(kk, c) * W::elem(vv, c);
         }
     }
-    seg_t kb[2][kDirBatch], vb[2][kDirBatch], qb[2][kDirBatch];
+    seg_t kb[2][kDirBatch], vb[2][kDirBatch], qb[2][kDirBatch], gb[2][DUAL ? kDirBatch : 1];
     auto load_batch = [&](int i0, int sl) {
 #pragma unroll
         for (int u = 0; u < kDirBatch; ++u) {
-            const uint32_t o = off(i0 + u);
-            kb[sl][u] = load(rk, o);
-            vb[sl][u] = load(rv, o);
-            qb[sl][u] = load(rq, o);
+            const uint32_t o = wk.off(i0 + u);
+            kb[sl][u] = W::template load<kLoadPolicy>(rk, o);
+            vb[sl][u] = W::template load<kLoadPolicy>(rv, o);
+            qb[sl][u] = W::template load<kLoadPolicy>(rq, o);
+            if constexpr (DUAL) gb[sl][u] = W::template load<kLoadPolicy>(rg, o);
         }
     };
     load_batch(0, 0);
-    for (int i = 0; i < nrows; i += 2 * kDirBatch) {
+    for (int i = 0; i < wk.nrows; i += 2 * kDirBatch) {
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {
             const int ib = i + sl * kDirBatch;
@@ -1642,28 +1703,128 @@ __global__ __launch_bounds__(64) void hyena_fwd_direct_kernel(Params p) {
                 for (int s = LH - 1; s > 0; --s)
 #pragma unroll
                     for (int c = 0; c < kDirCh; ++c) xw[s][c] = xw[s - 1][c];
-                float yv[kDirCh];
+                float y1[kDirCh], y2[kDirCh];
 #pragma unroll
                 for (int c = 0; c < kDirCh; ++c) {
-                    xw[0][c] = elem(kb[sl][u], c) * elem(vb[sl][u], c);
+                    xw[0][c] = W::elem(kb[sl][u], c) * W::elem(vb[sl][u], c);
                     float a = 0.0f;
 #pragma unroll
                     for (int s = LH - 1; s >= 0; --s) a = __builtin_fmaf(hv[c][s], xw[s][c], a);
-                    yv[c] = elem(qb[sl][u], c) * a;
+                    y1[c] = W::elem(qb[sl][u], c) * a;
+                    if constexpr (DUAL) y2[c] = W::elem(gb[sl][u], c) * a;
                 }
-                seg_t out;
-                if constexpr (F32) {
-#pragma unroll
-                    for (int c = 0; c < kDirCh; ++c) out[c] = __float_as_uint(yv[c]);
-                    __builtin_amdgcn_raw_buffer_store_b128(out, ry, off(ib + u), 0, kStorePolicy);
-                } else {
-                    out[0] = pack_bf16(yv[0], yv[1]);
-                    out[1] = pack_bf16(yv[2], yv[3]);
-                    __builtin_amdgcn_raw_buffer_store_b64(out, ry, off(ib + u), 0, kStorePolicy);
-                }
+                W::store(W::pack(y1), ry, wk.off(ib + u));
+                if constexpr (DUAL) W::store(W::pack(y2), ry2, wk.off(ib + u));
             }
         }
     }
+}
+
+// dq and the filter gradient's partial sums for short filters off the tile,
+// in one walk in time order: dq = dy * sum_s h[s] x[t - s] as the direct
+// forward with dy as the gate, and for each lane's channel c and tap s the
+// partial sum over the span's rows of dz[t] x[t - s] (dz = dy q in fp32,
+// x = k v from the same register window).  The partial sums go to
+// ws[B * spans][D][l_h]; a reduction adds them per group (pass 2 of page "04.
+// hardware-aware convolution kernels", section 7).
+template <bool F32, int LH>
+__global__ __launch_bounds__(64) void hyena_bwd_direct_dq_dh_kernel(DhParams p) {
+    using W = DirWalk<F32, LH, false>;
+    using seg_t = typename W::seg_t;
+    const W wk(p.L, p.D, p.n_slabs, p.n_spans, p.span_rows);
+    const uint32_t nrec = wk.nrec();
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + wk.base, nrec);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + wk.base, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + wk.base, nrec);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.dy + wk.base, nrec);
+    const bool want_dq = p.dq != nullptr;
+    const __amdgpu_buffer_rsrc_t rdq = make_rsrc((char *)(want_dq ? p.dq : p.ws) + wk.base, want_dq ? nrec : 0u);
+
+    float hv[kDirCh][LH];
+    wk.taps(p.h, p.group_size, p.l_h, hv);
+    float xw[LH][kDirCh];
+#pragma unroll
+    for (int s = 0; s < LH; ++s)
+#pragma unroll
+        for (int c = 0; c < kDirCh; ++c) xw[s][c] = 0.0f;
+#pragma unroll
+    for (int j = 1; j < LH; ++j) {
+        if (wk.t0 - j >= 0) {
+            const seg_t kk = W::template load<0>(rk, wk.off(-j)), vv = W::template load<0>(rv, wk.off(-j));
+#pragma unroll
+            for (int c = 0; c < kDirCh; ++c) xw[j - 1][c] = W::elem(kk, c) * W::elem(vv, c);
+        }
+    }
+    float P[kDirCh][LH];
+#pragma unroll
+    for (int c = 0; c < kDirCh; ++c)
+#pragma unroll
+        for (int s = 0; s < LH; ++s) P[c][s] = 0.0f;
+    seg_t kb[2][kDirBatch], vb[2][kDirBatch], qb[2][kDirBatch], db[2][kDirBatch];
+    auto load_batch = [&](int i0, int sl) {
+#pragma unroll
+        for (int u = 0; u < kDirBatch; ++u) {
+            const uint32_t o = wk.off(i0 + u);
+            kb[sl][u] = W::template load<kLoadPolicy>(rk, o);
+            vb[sl][u] = W::template load<kLoadPolicy>(rv, o);
+            qb[sl][u] = W::template load<kLoadPolicy>(rq, o);
+            db[sl][u] = W::template load<kLoadPolicy>(rd, o);
+        }
+    };
+    load_batch(0, 0);
+    for (int i = 0; i < wk.nrows; i += 2 * kDirBatch) {
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const int ib = i + sl * kDirBatch;
+            load_batch(ib + kDirBatch, sl ^ 1);
+#pragma unroll
+            for (int u = 0; u < kDirBatch; ++u) {
+#pragma unroll
+                for (int s = LH - 1; s > 0; --s)
+#pragma unroll
+                    for (int c = 0; c < kDirCh; ++c) xw[s][c] = xw[s - 1][c];
+                float y1[kDirCh];
+#pragma unroll
+                for (int c = 0; c < kDirCh; ++c) {
+                    xw[0][c] = W::elem(kb[sl][u], c) * W::elem(vb[sl][u], c);
+                    const float dyv = W::elem(db[sl][u], c);
+                    // rows past the span load as zero, so they add nothing here
+                    const float dz = dyv * W::elem(qb[sl][u], c);
+                    float a = 0.0f;
+#pragma unroll
+                    for (int s = LH - 1; s >= 0; --s) {
+                        a = __builtin_fmaf(hv[c][s], xw[s][c], a);
+                        P[c][s] = __builtin_fmaf(dz, xw[s][c], P[c][s]);
+                    }
+                    y1[c] = dyv * a;
+                }
+                if (want_dq) W::store(W::pack(y1), rdq, wk.off(ib + u));
+            }
+        }
+    }
+    if (wk.ok) {
+        float *dst = p.ws + ((size_t)(wk.b * p.n_spans + wk.spn) * (size_t)p.D + (size_t)wk.c0) * p.l_h;
+#pragma unroll
+        for (int c = 0; c < kDirCh; ++c)
+#pragma unroll
+            for (int s = 0; s < LH; ++s)
+                if (s < p.l_h) dst[c * p.l_h + s] = P[c][s];
+    }
+}
+
+// Pass 2 for the direct backward: dh[g, s] = sum over the partial rows and
+// the group's channels of ws[row][channel][s], rows outer, channels inner.
+__global__ __launch_bounds__(256) void hyena_bwd_direct_dh_reduce_kernel(const float *ws, float *dh, int rows,
+                                                                         int D, int group_size, int l_h, int G) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= G * l_h) return;
+    const int g = idx / l_h, s = idx % l_h;
+    float acc = 0.0f;
+    for (int r = 0; r < rows; ++r) {
+        const float *row = ws + ((size_t)r * D + (size_t)g * group_size) * l_h + s;
+        for (int c = 0; c < group_size; ++c) acc += row[(size_t)c * l_h];
+    }
+    dh[idx] = acc;
 }
 
 // Kernel families and their compiled span counts (indices into kSpans).
@@ -1836,12 +1997,21 @@ int dir_plan(int64_t B, int64_t L, int64_t D, int64_t l_h, int dtype, int64_t sp
     return HYENA_OK;
 }
 
-template <bool F32> KernelFn pick_direct(int lh) {
+template <bool F32, bool REV = false, bool DUAL = false> KernelFn pick_direct(int lh) {
     switch (lh) {
-    case 1: return hyena_fwd_direct_kernel<F32, 1>;
-    case 2: return hyena_fwd_direct_kernel<F32, 2>;
-    case 4: return hyena_fwd_direct_kernel<F32, 4>;
-    default: return hyena_fwd_direct_kernel<F32, 8>;
+    case 1: return hyena_fwd_direct_kernel<F32, 1, REV, DUAL>;
+    case 2: return hyena_fwd_direct_kernel<F32, 2, REV, DUAL>;
+    case 4: return hyena_fwd_direct_kernel<F32, 4, REV, DUAL>;
+    default: return hyena_fwd_direct_kernel<F32, 8, REV, DUAL>;
+    }
+}
+
+template <bool F32> DhFn pick_direct_dh(int lh) {
+    switch (lh) {
+    case 1: return hyena_bwd_direct_dq_dh_kernel<F32, 1>;
+    case 2: return hyena_bwd_direct_dq_dh_kernel<F32, 2>;
+    case 4: return hyena_bwd_direct_dq_dh_kernel<F32, 4>;
+    default: return hyena_bwd_direct_dq_dh_kernel<F32, 8>;
     }
 }
 
@@ -1899,10 +2069,10 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
         if (overlaps(out, nbytes, kp, pbytes) || overlaps(out, nbytes, vp, pbytes)) return HYENA_ERR_ALIAS;
     }
     const bool chunk_dir = group_size % kTile != 0;
-    if (chunk_dir && P > 0) return HYENA_ERR_UNSUPPORTED;  // history prefix: grouped path only
     // off the 16-channel tile: a few taps are summed directly, longer
-    // filters take the chunk-direction GEMMs
+    // filters take the chunk-direction GEMMs (which take no history prefix)
     const bool direct = chunk_dir && l_h <= kDirTaps;
+    if (chunk_dir && !direct && P > 0) return HYENA_ERR_UNSUPPORTED;
     Plan pl;
     st = direct      ? dir_plan(B, L, D, l_h, dtype, span_chunks, &pl)
          : chunk_dir ? cd_plan(B, L, D, l_h, dtype, span_chunks, &pl)
@@ -1925,7 +2095,7 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
     p.g2 = nullptr;
     p.y2 = nullptr;
     const bool f32 = dtype == HYENA_DTYPE_F32;
-    KernelFn fn = direct      ? (f32 ? pick_direct<true>(pl.kh) : pick_direct<false>(pl.kh))
+    KernelFn fn = direct      ? (f32 ? pick_direct<true>(pl.kh) : pick_direct<false>(pl.kh))  // (reads kp, vp when P > 0)
                   : chunk_dir ? (f32 ? pick_kernel<true, kCd>(pl.kh, pl.span_index)
                                      : pick_kernel<false, kCd>(pl.kh, pl.span_index))
                               : (f32 ? pick_kernel<true, kFwd>(pl.kh, pl.span_index)
@@ -1937,9 +2107,18 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
 }
 
 // Partial-row count of the filter-gradient pass 1 (one row per span per
-// batch row), for the workspace size.
+// batch row), for the workspace size.  Group sizes off the 16-channel tile
+// take the direct kernels (filters of at most kDirTaps taps; one partial row
+// per span per batch row and channel), else the grouped ones.
 static int dh_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, int dtype,
                    Plan *pl, int64_t *ws_bytes) {
+    if (group_size % kTile != 0) {
+        if (l_h > kDirTaps) return HYENA_ERR_UNSUPPORTED;
+        int st = dir_plan(B, L, D, l_h, dtype, 0, pl);
+        if (st != HYENA_OK) return st;
+        *ws_bytes = B * pl->n_spans * D * l_h * (int64_t)sizeof(float);
+        return HYENA_OK;
+    }
     int st = make_plan(B, L, D, group_size, l_h, dtype, 0, pl, kDh);
     if (st != HYENA_OK) return st;
     *ws_bytes = B * pl->n_spans * (D / kTile) * l_h * (int64_t)sizeof(float);
@@ -2016,8 +2195,58 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
         if (dh) return hipMemsetAsync(dh, 0, dhbytes, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_LAUNCH;
         return HYENA_OK;
     }
-    if (group_size % kTile != 0) return HYENA_ERR_UNSUPPORTED;
     const bool f32 = dtype == HYENA_DTYPE_F32;
+    if (group_size % kTile != 0) {
+        // short filters off the tile (dh_plan refused longer ones): the
+        // direct kernels, with the direct forward's plan
+        if (dh) {
+            DhParams p;
+            p.q = q; p.k = k; p.v = v; p.dy = dy;
+            p.ws = (float *)workspace;
+            p.h = h;
+            p.dq = dq;
+            p.dk = nullptr; p.dv = nullptr;
+            p.L = L;
+            p.D = (int32_t)D;
+            p.l_h = (int32_t)l_h;
+            p.n_spans = (int32_t)dpl.n_spans;
+            p.n_slabs = (int32_t)dpl.n_slabs;
+            p.group_size = (int32_t)group_size;
+            p.span_rows = (int32_t)(dpl.span * kChunk);
+            DhFn fn = f32 ? pick_direct_dh<true>(dpl.kh) : pick_direct_dh<false>(dpl.kh);
+            hipLaunchKernelGGL(fn, dim3((unsigned)dpl.workgroups), dim3(64), 0, (hipStream_t)stream, p);
+            if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+        } else if (dq) {
+            st = fwd_launch(dy, k, v, h, nullptr, nullptr, 0, B, L, D, group_size, l_h, dq, dtype, 0, stream);
+            if (st != HYENA_OK) return st;
+        }
+        if (dk) {
+            // dx walked backwards in time with x = dy q, gated by v and k
+            Params p;
+            p.q = v; p.k = dy; p.v = q; p.h = h; p.y = dk;
+            p.g2 = k; p.y2 = dv;
+            p.kp = nullptr; p.vp = nullptr; p.P = 0; p.span_blocks = 0;
+            p.span_rows = (int32_t)(dpl.span * kChunk);
+            p.L = L;
+            p.D = (int32_t)D;
+            p.group_size = (int32_t)group_size;
+            p.l_h = (int32_t)l_h;
+            p.n_spans = (int32_t)dpl.n_spans;
+            p.n_slabs = (int32_t)dpl.n_slabs;
+            KernelFn fn = f32 ? pick_direct<true, true, true>(dpl.kh) : pick_direct<false, true, true>(dpl.kh);
+            hipLaunchKernelGGL(fn, dim3((unsigned)dpl.workgroups), dim3(64), 0, (hipStream_t)stream, p);
+            if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+        }
+        if (dh) {
+            const int G = (int)(D / group_size);
+            const int n = G * (int)l_h;
+            hipLaunchKernelGGL(hyena_bwd_direct_dh_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                               (hipStream_t)stream, (const float *)workspace, dh, (int)(B * dpl.n_spans), (int)D,
+                               (int)group_size, (int)l_h, G);
+            if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+        }
+        return HYENA_OK;
+    }
     // bf16 with all four gradients: one kernel computes dq, dk, dv and the
     // partial dh, when its window (history, span, the dz rows past the span
     // and a chunk of slack) stays below 2^31 bytes; else, with dq and dh, one
@@ -2063,6 +2292,7 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
         p.dq = fused_dq ? dq : nullptr;
         p.dk = fused_all ? dk : nullptr;
         p.dv = fused_all ? dv : nullptr;
+        p.span_rows = 0;
         p.L = L;
         p.D = (int32_t)D;
         p.l_h = (int32_t)l_h;

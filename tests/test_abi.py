@@ -188,7 +188,7 @@ def _halo(kp=P["k"] + (64 << 20), vp=P["v"] + (64 << 20), Pn=127, out=P["out"], 
     (dict(Pn=-1), -2), (dict(kp=None), -1), (dict(vp=None), -1),
     (dict(kp=P["k"] + (64 << 20) + 8), -5), (dict(vp=P["v"] + (64 << 20) + 4), -5),
     (dict(out=P["k"] + (64 << 20)), -6), (dict(out=P["v"] + (64 << 20) - 16), -6),
-    (dict(l_h=200), -4), (dict(gs=8), -7),
+    (dict(l_h=200), -4), (dict(gs=8, l_h=9), -7),
 ])
 def test_halo_entry_validates_its_prefix_on_host(kw, code):
     assert _halo(**kw) == code
@@ -213,7 +213,7 @@ def _bwd(q=P["q"], k=P["k"], v=P["v"], h=P["h"], dy=P["out"] + (64 << 20), B=1, 
     (dict(dq=P["q"]), -6), (dict(dk=P["out"]), -6), (dict(dh=P["k"] + 64), -6),
     (dict(ws=P["v"]), -6), (dict(ws=P["out"] + (16 << 20)), -6),
     (dict(ws=None), -10), (dict(ws_n=16), -10),
-    (dict(l_h=0), -4), (dict(gs=8), -7), (dict(dtype=5), -9),
+    (dict(l_h=0), -4), (dict(gs=8, l_h=9), -7), (dict(dtype=5), -9),
 ])
 def test_backward_validates_on_host(kw, code):
     assert _bwd(**kw) == code
@@ -226,6 +226,14 @@ def test_backward_workspace_size():
     assert hc.bwd_workspace_bytes(0, 8192, 4096, 16, 128) == 0
     with pytest.raises(hc.HyenaError):
         hc.bwd_workspace_bytes(1, 64, 64, 16, 300)
+    # off the 16-channel tile, at most 8 taps: one partial row of l_h floats
+    # per span (the direct plan's), batch row and channel; longer filters are
+    # not supported there
+    for B, L, D, gs, l_h in ((1, 8192, 4096, 1, 7), (2, 1000, 96, 3, 5), (1, 100, 8, 2, 1)):
+        span, _ = hc.plan(B, L, D, gs, l_h)
+        assert hc.bwd_workspace_bytes(B, L, D, gs, l_h) == B * (-(-L // (64 * span))) * D * l_h * 4
+    with pytest.raises(hc.HyenaError):
+        hc.bwd_workspace_bytes(1, 8192, 4096, 8, 9)
 
 
 def _long(q=P["q"], k=P["k"], v=P["v"], h=P["h"], B=1, L=128, D=64, gs=16, l_h=1000,

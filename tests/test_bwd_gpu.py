@@ -197,3 +197,73 @@ def test_backward_mr_b4_sampled():
                          h[g:g + 1], dy[:, :, c].contiguous(), gs)
         _check_dh(dh[g:g + 1], ref[3], env[3], w.torch_dtype,
                   _rows(w.B, w.L, w.D, gs, lh, w.torch_dtype), "mr_b4 dh")
+
+
+# Off the 16-channel tile with at most 8 taps: the direct kernels (dq with
+# the partial dh sums in one walk, dx walked backwards in time with two
+# gates, a reduction per group).  B, L, D, group_size, l_h: lengths below the
+# filter and across span seams, partial 256-channel slabs, each compiled tap
+# count (1, 2, 4, 8) and the lengths padded up to them.
+BWD_DIRECT_SHAPES = [
+    (1, 1, 8, 1, 1), (1, 6, 8, 1, 4), (2, 130, 264, 3, 7), (1, 700, 40, 5, 8),
+    (3, 257, 96, 8, 2), (1, 2048, 512, 1, 7), (2, 515, 24, 2, 6),
+]
+
+
+def _direct_rows(B, L, D, gs, l_h, dtype):
+    """Partial sums behind each dh value: one per span, batch row and channel of the group."""
+    code = hc.DTYPE_BF16 if dtype == torch.bfloat16 else hc.DTYPE_F32
+    return max(1, hc.bwd_workspace_bytes(B, L, D, gs, l_h, code) // (D * l_h * 4)) * gs
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h", BWD_DIRECT_SHAPES)
+def test_backward_off_tile_short_filters_gaussian(dt, B, L, D, gs, l_h):
+    log("bwd direct %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=11 * L + l_h + gs)
+    dy = normal_activation((B, L, D), dtype, "cpu", seed=L + 9)
+    grads = _bwd_gpu(*[t.to(DEV) for t in (q, k, v, h, dy)], gs)
+    ref, env = _refs(q, k, v, h, dy, gs)
+    _check_all(grads, ref, env, l_h, dtype, _direct_rows(B, L, D, gs, l_h, dtype), "bwd direct")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h", [(1, 6, 8, 1, 4), (2, 777, 96, 3, 7), (1, 300, 264, 8, 8)])
+def test_backward_off_tile_integer_inputs_bitwise(dt, B, L, D, gs, l_h):
+    log("bwd direct integer %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = integer_inputs(B, L, D, gs, l_h, dtype, seed=L + 13)
+    dy = integer_inputs(B, L, D, gs, 1, dtype, seed=L + 14)[0]
+    grads = _bwd_gpu(*[t.to(DEV) for t in (q, k, v, h, dy)], gs)
+    ref = oracle.conv_bwd_ref(*[to_np(t) for t in (q, k, v, h, dy)], gs)
+    for name, g, r in zip(("dq", "dk", "dv", "dh"), grads, ref):
+        assert np.array_equal(to_np(g), r), name
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_backward_off_tile_subsets_match_the_full_call(dt):
+    """dq alone is the direct forward with dy as the gate, which sums as the
+    one walk does; dh alone and dk, dv alone are the same kernels as in the
+    full call: every gradient has the same bits on every route."""
+    dtype = DTYPES[dt]
+    B, L, D, gs, l_h = 2, 1000, 264, 3, 7
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=41)
+    dy = normal_activation((B, L, D), dtype, "cpu", seed=42)
+    dev = [t.to(DEV) for t in (q, k, v, h, dy)]
+    full = hc.conv_bwd(*dev, gs)
+    for need in SUBSETS:
+        part = hc.conv_bwd(*dev, gs, need_dq=need[0], need_dkv=need[1], need_dh=need[2])
+        torch.cuda.synchronize()
+        wanted = (need[0], need[1], need[1], need[2])
+        for name, want, f, g in zip(("dq", "dk", "dv", "dh"), wanted, full, part):
+            assert (g is not None) == want, (name, need)
+            if want:
+                assert torch.equal(f, g), (name, need)
+
+
+def test_backward_off_tile_long_filters_unsupported():
+    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(1, 128, 64, 8, 9, torch.bfloat16, seed=3))
+    with pytest.raises(hc.HyenaError) as ei:
+        hc.conv_bwd(q, k, v, h, q, 8)
+    assert ei.value.status == -7

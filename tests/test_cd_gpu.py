@@ -200,11 +200,12 @@ def test_direct_short_filter_span_independent_and_causal():
     assert not torch.equal(y0[:, t0], y1[:, t0])
 
 
-def test_halo_and_backward_stay_on_the_grouped_path():
-    """The history-prefix forward and the backward reject off-tile groups."""
-    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(1, 128, 64, 8, 7, torch.bfloat16, seed=3))
+def test_halo_and_backward_off_tile_need_short_filters():
+    """Off the 16-channel tile, the history-prefix forward and the backward
+    take the direct kernels: filters longer than 8 taps are rejected."""
+    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(1, 128, 64, 8, 9, torch.bfloat16, seed=3))
     with pytest.raises(hc.HyenaError) as ei:
-        hc.conv_fwd(q, k, v, h, 8, k_prev=k[:, :6].contiguous(), v_prev=v[:, :6].contiguous())
+        hc.conv_fwd(q, k, v, h, 8, k_prev=k[:, :8].contiguous(), v_prev=v[:, :8].contiguous())
     assert ei.value.status == -7
     with pytest.raises(hc.HyenaError) as ei:
         hc.conv_bwd(q, k, v, h, q, 8)

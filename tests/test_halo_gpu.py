@@ -81,3 +81,28 @@ def test_two_shards_rebuild_the_mr_workload_row_by_row():
     second = _run(q[:, s:].contiguous(), k[:, s:].contiguous(), v[:, s:].contiguous(), h, w.group_size,
                   0, k[:, s - (w.l_h - 1):s].contiguous(), v[:, s - (w.l_h - 1):s].contiguous())
     assert torch.equal(torch.cat([first, second], dim=1), full)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("gs,l_h,split,Pn", [(1, 7, 256, 6), (3, 8, 100, 7), (2, 4, 65, 2), (1, 1, 300, 0),
+                                             (5, 6, 700, 40)])
+def test_off_tile_short_filter_shard_with_prefix(dt, gs, l_h, split, Pn):
+    """Group sizes off the 16-channel tile with at most 8 taps take the direct
+    kernel, which reads the rows before row 0 from the prefix.  Its sums do
+    not depend on where a span starts, so a shard with its prefix gives the
+    whole sequence's bits once the prefix covers the filter (a shorter one
+    means zeros before it, checked against the oracle)."""
+    log("halo direct %s gs=%d l_h=%d split=%d P=%d" % (dt, gs, l_h, split, Pn))
+    dtype = DTYPES[dt]
+    B, L, D = 2, 1000, 120
+    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(B, L, D, gs, l_h, dtype, seed=split + l_h + gs))
+    full = _run(q, k, v, h, gs)
+    sl = lambda a: a[:, split:].contiguous()
+    kp = k[:, split - Pn:split].contiguous() if Pn else None
+    vp = v[:, split - Pn:split].contiguous() if Pn else None
+    shard = _run(sl(q), sl(k), sl(v), h, gs, 0, kp, vp)
+    if Pn >= l_h - 1:
+        assert torch.equal(shard, full[:, split:])
+    qc, kc, vc = (a[:, split - Pn:].cpu() for a in (q, k, v))
+    ref, env = ref_and_envelope(qc, kc, vc, h.cpu(), gs)
+    check(to_np(shard), ref[:, Pn:], env[:, Pn:], l_h, dtype, "halo direct shard")

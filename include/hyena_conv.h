@@ -26,12 +26,14 @@
  * Grouping: any group_size that divides D, down to one filter per channel.
  * When group_size is a multiple of 16 the channels of a group form the
  * matrix-core dimension (section 4 of the page above: one filter per group
- * lets the Toeplitz factors be shared across its channels).  Otherwise the
- * work is laid out along the chunk direction instead (same page, section 6):
- * per channel, 16 consecutive 16-row sub-chunks share each Toeplitz block.
- * That second layout needs D * element size to be a multiple of 16 bytes,
- * and covers the plain forward only: the history-prefix forward and the
- * backward return HYENA_ERR_UNSUPPORTED unless group_size % 16 == 0.
+ * lets the Toeplitz factors be shared across its channels).  Otherwise, for
+ * filters longer than 8 taps, the work is laid out along the chunk direction
+ * instead (same page, section 6): per channel, 16 consecutive 16-row
+ * sub-chunks share each Toeplitz block; and for at most 8 taps each output's
+ * few products are summed directly.  Off the 16-channel grouping D * element
+ * size must be a multiple of 16 bytes, and the history-prefix forward and
+ * the backward take filters of at most 8 taps (longer ones return
+ * HYENA_ERR_UNSUPPORTED).
  *
  * Layout (all row-major, no strides):
  *   q, k, v, out : [B, L, D], D contiguous.
@@ -40,7 +42,8 @@
  *   hyena_conv_fwd      : bf16 in, bf16 out.  k*v is formed in fp32 and
  *                         rounded once to bf16 (round to nearest even) as the
  *                         matrix-core operand; taps are bf16; sums are fp32;
- *                         the gated result is rounded once to bf16.
+ *                         the gated result is rounded once to bf16.  (The
+ *                         direct sums off the grouping keep k*v in fp32.)
  *   hyena_conv_fwd_f32  : fp32 in, fp32 out, fp32 products and sums.
  *
  * Ownership and asynchrony: every pointer is a DEVICE pointer owned by the
@@ -98,8 +101,8 @@ int hyena_conv_fwd_f32(const void *q, const void *k, const void *v,
 /* Either forward with an explicit work split: `dtype` is a hyena_dtype and
  * `span_chunks` is the number of consecutive 64-row chunks one workgroup
  * walks (0 = the library's choice, clamped to [1, ceil(L/64)]; when
- * group_size % 16 != 0 the walk is in 256-row blocks of 1, 2 or 4, and the
- * request is rounded to one of those).  The result
+ * group_size % 16 != 0 and l_h > 8 the walk is in 256-row blocks of 1, 2 or
+ * 4, and the request is rounded to one of those).  The result
  * does not depend on `span_chunks`; it exists for tuning and for tests that
  * cover spans which do not divide the chunk count. */
 int hyena_conv_fwd_ex(const void *q, const void *k, const void *v,

@@ -19,6 +19,13 @@ Reported (one JSON line):
                measured HBM bytes per launch from the committed rocprofv3
                counter summary, or null if the kernel source changed since;
   layers       the same figures for each layer's kernel;
+  chunk_direction  each layer with one filter per channel: the direct kernel
+               (8 taps or fewer; with its backward) or the chunk-direction
+               GEMM kernel;
+  long_filter  a filter as long as the sequence (the FFT path);
+  backward     dq, dk, dv and dh of each layer;
+  stream_reference  torch's addcmul and a copy over the same bytes (the
+               attainable streaming rate on the box);
   cpu_baseline the fp64 oracle on the host cores over the full step's inputs;
   naive_conv1d the same step written with torch's depthwise F.conv1d (bf16),
                with and without the layout permutes;
@@ -550,7 +557,51 @@ def chunk_direction_rates(layers, sets, stream, reps):
                                 "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                                 "span_chunks": span, "workgroups": wgs,
                                 "kernel": ("hyena_fwd_direct_kernel" if w.l_h <= 8 else "hyena_fwd_cd_kernel")}
+        if w.l_h <= 8:
+            res[w.name + "_gs1"]["backward"] = _direct_backward_rate(w, per, h1, stream, reps)
     return res
+
+
+def _direct_backward_rate(w, per, h1, stream, reps):
+    """dq, dk, dv, dh with one filter per channel (the direct kernels): the
+    dq/dh walk, the backwards two-gate walk and the per-group reduction."""
+    import torch
+    import gated_convolution_sequence_amd as hc
+    from workloads import normal_activation
+    code = hc.DTYPE_BF16 if w.dtype == "bf16" else hc.DTYPE_F32
+    dys = [normal_activation((w.B, w.L, w.D), w.torch_dtype, per[0][0].device, w.seed + 19 + i)
+           for i in range(len(per))]
+    dq, dk, dv = (torch.empty_like(per[0][0]) for _ in range(3))
+    dh = torch.empty((w.D, w.l_h), dtype=torch.float32, device=per[0][0].device)
+    ws_n = hc.bwd_workspace_bytes(w.B, w.L, w.D, 1, w.l_h, code)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=per[0][0].device)
+    fn = hc.lib().hyena_conv_bwd
+
+    def call(i):
+        q, k, v, _, _ = per[i % len(per)]
+        st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), h1.data_ptr(), dys[i % len(per)].data_ptr(),
+                w.B, w.L, w.D, 1, w.l_h, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), dh.data_ptr(),
+                ws.data_ptr(), ws_n, code, stream.cuda_stream)
+        if st != 0:
+            raise hc.HyenaError(st, "hyena_conv_bwd")
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    eb = 2 if w.dtype == "bf16" else 4
+    # the dq/dh walk reads q, k, v, dy and writes dq; the backwards walk reads
+    # dy, q, v, k and writes dk, dv: 11 element accesses per token*channel
+    moved = 11 * eb * w.elems
+    del dys
+    return {"us": round(us, 2), "G_tok_ch_per_s": round(w.elems / (us * 1e-6) / 1e9, 2),
+            "moved_bytes": moved, "GBs_moved": round(moved / (us * 1e-6) / 1e9, 1),
+            "kernels": 3, "workspace_bytes": ws_n}
 
 
 def long_filter_rates(w, stream, reps):

@@ -1697,6 +1697,9 @@ __global__ __launch_bounds__(64) void hyena_fwd_direct_kernel(Params p) {
         for (int sl = 0; sl < 2; ++sl) {
             const int ib = i + sl * kDirBatch;
             load_batch(ib + kDirBatch, sl ^ 1);
+            // the next batch's loads go out before this batch is used: kept
+            // in place, so the wait for this batch leaves them in flight
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < kDirBatch; ++u) {
 #pragma unroll
@@ -1777,6 +1780,9 @@ __global__ __launch_bounds__(64) void hyena_bwd_direct_dq_dh_kernel(DhParams p) 
         for (int sl = 0; sl < 2; ++sl) {
             const int ib = i + sl * kDirBatch;
             load_batch(ib + kDirBatch, sl ^ 1);
+            // the next batch's loads go out before this batch is used: kept
+            // in place, so the wait for this batch leaves them in flight
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < kDirBatch; ++u) {
 #pragma unroll
@@ -1819,11 +1825,23 @@ __global__ __launch_bounds__(256) void hyena_bwd_direct_dh_reduce_kernel(const f
     const int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= G * l_h) return;
     const int g = idx / l_h, s = idx % l_h;
+    // term n = r * group_size + c, added in that order; eight loads in
+    // flight before their adds
+    const int n_terms = rows * group_size;
+    auto term = [&](int n) -> float {
+        const int r = n / group_size, c = n % group_size;
+        return ws[((size_t)r * D + (size_t)g * group_size + c) * l_h + s];
+    };
     float acc = 0.0f;
-    for (int r = 0; r < rows; ++r) {
-        const float *row = ws + ((size_t)r * D + (size_t)g * group_size) * l_h + s;
-        for (int c = 0; c < group_size; ++c) acc += row[(size_t)c * l_h];
+    int n = 0;
+    for (; n + 8 <= n_terms; n += 8) {
+        float t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = term(n + u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += t[u];
     }
+    for (; n < n_terms; ++n) acc += term(n);
     dh[idx] = acc;
 }
 

@@ -563,8 +563,8 @@ def chunk_direction_rates(layers, sets, stream, reps):
 
 
 def _direct_backward_rate(w, per, h1, stream, reps):
-    """dq, dk, dv, dh with one filter per channel (the direct kernels): the
-    dq/dh walk, the backwards two-gate walk and the per-group reduction."""
+    """dq, dk, dv, dh with one filter per channel (the direct kernels): one
+    walk backwards in time over q, k, v, dy and the per-group reduction."""
     import torch
     import gated_convolution_sequence_amd as hc
     from workloads import normal_activation
@@ -595,13 +595,13 @@ def _direct_backward_rate(w, per, h1, stream, reps):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
     eb = 2 if w.dtype == "bf16" else 4
-    # the dq/dh walk reads q, k, v, dy and writes dq; the backwards walk reads
-    # dy, q, v, k and writes dk, dv: 11 element accesses per token*channel
-    moved = 11 * eb * w.elems
+    # q, k, v, dy read once, dq, dk, dv written once: 7 element accesses per
+    # token*channel (plus the l_h - 1 rows each span reads on either side)
+    moved = 7 * eb * w.elems
     del dys
     return {"us": round(us, 2), "G_tok_ch_per_s": round(w.elems / (us * 1e-6) / 1e9, 2),
             "moved_bytes": moved, "GBs_moved": round(moved / (us * 1e-6) / 1e9, 1),
-            "kernels": 3, "workspace_bytes": ws_n}
+            "kernels": 2, "workspace_bytes": ws_n}
 
 
 def long_filter_rates(w, stream, reps):

@@ -1564,7 +1564,8 @@ struct DirWalk {
     int64_t t0;
     size_t base;  // byte offset of the window's first physical row in a [B, L, D] tensor
 
-    __device__ DirWalk(int64_t L, int D, int n_slabs, int n_spans, int span_rows) {
+    // `tail`: walk rows past the span that the window also holds
+    __device__ DirWalk(int64_t L, int D, int n_slabs, int n_spans, int span_rows, int tail = 0) {
         int bid = blockIdx.x;
         const int slab = bid % n_slabs;
         bid /= n_slabs;
@@ -1574,22 +1575,24 @@ struct DirWalk {
         ok = c0 < D;  // D % 4 == 0: the lane's 4 channels are all in range
         t0 = (int64_t)spn * span_rows;
         const int64_t t1 = min(L, t0 + (int64_t)span_rows);
+        const int64_t t2 = min(L, t1 + (int64_t)tail);
         const int64_t r_lo = max((int64_t)0, t0 - (LH - 1));
         row_bytes = D * EB;
         rel0 = (int)(t0 - r_lo);
         nrows = (int)(t1 - t0);
-        nwin = (int)(t1 - r_lo);
-        // walk rows r_lo .. t1 - 1: physical rows r_lo .. t1 - 1, or (REV)
-        // L - t1 .. L - 1 - r_lo in decreasing order (the host keeps the
+        nwin = (int)(t2 - r_lo);
+        // walk rows r_lo .. t2 - 1: physical rows r_lo .. t2 - 1, or (REV)
+        // L - t2 .. L - 1 - r_lo in decreasing order (the host keeps the
         // window below 2^31 bytes)
-        base = ((size_t)b * (size_t)L + (size_t)(REV ? L - t1 : r_lo)) * (size_t)row_bytes;
+        base = ((size_t)b * (size_t)L + (size_t)(REV ? L - t2 : r_lo)) * (size_t)row_bytes;
     }
     __device__ uint32_t nrec() const { return (uint32_t)(nwin * row_bytes); }
     // byte offset of the lane's segment in walk row t0 + i (i >= -(LH - 1));
-    // rows past the span: out of range
-    __device__ uint32_t off(int i) const {
+    // rows past the span (or, with `past`, past the window): out of range
+    __device__ uint32_t off(int i, bool past = false) const {
         const int w = rel0 + i;
-        return (ok && i < nrows) ? (uint32_t)((REV ? nwin - 1 - w : w) * row_bytes + c0 * EB) : kOOB;
+        return (ok && (past ? w < nwin : i < nrows)) ? (uint32_t)((REV ? nwin - 1 - w : w) * row_bytes + c0 * EB)
+                                                     : kOOB;
     }
     template <int POLICY>
     __device__ static seg_t load(const __amdgpu_buffer_rsrc_t &r, uint32_t o) {
@@ -1723,88 +1726,116 @@ __global__ __launch_bounds__(64) void hyena_fwd_direct_kernel(Params p) {
     }
 }
 
-// dq and the filter gradient's partial sums for short filters off the tile,
-// in one walk in time order: dq = dy * sum_s h[s] x[t - s] as the direct
-// forward with dy as the gate, and for each lane's channel c and tap s the
-// partial sum over the span's rows of dz[t] x[t - s] (dz = dy q in fp32,
-// x = k v from the same register window).  The partial sums go to
-// ws[B * spans][D][l_h]; a reduction adds them per group (pass 2 of page "04.
-// hardware-aware convolution kernels", section 7).
+// The whole backward for short filters off the tile, in one walk backwards
+// in time (walk row r is physical row L - 1 - r), so that q, k, v and dy are
+// read once and dq, dk, dv written once:
+//   * dz = dy q and x = k v (fp32) go into register windows of the last LH
+//     walk rows, dy into a delay line as long;
+//   * dx of row r is the causal sum over the dz window, h[s] dz[r - s] in
+//     walk order (= dz[t + s] in time): dk = v dx and dv = k dx, with row r's
+//     gates still in registers;
+//   * the partial filter gradient pairs row r's x with the dz window:
+//     dh[s] gets x[u] dz[u + s] (in time) for each of the span's rows u;
+//   * dq needs the LH - 1 rows before it in time, which come after it in the
+//     walk: dq of walk row r - (LH - 1) is completed at row r from the x
+//     window read backwards, gated by dy from the delay line.
+// The walk starts LH - 1 rows before the span (dz only) and runs LH - 1 rows
+// past it (x only).  dx and dq sum over the taps in the orders the direct
+// forward kernels use, so dk, dv and dq have the same bits as those kernels.
+// The partial sums go to ws[B * spans][D][l_h]; a reduction adds them per
+// group (pass 2 of page "04. hardware-aware convolution kernels", section 7).
 template <bool F32, int LH>
-__global__ __launch_bounds__(64) void hyena_bwd_direct_dq_dh_kernel(DhParams p) {
-    using W = DirWalk<F32, LH, false>;
+__global__ __launch_bounds__(64) void hyena_bwd_direct_kernel(DhParams p) {
+    using W = DirWalk<F32, LH, true>;
     using seg_t = typename W::seg_t;
-    const W wk(p.L, p.D, p.n_slabs, p.n_spans, p.span_rows);
+    const W wk(p.L, p.D, p.n_slabs, p.n_spans, p.span_rows, LH - 1);
     const uint32_t nrec = wk.nrec();
     const __amdgpu_buffer_rsrc_t rq = make_rsrc((const char *)p.q + wk.base, nrec);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc((const char *)p.k + wk.base, nrec);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc((const char *)p.v + wk.base, nrec);
     const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char *)p.dy + wk.base, nrec);
-    const bool want_dq = p.dq != nullptr;
-    const __amdgpu_buffer_rsrc_t rdq = make_rsrc((char *)(want_dq ? p.dq : p.ws) + wk.base, want_dq ? nrec : 0u);
+    // outputs not asked for: an empty window, every store dropped
+    const __amdgpu_buffer_rsrc_t rdq = make_rsrc((char *)(p.dq ? p.dq : p.ws) + wk.base, p.dq ? nrec : 0u);
+    const __amdgpu_buffer_rsrc_t rdk = make_rsrc((char *)(p.dk ? p.dk : p.ws) + wk.base, p.dk ? nrec : 0u);
+    const __amdgpu_buffer_rsrc_t rdv = make_rsrc((char *)(p.dv ? p.dv : p.ws) + wk.base, p.dv ? nrec : 0u);
 
     float hv[kDirCh][LH];
     wk.taps(p.h, p.group_size, p.l_h, hv);
-    float xw[LH][kDirCh];
+    // windows: zw[s] = dz of walk row r - s, xw[s] = x of row r - s, yw[s]
+    // = dy of row r - s; rows outside the walk are zero
+    float zw[LH][kDirCh], xw[LH][kDirCh], yw[LH][kDirCh], P[kDirCh][LH];
 #pragma unroll
     for (int s = 0; s < LH; ++s)
 #pragma unroll
-        for (int c = 0; c < kDirCh; ++c) xw[s][c] = 0.0f;
-#pragma unroll
-    for (int j = 1; j < LH; ++j) {
-        if (wk.t0 - j >= 0) {
-            const seg_t kk = W::template load<0>(rk, wk.off(-j)), vv = W::template load<0>(rv, wk.off(-j));
-#pragma unroll
-            for (int c = 0; c < kDirCh; ++c) xw[j - 1][c] = W::elem(kk, c) * W::elem(vv, c);
-        }
-    }
-    float P[kDirCh][LH];
-#pragma unroll
-    for (int c = 0; c < kDirCh; ++c)
-#pragma unroll
-        for (int s = 0; s < LH; ++s) P[c][s] = 0.0f;
+        for (int c = 0; c < kDirCh; ++c) zw[s][c] = xw[s][c] = yw[s][c] = P[c][s] = 0.0f;
+    // walk rows i = -(LH - 1) .. nrows + LH - 2 relative to the span start:
+    // dz where i < nrows, x where i >= 0 (both zero past the sequence)
+    const int i_begin = -(LH - 1), i_end = wk.nrows + LH - 1;
     seg_t kb[2][kDirBatch], vb[2][kDirBatch], qb[2][kDirBatch], db[2][kDirBatch];
     auto load_batch = [&](int i0, int sl) {
 #pragma unroll
         for (int u = 0; u < kDirBatch; ++u) {
-            const uint32_t o = wk.off(i0 + u);
-            kb[sl][u] = W::template load<kLoadPolicy>(rk, o);
-            vb[sl][u] = W::template load<kLoadPolicy>(rv, o);
-            qb[sl][u] = W::template load<kLoadPolicy>(rq, o);
-            db[sl][u] = W::template load<kLoadPolicy>(rd, o);
+            const int i = i0 + u;
+            const bool in_walk = i < i_end && (int)wk.t0 + i >= 0;
+            const uint32_t oz = (in_walk && i < wk.nrows) ? wk.off(i) : kOOB;
+            const uint32_t ox = (in_walk && i >= 0) ? wk.off(i, true) : kOOB;
+            qb[sl][u] = W::template load<kLoadPolicy>(rq, oz);
+            db[sl][u] = W::template load<kLoadPolicy>(rd, oz);
+            kb[sl][u] = W::template load<kLoadPolicy>(rk, ox);
+            vb[sl][u] = W::template load<kLoadPolicy>(rv, ox);
         }
     };
-    load_batch(0, 0);
-    for (int i = 0; i < wk.nrows; i += 2 * kDirBatch) {
+    load_batch(i_begin, 0);
+    for (int i = i_begin; i < i_end; i += 2 * kDirBatch) {
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {
             const int ib = i + sl * kDirBatch;
             load_batch(ib + kDirBatch, sl ^ 1);
-            // the next batch's loads go out before this batch is used: kept
-            // in place, so the wait for this batch leaves them in flight
+            // the next batch's loads go out before this batch is used
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < kDirBatch; ++u) {
+                const int r = ib + u;
 #pragma unroll
                 for (int s = LH - 1; s > 0; --s)
 #pragma unroll
-                    for (int c = 0; c < kDirCh; ++c) xw[s][c] = xw[s - 1][c];
-                float y1[kDirCh];
+                    for (int c = 0; c < kDirCh; ++c) {
+                        zw[s][c] = zw[s - 1][c];
+                        xw[s][c] = xw[s - 1][c];
+                        yw[s][c] = yw[s - 1][c];
+                    }
+                float yk[kDirCh], yv[kDirCh], yq[kDirCh];
 #pragma unroll
                 for (int c = 0; c < kDirCh; ++c) {
-                    xw[0][c] = W::elem(kb[sl][u], c) * W::elem(vb[sl][u], c);
+                    const float kx = W::elem(kb[sl][u], c), vx = W::elem(vb[sl][u], c);
                     const float dyv = W::elem(db[sl][u], c);
-                    // rows past the span load as zero, so they add nothing here
-                    const float dz = dyv * W::elem(qb[sl][u], c);
+                    zw[0][c] = dyv * W::elem(qb[sl][u], c);
+                    xw[0][c] = kx * vx;
+                    yw[0][c] = dyv;
+                    // dx of row r (zero outside the span: its stores drop)
                     float a = 0.0f;
 #pragma unroll
-                    for (int s = LH - 1; s >= 0; --s) {
-                        a = __builtin_fmaf(hv[c][s], xw[s][c], a);
-                        P[c][s] = __builtin_fmaf(dz, xw[s][c], P[c][s]);
+                    for (int s = LH - 1; s >= 0; --s) a = __builtin_fmaf(hv[c][s], zw[s][c], a);
+                    yk[c] = vx * a;
+                    yv[c] = kx * a;
+                    // partial dh: x of row r (zero outside the span's rows
+                    // and the tail) with dz of the rows after it in time
+                    if (r >= 0 && r < wk.nrows) {
+#pragma unroll
+                        for (int s = 0; s < LH; ++s) P[c][s] = __builtin_fmaf(xw[0][c], zw[s][c], P[c][s]);
                     }
-                    y1[c] = dyv * a;
+                    // dq of walk row r - (LH - 1): x of the rows before it in time
+                    float aq = 0.0f;
+#pragma unroll
+                    for (int s = LH - 1; s >= 0; --s) aq = __builtin_fmaf(hv[c][s], xw[LH - 1 - s][c], aq);
+                    yq[c] = yw[LH - 1][c] * aq;
                 }
-                if (want_dq) W::store(W::pack(y1), rdq, wk.off(ib + u));
+                if (r >= 0 && r < wk.nrows) {
+                    W::store(W::pack(yk), rdk, wk.off(r));
+                    W::store(W::pack(yv), rdv, wk.off(r));
+                }
+                const int rq_row = r - (LH - 1);
+                if (rq_row >= 0 && rq_row < wk.nrows) W::store(W::pack(yq), rdq, wk.off(rq_row));
             }
         }
     }
@@ -1985,7 +2016,7 @@ int cd_plan(int64_t B, int64_t L, int64_t D, int64_t l_h, int dtype, int64_t spa
 // Plan of the short-filter direct kernel (group sizes off the 16-channel
 // tile, l_h <= kDirTaps).  One wave per 256-channel slab and span of rows;
 // spans of 256 rows, halved down to 64 while that leaves fewer than 1024
-// workgroups (four waves per CU) or a byte window (span + 8 rows) of 2^31
+// workgroups (four waves per CU) or a byte window (span + 16 rows) of 2^31
 // or more, or span_req chunks.  `kh` holds the compiled tap count (1, 2, 4 or
 // 8) and `span` the span in 64-row chunks.
 constexpr int64_t kDirWorkgroups = 1024;
@@ -2003,10 +2034,11 @@ int dir_plan(int64_t B, int64_t L, int64_t D, int64_t l_h, int dtype, int64_t sp
     } else {
         rows = 256;
         while (rows > kChunk && (B * pl->n_slabs * ((L + rows - 1) / rows) < kDirWorkgroups ||
-                                 (rows + kDirTaps) * D * eb >= kMaxWindowBytes))
+                                 (rows + 2 * kDirTaps) * D * eb >= kMaxWindowBytes))
             rows /= 2;
     }
-    if ((rows + kDirTaps) * D * eb >= kMaxWindowBytes) return HYENA_ERR_UNSUPPORTED;
+    // the windows: a span, the rows before it and (the backward) after it
+    if ((rows + 2 * kDirTaps) * D * eb >= kMaxWindowBytes) return HYENA_ERR_UNSUPPORTED;
     pl->span_index = 0;
     pl->span = rows / kChunk;
     pl->n_spans = (L + rows - 1) / rows;
@@ -2026,10 +2058,10 @@ template <bool F32, bool REV = false, bool DUAL = false> KernelFn pick_direct(in
 
 template <bool F32> DhFn pick_direct_dh(int lh) {
     switch (lh) {
-    case 1: return hyena_bwd_direct_dq_dh_kernel<F32, 1>;
-    case 2: return hyena_bwd_direct_dq_dh_kernel<F32, 2>;
-    case 4: return hyena_bwd_direct_dq_dh_kernel<F32, 4>;
-    default: return hyena_bwd_direct_dq_dh_kernel<F32, 8>;
+    case 1: return hyena_bwd_direct_kernel<F32, 1>;
+    case 2: return hyena_bwd_direct_kernel<F32, 2>;
+    case 4: return hyena_bwd_direct_kernel<F32, 4>;
+    default: return hyena_bwd_direct_kernel<F32, 8>;
     }
 }
 
@@ -2218,12 +2250,13 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
         // short filters off the tile (dh_plan refused longer ones): the
         // direct kernels, with the direct forward's plan
         if (dh) {
+            // the whole backward in one walk (any of dq, dk, dv may be absent)
             DhParams p;
             p.q = q; p.k = k; p.v = v; p.dy = dy;
             p.ws = (float *)workspace;
             p.h = h;
             p.dq = dq;
-            p.dk = nullptr; p.dv = nullptr;
+            p.dk = dk; p.dv = dv;
             p.L = L;
             p.D = (int32_t)D;
             p.l_h = (int32_t)l_h;
@@ -2238,7 +2271,7 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
             st = fwd_launch(dy, k, v, h, nullptr, nullptr, 0, B, L, D, group_size, l_h, dq, dtype, 0, stream);
             if (st != HYENA_OK) return st;
         }
-        if (dk) {
+        if (dk && !dh) {
             // dx walked backwards in time with x = dy q, gated by v and k
             Params p;
             p.q = v; p.k = dy; p.v = q; p.h = h; p.y = dk;

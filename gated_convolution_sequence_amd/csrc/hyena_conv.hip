@@ -197,7 +197,8 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     constexpr int kStBufs = KH >= HYENA_ST2_MIN_KH ? 2 : 1;
 
     // x = k*v of the current chunk (row-major, swizzled), the fp32
-    // accumulators of the current chunk (row-major, swizzled) and the filters.
+    // accumulators of the current chunk (and, with two staging buffers, of the
+    // previous one; row-major, swizzled) and the filters.
     __shared__ __attribute__((aligned(16))) unsigned char xs[kChunk * T::PITCH];
     __shared__ __attribute__((aligned(16))) unsigned char st[kStBufs * kChunk * ST_PITCH];
     __shared__ float hs[kWaves][kHLen];
@@ -549,7 +550,8 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
 // ---------------------------------------------------------------------------
 struct DhParams {
     const void *q, *k, *v, *dy;
-    float *ws;          // [B * n_spans][D / 16][l_h] partial sums
+    float *ws;          // partial sums: [B * n_spans][D / 16][l_h] (the
+                        // direct form: [B * n_spans][D][l_h])
     const void *h;      // filters (the fused forms only)
     void *dq;           // dq output (the fused forms only)
     void *dk, *dv;      // dk, dv outputs (the whole-backward form only)
@@ -2299,9 +2301,9 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
         return HYENA_OK;
     }
     // bf16 with all four gradients: one kernel computes dq, dk, dv and the
-    // partial dh, when its window (history, span, the dz rows past the span
-    // and a chunk of slack) stays below 2^31 bytes; else, with dq and dh, one
-    // kernel computes both (below)
+    // partial dh, when its window (history, span, the rows its walk reads
+    // past the span and a chunk of slack) stays below 2^31 bytes; else, with
+    // dq and dh, one kernel computes both (below)
     const int64_t fut_rows = ((32 * (int64_t)dpl.kh + kChunk - 1) / kChunk) * kChunk;
     const bool fused_all = dq && dk && dv && dh && !f32 &&
                            (dpl.span * kChunk + 32 * dpl.kh + fut_rows + kChunk) * D * (int64_t)eb < kMaxWindowBytes;

@@ -1156,9 +1156,10 @@ __global__ __launch_bounds__(256) void hyena_bwd_dh_reduce_kernel(const float *w
 
 typedef void (*KernelFn)(Params);
 
-// Chunks of k, v and q in flight per workgroup.  The fp32 path (twice the
-// bytes per element, one row per MFMA step) keeps two to stay spill-free.
-template <bool F32> constexpr int kPrefetch = F32 ? 2 : 3;
+// Chunks of k, v and q in flight per workgroup: two for both element types.
+// In bf16 three (KH = 4: 221 VGPRs against 174) measured 1-2% slower on
+// MI355X, at B = 1, L = 8192, D = 4096 and at L = 2^20 alike.
+template <bool F32> constexpr int kPrefetch = 2;
 
 // Spans (chunks per workgroup) with a compiled kernel; a requested span is
 // rounded down to one of these.  fp32 stops at 4 (register budget).
@@ -1956,9 +1957,16 @@ int make_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, 
     // Default span: long enough that the 32*KH history rows a workgroup
     // re-reads stay a small share of its rows (2*KH chunks: 1/4 at most),
     // short enough that many workgroups balance the CUs.  Measured on
-    // MI355X at B=1, L=8192, D=4096: SE best at 2 chunks, MR at 8.
+    // MI355X at D=4096 (SE then MR, bf16): MR best at 8 chunks from L=8192
+    // to 2^20; SE at 4 chunks while that grid has at most 2048 workgroups
+    // (L <= 16384 at B=1), at 2 from L=32768 on.
     int64_t want = span_req;
-    if (want <= 0) want = pl->kh <= 1 ? 2 : 2 * pl->kh;
+    if (want <= 0) {
+        want = pl->kh <= 1 ? 2 : 2 * pl->kh;
+        if (pl->kh <= 1 && family == kFwd && dtype == HYENA_DTYPE_BF16 &&
+            B * pl->n_slabs * ((pl->n_chunks + 3) / 4) <= 2048)
+            want = 4;
+    }
     // the filter-gradient kernel writes one partial row per span: longer
     if (family == kDh && span_req <= 0) want = 16;
     if (want > pl->n_chunks) want = pl->n_chunks;

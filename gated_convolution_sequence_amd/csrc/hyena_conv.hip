@@ -1852,6 +1852,13 @@ __global__ __launch_bounds__(64) void hyena_bwd_direct_kernel(DhParams p) {
     }
 }
 
+// dh of an empty problem (no rows): zeros, written by a kernel so that a
+// call captured into a graph records kernels only.
+__global__ __launch_bounds__(256) void hyena_zero_kernel(float *out, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) out[i] = 0.0f;
+}
+
 // Pass 2 for the direct backward: dh[g, s] = sum over the partial rows and
 // the group's channels of ws[row][channel][s], rows outer, channels inner.
 __global__ __launch_bounds__(256) void hyena_bwd_direct_dh_reduce_kernel(const float *ws, float *dh, int rows,
@@ -2252,7 +2259,13 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
     }
     if (dh && (!workspace || workspace_bytes < ws_need)) return HYENA_ERR_WORKSPACE;
     if (B == 0 || L == 0 || D == 0) {
-        if (dh) return hipMemsetAsync(dh, 0, dhbytes, (hipStream_t)stream) == hipSuccess ? HYENA_OK : HYENA_ERR_LAUNCH;
+        // no rows: dh is zero (D == 0: dh has no elements)
+        const int64_t n = (int64_t)(dhbytes / sizeof(float));
+        if (dh && n > 0) {
+            hipLaunchKernelGGL(hyena_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                               (hipStream_t)stream, dh, n);
+            if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+        }
         return HYENA_OK;
     }
     const bool f32 = dtype == HYENA_DTYPE_F32;

@@ -267,3 +267,24 @@ def test_backward_off_tile_long_filters_unsupported():
     with pytest.raises(hc.HyenaError) as ei:
         hc.conv_bwd(q, k, v, h, q, 8)
     assert ei.value.status == -7
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,gs,l_h", [(0, 64, 16, 7), (2, 0, 16, 128), (1, 0, 1, 7)])
+def test_backward_without_rows_zeroes_dh(dt, B, L, gs, l_h):
+    """No rows: dq, dk, dv are empty and dh is written with zeros (the caller's
+    buffer starts as NaN here), by a kernel."""
+    dtype, D = DTYPES[dt], 64
+    log("no rows %s B=%d L=%d gs=%d l_h=%d" % (dt, B, L, gs, l_h))
+    buf = torch.zeros(64, dtype=dtype, device=DEV)  # q, k, v, dy: no rows are read
+    h = torch.ones(D // gs, l_h, dtype=dtype, device=DEV)
+    dh = torch.full((D // gs, l_h), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    code = hc.DTYPE_BF16 if dt == "bf16" else hc.DTYPE_F32
+    p = buf.data_ptr()
+    st = hc.lib().hyena_conv_bwd(p, p, p, h.data_ptr(), p, B, L, D, gs, l_h, None, None, None,
+                                 dh.data_ptr(), ws.data_ptr(), 16, code,
+                                 torch.cuda.current_stream(DEV).cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(dh, torch.zeros_like(dh))

@@ -196,7 +196,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU: this operator is benchmarked on a single MI355X; "
-              "--gpus %d is not supported (the multi-GPU split is described in DESIGN.md)" % args.gpus,
+              "--gpus %d is not supported (a longer sequence splits into row shards, each run "
+              "with hyena_conv_fwd_halo on its own GPU)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 

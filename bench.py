@@ -12,7 +12,9 @@ long_stripe); the default line is the stripe.
 Reported (one JSON line):
   value        whole-step throughput, G(token*channel)/s = 2 * B*L*D / step time
                (both layers count), inputs resident in HBM;
-  roofline     the MR kernel (the longer of the two): algorithmic bytes per
+  roofline     the dominant kernel, the layer whose launches took longer in
+               this run (MR and SE now take about the same time, so either
+               can be reported; `kernel` names it): algorithmic bytes per
                launch (q, k, v read once, y written once: 8 B per
                token*channel) / its mean launch time from HIP events on the
                launch stream, against the 8 TB/s HBM3E peak; `traffic` is the

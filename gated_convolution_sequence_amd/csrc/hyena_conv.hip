@@ -127,25 +127,27 @@ __device__ inline uint32_t pack_bf16(float a, float b) {
 }
 
 // Element-type traits: the I/O width and the LDS tile geometry.
-template <bool F32> struct Tr;
-template <> struct Tr<false> {           // bf16 I/O
+// NW: waves per workgroup (one 16-channel tile each); the slab is 16 NW
+// channels.
+template <bool F32, int NW = kWaves> struct Tr;
+template <int NW> struct Tr<false, NW> { // bf16 I/O
     static constexpr int EB = 2;         // bytes per element
     static constexpr int VEC = 8;        // elements per 16-byte access
-    static constexpr int PITCH = kSlab * 2;          // LDS bytes per row
-    static constexpr int TPR = PITCH / 16;           // threads per row (8)
-    static constexpr int RPL = kThreads / TPR;       // rows per load (32)
+    static constexpr int PITCH = kTile * NW * 2;     // LDS bytes per row
+    static constexpr int TPR = PITCH / 16;           // threads per row (2 NW)
+    static constexpr int RPL = 64 * NW / TPR;        // rows per load (32)
     static constexpr int NLD = kChunk / RPL;         // loads per tensor per chunk (2)
     // XOR swizzle of the 16-byte segment index by row (conflict-free
     // time-major reads of 16 channels x 4 row groups).
     __device__ static int swz(int row) { return ((row >> 3) & 3) << 1; }
     static_assert(NLD * RPL == kChunk, "loads must tile the chunk");
 };
-template <> struct Tr<true> {            // fp32 I/O
+template <int NW> struct Tr<true, NW> {  // fp32 I/O
     static constexpr int EB = 4;
     static constexpr int VEC = 4;
-    static constexpr int PITCH = kSlab * 4;
-    static constexpr int TPR = PITCH / 16;           // 16
-    static constexpr int RPL = kThreads / TPR;       // 16
+    static constexpr int PITCH = kTile * NW * 4;
+    static constexpr int TPR = PITCH / 16;           // 4 NW
+    static constexpr int RPL = 64 * NW / TPR;        // 16
     static constexpr int NLD = kChunk / RPL;         // 4
     __device__ static int swz(int row) { return (row & 3) << 2; }
     static_assert(NLD * RPL == kChunk, "loads must tile the chunk");
@@ -191,9 +193,10 @@ template <> struct Mma<true> {
 // causal filter applied in the walk's order computes sum_s h[s] x[t+s] (the
 // input gradient of the operator).  DUAL gates the one convolution with two
 // tensors into two outputs (y = q acc, y2 = g2 acc).
-template <bool F32, int KH, int PF, int S, bool REV = false, bool DUAL = false>
-__global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
-    using T = Tr<F32>;
+template <bool F32, int KH, int PF, int S, bool REV = false, bool DUAL = false, int NW = kWaves>
+__global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
+    using T = Tr<F32, NW>;
+    constexpr int SLAB = kTile * NW;                      // channels per workgroup
     using M = Mma<F32>;
     using frag = typename M::frag;
     constexpr int HROWS = 32 * KH;                        // history rows before a span
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     constexpr int NI = S + H;                             // ingested chunks
     constexpr int NH = HROWS / M::ROWS;                   // history fragments
     constexpr int NX = NH + M::FPC;                       // fragments one chunk reads
-    constexpr int ST_PITCH = kSlab * 4;                   // fp32 staging row, bytes
+    constexpr int ST_PITCH = SLAB * 4;                    // fp32 staging row, bytes
     constexpr int kStBufs = KH >= HYENA_ST2_MIN_KH ? 2 : 1;
 
     // x = k*v of the current chunk (row-major, swizzled), the fp32
@@ -210,7 +213,7 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     // previous one; row-major, swizzled) and the filters.
     __shared__ __attribute__((aligned(16))) unsigned char xs[kChunk * T::PITCH];
     __shared__ __attribute__((aligned(16))) unsigned char st[kStBufs * kChunk * ST_PITCH];
-    __shared__ float hs[kWaves][kHLen];
+    __shared__ float hs[NW][kHLen];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;           // wave = 16-channel tile of the slab
@@ -227,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void hyena_fwd_kernel(Params p) {
     const int64_t t_begin = (int64_t)spn * S * kChunk;
     const int64_t t_stop = min(p.L, t_begin + (int64_t)S * kChunk);
     const int64_t base_row = max((int64_t)0, t_begin - HROWS);
-    const int c_begin = slab * kSlab;
+    const int c_begin = slab * SLAB;
     const int row_bytes = p.D * T::EB;
 
     // Byte window [base, base + nrec) of this workgroup: rows base_row ..
@@ -1924,6 +1927,24 @@ constexpr typename FnType<F32, Fam>::type kernel_of() {
         return hyena_fwd_cd_kernel<F32, KH>;
 }
 
+// The bf16 forward for KH <= 1 (filters of at most 33 taps) with 16 waves:
+// 256-channel slabs, so every row segment a workgroup reads or writes is
+// 512 contiguous bytes.  On MI355X a plain three-read, one-write streaming
+// kernel with 256 workgroups measured 2.4, 5.0, 5.5 and 6.1 TB/s for 64-,
+// 128-, 256- and 512-byte row segments per workgroup (B=1, L=8192, D=4096,
+// bf16).  One chunk in flight keeps it within 128 VGPRs (two spill).
+constexpr int kWideWaves = 16;
+constexpr int kWidePrefetch = 1;
+constexpr int64_t kWideWorkgroups = 256;  // one 16-wave workgroup per CU (112 KiB of LDS)
+template <int KH, int... Ss> KernelFn wide_entry(int si, std::integer_sequence<int, Ss...>) {
+    static constexpr KernelFn fns[] = {hyena_fwd_kernel<false, KH, kWidePrefetch, kSpans[Ss], false, false, kWideWaves>...};
+    return fns[si];
+}
+KernelFn pick_wide(int kh, int si) {
+    return kh == 0 ? wide_entry<0>(si, std::make_integer_sequence<int, kNumSpans>{})
+                   : wide_entry<1>(si, std::make_integer_sequence<int, kNumSpans>{});
+}
+
 template <bool F32, int Fam, int KH, int... Ss>
 typename FnType<F32, Fam>::type span_table_entry(int si, std::integer_sequence<int, Ss...>) {
     static constexpr typename FnType<F32, Fam>::type fns[] = {kernel_of<F32, Fam, KH, kSpans[Ss]>()...};
@@ -1947,6 +1968,7 @@ constexpr int64_t kMaxWindowBytes = (int64_t)1 << 31;
 struct Plan {
     int64_t span, n_spans, n_slabs, n_chunks, workgroups;
     int kh, span_index;
+    bool wide = false;  // the 16-wave forward (256-channel slabs)
 };
 
 int check_sizes(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, int dtype) {
@@ -1967,21 +1989,25 @@ int make_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, 
     const int64_t eb = dtype == HYENA_DTYPE_F32 ? 4 : 2;
     pl->kh = (int)((l_h - 1 + 31) / 32);
     pl->n_chunks = (L + kChunk - 1) / kChunk;
-    pl->n_slabs = (D + kSlab - 1) / kSlab;
+    pl->wide = family == kFwd && dtype == HYENA_DTYPE_BF16 && pl->kh <= 1;
+    pl->n_slabs = (D + (pl->wide ? kTile * kWideWaves : kSlab) - 1) / (pl->wide ? kTile * kWideWaves : kSlab);
     if (group_size % kTile != 0) return HYENA_ERR_UNSUPPORTED;
     if (D > INT32_MAX / 16) return HYENA_ERR_UNSUPPORTED;
     // Default span: long enough that the 32*KH history rows a workgroup
     // re-reads stay a small share of its rows (2*KH chunks: 1/4 at most),
     // short enough that many workgroups balance the CUs.  Measured on
     // MI355X at D=4096 (SE then MR, bf16): MR best at 8 chunks from L=8192
-    // to 2^20; SE at 4 chunks while that grid has at most 2048 workgroups
-    // (L <= 16384 at B=1), at 2 from L=32768 on.
+    // to 2^20.  The 16-wave SE kernel: spans up to 8 chunks while every CU
+    // still gets a workgroup (kWideWorkgroups); at B=1 that is 2 chunks at
+    // L=2048, 4 at 4096 and 8 from 8192 on, each the fastest (or within 1%
+    // of it) in the step.
     int64_t want = span_req;
     if (want <= 0) {
         want = pl->kh <= 1 ? 2 : 2 * pl->kh;
-        if (pl->kh <= 1 && family == kFwd && dtype == HYENA_DTYPE_BF16 &&
-            B * pl->n_slabs * ((pl->n_chunks + 3) / 4) <= 2048)
-            want = 4;
+        if (pl->wide) {
+            want = 8;
+            while (want > 1 && B * pl->n_slabs * ((pl->n_chunks + want - 1) / want) < kWideWorkgroups) want /= 2;
+        }
     }
     // the filter-gradient kernel writes one partial row per span: longer
     if (family == kDh && span_req <= 0) want = 16;
@@ -2174,9 +2200,11 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
     KernelFn fn = direct      ? (f32 ? pick_direct<true>(pl.kh) : pick_direct<false>(pl.kh))  // (reads kp, vp when P > 0)
                   : chunk_dir ? (f32 ? pick_kernel<true, kCd>(pl.kh, pl.span_index)
                                      : pick_kernel<false, kCd>(pl.kh, pl.span_index))
+                  : pl.wide   ? pick_wide(pl.kh, pl.span_index)
                               : (f32 ? pick_kernel<true, kFwd>(pl.kh, pl.span_index)
                                      : pick_kernel<false, kFwd>(pl.kh, pl.span_index));
-    hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(direct ? 64 : chunk_dir ? kCdThreads : kThreads), 0,
+    const int threads = direct ? 64 : chunk_dir ? kCdThreads : pl.wide ? 64 * kWideWaves : kThreads;
+    hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(threads), 0,
                        (hipStream_t)stream, p);
     if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
     return HYENA_OK;

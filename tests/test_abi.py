@@ -94,22 +94,24 @@ def test_binding_raises_with_status():
 
 
 @pytest.mark.parametrize("B,L,D,l_h,dtype,span,expect_span", [
-    # SE (l_h <= 33) in bf16: 4 chunks while that grid has at most 2048
-    # workgroups, else 2
-    (1, 8192, 4096, 7, 0, 0, 4), (1, 16384, 4096, 7, 0, 0, 4), (1, 32768, 4096, 7, 0, 0, 2),
-    (4, 8192, 4096, 33, 0, 0, 2), (1, 8192, 4096, 7, 1, 0, 2), (1, 8192, 4096, 128, 0, 0, 8),
+    # SE (l_h <= 33) in bf16: 256-channel slabs, spans up to 8 chunks while
+    # the grid keeps at least 256 workgroups
+    (1, 8192, 4096, 7, 0, 0, 8), (1, 16384, 4096, 7, 0, 0, 8), (1, 4096, 4096, 7, 0, 0, 4),
+    (1, 2048, 4096, 7, 0, 0, 2), (1, 1024, 4096, 7, 0, 0, 1), (4, 8192, 4096, 33, 0, 0, 8),
+    (1, 8192, 4096, 7, 1, 0, 2), (1, 8192, 4096, 128, 0, 0, 8),
     (4, 32768, 4096, 128, 0, 0, 8), (1, 1024, 256, 7, 1, 0, 2),
     (1, 1000, 64, 7, 0, 3, 2), (1, 1000, 64, 7, 0, 7, 4), (1, 100, 64, 7, 0, 50, 2),
     (1, 1 << 20, 4096, 128, 0, 0, 8), (1, 1 << 20, 4096, 128, 1, 0, 4),
     (1, 1 << 20, 4096, 128, 0, 1000, 32), (1, 1 << 20, 4096, 128, 1, 1000, 4),
-    (1, 130, 64, 7, 0, 0, 2), (1, 60, 64, 128, 0, 0, 1), (1, 8192, 4096, 66, 0, 0, 4),
-    (1, 8192, 4096, 1, 0, 0, 4),
+    (1, 130, 64, 7, 0, 0, 1), (1, 60, 64, 128, 0, 0, 1), (1, 8192, 4096, 66, 0, 0, 4),
+    (1, 8192, 4096, 1, 0, 0, 8),
 ])
 def test_plan_split(B, L, D, l_h, dtype, span, expect_span):
     s, wgs = hc.plan(B, L, D, 16, l_h, dtype, span)
     assert s == expect_span
     chunks = -(-L // 64)
-    assert wgs == B * (-(-D // hc.SLAB)) * (-(-chunks // s))
+    slab = 256 if dtype == hc.DTYPE_BF16 and l_h <= 33 else hc.SLAB  # the 16-wave SE kernel
+    assert wgs == B * (-(-D // slab)) * (-(-chunks // s))
 
 
 @pytest.mark.parametrize("B,L,D,gs,l_h,dtype,span,expect_span", [

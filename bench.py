@@ -134,7 +134,7 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cop
     fetch, write = _counter_means(fetch_dir), _counter_means(write_dir)
     layers = {}
     for name, kib in fetch.items():
-        m = re.search(r"hyena_fwd_kernel<false, (\d+), (\d+), (\d+)(?:, false, false)?>", name)
+        m = re.search(r"hyena_fwd_kernel<false, (\d+), (\d+), (\d+)(?:, false, false(?:, \d+)?)?>", name)
         if not m:
             continue
         kh = int(m.group(1))

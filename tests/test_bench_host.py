@@ -14,7 +14,7 @@ import bench
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 MR = "hyena_fwd_kernel<false, 4, 2, 8, false, false>(Params)"
-SE = "hyena_fwd_kernel<false, 1, 2, 4, false, false>(Params)"
+SE = "hyena_fwd_kernel<false, 1, 1, 8, false, false, 16>(Params)"
 COPY = "__amd_rocclr_copyBuffer"
 
 

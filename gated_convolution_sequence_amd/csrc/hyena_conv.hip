@@ -20,8 +20,11 @@
 //     gathered from the filter by the difference of its row and column index.
 //
 // gfx950 mapping (l_b = 64 rows, one 16-channel group per wave):
-//   * A workgroup of 8 waves owns a slab of 128 channels (8 groups of 16)
-//     and a span of consecutive 64-row chunks of one batch row, plus the
+//   * A workgroup of 8 waves owns a slab of 128 channels (8 groups of 16);
+//     for bf16 filters of at most 33 taps, 16 waves own 256 channels, so
+//     each row segment it reads is 512 bytes (HBM serves wider per-workgroup
+//     row segments faster).  It walks a span of consecutive 64-row chunks
+//     of one batch row, plus the
 //     32*KH rows before the span (the history its first chunks need), which
 //     it reads last (see the walk order below).
 //   * k and v arrive through 16-byte buffer loads, coalesced along channels;

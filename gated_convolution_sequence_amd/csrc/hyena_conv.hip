@@ -209,7 +209,9 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     constexpr int NH = HROWS / M::ROWS;                   // history fragments
     constexpr int NX = NH + M::FPC;                       // fragments one chunk reads
     constexpr int ST_PITCH = SLAB * 4;                    // fp32 staging row, bytes
-    constexpr int kStBufs = KH >= HYENA_ST2_MIN_KH ? 2 : 1;
+    constexpr int kStBufs = KH >= HYENA_ST2_MIN_KH && NW == kWaves ? 2 : 1;
+    // 16-wave form with history: Toeplitz fragments built per use, not kept
+    constexpr bool FLY = !F32 && NW > kWaves && KH >= 2;
 
     // x = k*v of the current chunk (row-major, swizzled), the fp32
     // accumulators of the current chunk (and, with two staging buffers, of the
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     // step kappa depends only on their distance: bf16 e = nt - 2 kappa (units
     // of 16 rows), fp32 e4 = 4 nt - kappa (units of 4 rows).
     constexpr int NE = F32 ? 16 + NH : 4 + 2 * KH;
-    frag F[NE];
+    frag F[FLY ? 1 : NE];
     const int ch = w * kTile + n16;
     int rd_base;
     if constexpr (F32) {
@@ -389,10 +391,12 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
         for (int i = 0; i < NE; ++i) F[i] = hs[w][4 * (i - 3) + n16 - q4 + kHOff];
         rd_base = q4 * T::PITCH + ((((ch >> 2) ^ (4 * q4))) << 4) + ((ch & 3) << 2);
     } else {
+        if constexpr (!FLY) {
 #pragma unroll
-        for (int e = 0; e < NE; ++e)
+            for (int e = 0; e < NE; ++e)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) F[e][j] = (__bf16)hs[w][16 * e + n16 - 8 * q4 - j + kHOff];
+                for (int j = 0; j < 8; ++j) F[e][j] = (__bf16)hs[w][16 * e + n16 - 8 * q4 - j + kHOff];
+        }
         // channel 16w + n16, rows 8 q4 + j (+ 32 kappa); their swizzle is 2 q4
         rd_base = (8 * q4) * T::PITCH + ((((ch >> 3) ^ (2 * q4))) << 4) + ((ch & 7) << 1);
     }
@@ -420,6 +424,26 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     // compute item j (chunk c) from its NX fragments Xc (history first):
     // the four 16-row output tiles into registers
     auto mma = [&](const frag *Xc, f32x4_t *acc) {
+        if constexpr (FLY) {
+            // e descending: for each output tile the input steps run in the
+            // same (ascending) order as below
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int e = NE - 1; e >= 0; --e) {
+                frag fe;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) fe[j] = (__bf16)hs[w][16 * e + n16 - 8 * q4 - j + kHOff];
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    if ((nt - e) % 2 != 0) continue;
+                    const int kk = NH + (nt - e) / 2;  // e = nt - 2 (kk - NH)
+                    if (kk < 0 || kk >= NX) continue;
+                    acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Xc[kk], fe, acc[nt], 0, 0, 0);
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
             acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -1930,22 +1954,35 @@ constexpr typename FnType<F32, Fam>::type kernel_of() {
         return hyena_fwd_cd_kernel<F32, KH>;
 }
 
-// The bf16 forward for KH <= 1 (filters of at most 33 taps) with 16 waves:
-// 256-channel slabs, so every row segment a workgroup reads or writes is
-// 512 contiguous bytes.  On MI355X a plain three-read, one-write streaming
-// kernel with 256 workgroups measured 2.4, 5.0, 5.5 and 6.1 TB/s for 64-,
-// 128-, 256- and 512-byte row segments per workgroup (B=1, L=8192, D=4096,
-// bf16).  One chunk in flight keeps it within 128 VGPRs (two spill).
+// The bf16 forward with 16 waves: 256-channel slabs, so every row segment a
+// workgroup reads or writes is 512 contiguous bytes.  On MI355X a plain
+// three-read, one-write streaming kernel with 256 workgroups measured 2.4,
+// 5.0, 5.5 and 6.1 TB/s for 64-, 128-, 256- and 512-byte row segments per
+// workgroup (B=1, L=8192, D=4096, bf16).  A 16-wave workgroup has 128 VGPRs
+// per lane: one chunk in flight (two spill), and for KH >= 2 the Toeplitz
+// fragments are built from the staged taps right before their MFMAs instead
+// of being kept (48 VGPRs for KH = 4), with one staging tile (two would not
+// fit the LDS).
 constexpr int kWideWaves = 16;
 constexpr int kWidePrefetch = 1;
 constexpr int64_t kWideWorkgroups = 256;  // one 16-wave workgroup per CU (112 KiB of LDS)
+// Longer filters take 16 waves from this many workgroups (8 per CU) on.
+// Measured on MI355X, l_h = 128, D = 4096, per launch: B=1, L=32768
+// 185 us with 8 waves against 194 with 16; L=65536 402 against 390;
+// B=4, L=32768 805 against 764.
+constexpr int64_t kWideMrWorkgroups = 2048;
 template <int KH, int... Ss> KernelFn wide_entry(int si, std::integer_sequence<int, Ss...>) {
     static constexpr KernelFn fns[] = {hyena_fwd_kernel<false, KH, kWidePrefetch, kSpans[Ss], false, false, kWideWaves>...};
     return fns[si];
 }
 KernelFn pick_wide(int kh, int si) {
-    return kh == 0 ? wide_entry<0>(si, std::make_integer_sequence<int, kNumSpans>{})
-                   : wide_entry<1>(si, std::make_integer_sequence<int, kNumSpans>{});
+    switch (kh) {
+    case 0: return wide_entry<0>(si, std::make_integer_sequence<int, kNumSpans>{});
+    case 1: return wide_entry<1>(si, std::make_integer_sequence<int, kNumSpans>{});
+    case 2: return wide_entry<2>(si, std::make_integer_sequence<int, kNumSpans>{});
+    case 3: return wide_entry<3>(si, std::make_integer_sequence<int, kNumSpans>{});
+    default: return wide_entry<4>(si, std::make_integer_sequence<int, kNumSpans>{});
+    }
 }
 
 template <bool F32, int Fam, int KH, int... Ss>
@@ -1992,7 +2029,13 @@ int make_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, 
     const int64_t eb = dtype == HYENA_DTYPE_F32 ? 4 : 2;
     pl->kh = (int)((l_h - 1 + 31) / 32);
     pl->n_chunks = (L + kChunk - 1) / kChunk;
-    pl->wide = family == kFwd && dtype == HYENA_DTYPE_BF16 && pl->kh <= 1;
+    // 16 waves: always for SE; for longer filters once the grid has
+    // kWideMrWorkgroups workgroups at 8-chunk spans (below that the 8-wave
+    // kernel, which overlaps each chunk's epilogue with the next chunk's
+    // MFMAs in a second staging tile, is faster)
+    pl->wide = family == kFwd && dtype == HYENA_DTYPE_BF16 &&
+               (pl->kh <= 1 || B * ((D + kTile * kWideWaves - 1) / (kTile * kWideWaves)) *
+                                       ((pl->n_chunks + 7) / 8) >= kWideMrWorkgroups);
     pl->n_slabs = (D + (pl->wide ? kTile * kWideWaves : kSlab) - 1) / (pl->wide ? kTile * kWideWaves : kSlab);
     if (group_size % kTile != 0) return HYENA_ERR_UNSUPPORTED;
     if (D > INT32_MAX / 16) return HYENA_ERR_UNSUPPORTED;
@@ -2009,7 +2052,7 @@ int make_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, 
         want = pl->kh <= 1 ? 2 : 2 * pl->kh;
         if (pl->wide) {
             want = 8;
-            while (want > 1 && B * pl->n_slabs * ((pl->n_chunks + want - 1) / want) < kWideWorkgroups) want /= 2;
+            while (pl->kh <= 1 && want > 1 && B * pl->n_slabs * ((pl->n_chunks + want - 1) / want) < kWideWorkgroups) want /= 2;
         }
     }
     // the filter-gradient kernel writes one partial row per span: longer

@@ -110,7 +110,10 @@ def test_plan_split(B, L, D, l_h, dtype, span, expect_span):
     s, wgs = hc.plan(B, L, D, 16, l_h, dtype, span)
     assert s == expect_span
     chunks = -(-L // 64)
-    slab = 256 if dtype == hc.DTYPE_BF16 and l_h <= 33 else hc.SLAB  # the 16-wave SE kernel
+    # the 16-wave kernel: bf16 SE always, longer filters from 2048 workgroups
+    # at 8-chunk spans
+    wide = dtype == hc.DTYPE_BF16 and (l_h <= 33 or B * (-(-D // 256)) * (-(-chunks // 8)) >= 2048)
+    slab = 256 if wide else hc.SLAB
     assert wgs == B * (-(-D // slab)) * (-(-chunks // s))
 
 

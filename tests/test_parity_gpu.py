@@ -5,6 +5,8 @@ compares with oracle.conv_fwd_ref on the very same inputs, using the bar in
 tests/gpu_util.py (spec gate plus an elementwise rounding bound), or
 bitwise where every intermediate is exactly representable.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -234,6 +236,18 @@ def test_mr_b4_sampled():
     q, k, v, h = make_inputs(w, DEV)
     y = run(q, k, v, h, w.group_size)
     _sampled_checks(w, q, k, v, h, y, n_groups=4, seed=4)
+
+
+def test_wide_mr_ragged_partial_slab_sampled():
+    """The 16-wave form of a 128-tap filter (taken from 2048 workgroups at
+    8-chunk spans on) on a ragged length and a partial 256-channel slab."""
+    w = dataclasses.replace(WORKLOADS["mr"], name="mr_wide_edge", B=2, L=262081, D=272)
+    span, wgs = hc.plan(w.B, w.L, w.D, w.group_size, w.l_h)
+    assert (span, wgs) == (8, 2 * 2 * 512)  # 2 slabs of 256 channels, 512 spans
+    log("mr_wide_edge: generate")
+    q, k, v, h = make_inputs(w, DEV)
+    y = run(q, k, v, h, w.group_size)
+    _sampled_checks(w, q, k, v, h, y, n_groups=2, seed=6)
 
 
 def test_long_stripe_sampled():

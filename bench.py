@@ -17,7 +17,10 @@ Reported (one JSON line):
                can be reported; `kernel` names it): algorithmic bytes per
                launch (q, k, v read once, y written once: 8 B per
                token*channel) / its mean launch time from HIP events on the
-               launch stream, against the 8 TB/s HBM3E peak; `traffic` is the
+               launch stream (one event per kernel boundary in every step of
+               an evented pass of max(K, 20) steps right after the timed
+               region; the timed region itself carries events in every 5th
+               step, reported beside), against the 8 TB/s HBM3E peak; `traffic` is the
                measured HBM bytes per launch from the committed rocprofv3
                counter summary, or null if the kernel source changed since;
   layers       the same figures for each layer's kernel;
@@ -26,12 +29,15 @@ Reported (one JSON line):
                GEMM kernel;
   long_filter  a filter as long as the sequence (the FFT path);
   backward     dq, dk, dv and dh of each layer;
-  stream_reference  torch's addcmul and a copy over the same bytes (the
-               attainable streaming rate on the box);
+  stream_reference  a hand-written read-3/write-1 streaming kernel with the
+               forward's access pattern (256- and 512-byte row segments; the
+               attainable rate on the box), torch's addcmul and a copy over the
+               same bytes; each layer's `frac_of_attainable` divides by the best;
   cpu_baseline the fp64 oracle on the host cores over the full step's inputs;
   naive_conv1d the same step written with torch's depthwise F.conv1d (bf16),
                with and without the layout permutes;
-  batched_mr   (with --batched) the MR layer at B=4, L=32768;
+  extra_shapes the MR layer at B=4, L=32768, and the 2^20-row stripe (SE then
+               MR; step time and per-layer launches), unless --skip-extra-shapes;
   halo_shard   (with --halo) the second half of the MR layer through the
                history-prefix entry point, beside the plain forward.
 Input sets rotate over ``--sets`` copies per layer so that no launch finds its
@@ -56,6 +62,7 @@ METRIC = "Hyena-SE/MR fwd: G(token·channel)/s and % of HBM-bandwidth roofline, 
 UNIT = "G(token·channel)/s"
 HBM_PEAK_GBS = 8000.0
 EVENT_EVERY = 5          # per-kernel events in every 5th timed step (coprime with the input sets)
+MIN_EVENT_STEPS = 20     # the evented pass after the timed region has at least this many steps
 KERNEL_SRC = os.path.join(ROOT, "gated_convolution_sequence_amd", "csrc", "hyena_conv.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -82,12 +89,13 @@ def parse():
     ap.add_argument("--skip-long-filter", action="store_true")
     ap.add_argument("--halo", action="store_true",
                     help="also time one shard of the MR layer through hyena_conv_fwd_halo (the second half "
-                         "of the sequence with its l_h - 1 prefix rows); off by default for the same "
-                         "reason as --batched")
-    ap.add_argument("--batched", action="store_true",
-                    help="also time the batched MR configuration (B=4, L=32768); off by default because "
-                         "its launches share the kernel instance of the B=1 MR layer, which would mix "
-                         "two shapes in a profiler's per-kernel statistics of the default command")
+                         "of the sequence with its l_h - 1 prefix rows); off by default because its "
+                         "launches share the MR layer's kernel instance")
+    ap.add_argument("--skip-extra-shapes", action="store_true",
+                    help="leave out the batched MR layer (B=4, L=32768) and the 2^20-row stripe; their "
+                         "launches share kernel instances with the default step's layers, so a "
+                         "profiler's per-kernel statistics of the step need this flag")
+    ap.add_argument("--skip-stream-reference", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="rough CPU budget of the oracle baseline")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -153,9 +161,9 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cop
            "layers": layers,
            "commands": [
                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- "
-               "python3 bench.py --steps 8 --warmup 2 --skip-cpu-baseline --skip-naive",
+               "python3 bench.py --steps 8 --warmup 2 --skip-cpu-baseline --skip-naive --skip-extra-shapes",
                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- "
-               "python3 bench.py --steps 8 --warmup 2 --skip-cpu-baseline --skip-naive",
+               "python3 bench.py --steps 8 --warmup 2 --skip-cpu-baseline --skip-naive --skip-extra-shapes",
                "rocprofv3 --pmc FETCH_SIZE ... -- python3 bench.py --calibrate-copy-mib %d" % copy_mib,
                "rocprofv3 --pmc WRITE_SIZE ... -- python3 bench.py --calibrate-copy-mib %d" % copy_mib]}
     with open(TRAFFIC_FILE, "w") as f:
@@ -276,10 +284,20 @@ def main():
 
     elems_step = sum(w.elems for w in layers)
     value = elems_step / (wall / K) / 1e9
+    timed_ms = [[hip_ev.elapsed_ms(ev[i][li], ev[i][li + 1]) for i in sampled] for li in range(len(layers))]
+
+    # ---- evented pass: the same steps with one event per kernel boundary in
+    # every step (at least MIN_EVENT_STEPS), after the timed region so that
+    # its wall clock carries no event records beyond the sampled ones
+    n_ev = max(K, MIN_EVENT_STEPS)
+    ev2 = [[hip_ev.create() for _ in range(len(layers) + 1)] for _ in range(n_ev)]
+    for i in range(n_ev):
+        step(K + i, ev2[i])
+    torch.cuda.synchronize()
 
     layer_stats = {}
     for li, w in enumerate(layers):
-        ms = [hip_ev.elapsed_ms(ev[i][li], ev[i][li + 1]) for i in sampled]
+        ms = [hip_ev.elapsed_ms(e[li], e[li + 1]) for e in ev2]
         mean_ms = sum(ms) / len(ms)
         alg_bytes = w.elems * (4 * (2 if w.dtype == "bf16" else 4))
         achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
@@ -293,7 +311,9 @@ def main():
             "G_tok_ch_per_s": round(w.elems / (mean_ms * 1e-3) / 1e9, 2),
             "alg_bytes": alg_bytes, "achieved_GBs": round(achieved, 1),
             "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
-            "span_chunks": span, "workgroups": wgs, "event_samples": len(sampled),
+            "span_chunks": span, "workgroups": wgs, "event_samples": len(ms),
+            "timed_region_mean_us": round(sum(timed_ms[li]) / len(timed_ms[li]) * 1e3, 2),
+            "timed_region_event_samples": len(timed_ms[li]),
         }
     dom = max(layer_stats, key=lambda n: layer_stats[n]["mean_us"])
     d = layer_stats[dom]
@@ -301,7 +321,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": d["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(d["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "hyena_fwd_kernel<bf16, KH=%d> (%s layer)" % (d["kernel_KH"], dom),
-                "alg_bytes_per_launch": d["alg_bytes"], "mean_launch_us": d["mean_us"]}
+                "alg_bytes_per_launch": d["alg_bytes"], "mean_launch_us": d["mean_us"],
+                "event_samples": d["event_samples"]}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": UNIT, "n_gpus": 1, "steps": K,
@@ -328,14 +349,19 @@ def main():
     if not args.skip_backward:
         out["backward"] = backward_rates(layers, sets, stream, max(5, K // 8))
 
-    # ---- the batched MR configuration (B=4, L=32768), outside the step ---
-    if args.batched:
-        out["batched_mr"] = batched_mr_rate(stream, max(10, K // 10))
     if args.halo:
         out["halo_shard"] = halo_shard_rate(layers[-1], sets[-1], stream, max(20, K // 4))
 
     # ---- attainable streaming rate on this GPU (same bytes, no convolution)
-    out["stream_reference"] = stream_reference(layers[-1], sets[-1], stream, max(10, K // 4))
+    if not args.skip_stream_reference:
+        ref = stream_reference(layers[-1], sets[-1], stream, max(MIN_EVENT_STEPS, K))
+        out["stream_reference"] = ref
+        att = ref.get("attainable_GBs")
+        if att:
+            for st in layer_stats.values():
+                st["frac_of_attainable"] = round(st["achieved_GBs"] / att, 4)
+            roofline["frac_of_attainable"] = round(d["achieved_GBs"] / att, 4)
+
 
     # ---- naive baseline: torch depthwise conv1d ---------------------------
     if not args.skip_naive:
@@ -346,6 +372,14 @@ def main():
         out["cpu_baseline"] = cpu_baseline(layers, sets, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
+    # ---- the other workload shapes: batched MR and the 2^20-row stripe -----
+    if not args.skip_extra_shapes and args.workload == "stripe_8k":
+        sets.clear()  # the step's inputs are no longer needed
+        torch.cuda.empty_cache()
+        out["extra_shapes"] = {
+            "mr_b4": batched_mr_rate(stream, max(MIN_EVENT_STEPS, K)),
+            "long_stripe": long_stripe_rate(stream, max(10, K // 2)),
+        }
     print(json.dumps(out), flush=True)
 
 
@@ -487,10 +521,42 @@ def halo_shard_rate(w, per, stream, reps):
     return res
 
 
+def _evented_launches(call, reps, stream):
+    """Per-launch durations (ms) of ``reps`` calls, each between two fence-free
+    HIP events on the launch stream, after three untimed calls."""
+    import torch
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    ev = HipEvents()
+    marks = [(ev.create(), ev.create()) for _ in range(reps)]
+    for i, (e0, e1) in enumerate(marks):
+        ev.record(e0, stream)
+        call(i)
+        ev.record(e1, stream)
+    torch.cuda.synchronize()
+    return [ev.elapsed_ms(e0, e1) for e0, e1 in marks]
+
+
+def _launch_stats(w, ms):
+    mean_ms = sum(ms) / len(ms)
+    alg = 8 * w.elems
+    import gated_convolution_sequence_amd as hc
+    span, wgs = hc.plan(w.B, w.L, w.D, w.group_size, w.l_h, hc.DTYPE_BF16)
+    return {"B": w.B, "L": w.L, "D": w.D, "group_size": w.group_size, "l_h": w.l_h,
+            "mean_us": round(mean_ms * 1e3, 1), "median_us": round(statistics.median(ms) * 1e3, 1),
+            "p10_us": round(sorted(ms)[len(ms) // 10] * 1e3, 1),
+            "p90_us": round(sorted(ms)[(9 * len(ms)) // 10] * 1e3, 1),
+            "G_tok_ch_per_s": round(w.elems / (mean_ms * 1e-3) / 1e9, 2),
+            "alg_bytes": alg, "achieved_GBs": round(alg / (mean_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "span_chunks": span, "workgroups": wgs, "event_samples": len(ms)}
+
+
 def batched_mr_rate(stream, reps):
     """The MR layer at B=4, L=32768, D=4096 (4 GiB of q, k, v and y per input
-    set; two sets alternate): mean launch time from fence-free HIP events
-    around each launch, and its fraction of the HBM peak at 8 B per
+    set; two sets alternate): per-launch durations from fence-free HIP events
+    around each launch, and the fraction of the HBM peak at 8 B per
     token*channel."""
     import torch
     import gated_convolution_sequence_amd as hc
@@ -502,27 +568,57 @@ def batched_mr_rate(stream, reps):
     def call(i):
         a, b, c, y = sets[i % 2]
         hc.conv_fwd(a, b, c, h, w.group_size, out=y, stream=stream)
-    for i in range(3):
-        call(i)
-    torch.cuda.synchronize()
-    ev = HipEvents()
-    marks = [(ev.create(), ev.create()) for _ in range(reps)]
-    for i, (e0, e1) in enumerate(marks):
-        ev.record(e0, stream)
-        call(i)
-        ev.record(e1, stream)
-    torch.cuda.synchronize()
-    ms = [ev.elapsed_ms(e0, e1) for e0, e1 in marks]
-    mean_ms = sum(ms) / len(ms)
-    alg = 8 * w.elems
-    span, wgs = hc.plan(w.B, w.L, w.D, w.group_size, w.l_h, hc.DTYPE_BF16)
-    res = {"B": w.B, "L": w.L, "D": w.D, "group_size": w.group_size, "l_h": w.l_h,
-           "mean_us": round(mean_ms * 1e3, 1), "median_us": round(statistics.median(ms) * 1e3, 1),
-           "G_tok_ch_per_s": round(w.elems / (mean_ms * 1e-3) / 1e9, 2),
-           "achieved_GBs": round(alg / (mean_ms * 1e-3) / 1e9, 1),
-           "hbm_frac": round(alg / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "span_chunks": span, "workgroups": wgs, "launches": reps}
+    res = _launch_stats(w, _evented_launches(call, reps, stream))
     del sets, q, k, v, h
+    torch.cuda.empty_cache()
+    return res
+
+
+def long_stripe_rate(stream, steps):
+    """The 2^20-row stripe (an SE layer, then an MR layer, B=1, D=4096; one
+    input set per layer, 32 GiB each, so nothing stays in a cache between
+    launches): the wall-clock time of ``steps`` steps between two device
+    synchronisations, and each layer's per-launch durations from fence-free
+    HIP events in every step."""
+    import torch
+    import gated_convolution_sequence_amd as hc
+    from workloads import WORKLOADS, make_inputs
+    ws = [WORKLOADS["long_se"], WORKLOADS["long_mr"]]
+    dev = torch.device("cuda:0")
+    data = []
+    for w in ws:
+        q, k, v, h = make_inputs(w, dev)
+        data.append((q, k, v, h, torch.empty_like(q)))
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        if events is not None:
+            hip_ev.record(events[0], stream)
+        for li, w in enumerate(ws):
+            q, k, v, h, y = data[li]
+            hc.conv_fwd(q, k, v, h, w.group_size, out=y, stream=stream)
+            if events is not None:
+                hip_ev.record(events[li + 1], stream)
+    hip_ev = HipEvents()
+    step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    evs = [[hip_ev.create() for _ in range(len(ws) + 1)] for _ in range(steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    res = {"workload": "long_se(B=1,L=1048576,D=4096,group_size=16,l_h=7) then "
+                       "long_mr(B=1,L=1048576,D=4096,group_size=16,l_h=128)",
+           "steps": steps, "ms_per_step": round(wall * 1e3, 3),
+           "value": round(sum(w.elems for w in ws) / wall / 1e9, 2), "unit": UNIT,
+           "hbm_frac_step": round(sum(8 * w.elems for w in ws) / wall / 1e9 / HBM_PEAK_GBS, 4), "layers": {}}
+    for li, w in enumerate(ws):
+        res["layers"][w.name] = _launch_stats(w, [hip_ev.elapsed_ms(e[li], e[li + 1]) for e in evs])
+    del data
     torch.cuda.empty_cache()
     return res
 
@@ -645,16 +741,53 @@ def long_filter_rates(w, stream, reps):
     return res
 
 
+def _stream_ref_lib():
+    import ctypes
+    from gated_convolution_sequence_amd import _build
+    if not os.path.exists(_build.STREAM_REF_LIB):
+        _build.build_stream_ref()
+    lib = ctypes.CDLL(_build.STREAM_REF_LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.hyena_stream_read3_write1.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp]
+    lib.hyena_stream_read3_write1.restype = ctypes.c_int
+    return lib
+
+
 def stream_reference(w, per, stream, reps):
     """What plain streaming kernels reach on the same tensors and rotation.
 
-    torch.addcmul(q, k, v, out=y) reads three [B, L, D] tensors and writes one
-    (the operator's 8 bytes per token*channel in one fused elementwise kernel);
-    a device copy reads one and writes one.  Timed with HIP events around
-    ``reps`` back-to-back launches.
+    ``hip_read3_write1_*``: the hand-written kernel in csrc/stream_ref.hip,
+    y = q*k*v (three bf16 reads, one write: the operator's 8 bytes per
+    token*channel) with the grouped forward kernel's access pattern (16-byte
+    non-temporal buffer loads, row segments of 256 or 512 bytes per
+    workgroup, 8-chunk spans, two chunks in flight), for 8 and 16 waves per
+    workgroup.  Per-launch durations from fence-free HIP events around each
+    launch, as for the operator's layers; ``attainable_GBs`` is the best of
+    them.  torch's addcmul (same bytes) and a device copy (one read, one
+    write) are timed around ``reps`` back-to-back launches.
     """
     import torch
     res = {}
+    lib = _stream_ref_lib()
+    eb = 2 if w.dtype == "bf16" else 4
+    best = 0.0
+    if w.dtype == "bf16":
+        for waves, seg in ((8, 256), (8, 512), (16, 256), (16, 512)):
+            def call(i, waves=waves, seg=seg):
+                q, k, v, _, y = per[i % len(per)]
+                st = lib.hyena_stream_read3_write1(q.data_ptr(), k.data_ptr(), v.data_ptr(), y.data_ptr(),
+                                                   w.B, w.L, w.D, seg, waves, stream.cuda_stream)
+                if st != 0:
+                    raise RuntimeError("hyena_stream_read3_write1: %d" % st)
+            ms = _evented_launches(call, reps, stream)
+            mean_ms = sum(ms) / len(ms)
+            gbs = w.elems * eb * 4 / (mean_ms * 1e-3) / 1e9
+            best = max(best, gbs)
+            res["hip_read3_write1_seg%d_w%d" % (seg, waves)] = {
+                "mean_us": round(mean_ms * 1e3, 2), "median_us": round(statistics.median(ms) * 1e3, 2),
+                "GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "event_samples": len(ms)}
+        res["attainable_GBs"] = round(best, 1)
+        res["attainable_frac_of_peak"] = round(best / HBM_PEAK_GBS, 4)
     for name, fn, nbytes in (
             ("addcmul_read3_write1", lambda s: torch.addcmul(s[0], s[1], s[2], out=s[4]), 4),
             ("copy_read1_write1", lambda s: s[4].copy_(s[0]), 2)):
@@ -668,7 +801,7 @@ def stream_reference(w, per, stream, reps):
         e1.record(stream)
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
-        moved = w.elems * (2 if w.dtype == "bf16" else 4) * nbytes
+        moved = w.elems * eb * nbytes
         res[name] = {"us": round(us, 2), "GBs": round(moved / (us * 1e-6) / 1e9, 1),
                      "frac_of_peak": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     return res

@@ -18,7 +18,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libhyena_conv.so")
 
 BLOCK_LEN = 64
-SLAB = 128  # channels per workgroup of the library's kernels
+SLAB = 128  # channels per 8-wave workgroup of the grouped forward (the 16-wave form takes 256)
+WIDE_SLAB = 256
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 

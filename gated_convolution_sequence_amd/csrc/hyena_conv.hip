@@ -21,9 +21,10 @@
 //
 // gfx950 mapping (l_b = 64 rows, one 16-channel group per wave):
 //   * A workgroup of 8 waves owns a slab of 128 channels (8 groups of 16);
-//     for bf16 filters of at most 33 taps, 16 waves own 256 channels, so
-//     each row segment it reads is 512 bytes (HBM serves wider per-workgroup
-//     row segments faster).  It walks a span of consecutive 64-row chunks
+//     in bf16, 16 waves own 256 channels, so each row segment it reads is
+//     512 bytes (HBM serves wider per-workgroup row segments faster): always
+//     for filters of at most 33 taps, and for longer ones on grids of at
+//     least 2048 workgroups.  It walks a span of consecutive 64-row chunks
 //     of one batch row, plus the
 //     32*KH rows before the span (the history its first chunks need), which
 //     it reads last (see the walk order below).
@@ -2492,7 +2493,7 @@ const char *hyena_conv_strerror(int status) {
     case HYENA_ERR_FILTER_LEN: return "l_h must be in [1, 128]";
     case HYENA_ERR_ALIGN: return "q, k, v and out must be 16-byte aligned; h element aligned";
     case HYENA_ERR_ALIAS: return "out overlaps an input";
-    case HYENA_ERR_UNSUPPORTED: return "unsupported case (backward and history prefix need group_size a multiple of 16; rows must be a multiple of 16 bytes; or the shape is too large to address)";
+    case HYENA_ERR_UNSUPPORTED: return "unsupported case (off the 16-channel grouping: rows must be a multiple of 16 bytes, and the backward and history prefix take filters of at most 8 taps; long filters: D must be even and the transform at most 2^22 points; or the shape is too large to address)";
     case HYENA_ERR_LAUNCH: return "kernel launch failed";
     case HYENA_ERR_DTYPE: return "unknown dtype code";
     case HYENA_ERR_WORKSPACE: return "workspace missing or smaller than hyena_conv_bwd_workspace reports";

@@ -703,6 +703,14 @@ int fft_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, i
     if (group_size < 1 || D % group_size != 0) return HYENA_ERR_GROUP;
     if (l_h < 1) return HYENA_ERR_FILTER_LEN;
     if (D % 2 != 0) return HYENA_ERR_UNSUPPORTED;  // channels travel in pairs
+    // the kernels take the filter row pitch as a 32-bit count; the sequence
+    // must fit one transform (checked before L + taps - 1 is formed)
+    if (l_h > INT32_MAX || L > ((int64_t)1 << kFftMaxLogN)) return HYENA_ERR_UNSUPPORTED;
+    if (B > 0 && L > 0 && D > 0) {
+        const int64_t lim = INT64_MAX / 8;  // element count times 4-byte elements, with room
+        if (L > lim / D || B > lim / (L * D)) return HYENA_ERR_SHAPE;
+    }
+    if (l_h > (INT64_MAX / 8) / (D / group_size > 0 ? D / group_size : 1)) return HYENA_ERR_SHAPE;
     const int64_t taps = l_h < L ? l_h : L;         // taps past row L - 1 never contribute
     const int logN = ilog2(L + taps - 1 > 4 ? L + taps - 1 : 4);
     if (logN > kFftMaxLogN) return HYENA_ERR_UNSUPPORTED;
@@ -737,6 +745,8 @@ int fft_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, i
         return HYENA_ERR_UNSUPPORTED;
     const int64_t Gp = G + (G & 1);
     pl->ws_pairs = B * (D / 2) > Gp / 2 ? B * (D / 2) : Gp / 2;
+    // N (ws_pairs + Gp) complex values of 8 bytes must not overflow
+    if (pl->ws_pairs > (INT64_MAX / 16) / pl->N - Gp) return HYENA_ERR_SHAPE;
     pl->hs_bytes = pl->N * Gp * (int64_t)sizeof(float2);
     pl->ws_bytes = pl->N * pl->ws_pairs * (int64_t)sizeof(float2) + pl->hs_bytes;
     return HYENA_OK;

@@ -76,6 +76,38 @@ def test_host_validation_rejects_before_any_gpu_call(kw, code):
     assert _call(**kw) == code
 
 
+def _call_named(name, q=P["q"], k=P["k"], v=P["v"], h=P["h"], B=1, L=128, D=64, gs=16, l_h=7,
+                out=P["out"]):
+    return getattr(hc.lib(), name)(q, k, v, h, B, L, D, gs, l_h, out, None)
+
+
+@pytest.mark.parametrize("name,eb", [("hyena_conv_fwd", 2), ("hyena_conv_fwd_f32", 4)])
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(h=None), -1),
+    (dict(out=None), -1),
+    (dict(B=-1), -2), (dict(L=-5), -2), (dict(D=-16), -2), (dict(L=1 << 40, D=1 << 30), -2),
+    (dict(gs=0), -3), (dict(D=64, gs=48), -3),
+    (dict(l_h=0), -4), (dict(l_h=129), -4),
+    (dict(q=P["q"] + 8), -5), (dict(out=P["out"] + 4), -5),
+    (dict(out=P["q"]), -6), (dict(out=P["k"] + 64), -6), (dict(out=P["h"] - 64), -6),
+])
+def test_named_forward_entry_points_validate_on_host(name, eb, kw, code):
+    """The two entry points with the operator's own signature (bf16 and fp32)
+    run the same host checks as the explicit-dtype one."""
+    assert _call_named(name, **kw) == code
+
+
+def test_named_forward_entry_points_check_their_own_element_size():
+    # a filter aligned for bf16 but not for fp32 is refused only by the fp32 entry
+    assert _call_named("hyena_conv_fwd_f32", h=P["h"] + 2) == -5
+    assert _call_named("hyena_conv_fwd", h=P["h"] + 1) == -5
+    # rows of 24 bytes (12 bf16 or 6 fp32 channels) are not a multiple of 16 off the tile
+    assert _call_named("hyena_conv_fwd", D=12, gs=1) == -7
+    assert _call_named("hyena_conv_fwd_f32", D=6, gs=3) == -7
+    for name in ("hyena_conv_fwd", "hyena_conv_fwd_f32"):
+        assert _call_named(name, q=None, k=None, v=None, h=None, out=None, B=0) == 0
+
+
 def test_empty_problems_are_noops_even_with_null_pointers():
     for B, L, D in [(0, 10, 16), (1, 0, 16), (1, 10, 0)]:
         assert _call(q=None, k=None, v=None, h=None, out=None, B=B, L=L, D=D) == 0
@@ -113,7 +145,7 @@ def test_plan_split(B, L, D, l_h, dtype, span, expect_span):
     # the 16-wave kernel: bf16 SE always, longer filters from 2048 workgroups
     # at 8-chunk spans
     wide = dtype == hc.DTYPE_BF16 and (l_h <= 33 or B * (-(-D // 256)) * (-(-chunks // 8)) >= 2048)
-    slab = 256 if wide else hc.SLAB
+    slab = hc.WIDE_SLAB if wide else hc.SLAB
     assert wgs == B * (-(-D // slab)) * (-(-chunks // s))
 
 
@@ -273,3 +305,19 @@ def test_long_filter_workspace_size():
     assert hc.long_workspace_bytes(0, 8192, 4096, 16, 8192) == 0
     with pytest.raises(hc.HyenaError):
         hc.long_workspace_bytes(1, 100, 7, 1, 10)  # odd D
+
+
+def test_long_filter_plan_rejects_unaddressable_sizes():
+    """Filter lengths past a 32-bit row pitch, element counts past 2^60 and
+    workspace sizes past 2^63 bytes are refused on the host."""
+    n = ctypes.c_int64(-1)
+    ws = lambda B, L, D, gs, l_h: hc.lib().hyena_conv_fwd_long_workspace(B, L, D, gs, l_h, hc.DTYPE_BF16,
+                                                                         ctypes.byref(n))
+    assert ws(1, 100, 64, 16, (1 << 31)) == -7          # l_h past a 32-bit pitch
+    assert ws(1, 100, 64, 16, (1 << 31) - 1) == 0       # (taps past L never contribute)
+    assert ws(1 << 40, 1 << 20, 1 << 20, 16, 7) == -2   # B L D overflows
+    assert ws(1, 1 << 62, 64, 16, 7) == -7              # longer than one transform
+    assert ws(1 << 30, 1, (1 << 30) - 2, 1, 1) == -2    # workspace bytes overflow
+    assert ws(1, 100, (1 << 30) - 2, 1, (1 << 31) - 1) == -2  # G l_h taps overflow
+    assert _long(l_h=1 << 31) == -7
+    assert _long(B=1 << 40, L=1 << 20, D=1 << 20) == -2

@@ -27,14 +27,14 @@ STATUS = {
     0: "HYENA_OK", -1: "HYENA_ERR_NULL", -2: "HYENA_ERR_SHAPE", -3: "HYENA_ERR_GROUP",
     -4: "HYENA_ERR_FILTER_LEN", -5: "HYENA_ERR_ALIGN", -6: "HYENA_ERR_ALIAS",
     -7: "HYENA_ERR_UNSUPPORTED", -8: "HYENA_ERR_LAUNCH", -9: "HYENA_ERR_DTYPE",
-    -10: "HYENA_ERR_WORKSPACE",
+    -10: "HYENA_ERR_WORKSPACE", -11: "HYENA_ERR_SCRATCH",
 }
 
 # Every symbol include/hyena_conv.h declares.
 EXPORTS = ("hyena_conv_fwd", "hyena_conv_fwd_f32", "hyena_conv_fwd_ex", "hyena_conv_fwd_halo",
            "hyena_conv_bwd", "hyena_conv_bwd_workspace", "hyena_conv_fwd_long",
            "hyena_conv_fwd_long_workspace", "hyena_conv_plan", "hyena_conv_strerror",
-           "hyena_conv_block_len")
+           "hyena_conv_block_len", "hyena_conv_bwd_noalloc", "hyena_conv_scratch_bytes")
 
 
 class HyenaError(RuntimeError):
@@ -70,6 +70,11 @@ def lib() -> ctypes.CDLL:
         L.hyena_conv_bwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp,
                                      vp, i64, ctypes.c_int, vp]
         L.hyena_conv_bwd.restype = ctypes.c_int
+        L.hyena_conv_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp,
+                                             vp, ctypes.c_int, vp]
+        L.hyena_conv_bwd_noalloc.restype = ctypes.c_int
+        L.hyena_conv_scratch_bytes.argtypes = []
+        L.hyena_conv_scratch_bytes.restype = i64
         L.hyena_conv_bwd_workspace.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                                ctypes.POINTER(i64)]
         L.hyena_conv_bwd_workspace.restype = ctypes.c_int

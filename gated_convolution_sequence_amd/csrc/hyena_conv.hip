@@ -54,6 +54,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -2169,6 +2170,46 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// Fixed device scratch of the no-allocation backward: the partial filter
+// gradients of pass 1 (one row of l_h floats per batch row, span and
+// 16-channel tile, or per channel off the tile).  Every device the library
+// runs on holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address is
+// looked up once per device, with that device current, and only that
+// address is used from then on.
+constexpr int64_t kScratchBytes = (int64_t)16 << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The scratch array's address on the device `stream` belongs to (the
+// current device for the null stream), or null if HIP reports an error.
+void *scratch_on_stream_device(void *stream) {
+    int dev = -1;
+    if (stream) {
+        hipDevice_t d;
+        if (hipStreamGetDevice((hipStream_t)stream, &d) != hipSuccess) return nullptr;
+        dev = (int)d;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+        void *ptr = nullptr;
+        const hipError_t rc = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return nullptr;
+        if (rc != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -2304,10 +2345,14 @@ int hyena_conv_bwd_workspace(int64_t B, int64_t L, int64_t D, int64_t group_size
     return dh_plan(B, L, D, group_size, l_h, dtype, &pl, bytes_out);
 }
 
-int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, const void *dy,
-                   int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, void *dq,
-                   void *dk, void *dv, float *dh, void *workspace, int64_t workspace_bytes,
-                   int dtype, void *stream) {
+// The backward of both entry points.  `scratch` set: the partial filter
+// gradients go to this library's fixed device array instead of `workspace`
+// (which is then ignored); its address on the stream's device is looked up
+// only after every host check has passed.
+static int bwd_entry(const void *q, const void *k, const void *v, const void *h, const void *dy,
+                     int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, void *dq,
+                     void *dk, void *dv, float *dh, void *workspace, int64_t workspace_bytes,
+                     int dtype, void *stream, bool scratch) {
     int st = check_sizes(B, L, D, group_size, l_h, dtype);
     if (st != HYENA_OK) return st;
     if (!q || !k || !v || !h || !dy) return HYENA_ERR_NULL;
@@ -2320,6 +2365,7 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
     if (dq) mis |= (uintptr_t)dq;
     if (dk) mis |= (uintptr_t)dk | (uintptr_t)dv;
     if (mis & 15u) return HYENA_ERR_ALIGN;
+    if (scratch) workspace = nullptr;
     if (((uintptr_t)h & (eb - 1)) || ((uintptr_t)dh & 3u) || ((uintptr_t)workspace & 15u))
         return HYENA_ERR_ALIGN;
     // every output and the workspace are disjoint from every input and
@@ -2341,7 +2387,15 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
         for (int j = i + 1; j < 5; ++j)
             if (out[j] && overlaps(out[i], out_n[i], out[j], out_n[j])) return HYENA_ERR_ALIAS;
     }
-    if (dh && (!workspace || workspace_bytes < ws_need)) return HYENA_ERR_WORKSPACE;
+    if (scratch) {
+        if (dh && ws_need > kScratchBytes) return HYENA_ERR_SCRATCH;
+        if (dh && ws_need > 0) {
+            workspace = scratch_on_stream_device(stream);
+            if (!workspace) return HYENA_ERR_LAUNCH;
+        }
+    } else if (dh && (!workspace || workspace_bytes < ws_need)) {
+        return HYENA_ERR_WORKSPACE;
+    }
     if (B == 0 || L == 0 || D == 0) {
         // no rows: dh is zero (D == 0: dh has no elements)
         const int64_t n = (int64_t)(dhbytes / sizeof(float));
@@ -2473,6 +2527,24 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, c
     return HYENA_OK;
 }
 
+int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h, const void *dy,
+                   int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, void *dq,
+                   void *dk, void *dv, float *dh, void *workspace, int64_t workspace_bytes,
+                   int dtype, void *stream) {
+    return bwd_entry(q, k, v, h, dy, B, L, D, group_size, l_h, dq, dk, dv, dh, workspace,
+                     workspace_bytes, dtype, stream, false);
+}
+
+int hyena_conv_bwd_noalloc(const void *q, const void *k, const void *v, const void *h,
+                           const void *dy, int64_t B, int64_t L, int64_t D, int64_t group_size,
+                           int64_t l_h, void *dq, void *dk, void *dv, float *dh, int dtype,
+                           void *stream) {
+    return bwd_entry(q, k, v, h, dy, B, L, D, group_size, l_h, dq, dk, dv, dh, nullptr, 0, dtype,
+                     stream, true);
+}
+
+int64_t hyena_conv_scratch_bytes(void) { return kScratchBytes; }
+
 int hyena_conv_fwd(const void *q, const void *k, const void *v, const void *h, int64_t B, int64_t L,
                    int64_t D, int64_t group_size, int64_t l_h, void *out, void *stream) {
     return hyena_conv_fwd_ex(q, k, v, h, B, L, D, group_size, l_h, out, HYENA_DTYPE_BF16, 0, stream);
@@ -2497,6 +2569,7 @@ const char *hyena_conv_strerror(int status) {
     case HYENA_ERR_LAUNCH: return "kernel launch failed";
     case HYENA_ERR_DTYPE: return "unknown dtype code";
     case HYENA_ERR_WORKSPACE: return "workspace missing or smaller than hyena_conv_bwd_workspace reports";
+    case HYENA_ERR_SCRATCH: return "the problem needs more scratch than the no-allocation entry point's fixed device array holds (hyena_conv_scratch_bytes)";
     default: return "unknown status";
     }
 }

@@ -48,7 +48,8 @@
  *
  * Ownership and asynchrony: every pointer is a DEVICE pointer owned by the
  * caller.  The library allocates no device memory and keeps no state between
- * calls.  Work is enqueued on
+ * calls (apart from the fixed scratch array of hyena_conv_bwd_noalloc, below,
+ * which is part of the loaded library).  Work is enqueued on
  * `stream` (a hipStream_t; NULL means the default stream) and the call
  * returns without waiting; the result is valid once the caller synchronises
  * that stream.  Calls on distinct streams are independent.
@@ -78,7 +79,8 @@ enum hyena_status {
     HYENA_ERR_UNSUPPORTED = -7, /* a case outside the kernels' reach (see "Grouping"), or a shape they cannot address */
     HYENA_ERR_LAUNCH = -8,      /* the HIP runtime reported an error at launch */
     HYENA_ERR_DTYPE = -9,       /* unknown element-type code */
-    HYENA_ERR_WORKSPACE = -10   /* workspace missing or too small */
+    HYENA_ERR_WORKSPACE = -10,  /* workspace missing or too small */
+    HYENA_ERR_SCRATCH = -11     /* more scratch than hyena_conv_bwd_noalloc's fixed array holds */
 };
 
 enum hyena_dtype {
@@ -152,6 +154,28 @@ int hyena_conv_bwd(const void *q, const void *k, const void *v, const void *h,
                    int64_t group_size, int64_t l_h, void *dq, void *dk,
                    void *dv, float *dh, void *workspace,
                    int64_t workspace_bytes, int dtype, void *stream);
+
+/* hyena_conv_bwd without a caller workspace and without any device
+ * allocation, for callers that cannot allocate (code being captured into a
+ * HIP graph, tight serving or training loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and bits as hyena_conv_bwd; the
+ * partial filter gradients go to a fixed device array of the library,
+ * hyena_conv_scratch_bytes() = 16 MiB, that every GPU the library runs on
+ * holds until the process ends (its address is looked up on the first call
+ * that needs it on a device).  A problem whose dh needs more than that
+ * (hyena_conv_bwd_workspace reports the size: 16 MiB is B = 4, L = 32768,
+ * D = 4096, 16-channel groups, l_h = 128) returns HYENA_ERR_SCRATCH before
+ * any HIP call.  The array is shared by every call on one GPU and every
+ * such call overwrites it before reading it: calls that may overlap in time
+ * on one GPU (other streams, other host threads) race on it and must be
+ * serialised by the caller.  Calls that do not compute dh do not touch it. */
+int hyena_conv_bwd_noalloc(const void *q, const void *k, const void *v, const void *h,
+                           const void *dy, int64_t B, int64_t L, int64_t D,
+                           int64_t group_size, int64_t l_h, void *dq, void *dk,
+                           void *dv, float *dh, int dtype, void *stream);
+
+/* Size in bytes of hyena_conv_bwd_noalloc's fixed device array (16 MiB). */
+int64_t hyena_conv_scratch_bytes(void);
 
 /* Bytes of workspace hyena_conv_bwd needs to compute dh for these sizes
  * (written to *bytes_out).  Host only.  Returns a status. */

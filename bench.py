@@ -748,8 +748,10 @@ def _stream_ref_lib():
         _build.build_stream_ref()
     lib = ctypes.CDLL(_build.STREAM_REF_LIB)
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
-    lib.hyena_stream_read3_write1.argtypes = [vp, vp, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp]
+    lib.hyena_stream_read3_write1.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.hyena_stream_read3_write1.restype = ctypes.c_int
+    lib.hyena_stream_configs.restype = ctypes.c_int
+    lib.hyena_stream_config.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
     return lib
 
 
@@ -758,32 +760,37 @@ def stream_reference(w, per, stream, reps):
 
     ``hip_read3_write1_*``: the hand-written kernel in csrc/stream_ref.hip,
     y = q*k*v (three bf16 reads, one write: the operator's 8 bytes per
-    token*channel) with the grouped forward kernel's access pattern (16-byte
-    non-temporal buffer loads, row segments of 256 or 512 bytes per
-    workgroup, 8-chunk spans, two chunks in flight), for 8 and 16 waves per
-    workgroup.  Per-launch durations from fence-free HIP events around each
-    launch, as for the operator's layers; ``attainable_GBs`` is the best of
-    them.  torch's addcmul (same bytes) and a device copy (one read, one
-    write) are timed around ``reps`` back-to-back launches.
+    token*channel) with 16-byte non-temporal buffer loads and the grouped
+    forward kernels' access patterns (row segments of 256 or 512 bytes per
+    workgroup, 8-chunk spans) and the fastest patterns a sweep found (shorter
+    spans, wider segments).  Per-launch durations from fence-free HIP events
+    around each launch, as for the operator's layers; ``attainable_GBs`` is
+    the best of them.  torch's addcmul (same bytes) and a device copy (one
+    read, one write) are timed around ``reps`` back-to-back launches.
     """
+    import ctypes
     import torch
     res = {}
     lib = _stream_ref_lib()
     eb = 2 if w.dtype == "bf16" else 4
     best = 0.0
     if w.dtype == "bf16":
-        for waves, seg in ((8, 256), (8, 512), (16, 256), (16, 512)):
-            def call(i, waves=waves, seg=seg):
+        cfg = (ctypes.c_int * 6)()
+        for ci in range(lib.hyena_stream_configs()):
+            lib.hyena_stream_config(ci, cfg)
+            waves, seg, span, pf, order = list(cfg)[:5]
+
+            def call(i, ci=ci):
                 q, k, v, _, y = per[i % len(per)]
-                st = lib.hyena_stream_read3_write1(q.data_ptr(), k.data_ptr(), v.data_ptr(), y.data_ptr(),
-                                                   w.B, w.L, w.D, seg, waves, stream.cuda_stream)
+                st = lib.hyena_stream_read3_write1(ci, q.data_ptr(), k.data_ptr(), v.data_ptr(), y.data_ptr(),
+                                                   w.B, w.L, w.D, stream.cuda_stream)
                 if st != 0:
                     raise RuntimeError("hyena_stream_read3_write1: %d" % st)
             ms = _evented_launches(call, reps, stream)
             mean_ms = sum(ms) / len(ms)
             gbs = w.elems * eb * 4 / (mean_ms * 1e-3) / 1e9
             best = max(best, gbs)
-            res["hip_read3_write1_seg%d_w%d" % (seg, waves)] = {
+            res["hip_read3_write1_seg%d_w%d_span%d_pf%d%s" % (seg, waves, span, pf, "_spans_fastest" if order else "")] = {
                 "mean_us": round(mean_ms * 1e3, 2), "median_us": round(statistics.median(ms) * 1e3, 2),
                 "GBs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "event_samples": len(ms)}
         res["attainable_GBs"] = round(best, 1)

@@ -24,7 +24,7 @@
 //     in bf16, 16 waves own 256 channels, so each row segment it reads is
 //     512 bytes (HBM serves wider per-workgroup row segments faster): always
 //     for filters of at most 33 taps, and for longer ones on grids of at
-//     least 2048 workgroups.  It walks a span of consecutive 64-row chunks
+//     least 1024 workgroups.  It walks a span of consecutive 64-row chunks
 //     of one batch row, plus the
 //     32*KH rows before the span (the history its first chunks need), which
 //     it reads last (see the walk order below).
@@ -180,19 +180,36 @@ template <> struct Mma<true> {
 #define HYENA_ST2_MIN_KH 2
 #endif
 
+
 // Kernel: F32 selects the element type, KH the 32-row history steps
 // (KH = ceil((l_h - 1) / 32)), PF the chunks of k, v and q kept in flight,
 // S the chunks of one span.  The walk over the span is fully unrolled: the
 // prefetched registers are then never loop-carried, so the compiler's
 // memory-counter waits are exact and no in-flight load is copied.
 //
-// Walk order.  A span first ingests its own S chunks.  The first ND chunks
-// need rows from before the span (the history); their operand fragments are
-// kept and their outputs deferred.  The history rows are ingested last: at
-// that time the workgroup of the preceding span (same slab, same XCD under
-// the round-robin dispatch, launched together) is reading the same rows as
-// its own last chunks, so they come from L2 instead of HBM.  Then the
-// deferred chunks are computed.
+// Walk order.  Chunk c of a span needs its own rows and the 32*KH rows
+// before it, i.e. chunks c - H .. c (H history chunks before the span).  The
+// rows two workgroups read -- the last H chunks of a span, which are the
+// next span's history -- use the L2-allocating policy, so that whichever of
+// the two reads comes second hits in L2.  Two walks place those reads:
+//   * deferred (the kernels that keep their Toeplitz fragments in
+//     registers): the span's own chunks first, computing each from chunk
+//     ND on right after it is ingested; the first ND chunks need history,
+//     so their operand fragments are kept and their outputs deferred.  The
+//     history is ingested last, while the preceding span's workgroup (same
+//     slab, same XCD under the round-robin dispatch, dispatched together)
+//     reads the same rows as its own last chunks; then the deferred chunks.
+//   * alternating (the 16-wave kernels that build fragments per use; no
+//     registers to spare for deferred fragments): even spans walk up, the
+//     history and then chunks 0 .. S-1, each computed right after it is
+//     ingested; odd spans walk down, chunks S-1 .. 0 and then the history,
+//     chunk c computed right after chunk c - H is ingested.  A shared chunk
+//     is then read by both workgroups at the same point of their walks: at
+//     the start of an odd span and of the even span after it, and at the end
+//     of an even span and of the odd span after it.
+// Every output tile sums its input steps in the same (ascending) order in
+// either walk and direction, so the walk does not change a bit of the
+// result.
 //
 // REV walks time backwards: logical row t is physical row L-1-t, so the same
 // causal filter applied in the walk's order computes sum_s h[s] x[t+s] (the
@@ -206,21 +223,21 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     using frag = typename M::frag;
     constexpr int HROWS = 32 * KH;                        // history rows before a span
     constexpr int H = (HROWS + kChunk - 1) / kChunk;      // history chunks
-    constexpr int ND = (KH + 1) / 2 < S ? (KH + 1) / 2 : S;  // deferred chunks
     constexpr int NI = S + H;                             // ingested chunks
     constexpr int NH = HROWS / M::ROWS;                   // history fragments
     constexpr int NX = NH + M::FPC;                       // fragments one chunk reads
     constexpr int ST_PITCH = SLAB * 4;                    // fp32 staging row, bytes
     constexpr int kStBufs = KH >= HYENA_ST2_MIN_KH && NW == kWaves ? 2 : 1;
-    // 16-wave form with history: Toeplitz fragments built per use, not kept
-    constexpr bool FLY = !F32 && NW > kWaves && KH >= 2;
 
     // x = k*v of the current chunk (row-major, swizzled), the fp32
     // accumulators of the current chunk (and, with two staging buffers, of the
     // previous one; row-major, swizzled) and the filters.
     __shared__ __attribute__((aligned(16))) unsigned char xs[kChunk * T::PITCH];
     __shared__ __attribute__((aligned(16))) unsigned char st[kStBufs * kChunk * ST_PITCH];
-    __shared__ float hs[NW][kHLen];
+    // the filter, zero outside [0, l_h), index tap + kHOff: fp32 taps, or in
+    // bf16 pairs (h[t], h[t-1]) in one dword (low, high half), so a Toeplitz
+    // fragment (8 taps descending) is 4 dwords two entries apart
+    __shared__ std::conditional_t<F32, float, uint32_t> hs[NW][kHLen];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;           // wave = 16-channel tile of the slab
@@ -233,6 +250,13 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     bid /= p.n_slabs;
     const int spn = bid % p.n_spans;
     const int b = bid / p.n_spans;
+    // 16-wave form with history: Toeplitz fragments built per use, not kept
+    constexpr bool FLY = !F32 && NW > kWaves && KH >= 2;
+    // walk (see above): deferred for the kernels that keep their Toeplitz
+    // fragments in registers, alternating for FLY
+    constexpr int kWalk = FLY ? 1 : 0;
+    const bool desc = kWalk == 1 && H > 0 && (spn & 1);
+    constexpr int ND = kWalk != 0 ? 0 : (KH + 1) / 2 < S ? (KH + 1) / 2 : S;  // deferred chunks (walk 0)
 
     const int64_t t_begin = (int64_t)spn * S * kChunk;
     const int64_t t_stop = min(p.L, t_begin + (int64_t)S * kChunk);
@@ -272,14 +296,16 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
         const int g = tile_ok ? (c_begin + w * kTile) / p.group_size : 0;
         for (int i = l; i < kHLen; i += 64) {
             const int tap = i - kHOff;
-            float hv = 0.0f;
-            if (tile_ok && tap >= 0 && tap < p.l_h) {
-                if constexpr (F32)
-                    hv = ((const float *)p.h)[(size_t)g * p.l_h + tap];
-                else
-                    hv = bf_lo(((const uint16_t *)p.h)[(size_t)g * p.l_h + tap]);
+            if constexpr (F32) {
+                float hv = 0.0f;
+                if (tile_ok && tap >= 0 && tap < p.l_h) hv = ((const float *)p.h)[(size_t)g * p.l_h + tap];
+                hs[w][i] = hv;
+            } else {
+                const uint16_t *hg = (const uint16_t *)p.h + (size_t)g * p.l_h;
+                const uint32_t lo = tile_ok && tap >= 0 && tap < p.l_h ? hg[tap] : 0u;
+                const uint32_t hi = tile_ok && tap >= 1 && tap <= p.l_h ? hg[tap - 1] : 0u;
+                hs[w][i] = lo | (hi << 16);
             }
-            hs[w][i] = hv;
         }
     }
 
@@ -297,27 +323,21 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
         const int r = (REV ? nwin - 1 - lr : lr) * row_bytes + ld_base;
         return (seg_ok && need) ? (uint32_t)r : kOOB;
     };
-    // chunk of ingest item i: the span's chunks, then the history chunks
-    auto item_chunk = [](int i) -> int { return i < S ? i : -H + (i - S); };
-    // chunk of compute item j: the non-deferred chunks, then the deferred ones
-    auto comp_chunk = [](int j) -> int { return j < S - ND ? ND + j : j - (S - ND); };
-
     constexpr int NG = DUAL ? 2 : 1;  // gates per row
     u32x4_t kr[PF][T::NLD], vr[PF][T::NLD], qr[PF][NG][T::NLD];
 
-    // The last H chunks of a span are the next span's history.  Both reads
-    // of those rows, as the span's own chunks and as the neighbour's history,
-    // use the default (L2-allocating) policy, so whichever workgroup comes
-    // second hits in L2 (measured: 2% faster for l_h = 128 than streaming
-    // the history reads).  Every other row is read once and streams past L2.
-    auto load_kv = [&](int item, u32x4_t *kd, u32x4_t *vd) {
-        const bool need = item < NI;
-        const int c = need ? item_chunk(item) : S;
-        const bool keep = need && item >= S - H;
+    // Load chunk c (relative to the span start; history chunks are
+    // negative) of k and v.  The rows two workgroups read -- a span's last H
+    // chunks, which are the next span's history -- use the default
+    // (L2-allocating) policy, so that the second of the two reads hits in L2;
+    // every other row is read once and streams past L2.  `need` = false
+    // sends the access outside the window (no traffic).
+    auto load_kv = [&](int c, bool need, u32x4_t *kd, u32x4_t *vd) {
+        const bool keep = need && (c >= S - H || c < 0);
         // a chunk lies wholly before or wholly after row 0 (spans start on
         // chunk boundaries); before it, read the prefix rows P + t
         const int64_t t0c = t_begin + (int64_t)c * kChunk;
-        const bool pre = t0c < 0;
+        const bool pre = need && t0c < 0;
         const __amdgpu_buffer_rsrc_t sk = pre ? rkp : rk;
         const __amdgpu_buffer_rsrc_t sv = pre ? rvp : rv;
 #pragma unroll
@@ -334,15 +354,22 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
             }
         }
     };
-    auto load_q = [&](int j, u32x4_t (*qd)[T::NLD]) {
-        const bool need = j < S;
-        const int c = need ? comp_chunk(j) : S;
+    auto load_q = [&](int c, bool need, u32x4_t (*qd)[T::NLD]) {
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
             qd[0][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, io_off(c, i, need), 0, kLoadPolicy));
             if constexpr (DUAL)
                 qd[NG - 1][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rg2, io_off(c, i, need), 0, kLoadPolicy));
         }
+    };
+    // chunk of ingest item i and of compute item j
+    auto ld_chunk = [&](int i) -> int {
+        if constexpr (kWalk == 0) return i < S ? i : -H + (i - S);
+        return desc ? S - 1 - i : i - H;
+    };
+    auto cp_chunk = [&](int j) -> int {
+        if constexpr (kWalk == 0) return j < S - ND ? ND + j : j - (S - ND);
+        return desc ? S - 1 - j : j;
     };
     // x = k*v for this thread's rows -> xs.
     auto store_x = [&](const u32x4_t *kd, const u32x4_t *vd) {
@@ -373,8 +400,8 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     // each compute the q slot with the compute item PF ahead.
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
-        load_kv(s, kr[s], vr[s]);
-        load_q(s, qr[s]);
+        load_kv(s < NI ? ld_chunk(s) : S, s < NI, kr[s], vr[s]);
+        load_q(s < S ? cp_chunk(s) : S, s < S, qr[s]);
     }
 
     __syncthreads();  // filters staged
@@ -386,6 +413,16 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     // of 16 rows), fp32 e4 = 4 nt - kappa (units of 4 rows).
     constexpr int NE = F32 ? 16 + NH : 4 + 2 * KH;
     frag F[FLY ? 1 : NE];
+    // bf16 Toeplitz fragment e: element j = h[16 e + n16 - 8 q4 - j]
+    auto tap_frag = [&](int e) -> frag {
+        if constexpr (F32) {
+            return frag{};
+        } else {
+            const uint32_t *hw = &hs[w][16 * e + n16 - 8 * q4 + kHOff];
+            const u32x4_t d = {hw[0], hw[-2], hw[-4], hw[-6]};
+            return __builtin_bit_cast(frag, d);
+        }
+    };
     const int ch = w * kTile + n16;
     int rd_base;
     if constexpr (F32) {
@@ -395,9 +432,7 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     } else {
         if constexpr (!FLY) {
 #pragma unroll
-            for (int e = 0; e < NE; ++e)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) F[e][j] = (__bf16)hs[w][16 * e + n16 - 8 * q4 - j + kHOff];
+            for (int e = 0; e < NE; ++e) F[e] = tap_frag(e);
         }
         // channel 16w + n16, rows 8 q4 + j (+ 32 kappa); their swizzle is 2 q4
         rd_base = (8 * q4) * T::PITCH + ((((ch >> 3) ^ (2 * q4))) << 4) + ((ch & 7) << 1);
@@ -416,13 +451,6 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
                     dst[kk][j] = __builtin_bit_cast(__bf16, *(const uint16_t *)(&xs[rd_base + (32 * kk + j) * T::PITCH]));
         }
     };
-    // ingest item i: k*v -> xs, refill its slot, and read its fragments
-    auto ingest = [&](int i, frag *dst) {
-        store_x(kr[i % PF], vr[i % PF]);
-        load_kv(i + PF, kr[i % PF], vr[i % PF]);
-        __syncthreads();
-        read_frags(dst);
-    };
     // compute item j (chunk c) from its NX fragments Xc (history first):
     // the four 16-row output tiles into registers
     auto mma = [&](const frag *Xc, f32x4_t *acc) {
@@ -433,9 +461,7 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
             for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int e = NE - 1; e >= 0; --e) {
-                frag fe;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) fe[j] = (__bf16)hs[w][16 * e + n16 - 8 * q4 - j + kHOff];
+                const frag fe = tap_frag(e);
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
                     if ((nt - e) % 2 != 0) continue;
@@ -476,7 +502,7 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     // are in walk order; io_off maps the thread's walk row to its physical
     // row (REV: backwards) for the gate load and the store alike.
     auto finish = [&](int j) {
-        const int c = comp_chunk(j);
+        const int c = cp_chunk(j);
         const unsigned char *sb = st + (j % kStBufs) * (kChunk * ST_PITCH);
         u32x4_t (*qd)[T::NLD] = qr[j % PF];
         u32x4_t yv[NG][T::NLD];
@@ -505,7 +531,7 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
             }
         }
         // refill q before storing y, so y never shares registers with q
-        load_q(j + PF, qd);
+        load_q(j + PF < S ? cp_chunk(j + PF) : S, j + PF < S, qd);
 #pragma unroll
         for (int i = 0; i < T::NLD; ++i) {
             __builtin_amdgcn_raw_buffer_store_b128(yv[0][i], ry, io_off(c, i, true), 0, kFwdStorePolicy);
@@ -529,47 +555,96 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
         if constexpr (kStBufs == 1) finish(j);
     };
 
-    // ---- phase 1: the span's own chunks ------------------------------------
-    // X holds the NX fragments chunk c reads: NH history fragments, then its
-    // own FPC.  Chunks before ND keep their fragments for phase 3.
-    frag X[NX];
-    frag Xsave[ND * M::FPC > 0 ? ND * M::FPC : 1];
+    // ---- the walk: ingest items, each compute item right after its last
+    // input chunk.  Xa holds the fragments of every ingest item (registers:
+    // each is live only from its ingest to the last compute that reads it,
+    // H + 1 items later).  The loop is written once per direction, since
+    // which registers hold the oldest input steps of a compute item is fixed
+    // at compile time.
+    auto walk = [&](auto desc_tag) {
+        constexpr bool DESC = decltype(desc_tag)::value;
+        frag Xa[NI * M::FPC];
 #pragma unroll
-    for (int c = 0; c < S; ++c) {
-        ingest(c, &X[NH]);
-        if (c >= ND) {
-            compute(c - ND, X);
-        } else {
-#pragma unroll
-            for (int f = 0; f < M::FPC; ++f) Xsave[c * M::FPC + f] = X[NH + f];
-            __syncthreads();  // xs is rewritten by the next ingest
-        }
-#pragma unroll
-        for (int i = 0; i < NH; ++i) X[i] = X[i + M::FPC];
-    }
-    if constexpr (ND > 0) {
-        // ---- phase 2: the history rows before the span ---------------------
-        frag Hst[H * M::FPC];
-#pragma unroll
-        for (int i = S; i < NI; ++i) {
-            ingest(i, &Hst[(i - S) * M::FPC]);
-            __syncthreads();  // xs is rewritten by the next ingest
-        }
-        // ---- phase 3: the deferred chunks ----------------------------------
-        // fragment g (input step relative to the span start) of chunk c's
-        // window: history if g < 0 (Hst ends at step -1), else saved
-        constexpr int HF = H * M::FPC;
-#pragma unroll
-        for (int c = 0; c < ND; ++c) {
-            if (kStBufs == 1 && c > 0) __syncthreads();  // st is rewritten by this compute
+        for (int i = 0; i < NI; ++i) {
+            store_x(kr[i % PF], vr[i % PF]);
+            const int n = i + PF;  // the ingest item this slot loads next
+            load_kv(n < NI ? (DESC ? S - 1 - n : n - H) : S, n < NI, kr[i % PF], vr[i % PF]);
+            __syncthreads();
+            read_frags(&Xa[i * M::FPC]);
+            const int j = i - H;  // the compute item whose inputs are now all in
+            if (j < 0) {
+                __syncthreads();  // xs is rewritten by the next ingest
+                continue;
+            }
+            // input step g (in fragments, relative to the span start) of
+            // chunk c, oldest first: g = c FPC - NH + kk; its chunk gc and
+            // the ingest item that brought gc in
+            const int c = DESC ? S - 1 - j : j;
             frag Xc[NX];
 #pragma unroll
             for (int kk = 0; kk < NX; ++kk) {
-                const int g = c * M::FPC + kk - NH;
-                Xc[kk] = g < 0 ? Hst[HF + g] : Xsave[g];
+                const int g = c * M::FPC - NH + kk;
+                const int gc = g >= 0 ? g / M::FPC : -((-g + M::FPC - 1) / M::FPC);
+                const int item = DESC ? S - 1 - gc : gc + H;
+                Xc[kk] = Xa[item * M::FPC + (g - gc * M::FPC)];
             }
-            compute(S - ND + c, Xc);
+            compute(j, Xc);
         }
+    };
+    if constexpr (kWalk == 0) {
+        // ---- walk 0.  The span's own chunks first: the first ND need rows
+        // from before the span, so their fragments are kept and their outputs
+        // deferred.  Then the history rows, while the workgroup of the
+        // preceding span reads the same rows as its own last chunks; then the
+        // deferred chunks.
+        auto ingest = [&](int i, frag *dst) {
+            store_x(kr[i % PF], vr[i % PF]);
+            const int n = i + PF;
+            load_kv(n < NI ? ld_chunk(n) : S, n < NI, kr[i % PF], vr[i % PF]);
+            __syncthreads();
+            read_frags(dst);
+        };
+        frag X[NX];
+        frag Xsave[ND * M::FPC > 0 ? ND * M::FPC : 1];
+#pragma unroll
+        for (int c = 0; c < S; ++c) {
+            ingest(c, &X[NH]);
+            if (c >= ND) {
+                compute(c - ND, X);
+            } else {
+#pragma unroll
+                for (int f = 0; f < M::FPC; ++f) Xsave[c * M::FPC + f] = X[NH + f];
+                __syncthreads();  // xs is rewritten by the next ingest
+            }
+#pragma unroll
+            for (int i = 0; i < NH; ++i) X[i] = X[i + M::FPC];
+        }
+        if constexpr (ND > 0) {
+            frag Hst[H * M::FPC];
+#pragma unroll
+            for (int i = S; i < NI; ++i) {
+                ingest(i, &Hst[(i - S) * M::FPC]);
+                __syncthreads();  // xs is rewritten by the next ingest
+            }
+            // fragment g (input step relative to the span start) of chunk
+            // c's window: history if g < 0 (Hst ends at step -1), else saved
+            constexpr int HF = H * M::FPC;
+#pragma unroll
+            for (int c = 0; c < ND; ++c) {
+                if (kStBufs == 1 && c > 0) __syncthreads();  // st is rewritten by this compute
+                frag Xc[NX];
+#pragma unroll
+                for (int kk = 0; kk < NX; ++kk) {
+                    const int g = c * M::FPC + kk - NH;
+                    Xc[kk] = g < 0 ? Hst[HF + g] : Xsave[g];
+                }
+                compute(S - ND + c, Xc);
+            }
+        }
+    } else if (desc) {
+        walk(std::true_type{});
+    } else {
+        walk(std::false_type{});
     }
     if constexpr (kStBufs == 2) finish(S - 1);
 }
@@ -1958,21 +2033,23 @@ constexpr typename FnType<F32, Fam>::type kernel_of() {
 
 // The bf16 forward with 16 waves: 256-channel slabs, so every row segment a
 // workgroup reads or writes is 512 contiguous bytes.  On MI355X a plain
-// three-read, one-write streaming kernel with 256 workgroups measured 2.4,
-// 5.0, 5.5 and 6.1 TB/s for 64-, 128-, 256- and 512-byte row segments per
-// workgroup (B=1, L=8192, D=4096, bf16).  A 16-wave workgroup has 128 VGPRs
-// per lane: one chunk in flight (two spill), and for KH >= 2 the Toeplitz
-// fragments are built from the staged taps right before their MFMAs instead
-// of being kept (48 VGPRs for KH = 4), with one staging tile (two would not
-// fit the LDS).
+// three-read, one-write streaming kernel at B=1, L=8192, D=4096 (bf16, spans
+// of 8 chunks, two in flight) took 48.8 us with 8 waves and 256-byte
+// segments against 46.9 us with 16 waves and 512-byte segments.  A 16-wave
+// workgroup has 128 VGPRs per lane: one chunk in flight (two spill), and for
+// KH >= 2 the Toeplitz fragments are built from the staged tap pairs right
+// before their MFMAs instead of being kept (48 VGPRs for KH = 4), with one
+// staging tile (two would not fit the LDS).
 constexpr int kWideWaves = 16;
 constexpr int kWidePrefetch = 1;
 constexpr int64_t kWideWorkgroups = 256;  // one 16-wave workgroup per CU (112 KiB of LDS)
-// Longer filters take 16 waves from this many workgroups (8 per CU) on.
-// Measured on MI355X, l_h = 128, D = 4096, per launch: B=1, L=32768
-// 185 us with 8 waves against 194 with 16; L=65536 402 against 390;
-// B=4, L=32768 805 against 764.
-constexpr int64_t kWideMrWorkgroups = 2048;
+// Longer filters take 16 waves from this many workgroups (4 per CU) on: the
+// 16-wave form's matrix-core work is not hidden while every workgroup runs
+// in one round.  Measured on MI355X, l_h = 128, D = 4096, per launch, 8 /
+// 16 waves: B=1, L=8192 48.0 / 52.5 us; L=16384 93.5 / 96.0 (512
+// workgroups); L=32768 195 / 185 (1024); L=65536 403 / 365; B=4, L=32768
+// 808 / 720; L=2^20 6.43 / 5.72 ms.
+constexpr int64_t kWideMrWorkgroups = 1024;
 template <int KH, int... Ss> KernelFn wide_entry(int si, std::integer_sequence<int, Ss...>) {
     static constexpr KernelFn fns[] = {hyena_fwd_kernel<false, KH, kWidePrefetch, kSpans[Ss], false, false, kWideWaves>...};
     return fns[si];

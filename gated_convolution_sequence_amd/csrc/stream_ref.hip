@@ -1,26 +1,29 @@
 // Streaming reference for the benchmark (not part of the operator's ABI):
 //     y = q * k * v   (bf16 in, fp32 products, bf16 out, round to nearest even)
-// over [B, L, D] tensors, with the access pattern of the grouped forward
-// kernel in hyena_conv.hip and none of its arithmetic or on-chip staging:
-//   * a workgroup owns one row segment of SEG bytes (256 or 512: the slab of
-//     an 8- or a 16-wave forward workgroup) and a span of 8 chunks of 64 rows
-//     of one batch row;
+// over [B, L, D] tensors, with access patterns of the grouped forward kernels
+// in hyena_conv.hip and none of their arithmetic or on-chip staging:
+//   * a workgroup owns one row segment of SEG bytes (256: the slab of an
+//     8-wave forward workgroup; 512: a 16-wave one; 1024) and a span of
+//     4 or 8 chunks of 64 rows of one batch row;
 //   * every lane moves 16 bytes per access, through buffer loads with the
 //     non-temporal policy, and stores with non-temporal, system-scope policy
 //     (the forward kernel's store policy);
-//   * two chunks of q, k and v are in flight in registers, and the walk over
-//     the span is unrolled at compile time.
+//   * PF chunks of q, k and v are in flight in registers, and the walk over
+//     the span is unrolled at compile time;
+//   * the grid runs slabs fastest (as the forward) or spans fastest.
 // It reads three tensors and writes one, the operator's 8 bytes per
-// token*channel, so its rate is what the memory system gives that traffic
-// pattern: the attainable ceiling the forward kernels are measured against.
+// token*channel, so its best rate is what the memory system gives that
+// traffic: the attainable ceiling the forward kernels are measured against.
 //
-// C entry point (declared here only; the benchmark loads it with ctypes):
-//   int hyena_stream_read3_write1(const void *q, const void *k, const void *v,
-//                                 void *y, int64_t B, int64_t L, int64_t D,
-//                                 int seg_bytes, int waves, void *stream);
-// seg_bytes is 256 or 512 and waves 8 or 16; q, k, v, y are bf16 device
-// pointers, 16-byte aligned, D * 2 a multiple of 16.  Returns 0, -1 for bad
-// arguments, -8 if the launch failed.  Enqueued on `stream`, not waited for.
+// C entry points (declared here only; the benchmark loads them with ctypes):
+//   int hyena_stream_configs(void);                  number of patterns
+//   int hyena_stream_config(int i, int *out6);       waves, SEG, span, PF, order, 0
+//   int hyena_stream_read3_write1(int i, const void *q, const void *k,
+//                                 const void *v, void *y, int64_t B,
+//                                 int64_t L, int64_t D, void *stream);
+// q, k, v, y are bf16 device pointers, 16-byte aligned, D * 2 a multiple of
+// 16.  Returns 0, -1 for bad arguments, -8 if the launch failed.  Enqueued on
+// `stream`, not waited for.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -31,7 +34,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kRows = 64;      // rows per chunk
-constexpr int kSpan = 8;       // chunks per workgroup
 constexpr int kLoadPolicy = 2;    // nt
 constexpr int kStorePolicy = 19;  // nt, sc0, sc1
 constexpr uint32_t kOOB = 0x80000000u;
@@ -49,23 +51,23 @@ __device__ inline uint32_t mul3(uint32_t a, uint32_t b, uint32_t c) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
-template <int NW, int SEG>
+template <int NW, int SEG, int S, int PF, int ORD>
 __global__ __launch_bounds__(64 * NW) void stream_read3_write1_kernel(const void *q, const void *k, const void *v,
                                                                       void *y, int64_t L, int D, int n_spans,
                                                                       int n_slabs) {
     constexpr int TPR = SEG / 16;          // lanes per row
     constexpr int RPL = 64 * NW / TPR;     // rows per access
     constexpr int NLD = kRows / RPL;       // accesses per tensor per chunk
-    constexpr int PF = 2;                  // chunks in flight
     static_assert(NLD * RPL == kRows, "accesses must tile the chunk");
 
     int bid = blockIdx.x;
-    const int slab = bid % n_slabs;
-    bid /= n_slabs;
-    const int spn = bid % n_spans;
-    const int b = bid / n_spans;
-    const int64_t t0 = (int64_t)spn * kSpan * kRows;
-    const int64_t t1 = min(L, t0 + (int64_t)kSpan * kRows);
+    const int per_b = n_spans * n_slabs;
+    const int b = bid / per_b;
+    bid -= b * per_b;
+    const int slab = ORD == 0 ? bid % n_slabs : bid / n_spans;
+    const int spn = ORD == 0 ? bid / n_slabs : bid % n_spans;
+    const int64_t t0 = (int64_t)spn * S * kRows;
+    const int64_t t1 = min(L, t0 + (int64_t)S * kRows);
     const int row_bytes = D * 2;
     const int c_off = slab * SEG;
     const size_t base = ((size_t)b * (size_t)L + (size_t)t0) * (size_t)row_bytes + (size_t)c_off;
@@ -96,35 +98,56 @@ __global__ __launch_bounds__(64 * NW) void stream_read3_write1_kernel(const void
 #pragma unroll
     for (int s = 0; s < PF; ++s) load(s, s);
 #pragma unroll
-    for (int c = 0; c < kSpan; ++c) {
+    for (int c = 0; c < S; ++c) {
         const int s = c % PF;
         u32x4_t yv[NLD];
 #pragma unroll
         for (int i = 0; i < NLD; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) yv[i][e] = mul3(qr[s][i][e], kr[s][i][e], vr[s][i][e]);
-        if (c + PF < kSpan) load(c + PF, s);
+        if (c + PF < S) load(c + PF, s);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) __builtin_amdgcn_raw_buffer_store_b128(yv[i], ry, off(c, i), 0, kStorePolicy);
     }
 }
 
+typedef void (*StreamFn)(const void *, const void *, const void *, void *, int64_t, int, int, int);
+struct Config {
+    int waves, seg, span, pf, order;
+    StreamFn fn;
+};
+#define CFG(NW, SEG, S, PF, ORD) {NW, SEG, S, PF, ORD, stream_read3_write1_kernel<NW, SEG, S, PF, ORD>}
+// The grouped forward kernels' patterns, then the fastest ones a sweep of
+// waves, SEG, span, PF and order found on MI355X at B=1, L=8192, D=4096.
+const Config kConfigs[] = {
+    CFG(8, 256, 8, 2, 0), CFG(16, 512, 8, 1, 0), CFG(16, 512, 8, 2, 0),
+    CFG(16, 512, 4, 2, 0), CFG(8, 1024, 4, 1, 1), CFG(16, 512, 8, 3, 0),
+};
+constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+
 }  // namespace
 
-extern "C" int hyena_stream_read3_write1(const void *q, const void *k, const void *v, void *y, int64_t B,
-                                         int64_t L, int64_t D, int seg_bytes, int waves, void *stream) {
+extern "C" int hyena_stream_configs(void) { return kNumConfigs; }
+
+extern "C" int hyena_stream_config(int i, int *out6) {
+    if (i < 0 || i >= kNumConfigs || !out6) return -1;
+    const Config &c = kConfigs[i];
+    out6[0] = c.waves; out6[1] = c.seg; out6[2] = c.span; out6[3] = c.pf; out6[4] = c.order; out6[5] = 0;
+    return 0;
+}
+
+extern "C" int hyena_stream_read3_write1(int i, const void *q, const void *k, const void *v, void *y, int64_t B,
+                                         int64_t L, int64_t D, void *stream) {
+    if (i < 0 || i >= kNumConfigs) return -1;
+    const Config &c = kConfigs[i];
     if (!q || !k || !v || !y || B < 1 || L < 1 || D < 8 || (D * 2) % 16 != 0 || D > (1 << 28)) return -1;
     if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)y) & 15u) != 0) return -1;
-    if ((seg_bytes != 256 && seg_bytes != 512) || (waves != 8 && waves != 16)) return -1;
-    if ((int64_t)kSpan * kRows * D * 2 >= ((int64_t)1 << 31)) return -1;  // 32-bit window offsets
-    const int64_t n_spans = (L + kSpan * kRows - 1) / (kSpan * kRows);
-    const int64_t n_slabs = (D * 2 + seg_bytes - 1) / seg_bytes;
+    if ((int64_t)c.span * kRows * D * 2 >= ((int64_t)1 << 31)) return -1;  // 32-bit window offsets
+    const int64_t n_spans = (L + c.span * kRows - 1) / (c.span * kRows);
+    const int64_t n_slabs = (D * 2 + c.seg - 1) / c.seg;
     const int64_t grid = B * n_spans * n_slabs;
-    if (grid > INT32_MAX || n_spans > INT32_MAX) return -1;
-    void (*fn)(const void *, const void *, const void *, void *, int64_t, int, int, int) =
-        waves == 8 ? (seg_bytes == 256 ? stream_read3_write1_kernel<8, 256> : stream_read3_write1_kernel<8, 512>)
-                   : (seg_bytes == 256 ? stream_read3_write1_kernel<16, 256> : stream_read3_write1_kernel<16, 512>);
-    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * waves), 0, (hipStream_t)stream, q, k, v, y, L, (int)D,
+    if (grid > INT32_MAX || n_spans * n_slabs > INT32_MAX) return -1;
+    hipLaunchKernelGGL(c.fn, dim3((unsigned)grid), dim3(64 * c.waves), 0, (hipStream_t)stream, q, k, v, y, L, (int)D,
                        (int)n_spans, (int)n_slabs);
     return hipGetLastError() == hipSuccess ? 0 : -8;
 }

@@ -142,9 +142,9 @@ def test_plan_split(B, L, D, l_h, dtype, span, expect_span):
     s, wgs = hc.plan(B, L, D, 16, l_h, dtype, span)
     assert s == expect_span
     chunks = -(-L // 64)
-    # the 16-wave kernel: bf16 SE always, longer filters from 2048 workgroups
+    # the 16-wave kernel: bf16 SE always, longer filters from 1024 workgroups
     # at 8-chunk spans
-    wide = dtype == hc.DTYPE_BF16 and (l_h <= 33 or B * (-(-D // 256)) * (-(-chunks // 8)) >= 2048)
+    wide = dtype == hc.DTYPE_BF16 and (l_h <= 33 or B * (-(-D // 256)) * (-(-chunks // 8)) >= 1024)
     slab = hc.WIDE_SLAB if wide else hc.SLAB
     assert wgs == B * (-(-D // slab)) * (-(-chunks // s))
 

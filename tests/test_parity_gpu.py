@@ -238,60 +238,66 @@ def _assert_all_finite(y, what):
         assert bool(torch.isfinite(flat[i:i + step]).all()), "%s: unwritten or non-finite output" % what
 
 
-def _rows_match_b1_calls(w, q, k, v, h, y):
-    """Each batch row, run alone (B = 1: a grid a quarter as wide, so the plan
-    takes the 8-wave kernel whose Toeplitz fragments stay in registers), gives
-    the same bits as the batched call: every output tile sums the same input
-    steps in the same order."""
-    out = torch.empty_like(y[0:1])
-    for b in range(w.B):
-        log("  batch row %d alone" % b)
-        hc.conv_fwd(q[b:b + 1], k[b:b + 1], v[b:b + 1], h, w.group_size, out=out)
-        assert torch.equal(out, y[b:b + 1]), "batch row %d differs from its own B=1 call" % b
-
-
 def _shards_match(w, q, k, v, h, y, rows):
-    """Rows [s, s + rows) through the history-prefix entry (the l_h - 1 rows
-    before s as the prefix) give the same bits as the whole-sequence call:
-    spans start on chunk boundaries, so each output sums the same terms in
-    the same order (StripedHyena 2 explainer, page "01. overview", section 5:
-    point-to-point context parallelism)."""
-    assert w.B == 1 and w.L % rows == 0 and rows % 64 == 0
+    """Rows [s, s + rows) of each batch row (the last shard may be shorter),
+    run through the history-prefix entry with the l_h - 1 rows before s as
+    the prefix, give the same bits as the big call: spans start on chunk
+    boundaries, so each output sums the same terms in the same order
+    (StripedHyena 2 explainer, page "01. overview", section 5:
+    point-to-point context parallelism).  A shard is a small grid with small
+    (32-bit) offsets; for a 128-tap filter it takes the 8-wave kernel, whose
+    Toeplitz fragments stay in registers, where the big call takes the
+    16-wave one, so two kernels and two address ranges must agree."""
+    assert rows % 64 == 0
     P = w.l_h - 1
-    out = torch.empty_like(y[:, :rows])
-    for s in range(0, w.L, rows):
-        if s == 0 or P == 0:
-            hc.conv_fwd(q[:, :rows], k[:, :rows], v[:, :rows], h, w.group_size, out=out)
-        else:
-            hc.conv_fwd(q[:, s:s + rows], k[:, s:s + rows], v[:, s:s + rows], h, w.group_size,
-                        out=out, k_prev=k[:, s - P:s], v_prev=v[:, s - P:s])
-        assert torch.equal(out, y[:, s:s + rows]), "%s: shard at row %d differs" % (w.name, s)
+    out = torch.empty((1, rows, w.D), dtype=y.dtype, device=y.device)
+    for b in range(w.B):
+        for s in range(0, w.L, rows):
+            e = min(w.L, s + rows)
+            sl = lambda a: a[b:b + 1, s:e]
+            o = out[:, :e - s]
+            if s == 0 or P == 0:
+                hc.conv_fwd(sl(q), sl(k), sl(v), h, w.group_size, out=o)
+            else:
+                hc.conv_fwd(sl(q), sl(k), sl(v), h, w.group_size, out=o,
+                            k_prev=k[b:b + 1, s - P:s], v_prev=v[b:b + 1, s - P:s])
+            assert torch.equal(o, y[b:b + 1, s:e]), "%s: batch row %d, shard at row %d differs" % (w.name, b, s)
+
+
+def _slab_width(B, L, D, gs, l_h):
+    """Channels per workgroup of the plan: 256 (16 waves) or 128 (8 waves)."""
+    span, wgs = hc.plan(B, L, D, gs, l_h)
+    spans = B * -(-(-(-L // 64)) // span)
+    assert wgs in (spans * -(-D // 256), spans * -(-D // 128))
+    return 256 if wgs == spans * -(-D // 256) else 128
 
 
 def test_mr_b4_sampled():
     w = WORKLOADS["mr_b4"]
+    assert _slab_width(w.B, w.L, w.D, w.group_size, w.l_h) == 256
+    assert _slab_width(1, 16384, w.D, w.group_size, w.l_h) == 128
     log("mr_b4: generate")
     q, k, v, h = make_inputs(w, DEV)
-    span, wgs = hc.plan(w.B, w.L, w.D, w.group_size, w.l_h)
-    log("mr_b4: span %d, %d workgroups" % (span, wgs))
     y = run(q, k, v, h, w.group_size)
     _assert_all_finite(y, "mr_b4")
-    _rows_match_b1_calls(w, q, k, v, h, y)
+    log("mr_b4: 16384-row shards")
+    _shards_match(w, q, k, v, h, y, 16384)
     _sampled_checks(w, q, k, v, h, y, n_groups=6, seed=4)
 
 
 def test_wide_mr_ragged_partial_slab_sampled():
-    """The 16-wave form of a 128-tap filter (taken from 2048 workgroups at
+    """The 16-wave form of a 128-tap filter (taken from 1024 workgroups at
     8-chunk spans on) on a ragged length and a partial 256-channel slab."""
     w = dataclasses.replace(WORKLOADS["mr"], name="mr_wide_edge", B=2, L=262081, D=272)
     span, wgs = hc.plan(w.B, w.L, w.D, w.group_size, w.l_h)
     assert (span, wgs) == (8, 2 * 2 * 512)  # 2 slabs of 256 channels, 512 spans
-    assert hc.plan(1, w.L, w.D, w.group_size, w.l_h) == (8, 3 * 512)  # B=1: 8-wave, 128-channel slabs
+    assert _slab_width(1, 16384, w.D, w.group_size, w.l_h) == 128
     log("mr_wide_edge: generate")
     q, k, v, h = make_inputs(w, DEV)
     y = run(q, k, v, h, w.group_size)
     _assert_all_finite(y, "mr_wide_edge")
-    _rows_match_b1_calls(w, q, k, v, h, y)
+    log("mr_wide_edge: 16384-row shards")
+    _shards_match(w, q, k, v, h, y, 16384)
     _sampled_checks(w, q, k, v, h, y, n_groups=2, seed=6)
 
 
@@ -299,10 +305,11 @@ def test_long_stripe_sampled():
     """SE layer then MR layer at L = 2^20 (2^32 elements per tensor), one stream.
 
     Every output element is checked three ways: the whole NaN-prefilled
-    output must be written; 32 shards of 32768 rows, each run through the
-    history-prefix entry with small (32-bit) offsets, must give the same bits;
-    and windows (one straddling element 2^31) and eight full-length groups
-    (first, last, six seeded) are compared with the oracle.
+    output must be written; 16384-row shards, each run through the
+    history-prefix entry with small (32-bit) offsets (for MR on the 8-wave
+    kernel), must give the same bits; and windows (one straddling element
+    2^31) and eight full-length groups (first, last, six seeded) are
+    compared with the oracle.
     """
     outs = []
     for name in ("long_se", "long_mr"):
@@ -316,8 +323,8 @@ def test_long_stripe_sampled():
     for w, q, k, v, h, y in outs:
         log("%s: whole-output scan" % w.name)
         _assert_all_finite(y, w.name)
-        log("%s: 32768-row shards" % w.name)
-        _shards_match(w, q, k, v, h, y, 32768)
+        log("%s: 16384-row shards" % w.name)
+        _shards_match(w, q, k, v, h, y, 16384)
         log("%s: sampled checks" % w.name)
         _sampled_checks(w, q, k, v, h, y, n_groups=6, seed=5)
         del q, k, v, h, y

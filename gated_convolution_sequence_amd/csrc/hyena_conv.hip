@@ -1343,7 +1343,7 @@ template <bool F32> struct CdTr {
     static_assert(SEGS <= 8, "swizzle keys 0..7");
 };
 
-template <bool F32, int KH>
+template <bool F32, int KH, bool REV = false, bool DUAL = false>
 __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
     using T = CdTr<F32>;
     constexpr int SLAB = T::SLAB;
@@ -1352,6 +1352,8 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
     constexpr int NPT = (SLAB * PTN + kCdThreads - 1) / kCdThreads;
     __shared__ __attribute__((aligned(16))) unsigned char xr[SLAB * T::RING_B];
     __shared__ __attribute__((aligned(16))) unsigned char qy[SLAB * T::QY_B];
+    // the second gate's rows, overwritten by y2 = g2 acc (two-output form)
+    __shared__ __attribute__((aligned(16))) unsigned char qy2[DUAL ? SLAB * T::QY_B : 16];
     __shared__ uint32_t pt[SLAB * PTN];
 
     const int tid = threadIdx.x;
@@ -1385,9 +1387,12 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
     // its size must not go negative, or the out-of-bounds offset kOOB would
     // land inside it.  Base and size are made wave-uniform explicitly, so the
     // descriptor lives in scalar registers.
+    // Under REV the window holds logical rows r0 .. r0 + rows - 1 at
+    // physical rows L - r0 - rows .. L - r0 - 1, in decreasing order (see off).
     auto window = [&](const void *base, int64_t r0, int rows) {
         const int n = rows * row_bytes - c_begin * T::EB;
-        const uint64_t a = (uint64_t)((const char *)base + batch_off + (size_t)r0 * (size_t)row_bytes);
+        const int64_t pr0 = REV ? p.L - r0 - (rows > 0 ? rows : 0) : r0;
+        const uint64_t a = (uint64_t)((const char *)base + batch_off + (size_t)pr0 * (size_t)row_bytes);
         const uint64_t au = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
                             (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
         return make_rsrc((const void *)au, (uint32_t)__builtin_amdgcn_readfirstlane(n > 0 ? n : 0));
@@ -1398,27 +1403,32 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
     const int sg = tid % T::SEGS;
     const int g4 = tid / T::SEGS;
     const bool seg_ok = c_begin + sg * T::VEC < p.D;
-    auto off = [&](int r, bool need) -> uint32_t {
-        return (seg_ok && need) ? (uint32_t)(r * row_bytes + sg * 16) : kOOB;
+    // byte offset of logical row r of a window of `rows` rows
+    auto off = [&](int r, int rows, bool need) -> uint32_t {
+        return (seg_ok && need) ? (uint32_t)((REV ? rows - 1 - r : r) * row_bytes + sg * 16) : kOOB;
     };
     // LDS byte address of time index r in channel ch's row (pitch rb)
     auto pos = [&](int ch, int r, int rb) -> int {
         return ch * rb + ((((r / T::VEC) ^ ((ch / T::VEC) & 7))) << 4) + (r % T::VEC) * T::EB;
     };
 
-    u32x4_t k0[4], v0[4], q0[4], k1[4], v1[4], q1[4];
-    auto load_block = [&](int blk, u32x4_t *kd, u32x4_t *vd, u32x4_t *qd) {
+    constexpr int NG = DUAL ? 2 : 1;  // gates per row
+    u32x4_t k0[4], v0[4], q0[NG][4], k1[4], v1[4], q1[NG][4];
+    auto load_block = [&](int blk, u32x4_t *kd, u32x4_t *vd, u32x4_t (*qd)[4]) {
         const int64_t r0 = min(t_begin + (int64_t)blk * kCdBlock, t_stop);  // past the span: empty
         const int rows = min(kCdBlock, (int)(t_stop - r0));
         const __amdgpu_buffer_rsrc_t rq = window(p.q, r0, rows);
         const __amdgpu_buffer_rsrc_t rk = window(p.k, r0, rows);
         const __amdgpu_buffer_rsrc_t rv = window(p.v, r0, rows);
+        const __amdgpu_buffer_rsrc_t rg = window(DUAL ? p.g2 : p.q, r0, DUAL ? rows : 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint32_t o = off(4 * g4 + i, true);
+            const uint32_t o = off(4 * g4 + i, rows, true);
             kd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, kLoadPolicy));
             vd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, kLoadPolicy));
-            qd[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, kLoadPolicy));
+            qd[0][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, kLoadPolicy));
+            if constexpr (DUAL)
+                qd[1][i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rg, o, 0, kLoadPolicy));
         }
     };
     // HBM requests first: the first block, then the history rows before the
@@ -1427,16 +1437,35 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
     u32x4_t hk[4], hv[4];
     const bool hist = g4 < HROWS / 4;
     if constexpr (HROWS > 0) {
-        const int64_t hr0 = max((int64_t)0, t_begin - HROWS);
-        const __amdgpu_buffer_rsrc_t rk = window(p.k, hr0, (int)(t_begin - hr0));
-        const __amdgpu_buffer_rsrc_t rv = window(p.v, hr0, (int)(t_begin - hr0));
-        const int rel = (int)(t_begin - HROWS - hr0);  // <= 0: rows before 0 read as zero
+        if (t_begin > 0) {
+            // spans start on block boundaries, so every history row of a
+            // later span lies at or after row 0
+            const int64_t hr0 = t_begin - HROWS;
+            const __amdgpu_buffer_rsrc_t rk = window(p.k, hr0, HROWS);
+            const __amdgpu_buffer_rsrc_t rv = window(p.v, hr0, HROWS);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rel + 4 * g4 + i;
-            const uint32_t o = off(r, hist && r >= 0);
-            hk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
-            hv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t o = off(4 * g4 + i, HROWS, hist);
+                hk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+                hv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+            }
+        } else {
+            // the first span: the HROWS rows before row 0 are the last rows
+            // of the caller's prefix (P rows of kp, vp per batch row; none:
+            // zeros), row P + t for time t < 0
+            const size_t pre_off = (size_t)b * (size_t)p.P * (size_t)row_bytes + (size_t)c_begin * T::EB;
+            const int np = p.P > 0 ? p.P * row_bytes - c_begin * T::EB : 0;
+            const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.P > 0 ? (const char *)p.kp + pre_off : (const char *)p.k,
+                                                        (uint32_t)(np > 0 ? np : 0));
+            const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.P > 0 ? (const char *)p.vp + pre_off : (const char *)p.v,
+                                                        (uint32_t)(np > 0 ? np : 0));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int pr = p.P - HROWS + 4 * g4 + i;  // prefix row of time -HROWS + 4 g4 + i
+                const uint32_t o = (seg_ok && hist && pr >= 0) ? (uint32_t)(pr * row_bytes + sg * 16) : kOOB;
+                hk[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+                hv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+            }
         }
     }
     // Every tap load is issued unconditionally (an index outside the filter
@@ -1495,21 +1524,21 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
             }
         }
     };
-    // q of rows 4 g4 .. 4 g4 + 3 -> the gate rows (time 4 g4 of the block)
-    auto put_q = [&](const u32x4_t *qd) {
+    // a gate's rows 4 g4 .. 4 g4 + 3 -> its gate rows (time 4 g4 of the block)
+    auto put_q = [&](const u32x4_t *qd, unsigned char *dst) {
 #pragma unroll
         for (int e = 0; e < T::VEC; ++e) {
             const int ch = sg * T::VEC + e;
             if constexpr (F32) {
                 const u32x4_t qv = {qd[0][e], qd[1][e], qd[2][e], qd[3][e]};
-                *(u32x4_t *)(&qy[pos(ch, 4 * g4, T::QY_B)]) = qv;
+                *(u32x4_t *)(&dst[pos(ch, 4 * g4, T::QY_B)]) = qv;
             } else {
                 const int d = e >> 1;
                 uint32_t h4[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) h4[i] = (e & 1) ? (qd[i][d] >> 16) : (qd[i][d] & 0xffffu);
                 const u32x2_t qv = {h4[0] | (h4[1] << 16), h4[2] | (h4[3] << 16)};
-                *(u32x2_t *)(&qy[pos(ch, 4 * g4, T::QY_B)]) = qv;
+                *(u32x2_t *)(&dst[pos(ch, 4 * g4, T::QY_B)]) = qv;
             }
         }
     };
@@ -1536,13 +1565,14 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
     // always in flight.  They are issued unconditionally: past the span the
     // window is empty and they read nothing.  (Behind a branch, the
     // compiler's wait for this block's data would also wait for them.)
-    auto process = [&](int blk, const u32x4_t *kd, const u32x4_t *vd, const u32x4_t *qd,
-                       u32x4_t *kn, u32x4_t *vn, u32x4_t *qn) {
+    auto process = [&](int blk, const u32x4_t *kd, const u32x4_t *vd, const u32x4_t (*qd)[4],
+                       u32x4_t *kn, u32x4_t *vn, u32x4_t (*qn)[4]) {
         const int rb0 = (blk % 3) * 256 + 128 >= kCdRing ? (blk % 3) * 256 + 128 - kCdRing
                                                          : (blk % 3) * 256 + 128;  // (256 blk + 128) mod 384
         load_block(blk + 1, kn, vn, qn);
         put_x(wrap(rb0 + 4 * g4), kd, vd);
-        put_q(qd);
+        put_q(qd[0], qy);
+        if constexpr (DUAL) put_q(qd[1], qy2);
         // B-operand offsets of this lane within a channel's ring row, one per
         // step: the wave's channels share the swizzle key (one row segment),
         // so these serve all of them.  bf16: steps of 32 input rows; the last
@@ -1596,46 +1626,55 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, hv[ks]),
                                                                   __builtin_bit_cast(bf16x8_t, xv[ks]), acc, 0, 0, 0);
             }
-            // y = q acc in place of q
+            // y = q acc in place of q (and y2 = g2 acc in place of g2)
             const int qa = pos(dl, lane_t4, T::QY_B);
-            if constexpr (F32) {
-                const f32x4_t qv = *(const f32x4_t *)(&qy[qa]);
-                *(f32x4_t *)(&qy[qa]) = qv * acc;
-            } else {
-                const u32x2_t qv = *(const u32x2_t *)(&qy[qa]);
-                const u32x2_t yv = {pack_bf16(bf_lo(qv[0]) * acc[0], bf_hi(qv[0]) * acc[1]),
-                                    pack_bf16(bf_lo(qv[1]) * acc[2], bf_hi(qv[1]) * acc[3])};
-                *(u32x2_t *)(&qy[qa]) = yv;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                unsigned char *gr = gi == 0 ? qy : qy2;
+                if constexpr (F32) {
+                    const f32x4_t qv = *(const f32x4_t *)(&gr[qa]);
+                    *(f32x4_t *)(&gr[qa]) = qv * acc;
+                } else {
+                    const u32x2_t qv = *(const u32x2_t *)(&gr[qa]);
+                    const u32x2_t yv = {pack_bf16(bf_lo(qv[0]) * acc[0], bf_hi(qv[0]) * acc[1]),
+                                        pack_bf16(bf_lo(qv[1]) * acc[2], bf_hi(qv[1]) * acc[3])};
+                    *(u32x2_t *)(&gr[qa]) = yv;
+                }
             }
         }
         __syncthreads();
         // ---- epilogue: rows 4 g4 .. 4 g4 + 3 back to row-major, 16-byte stores
-        u32x4_t yrow[4];
-        if constexpr (F32) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const u32x4_t cv = *(const u32x4_t *)(&qy[pos(sg * 4 + e, 4 * g4, T::QY_B)]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) yrow[i][e] = cv[i];
-            }
-        } else {
-            u32x2_t cv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) cv[e] = *(const u32x2_t *)(&qy[pos(sg * 8 + e, 4 * g4, T::QY_B)]);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const u32x2_t a = cv[2 * d], c = cv[2 * d + 1];
-                yrow[0][d] = (a[0] & 0xffffu) | (c[0] << 16);
-                yrow[1][d] = (a[0] >> 16) | (c[0] & 0xffff0000u);
-                yrow[2][d] = (a[1] & 0xffffu) | (c[1] << 16);
-                yrow[3][d] = (a[1] >> 16) | (c[1] & 0xffff0000u);
-            }
-        }
         const int64_t r0 = t_begin + (int64_t)blk * kCdBlock;
-        const __amdgpu_buffer_rsrc_t ry = window(p.y, r0, min(kCdBlock, (int)(t_stop - r0)));
+        const int brows = min(kCdBlock, (int)(t_stop - r0));
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_raw_buffer_store_b128(yrow[i], ry, off(4 * g4 + i, true), 0, kStorePolicy);
+        for (int gi = 0; gi < NG; ++gi) {
+            const unsigned char *gr = gi == 0 ? qy : qy2;
+            u32x4_t yrow[4];
+            if constexpr (F32) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const u32x4_t cv = *(const u32x4_t *)(&gr[pos(sg * 4 + e, 4 * g4, T::QY_B)]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) yrow[i][e] = cv[i];
+                }
+            } else {
+                u32x2_t cv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cv[e] = *(const u32x2_t *)(&gr[pos(sg * 8 + e, 4 * g4, T::QY_B)]);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const u32x2_t a = cv[2 * d], c = cv[2 * d + 1];
+                    yrow[0][d] = (a[0] & 0xffffu) | (c[0] << 16);
+                    yrow[1][d] = (a[0] >> 16) | (c[0] & 0xffff0000u);
+                    yrow[2][d] = (a[1] & 0xffffu) | (c[1] << 16);
+                    yrow[3][d] = (a[1] >> 16) | (c[1] & 0xffff0000u);
+                }
+            }
+            const __amdgpu_buffer_rsrc_t ry = window(gi == 0 ? p.y : p.y2, r0, brows);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_raw_buffer_store_b128(yrow[i], ry, off(4 * g4 + i, brows, true), 0, kStorePolicy);
+        }
         __syncthreads();  // the gate rows and the oldest ring entries are rewritten next
     };
     for (int blk = 0; blk < nb; blk += 2) {
@@ -2002,8 +2041,190 @@ __global__ __launch_bounds__(256) void hyena_bwd_direct_dh_reduce_kernel(const f
     dh[idx] = acc;
 }
 
+// ---------------------------------------------------------------------------
+// Filter gradient, pass 1, for group sizes off the 16-channel tile and
+// filters of more than 8 taps (page "04. hardware-aware convolution
+// kernels", section 7: block-local partial filter gradients, then a
+// reduction).  Per channel d and tap s < l_h,
+//     ws[b * n_spans + span][d][s] = sum_{t in span} dz[b, t, d] x[b, t - s, d],
+// with dz = dy q and x = k v formed in fp32 (exact for bf16 inputs); the
+// reduction adds the rows and the group's channels.  Without a shared
+// filter there is no channel dimension to contract on the matrix cores, so
+// the lag products are fp32 multiply-adds.
+//
+// A workgroup owns kLagCh channels of one batch row and a span of rows,
+// walked in 64-row blocks.  dz of the block and x of the block and the 128
+// rows before it sit in LDS, time-major, so the 64 lanes of a wave (one
+// channel each) read 64 consecutive words.  Wave w takes tap group
+// jg = w % NG2 (taps 16 jg .. 16 jg + 15) and time slice jt = w / NG2 of
+// every block (64 NG2 / 8 rows), in steps of 8 rows: 8 values of dz and a
+// window of 23 values of x, then 128 multiply-adds from registers.  Each
+// block's products are summed on their own and then added to the span's, and
+// the time slices are added in a fixed order at the end, so the result is the
+// same run to run.  The next block's rows are loaded while this one is
+// summed.
+// ---------------------------------------------------------------------------
+constexpr int kLagCh = 64;        // channels per workgroup
+constexpr int kLagRing = 256;     // x rows per channel in LDS (a block, the 128 before it, slack)
+constexpr int kLagSpanRows = 1024;
+
+template <bool F32, int NG2>
+__global__ __launch_bounds__(512) void hyena_bwd_dh_lag_kernel(DhParams p) {
+    constexpr int EB = F32 ? 4 : 2;
+    constexpr int REPS = 8 / NG2;   // time slices of a block
+    constexpr int RPT = 64 / REPS;  // rows per slice
+    constexpr int NT = 16 * NG2;    // taps this workgroup sums (>= l_h)
+    constexpr int NLD = F32 ? 2 : 1;  // 16-byte loads per tensor per thread and block
+    __shared__ float xs[kLagRing][kLagCh];
+    __shared__ float zs[64][kLagCh];
+
+    const int tid = threadIdx.x, w = tid >> 6, cl = tid & 63;
+    const int jg = w % NG2, jt = w / NG2;
+    int bid = blockIdx.x;
+    const int slab = bid % p.n_slabs;
+    bid /= p.n_slabs;
+    const int spn = bid % p.n_spans;
+    const int b = bid / p.n_spans;
+    const int64_t t_begin = (int64_t)spn * p.span_rows;
+    const int64_t t_stop = min(p.L, t_begin + (int64_t)p.span_rows);
+    const int nblk = (int)((t_stop - t_begin + 63) / 64);
+    const int c_begin = slab * kLagCh;
+    const int row_bytes = p.D * EB;
+    const size_t batch_off = (size_t)b * (size_t)p.L * (size_t)row_bytes + (size_t)c_begin * EB;
+
+    // loader role: row lr of a 64-row block, 8 channels from 8 sg (bf16: one
+    // 16-byte access; fp32: two)
+    const int lr = tid >> 3, sg = tid & 7;
+    auto window = [&](const void *base, int64_t r0, int rows) {
+        const int n = rows * row_bytes - c_begin * EB;
+        return make_rsrc((const char *)base + batch_off + (size_t)r0 * (size_t)row_bytes, (uint32_t)(n > 0 ? n : 0));
+    };
+    // byte offset of window row r, this thread's channels (half h), or
+    // outside every window (fp32: each half is 4 channels)
+    auto off = [&](int r, int h) -> uint32_t {
+        const bool ok = r >= 0 && c_begin + sg * 8 + 4 * h < p.D;
+        return ok ? (uint32_t)(r * row_bytes + sg * 8 * EB + 16 * h) : kOOB;
+    };
+    // 8 fp32 values of a * b for this thread's row segment
+    auto prod8 = [&](const u32x4_t *a, const u32x4_t *c, float *out) {
+        if constexpr (F32) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[4 * h + e] = __uint_as_float(a[h][e]) * __uint_as_float(c[h][e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                out[2 * e] = bf_lo(a[0][e]) * bf_lo(c[0][e]);
+                out[2 * e + 1] = bf_hi(a[0][e]) * bf_hi(c[0][e]);
+            }
+        }
+    };
+    // ring row of time t (t >= t_begin - 128)
+    auto ring = [&](int64_t t) -> int { return (int)((t - t_begin + 128) & (kLagRing - 1)); };
+
+    // the 128 rows of x before the span (rows before 0 read as zero)
+    {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int64_t r0 = t_begin - 128 + 64 * half;
+            const int64_t c0 = max(r0, (int64_t)0);
+            const int rows = (int)(r0 + 64 - c0);  // rows of this block at or after row 0
+            const __amdgpu_buffer_rsrc_t rk = window(p.k, c0, rows);
+            const __amdgpu_buffer_rsrc_t rv = window(p.v, c0, rows);
+            const int rel = (int)(r0 - c0);  // <= 0
+            u32x4_t kk[NLD], vv[NLD];
+#pragma unroll
+            for (int h = 0; h < NLD; ++h) {
+                const uint32_t o = off(lr + rel, h);
+                kk[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+                vv[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+            }
+            float x8[8];
+            prod8(kk, vv, x8);
+            const int rr = ring(r0 + lr);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xs[rr][sg * 8 + e] = x8[e];
+        }
+    }
+    // one block's rows of dy, q, k, v in registers
+    u32x4_t dy_r[NLD], q_r[NLD], k_r[NLD], v_r[NLD];
+    auto load_blk = [&](int blk) {
+        const int64_t r0 = min(t_begin + 64 * (int64_t)blk, t_stop);
+        const int rows = (int)min((int64_t)64, t_stop - r0);
+        const __amdgpu_buffer_rsrc_t rd = window(p.dy, r0, rows), rq = window(p.q, r0, rows),
+                                     rk = window(p.k, r0, rows), rv = window(p.v, r0, rows);
+#pragma unroll
+        for (int h = 0; h < NLD; ++h) {
+            const uint32_t o = off(lr, h);
+            dy_r[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rd, o, 0, kLoadPolicy));
+            q_r[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, kLoadPolicy));
+            k_r[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0));
+            v_r[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0));
+        }
+    };
+    load_blk(0);
+
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int64_t t0 = t_begin + 64 * (int64_t)blk;
+        {
+            float z8[8], x8[8];
+            prod8(dy_r, q_r, z8);
+            prod8(k_r, v_r, x8);
+            const int rr = ring(t0 + lr);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                zs[lr][sg * 8 + e] = z8[e];
+                xs[rr][sg * 8 + e] = x8[e];
+            }
+        }
+        load_blk(blk + 1);  // past the span: an empty window, nothing read
+        __syncthreads();
+        float bacc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bacc[i] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < RPT / 8; ++m) {
+            const int u0 = jt * RPT + 8 * m;  // first row of this step, relative to t0
+            float z8[8], xw[23];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) z8[u] = zs[u0 + u][cl];
+            // xw[i] = x[t0 + u0 - 16 jg - 15 + i]
+#pragma unroll
+            for (int i = 0; i < 23; ++i) xw[i] = xs[ring(t0 + u0 - 16 * jg - 15 + i)][cl];
+            // row u, tap 16 jg + k: x index u - k + 15
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int k = 0; k < 16; ++k) bacc[k] = fmaf(z8[u], xw[u - k + 15], bacc[k]);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] += bacc[i];
+        __syncthreads();  // zs and the oldest ring rows are rewritten next
+    }
+    // the time slices' sums, added in slice order; red[jt][cl][tap] in xs
+    float *red = &xs[0][0];
+    constexpr int RP = NT + 1;  // row pitch (words) of one channel's taps
+    static_assert(REPS * kLagCh * RP <= kLagRing * kLagCh, "reduction fits the ring");
+#pragma unroll
+    for (int k = 0; k < 16; ++k) red[(jt * kLagCh + cl) * RP + 16 * jg + k] = acc[k];
+    __syncthreads();
+    float *ws = p.ws + ((size_t)(b * p.n_spans + spn) * p.D + c_begin) * p.l_h;
+    for (int o = tid; o < kLagCh * NT; o += 512) {
+        const int c = o / NT, sidx = o % NT;
+        if (c_begin + c >= p.D || sidx >= p.l_h) continue;
+        float sum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < REPS; ++r) sum += red[(r * kLagCh + c) * RP + sidx];
+        ws[(size_t)c * p.l_h + sidx] = sum;
+    }
+}
+
 // Kernel families and their compiled span counts (indices into kSpans).
-enum Family { kFwd = 0, kRevDual = 1, kDh = 2, kCd = 3, kDqDh = 4, kBwd = 5 };
+enum Family { kFwd = 0, kRevDual = 1, kDh = 2, kCd = 3, kDqDh = 4, kBwd = 5, kCdRevDual = 6 };
 // (the chunk-direction kernel takes its span at run time: one entry)
 template <bool F32, int Fam> constexpr int kSpanCount =
     Fam == kFwd ? kNumSpansFor<F32> : Fam == kRevDual ? (F32 ? 2 : 4) : Fam == kDh ? (F32 ? 3 : 5)
@@ -2027,6 +2248,8 @@ constexpr typename FnType<F32, Fam>::type kernel_of() {
         return hyena_bwd_dq_dh_kernel<KH, Sp, 1, false>;  // bf16 only
     else if constexpr (Fam == kBwd)
         return hyena_bwd_dq_dh_kernel<KH, Sp, 1, true>;  // bf16 only
+    else if constexpr (Fam == kCdRevDual)
+        return hyena_fwd_cd_kernel<F32, KH, true, true>;
     else
         return hyena_fwd_cd_kernel<F32, KH>;
 }
@@ -2233,6 +2456,34 @@ template <bool F32, bool REV = false, bool DUAL = false> KernelFn pick_direct(in
     }
 }
 
+template <bool F32> DhFn pick_lag(int ng2) {
+    switch (ng2) {
+    case 1: return hyena_bwd_dh_lag_kernel<F32, 1>;
+    case 2: return hyena_bwd_dh_lag_kernel<F32, 2>;
+    case 4: return hyena_bwd_dh_lag_kernel<F32, 4>;
+    default: return hyena_bwd_dh_lag_kernel<F32, 8>;
+    }
+}
+
+// Plan of the off-tile filter-gradient pass for filters over kDirTaps taps:
+// kLagCh channels and kLagSpanRows rows (fewer for a shorter sequence) per
+// workgroup; `kh` holds the tap groups of 16 the kernel sums (a power of 2,
+// NG2) and `span` the span in 64-row chunks.
+int lag_plan(int64_t B, int64_t L, int64_t D, int64_t l_h, Plan *pl) {
+    if (D > INT32_MAX / 16) return HYENA_ERR_UNSUPPORTED;
+    const int ng = (int)((l_h + 15) / 16);
+    pl->kh = ng <= 1 ? 1 : ng <= 2 ? 2 : ng <= 4 ? 4 : 8;
+    pl->n_chunks = (L + kChunk - 1) / kChunk;
+    const int64_t rows = min((int64_t)kLagSpanRows, pl->n_chunks * kChunk);
+    pl->span_index = 0;
+    pl->span = rows / kChunk;
+    pl->n_spans = (L + rows - 1) / rows;
+    pl->n_slabs = (D + kLagCh - 1) / kLagCh;
+    pl->workgroups = pl->n_spans * pl->n_slabs * B;
+    if (pl->workgroups > INT32_MAX || B * pl->n_spans > INT32_MAX) return HYENA_ERR_UNSUPPORTED;
+    return HYENA_OK;
+}
+
 template <bool F32> DhFn pick_direct_dh(int lh) {
     switch (lh) {
     case 1: return hyena_bwd_direct_kernel<F32, 1>;
@@ -2339,7 +2590,6 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
     // off the 16-channel tile: a few taps are summed directly, longer
     // filters take the chunk-direction GEMMs (which take no history prefix)
     const bool direct = chunk_dir && l_h <= kDirTaps;
-    if (chunk_dir && !direct && P > 0) return HYENA_ERR_UNSUPPORTED;
     Plan pl;
     st = direct      ? dir_plan(B, L, D, l_h, dtype, span_chunks, &pl)
          : chunk_dir ? cd_plan(B, L, D, l_h, dtype, span_chunks, &pl)
@@ -2382,9 +2632,9 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
 static int dh_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, int dtype,
                    Plan *pl, int64_t *ws_bytes) {
     if (group_size % kTile != 0) {
-        if (l_h > kDirTaps) return HYENA_ERR_UNSUPPORTED;
-        int st = dir_plan(B, L, D, l_h, dtype, 0, pl);
+        int st = l_h <= kDirTaps ? dir_plan(B, L, D, l_h, dtype, 0, pl) : lag_plan(B, L, D, l_h, pl);
         if (st != HYENA_OK) return st;
+        if ((D * (dtype == HYENA_DTYPE_F32 ? 4 : 2)) % 16 != 0) return HYENA_ERR_UNSUPPORTED;
         *ws_bytes = B * pl->n_spans * D * l_h * (int64_t)sizeof(float);
         return HYENA_OK;
     }
@@ -2484,9 +2734,63 @@ static int bwd_entry(const void *q, const void *k, const void *v, const void *h,
         return HYENA_OK;
     }
     const bool f32 = dtype == HYENA_DTYPE_F32;
+    if (group_size % kTile != 0 && l_h > kDirTaps) {
+        // longer filters off the tile: dq is the chunk-direction forward with
+        // dy as the gate; dk and dv the same walked backwards in time (x =
+        // dy q, gated by v and by k); dh the lag products per channel and the
+        // per-group reduction
+        if (dq) {
+            st = fwd_launch(dy, k, v, h, nullptr, nullptr, 0, B, L, D, group_size, l_h, dq, dtype, 0, stream);
+            if (st != HYENA_OK) return st;
+        }
+        if (dk) {
+            Plan pl;
+            st = cd_plan(B, L, D, l_h, dtype, 0, &pl);
+            if (st != HYENA_OK) return st;
+            Params p;
+            p.q = v; p.k = dy; p.v = q; p.h = h; p.y = dk;
+            p.g2 = k; p.y2 = dv;
+            p.kp = nullptr; p.vp = nullptr; p.P = 0;
+            p.span_blocks = (int32_t)(pl.span / (kCdBlock / kChunk));
+            p.span_rows = (int32_t)(pl.span * kChunk);
+            p.L = L;
+            p.D = (int32_t)D;
+            p.group_size = (int32_t)group_size;
+            p.l_h = (int32_t)l_h;
+            p.n_spans = (int32_t)pl.n_spans;
+            p.n_slabs = (int32_t)pl.n_slabs;
+            KernelFn fn = f32 ? pick_kernel<true, kCdRevDual>(pl.kh, 0) : pick_kernel<false, kCdRevDual>(pl.kh, 0);
+            hipLaunchKernelGGL(fn, dim3((unsigned)pl.workgroups), dim3(kCdThreads), 0, (hipStream_t)stream, p);
+            if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+        }
+        if (dh) {
+            DhParams p;
+            p.q = q; p.k = k; p.v = v; p.dy = dy;
+            p.ws = (float *)workspace;
+            p.h = h;
+            p.dq = nullptr; p.dk = nullptr; p.dv = nullptr;
+            p.L = L;
+            p.D = (int32_t)D;
+            p.l_h = (int32_t)l_h;
+            p.n_spans = (int32_t)dpl.n_spans;
+            p.n_slabs = (int32_t)dpl.n_slabs;
+            p.group_size = (int32_t)group_size;
+            p.span_rows = (int32_t)(dpl.span * kChunk);
+            DhFn fn = f32 ? pick_lag<true>(dpl.kh) : pick_lag<false>(dpl.kh);
+            hipLaunchKernelGGL(fn, dim3((unsigned)dpl.workgroups), dim3(512), 0, (hipStream_t)stream, p);
+            if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+            const int G = (int)(D / group_size);
+            const int n = G * (int)l_h;
+            hipLaunchKernelGGL(hyena_bwd_direct_dh_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                               (hipStream_t)stream, (const float *)workspace, dh, (int)(B * dpl.n_spans), (int)D,
+                               (int)group_size, (int)l_h, G);
+            if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+        }
+        return HYENA_OK;
+    }
     if (group_size % kTile != 0) {
-        // short filters off the tile (dh_plan refused longer ones): the
-        // direct kernels, with the direct forward's plan
+        // short filters off the tile: the direct kernels, with the direct
+        // forward's plan
         if (dh) {
             // the whole backward in one walk (any of dq, dk, dv may be absent)
             DhParams p;
@@ -2642,7 +2946,7 @@ const char *hyena_conv_strerror(int status) {
     case HYENA_ERR_FILTER_LEN: return "l_h must be in [1, 128]";
     case HYENA_ERR_ALIGN: return "q, k, v and out must be 16-byte aligned; h element aligned";
     case HYENA_ERR_ALIAS: return "out overlaps an input";
-    case HYENA_ERR_UNSUPPORTED: return "unsupported case (off the 16-channel grouping: rows must be a multiple of 16 bytes, and the backward and history prefix take filters of at most 8 taps; long filters: D must be even and the transform at most 2^22 points; or the shape is too large to address)";
+    case HYENA_ERR_UNSUPPORTED: return "unsupported case (off the 16-channel grouping rows must be a multiple of 16 bytes; long filters: D must be even and the transform at most 2^22 points; or the shape is too large to address)";
     case HYENA_ERR_LAUNCH: return "kernel launch failed";
     case HYENA_ERR_DTYPE: return "unknown dtype code";
     case HYENA_ERR_WORKSPACE: return "workspace missing or smaller than hyena_conv_bwd_workspace reports";

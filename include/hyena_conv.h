@@ -31,9 +31,7 @@
  * instead (same page, section 6): per channel, 16 consecutive 16-row
  * sub-chunks share each Toeplitz block; and for at most 8 taps each output's
  * few products are summed directly.  Off the 16-channel grouping D * element
- * size must be a multiple of 16 bytes, and the history-prefix forward and
- * the backward take filters of at most 8 taps (longer ones return
- * HYENA_ERR_UNSUPPORTED).
+ * size must be a multiple of 16 bytes (else HYENA_ERR_UNSUPPORTED).
  *
  * Layout (all row-major, no strides):
  *   q, k, v, out : [B, L, D], D contiguous.

@@ -228,7 +228,7 @@ def _halo(kp=P["k"] + (64 << 20), vp=P["v"] + (64 << 20), Pn=127, out=P["out"], 
     (dict(Pn=-1), -2), (dict(kp=None), -1), (dict(vp=None), -1),
     (dict(kp=P["k"] + (64 << 20) + 8), -5), (dict(vp=P["v"] + (64 << 20) + 4), -5),
     (dict(out=P["k"] + (64 << 20)), -6), (dict(out=P["v"] + (64 << 20) - 16), -6),
-    (dict(l_h=200), -4), (dict(gs=8, l_h=9), -7),
+    (dict(l_h=200), -4), (dict(D=12, gs=3, l_h=9), -7),
 ])
 def test_halo_entry_validates_its_prefix_on_host(kw, code):
     assert _halo(**kw) == code
@@ -253,7 +253,7 @@ def _bwd(q=P["q"], k=P["k"], v=P["v"], h=P["h"], dy=P["out"] + (64 << 20), B=1, 
     (dict(dq=P["q"]), -6), (dict(dk=P["out"]), -6), (dict(dh=P["k"] + 64), -6),
     (dict(ws=P["v"]), -6), (dict(ws=P["out"] + (16 << 20)), -6),
     (dict(ws=None), -10), (dict(ws_n=16), -10),
-    (dict(l_h=0), -4), (dict(gs=8, l_h=9), -7), (dict(dtype=5), -9),
+    (dict(l_h=0), -4), (dict(D=12, gs=3, l_h=9), -7), (dict(D=12, gs=1, l_h=7), -7), (dict(dtype=5), -9),
 ])
 def test_backward_validates_on_host(kw, code):
     assert _bwd(**kw) == code
@@ -272,8 +272,12 @@ def test_backward_workspace_size():
     for B, L, D, gs, l_h in ((1, 8192, 4096, 1, 7), (2, 1000, 96, 3, 5), (1, 100, 8, 2, 1)):
         span, _ = hc.plan(B, L, D, gs, l_h)
         assert hc.bwd_workspace_bytes(B, L, D, gs, l_h) == B * (-(-L // (64 * span))) * D * l_h * 4
+    # longer filters off the tile: one partial row per 1024-row span, batch
+    # row and channel (the lag-product pass); rows of 24 bytes are refused
+    for B, L, D, gs, l_h in ((1, 8192, 4096, 8, 9), (2, 1000, 96, 3, 128), (3, 2049, 64, 1, 65)):
+        assert hc.bwd_workspace_bytes(B, L, D, gs, l_h) == B * (-(-L // 1024)) * D * l_h * 4
     with pytest.raises(hc.HyenaError):
-        hc.bwd_workspace_bytes(1, 8192, 4096, 8, 9)
+        hc.bwd_workspace_bytes(1, 8192, 12, 3, 9)
 
 
 def _long(q=P["q"], k=P["k"], v=P["v"], h=P["h"], B=1, L=128, D=64, gs=16, l_h=1000,

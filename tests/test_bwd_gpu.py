@@ -262,11 +262,77 @@ def test_backward_off_tile_subsets_match_the_full_call(dt):
                 assert torch.equal(f, g), (name, need)
 
 
-def test_backward_off_tile_long_filters_unsupported():
-    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(1, 128, 64, 8, 9, torch.bfloat16, seed=3))
-    with pytest.raises(hc.HyenaError) as ei:
-        hc.conv_bwd(q, k, v, h, q, 8)
-    assert ei.value.status == -7
+# Off the 16-channel tile with more than 8 taps: dq and dk, dv from the
+# chunk-direction kernel (forward, and walked backwards in time with two
+# gates), dh from per-channel lag products and the per-group reduction.
+# B, L, D, group_size, l_h: group sizes 1, 3 and 8 and filters of 9, 65 and
+# 128 taps among them, lengths across 64-row blocks, 256-row chunk-direction
+# blocks and 1024-row filter-gradient spans, partial channel slabs.
+BWD_CD_SHAPES = [
+    (1, 300, 64, 1, 9), (2, 1000, 72, 3, 65), (1, 700, 128, 8, 128), (1, 2100, 40, 5, 100),
+    (3, 64, 24, 3, 33), (1, 1, 16, 8, 9), (2, 130, 48, 1, 128), (1, 1030, 264, 8, 65),
+    (1, 500, 72, 3, 9), (2, 257, 64, 1, 65), (1, 1100, 24, 3, 128),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h", BWD_CD_SHAPES)
+def test_backward_off_tile_long_filters_gaussian(dt, B, L, D, gs, l_h):
+    log("bwd cd %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=13 * L + l_h + gs)
+    dy = normal_activation((B, L, D), dtype, "cpu", seed=L + 19)
+    grads = _bwd_gpu(*[t.to(DEV) for t in (q, k, v, h, dy)], gs)
+    ref, env = _refs(q, k, v, h, dy, gs)
+    _check_all(grads, ref, env, l_h, dtype, _direct_rows(B, L, D, gs, l_h, dtype), "bwd cd")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h", [(1, 300, 64, 1, 9), (2, 777, 96, 3, 65), (1, 600, 264, 8, 128)])
+def test_backward_off_tile_long_filters_integer_bitwise(dt, B, L, D, gs, l_h):
+    log("bwd cd integer %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = integer_inputs(B, L, D, gs, l_h, dtype, seed=L + 23)
+    dy = integer_inputs(B, L, D, gs, 1, dtype, seed=L + 24)[0]
+    grads = _bwd_gpu(*[t.to(DEV) for t in (q, k, v, h, dy)], gs)
+    ref = oracle.conv_bwd_ref(*[to_np(t) for t in (q, k, v, h, dy)], gs)
+    for name, g, r in zip(("dq", "dk", "dv", "dh"), grads, ref):
+        assert np.array_equal(to_np(g), r), name
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_backward_off_tile_long_filters_subsets_and_determinism(dt):
+    """Each gradient has one kernel whatever else is requested, so every
+    subset gives the full call's bits; a second call gives the same bits."""
+    dtype = DTYPES[dt]
+    B, L, D, gs, l_h = 2, 1300, 72, 3, 100
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=43)
+    dy = normal_activation((B, L, D), dtype, "cpu", seed=44)
+    dev = [t.to(DEV) for t in (q, k, v, h, dy)]
+    full = hc.conv_bwd(*dev, gs)
+    again = hc.conv_bwd(*dev, gs)
+    torch.cuda.synchronize()
+    for f, g in zip(full, again):
+        assert torch.equal(f, g)
+    for need in SUBSETS:
+        part = hc.conv_bwd(*dev, gs, need_dq=need[0], need_dkv=need[1], need_dh=need[2])
+        torch.cuda.synchronize()
+        wanted = (need[0], need[1], need[1], need[2])
+        for name, want, f, g in zip(("dq", "dk", "dv", "dh"), wanted, full, part):
+            assert (g is not None) == want, (name, need)
+            if want:
+                assert torch.equal(f, g), (name, need)
+
+
+def test_backward_off_tile_one_filter_per_channel_medium():
+    """group_size 1, l_h = 128 (the MR filter length), B=1, L=2048, D=512 bf16."""
+    B, L, D, gs, l_h = 1, 2048, 512, 1, 128
+    log("bwd cd medium")
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, torch.bfloat16, seed=51)
+    dy = normal_activation((B, L, D), torch.bfloat16, "cpu", seed=52)
+    grads = _bwd_gpu(*[t.to(DEV) for t in (q, k, v, h, dy)], gs)
+    ref, env = _refs(q, k, v, h, dy, gs)
+    _check_all(grads, ref, env, l_h, torch.bfloat16, _direct_rows(B, L, D, gs, l_h, torch.bfloat16), "bwd cd medium")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])

@@ -200,13 +200,32 @@ def test_direct_short_filter_span_independent_and_causal():
     assert not torch.equal(y0[:, t0], y1[:, t0])
 
 
-def test_halo_and_backward_off_tile_need_short_filters():
-    """Off the 16-channel tile, the history-prefix forward and the backward
-    take the direct kernels: filters longer than 8 taps are rejected."""
-    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(1, 128, 64, 8, 9, torch.bfloat16, seed=3))
-    with pytest.raises(hc.HyenaError) as ei:
-        hc.conv_fwd(q, k, v, h, 8, k_prev=k[:, :8].contiguous(), v_prev=v[:, :8].contiguous())
-    assert ei.value.status == -7
-    with pytest.raises(hc.HyenaError) as ei:
-        hc.conv_bwd(q, k, v, h, q, 8)
-    assert ei.value.status == -7
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h,split,Pn", [
+    (1, 1000, 64, 1, 9, 256, 8), (2, 1100, 72, 3, 65, 512, 64), (1, 900, 128, 8, 128, 768, 127),
+    (1, 1500, 40, 1, 128, 1024, 200), (2, 800, 24, 3, 100, 256, 30), (1, 700, 64, 2, 33, 100, 40),
+    (1, 600, 64, 1, 128, 320, 127),
+])
+def test_off_tile_long_filter_shard_with_prefix(dt, B, L, D, gs, l_h, split, Pn):
+    """Off the 16-channel tile, filters over 8 taps: the chunk-direction
+    kernel reads the rows before row 0 of the first span from the caller's
+    prefix (StripedHyena 2 explainer, page "01. overview", section 5).  Each
+    output's sum runs over its 16-row sub-chunk's input steps, so where the
+    split is a multiple of 16 and the prefix covers the filter the shard has
+    the whole sequence's bits; every shard is checked against the oracle on
+    the concatenated sequence (a short prefix means zeros before it)."""
+    log("halo cd %s B=%d L=%d D=%d gs=%d l_h=%d split=%d P=%d" % (dt, B, L, D, gs, l_h, split, Pn))
+    dtype = DTYPES[dt]
+    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(B, L, D, gs, l_h, dtype, seed=split + l_h + gs + D))
+    full = run(q, k, v, h, gs)
+    sl = lambda a: a[:, split:].contiguous()
+    kp = k[:, split - Pn:split].contiguous()
+    vp = v[:, split - Pn:split].contiguous()
+    shard = torch.full_like(sl(q), float("nan"))
+    hc.conv_fwd(sl(q), sl(k), sl(v), h, gs, out=shard, k_prev=kp, v_prev=vp)
+    torch.cuda.synchronize()
+    if split % 16 == 0 and Pn >= l_h - 1:
+        assert torch.equal(shard, full[:, split:])
+    qc, kc, vc = (a[:, split - Pn:].cpu() for a in (q, k, v))
+    ref, env = ref_and_envelope(qc, kc, vc, h.cpu(), gs)
+    check(to_np(shard), ref[:, Pn:], env[:, Pn:], l_h, dtype, "halo cd shard")

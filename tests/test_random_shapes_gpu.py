@@ -57,6 +57,21 @@ def _draw(kind, seed):
             L = min(L, 1500)
             l_h = int(rng.integers(1, 129))
             cases.append((dt, B, L, D, gs, l_h, 0))
+        elif kind == "backward_off_tile":
+            gs = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 12, 24]))
+            unit = np.lcm(gs, 8 if dt == "bf16" else 4)  # whole 16-byte rows
+            D = int(unit * rng.integers(1, max(2, 192 // unit) + 1))
+            L = min(L, 1500)
+            l_h = int(rng.integers(1, 129))
+            cases.append((dt, B, L, D, gs, l_h, 0))
+        elif kind == "halo":
+            gs = int(rng.choice([1, 3, 8, 16, 32]))
+            unit = np.lcm(gs, 8 if dt == "bf16" else 4) if gs % 16 else gs
+            D = int(unit * rng.integers(1, max(2, 192 // unit) + 1))
+            L = max(L, 2)
+            l_h = int(rng.integers(1, 129))
+            # (the span column carries the prefix length P)
+            cases.append((dt, B, L, D, gs, l_h, int(rng.integers(0, 200))))
         else:  # long filters
             gs = int(rng.choice([1, 2, 3, 4, 8, 16]))
             D = int(np.lcm(gs, 2) * rng.integers(1, max(2, 48 // np.lcm(gs, 2)) + 1))
@@ -73,6 +88,8 @@ GROUPED = _draw("grouped", 101)
 CHUNK_DIR = _draw("chunk_direction", 202)
 BACKWARD = _draw("backward", 303)
 LONG = _draw("long", 404)
+BACKWARD_OFF = _draw("backward_off_tile", 505)
+HALO = _draw("halo", 606)
 
 
 @pytest.mark.parametrize("dt,B,L,D,gs,l_h,span", GROUPED, ids=_ids(GROUPED))
@@ -114,3 +131,39 @@ def test_random_long_filter(dt, B, L, D, gs, l_h, span):
     q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B * 100057 + L * 17 + D + l_h)
     y = run_long(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), gs)
     check_long(y, q, k, v, h, gs, dtype, "random long filter")
+
+
+@pytest.mark.parametrize("dt,B,L,D,gs,l_h,span", BACKWARD_OFF, ids=_ids(BACKWARD_OFF))
+def test_random_backward_off_tile(dt, B, L, D, gs, l_h, span):
+    """Group sizes off the 16-channel tile: the direct kernels (8 taps or
+    fewer) or the chunk-direction kernel and the lag products (longer)."""
+    log("random backward off tile %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B * 100069 + L * 19 + D + l_h)
+    dy = normal_activation((B, L, D), dtype, "cpu", seed=L + D + 5)
+    grads = hc.conv_bwd(*[t.to(DEV) for t in (q, k, v, h, dy)], gs)
+    torch.cuda.synchronize()
+    ref, env = bwd_refs(q, k, v, h, dy, gs)
+    code = hc.DTYPE_BF16 if dtype == torch.bfloat16 else hc.DTYPE_F32
+    rows = max(1, hc.bwd_workspace_bytes(B, L, D, gs, l_h, code) // (D * l_h * 4)) * gs
+    check_bwd(grads, ref, env, l_h, dtype, rows, "random backward off tile")
+
+
+@pytest.mark.parametrize("dt,B,L,D,gs,l_h,P", HALO, ids=_ids(HALO))
+def test_random_history_prefix(dt, B, L, D, gs, l_h, P):
+    """A shard of a longer sequence: the last L rows of P + L, with the first
+    P rows passed as the prefix, against the oracle on the whole sequence."""
+    log("random prefix %s B=%d L=%d D=%d gs=%d l_h=%d P=%d" % (dt, B, L, D, gs, l_h, P))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, P + L, D, gs, l_h, dtype, seed=B * 100103 + L * 23 + D + l_h + P)
+    qd, kd, vd, hd = (t.to(DEV) for t in (q, k, v, h))
+    sl = lambda a: a[:, P:].contiguous()
+    out = torch.full_like(sl(qd), float("nan"))
+    if P:
+        hc.conv_fwd(sl(qd), sl(kd), sl(vd), hd, gs, out=out, k_prev=kd[:, :P].contiguous(),
+                    v_prev=vd[:, :P].contiguous())
+    else:
+        hc.conv_fwd(sl(qd), sl(kd), sl(vd), hd, gs, out=out)
+    torch.cuda.synchronize()
+    ref, env = ref_and_envelope(q, k, v, h, gs)
+    check(to_np(out), ref[:, P:], env[:, P:], l_h, dtype, "random prefix")

@@ -34,7 +34,8 @@ STATUS = {
 EXPORTS = ("hyena_conv_fwd", "hyena_conv_fwd_f32", "hyena_conv_fwd_ex", "hyena_conv_fwd_halo",
            "hyena_conv_bwd", "hyena_conv_bwd_workspace", "hyena_conv_fwd_long",
            "hyena_conv_fwd_long_workspace", "hyena_conv_plan", "hyena_conv_strerror",
-           "hyena_conv_block_len", "hyena_conv_bwd_noalloc", "hyena_conv_scratch_bytes")
+           "hyena_conv_block_len", "hyena_conv_bwd_noalloc", "hyena_conv_scratch_bytes",
+           "hyena_conv_fwd_long_ex")
 
 
 class HyenaError(RuntimeError):
@@ -81,6 +82,9 @@ def lib() -> ctypes.CDLL:
         L.hyena_conv_fwd_long.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, ctypes.c_int,
                                           vp, i64, vp]
         L.hyena_conv_fwd_long.restype = ctypes.c_int
+        L.hyena_conv_fwd_long_ex.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, ctypes.c_int,
+                                             vp, i64, ctypes.c_int, vp]
+        L.hyena_conv_fwd_long_ex.restype = ctypes.c_int
         L.hyena_conv_fwd_long_workspace.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                                     ctypes.POINTER(i64)]
         L.hyena_conv_fwd_long_workspace.restype = ctypes.c_int
@@ -251,11 +255,14 @@ def long_workspace_bytes(B: int, L: int, D: int, group_size: int, l_h: int,
 def conv_fwd_long(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Tensor,
                   group_size: int, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None,
-                  stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+                  stream: Optional[torch.cuda.Stream] = None,
+                  reuse_spectra: bool = False) -> torch.Tensor:
     """y = q (.) (h * (k (.) v)) by FFT convolution, for filters of any length.
 
     Same tensors as conv_fwd; h is [D // group_size, l_h] with any l_h >= 1.
     ``workspace`` (uint8, on q's device) is allocated here if not given.
+    ``reuse_spectra``: the workspace already holds h's spectra from an
+    earlier call with the same h, L and sizes (hyena_conv_fwd_long_ex).
     """
     dt, dev = q.dtype, q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("h", h)):
@@ -273,6 +280,8 @@ def conv_fwd_long(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Te
     elif out.shape != q.shape or out.dtype != dt or out.device != dev or not out.is_contiguous():
         raise ValueError("out must be a contiguous tensor like q")
     ws_n = long_workspace_bytes(B, L, D, group_size, l_h, code)
+    if reuse_spectra and workspace is None:
+        raise ValueError("reuse_spectra needs the workspace of an earlier call")
     if workspace is None:
         workspace = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
@@ -281,14 +290,14 @@ def conv_fwd_long(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Te
         stream = torch.cuda.current_stream(dev)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(), B, L, D, group_size, l_h,
             out.data_ptr(), code, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-            stream.cuda_stream)
+            int(bool(reuse_spectra)), stream.cuda_stream)
     if dev.index == torch.cuda.current_device():
-        st = lib().hyena_conv_fwd_long(*args)
+        st = lib().hyena_conv_fwd_long_ex(*args)
     else:
         with torch.cuda.device(dev):
-            st = lib().hyena_conv_fwd_long(*args)
+            st = lib().hyena_conv_fwd_long_ex(*args)
     if st != 0:
-        raise HyenaError(st, "hyena_conv_fwd_long")
+        raise HyenaError(st, "hyena_conv_fwd_long_ex")
     return out
 
 

@@ -770,21 +770,22 @@ int hyena_conv_fwd_long_workspace(int64_t B, int64_t L, int64_t D, int64_t group
     return HYENA_OK;
 }
 
-int hyena_conv_fwd_long(const void *q, const void *k, const void *v, const void *h, int64_t B, int64_t L,
-                        int64_t D, int64_t group_size, int64_t l_h, void *out, int dtype, void *workspace,
-                        int64_t workspace_bytes, void *stream) {
+int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v, const void *h, int64_t B, int64_t L,
+                           int64_t D, int64_t group_size, int64_t l_h, void *out, int dtype, void *workspace,
+                           int64_t workspace_bytes, int reuse_spectra, void *stream) {
     FftPlan pl;
     int st = fft_plan(B, L, D, group_size, l_h, dtype, &pl);
     if (st != HYENA_OK) return st;
+    if (reuse_spectra != 0 && reuse_spectra != 1) return HYENA_ERR_SHAPE;
     if (B == 0 || L == 0 || D == 0) return HYENA_OK;
-    if (!q || !k || !v || !h || !out) return HYENA_ERR_NULL;
+    if (!q || !k || !v || (!h && !reuse_spectra) || !out) return HYENA_ERR_NULL;
     if (!workspace || workspace_bytes < pl.ws_bytes) return HYENA_ERR_WORKSPACE;
     const size_t eb = dtype == HYENA_DTYPE_F32 ? 4 : 2;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)workspace) & 15u)
         return HYENA_ERR_ALIGN;
     if ((uintptr_t)h & (eb - 1)) return HYENA_ERR_ALIGN;
     const size_t nbytes = (size_t)B * (size_t)L * (size_t)D * eb;
-    const size_t hbytes = (size_t)(D / group_size) * (size_t)l_h * eb;
+    const size_t hbytes = h ? (size_t)(D / group_size) * (size_t)l_h * eb : 0;
     const size_t wbytes = (size_t)pl.ws_bytes;
     if (overlaps(out, nbytes, q, nbytes) || overlaps(out, nbytes, k, nbytes) || overlaps(out, nbytes, v, nbytes) ||
         overlaps(out, nbytes, h, hbytes) || overlaps(workspace, wbytes, q, nbytes) ||
@@ -838,14 +839,17 @@ int hyena_conv_fwd_long(const void *q, const void *k, const void *v, const void 
     const int64_t row_units = pl.three ? (int64_t)pl.N1 * pl.N2 : pl.N1;
     const int64_t mid_units = (int64_t)pl.N1 * pl.N3;
 
-    // filter spectra: the filters as one sequence of G channels, min(l_h, L) rows
-    FftParams ph = p;
-    ph.L = l_h < L ? l_h : L;
-    ph.np = p.Gp / 2;
-    st = launch(rows_flt, ph, pl.P_rows, row_units, 1, pl.lds_rows);
-    if (st == HYENA_OK && pl.three)
-        st = launch((const void *)fft_mid_kernel<false>, ph, pl.P_mid, mid_units, 1, pl.lds_mid);
-    if (st == HYENA_OK) st = launch((const void *)fft_cols_kernel<0>, ph, pl.P_cols, cols, 1, pl.lds_cols);
+    // filter spectra: the filters as one sequence of G channels, min(l_h, L)
+    // rows (kept from an earlier call when the caller says so)
+    if (!reuse_spectra) {
+        FftParams ph = p;
+        ph.L = l_h < L ? l_h : L;
+        ph.np = p.Gp / 2;
+        st = launch(rows_flt, ph, pl.P_rows, row_units, 1, pl.lds_rows);
+        if (st == HYENA_OK && pl.three)
+            st = launch((const void *)fft_mid_kernel<false>, ph, pl.P_mid, mid_units, 1, pl.lds_mid);
+        if (st == HYENA_OK) st = launch((const void *)fft_cols_kernel<0>, ph, pl.P_cols, cols, 1, pl.lds_cols);
+    }
     // the sequence
     p.L = L;
     p.np = (int32_t)(D / 2);
@@ -862,6 +866,13 @@ int hyena_conv_fwd_long(const void *q, const void *k, const void *v, const void 
     if (st != HYENA_OK) return st;
     if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
     return HYENA_OK;
+}
+
+int hyena_conv_fwd_long(const void *q, const void *k, const void *v, const void *h, int64_t B, int64_t L,
+                        int64_t D, int64_t group_size, int64_t l_h, void *out, int dtype, void *workspace,
+                        int64_t workspace_bytes, void *stream) {
+    return hyena_conv_fwd_long_ex(q, k, v, h, B, L, D, group_size, l_h, out, dtype, workspace, workspace_bytes, 0,
+                                  stream);
 }
 
 }  // extern "C"

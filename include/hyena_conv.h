@@ -196,11 +196,28 @@ int hyena_conv_bwd_workspace(int64_t B, int64_t L, int64_t D,
  * initialised) receives the filter spectra and the transform work area.  D
  * must be even (channels are transformed in pairs), else
  * HYENA_ERR_UNSUPPORTED.  Inputs, output and workspace must not overlap.  The
- * filter spectra are recomputed on every call. */
+ * filter spectra are recomputed on every call (hyena_conv_fwd_long_ex can
+ * keep them). */
 int hyena_conv_fwd_long(const void *q, const void *k, const void *v,
                         const void *h, int64_t B, int64_t L, int64_t D,
                         int64_t group_size, int64_t l_h, void *out, int dtype,
                         void *workspace, int64_t workspace_bytes, void *stream);
+
+/* hyena_conv_fwd_long with the filter spectra kept across calls.  The
+ * spectra occupy the first 8 N G' bytes of `workspace` (N the transform
+ * length, G' the filter count rounded up to even; they depend on L, l_h, D,
+ * group_size and the filter, not on B).  reuse_spectra = 0: compute them
+ * from h, as hyena_conv_fwd_long does; 1: the workspace already holds them,
+ * left there by an earlier call on this stream with the same h, L, l_h, D,
+ * group_size and dtype, and h is not read (it may be NULL).  The result has
+ * the same bits either way.  With a workspace that does not hold them, the
+ * output is meaningless (nothing is checked on the device).  Any other
+ * reuse_spectra value returns HYENA_ERR_SHAPE. */
+int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v,
+                           const void *h, int64_t B, int64_t L, int64_t D,
+                           int64_t group_size, int64_t l_h, void *out, int dtype,
+                           void *workspace, int64_t workspace_bytes,
+                           int reuse_spectra, void *stream);
 
 /* Bytes of workspace hyena_conv_fwd_long needs (written to *bytes_out):
  * 8 N (max(B D/2, G'/2) + G'), N the transform length and G' the filter

@@ -325,3 +325,13 @@ def test_long_filter_plan_rejects_unaddressable_sizes():
     assert ws(1, 100, (1 << 30) - 2, 1, (1 << 31) - 1) == -2  # G l_h taps overflow
     assert _long(l_h=1 << 31) == -7
     assert _long(B=1 << 40, L=1 << 20, D=1 << 20) == -2
+
+
+def test_long_filter_spectra_flag_is_checked_on_host():
+    lib = hc.lib()
+    a = dict(q=P["q"], k=P["k"], v=P["v"], h=P["h"], out=P["out"], ws=P["out"] + (64 << 20))
+    call = lambda h, flag: lib.hyena_conv_fwd_long_ex(a["q"], a["k"], a["v"], h, 1, 128, 64, 16, 1000,
+                                                      a["out"], hc.DTYPE_BF16, a["ws"], 1 << 10, flag, None)
+    assert call(a["h"], 2) == -2 and call(a["h"], -1) == -2
+    assert call(None, 0) == -1          # the spectra are computed from h
+    assert call(None, 1) == -10         # h is not needed with kept spectra; the workspace still is

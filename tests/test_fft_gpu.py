@@ -167,3 +167,28 @@ def test_rejects_odd_width():
     with pytest.raises(hc.HyenaError) as ei:
         hc.conv_fwd_long(q5, q5, q5, torch.zeros(5, 20, device=DEV, dtype=torch.bfloat16), 1)
     assert ei.value.status == -7
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("L,D,gs,l_h", [(1000, 64, 16, 1000), (3000, 48, 3, 700), (300, 8, 1, 5000)])
+def test_kept_filter_spectra_give_the_same_bits(dt, L, D, gs, l_h):
+    """hyena_conv_fwd_long_ex with reuse_spectra: a call on other inputs (and
+    another batch size) with the spectra an earlier call left in the
+    workspace equals a call that computes them, bit for bit; the rest of the
+    workspace is filled with NaN in between."""
+    dtype = DTYPES[dt]
+    log("kept spectra %s L=%d D=%d gs=%d l_h=%d" % (dt, L, D, gs, l_h))
+    qa, ka, va, h = (t.to(DEV) for t in gaussian_inputs(1, L, D, gs, l_h, dtype, seed=L + 1))
+    qb, kb, vb, _ = (t.to(DEV) for t in gaussian_inputs(3, L, D, gs, l_h, dtype, seed=L + 2))
+    code = hc.DTYPE_BF16 if dtype == torch.bfloat16 else hc.DTYPE_F32
+    ws = torch.empty(hc.long_workspace_bytes(3, L, D, gs, l_h, code), dtype=torch.uint8, device=DEV)
+    hc.conv_fwd_long(qa, ka, va, h, gs, workspace=ws)
+    n = 1 << max(2, (L + min(l_h, L) - 2).bit_length())
+    G = D // gs
+    spectra = 8 * n * (G + (G & 1))
+    ws[spectra:].view(torch.float32).fill_(float("nan"))
+    kept = hc.conv_fwd_long(qb, kb, vb, h, gs, workspace=ws, reuse_spectra=True)
+    fresh = hc.conv_fwd_long(qb, kb, vb, h, gs)
+    torch.cuda.synchronize()
+    assert torch.equal(kept, fresh)
+    check_long(kept, qb.cpu(), kb.cpu(), vb.cpu(), h.cpu(), gs, dtype, "kept spectra")

@@ -234,9 +234,11 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     // previous one; row-major, swizzled) and the filters.
     __shared__ __attribute__((aligned(16))) unsigned char xs[kChunk * T::PITCH];
     __shared__ __attribute__((aligned(16))) unsigned char st[kStBufs * kChunk * ST_PITCH];
-    // the filter, zero outside [0, l_h), index tap + kHOff: fp32 taps, or in
-    // bf16 pairs (h[t], h[t-1]) in one dword (low, high half), so a Toeplitz
-    // fragment (8 taps descending) is 4 dwords two entries apart
+    // the filter, zero outside [0, l_h): fp32 taps at index tap + kHOff, or
+    // in bf16 pairs (h[t], h[t-1]) in one dword (low, high half) at index
+    // kHLen - 1 - (t + kHOff), so that a Toeplitz fragment (8 taps
+    // descending) is 4 dwords two entries apart at rising addresses, in
+    // fragment order
     __shared__ std::conditional_t<F32, float, uint32_t> hs[NW][kHLen];
 
     const int tid = threadIdx.x;
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
                 const uint16_t *hg = (const uint16_t *)p.h + (size_t)g * p.l_h;
                 const uint32_t lo = tile_ok && tap >= 0 && tap < p.l_h ? hg[tap] : 0u;
                 const uint32_t hi = tile_ok && tap >= 1 && tap <= p.l_h ? hg[tap - 1] : 0u;
-                hs[w][i] = lo | (hi << 16);
+                hs[w][kHLen - 1 - i] = lo | (hi << 16);
             }
         }
     }
@@ -413,13 +415,18 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     // of 16 rows), fp32 e4 = 4 nt - kappa (units of 4 rows).
     constexpr int NE = F32 ? 16 + NH : 4 + 2 * KH;
     frag F[FLY ? 1 : NE];
-    // bf16 Toeplitz fragment e: element j = h[16 e + n16 - 8 q4 - j]
+    // bf16 Toeplitz fragment e: element j = h[16 e + n16 - 8 q4 - j], i.e.
+    // the pairs of taps 16 e + n16 - 8 q4 - 2 m, m = 0..3, which sit at
+    // entries kHLen - 1 - kHOff - 16 e - n16 + 8 q4 + 2 m: one base per lane
+    // (that of e = NE - 1, at least 0) and constant offsets
+    const uint32_t *hbase = nullptr;
+    if constexpr (!F32) hbase = &hs[w][kHLen - 1 - kHOff - 16 * (NE - 1) - n16 + 8 * q4];
     auto tap_frag = [&](int e) -> frag {
         if constexpr (F32) {
             return frag{};
         } else {
-            const uint32_t *hw = &hs[w][16 * e + n16 - 8 * q4 + kHOff];
-            const u32x4_t d = {hw[0], hw[-2], hw[-4], hw[-6]};
+            const uint32_t *hw = hbase + 16 * (NE - 1 - e);
+            const u32x4_t d = {hw[0], hw[2], hw[4], hw[6]};
             return __builtin_bit_cast(frag, d);
         }
     };
@@ -459,9 +466,12 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
             // same (ascending) order as below
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            // each fragment is read while the previous one's MFMAs run
+            frag fnext = tap_frag(NE - 1);
 #pragma unroll
             for (int e = NE - 1; e >= 0; --e) {
-                const frag fe = tap_frag(e);
+                const frag fe = fnext;
+                if (e > 0) fnext = tap_frag(e - 1);
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
                     if ((nt - e) % 2 != 0) continue;

@@ -233,7 +233,14 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     // accumulators of the current chunk (and, with two staging buffers, of the
     // previous one; row-major, swizzled) and the filters.
     __shared__ __attribute__((aligned(16))) unsigned char xs[kChunk * T::PITCH];
-    __shared__ __attribute__((aligned(16))) unsigned char st[kStBufs * kChunk * ST_PITCH];
+    // 16-wave form with history (Toeplitz fragments built per use): the
+    // gated output is staged instead of the accumulators (see gate below)
+    constexpr bool GSTAGE = !F32 && NW > kWaves && KH >= 2;
+    __shared__ __attribute__((aligned(16))) unsigned char st[GSTAGE ? 16 : kStBufs * kChunk * ST_PITCH];
+    // (GSTAGE) q of the next compute item, and two tiles of gated output,
+    // bf16 row-major with 16- and 8-byte units XOR-swizzled by row (gaddr)
+    __shared__ __attribute__((aligned(16))) unsigned char qs[GSTAGE ? kChunk * T::PITCH : 16];
+    __shared__ __attribute__((aligned(16))) unsigned char ys[GSTAGE ? 2 * kChunk * T::PITCH : 16];
     // the filter, zero outside [0, l_h): fp32 taps at index tap + kHOff, or
     // in bf16 pairs (h[t], h[t-1]) in one dword (low, high half) at index
     // kHLen - 1 - (t + kHOff), so that a Toeplitz fragment (8 taps
@@ -549,6 +556,69 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
                 __builtin_amdgcn_raw_buffer_store_b128(yv[NG - 1][i], ry2, io_off(c, i, true), 0, kFwdStorePolicy);
         }
     };
+    // ---- (GSTAGE) gated staging.  Two tiles of fp32 accumulators would not
+    // fit beside the 16-wave x tile, so each compute item gates its own
+    // accumulators, y = q acc in fp32 rounded to bf16 (the same values as
+    // gating row-major), in the MFMA layout, with q read from LDS, and
+    // stages y: two 32 KiB tiles, so that an item's write-back runs while
+    // the next item's MFMAs execute.  Byte b of row r sits at
+    //     r PITCH + 16 ((b >> 4) ^ U(r)) + 8 (((b >> 3) & 1) ^ V(r)) + (b & 7),
+    //     U(r) = (r & 7) ^ 2 ((r >> 3) & 3),   V(r) = (r >> 3) & 1:
+    // the 16 rows of an MFMA tile at one 8-byte channel quad land on 32
+    // distinct banks, and a row's 16-byte units stay a permutation of the
+    // row's (row-major accesses are conflict-free too).
+    auto gaddr = [](int row, int byte) -> int {
+        const int u = (row & 7) ^ (((row >> 3) & 3) << 1);
+        const int v = (row >> 3) & 1;
+        return row * T::PITCH + (((byte >> 4) ^ u) << 4) + ((((byte >> 3) & 1) ^ v) << 3) + (byte & 7);
+    };
+    // start of the 16-byte unit holding byte b of row r (a 16-byte access
+    // there carries the unit's halves swapped where V = 1)
+    auto gaddr16 = [](int row, int byte) -> int {
+        const int u = (row & 7) ^ (((row >> 3) & 3) << 1);
+        return row * T::PITCH + (((byte >> 4) ^ u) << 4);
+    };
+    // this thread's rows of a row-major 16-byte vector -> tile, and back
+    auto put_rows = [&](unsigned char *tile, const u32x4_t *src) {
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const int row = i * T::RPL + ld_row;
+            const u32x4_t x = src[i];
+            const u32x4_t xs2 = ((row >> 3) & 1) ? u32x4_t{x[2], x[3], x[0], x[1]} : x;
+            *(u32x4_t *)(&tile[gaddr16(row, ld_seg * 16)]) = xs2;
+        }
+    };
+    auto get_rows = [&](const unsigned char *tile, u32x4_t *dst) {
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i) {
+            const int row = i * T::RPL + ld_row;
+            const u32x4_t x = *(const u32x4_t *)(&tile[gaddr16(row, ld_seg * 16)]);
+            dst[i] = ((row >> 3) & 1) ? u32x4_t{x[2], x[3], x[0], x[1]} : x;
+        }
+    };
+    // y = q acc of compute item j in the MFMA layout (lane: output time
+    // 16 nt + n16, channels 4 q4 .. 4 q4 + 3 of this wave's group) -> ys
+    auto gate = [&](int j, const f32x4_t *acc) {
+        unsigned char *yt = ys + (j & 1) * (kChunk * T::PITCH);
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int a = gaddr(16 * nt + n16, (16 * w + 4 * q4) * 2);
+            const u32x2_t qv = *(const u32x2_t *)(&qs[a]);
+            const u32x2_t yv = {pack_bf16(bf_lo(qv[0]) * acc[nt][0], bf_hi(qv[0]) * acc[nt][1]),
+                                pack_bf16(bf_lo(qv[1]) * acc[nt][2], bf_hi(qv[1]) * acc[nt][3])};
+            *(u32x2_t *)(&yt[a]) = yv;
+        }
+    };
+    // write-back of compute item j from its ys tile
+    auto finish_g = [&](int j) {
+        const int c = cp_chunk(j);
+        u32x4_t yv[T::NLD];
+        get_rows(ys + (j & 1) * (kChunk * T::PITCH), yv);
+#pragma unroll
+        for (int i = 0; i < T::NLD; ++i)
+            __builtin_amdgcn_raw_buffer_store_b128(yv[i], ry, io_off(c, i, true), 0, kFwdStorePolicy);
+    };
+
     // compute item j.  With two staging buffers the previous item's
     // epilogue runs here, while this item's MFMAs execute; its buffer was
     // completed before the last barrier, and the buffer this item stages
@@ -557,12 +627,18 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     auto compute = [&](int j, const frag *Xc) {
         f32x4_t acc[4];
         mma(Xc, acc);
-        if constexpr (kStBufs == 2) {
-            if (j > 0) finish(j - 1);
+        if constexpr (GSTAGE) {
+            if (j > 0) finish_g(j - 1);
+            gate(j, acc);
+            __syncthreads();
+        } else {
+            if constexpr (kStBufs == 2) {
+                if (j > 0) finish(j - 1);
+            }
+            stage(j, acc);
+            __syncthreads();
+            if constexpr (kStBufs == 1) finish(j);
         }
-        stage(j, acc);
-        __syncthreads();
-        if constexpr (kStBufs == 1) finish(j);
     };
 
     // ---- the walk: ingest items, each compute item right after its last
@@ -579,6 +655,16 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
             store_x(kr[i % PF], vr[i % PF]);
             const int n = i + PF;  // the ingest item this slot loads next
             load_kv(n < NI ? (DESC ? S - 1 - n : n - H) : S, n < NI, kr[i % PF], vr[i % PF]);
+            if constexpr (GSTAGE) {
+                // q of the compute item this ingest completes -> qs, and its
+                // slot refilled with the compute item PF ahead
+                const int jq = i - H;
+                if (jq >= 0) {
+                    put_rows(qs, qr[jq % PF][0]);
+                    const int nq = jq + PF;
+                    load_q(nq < S ? (DESC ? S - 1 - nq : nq) : S, nq < S, qr[jq % PF]);
+                }
+            }
             __syncthreads();
             read_frags(&Xa[i * M::FPC]);
             const int j = i - H;  // the compute item whose inputs are now all in
@@ -656,7 +742,10 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     } else {
         walk(std::false_type{});
     }
-    if constexpr (kStBufs == 2) finish(S - 1);
+    if constexpr (GSTAGE)
+        finish_g(S - 1);
+    else if constexpr (kStBufs == 2)
+        finish(S - 1);
 }
 
 // ---------------------------------------------------------------------------

@@ -28,7 +28,8 @@ Reported (one JSON line):
                (8 taps or fewer; with its backward) or the chunk-direction
                GEMM kernel;
   long_filter  a filter as long as the sequence (the FFT path), with the
-               filter spectra computed per call and kept across calls;
+               filter spectra computed per call and kept across calls, and
+               its backward (dq, dk, dv, dh);
   backward     dq, dk, dv and dh of each layer;
   stream_reference  a hand-written read-3/write-1 streaming kernel with the
                forward's access pattern (256- and 512-byte row segments; the
@@ -735,6 +736,23 @@ def long_filter_rates(w, stream, reps):
         return e0.elapsed_time(e1) * 1e3 / reps
     us = timed(False)
     us_kept = timed(True)
+    # the backward (hyena_conv_bwd_long: dq, dk, dv and dh) on the same inputs
+    g = torch.Generator(device=q.device).manual_seed(lw.seed + 51)
+    dy = torch.randn(q.shape, generator=g, device=q.device).to(q.dtype)
+    ws_b = torch.empty(hc.bwd_long_workspace_bytes(lw.B, lw.L, lw.D, lw.group_size, lw.l_h, code),
+                       dtype=torch.uint8, device=q.device)
+    for _ in range(2):
+        hc.conv_bwd_long(q, k, v, h, dy, lw.group_size, workspace=ws_b, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        hc.conv_bwd_long(q, k, v, h, dy, lw.group_size, workspace=ws_b, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_bwd = e0.elapsed_time(e1) * 1e3 / reps
+    ws_bwd = ws_b.numel()
+    del dy, ws_b
     moved = 40 * lw.elems
     res = {"B": lw.B, "L": lw.L, "D": lw.D, "group_size": lw.group_size, "l_h": lw.l_h,
            "us": round(us, 1), "G_tok_ch_per_s": round(lw.elems / (us * 1e-6) / 1e9, 2),
@@ -742,7 +760,10 @@ def long_filter_rates(w, stream, reps):
            "frac_of_peak_moved": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
            "workspace_bytes": ws_n, "kernels": 5,
            "us_spectra_kept": round(us_kept, 1), "kernels_spectra_kept": 3,
-           "G_tok_ch_per_s_spectra_kept": round(lw.elems / (us_kept * 1e-6) / 1e9, 2)}
+           "G_tok_ch_per_s_spectra_kept": round(lw.elems / (us_kept * 1e-6) / 1e9, 2),
+           "backward": {"us": round(us_bwd, 1), "G_tok_ch_per_s": round(lw.elems / (us_bwd * 1e-6) / 1e9, 2),
+                        "workspace_bytes": ws_bwd, "kernels": 9,
+                        "frac_of_peak_min_bytes": round(14 * lw.elems / (us_bwd * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
     del q, k, v, h, y, ws
     return res
 

@@ -35,7 +35,7 @@ EXPORTS = ("hyena_conv_fwd", "hyena_conv_fwd_f32", "hyena_conv_fwd_ex", "hyena_c
            "hyena_conv_bwd", "hyena_conv_bwd_workspace", "hyena_conv_fwd_long",
            "hyena_conv_fwd_long_workspace", "hyena_conv_plan", "hyena_conv_strerror",
            "hyena_conv_block_len", "hyena_conv_bwd_noalloc", "hyena_conv_scratch_bytes",
-           "hyena_conv_fwd_long_ex")
+           "hyena_conv_fwd_long_ex", "hyena_conv_bwd_long", "hyena_conv_bwd_long_workspace")
 
 
 class HyenaError(RuntimeError):
@@ -88,6 +88,12 @@ def lib() -> ctypes.CDLL:
         L.hyena_conv_fwd_long_workspace.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                                     ctypes.POINTER(i64)]
         L.hyena_conv_fwd_long_workspace.restype = ctypes.c_int
+        L.hyena_conv_bwd_long.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp,
+                                          ctypes.c_int, vp, i64, vp]
+        L.hyena_conv_bwd_long.restype = ctypes.c_int
+        L.hyena_conv_bwd_long_workspace.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
+                                                    ctypes.POINTER(i64)]
+        L.hyena_conv_bwd_long_workspace.restype = ctypes.c_int
         L.hyena_conv_plan.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, i64,
                                       ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.hyena_conv_plan.restype = ctypes.c_int
@@ -301,6 +307,61 @@ def conv_fwd_long(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Te
     return out
 
 
+def bwd_long_workspace_bytes(B: int, L: int, D: int, group_size: int, l_h: int,
+                             dtype: int = DTYPE_BF16) -> int:
+    """Workspace bytes hyena_conv_bwd_long needs."""
+    n = ctypes.c_int64()
+    st = lib().hyena_conv_bwd_long_workspace(B, L, D, group_size, l_h, dtype, ctypes.byref(n))
+    if st != 0:
+        raise HyenaError(st, "hyena_conv_bwd_long_workspace")
+    return n.value
+
+
+def conv_bwd_long(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Tensor,
+                  dy: torch.Tensor, group_size: int, need_dq: bool = True, need_dkv: bool = True,
+                  need_dh: bool = True, workspace: Optional[torch.Tensor] = None,
+                  stream: Optional[torch.cuda.Stream] = None):
+    """Gradients (dq, dk, dv, dh) of the long-filter forward (FFT), any l_h.
+
+    Same tensors and results as conv_bwd; parts not requested are None.
+    ``workspace`` (uint8, on q's device) is allocated here if not given.
+    """
+    dt, dev = q.dtype, q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("h", h), ("dy", dy)):
+        if t.dtype != dt or t.device != dev or dev.type != "cuda" or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor like q" % name)
+    if q.dim() != 3 or any(t.shape != q.shape for t in (k, v, dy)) or h.dim() != 2:
+        raise ValueError("q, k, v, dy must be [B, L, D]; h [D // group_size, l_h]")
+    code = _dtype_code(dt)
+    B, L, D = q.shape
+    G, l_h = h.shape
+    if group_size < 1 or D % group_size != 0 or G != D // group_size:
+        raise ValueError("h has %d filters; D=%d, group_size=%d" % (G, D, group_size))
+    dq = torch.empty_like(q) if need_dq else None
+    dk = torch.empty_like(q) if need_dkv else None
+    dv = torch.empty_like(q) if need_dkv else None
+    dh = torch.empty((G, l_h), dtype=torch.float32, device=dev) if need_dh else None
+    ws_n = bwd_long_workspace_bytes(B, L, D, group_size, l_h, code)
+    if workspace is None:
+        workspace = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
+        raise ValueError("workspace must hold %d bytes on q's device" % ws_n)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(), dy.data_ptr(), B, L, D,
+            group_size, l_h, ptr(dq), ptr(dk), ptr(dv), ptr(dh), code, workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if dev.index == torch.cuda.current_device():
+        st = lib().hyena_conv_bwd_long(*args)
+    else:
+        with torch.cuda.device(dev):
+            st = lib().hyena_conv_bwd_long(*args)
+    if st != 0:
+        raise HyenaError(st, "hyena_conv_bwd_long")
+    return dq, dk, dv, dh
+
+
 class HyenaConv(torch.autograd.Function):
     """Autograd wrapper: y = HyenaConv.apply(q, k, v, h, group_size).
 
@@ -319,5 +380,28 @@ class HyenaConv(torch.autograd.Function):
         need = ctx.needs_input_grad
         dq, dk, dv, dh = conv_bwd(q, k, v, h, dy.contiguous(), ctx.group_size,
                                   need_dq=need[0], need_dkv=need[1] or need[2], need_dh=need[3])
+        return (dq, dk if need[1] else None, dv if need[2] else None,
+                dh.to(h.dtype) if dh is not None else None, None)
+
+
+class HyenaConvLong(torch.autograd.Function):
+    """Autograd wrapper of the long-filter (FFT) path: y = HyenaConvLong.apply(q, k, v, h, group_size).
+
+    Any filter length; the filter gradient comes back in h's dtype (fp32 sums).
+    """
+
+    @staticmethod
+    def forward(ctx, q, k, v, h, group_size):
+        ctx.save_for_backward(q, k, v, h)
+        ctx.group_size = group_size
+        return conv_fwd_long(q, k, v, h, group_size)
+
+    @staticmethod
+    def backward(ctx, dy):
+        q, k, v, h = ctx.saved_tensors
+        need = ctx.needs_input_grad
+        dq, dk, dv, dh = conv_bwd_long(q, k, v, h, dy.contiguous(), ctx.group_size,
+                                       need_dq=need[0], need_dkv=need[1] or need[2],
+                                       need_dh=need[3])
         return (dq, dk if need[1] else None, dv if need[2] else None,
                 dh.to(h.dtype) if dh is not None else None, None)

@@ -53,8 +53,12 @@ constexpr int kFftMaxLdsBytes = 160 * 1024;
 struct FftParams {
     const void *q, *k, *v, *h;
     void *y;
+    void *y2;            // second output (the backward's dv), else unused
     float2 *ws;          // [nb][N2][N1][np] complex work area
     float2 *hs;          // [N2][N1][Gp] filter spectra
+    float2 *part;        // backward: filter-gradient spectral partial sums, or null
+    int32_t nb;          // backward: batch rows (a work area holds nb N np values)
+    int32_t pb_log, pb_tiles, n_slots;  // backward: pairs per column tile (log2), those tiles, group slots per tile
     int64_t L;           // rows of the input sequence (the filter pass: taps)
     int32_t D;           // channels (row pitch) of q, k, v, y
     int32_t np;          // channel pairs of this pass
@@ -502,6 +506,260 @@ __global__ __launch_bounds__(kFftThreads) void fft_col1_kernel(FftParams p) {
     }
 }
 
+// Backward column kernel.  The work area holds two transforms side by side:
+// x = k v (the first nb N np values) and dz = dy q (the next).  Per (batch,
+// column pair {f2, M - f2}, pair tile): the N1-point transforms of both
+// columns of both, then per frequency f, with a = P[f] and m = conj(P[-f]) of
+// a packed pair spectrum and H0, H1 its two channels' filter spectra,
+//     Z  = (H0 + H1)/2 a_x  + (H0 - H1)/2 m_x          (z = h * x, for dq)
+//     DX = conj((H0 + H1)/2) a_dz + conj((H0 - H1)/2) m_dz   (dx, for dk, dv)
+// since dx[t] = sum_s h[s] dz[t + s] is the correlation with h, whose
+// spectrum is conj(H) DZ.  Both are transformed back along f1, twiddled and
+// stored in place, as in the forward.  With `part` set it also writes the
+// filter gradient's spectral partial sums: dh[g, s] = sum_{b, c in g} (dz_c
+// correlated with x_c)[s], whose spectrum is sum DZ_c conj(X_c), the channel
+// spectra separated as X_0 = (a + m)/2, X_1 = (a - m)/(2i):
+//     channel 2j: (a_dz + m_dz) conj(a_x + m_x) / 4,
+//     channel 2j + 1: (a_dz - m_dz) conj(a_x - m_x) / 4,
+// summed over the tile's channels of each group into
+// part[b][f2][f1][tile][slot], slot = group - first group of the tile.
+// LDS (dynamic): two buffers of 4 N1 P values -- element (t1, src, col,
+// pair) at ((2 t1 + src) 2 + col) P + pair -- the N1 inner twiddles and,
+// per column, the N1 inter-step twiddles W_N^(-t1 f2).
+__global__ __launch_bounds__(kFftThreads) void fft_bwd_cols_kernel(FftParams p) {
+    extern __shared__ float2 lds[];
+    const int item = xcd_item();
+    const int tile = item % p.n_tiles;
+    const int M = p.N2 * p.N3;  // columns
+    const int c = (item / p.n_tiles) % (M / 2 + 1);
+    const int b = item / (p.n_tiles * (M / 2 + 1));
+    const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1;
+    const int lP2 = logP + 1, lS = logP + 2;
+    const int NS = N1 << lS;
+    const int sdz = 1 << lP2;  // from an x sequence to the dz sequence of the same column and pair
+    const int64_t N = (int64_t)N1 * M;
+    const int64_t area = (int64_t)p.nb * N * p.np;
+    const int fa = c, fb = (M - c) & (M - 1);
+    const bool self = fa == fb;
+    auto cpos = [&](int f) -> int64_t { return (int64_t)(f & (p.N3 - 1)) * p.N2 + (f >> p.log3); };
+    auto wpos = [&](int src, int col, int t1, int j) -> int64_t {
+        return src * area + (((int64_t)b * M + cpos(col ? fb : fa)) * N1 + t1) * p.np + j;
+    };
+    float2 *bufA = lds, *bufB = lds + NS, *tw = lds + 2 * NS;
+    float2 *wt[2] = {tw + N1, tw + 2 * N1};
+    stage_in(bufA, NS, [&](int i) {
+        const int col = (i >> logP) & 1, src = (i >> lP2) & 1;
+        const int j = (tile << logP) + (i & pmask);
+        const bool ok = j < p.np;
+        const float2 v = p.ws[wpos(src, col, i >> lS, ok ? j : 0)];
+        return ok ? v : make_float2(0.0f, 0.0f);
+    });
+    fill_twiddles(tw, N1);
+    for (int i = threadIdx.x; i < 2 * N1; i += kFftThreads) {
+        const int col = i >= N1 ? 1 : 0, t1 = i - col * N1;
+        wt[col][t1] = cconj(twiddle(((int64_t)t1 * (col ? fb : fa)) & (N - 1), N));
+    }
+    __syncthreads();
+    float2 *S = lds_fft(bufA, bufB, tw, N1, p.log1, lS, false);
+    float2 *Z = S == bufA ? bufB : bufA;
+    // 2P divides the thread count: a thread keeps one column and pair
+    const int my_col = (threadIdx.x >> logP) & 1, my_pp = threadIdx.x & pmask;
+    const int my_f2 = my_col ? fb : fa;
+    const int my_j = (tile << logP) + my_pp;
+    const int jc = min(my_j, p.np - 1);
+    const float2 *hrow0 = p.hs + (size_t)my_f2 * N1 * p.Gp + (2 * jc) / p.group_size;
+    const float2 *hrow1 = p.hs + (size_t)my_f2 * N1 * p.Gp + (2 * jc + 1) / p.group_size;
+    const int NP2 = N1 << lP2;
+    for (int base = 0; base < NP2; base += kBatch * kFftThreads) {
+        float2 h0[kBatch], h1[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int f1 = min(base + u * kFftThreads + (int)threadIdx.x, NP2 - 1) >> lP2;
+            h0[u] = hrow0[(size_t)f1 * p.Gp];
+            h1[u] = hrow1[(size_t)f1 * p.Gp];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = base + u * kFftThreads + (int)threadIdx.x;
+            if (i >= NP2) continue;
+            const int f1 = i >> lP2;
+            const int f1m = (N1 - f1 - (my_f2 > 0 ? 1 : 0)) & (N1 - 1);
+            const int ix = (f1 << lS) | (my_col << logP) | my_pp;
+            const int im = (f1m << lS) | ((my_col ^ 1) << logP) | my_pp;
+            const float2 sm = make_float2(0.5f * (h0[u].x + h1[u].x), 0.5f * (h0[u].y + h1[u].y));
+            const float2 df = make_float2(0.5f * (h0[u].x - h1[u].x), 0.5f * (h0[u].y - h1[u].y));
+            const float2 ax = S[ix], mx = cconj(S[im]), az = S[ix + sdz], mz = cconj(S[im + sdz]);
+            const float2 zx0 = cmul(sm, ax), zx1 = cmul(df, mx);
+            const float2 zd0 = cmul(cconj(sm), az), zd1 = cmul(cconj(df), mz);
+            const bool ok = my_j < p.np;
+            Z[ix] = ok ? make_float2(zx0.x + zx1.x, zx0.y + zx1.y) : make_float2(0.0f, 0.0f);
+            Z[ix + sdz] = ok ? make_float2(zd0.x + zd1.x, zd0.y + zd1.y) : make_float2(0.0f, 0.0f);
+        }
+    }
+    if (p.part != nullptr) {
+        // one item per (f1, column, group slot): the sum over the group's
+        // channels in this tile (a self-paired column once)
+        const int c_lo = (tile << logP) * 2;
+        const int c_end = min(c_lo + (2 << logP), 2 * p.np);
+        const int g0 = c_lo / p.group_size;
+        const int n_items = N1 * 2 * p.n_slots;
+        for (int it = threadIdx.x; it < n_items; it += kFftThreads) {
+            const int slot = it % p.n_slots;
+            const int col = (it / p.n_slots) & 1;
+            const int f1 = it / (2 * p.n_slots);
+            const int g = g0 + slot;
+            const int lo = max(c_lo, g * p.group_size), hi = min(c_end, (g + 1) * p.group_size);
+            if ((self && col) || lo >= hi) continue;
+            const int f2 = col ? fb : fa;
+            const int f1m = (N1 - f1 - (f2 > 0 ? 1 : 0)) & (N1 - 1);
+            float2 acc = make_float2(0.0f, 0.0f);
+            for (int ch = lo; ch < hi; ++ch) {
+                const int pp = (ch - c_lo) >> 1;
+                const int ix = (f1 << lS) | (col << logP) | pp;
+                const int im = (f1m << lS) | ((col ^ 1) << logP) | pp;
+                const float sg = (ch & 1) ? -1.0f : 1.0f;
+                const float2 ax = S[ix], mx = cconj(S[im]), az = S[ix + sdz], mz = cconj(S[im + sdz]);
+                const float2 u = make_float2(az.x + sg * mz.x, az.y + sg * mz.y);
+                const float2 w = make_float2(ax.x + sg * mx.x, ax.y + sg * mx.y);
+                const float2 pr = cmul(u, cconj(w));
+                acc.x += pr.x;
+                acc.y += pr.y;
+            }
+            p.part[((((int64_t)b * M + f2) * N1 + f1) * p.n_tiles + tile) * p.n_slots + slot] =
+                make_float2(0.25f * acc.x, 0.25f * acc.y);
+        }
+    }
+    __syncthreads();
+    const float2 *U = lds_fft(Z, S, tw, N1, p.log1, lS, true);
+    for (int i = threadIdx.x; i < NS; i += kFftThreads) {
+        const int t1 = i >> lS, col = (i >> logP) & 1, src = (i >> lP2) & 1;
+        const int j = (tile << logP) + (i & pmask);
+        if (j >= p.np || (self && col)) continue;
+        p.ws[wpos(src, col, t1, j)] = cmul(U[i], wt[col][t1]);
+    }
+}
+
+// Filter-gradient column kernel.  Per (column pair {f2, M - f2}, tile of P
+// group pairs): the spectrum of each group g, S_g = the partial sums over
+// the batch rows and the column tiles holding g's channels; its Hermitian
+// part, whose inverse transform is the real part of S_g's
+// (H_g[f] = (S_g[f] + conj(S_g[-f]))/2); two groups packed as one complex
+// sequence, Q = H_2m + i H_2m+1 (real and imaginary parts of the result
+// are then the two gradients); the inverse N1-point transform along f1 and
+// the twiddle W_N^(-t1 f2), stored as a one-row work area of Gp/2 pairs.
+// p.np = Gp/2 here; pb_log, pb_tiles and n_slots describe the backward
+// column tiles that wrote `part`.
+// LDS (dynamic): the sums (4 N1 P values: element (f1, col, group) at
+// (2 f1 + col) 2P + group), two buffers of 2 N1 P values, the N1 inner
+// twiddles and 2 N1 inter-step twiddles.
+__global__ __launch_bounds__(kFftThreads) void fft_dh_cols_kernel(FftParams p) {
+    extern __shared__ float2 lds[];
+    const int item = xcd_item();
+    const int tile = item % p.n_tiles;
+    const int M = p.N2 * p.N3;
+    const int c = item / p.n_tiles;
+    const int logP = p.logP, N1 = p.N1;
+    const int lG = logP + 1;            // groups of the tile (log2)
+    const int lS = logP + 2;            // (col, group) sequences of the sums
+    const int lQ = logP + 1;            // (col, group pair) sequences of the transform
+    const int64_t N = (int64_t)N1 * M;
+    const int fa = c, fb = (M - c) & (M - 1);
+    const bool self = fa == fb;
+    auto cpos = [&](int f) -> int64_t { return (int64_t)(f & (p.N3 - 1)) * p.N2 + (f >> p.log3); };
+    float2 *sums = lds, *bufA = lds + (N1 << lS), *bufB = bufA + (N1 << lQ), *tw = bufB + (N1 << lQ);
+    float2 *wt[2] = {tw + N1, tw + 2 * N1};
+    const int cpt = 2 << p.pb_log;      // channels per backward column tile
+    for (int e = threadIdx.x; e < (N1 << lS); e += kFftThreads) {
+        const int f1 = e >> lS, col = (e >> lG) & 1;
+        const int g = (tile << lG) + (e & ((1 << lG) - 1));
+        float2 acc = make_float2(0.0f, 0.0f);
+        if (g < p.G) {
+            const int f2 = (self || !col) ? fa : fb;
+            const int t_lo = (g * p.group_size) / cpt, t_hi = ((g + 1) * p.group_size - 1) / cpt;
+            for (int b = 0; b < p.nb; ++b) {
+                const float2 *row = p.part + (((int64_t)b * M + f2) * N1 + f1) * p.pb_tiles * p.n_slots;
+                for (int t = t_lo; t <= t_hi; ++t) {
+                    const float2 v = row[(int64_t)t * p.n_slots + (g - (t * cpt) / p.group_size)];
+                    acc.x += v.x;
+                    acc.y += v.y;
+                }
+            }
+        }
+        sums[e] = acc;
+    }
+    fill_twiddles(tw, N1);
+    for (int i = threadIdx.x; i < 2 * N1; i += kFftThreads) {
+        const int col = i >= N1 ? 1 : 0, t1 = i - col * N1;
+        wt[col][t1] = cconj(twiddle(((int64_t)t1 * (col ? fb : fa)) & (N - 1), N));
+    }
+    __syncthreads();
+    const int gmask = (1 << logP) - 1;
+    for (int e = threadIdx.x; e < (N1 << lQ); e += kFftThreads) {
+        const int f1 = e >> lQ, col = (e >> logP) & 1, m = e & gmask;
+        const int f2 = col ? fb : fa;
+        const int f1m = (N1 - f1 - (f2 > 0 ? 1 : 0)) & (N1 - 1);
+        const int ia = (((f1 << 1) | col) << lG) + 2 * m;
+        const int ib = (((f1m << 1) | (col ^ 1)) << lG) + 2 * m;
+        const float2 s0 = sums[ia], s1 = sums[ia + 1], r0 = sums[ib], r1 = sums[ib + 1];
+        // H = (S[f] + conj(S[-f]))/2 for both groups, then H0 + i H1
+        const float2 h0 = make_float2(0.5f * (s0.x + r0.x), 0.5f * (s0.y - r0.y));
+        const float2 h1 = make_float2(0.5f * (s1.x + r1.x), 0.5f * (s1.y - r1.y));
+        bufA[e] = make_float2(h0.x - h1.y, h0.y + h1.x);
+    }
+    __syncthreads();
+    const float2 *U = lds_fft(bufA, bufB, tw, N1, p.log1, lQ, true);
+    for (int e = threadIdx.x; e < (N1 << lQ); e += kFftThreads) {
+        const int t1 = e >> lQ, col = (e >> logP) & 1;
+        const int j = (tile << logP) + (e & gmask);
+        if (j >= p.np || (self && col)) continue;
+        p.ws[(cpos(col ? fb : fa) * N1 + t1) * p.np + j] = cmul(U[e], wt[col][t1]);
+    }
+}
+
+// Filter-gradient taps past the sequence (l_h > L: no row reaches them): zero.
+__global__ __launch_bounds__(256) void fft_dh_tail_kernel(float *dh, int64_t G, int64_t l_h, int64_t from) {
+    const int64_t w = l_h - from;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < G * w) dh[(i / w) * l_h + from + i % w] = 0.0f;
+}
+
+// Output of the last inverse pass for channel pair j at row t (values
+// already scaled).  MODE 0: y = q z (the forward; the backward's dq with dy in
+// q's place).  MODE 1: the backward's dk = z v and dv = z k (z = dx).  MODE 2:
+// the filter gradient, fp32 [G][l_h], groups 2j and 2j + 1 at tap t.
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+    const __bf16 x = (__bf16)a, y = (__bf16)b;
+    return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+template <bool F32, int MODE>
+__device__ inline void store_out(const FftParams &p, int b, int64_t t, int j, float z0, float z1) {
+    if constexpr (MODE == 2) {
+        float *dh = (float *)p.y;
+        dh[(size_t)(2 * j) * (size_t)p.l_h + (size_t)t] = z0;
+        if (2 * j + 1 < p.G) dh[(size_t)(2 * j + 1) * (size_t)p.l_h + (size_t)t] = z1;
+        return;
+    }
+    const size_t o = ((size_t)b * (size_t)p.L + (size_t)t) * (size_t)p.D + 2 * (size_t)j;
+    const void *ga = MODE == 0 ? p.q : p.v;
+    if constexpr (F32) {
+        const float2 g = *(const float2 *)((const float *)ga + o);
+        *(float2 *)((float *)p.y + o) = make_float2(g.x * z0, g.y * z1);
+        if constexpr (MODE == 1) {
+            const float2 g2 = *(const float2 *)((const float *)p.k + o);
+            *(float2 *)((float *)p.y2 + o) = make_float2(g2.x * z0, g2.y * z1);
+        }
+    } else {
+        const uint32_t g = *(const uint32_t *)((const uint16_t *)ga + o);
+        *(uint32_t *)((uint16_t *)p.y + o) =
+            pack_bf16x2(__uint_as_float(g << 16) * z0, __uint_as_float(g & 0xffff0000u) * z1);
+        if constexpr (MODE == 1) {
+            const uint32_t g2 = *(const uint32_t *)((const uint16_t *)p.k + o);
+            *(uint32_t *)((uint16_t *)p.y2 + o) =
+                pack_bf16x2(__uint_as_float(g2 << 16) * z0, __uint_as_float(g2 & 0xffff0000u) * z1);
+        }
+    }
+}
+
 // Three-level split (large N): N = N1 N2 N3, t = t1 + N1 t2 + N1 N2 t3.
 // The M = N2 N3 point transform along t2 + N2 t3 that the row kernel does
 // in one piece is done in two passes, as a four-step of its own:
@@ -576,7 +834,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_mid_kernel(FftParams p) {
     }
 }
 
-template <bool F32>
+template <bool F32, int MODE>
 __global__ __launch_bounds__(kFftThreads) void fft_out3_kernel(FftParams p) {
     extern __shared__ float2 lds[];
     const int item = xcd_item();
@@ -603,24 +861,13 @@ __global__ __launch_bounds__(kFftThreads) void fft_out3_kernel(FftParams p) {
         const int j = (tile << logP) + (i & pmask);
         const int64_t t = t1 + (int64_t)N1 * (t2 + (int64_t)N2 * t3);
         if (j >= p.np || t >= p.L) continue;
-        const size_t o = ((size_t)b * (size_t)p.L + (size_t)t) * (size_t)p.D + 2 * (size_t)j;
-        const float z0 = z[i].x * scale, z1 = z[i].y * scale;
-        if constexpr (F32) {
-            const float2 qq = *(const float2 *)((const float *)p.q + o);
-            *(float2 *)((float *)p.y + o) = make_float2(qq.x * z0, qq.y * z1);
-        } else {
-            const uint32_t qq = *(const uint32_t *)((const uint16_t *)p.q + o);
-            const __bf16 y0 = (__bf16)(__uint_as_float(qq << 16) * z0);
-            const __bf16 y1 = (__bf16)(__uint_as_float(qq & 0xffff0000u) * z1);
-            *(uint32_t *)((uint16_t *)p.y + o) =
-                (uint32_t)__builtin_bit_cast(uint16_t, y0) | ((uint32_t)__builtin_bit_cast(uint16_t, y1) << 16);
-        }
+        store_out<F32, MODE>(p, b, t, j, z[i].x * scale, z[i].y * scale);
     }
 }
 
 // Kernel 3: inverse transform along f2 for one t1, scale, gate, store.
 // LDS (dynamic): two buffers of N2 P values and the N2 inner twiddles.
-template <bool F32>
+template <bool F32, int MODE>
 __global__ __launch_bounds__(kFftThreads) void fft_out_kernel(FftParams p) {
     extern __shared__ float2 lds[];
     const int item = xcd_item();
@@ -645,18 +892,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_out_kernel(FftParams p) {
         const int j = (tile << logP) + (i & pmask);
         const int64_t t = t1 + (int64_t)N1 * t2;
         if (j >= p.np || t >= p.L) continue;
-        const size_t o = ((size_t)b * (size_t)p.L + (size_t)t) * (size_t)p.D + 2 * (size_t)j;
-        const float z0 = z[i].x * scale, z1 = z[i].y * scale;
-        if constexpr (F32) {
-            const float2 qq = *(const float2 *)((const float *)p.q + o);
-            *(float2 *)((float *)p.y + o) = make_float2(qq.x * z0, qq.y * z1);
-        } else {
-            const uint32_t qq = *(const uint32_t *)((const uint16_t *)p.q + o);
-            const __bf16 y0 = (__bf16)(__uint_as_float(qq << 16) * z0);
-            const __bf16 y1 = (__bf16)(__uint_as_float(qq & 0xffff0000u) * z1);
-            *(uint32_t *)((uint16_t *)p.y + o) =
-                (uint32_t)__builtin_bit_cast(uint16_t, y0) | ((uint32_t)__builtin_bit_cast(uint16_t, y1) << 16);
-        }
+        store_out<F32, MODE>(p, b, t, j, z[i].x * scale, z[i].y * scale);
     }
 }
 
@@ -666,6 +902,11 @@ struct FftPlan {
     bool three;                      // three-level split (N3 > 1)
     int P_rows, P_mid, P_cols, P_col1;          // pairs per workgroup: row (rows3/out3), middle,
     int lds_rows, lds_mid, lds_cols, lds_col1;  // column (paired, single) kernels; their LDS bytes
+    // backward: column kernel (pairs per tile, tiles, group slots per tile),
+    // filter-gradient column kernel (group pairs per tile), LDS, and the
+    // workspace: spectra, two work areas, partial sums
+    int P_bwd, P_dh, lds_bwd, lds_dh;
+    int64_t pb_tiles, n_slots, area_bytes, part_bytes, bwd_ws_bytes;
 };
 
 // Largest N done with the two-level split (columns of at most 256 points);
@@ -757,6 +998,43 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
+// The backward's additions to the plan (after fft_plan succeeded).
+int fft_bwd_plan(int64_t B, int64_t D, int64_t group_size, FftPlan *pl) {
+    const int64_t G = D / group_size, Gp = G + (G & 1);
+    const int64_t pairs = D / 2;
+    pl->P_bwd = pick_pairs(pl->N1, 8, pairs, kFftColsBudget);
+    pl->lds_bwd = (8 * pl->N1 * pl->P_bwd + 3 * pl->N1) * (int)sizeof(float2);
+    pl->P_dh = pick_pairs(pl->N1, 8, Gp / 2, kFftColsBudget);
+    pl->lds_dh = (8 * pl->N1 * pl->P_dh + 3 * pl->N1) * (int)sizeof(float2);
+    if (pl->lds_bwd > kFftMaxLdsBytes || pl->lds_dh > kFftMaxLdsBytes) return HYENA_ERR_UNSUPPORTED;
+    pl->pb_tiles = (pairs + pl->P_bwd - 1) / pl->P_bwd;
+    // groups a tile of 2P channels can touch
+    const int64_t span = (2 * (int64_t)pl->P_bwd - 1 + group_size - 1) / group_size + 1;
+    pl->n_slots = span < G ? span : G;
+    // B N (pairs + pb_tiles n_slots) complex values plus the spectra must not overflow
+    const int64_t per_n = 2 * pairs + pl->pb_tiles * pl->n_slots;
+    if (B > 0 && per_n > ((INT64_MAX / 16) / pl->N - Gp) / B) return HYENA_ERR_SHAPE;
+    pl->area_bytes = B * pl->N * pairs * (int64_t)sizeof(float2);
+    pl->part_bytes = B * pl->N * pl->pb_tiles * pl->n_slots * (int64_t)sizeof(float2);
+    pl->bwd_ws_bytes = pl->hs_bytes + 2 * pl->area_bytes + pl->part_bytes;
+    return HYENA_OK;
+}
+
+// One launch: pair tile P, grid (batch rows x units x tiles), dynamic LDS.
+int fft_launch(const void *fn, FftParams q_, int P, int64_t units, int64_t nb, int lds, hipStream_t s) {
+    q_.logP = 0;
+    while ((1 << q_.logP) < P) ++q_.logP;
+    q_.n_tiles = (q_.np + P - 1) / P;
+    const int64_t grid = nb * units * q_.n_tiles;
+    if (grid > INT32_MAX) return HYENA_ERR_UNSUPPORTED;
+    if (lds > 64 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+        return HYENA_ERR_LAUNCH;
+    void *args[] = {&q_};
+    if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kFftThreads), args, (size_t)lds, s) != hipSuccess)
+        return HYENA_ERR_LAUNCH;
+    return HYENA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -794,7 +1072,7 @@ int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v, const vo
         return HYENA_ERR_ALIAS;
 
     const int64_t G = D / group_size;
-    FftParams p;
+    FftParams p = {};
     p.q = q; p.k = k; p.v = v; p.h = h; p.y = out;
     p.hs = (float2 *)workspace;
     p.ws = (float2 *)((char *)workspace + pl.hs_bytes);
@@ -808,20 +1086,8 @@ int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v, const vo
     const bool f32 = dtype == HYENA_DTYPE_F32;
     hipStream_t s = (hipStream_t)stream;
 
-    // One launch: pair tile, grid (batch rows x units x tiles), dynamic LDS.
-    auto launch = [&](const void *fn, FftParams q_, int P, int64_t units, int64_t nb, int lds) -> int {
-        q_.logP = 0;
-        while ((1 << q_.logP) < P) ++q_.logP;
-        q_.n_tiles = (q_.np + P - 1) / P;
-        const int64_t grid = nb * units * q_.n_tiles;
-        if (grid > INT32_MAX) return HYENA_ERR_UNSUPPORTED;
-        if (lds > 64 * 1024 &&
-            hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
-            return HYENA_ERR_LAUNCH;
-        void *args[] = {&q_};
-        if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kFftThreads), args, (size_t)lds, s) != hipSuccess)
-            return HYENA_ERR_LAUNCH;
-        return HYENA_OK;
+    auto launch = [&](const void *fn, const FftParams &q_, int P, int64_t units, int64_t nb, int lds) -> int {
+        return fft_launch(fn, q_, P, units, nb, lds, s);
     };
     const int64_t M = (int64_t)pl.N2 * pl.N3;  // columns
     const int64_t cols = M / 2 + 1;
@@ -829,11 +1095,11 @@ int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v, const vo
     if (pl.three) {
         rows_seq = f32 ? (const void *)fft_rows3_kernel<true, 0> : (const void *)fft_rows3_kernel<false, 0>;
         rows_flt = f32 ? (const void *)fft_rows3_kernel<true, 1> : (const void *)fft_rows3_kernel<false, 1>;
-        out_fn = f32 ? (const void *)fft_out3_kernel<true> : (const void *)fft_out3_kernel<false>;
+        out_fn = f32 ? (const void *)fft_out3_kernel<true, 0> : (const void *)fft_out3_kernel<false, 0>;
     } else {
         rows_seq = f32 ? (const void *)fft_rows_kernel<true, 0> : (const void *)fft_rows_kernel<false, 0>;
         rows_flt = f32 ? (const void *)fft_rows_kernel<true, 1> : (const void *)fft_rows_kernel<false, 1>;
-        out_fn = f32 ? (const void *)fft_out_kernel<true> : (const void *)fft_out_kernel<false>;
+        out_fn = f32 ? (const void *)fft_out_kernel<true, 0> : (const void *)fft_out_kernel<false, 0>;
     }
     // units per batch row of the row and output kernels: t1 (x t2 when three-level)
     const int64_t row_units = pl.three ? (int64_t)pl.N1 * pl.N2 : pl.N1;
@@ -873,6 +1139,174 @@ int hyena_conv_fwd_long(const void *q, const void *k, const void *v, const void 
                         int64_t workspace_bytes, void *stream) {
     return hyena_conv_fwd_long_ex(q, k, v, h, B, L, D, group_size, l_h, out, dtype, workspace, workspace_bytes, 0,
                                   stream);
+}
+
+int hyena_conv_bwd_long_workspace(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, int dtype,
+                                  int64_t *bytes_out) {
+    FftPlan pl;
+    int st = fft_plan(B, L, D, group_size, l_h, dtype, &pl);
+    if (st == HYENA_OK) st = fft_bwd_plan(B, D, group_size, &pl);
+    if (st != HYENA_OK) return st;
+    if (bytes_out) *bytes_out = (B == 0 || L == 0 || D == 0) ? 0 : pl.bwd_ws_bytes;
+    return HYENA_OK;
+}
+
+int hyena_conv_bwd_long(const void *q, const void *k, const void *v, const void *h, const void *dy, int64_t B,
+                        int64_t L, int64_t D, int64_t group_size, int64_t l_h, void *dq, void *dk, void *dv,
+                        float *dh, int dtype, void *workspace, int64_t workspace_bytes, void *stream) {
+    FftPlan pl;
+    int st = fft_plan(B, L, D, group_size, l_h, dtype, &pl);
+    if (st == HYENA_OK) st = fft_bwd_plan(B, D, group_size, &pl);
+    if (st != HYENA_OK) return st;
+    if (!q || !k || !v || !h || !dy) return HYENA_ERR_NULL;
+    if ((dk == nullptr) != (dv == nullptr)) return HYENA_ERR_NULL;
+    const size_t eb = dtype == HYENA_DTYPE_F32 ? 4 : 2;
+    uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)dy | (uintptr_t)workspace;
+    if (dq) mis |= (uintptr_t)dq;
+    if (dk) mis |= (uintptr_t)dk | (uintptr_t)dv;
+    if (mis & 15u) return HYENA_ERR_ALIGN;
+    if (((uintptr_t)h & (eb - 1)) || ((uintptr_t)dh & 3u)) return HYENA_ERR_ALIGN;
+    const int64_t G = D / group_size;
+    const bool empty = B == 0 || L == 0 || D == 0;
+    const size_t nbytes = (size_t)B * (size_t)L * (size_t)D * eb;
+    const size_t hbytes = (size_t)G * (size_t)l_h * eb;
+    const size_t dhbytes = (size_t)G * (size_t)l_h * sizeof(float);
+    const size_t wbytes = empty ? 0 : (size_t)pl.bwd_ws_bytes;
+    // every output and the workspace are disjoint from every input and from each other
+    const void *in[5] = {q, k, v, dy, h};
+    const size_t in_n[5] = {nbytes, nbytes, nbytes, nbytes, hbytes};
+    const void *outs[5] = {dq, dk, dv, dh, empty ? nullptr : workspace};
+    const size_t out_n[5] = {nbytes, nbytes, nbytes, dhbytes, wbytes};
+    for (int i = 0; i < 5; ++i) {
+        if (!outs[i]) continue;
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(outs[i], out_n[i], in[j], in_n[j])) return HYENA_ERR_ALIAS;
+        for (int j = i + 1; j < 5; ++j)
+            if (outs[j] && overlaps(outs[i], out_n[i], outs[j], out_n[j])) return HYENA_ERR_ALIAS;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t taps = l_h < L ? l_h : L;
+    if (dh && (G * l_h + 255) / 256 > INT32_MAX) return HYENA_ERR_UNSUPPORTED;  // the zero-fill grid
+    if (empty || (!dq && !dk && !dh)) {
+        // no rows: dh is zero (D == 0: dh has no elements)
+        if (dh && G * l_h > 0) {
+            hipLaunchKernelGGL(fft_dh_tail_kernel, dim3((unsigned)((G * l_h + 255) / 256)), dim3(256), 0, s, dh, G,
+                               l_h, (int64_t)0);
+            if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+        }
+        return HYENA_OK;
+    }
+    if (!workspace || workspace_bytes < pl.bwd_ws_bytes) return HYENA_ERR_WORKSPACE;
+
+    FftParams p = {};
+    p.h = h;
+    p.hs = (float2 *)workspace;
+    p.ws = (float2 *)((char *)workspace + pl.hs_bytes);
+    p.D = (int32_t)D;
+    p.G = (int32_t)G;
+    p.Gp = (int32_t)(G + (G & 1));
+    p.group_size = (int32_t)group_size;
+    p.l_h = (int32_t)l_h;
+    p.N1 = pl.N1; p.N2 = pl.N2; p.log1 = pl.log1; p.log2 = pl.log2;
+    p.N3 = pl.N3; p.log3 = pl.log3;
+    p.nb = (int32_t)B;
+    const bool f32 = dtype == HYENA_DTYPE_F32;
+    auto launch = [&](const void *fn, const FftParams &q_, int P, int64_t units, int64_t nb, int lds) -> int {
+        return fft_launch(fn, q_, P, units, nb, lds, s);
+    };
+    const int64_t M = (int64_t)pl.N2 * pl.N3;
+    const int64_t cols = M / 2 + 1;
+    const int64_t row_units = pl.three ? (int64_t)pl.N1 * pl.N2 : pl.N1;
+    const int64_t mid_units = (int64_t)pl.N1 * pl.N3;
+    const void *rows_seq, *rows_flt;
+    if (pl.three) {
+        rows_seq = f32 ? (const void *)fft_rows3_kernel<true, 0> : (const void *)fft_rows3_kernel<false, 0>;
+        rows_flt = f32 ? (const void *)fft_rows3_kernel<true, 1> : (const void *)fft_rows3_kernel<false, 1>;
+    } else {
+        rows_seq = f32 ? (const void *)fft_rows_kernel<true, 0> : (const void *)fft_rows_kernel<false, 0>;
+        rows_flt = f32 ? (const void *)fft_rows_kernel<true, 1> : (const void *)fft_rows_kernel<false, 1>;
+    }
+    // the last inverse pass with each output form
+    auto out_fn = [&](int mode) -> const void * {
+        if (pl.three) {
+            if (mode == 0) return f32 ? (const void *)fft_out3_kernel<true, 0> : (const void *)fft_out3_kernel<false, 0>;
+            if (mode == 1) return f32 ? (const void *)fft_out3_kernel<true, 1> : (const void *)fft_out3_kernel<false, 1>;
+            return (const void *)fft_out3_kernel<true, 2>;
+        }
+        if (mode == 0) return f32 ? (const void *)fft_out_kernel<true, 0> : (const void *)fft_out_kernel<false, 0>;
+        if (mode == 1) return f32 ? (const void *)fft_out_kernel<true, 1> : (const void *)fft_out_kernel<false, 1>;
+        return (const void *)fft_out_kernel<true, 2>;
+    };
+
+    // filter spectra (the first work area serves as the filter pass's)
+    {
+        FftParams ph = p;
+        ph.L = taps;
+        ph.np = p.Gp / 2;
+        st = launch(rows_flt, ph, pl.P_rows, row_units, 1, pl.lds_rows);
+        if (st == HYENA_OK && pl.three)
+            st = launch((const void *)fft_mid_kernel<false>, ph, pl.P_mid, mid_units, 1, pl.lds_mid);
+        if (st == HYENA_OK) st = launch((const void *)fft_cols_kernel<0>, ph, pl.P_cols, cols, 1, pl.lds_cols);
+    }
+    p.L = L;
+    p.np = (int32_t)(D / 2);
+    float2 *area_dz = (float2 *)((char *)p.ws + pl.area_bytes);
+    // x = k v into the first work area, dz = dy q into the second
+    {
+        FftParams px = p;
+        px.k = k; px.v = v;
+        if (st == HYENA_OK) st = launch(rows_seq, px, pl.P_rows, row_units, B, pl.lds_rows);
+        FftParams pz = p;
+        pz.k = dy; pz.v = q; pz.ws = area_dz;
+        if (st == HYENA_OK) st = launch(rows_seq, pz, pl.P_rows, row_units, B, pl.lds_rows);
+    }
+    // the middle passes cover both work areas as 2B batch rows
+    if (st == HYENA_OK && pl.three)
+        st = launch((const void *)fft_mid_kernel<false>, p, pl.P_mid, mid_units, 2 * B, pl.lds_mid);
+    {
+        FftParams pc = p;
+        pc.part = dh ? (float2 *)((char *)p.ws + 2 * pl.area_bytes) : nullptr;
+        pc.n_slots = (int32_t)pl.n_slots;
+        if (st == HYENA_OK) st = launch((const void *)fft_bwd_cols_kernel, pc, pl.P_bwd, cols, B, pl.lds_bwd);
+    }
+    if (st == HYENA_OK && pl.three && (dq || dk))
+        st = launch((const void *)fft_mid_kernel<true>, p, pl.P_mid, mid_units, 2 * B, pl.lds_mid);
+    if (st == HYENA_OK && dq) {
+        FftParams po = p;
+        po.q = dy; po.y = dq;
+        st = launch(out_fn(0), po, pl.P_rows, row_units, B, pl.lds_rows);
+    }
+    if (st == HYENA_OK && dk) {
+        FftParams po = p;
+        po.ws = area_dz; po.k = k; po.v = v; po.y = dk; po.y2 = dv;
+        st = launch(out_fn(1), po, pl.P_rows, row_units, B, pl.lds_rows);
+    }
+    if (st == HYENA_OK && dh) {
+        // group spectra -> one-row work area of Gp/2 group pairs (the first
+        // work area, free once dq is out) -> inverse along f2 -> dh rows < taps
+        FftParams pd = p;
+        pd.part = (float2 *)((char *)p.ws + 2 * pl.area_bytes);
+        pd.np = p.Gp / 2;
+        pd.nb = (int32_t)B;
+        pd.pb_log = 0;
+        while ((1 << pd.pb_log) < pl.P_bwd) ++pd.pb_log;
+        pd.pb_tiles = (int32_t)pl.pb_tiles;
+        pd.n_slots = (int32_t)pl.n_slots;
+        st = launch((const void *)fft_dh_cols_kernel, pd, pl.P_dh, cols, 1, pl.lds_dh);
+        pd.L = taps;
+        pd.y = dh;
+        if (st == HYENA_OK && pl.three)
+            st = launch((const void *)fft_mid_kernel<true>, pd, pl.P_mid, mid_units, 1, pl.lds_mid);
+        if (st == HYENA_OK) st = launch(out_fn(2), pd, pl.P_rows, row_units, 1, pl.lds_rows);
+        if (st == HYENA_OK && l_h > taps) {
+            const int64_t n = G * (l_h - taps);
+            hipLaunchKernelGGL(fft_dh_tail_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dh, G, l_h,
+                               taps);
+        }
+    }
+    if (st != HYENA_OK) return st;
+    if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
+    return HYENA_OK;
 }
 
 }  // extern "C"

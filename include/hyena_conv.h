@@ -226,6 +226,41 @@ int hyena_conv_fwd_long_workspace(int64_t B, int64_t L, int64_t D,
                                   int64_t group_size, int64_t l_h, int dtype,
                                   int64_t *bytes_out);
 
+/* Backward of the long-filter forward, for filters of any length l_h >= 1:
+ * the gradients of hyena_conv_bwd (same definitions, layouts, dtypes and
+ * optional outputs: any of dq, dh may be NULL; dk and dv are both given or
+ * both NULL; dh is float32 [D / group_size, l_h]), computed with the FFT
+ * convolution of hyena_conv_fwd_long (StripedHyena 2 explainer: page
+ * "01. overview", section 2, long convolutions in O(N log N); page
+ * "04. hardware-aware convolution kernels", section 7, the filter gradient
+ * is a global accumulation, here summed over channels and batch rows in the
+ * frequency domain before one inverse transform per group).  With
+ * N >= L + min(l_h, L) - 1 a power of two (at most 2^22):
+ *     dq = dy (.) IFFT(H X),  dx = IFFT(conj(H) DZ),  dk = dx (.) v,
+ *     dv = dx (.) k,  dh[g, s] = IFFT(sum_{b, c in g} DZ_c conj(X_c))[s],
+ * x = k (.) v and dz = dy (.) q (exact in fp32 for bf16 inputs); dh is zero
+ * at taps s >= L.  Transforms and sums are fp32 for both dtypes, with the
+ * error of an fp32 FFT.  `workspace` (16-byte aligned, at least
+ * hyena_conv_bwd_long_workspace bytes whenever an output is requested and
+ * the problem has rows; contents need not be initialised) is overwritten.
+ * D must be even, else HYENA_ERR_UNSUPPORTED.  Outputs and workspace must
+ * not overlap the inputs or each other.  Results are the same run to run
+ * (no atomics; fixed summation order). */
+int hyena_conv_bwd_long(const void *q, const void *k, const void *v,
+                        const void *h, const void *dy, int64_t B, int64_t L,
+                        int64_t D, int64_t group_size, int64_t l_h, void *dq,
+                        void *dk, void *dv, float *dh, int dtype,
+                        void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Bytes of workspace hyena_conv_bwd_long needs (written to *bytes_out):
+ * 8 N (G' + B D + B T S) with N the transform length, G' the filter count
+ * rounded up to even and T S the column tiles times the group slots per
+ * tile of the filter gradient's partial sums (T S <= G + D).  Host only.
+ * Returns a status. */
+int hyena_conv_bwd_long_workspace(int64_t B, int64_t L, int64_t D,
+                                  int64_t group_size, int64_t l_h, int dtype,
+                                  int64_t *bytes_out);
+
 /* The work split hyena_conv_fwd_ex would use: writes the chunks per
  * workgroup and the workgroup count.  Host only; runs the same argument
  * checks on the sizes (pointers are not inspected).  Returns a status. */

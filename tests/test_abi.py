@@ -335,3 +335,57 @@ def test_long_filter_spectra_flag_is_checked_on_host():
     assert call(a["h"], 2) == -2 and call(a["h"], -1) == -2
     assert call(None, 0) == -1          # the spectra are computed from h
     assert call(None, 1) == -10         # h is not needed with kept spectra; the workspace still is
+
+
+def _bwd_long(q=P["q"], k=P["k"], v=P["v"], h=P["h"], dy=P["out"] + (128 << 20), B=1, L=128, D=64, gs=16,
+              l_h=1000, dq=P["out"], dk=P["out"] + (1 << 20), dv=P["out"] + (2 << 20),
+              dh=P["out"] + (3 << 20), dtype=hc.DTYPE_BF16, ws=P["out"] + (64 << 20), ws_n=1 << 30):
+    return hc.lib().hyena_conv_bwd_long(q, k, v, h, dy, B, L, D, gs, l_h, dq, dk, dv, dh, dtype, ws, ws_n,
+                                        None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(dy=None), -1), (dict(h=None), -1), (dict(dk=None), -1), (dict(dv=None), -1),
+    (dict(B=-1), -2), (dict(gs=0), -3), (dict(D=64, gs=48), -3), (dict(l_h=0), -4),
+    (dict(D=63, gs=1), -7), (dict(L=1 << 23), -7),
+    (dict(q=P["q"] + 8), -5), (dict(dq=P["out"] + 8), -5), (dict(dh=P["out"] + (3 << 20) + 2), -5),
+    (dict(ws=P["out"] + (64 << 20) + 4), -5),
+    (dict(dq=P["k"]), -6), (dict(dh=P["h"]), -6), (dict(ws=P["v"]), -6), (dict(ws=P["out"]), -6),
+    (dict(dk=P["out"] + (2 << 20), dv=P["out"] + (2 << 20)), -6),
+    (dict(ws=None), -10), (dict(ws_n=1024), -10), (dict(dtype=3), -9),
+])
+def test_long_filter_backward_validates_on_host(kw, code):
+    assert _bwd_long(**kw) == code
+
+
+def test_long_filter_backward_without_outputs_is_a_host_no_op():
+    assert _bwd_long(dq=None, dk=None, dv=None, dh=None, ws=None, ws_n=0) == 0
+
+
+def test_long_filter_backward_workspace_size():
+    # 8 N (G' + B D + B T S): spectra, the x and dz work areas, and the
+    # filter gradient's partial sums (T column tiles of P channel pairs, S
+    # group slots per tile).  P: the largest power of two <= 64 with 8 N1 P <= 4096
+    # complex values of LDS, no larger than needed for D / 2 pairs.
+    def expect(B, L, D, gs, l_h):
+        n = 1 << max(2, (L + min(l_h, L) - 2).bit_length())
+        log_n = n.bit_length() - 1
+        log1 = (log_n + 2) // 3 if log_n > 16 else (log_n + 1) // 2
+        n1 = 1 << log1
+        P = 64
+        while P > 1 and 8 * n1 * P > 4096:
+            P //= 2
+        while P > 1 and P // 2 >= D // 2:
+            P //= 2
+        G = D // gs
+        Gp = G + (G & 1)
+        T = (D // 2 + P - 1) // P
+        S = min(G, (2 * P - 1 + gs - 1) // gs + 1)
+        assert T * S <= G + D
+        return 8 * n * (Gp + B * D + B * T * S)
+    for args in [(1, 8192, 4096, 16, 8192), (2, 1000, 64, 1, 37), (1, 5, 6, 3, 1000), (3, 1, 2, 1, 1),
+                 (1, 1 << 20, 64, 64, 1 << 20), (2, 3000, 10, 5, 100)]:
+        assert hc.bwd_long_workspace_bytes(*args) == expect(*args), args
+    assert hc.bwd_long_workspace_bytes(0, 8192, 4096, 16, 8192) == 0
+    with pytest.raises(hc.HyenaError):
+        hc.bwd_long_workspace_bytes(1, 100, 7, 1, 10)  # odd D

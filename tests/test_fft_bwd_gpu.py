@@ -1,0 +1,245 @@
+"""GPU parity of the long-filter backward (hyena_conv_bwd_long, FFT convolution).
+
+Bars, per channel d of group g, batch row b and transform length N (fp32
+transforms for both I/O types; x = k v and dz = dy q are exact in fp32 for
+bf16 inputs), with e = (log2 N + 2) * 7 * 2^-24 and r = 2^-8 (bf16 output
+rounding) or 2^-24 (fp32), the norm-wise error of an fp32 FFT convolution
+carried through two forward transforms, the product and the inverse:
+
+    dq: |err| <= r |ref| + |dy| * 3 e sqrt(N) ||h_g|| ||x_bd||
+    dk: |err| <= r |ref| + |v|  * 3 e sqrt(N) ||h_g|| ||dz_bd||     (dv: |k|)
+    dh: |err| <= 3 e sqrt(N) * sum_{b, d in g} ||dz_bd|| ||x_bd||
+
+plus the gates max|err| <= 1e-2 max|ref| (bf16) or 1e-5 max|ref| (fp32) for
+dq, dk, dv, and 1e-5 max|ref| for dh (fp32 output; an fp32 FFT correlation of
+N(0, 1) sequences errs by about 2e-7 of the largest lag).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gated_convolution_sequence_amd as hc
+import oracle
+from gpu_util import DEV, TINY, log, to_np, transform_len
+from workloads import gaussian_inputs
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    hc.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _dy(B, L, D, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(B, L, D, generator=g).to(dtype)
+
+
+def _run(q, k, v, h, dy, gs, pad=16, **need):
+    """hyena_conv_bwd_long into NaN-filled outputs with canaries around each."""
+    B, L, D = q.shape
+    G, l_h = h.shape
+    n = q.numel()
+    bigs, outs = [], []
+    for shape, dt, cnt in (((B, L, D), q.dtype, n), ((B, L, D), q.dtype, n), ((B, L, D), q.dtype, n),
+                           ((G, l_h), torch.float32, G * l_h)):
+        big = torch.full((cnt + 2 * pad,), 7.0, dtype=dt, device=DEV)
+        out = big[pad:pad + cnt].view(shape)
+        out.fill_(float("nan"))
+        bigs.append(big)
+        outs.append(out)
+    want = [need.get("dq", True), need.get("dkv", True), need.get("dkv", True), need.get("dh", True)]
+    code = hc.DTYPE_BF16 if q.dtype == torch.bfloat16 else hc.DTYPE_F32
+    ws_n = hc.bwd_long_workspace_bytes(B, L, D, gs, l_h, code)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xff)  # contents need not be initialised
+    ptr = lambda t, w: t.data_ptr() if w else None
+    st = hc.lib().hyena_conv_bwd_long(q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(), dy.data_ptr(),
+                                      B, L, D, gs, l_h, *[ptr(o, w) for o, w in zip(outs, want)], code,
+                                      ws.data_ptr(), ws_n, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, hc.strerror(st)
+    torch.cuda.synchronize()
+    for big, cnt in zip(bigs, (n, n, n, G * l_h)):
+        assert torch.all(big[:pad] == 7.0) and torch.all(big[pad + cnt:] == 7.0), "write outside an output"
+    return [o if w else None for o, w in zip(outs, want)]
+
+
+def check_long_bwd(got, q, k, v, h, dy, gs, dtype, what=""):
+    """Gates and norm-wise FFT bounds of all four gradients against the fp64 oracle."""
+    qn, kn, vn, hn, dyn = (to_np(t) for t in (q, k, v, h, dy))
+    ref = oracle.conv_bwd_ref(qn, kn, vn, hn, dyn, gs)
+    B, L, D = qn.shape
+    N = transform_len(L, hn.shape[1])
+    e = (math.log2(N) + 2) * 7 * 2.0 ** -24
+    r = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -24
+    x = kn * vn
+    dz = dyn * qn
+    xn = np.sqrt(np.sum(x * x, axis=1))                    # [B, D]
+    zn = np.sqrt(np.sum(dz * dz, axis=1))                  # [B, D]
+    hnorm = np.sqrt(np.sum(hn * hn, axis=1))[np.arange(D) // gs]  # [D]
+    k3 = 3 * e * math.sqrt(N)
+    rel = {}
+    bounds = {
+        "dq": np.abs(dyn) * (k3 * hnorm[None, None, :] * xn[:, None, :]),
+        "dk": np.abs(vn) * (k3 * hnorm[None, None, :] * zn[:, None, :]),
+        "dv": np.abs(kn) * (k3 * hnorm[None, None, :] * zn[:, None, :]),
+    }
+    for i, name in enumerate(("dq", "dk", "dv")):
+        if got[i] is None:
+            continue
+        y = to_np(got[i])
+        assert np.all(np.isfinite(y)), "%s %s" % (what, name)
+        err = np.abs(y - ref[i])
+        scale = float(np.max(np.abs(ref[i]))) if ref[i].size else 0.0
+        gate = (1e-2 if dtype == torch.bfloat16 else 1e-5) * scale
+        assert float(np.max(err, initial=0.0)) <= gate, "%s %s: max err %.3e > gate %.3e" % (
+            what, name, np.max(err), gate)
+        bad = np.argwhere(err > r * np.abs(ref[i]) + bounds[name] + TINY)
+        assert bad.size == 0, "%s %s: FFT bound broken at %s" % (what, name, bad[0])
+        rel[name] = float(np.max(err, initial=0.0)) / scale if scale else 0.0
+    if got[3] is not None:
+        dh = to_np(got[3])
+        assert np.all(np.isfinite(dh)), "%s dh" % what
+        err = np.abs(dh - ref[3])
+        scale = float(np.max(np.abs(ref[3]))) if ref[3].size else 0.0
+        assert float(np.max(err, initial=0.0)) <= 1e-5 * scale + TINY, "%s dh: max err %.3e > gate %.3e" % (
+            what, np.max(err), 1e-5 * scale)
+        G = D // gs
+        terms = (zn * xn).sum(axis=0).reshape(G, gs).sum(axis=1)  # [G]
+        bad = np.argwhere(err > k3 * terms[:, None] + TINY)
+        assert bad.size == 0, "%s dh: FFT bound broken at %s" % (what, bad[0])
+        taps = min(hn.shape[1], L)
+        assert np.all(dh[:, taps:] == 0.0), "%s dh: taps past the sequence must be zero" % what
+        rel["dh"] = float(np.max(err, initial=0.0)) / scale if scale else 0.0
+    return rel
+
+
+SHAPES = [
+    # B, L, D, group_size, l_h
+    (1, 1, 2, 1, 1), (1, 6, 4, 2, 4), (1, 100, 8, 1, 100), (2, 257, 16, 16, 257),
+    (1, 1000, 32, 2, 1000), (1, 1000, 32, 1, 37), (3, 777, 6, 3, 500), (1, 2048, 10, 5, 3000),
+    (2, 3000, 128, 16, 128), (1, 4096, 64, 16, 4096), (1, 3000, 256, 256, 3000),
+    (1, 8192, 16, 1, 8192),
+    (1, 40000, 4, 2, 40000),     # N = 2^17: the three-level split
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h", SHAPES)
+def test_long_backward_gaussian(dt, B, L, D, gs, l_h):
+    log("long bwd %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=3 * L + l_h + gs)
+    dy = _dy(B, L, D, dtype, seed=L + 5)
+    got = _run(*(t.to(DEV) for t in (q, k, v, h, dy)), gs)
+    rel = check_long_bwd(got, q, k, v, h, dy, gs, dtype, "long bwd")
+    log("  rel err %s" % ", ".join("%s %.2e" % kv for kv in rel.items()))
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_subsets_give_the_same_bits(dt):
+    """dq alone, dk and dv alone, dh alone: the same bits as the full call."""
+    dtype = DTYPES[dt]
+    B, L, D, gs, l_h = 2, 1500, 24, 3, 900
+    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(B, L, D, gs, l_h, dtype, seed=77))
+    dy = _dy(B, L, D, dtype, seed=78).to(DEV)
+    full = [t.clone() for t in _run(q, k, v, h, dy, gs)]
+    dq = _run(q, k, v, h, dy, gs, dkv=False, dh=False)
+    dkv = _run(q, k, v, h, dy, gs, dq=False, dh=False)
+    dh = _run(q, k, v, h, dy, gs, dq=False, dkv=False)
+    assert dq[1] is None and dq[3] is None and dkv[0] is None and dh[0] is None
+    assert torch.equal(dq[0], full[0])
+    assert torch.equal(dkv[1], full[1]) and torch.equal(dkv[2], full[2])
+    assert torch.equal(dh[3], full[3])
+    again = _run(q, k, v, h, dy, gs)
+    for a, b in zip(again, full):
+        assert torch.equal(a, b)  # run to run
+
+
+def test_matches_the_grouped_backward_for_short_filters():
+    """l_h <= 128 with 16-channel groups: the FFT backward and the grouped
+    kernels' backward (fp32) agree within their bars."""
+    B, L, D, gs, l_h = 2, 5000, 256, 16, 128
+    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(B, L, D, gs, l_h, torch.float32, seed=15))
+    dy = _dy(B, L, D, torch.float32, seed=16).to(DEV)
+    log("fft bwd vs grouped bwd")
+    fft = _run(q, k, v, h, dy, gs)
+    direct = hc.conv_bwd(q, k, v, h, dy, gs)
+    torch.cuda.synchronize()
+    for a, b, name in zip(fft, direct, ("dq", "dk", "dv", "dh")):
+        scale = float(b.abs().max())
+        assert float((a - b).abs().max()) <= 2e-5 * scale, name
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_impulse_gradients_three_level(dt):
+    """L = l_h = 2^19 (N = 2^20, three-level split), k = v = q = 1 and dy an
+    impulse at t0 on every channel: dz is that impulse, so dx[t] = h[t0 - t]
+    for t <= t0 and 0 after; dh[g, s] = group_size for s <= t0 (x = 1 at every
+    row), 0 after; dq = h's prefix sums at t0 on row t0 only."""
+    dtype = DTYPES[dt]
+    B, L, D, gs = 1, 1 << 19, 4, 2
+    t0 = 300000
+    g = torch.Generator().manual_seed(19)
+    h = (torch.randn(D // gs, L, generator=g) / math.sqrt(L)).to(dtype)
+    ones = torch.ones(B, L, D, dtype=dtype)
+    dy = torch.zeros(B, L, D, dtype=dtype)
+    dy[0, t0, :] = 1.0
+    log("impulse three-level %s" % dt)
+    dq, dk, dv, dh = (t.float().cpu() for t in _run(*(t.to(DEV) for t in (ones, ones, ones, h, dy)), gs))
+    hh = torch.repeat_interleave(h.float(), gs, dim=0)                # [D, L]
+    expect_dx = torch.zeros(L, D)
+    expect_dx[:t0 + 1, :] = hh[:, :t0 + 1].flip(1).T
+    tol_x = (1e-2 if dtype == torch.bfloat16 else 1e-5) * float(expect_dx.abs().max())
+    assert float((dk[0] - expect_dx).abs().max()) <= tol_x
+    assert float((dv[0] - expect_dx).abs().max()) <= tol_x
+    expect_dh = torch.zeros(D // gs, L)
+    expect_dh[:, :t0 + 1] = gs
+    assert float((dh - expect_dh).abs().max()) <= 1e-4 * gs
+    expect_dq_t0 = hh[:, :t0 + 1].sum(dim=1)                          # z[t0] = sum_s h[s] x[t0 - s]
+    scale = float(expect_dq_t0.abs().max())
+    assert float((dq[0, t0] - expect_dq_t0).abs().max()) <= (1e-2 if dtype == torch.bfloat16 else 1e-4) * scale
+    dq[0, t0] = 0
+    assert float(dq.abs().max()) == 0.0   # dy is zero elsewhere
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,gs,l_h", [(0, 100, 2, 300), (2, 0, 1, 7)])
+def test_backward_without_rows_zeroes_dh(dt, B, L, gs, l_h):
+    """No rows: dh is written with zeros (the caller's buffer starts as NaN
+    here), by a kernel; no workspace is needed."""
+    dtype, D = DTYPES[dt], 8
+    log("long bwd no rows %s B=%d L=%d" % (dt, B, L))
+    buf = torch.zeros(64, dtype=dtype, device=DEV)  # q, k, v, dy: no rows are read
+    h = torch.ones(D // gs, l_h, dtype=dtype, device=DEV)
+    dh = torch.full((D // gs, l_h), float("nan"), dtype=torch.float32, device=DEV)
+    code = hc.DTYPE_BF16 if dt == "bf16" else hc.DTYPE_F32
+    assert hc.bwd_long_workspace_bytes(B, L, D, gs, l_h, code) == 0
+    p = buf.data_ptr()
+    st = hc.lib().hyena_conv_bwd_long(p, p, p, h.data_ptr(), p, B, L, D, gs, l_h, None, None, None,
+                                      dh.data_ptr(), code, None, 0, torch.cuda.current_stream(DEV).cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(dh, torch.zeros_like(dh))
+
+
+def test_autograd_wrapper_matches_the_entry_point():
+    B, L, D, gs, l_h = 2, 700, 12, 3, 900
+    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(B, L, D, gs, l_h, torch.float32, seed=31))
+    dy = _dy(B, L, D, torch.float32, seed=32).to(DEV)
+    leaves = [t.clone().requires_grad_(True) for t in (q, k, v, h)]
+    y = hc.HyenaConvLong.apply(*leaves, gs)
+    y.backward(dy)
+    want = hc.conv_bwd_long(q, k, v, h, dy, gs)
+    torch.cuda.synchronize()
+    assert torch.equal(y, hc.conv_fwd_long(q, k, v, h, gs))
+    for leaf, w in zip(leaves, want):
+        assert torch.equal(leaf.grad, w)

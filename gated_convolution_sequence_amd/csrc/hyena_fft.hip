@@ -639,6 +639,104 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_cols_kernel(FftParams p) 
     }
 }
 
+// Backward column kernel, single-column form, for even group sizes (both
+// channels of every pair share a filter: H0 = H1 = H).  Per (batch, column
+// f2, pair tile): the N1-point transforms of the x and dz columns, then
+//     Z = H P_x[f],   DX = conj(H) P_dz[f],
+// both transformed back, twiddled and stored in place; and with `part` set
+// the partial sums P_dz[f] conj(P_x[f]) over the group's pairs in this tile.
+// For a pair (c0, c1) of one group the real part of the inverse transform of
+// P_dz conj(P_x) is the sum of the two channels' correlations (the cross
+// terms are imaginary); the filter-gradient column kernel keeps only the
+// Hermitian part of each group's spectrum, which is that real part.
+// LDS (dynamic): two buffers of 2 N1 P values -- element (t1, src, pair) at
+// (2 t1 + src) P + pair -- the N1 inner twiddles and the N1 inter-step
+// twiddles W_N^(-t1 f2).
+__global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) {
+    extern __shared__ float2 lds[];
+    const int item = xcd_item();
+    const int tile = item % p.n_tiles;
+    const int M = p.N2 * p.N3;  // columns
+    const int f2 = (item / p.n_tiles) % M;
+    const int b = item / (p.n_tiles * M);
+    const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1;
+    const int lS = logP + 1;
+    const int NS = N1 << lS;
+    const int sdz = 1 << logP;
+    const int64_t N = (int64_t)N1 * M;
+    const int64_t area = (int64_t)p.nb * N * p.np;
+    // work-area row of (f2, t1 = 0): column position as in the paired form
+    const int64_t col0 = ((int64_t)b * M + (int64_t)(f2 & (p.N3 - 1)) * p.N2 + (f2 >> p.log3)) * N1;
+    float2 *bufA = lds, *bufB = lds + NS, *tw = lds + 2 * NS, *wt = tw + N1;
+    stage_in(bufA, NS, [&](int i) {
+        const int src = (i >> logP) & 1;
+        const int j = (tile << logP) + (i & pmask);
+        const bool ok = j < p.np;
+        const float2 v = p.ws[src * area + (col0 + (i >> lS)) * p.np + (ok ? j : 0)];
+        return ok ? v : make_float2(0.0f, 0.0f);
+    });
+    fill_twiddles(tw, N1);
+    for (int t1 = threadIdx.x; t1 < N1; t1 += kFftThreads)
+        wt[t1] = cconj(twiddle(((int64_t)t1 * f2) & (N - 1), N));
+    __syncthreads();
+    float2 *S = lds_fft(bufA, bufB, tw, N1, p.log1, lS, false);
+    float2 *Z = S == bufA ? bufB : bufA;
+    // P divides the thread count: a thread keeps one pair (and filter row)
+    const int my_pp = threadIdx.x & pmask;
+    const int my_j = (tile << logP) + my_pp;
+    const int jc = min(my_j, p.np - 1);
+    const float2 *hrow = p.hs + (size_t)f2 * N1 * p.Gp + (2 * jc) / p.group_size;
+    const int NP = N1 << logP;
+    for (int base = 0; base < NP; base += kBatch * kFftThreads) {
+        float2 hh[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int f1 = min(base + u * kFftThreads + (int)threadIdx.x, NP - 1) >> logP;
+            hh[u] = hrow[(size_t)f1 * p.Gp];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = base + u * kFftThreads + (int)threadIdx.x;
+            if (i >= NP) continue;
+            const int ix = ((i >> logP) << lS) | my_pp;
+            const bool ok = my_j < p.np;
+            Z[ix] = ok ? cmul(hh[u], S[ix]) : make_float2(0.0f, 0.0f);
+            Z[ix + sdz] = ok ? cmul(cconj(hh[u]), S[ix + sdz]) : make_float2(0.0f, 0.0f);
+        }
+    }
+    if (p.part != nullptr) {
+        // one item per (f1, group slot): pairs lie inside one group
+        const int c_lo = (tile << logP) * 2;
+        const int c_end = min(c_lo + (2 << logP), 2 * p.np);
+        const int g0 = c_lo / p.group_size;
+        const int n_items = N1 * p.n_slots;
+        for (int it = threadIdx.x; it < n_items; it += kFftThreads) {
+            const int slot = it % p.n_slots;
+            const int f1 = it / p.n_slots;
+            const int g = g0 + slot;
+            const int lo = max(c_lo, g * p.group_size), hi = min(c_end, (g + 1) * p.group_size);
+            if (lo >= hi) continue;
+            float2 acc = make_float2(0.0f, 0.0f);
+            for (int pp = (lo - c_lo) >> 1; pp < (hi - c_lo) >> 1; ++pp) {
+                const int ix = (f1 << lS) | pp;
+                const float2 pr = cmul(S[ix + sdz], cconj(S[ix]));
+                acc.x += pr.x;
+                acc.y += pr.y;
+            }
+            p.part[((((int64_t)b * M + f2) * N1 + f1) * p.n_tiles + tile) * p.n_slots + slot] = acc;
+        }
+    }
+    __syncthreads();
+    const float2 *U = lds_fft(Z, S, tw, N1, p.log1, lS, true);
+    for (int i = threadIdx.x; i < NS; i += kFftThreads) {
+        const int src = (i >> logP) & 1;
+        const int j = (tile << logP) + (i & pmask);
+        if (j >= p.np) continue;
+        const int t1 = i >> lS;
+        p.ws[src * area + (col0 + t1) * p.np + j] = cmul(U[i], wt[t1]);
+    }
+}
+
 // Filter-gradient column kernel.  Per (column pair {f2, M - f2}, tile of P
 // group pairs): the spectrum of each group g, S_g = the partial sums over
 // the batch rows and the column tiles holding g's channels; its Hermitian
@@ -906,6 +1004,7 @@ struct FftPlan {
     // filter-gradient column kernel (group pairs per tile), LDS, and the
     // workspace: spectra, two work areas, partial sums
     int P_bwd, P_dh, lds_bwd, lds_dh;
+    bool bwd_col1;                   // the backward's single-column form (even group sizes)
     int64_t pb_tiles, n_slots, area_bytes, part_bytes, bwd_ws_bytes;
 };
 
@@ -924,6 +1023,10 @@ constexpr int kFftBudget = HYENA_FFT_BUDGET;
 #define HYENA_FFT_COLS_BUDGET HYENA_FFT_BUDGET
 #endif
 constexpr int kFftColsBudget = HYENA_FFT_COLS_BUDGET;  // the column kernel's
+#ifndef HYENA_FFT_BWD_BUDGET
+#define HYENA_FFT_BWD_BUDGET HYENA_FFT_BUDGET
+#endif
+constexpr int kFftBwdBudget = HYENA_FFT_BWD_BUDGET;  // the backward column kernels'
 int pick_pairs(int M, int buffers, int64_t pairs, int budget = kFftBudget) {
     int P = 64;
     while (P > 1 && (int64_t)buffers * M * P > budget) P >>= 1;
@@ -1002,8 +1105,15 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 int fft_bwd_plan(int64_t B, int64_t D, int64_t group_size, FftPlan *pl) {
     const int64_t G = D / group_size, Gp = G + (G & 1);
     const int64_t pairs = D / 2;
-    pl->P_bwd = pick_pairs(pl->N1, 8, pairs, kFftColsBudget);
-    pl->lds_bwd = (8 * pl->N1 * pl->P_bwd + 3 * pl->N1) * (int)sizeof(float2);
+    // even group sizes: the single-column form (4 N1 P values of LDS), else the paired one (8 N1 P)
+    pl->bwd_col1 = group_size % 2 == 0;
+    if (pl->bwd_col1) {
+        pl->P_bwd = pick_pairs(pl->N1, 4, pairs, kFftBwdBudget);
+        pl->lds_bwd = (4 * pl->N1 * pl->P_bwd + 2 * pl->N1) * (int)sizeof(float2);
+    } else {
+        pl->P_bwd = pick_pairs(pl->N1, 8, pairs, kFftBwdBudget);
+        pl->lds_bwd = (8 * pl->N1 * pl->P_bwd + 3 * pl->N1) * (int)sizeof(float2);
+    }
     pl->P_dh = pick_pairs(pl->N1, 8, Gp / 2, kFftColsBudget);
     pl->lds_dh = (8 * pl->N1 * pl->P_dh + 3 * pl->N1) * (int)sizeof(float2);
     if (pl->lds_bwd > kFftMaxLdsBytes || pl->lds_dh > kFftMaxLdsBytes) return HYENA_ERR_UNSUPPORTED;
@@ -1267,7 +1377,9 @@ int hyena_conv_bwd_long(const void *q, const void *k, const void *v, const void 
         FftParams pc = p;
         pc.part = dh ? (float2 *)((char *)p.ws + 2 * pl.area_bytes) : nullptr;
         pc.n_slots = (int32_t)pl.n_slots;
-        if (st == HYENA_OK) st = launch((const void *)fft_bwd_cols_kernel, pc, pl.P_bwd, cols, B, pl.lds_bwd);
+        if (st == HYENA_OK)
+            st = pl.bwd_col1 ? launch((const void *)fft_bwd_col1_kernel, pc, pl.P_bwd, M, B, pl.lds_bwd)
+                             : launch((const void *)fft_bwd_cols_kernel, pc, pl.P_bwd, cols, B, pl.lds_bwd);
     }
     if (st == HYENA_OK && pl.three && (dq || dk))
         st = launch((const void *)fft_mid_kernel<true>, p, pl.P_mid, mid_units, 2 * B, pl.lds_mid);

@@ -49,6 +49,28 @@ constexpr int kFftThreads = 256;
 static_assert(kFftThreads % 128 == 0, "pair tiles of up to 64 pairs");
 constexpr int kFftMaxLogN = 22;      // N <= 2^22
 constexpr int kFftMaxLdsBytes = 160 * 1024;
+// LDS per workgroup in complex values (pair tiles are sized to it)
+#ifndef HYENA_FFT_BUDGET
+#define HYENA_FFT_BUDGET 4096
+#endif
+constexpr int kFftBudget = HYENA_FFT_BUDGET;
+#ifndef HYENA_FFT_COLS_BUDGET
+#define HYENA_FFT_COLS_BUDGET HYENA_FFT_BUDGET
+#endif
+constexpr int kFftColsBudget = HYENA_FFT_COLS_BUDGET;  // the paired column kernels'
+#ifndef HYENA_FFT_BWD_BUDGET
+#define HYENA_FFT_BWD_BUDGET HYENA_FFT_BUDGET
+#endif
+constexpr int kFftBwdBudget = HYENA_FFT_BWD_BUDGET;  // the backward column kernels'
+// The row, middle, output and single-column kernels transform in place (one
+// LDS buffer: every value of a stage is read into registers, a barrier, then
+// written), so their pair tiles are twice as wide as with two buffers.
+#ifndef HYENA_FFT_INPLACE
+#define HYENA_FFT_INPLACE 1
+#endif
+constexpr bool kFftInPlace = HYENA_FFT_INPLACE != 0;
+// values per thread an in-place stage holds: M P <= kFftIpVals * kFftThreads
+constexpr int kFftIpVals = kFftBudget / kFftThreads > 16 ? kFftBudget / kFftThreads : 16;
 
 struct FftParams {
     const void *q, *k, *v, *h;
@@ -251,25 +273,107 @@ __device__ __forceinline__ float2 *lds_fft(float2 *x, float2 *y, const float2 *t
     return x;
 }
 
-// Global -> LDS staging of n values, kBatch per thread at a time: the loads
-// of a batch are issued together (indices clamped into range, so none is
-// conditional) and waited for once.
+// One Stockham stage in place: the same butterflies as fft_stage, every
+// value read into registers first (at most kFftIpVals per thread), then a
+// barrier, then the writes.
+template <int R, bool INV>
+__device__ __forceinline__ void fft_stage_ip(float2 *x, const float2 *tw, int M, int logP, int Ns, int logNs) {
+    constexpr int U = kFftIpVals / R > 0 ? kFftIpVals / R : 1;
+    const int pmask = (1 << logP) - 1;
+    const int n = (M / R) << logP;
+    const int tstride = (M / R) >> logNs;
+    float2 v[U][R];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = threadIdx.x + u * kFftThreads;
+        if (i >= n) continue;
+        const int k = (i >> logP) & (Ns - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) v[u][r] = x[i + r * n];
+        if (Ns > 1) {
+#pragma unroll
+            for (int r = 1; r < R; ++r) {
+                float2 w = tw[r * k * tstride];
+                if (INV) w.y = -w.y;
+                v[u][r] = cmul(v[u][r], w);
+            }
+        }
+        dft<R, INV>(v[u]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = threadIdx.x + u * kFftThreads;
+        if (i >= n) continue;
+        const int j = i >> logP, p = i & pmask, k = j & (Ns - 1);
+        const int d = (j - k) * R + k;
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[((d + r * Ns) << logP) + p] = v[u][r];
+    }
+    __syncthreads();
+}
+
+// lds_fft in place on x (M P <= kFftIpVals * kFftThreads); ends synchronised.
+__device__ __forceinline__ void lds_fft_ip(float2 *x, const float2 *tw, int M, int logM, int logP, bool inverse) {
+    int Ns = 1, logNs = 0;
+    while (logNs < logM) {
+        const int lr = logM - logNs >= 4 ? 4 : logM - logNs;
+        if (inverse) {
+            if (lr == 4) fft_stage_ip<16, true>(x, tw, M, logP, Ns, logNs);
+            else if (lr == 3) fft_stage_ip<8, true>(x, tw, M, logP, Ns, logNs);
+            else if (lr == 2) fft_stage_ip<4, true>(x, tw, M, logP, Ns, logNs);
+            else fft_stage_ip<2, true>(x, tw, M, logP, Ns, logNs);
+        } else {
+            if (lr == 4) fft_stage_ip<16, false>(x, tw, M, logP, Ns, logNs);
+            else if (lr == 3) fft_stage_ip<8, false>(x, tw, M, logP, Ns, logNs);
+            else if (lr == 2) fft_stage_ip<4, false>(x, tw, M, logP, Ns, logNs);
+            else fft_stage_ip<2, false>(x, tw, M, logP, Ns, logNs);
+        }
+        Ns <<= lr;
+        logNs += lr;
+    }
+}
+
+// The transform of the row-like kernels: in place on buf0 (buf1 unused), or
+// ping-ponged between buf0 and buf1.  Returns the buffer holding the result.
+__device__ __forceinline__ float2 *lds_fft1(float2 *buf0, float2 *buf1, const float2 *tw, int M, int logM, int logP,
+                                          bool inverse) {
+    if constexpr (kFftInPlace) {
+        lds_fft_ip(buf0, tw, M, logM, logP, inverse);
+        return buf0;
+    } else {
+        return lds_fft(buf0, buf1, tw, M, logM, logP, inverse);
+    }
+}
+constexpr int kRowBufs = kFftInPlace ? 1 : 2;  // LDS buffers of the row-like kernels
+
+// Global -> LDS staging of n values, NB per thread at a time: the loads of a
+// batch are issued together (indices clamped into range, so none is
+// conditional) and waited for once.  Sixteen at a time when a thread stages
+// at least that many (all of a 4096-value tile in one batch), else eight.
 #ifndef HYENA_FFT_BATCH
 #define HYENA_FFT_BATCH 8
 #endif
-constexpr int kBatch = HYENA_FFT_BATCH;
-template <typename Load>
-__device__ inline void stage_in(float2 *dst, int n, Load load) {
-    for (int base = 0; base < n; base += kBatch * kFftThreads) {
-        float2 r[kBatch];
+constexpr int kBatch = HYENA_FFT_BATCH;  // also the batch of the filter-spectrum loads
+template <int NB, typename Load>
+__device__ inline void stage_in_nb(float2 *dst, int n, Load load) {
+    for (int base = 0; base < n; base += NB * kFftThreads) {
+        float2 r[NB];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) r[u] = load(min(base + u * kFftThreads + (int)threadIdx.x, n - 1));
+        for (int u = 0; u < NB; ++u) r[u] = load(min(base + u * kFftThreads + (int)threadIdx.x, n - 1));
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+        for (int u = 0; u < NB; ++u) {
             const int i = base + u * kFftThreads + (int)threadIdx.x;
             if (i < n) dst[i] = r[u];
         }
     }
+}
+template <typename Load>
+__device__ inline void stage_in(float2 *dst, int n, Load load) {
+    if (n >= 16 * kFftThreads)
+        stage_in_nb<16>(dst, n, load);
+    else
+        stage_in_nb<kBatch>(dst, n, load);
 }
 
 // Input pair j at row t, zero past the end of the sequence or the pairs:
@@ -324,14 +428,14 @@ __global__ __launch_bounds__(kFftThreads) void fft_rows_kernel(FftParams p) {
     const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1, N2 = p.N2;
     const int NP = N2 << logP;
     const int64_t N = (int64_t)N1 * N2;
-    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + 2 * NP, *wt = tw + N2;
+    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + kRowBufs * NP, *wt = tw + N2;
     stage_in(buf0, NP, [&](int i) {
         return load_pair<F32, SRC>(p, b, t1 + (int64_t)N1 * (i >> logP), (tile << logP) + (i & pmask));
     });
     fill_twiddles(tw, N2);
     for (int f2 = threadIdx.x; f2 < N2; f2 += kFftThreads) wt[f2] = twiddle(((int64_t)t1 * f2) & (N - 1), N);
     __syncthreads();
-    const float2 *X = lds_fft(buf0, buf1, tw, N2, p.log2, logP, false);
+    const float2 *X = lds_fft1(buf0, buf1, tw, N2, p.log2, logP, false);
     for (int i = threadIdx.x; i < NP; i += kFftThreads) {
         const int f2 = i >> logP;
         const int j = (tile << logP) + (i & pmask);
@@ -464,7 +568,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_col1_kernel(FftParams p) {
     const int64_t N = (int64_t)N1 * M;
     // work-area row of (f2, t1 = 0): column position as in the paired form
     const int64_t col0 = ((int64_t)b * M + (int64_t)(f2 & (p.N3 - 1)) * p.N2 + (f2 >> p.log3)) * N1;
-    float2 *bufA = lds, *bufB = lds + NP, *tw = lds + 2 * NP, *wt = tw + N1;
+    float2 *bufA = lds, *bufB = lds + NP, *tw = lds + kRowBufs * NP, *wt = tw + N1;
     stage_in(bufA, NP, [&](int i) {
         const int j = (tile << logP) + (i & pmask);
         const bool ok = j < p.np;
@@ -475,8 +579,10 @@ __global__ __launch_bounds__(kFftThreads) void fft_col1_kernel(FftParams p) {
     for (int t1 = threadIdx.x; t1 < N1; t1 += kFftThreads)
         wt[t1] = cconj(twiddle(((int64_t)t1 * f2) & (N - 1), N));
     __syncthreads();
-    float2 *S = lds_fft(bufA, bufB, tw, N1, p.log1, logP, false);
-    float2 *Z = S == bufA ? bufB : bufA;
+    float2 *S = lds_fft1(bufA, bufB, tw, N1, p.log1, logP, false);
+    // the product goes to the other buffer, or (in place) over S: each
+    // thread rewrites only the values it reads
+    float2 *Z = kFftInPlace ? S : (S == bufA ? bufB : bufA);
     // P divides the thread count, so a thread always has the same pair and
     // its filter spectrum row is fixed
     const int my_j = (tile << logP) + (threadIdx.x & pmask);
@@ -497,7 +603,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_col1_kernel(FftParams p) {
         }
     }
     __syncthreads();
-    const float2 *U = lds_fft(Z, S, tw, N1, p.log1, logP, true);
+    const float2 *U = lds_fft1(Z, S, tw, N1, p.log1, logP, true);
     for (int i = threadIdx.x; i < NP; i += kFftThreads) {
         const int j = (tile << logP) + (i & pmask);
         if (j >= p.np) continue;
@@ -667,7 +773,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) 
     const int64_t area = (int64_t)p.nb * N * p.np;
     // work-area row of (f2, t1 = 0): column position as in the paired form
     const int64_t col0 = ((int64_t)b * M + (int64_t)(f2 & (p.N3 - 1)) * p.N2 + (f2 >> p.log3)) * N1;
-    float2 *bufA = lds, *bufB = lds + NS, *tw = lds + 2 * NS, *wt = tw + N1;
+    float2 *bufA = lds, *bufB = lds + NS, *tw = lds + kRowBufs * NS, *wt = tw + N1;
     stage_in(bufA, NS, [&](int i) {
         const int src = (i >> logP) & 1;
         const int j = (tile << logP) + (i & pmask);
@@ -679,8 +785,33 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) 
     for (int t1 = threadIdx.x; t1 < N1; t1 += kFftThreads)
         wt[t1] = cconj(twiddle(((int64_t)t1 * f2) & (N - 1), N));
     __syncthreads();
-    float2 *S = lds_fft(bufA, bufB, tw, N1, p.log1, lS, false);
-    float2 *Z = S == bufA ? bufB : bufA;
+    float2 *S = lds_fft1(bufA, bufB, tw, N1, p.log1, lS, false);
+    // products to the other buffer, or (in place) over S once the partial
+    // sums, which read other threads' values, are done
+    float2 *Z = kFftInPlace ? S : (S == bufA ? bufB : bufA);
+    if (p.part != nullptr) {
+        // one item per (f1, group slot): pairs lie inside one group
+        const int c_lo = (tile << logP) * 2;
+        const int c_end = min(c_lo + (2 << logP), 2 * p.np);
+        const int g0 = c_lo / p.group_size;
+        const int n_items = N1 * p.n_slots;
+        for (int it = threadIdx.x; it < n_items; it += kFftThreads) {
+            const int slot = it % p.n_slots;
+            const int f1 = it / p.n_slots;
+            const int g = g0 + slot;
+            const int lo = max(c_lo, g * p.group_size), hi = min(c_end, (g + 1) * p.group_size);
+            if (lo >= hi) continue;
+            float2 acc = make_float2(0.0f, 0.0f);
+            for (int pp = (lo - c_lo) >> 1; pp < (hi - c_lo) >> 1; ++pp) {
+                const int ix = (f1 << lS) | pp;
+                const float2 pr = cmul(S[ix + sdz], cconj(S[ix]));
+                acc.x += pr.x;
+                acc.y += pr.y;
+            }
+            p.part[((((int64_t)b * M + f2) * N1 + f1) * p.n_tiles + tile) * p.n_slots + slot] = acc;
+        }
+    }
+    if constexpr (kFftInPlace) __syncthreads();
     // P divides the thread count: a thread keeps one pair (and filter row)
     const int my_pp = threadIdx.x & pmask;
     const int my_j = (tile << logP) + my_pp;
@@ -704,30 +835,8 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) 
             Z[ix + sdz] = ok ? cmul(cconj(hh[u]), S[ix + sdz]) : make_float2(0.0f, 0.0f);
         }
     }
-    if (p.part != nullptr) {
-        // one item per (f1, group slot): pairs lie inside one group
-        const int c_lo = (tile << logP) * 2;
-        const int c_end = min(c_lo + (2 << logP), 2 * p.np);
-        const int g0 = c_lo / p.group_size;
-        const int n_items = N1 * p.n_slots;
-        for (int it = threadIdx.x; it < n_items; it += kFftThreads) {
-            const int slot = it % p.n_slots;
-            const int f1 = it / p.n_slots;
-            const int g = g0 + slot;
-            const int lo = max(c_lo, g * p.group_size), hi = min(c_end, (g + 1) * p.group_size);
-            if (lo >= hi) continue;
-            float2 acc = make_float2(0.0f, 0.0f);
-            for (int pp = (lo - c_lo) >> 1; pp < (hi - c_lo) >> 1; ++pp) {
-                const int ix = (f1 << lS) | pp;
-                const float2 pr = cmul(S[ix + sdz], cconj(S[ix]));
-                acc.x += pr.x;
-                acc.y += pr.y;
-            }
-            p.part[((((int64_t)b * M + f2) * N1 + f1) * p.n_tiles + tile) * p.n_slots + slot] = acc;
-        }
-    }
     __syncthreads();
-    const float2 *U = lds_fft(Z, S, tw, N1, p.log1, lS, true);
+    const float2 *U = lds_fft1(Z, S, tw, N1, p.log1, lS, true);
     for (int i = threadIdx.x; i < NS; i += kFftThreads) {
         const int src = (i >> logP) & 1;
         const int j = (tile << logP) + (i & pmask);
@@ -881,7 +990,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_rows3_kernel(FftParams p) {
     const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1, N2 = p.N2, N3 = p.N3;
     const int NP = N3 << logP;
     const int64_t M = (int64_t)N2 * N3;
-    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + 2 * NP, *wt = tw + N3;
+    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + kRowBufs * NP, *wt = tw + N3;
     stage_in(buf0, NP, [&](int i) {
         return load_pair<F32, SRC>(p, b, t1 + (int64_t)N1 * (t2 + (int64_t)N2 * (i >> logP)),
                                    (tile << logP) + (i & pmask));
@@ -889,7 +998,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_rows3_kernel(FftParams p) {
     fill_twiddles(tw, N3);
     for (int f3 = threadIdx.x; f3 < N3; f3 += kFftThreads) wt[f3] = twiddle(((int64_t)t2 * f3) & (M - 1), M);
     __syncthreads();
-    const float2 *X = lds_fft(buf0, buf1, tw, N3, p.log3, logP, false);
+    const float2 *X = lds_fft1(buf0, buf1, tw, N3, p.log3, logP, false);
     for (int i = threadIdx.x; i < NP; i += kFftThreads) {
         const int f3 = i >> logP;
         const int j = (tile << logP) + (i & pmask);
@@ -910,7 +1019,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_mid_kernel(FftParams p) {
     const int NP = N2 << logP;
     const int64_t M = (int64_t)N2 * N3;
     const int64_t N = M * N1;
-    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + 2 * NP, *wt = tw + N2;
+    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + kRowBufs * NP, *wt = tw + N2;
     const int64_t row0 = (int64_t)b * M + (int64_t)f3 * N2;  // position of index 0 along t2 / f2
     stage_in(buf0, NP, [&](int i) {
         const int j = (tile << logP) + (i & pmask);
@@ -923,7 +1032,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_mid_kernel(FftParams p) {
         wt[u] = INV ? cconj(twiddle(((int64_t)u * f3) & (M - 1), M))
                     : twiddle(((int64_t)t1 * (f3 + (int64_t)N3 * u)) & (N - 1), N);
     __syncthreads();
-    const float2 *X = lds_fft(buf0, buf1, tw, N2, p.log2, logP, INV);
+    const float2 *X = lds_fft1(buf0, buf1, tw, N2, p.log2, logP, INV);
     for (int i = threadIdx.x; i < NP; i += kFftThreads) {
         const int u = i >> logP;
         const int j = (tile << logP) + (i & pmask);
@@ -944,7 +1053,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_out3_kernel(FftParams p) {
     const int NP = N3 << logP;
     const int64_t M = (int64_t)N2 * N3;
     const float scale = 1.0f / ((float)N1 * (float)M);
-    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + 2 * NP;
+    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + kRowBufs * NP;
     stage_in(buf0, NP, [&](int i) {
         const int j = (tile << logP) + (i & pmask);
         const bool ok = j < p.np;
@@ -953,7 +1062,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_out3_kernel(FftParams p) {
     });
     fill_twiddles(tw, N3);
     __syncthreads();
-    const float2 *z = lds_fft(buf0, buf1, tw, N3, p.log3, logP, true);
+    const float2 *z = lds_fft1(buf0, buf1, tw, N3, p.log3, logP, true);
     for (int i = threadIdx.x; i < NP; i += kFftThreads) {
         const int t3 = i >> logP;
         const int j = (tile << logP) + (i & pmask);
@@ -975,7 +1084,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_out_kernel(FftParams p) {
     const int logP = p.logP, pmask = (1 << logP) - 1, N1 = p.N1, N2 = p.N2;
     const int NP = N2 << logP;
     const float scale = 1.0f / ((float)N1 * (float)N2);
-    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + 2 * NP;
+    float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + kRowBufs * NP;
     stage_in(buf0, NP, [&](int i) {
         const int j = (tile << logP) + (i & pmask);
         const bool ok = j < p.np;
@@ -984,7 +1093,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_out_kernel(FftParams p) {
     });
     fill_twiddles(tw, N2);
     __syncthreads();
-    const float2 *z = lds_fft(buf0, buf1, tw, N2, p.log2, logP, true);
+    const float2 *z = lds_fft1(buf0, buf1, tw, N2, p.log2, logP, true);
     for (int i = threadIdx.x; i < NP; i += kFftThreads) {
         const int t2 = i >> logP;
         const int j = (tile << logP) + (i & pmask);
@@ -1015,18 +1124,6 @@ constexpr int kFftTwoLevelMaxLogN = 16;
 // Pairs per workgroup: LDS of about kFftBudget complex values (several
 // workgroups per CU), at most 64 pairs, no more than the pairs there are; a
 // single pair when even that exceeds the budget (the largest transforms).
-#ifndef HYENA_FFT_BUDGET
-#define HYENA_FFT_BUDGET 4096
-#endif
-constexpr int kFftBudget = HYENA_FFT_BUDGET;
-#ifndef HYENA_FFT_COLS_BUDGET
-#define HYENA_FFT_COLS_BUDGET HYENA_FFT_BUDGET
-#endif
-constexpr int kFftColsBudget = HYENA_FFT_COLS_BUDGET;  // the column kernel's
-#ifndef HYENA_FFT_BWD_BUDGET
-#define HYENA_FFT_BWD_BUDGET HYENA_FFT_BUDGET
-#endif
-constexpr int kFftBwdBudget = HYENA_FFT_BWD_BUDGET;  // the backward column kernels'
 int pick_pairs(int M, int buffers, int64_t pairs, int budget = kFftBudget) {
     int P = 64;
     while (P > 1 && (int64_t)buffers * M * P > budget) P >>= 1;
@@ -1076,14 +1173,19 @@ int fft_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, i
     const int64_t G = D / group_size;
     const int64_t pairs = D / 2 > (G + 1) / 2 ? D / 2 : (G + 1) / 2;
     const int Mr = pl->three ? pl->N3 : pl->N2;  // transform length of the row (and output) kernels
-    pl->P_rows = pick_pairs(Mr, 2, pairs);
-    pl->P_mid = pick_pairs(pl->N2, 2, pairs);
+    pl->P_rows = pick_pairs(Mr, kRowBufs, pairs);
+    pl->P_mid = pick_pairs(pl->N2, kRowBufs, pairs);
     pl->P_cols = pick_pairs(pl->N1, 4, pairs, kFftColsBudget);
-    pl->lds_rows = (2 * Mr * pl->P_rows + 2 * Mr) * (int)sizeof(float2);
-    pl->lds_mid = (2 * pl->N2 * pl->P_mid + 2 * pl->N2) * (int)sizeof(float2);
+    pl->lds_rows = (kRowBufs * Mr * pl->P_rows + 2 * Mr) * (int)sizeof(float2);
+    pl->lds_mid = (kRowBufs * pl->N2 * pl->P_mid + 2 * pl->N2) * (int)sizeof(float2);
     pl->lds_cols = (4 * pl->N1 * pl->P_cols + 3 * pl->N1) * (int)sizeof(float2);
-    pl->P_col1 = pick_pairs(pl->N1, 2, pairs);
-    pl->lds_col1 = (2 * pl->N1 * pl->P_col1 + 2 * pl->N1) * (int)sizeof(float2);
+    pl->P_col1 = pick_pairs(pl->N1, kRowBufs, pairs);
+    pl->lds_col1 = (kRowBufs * pl->N1 * pl->P_col1 + 2 * pl->N1) * (int)sizeof(float2);
+    // an in-place stage holds M P / kFftThreads values per thread
+    if (kFftInPlace && ((int64_t)Mr * pl->P_rows > kFftIpVals * kFftThreads ||
+                        (int64_t)pl->N2 * pl->P_mid > kFftIpVals * kFftThreads ||
+                        (int64_t)pl->N1 * pl->P_col1 > kFftIpVals * kFftThreads))
+        return HYENA_ERR_UNSUPPORTED;
     if (pl->lds_rows > kFftMaxLdsBytes || pl->lds_cols > kFftMaxLdsBytes || pl->lds_mid > kFftMaxLdsBytes ||
         pl->lds_col1 > kFftMaxLdsBytes)
         return HYENA_ERR_UNSUPPORTED;
@@ -1108,8 +1210,9 @@ int fft_bwd_plan(int64_t B, int64_t D, int64_t group_size, FftPlan *pl) {
     // even group sizes: the single-column form (4 N1 P values of LDS), else the paired one (8 N1 P)
     pl->bwd_col1 = group_size % 2 == 0;
     if (pl->bwd_col1) {
-        pl->P_bwd = pick_pairs(pl->N1, 4, pairs, kFftBwdBudget);
-        pl->lds_bwd = (4 * pl->N1 * pl->P_bwd + 2 * pl->N1) * (int)sizeof(float2);
+        pl->P_bwd = pick_pairs(pl->N1, 2 * kRowBufs, pairs, kFftBwdBudget);
+        pl->lds_bwd = (2 * kRowBufs * pl->N1 * pl->P_bwd + 2 * pl->N1) * (int)sizeof(float2);
+        if (kFftInPlace && (int64_t)2 * pl->N1 * pl->P_bwd > kFftIpVals * kFftThreads) return HYENA_ERR_UNSUPPORTED;
     } else {
         pl->P_bwd = pick_pairs(pl->N1, 8, pairs, kFftBwdBudget);
         pl->lds_bwd = (8 * pl->N1 * pl->P_bwd + 3 * pl->N1) * (int)sizeof(float2);

@@ -569,6 +569,19 @@ __global__ __launch_bounds__(kFftThreads) void fft_col1_kernel(FftParams p) {
     // work-area row of (f2, t1 = 0): column position as in the paired form
     const int64_t col0 = ((int64_t)b * M + (int64_t)(f2 & (p.N3 - 1)) * p.N2 + (f2 >> p.log3)) * N1;
     float2 *bufA = lds, *bufB = lds + NP, *tw = lds + kRowBufs * NP, *wt = tw + N1;
+    // P divides the thread count, so a thread always has the same pair and
+    // its filter spectrum row is fixed; its spectrum values (value u of the
+    // thread: i = tid + u kFftThreads, NP <= kFftIpVals kFftThreads) are
+    // loaded before the transform, to hide their latency behind it
+    const int my_j = (tile << logP) + (threadIdx.x & pmask);
+    const int jc = min(my_j, p.np - 1);
+    const float2 *hrow = p.hs + (size_t)f2 * N1 * p.Gp + (2 * jc) / p.group_size;
+    float2 hh[kFftIpVals];
+#pragma unroll
+    for (int u = 0; u < kFftIpVals; ++u) {
+        const int i = threadIdx.x + u * kFftThreads;
+        if (i < NP) hh[u] = hrow[(size_t)(i >> logP) * p.Gp];
+    }
     stage_in(bufA, NP, [&](int i) {
         const int j = (tile << logP) + (i & pmask);
         const bool ok = j < p.np;
@@ -583,24 +596,10 @@ __global__ __launch_bounds__(kFftThreads) void fft_col1_kernel(FftParams p) {
     // the product goes to the other buffer, or (in place) over S: each
     // thread rewrites only the values it reads
     float2 *Z = kFftInPlace ? S : (S == bufA ? bufB : bufA);
-    // P divides the thread count, so a thread always has the same pair and
-    // its filter spectrum row is fixed
-    const int my_j = (tile << logP) + (threadIdx.x & pmask);
-    const int jc = min(my_j, p.np - 1);
-    const float2 *hrow = p.hs + (size_t)f2 * N1 * p.Gp + (2 * jc) / p.group_size;
-    for (int base = 0; base < NP; base += kBatch * kFftThreads) {
-        float2 hh[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int f1 = min(base + u * kFftThreads + (int)threadIdx.x, NP - 1) >> logP;
-            hh[u] = hrow[(size_t)f1 * p.Gp];
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int i = base + u * kFftThreads + (int)threadIdx.x;
-            if (i >= NP) continue;
-            Z[i] = my_j < p.np ? cmul(hh[u], S[i]) : make_float2(0.0f, 0.0f);
-        }
+    for (int u = 0; u < kFftIpVals; ++u) {
+        const int i = threadIdx.x + u * kFftThreads;
+        if (i < NP) Z[i] = my_j < p.np ? cmul(hh[u], S[i]) : make_float2(0.0f, 0.0f);
     }
     __syncthreads();
     const float2 *U = lds_fft1(Z, S, tw, N1, p.log1, logP, true);
@@ -774,6 +773,20 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) 
     // work-area row of (f2, t1 = 0): column position as in the paired form
     const int64_t col0 = ((int64_t)b * M + (int64_t)(f2 & (p.N3 - 1)) * p.N2 + (f2 >> p.log3)) * N1;
     float2 *bufA = lds, *bufB = lds + NS, *tw = lds + kRowBufs * NS, *wt = tw + N1;
+    // P divides the thread count: a thread keeps one pair (and filter row);
+    // its spectrum values (value u: (f1, pair) index i = tid + u kFftThreads
+    // < N1 P) are loaded before the transform
+    const int my_pp = threadIdx.x & pmask;
+    const int my_j = (tile << logP) + my_pp;
+    const int jc = min(my_j, p.np - 1);
+    const float2 *hrow = p.hs + (size_t)f2 * N1 * p.Gp + (2 * jc) / p.group_size;
+    const int NP = N1 << logP;
+    float2 hh[kFftIpVals / 2];
+#pragma unroll
+    for (int u = 0; u < kFftIpVals / 2; ++u) {
+        const int i = threadIdx.x + u * kFftThreads;
+        if (i < NP) hh[u] = hrow[(size_t)(i >> logP) * p.Gp];
+    }
     stage_in(bufA, NS, [&](int i) {
         const int src = (i >> logP) & 1;
         const int j = (tile << logP) + (i & pmask);
@@ -812,28 +825,14 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) 
         }
     }
     if constexpr (kFftInPlace) __syncthreads();
-    // P divides the thread count: a thread keeps one pair (and filter row)
-    const int my_pp = threadIdx.x & pmask;
-    const int my_j = (tile << logP) + my_pp;
-    const int jc = min(my_j, p.np - 1);
-    const float2 *hrow = p.hs + (size_t)f2 * N1 * p.Gp + (2 * jc) / p.group_size;
-    const int NP = N1 << logP;
-    for (int base = 0; base < NP; base += kBatch * kFftThreads) {
-        float2 hh[kBatch];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int f1 = min(base + u * kFftThreads + (int)threadIdx.x, NP - 1) >> logP;
-            hh[u] = hrow[(size_t)f1 * p.Gp];
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int i = base + u * kFftThreads + (int)threadIdx.x;
-            if (i >= NP) continue;
-            const int ix = ((i >> logP) << lS) | my_pp;
-            const bool ok = my_j < p.np;
-            Z[ix] = ok ? cmul(hh[u], S[ix]) : make_float2(0.0f, 0.0f);
-            Z[ix + sdz] = ok ? cmul(cconj(hh[u]), S[ix + sdz]) : make_float2(0.0f, 0.0f);
-        }
+    for (int u = 0; u < kFftIpVals / 2; ++u) {
+        const int i = threadIdx.x + u * kFftThreads;
+        if (i >= NP) continue;
+        const int ix = ((i >> logP) << lS) | my_pp;
+        const bool ok = my_j < p.np;
+        Z[ix] = ok ? cmul(hh[u], S[ix]) : make_float2(0.0f, 0.0f);
+        Z[ix + sdz] = ok ? cmul(cconj(hh[u]), S[ix + sdz]) : make_float2(0.0f, 0.0f);
     }
     __syncthreads();
     const float2 *U = lds_fft1(Z, S, tw, N1, p.log1, lS, true);
@@ -938,8 +937,36 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
     const __bf16 x = (__bf16)a, y = (__bf16)b;
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
+// The gates of one output (raw bits: a bf16 pair in .x, or an fp32 pair),
+// loaded before the last transform so that their latency is hidden behind it.
+template <bool F32, int MODE> struct Gates {
+    static constexpr int NG = MODE == 2 ? 0 : (MODE == 1 ? 2 : 1);   // gates per output
+    static constexpr int NW = NG * (F32 ? 2 : 1);                    // 4-byte words
+    uint32_t w[NW > 0 ? NW : 1];
+};
 template <bool F32, int MODE>
-__device__ inline void store_out(const FftParams &p, int b, int64_t t, int j, float z0, float z1) {
+__device__ inline void load_gates(const FftParams &p, int b, int64_t t, int j, Gates<F32, MODE> &r) {
+    if constexpr (MODE != 2) {
+        const size_t o = ((size_t)b * (size_t)p.L + (size_t)t) * (size_t)p.D + 2 * (size_t)j;
+        const void *ga = MODE == 0 ? p.q : p.v;
+        if constexpr (F32) {
+            const uint2 a = *(const uint2 *)((const float *)ga + o);
+            r.w[0] = a.x;
+            r.w[1] = a.y;
+            if constexpr (MODE == 1) {
+                const uint2 c = *(const uint2 *)((const float *)p.k + o);
+                r.w[2] = c.x;
+                r.w[3] = c.y;
+            }
+        } else {
+            r.w[0] = *(const uint32_t *)((const uint16_t *)ga + o);
+            if constexpr (MODE == 1) r.w[1] = *(const uint32_t *)((const uint16_t *)p.k + o);
+        }
+    }
+}
+template <bool F32, int MODE>
+__device__ inline void store_out(const FftParams &p, int b, int64_t t, int j, float z0, float z1,
+                                 const Gates<F32, MODE> &g) {
     if constexpr (MODE == 2) {
         float *dh = (float *)p.y;
         dh[(size_t)(2 * j) * (size_t)p.l_h + (size_t)t] = z0;
@@ -947,23 +974,16 @@ __device__ inline void store_out(const FftParams &p, int b, int64_t t, int j, fl
         return;
     }
     const size_t o = ((size_t)b * (size_t)p.L + (size_t)t) * (size_t)p.D + 2 * (size_t)j;
-    const void *ga = MODE == 0 ? p.q : p.v;
     if constexpr (F32) {
-        const float2 g = *(const float2 *)((const float *)ga + o);
-        *(float2 *)((float *)p.y + o) = make_float2(g.x * z0, g.y * z1);
-        if constexpr (MODE == 1) {
-            const float2 g2 = *(const float2 *)((const float *)p.k + o);
-            *(float2 *)((float *)p.y2 + o) = make_float2(g2.x * z0, g2.y * z1);
-        }
+        *(float2 *)((float *)p.y + o) = make_float2(__uint_as_float(g.w[0]) * z0, __uint_as_float(g.w[1]) * z1);
+        if constexpr (MODE == 1)
+            *(float2 *)((float *)p.y2 + o) = make_float2(__uint_as_float(g.w[2]) * z0, __uint_as_float(g.w[3]) * z1);
     } else {
-        const uint32_t g = *(const uint32_t *)((const uint16_t *)ga + o);
         *(uint32_t *)((uint16_t *)p.y + o) =
-            pack_bf16x2(__uint_as_float(g << 16) * z0, __uint_as_float(g & 0xffff0000u) * z1);
-        if constexpr (MODE == 1) {
-            const uint32_t g2 = *(const uint32_t *)((const uint16_t *)p.k + o);
+            pack_bf16x2(__uint_as_float(g.w[0] << 16) * z0, __uint_as_float(g.w[0] & 0xffff0000u) * z1);
+        if constexpr (MODE == 1)
             *(uint32_t *)((uint16_t *)p.y2 + o) =
-                pack_bf16x2(__uint_as_float(g2 << 16) * z0, __uint_as_float(g2 & 0xffff0000u) * z1);
-        }
+                pack_bf16x2(__uint_as_float(g.w[1] << 16) * z0, __uint_as_float(g.w[1] & 0xffff0000u) * z1);
     }
 }
 
@@ -1054,6 +1074,15 @@ __global__ __launch_bounds__(kFftThreads) void fft_out3_kernel(FftParams p) {
     const int64_t M = (int64_t)N2 * N3;
     const float scale = 1.0f / ((float)N1 * (float)M);
     float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + kRowBufs * NP;
+    // output u of this thread: i = tid + u kFftThreads (NP <= kFftIpVals kFftThreads)
+    auto out_row = [&](int i) -> int64_t { return t1 + (int64_t)N1 * (t2 + (int64_t)N2 * (i >> logP)); };
+    Gates<F32, MODE> gv[kFftIpVals];
+#pragma unroll
+    for (int u = 0; u < kFftIpVals; ++u) {
+        const int i = threadIdx.x + u * kFftThreads;
+        const int j = (tile << logP) + (i & pmask);
+        if (i < NP && j < p.np && out_row(i) < p.L) load_gates<F32, MODE>(p, b, out_row(i), j, gv[u]);
+    }
     stage_in(buf0, NP, [&](int i) {
         const int j = (tile << logP) + (i & pmask);
         const bool ok = j < p.np;
@@ -1063,12 +1092,12 @@ __global__ __launch_bounds__(kFftThreads) void fft_out3_kernel(FftParams p) {
     fill_twiddles(tw, N3);
     __syncthreads();
     const float2 *z = lds_fft1(buf0, buf1, tw, N3, p.log3, logP, true);
-    for (int i = threadIdx.x; i < NP; i += kFftThreads) {
-        const int t3 = i >> logP;
+#pragma unroll
+    for (int u = 0; u < kFftIpVals; ++u) {
+        const int i = threadIdx.x + u * kFftThreads;
         const int j = (tile << logP) + (i & pmask);
-        const int64_t t = t1 + (int64_t)N1 * (t2 + (int64_t)N2 * t3);
-        if (j >= p.np || t >= p.L) continue;
-        store_out<F32, MODE>(p, b, t, j, z[i].x * scale, z[i].y * scale);
+        if (i < NP && j < p.np && out_row(i) < p.L)
+            store_out<F32, MODE>(p, b, out_row(i), j, z[i].x * scale, z[i].y * scale, gv[u]);
     }
 }
 
@@ -1085,6 +1114,15 @@ __global__ __launch_bounds__(kFftThreads) void fft_out_kernel(FftParams p) {
     const int NP = N2 << logP;
     const float scale = 1.0f / ((float)N1 * (float)N2);
     float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + kRowBufs * NP;
+    // output u of this thread: i = tid + u kFftThreads (NP <= kFftIpVals kFftThreads)
+    Gates<F32, MODE> gv[kFftIpVals];
+#pragma unroll
+    for (int u = 0; u < kFftIpVals; ++u) {
+        const int i = threadIdx.x + u * kFftThreads;
+        const int j = (tile << logP) + (i & pmask);
+        const int64_t t = t1 + (int64_t)N1 * (i >> logP);
+        if (i < NP && j < p.np && t < p.L) load_gates<F32, MODE>(p, b, t, j, gv[u]);
+    }
     stage_in(buf0, NP, [&](int i) {
         const int j = (tile << logP) + (i & pmask);
         const bool ok = j < p.np;
@@ -1094,12 +1132,12 @@ __global__ __launch_bounds__(kFftThreads) void fft_out_kernel(FftParams p) {
     fill_twiddles(tw, N2);
     __syncthreads();
     const float2 *z = lds_fft1(buf0, buf1, tw, N2, p.log2, logP, true);
-    for (int i = threadIdx.x; i < NP; i += kFftThreads) {
-        const int t2 = i >> logP;
+#pragma unroll
+    for (int u = 0; u < kFftIpVals; ++u) {
+        const int i = threadIdx.x + u * kFftThreads;
         const int j = (tile << logP) + (i & pmask);
-        const int64_t t = t1 + (int64_t)N1 * t2;
-        if (j >= p.np || t >= p.L) continue;
-        store_out<F32, MODE>(p, b, t, j, z[i].x * scale, z[i].y * scale);
+        const int64_t t = t1 + (int64_t)N1 * (i >> logP);
+        if (i < NP && j < p.np && t < p.L) store_out<F32, MODE>(p, b, t, j, z[i].x * scale, z[i].y * scale, gv[u]);
     }
 }
 
@@ -1181,6 +1219,11 @@ int fft_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, i
     pl->lds_cols = (4 * pl->N1 * pl->P_cols + 3 * pl->N1) * (int)sizeof(float2);
     pl->P_col1 = pick_pairs(pl->N1, kRowBufs, pairs);
     pl->lds_col1 = (kRowBufs * pl->N1 * pl->P_col1 + 2 * pl->N1) * (int)sizeof(float2);
+    // the output kernels hold the gates of Mr P / kFftThreads outputs per
+    // thread, the single-column kernel N1 P / kFftThreads filter-spectrum values
+    if ((int64_t)Mr * pl->P_rows > kFftIpVals * kFftThreads ||
+        (int64_t)pl->N1 * pl->P_col1 > kFftIpVals * kFftThreads)
+        return HYENA_ERR_UNSUPPORTED;
     // an in-place stage holds M P / kFftThreads values per thread
     if (kFftInPlace && ((int64_t)Mr * pl->P_rows > kFftIpVals * kFftThreads ||
                         (int64_t)pl->N2 * pl->P_mid > kFftIpVals * kFftThreads ||
@@ -1212,7 +1255,7 @@ int fft_bwd_plan(int64_t B, int64_t D, int64_t group_size, FftPlan *pl) {
     if (pl->bwd_col1) {
         pl->P_bwd = pick_pairs(pl->N1, 2 * kRowBufs, pairs, kFftBwdBudget);
         pl->lds_bwd = (2 * kRowBufs * pl->N1 * pl->P_bwd + 2 * pl->N1) * (int)sizeof(float2);
-        if (kFftInPlace && (int64_t)2 * pl->N1 * pl->P_bwd > kFftIpVals * kFftThreads) return HYENA_ERR_UNSUPPORTED;
+        if ((int64_t)2 * pl->N1 * pl->P_bwd > kFftIpVals * kFftThreads) return HYENA_ERR_UNSUPPORTED;
     } else {
         pl->P_bwd = pick_pairs(pl->N1, 8, pairs, kFftBwdBudget);
         pl->lds_bwd = (8 * pl->N1 * pl->P_bwd + 3 * pl->N1) * (int)sizeof(float2);

@@ -401,18 +401,39 @@ __device__ inline float2 load_pair(const FftParams &p, int b, int64_t t, int j) 
             c = __uint_as_float(kk & 0xffff0000u) * __uint_as_float(vv & 0xffff0000u);
         }
     } else {
-        const int g0 = 2 * jc, g1 = min(2 * jc + 1, p.G - 1);
-        const size_t o0 = (size_t)g0 * p.l_h + tc, o1 = (size_t)g1 * p.l_h + tc;
-        if constexpr (F32) {
-            a = ((const float *)p.h)[o0];
-            c = ((const float *)p.h)[o1];
-        } else {
-            a = __uint_as_float((uint32_t)((const uint16_t *)p.h)[o0] << 16);
-            c = __uint_as_float((uint32_t)((const uint16_t *)p.h)[o1] << 16);
-        }
-        if (2 * jc + 1 >= p.G) c = 0.0f;
+        // the filters transposed to fp32 [taps][Gp] (fft_filter_transpose_kernel)
+        const float2 hh = *(const float2 *)((const float *)p.h + (size_t)tc * p.Gp + 2 * (size_t)jc);
+        a = hh.x;
+        c = hh.y;
     }
     return ok ? make_float2(a, c) : make_float2(0.0f, 0.0f);
+}
+
+// The filters h [G][l_h] (dtype) -> hT [taps][Gp] fp32, filter Gp - 1 zero
+// when G is odd: the filter pass of the row kernel then reads a pair of
+// filters at one tap as 8 contiguous bytes, as it reads channel pairs of the
+// sequence.  64 x 64 tiles through LDS; reads run along taps, writes along
+// filters.
+template <bool F32>
+__global__ __launch_bounds__(256) void fft_filter_transpose_kernel(const void *h, float *hT, int G, int Gp, int l_h,
+                                                                  int taps) {
+    __shared__ float tile[64][65];
+    const int t0 = blockIdx.x * 64, g0 = blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int r = ty; r < 64; r += 4) {
+        const int g = g0 + r, t = t0 + tx;
+        float v = 0.0f;
+        if (g < G && t < taps) {
+            const size_t o = (size_t)g * l_h + t;
+            v = F32 ? ((const float *)h)[o] : __uint_as_float((uint32_t)((const uint16_t *)h)[o] << 16);
+        }
+        tile[r][tx] = v;
+    }
+    __syncthreads();
+    for (int r = ty; r < 64; r += 4) {
+        const int t = t0 + r, g = g0 + tx;
+        if (t < taps && g < Gp) hT[(size_t)t * Gp + g] = tile[tx][r];
+    }
 }
 
 // Kernel 1: forward transform along t2 for one t1, then the twiddle.
@@ -1276,6 +1297,18 @@ int fft_bwd_plan(int64_t B, int64_t D, int64_t group_size, FftPlan *pl) {
     return HYENA_OK;
 }
 
+// The filters to [taps][Gp] fp32 at hT (taps Gp 4 <= 8 N Gp bytes: the
+// spectra's region).
+int transpose_filters(const void *h, bool f32, int64_t G, int64_t Gp, int64_t l_h, int64_t taps, void *hT,
+                      hipStream_t s) {
+    const int64_t gx = (taps + 63) / 64, gy = (Gp + 63) / 64;
+    if (gx > INT32_MAX || gy > 65535) return HYENA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(f32 ? fft_filter_transpose_kernel<true> : fft_filter_transpose_kernel<false>,
+                       dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, h, (float *)hT, (int)G, (int)Gp, (int)l_h,
+                       (int)taps);
+    return hipGetLastError() == hipSuccess ? HYENA_OK : HYENA_ERR_LAUNCH;
+}
+
 // One launch: pair tile P, grid (batch rows x units x tiles), dynamic LDS.
 int fft_launch(const void *fn, FftParams q_, int P, int64_t units, int64_t nb, int lds, hipStream_t s) {
     q_.logP = 0;
@@ -1367,7 +1400,9 @@ int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v, const vo
         FftParams ph = p;
         ph.L = l_h < L ? l_h : L;
         ph.np = p.Gp / 2;
-        st = launch(rows_flt, ph, pl.P_rows, row_units, 1, pl.lds_rows);
+        st = transpose_filters(h, f32, p.G, p.Gp, l_h, ph.L, p.hs, s);
+        ph.h = p.hs;  // [taps][Gp] fp32, in the spectra's place until the column pass writes them
+        if (st == HYENA_OK) st = launch(rows_flt, ph, pl.P_rows, row_units, 1, pl.lds_rows);
         if (st == HYENA_OK && pl.three)
             st = launch((const void *)fft_mid_kernel<false>, ph, pl.P_mid, mid_units, 1, pl.lds_mid);
         if (st == HYENA_OK) st = launch((const void *)fft_cols_kernel<0>, ph, pl.P_cols, cols, 1, pl.lds_cols);
@@ -1499,7 +1534,9 @@ int hyena_conv_bwd_long(const void *q, const void *k, const void *v, const void 
         FftParams ph = p;
         ph.L = taps;
         ph.np = p.Gp / 2;
-        st = launch(rows_flt, ph, pl.P_rows, row_units, 1, pl.lds_rows);
+        st = transpose_filters(h, f32, p.G, p.Gp, l_h, taps, p.hs, s);
+        ph.h = p.hs;  // [taps][Gp] fp32, in the spectra's place until the column pass writes them
+        if (st == HYENA_OK) st = launch(rows_flt, ph, pl.P_rows, row_units, 1, pl.lds_rows);
         if (st == HYENA_OK && pl.three)
             st = launch((const void *)fft_mid_kernel<false>, ph, pl.P_mid, mid_units, 1, pl.lds_mid);
         if (st == HYENA_OK) st = launch((const void *)fft_cols_kernel<0>, ph, pl.P_cols, cols, 1, pl.lds_cols);

@@ -758,11 +758,11 @@ def long_filter_rates(w, stream, reps):
            "us": round(us, 1), "G_tok_ch_per_s": round(lw.elems / (us * 1e-6) / 1e9, 2),
            "moved_bytes_model": moved, "GBs_moved": round(moved / (us * 1e-6) / 1e9, 1),
            "frac_of_peak_moved": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-           "workspace_bytes": ws_n, "kernels": 5,
+           "workspace_bytes": ws_n, "kernels": 6,
            "us_spectra_kept": round(us_kept, 1), "kernels_spectra_kept": 3,
            "G_tok_ch_per_s_spectra_kept": round(lw.elems / (us_kept * 1e-6) / 1e9, 2),
            "backward": {"us": round(us_bwd, 1), "G_tok_ch_per_s": round(lw.elems / (us_bwd * 1e-6) / 1e9, 2),
-                        "workspace_bytes": ws_bwd, "kernels": 9,
+                        "workspace_bytes": ws_bwd, "kernels": 10,
                         "frac_of_peak_min_bytes": round(14 * lw.elems / (us_bwd * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
     del q, k, v, h, y, ws
     return res

@@ -738,8 +738,14 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_cols_kernel(FftParams p) 
             if ((self && col) || lo >= hi) continue;
             const int f2 = col ? fb : fa;
             const int f1m = (N1 - f1 - (f2 > 0 ? 1 : 0)) & (N1 - 1);
+            // the group's channels from a start rotated by f1 (see the
+            // single-column kernel: the lanes' rows would share a bank)
+            const int nch = hi - lo;
+            int kk = f1 % nch;
             float2 acc = make_float2(0.0f, 0.0f);
-            for (int ch = lo; ch < hi; ++ch) {
+            for (int k = 0; k < nch; ++k) {
+                const int ch = lo + kk;
+                kk = kk + 1 == nch ? 0 : kk + 1;
                 const int pp = (ch - c_lo) >> 1;
                 const int ix = (f1 << lS) | (col << logP) | pp;
                 const int im = (f1m << lS) | ((col ^ 1) << logP) | pp;
@@ -835,9 +841,15 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) 
             const int g = g0 + slot;
             const int lo = max(c_lo, g * p.group_size), hi = min(c_end, (g + 1) * p.group_size);
             if (lo >= hi) continue;
+            // the group's pairs, from a start rotated by f1: the lanes of a
+            // wave hold different f1 (rows of the tile 8 << lS bytes apart,
+            // one bank), and would otherwise read one pair at a time
+            const int p0 = (lo - c_lo) >> 1, npg = ((hi - c_lo) >> 1) - p0;
+            int kk = f1 % npg;
             float2 acc = make_float2(0.0f, 0.0f);
-            for (int pp = (lo - c_lo) >> 1; pp < (hi - c_lo) >> 1; ++pp) {
-                const int ix = (f1 << lS) | pp;
+            for (int k = 0; k < npg; ++k) {
+                const int ix = (f1 << lS) | (p0 + kk);
+                kk = kk + 1 == npg ? 0 : kk + 1;
                 const float2 pr = cmul(S[ix + sdz], cconj(S[ix]));
                 acc.x += pr.x;
                 acc.y += pr.y;

@@ -77,3 +77,16 @@ def test_backward_in_a_graph():
         q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, torch.bfloat16, seed=300 + r)
         return q, k, v, h, normal_activation((B, L, D), torch.bfloat16, "cpu", seed=400 + r)
     _replays(mk, lambda q, k, v, h, dy: hc.conv_bwd(q, k, v, h, dy, gs))
+
+
+@pytest.mark.parametrize("gs", [16, 3])
+def test_long_filter_backward_in_a_graph(gs):
+    """hyena_conv_bwd_long (its dh tail is zeroed by a kernel: l_h > L here)."""
+    log("graph long backward gs=%d" % gs)
+    B, L, D, l_h = 2, 700, 48, 900
+    ws = torch.empty(hc.bwd_long_workspace_bytes(B, L, D, gs, l_h), dtype=torch.uint8, device=DEV)
+
+    def mk(r):
+        q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, torch.bfloat16, seed=500 + r)
+        return q, k, v, h, normal_activation((B, L, D), torch.bfloat16, "cpu", seed=600 + r)
+    _replays(mk, lambda q, k, v, h, dy: hc.conv_bwd_long(q, k, v, h, dy, gs, workspace=ws))

@@ -1,11 +1,12 @@
 """Concurrent calls on distinct streams from several host threads.
 
 The library keeps no state between calls and allocates no device memory, so
-calls on distinct streams are independent (the header's contract).  Four
+calls on distinct streams are independent (the header's contract).  Five
 host threads, each with its own stream (default priority), repeatedly run
 a different entry point -- grouped forward, chunk-direction forward,
-long-filter forward, backward -- while the others run; the host calls
-overlap (ctypes releases the interpreter lock) and so can the kernels.
+long-filter forward, backward, long-filter backward -- while the others
+run; the host calls overlap (ctypes releases the interpreter lock) and so
+can the kernels.
 Every result must equal the same call made alone, bit for bit.
 """
 import threading
@@ -53,7 +54,17 @@ def _jobs():
         def run(s):
             res["g"] = hc.conv_bwd(q, k, v, h, dy, 16, stream=s)
         return run, res
-    return [grouped(), chunk_direction(), long_filter(), backward()]
+
+    def long_backward():
+        q, k, v, h = (t.to(DEV) for t in gaussian_inputs(1, 1500, 48, 3, 1500, torch.bfloat16, seed=6))
+        dy = normal_activation((1, 1500, 48), torch.bfloat16, DEV, seed=7)
+        ws = torch.empty(hc.bwd_long_workspace_bytes(1, 1500, 48, 3, 1500), dtype=torch.uint8, device=DEV)
+        res = {}
+
+        def run(s):
+            res["g"] = hc.conv_bwd_long(q, k, v, h, dy, 3, workspace=ws, stream=s)
+        return run, res
+    return [grouped(), chunk_direction(), long_filter(), backward(), long_backward()]
 
 
 def _snapshot(outs):
@@ -83,7 +94,7 @@ def test_concurrent_calls_on_distinct_streams():
             streams[i].synchronize()
         except Exception as e:  # reported by the main thread
             errors.append((i, repr(e)))
-    log("4 threads x 12 calls on 4 streams")
+    log("%d threads x 12 calls on %d streams" % (len(jobs), len(jobs)))
     threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(jobs))]
     for t in threads:
         t.start()

@@ -416,9 +416,9 @@ __device__ inline float2 load_pair(const FftParams &p, int b, int64_t t, int j) 
 // filters.
 template <bool F32>
 __global__ __launch_bounds__(256) void fft_filter_transpose_kernel(const void *h, float *hT, int G, int Gp, int l_h,
-                                                                  int taps) {
+                                                                  int taps, int n_tblk) {
     __shared__ float tile[64][65];
-    const int t0 = blockIdx.x * 64, g0 = blockIdx.y * 64;
+    const int t0 = (int)(blockIdx.x % n_tblk) * 64, g0 = (int)(blockIdx.x / n_tblk) * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     for (int r = ty; r < 64; r += 4) {
         const int g = g0 + r, t = t0 + tx;
@@ -1314,10 +1314,10 @@ int fft_bwd_plan(int64_t B, int64_t D, int64_t group_size, FftPlan *pl) {
 int transpose_filters(const void *h, bool f32, int64_t G, int64_t Gp, int64_t l_h, int64_t taps, void *hT,
                       hipStream_t s) {
     const int64_t gx = (taps + 63) / 64, gy = (Gp + 63) / 64;
-    if (gx > INT32_MAX || gy > 65535) return HYENA_ERR_UNSUPPORTED;
+    if (gx * gy > INT32_MAX) return HYENA_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(f32 ? fft_filter_transpose_kernel<true> : fft_filter_transpose_kernel<false>,
-                       dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s, h, (float *)hT, (int)G, (int)Gp, (int)l_h,
-                       (int)taps);
+                       dim3((unsigned)(gx * gy)), dim3(256), 0, s, h, (float *)hT, (int)G, (int)Gp, (int)l_h,
+                       (int)taps, (int)gx);
     return hipGetLastError() == hipSuccess ? HYENA_OK : HYENA_ERR_LAUNCH;
 }
 

@@ -472,8 +472,10 @@ __global__ __launch_bounds__(kFftThreads) void fft_rows_kernel(FftParams p) {
 // The two columns are interleaved in LDS -- element (t1, col, pair) at
 // (2 t1 + col) P + pair -- so one transform of 2P sequences covers both.  A
 // self-paired column (f2 = 0 or N2/2) is staged twice and stored once.
-// LDS (dynamic): two buffers of 2 N1 P values, the N1 inner twiddles and,
-// per column, the N1 inter-step twiddles W_N^(-t1 f2).
+// In place (one buffer) the products go to registers first: each reads a
+// partner value another thread may overwrite.
+// LDS (dynamic): one (in place) or two buffers of 2 N1 P values, the N1
+// inner twiddles and, per column, the N1 inter-step twiddles W_N^(-t1 f2).
 template <int MODE>
 __global__ __launch_bounds__(kFftThreads) void fft_cols_kernel(FftParams p) {
     extern __shared__ float2 lds[];
@@ -491,7 +493,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_cols_kernel(FftParams p) {
     // work-area position of column f: (f mod N3) N2 + f / N3 (the identity
     // for the two-level split), so the middle passes work in place
     auto cpos = [&](int f) -> int64_t { return (int64_t)(f & (p.N3 - 1)) * p.N2 + (f >> p.log3); };
-    float2 *bufA = lds, *bufB = lds + NP2, *tw = lds + 2 * NP2;
+    float2 *bufA = lds, *bufB = lds + NP2, *tw = lds + kRowBufs * NP2;
     float2 *wt[2] = {tw + N1, tw + 2 * N1};
     stage_in(bufA, NP2, [&](int i) {
         const int col = (i >> logP) & 1;
@@ -508,8 +510,8 @@ __global__ __launch_bounds__(kFftThreads) void fft_cols_kernel(FftParams p) {
         }
     }
     __syncthreads();
-    float2 *S = lds_fft(bufA, bufB, tw, N1, p.log1, lP2, false);
-    float2 *Z = S == bufA ? bufB : bufA;
+    float2 *S = lds_fft1(bufA, bufB, tw, N1, p.log1, lP2, false);
+    float2 *Z = kFftInPlace ? S : (S == bufA ? bufB : bufA);
     // 2P divides the thread count, so a thread always has the same column
     // and channel pair: its filter spectra rows are fixed
     const int my_col = (threadIdx.x >> logP) & 1, my_pp = threadIdx.x & pmask;
@@ -518,7 +520,12 @@ __global__ __launch_bounds__(kFftThreads) void fft_cols_kernel(FftParams p) {
     const int jc = min(my_j, p.np - 1);
     const float2 *hrow0 = p.hs + (size_t)my_f2 * N1 * p.Gp + (2 * jc) / p.group_size;
     const float2 *hrow1 = p.hs + (size_t)my_f2 * N1 * p.Gp + (2 * jc + 1) / p.group_size;
-    for (int base = 0; base < NP2; base += kBatch * kFftThreads) {
+    // (in place) this thread's products, value u at i = tid + u kFftThreads
+    float2 zr[kFftInPlace && MODE == 1 ? kFftIpVals : 1];
+#pragma unroll
+    for (int ub = 0; ub < kFftIpVals; ub += kBatch) {
+        const int base = ub * kFftThreads;
+        if (base >= NP2) break;
         float2 h0[kBatch], h1[kBatch];
         if constexpr (MODE == 1) {
             // filter spectra of this batch, all loads in flight together
@@ -552,13 +559,25 @@ __global__ __launch_bounds__(kFftThreads) void fft_cols_kernel(FftParams p) {
                 const float2 sm = make_float2(0.5f * (h0[u].x + h1[u].x), 0.5f * (h0[u].y + h1[u].y));
                 const float2 df = make_float2(0.5f * (h0[u].x - h1[u].x), 0.5f * (h0[u].y - h1[u].y));
                 const float2 pu = cmul(sm, a), pv = cmul(df, m);
-                Z[i] = j < p.np ? make_float2(pu.x + pv.x, pu.y + pv.y) : make_float2(0.0f, 0.0f);
+                const float2 zv = j < p.np ? make_float2(pu.x + pv.x, pu.y + pv.y) : make_float2(0.0f, 0.0f);
+                if constexpr (kFftInPlace)
+                    zr[ub + u] = zv;
+                else
+                    Z[i] = zv;
             }
         }
     }
     if constexpr (MODE == 1) {
         __syncthreads();
-        const float2 *U = lds_fft(Z, S, tw, N1, p.log1, lP2, true);
+        if constexpr (kFftInPlace) {
+#pragma unroll
+            for (int u = 0; u < kFftIpVals; ++u) {
+                const int i = threadIdx.x + u * kFftThreads;
+                if (i < NP2) Z[i] = zr[u];
+            }
+            __syncthreads();
+        }
+        const float2 *U = lds_fft1(Z, S, tw, N1, p.log1, lP2, true);
         for (int i = threadIdx.x; i < NP2; i += kFftThreads) {
             const int t1 = i >> lP2, col = (i >> logP) & 1;
             const int j = (tile << logP) + (i & pmask);
@@ -671,7 +690,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_cols_kernel(FftParams p) 
     auto wpos = [&](int src, int col, int t1, int j) -> int64_t {
         return src * area + (((int64_t)b * M + cpos(col ? fb : fa)) * N1 + t1) * p.np + j;
     };
-    float2 *bufA = lds, *bufB = lds + NS, *tw = lds + 2 * NS;
+    float2 *bufA = lds, *bufB = lds + NS, *tw = lds + kRowBufs * NS;
     float2 *wt[2] = {tw + N1, tw + 2 * N1};
     stage_in(bufA, NS, [&](int i) {
         const int col = (i >> logP) & 1, src = (i >> lP2) & 1;
@@ -686,42 +705,8 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_cols_kernel(FftParams p) 
         wt[col][t1] = cconj(twiddle(((int64_t)t1 * (col ? fb : fa)) & (N - 1), N));
     }
     __syncthreads();
-    float2 *S = lds_fft(bufA, bufB, tw, N1, p.log1, lS, false);
-    float2 *Z = S == bufA ? bufB : bufA;
-    // 2P divides the thread count: a thread keeps one column and pair
-    const int my_col = (threadIdx.x >> logP) & 1, my_pp = threadIdx.x & pmask;
-    const int my_f2 = my_col ? fb : fa;
-    const int my_j = (tile << logP) + my_pp;
-    const int jc = min(my_j, p.np - 1);
-    const float2 *hrow0 = p.hs + (size_t)my_f2 * N1 * p.Gp + (2 * jc) / p.group_size;
-    const float2 *hrow1 = p.hs + (size_t)my_f2 * N1 * p.Gp + (2 * jc + 1) / p.group_size;
-    const int NP2 = N1 << lP2;
-    for (int base = 0; base < NP2; base += kBatch * kFftThreads) {
-        float2 h0[kBatch], h1[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int f1 = min(base + u * kFftThreads + (int)threadIdx.x, NP2 - 1) >> lP2;
-            h0[u] = hrow0[(size_t)f1 * p.Gp];
-            h1[u] = hrow1[(size_t)f1 * p.Gp];
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int i = base + u * kFftThreads + (int)threadIdx.x;
-            if (i >= NP2) continue;
-            const int f1 = i >> lP2;
-            const int f1m = (N1 - f1 - (my_f2 > 0 ? 1 : 0)) & (N1 - 1);
-            const int ix = (f1 << lS) | (my_col << logP) | my_pp;
-            const int im = (f1m << lS) | ((my_col ^ 1) << logP) | my_pp;
-            const float2 sm = make_float2(0.5f * (h0[u].x + h1[u].x), 0.5f * (h0[u].y + h1[u].y));
-            const float2 df = make_float2(0.5f * (h0[u].x - h1[u].x), 0.5f * (h0[u].y - h1[u].y));
-            const float2 ax = S[ix], mx = cconj(S[im]), az = S[ix + sdz], mz = cconj(S[im + sdz]);
-            const float2 zx0 = cmul(sm, ax), zx1 = cmul(df, mx);
-            const float2 zd0 = cmul(cconj(sm), az), zd1 = cmul(cconj(df), mz);
-            const bool ok = my_j < p.np;
-            Z[ix] = ok ? make_float2(zx0.x + zx1.x, zx0.y + zx1.y) : make_float2(0.0f, 0.0f);
-            Z[ix + sdz] = ok ? make_float2(zd0.x + zd1.x, zd0.y + zd1.y) : make_float2(0.0f, 0.0f);
-        }
-    }
+    float2 *S = lds_fft1(bufA, bufB, tw, N1, p.log1, lS, false);
+    float2 *Z = kFftInPlace ? S : (S == bufA ? bufB : bufA);
     if (p.part != nullptr) {
         // one item per (f1, column, group slot): the sum over the group's
         // channels in this tile (a self-paired column once)
@@ -761,8 +746,67 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_cols_kernel(FftParams p) 
                 make_float2(0.25f * acc.x, 0.25f * acc.y);
         }
     }
+    // 2P divides the thread count: a thread keeps one column and pair
+    const int my_col = (threadIdx.x >> logP) & 1, my_pp = threadIdx.x & pmask;
+    const int my_f2 = my_col ? fb : fa;
+    const int my_j = (tile << logP) + my_pp;
+    const int jc = min(my_j, p.np - 1);
+    const float2 *hrow0 = p.hs + (size_t)my_f2 * N1 * p.Gp + (2 * jc) / p.group_size;
+    const float2 *hrow1 = p.hs + (size_t)my_f2 * N1 * p.Gp + (2 * jc + 1) / p.group_size;
+    const int NP2 = N1 << lP2;
+    // (in place) this thread's products, value u at i = tid + u kFftThreads,
+    // written over the spectra after a barrier: they read partner values
+    constexpr int UZ = kFftIpVals / 2;  // NP2 = NS / 2 <= UZ kFftThreads
+    float2 zxr[kFftInPlace ? UZ : 1], zdr[kFftInPlace ? UZ : 1];
+#pragma unroll
+    for (int ub = 0; ub < UZ; ub += kBatch) {
+        const int base = ub * kFftThreads;
+        if (base >= NP2) break;
+        float2 h0[kBatch], h1[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int f1 = min(base + u * kFftThreads + (int)threadIdx.x, NP2 - 1) >> lP2;
+            h0[u] = hrow0[(size_t)f1 * p.Gp];
+            h1[u] = hrow1[(size_t)f1 * p.Gp];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int i = base + u * kFftThreads + (int)threadIdx.x;
+            if (i >= NP2) continue;
+            const int f1 = i >> lP2;
+            const int f1m = (N1 - f1 - (my_f2 > 0 ? 1 : 0)) & (N1 - 1);
+            const int ix = (f1 << lS) | (my_col << logP) | my_pp;
+            const int im = (f1m << lS) | ((my_col ^ 1) << logP) | my_pp;
+            const float2 sm = make_float2(0.5f * (h0[u].x + h1[u].x), 0.5f * (h0[u].y + h1[u].y));
+            const float2 df = make_float2(0.5f * (h0[u].x - h1[u].x), 0.5f * (h0[u].y - h1[u].y));
+            const float2 ax = S[ix], mx = cconj(S[im]), az = S[ix + sdz], mz = cconj(S[im + sdz]);
+            const float2 zx0 = cmul(sm, ax), zx1 = cmul(df, mx);
+            const float2 zd0 = cmul(cconj(sm), az), zd1 = cmul(cconj(df), mz);
+            const bool ok = my_j < p.np;
+            const float2 zx = ok ? make_float2(zx0.x + zx1.x, zx0.y + zx1.y) : make_float2(0.0f, 0.0f);
+            const float2 zd = ok ? make_float2(zd0.x + zd1.x, zd0.y + zd1.y) : make_float2(0.0f, 0.0f);
+            if constexpr (kFftInPlace) {
+                zxr[ub + u] = zx;
+                zdr[ub + u] = zd;
+            } else {
+                Z[ix] = zx;
+                Z[ix + sdz] = zd;
+            }
+        }
+    }
     __syncthreads();
-    const float2 *U = lds_fft(Z, S, tw, N1, p.log1, lS, true);
+    if constexpr (kFftInPlace) {
+#pragma unroll
+        for (int u = 0; u < UZ; ++u) {
+            const int i = threadIdx.x + u * kFftThreads;
+            if (i >= NP2) continue;
+            const int ix = ((i >> lP2) << lS) | (my_col << logP) | my_pp;
+            Z[ix] = zxr[u];
+            Z[ix + sdz] = zdr[u];
+        }
+        __syncthreads();
+    }
+    const float2 *U = lds_fft1(Z, S, tw, N1, p.log1, lS, true);
     for (int i = threadIdx.x; i < NS; i += kFftThreads) {
         const int t1 = i >> lS, col = (i >> logP) & 1, src = (i >> lP2) & 1;
         const int j = (tile << logP) + (i & pmask);
@@ -1246,16 +1290,17 @@ int fft_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, i
     const int Mr = pl->three ? pl->N3 : pl->N2;  // transform length of the row (and output) kernels
     pl->P_rows = pick_pairs(Mr, kRowBufs, pairs);
     pl->P_mid = pick_pairs(pl->N2, kRowBufs, pairs);
-    pl->P_cols = pick_pairs(pl->N1, 4, pairs, kFftColsBudget);
+    pl->P_cols = pick_pairs(pl->N1, 2 * kRowBufs, pairs, kFftColsBudget);
     pl->lds_rows = (kRowBufs * Mr * pl->P_rows + 2 * Mr) * (int)sizeof(float2);
     pl->lds_mid = (kRowBufs * pl->N2 * pl->P_mid + 2 * pl->N2) * (int)sizeof(float2);
-    pl->lds_cols = (4 * pl->N1 * pl->P_cols + 3 * pl->N1) * (int)sizeof(float2);
+    pl->lds_cols = (2 * kRowBufs * pl->N1 * pl->P_cols + 3 * pl->N1) * (int)sizeof(float2);
     pl->P_col1 = pick_pairs(pl->N1, kRowBufs, pairs);
     pl->lds_col1 = (kRowBufs * pl->N1 * pl->P_col1 + 2 * pl->N1) * (int)sizeof(float2);
     // the output kernels hold the gates of Mr P / kFftThreads outputs per
     // thread, the single-column kernel N1 P / kFftThreads filter-spectrum values
     if ((int64_t)Mr * pl->P_rows > kFftIpVals * kFftThreads ||
-        (int64_t)pl->N1 * pl->P_col1 > kFftIpVals * kFftThreads)
+        (int64_t)pl->N1 * pl->P_col1 > kFftIpVals * kFftThreads ||
+        (int64_t)2 * pl->N1 * pl->P_cols > kFftIpVals * kFftThreads)
         return HYENA_ERR_UNSUPPORTED;
     // an in-place stage holds M P / kFftThreads values per thread
     if (kFftInPlace && ((int64_t)Mr * pl->P_rows > kFftIpVals * kFftThreads ||
@@ -1290,8 +1335,9 @@ int fft_bwd_plan(int64_t B, int64_t D, int64_t group_size, FftPlan *pl) {
         pl->lds_bwd = (2 * kRowBufs * pl->N1 * pl->P_bwd + 2 * pl->N1) * (int)sizeof(float2);
         if ((int64_t)2 * pl->N1 * pl->P_bwd > kFftIpVals * kFftThreads) return HYENA_ERR_UNSUPPORTED;
     } else {
-        pl->P_bwd = pick_pairs(pl->N1, 8, pairs, kFftBwdBudget);
-        pl->lds_bwd = (8 * pl->N1 * pl->P_bwd + 3 * pl->N1) * (int)sizeof(float2);
+        pl->P_bwd = pick_pairs(pl->N1, 4 * kRowBufs, pairs, kFftBwdBudget);
+        pl->lds_bwd = (4 * kRowBufs * pl->N1 * pl->P_bwd + 3 * pl->N1) * (int)sizeof(float2);
+        if ((int64_t)4 * pl->N1 * pl->P_bwd > kFftIpVals * kFftThreads) return HYENA_ERR_UNSUPPORTED;
     }
     pl->P_dh = pick_pairs(pl->N1, 8, Gp / 2, kFftColsBudget);
     pl->lds_dh = (8 * pl->N1 * pl->P_dh + 3 * pl->N1) * (int)sizeof(float2);

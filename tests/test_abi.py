@@ -367,15 +367,15 @@ def test_long_filter_backward_workspace_size():
     # filter gradient's partial sums (T column tiles of P channel pairs, S
     # group slots per tile).  P: the largest power of two <= 64 with c N1 P <=
     # 4096 complex values of LDS, no larger than needed for D / 2 pairs; c = 2
-    # for even group sizes (single columns, transformed in place), 8 otherwise
-    # (column pairs, two buffers).
+    # for even group sizes (single columns), 4 otherwise (column pairs); both
+    # transformed in place.
     def expect(B, L, D, gs, l_h):
         n = 1 << max(2, (L + min(l_h, L) - 2).bit_length())
         log_n = n.bit_length() - 1
         log1 = (log_n + 2) // 3 if log_n > 16 else (log_n + 1) // 2
         n1 = 1 << log1
         P = 64
-        while P > 1 and (2 if gs % 2 == 0 else 8) * n1 * P > 4096:
+        while P > 1 and (2 if gs % 2 == 0 else 4) * n1 * P > 4096:
             P //= 2
         while P > 1 and P // 2 >= D // 2:
             P //= 2

@@ -420,16 +420,21 @@ __global__ __launch_bounds__(256) void fft_filter_transpose_kernel(const void *h
     __shared__ float tile[64][65];
     const int t0 = (int)(blockIdx.x % n_tblk) * 64, g0 = (int)(blockIdx.x / n_tblk) * 64;
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int r = ty; r < 64; r += 4) {
-        const int g = g0 + r, t = t0 + tx;
-        float v = 0.0f;
+    // all 16 loads of a thread in flight together
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int g = g0 + ty + 4 * u, t = t0 + tx;
+        v[u] = 0.0f;
         if (g < G && t < taps) {
             const size_t o = (size_t)g * l_h + t;
-            v = F32 ? ((const float *)h)[o] : __uint_as_float((uint32_t)((const uint16_t *)h)[o] << 16);
+            v[u] = F32 ? ((const float *)h)[o] : __uint_as_float((uint32_t)((const uint16_t *)h)[o] << 16);
         }
-        tile[r][tx] = v;
     }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) tile[ty + 4 * u][tx] = v[u];
     __syncthreads();
+#pragma unroll
     for (int r = ty; r < 64; r += 4) {
         const int t = t0 + r, g = g0 + tx;
         if (t < taps && g < Gp) hT[(size_t)t * Gp + g] = tile[tx][r];

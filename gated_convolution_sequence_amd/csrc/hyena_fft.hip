@@ -30,7 +30,8 @@
 // whose inverse transform is z0 + i z1 (H0, H1: the two channels' filter
 // spectra; equal filters make the second term vanish).  The filter spectra
 // come from the same two kernels run on the filters (pairs of filters,
-// separated the same way), once per call.
+// separated the same way; the filters first transposed to [taps][G'] fp32),
+// once per call or kept across calls.
 // Inner transforms are Stockham (self-sorting) in LDS, radix 16 (two radix-4
 // levels in registers) per pass, with twiddles tabulated per workgroup;
 // arithmetic is fp32 for both I/O types.
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(256) void fft_filter_transpose_kernel(const void *h
 }
 
 // Kernel 1: forward transform along t2 for one t1, then the twiddle.
-// LDS (dynamic): two buffers of N2 P values, the N2 inner twiddles and the
+// LDS (dynamic): one buffer (in place) of N2 P values, the N2 inner twiddles and the
 // N2 inter-step twiddles W_N^(t1 f2) of this t1.
 template <bool F32, int SRC>
 __global__ __launch_bounds__(kFftThreads) void fft_rows_kernel(FftParams p) {
@@ -599,7 +600,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_cols_kernel(FftParams p) {
 // W_N^(-t1 f2), store in place.  Half the LDS of the paired form per pair,
 // so tiles are twice as wide (whole 128-byte work-area segments) and each
 // point reads one filter spectrum value.
-// LDS (dynamic): two buffers of N1 P values, the N1 inner twiddles and the N1
+// LDS (dynamic): one buffer (in place) of N1 P values, the N1 inner twiddles and the N1
 // inter-step twiddles.
 __global__ __launch_bounds__(kFftThreads) void fft_col1_kernel(FftParams p) {
     extern __shared__ float2 lds[];
@@ -673,7 +674,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_col1_kernel(FftParams p) {
 //     channel 2j + 1: (a_dz - m_dz) conj(a_x - m_x) / 4,
 // summed over the tile's channels of each group into
 // part[b][f2][f1][tile][slot], slot = group - first group of the tile.
-// LDS (dynamic): two buffers of 4 N1 P values -- element (t1, src, col,
+// LDS (dynamic): one buffer (in place) of 4 N1 P values -- element (t1, src, col,
 // pair) at ((2 t1 + src) 2 + col) P + pair -- the N1 inner twiddles and,
 // per column, the N1 inter-step twiddles W_N^(-t1 f2).
 __global__ __launch_bounds__(kFftThreads) void fft_bwd_cols_kernel(FftParams p) {
@@ -830,7 +831,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_cols_kernel(FftParams p) 
 // P_dz conj(P_x) is the sum of the two channels' correlations (the cross
 // terms are imaginary); the filter-gradient column kernel keeps only the
 // Hermitian part of each group's spectrum, which is that real part.
-// LDS (dynamic): two buffers of 2 N1 P values -- element (t1, src, pair) at
+// LDS (dynamic): one buffer (in place) of 2 N1 P values -- element (t1, src, pair) at
 // (2 t1 + src) P + pair -- the N1 inner twiddles and the N1 inter-step
 // twiddles W_N^(-t1 f2).
 __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) {
@@ -1079,7 +1080,7 @@ __device__ inline void store_out(const FftParams &p, int b, int64_t t, int j, fl
 // after which column c (position (c mod N3) N2 + c / N3) is what the column
 // kernel expects.  The inverse runs mid (inverse, twiddle conj W_M^(t2 f3))
 // and out3 (inverse N3-point FFT over f3, scale, gate, store).
-// LDS (dynamic) of either: two buffers of N3 P (N2 P) values, the inner
+// LDS (dynamic) of either: one buffer (in place) of N3 P (N2 P) values, the inner
 // twiddles and the N3 (N2) inter-step twiddles.
 template <bool F32, int SRC>
 __global__ __launch_bounds__(kFftThreads) void fft_rows3_kernel(FftParams p) {
@@ -1184,7 +1185,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_out3_kernel(FftParams p) {
 }
 
 // Kernel 3: inverse transform along f2 for one t1, scale, gate, store.
-// LDS (dynamic): two buffers of N2 P values and the N2 inner twiddles.
+// LDS (dynamic): one buffer (in place) of N2 P values and the N2 inner twiddles.
 template <bool F32, int MODE>
 __global__ __launch_bounds__(kFftThreads) void fft_out_kernel(FftParams p) {
     extern __shared__ float2 lds[];

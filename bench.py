@@ -751,6 +751,13 @@ def long_filter_rates(w, stream, reps):
     e1.record(stream)
     torch.cuda.synchronize()
     us_bwd = e0.elapsed_time(e1) * 1e3 / reps
+    # the same with the filter spectra the previous calls left in the workspace
+    e0.record(stream)
+    for _ in range(reps):
+        hc.conv_bwd_long(q, k, v, h, dy, lw.group_size, workspace=ws_b, stream=stream, reuse_spectra=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us_bwd_kept = e0.elapsed_time(e1) * 1e3 / reps
     ws_bwd = ws_b.numel()
     del dy, ws_b
     moved = 40 * lw.elems
@@ -763,6 +770,7 @@ def long_filter_rates(w, stream, reps):
            "G_tok_ch_per_s_spectra_kept": round(lw.elems / (us_kept * 1e-6) / 1e9, 2),
            "backward": {"us": round(us_bwd, 1), "G_tok_ch_per_s": round(lw.elems / (us_bwd * 1e-6) / 1e9, 2),
                         "workspace_bytes": ws_bwd, "kernels": 10,
+                        "us_spectra_kept": round(us_bwd_kept, 1), "kernels_spectra_kept": 7,
                         "frac_of_peak_min_bytes": round(14 * lw.elems / (us_bwd * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
     del q, k, v, h, y, ws
     return res

@@ -35,7 +35,8 @@ EXPORTS = ("hyena_conv_fwd", "hyena_conv_fwd_f32", "hyena_conv_fwd_ex", "hyena_c
            "hyena_conv_bwd", "hyena_conv_bwd_workspace", "hyena_conv_fwd_long",
            "hyena_conv_fwd_long_workspace", "hyena_conv_plan", "hyena_conv_strerror",
            "hyena_conv_block_len", "hyena_conv_bwd_noalloc", "hyena_conv_scratch_bytes",
-           "hyena_conv_fwd_long_ex", "hyena_conv_bwd_long", "hyena_conv_bwd_long_workspace")
+           "hyena_conv_fwd_long_ex", "hyena_conv_bwd_long", "hyena_conv_bwd_long_workspace",
+           "hyena_conv_bwd_long_ex")
 
 
 class HyenaError(RuntimeError):
@@ -91,6 +92,9 @@ def lib() -> ctypes.CDLL:
         L.hyena_conv_bwd_long.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp,
                                           ctypes.c_int, vp, i64, vp]
         L.hyena_conv_bwd_long.restype = ctypes.c_int
+        L.hyena_conv_bwd_long_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, vp, vp, vp, vp,
+                                             ctypes.c_int, vp, i64, ctypes.c_int, vp]
+        L.hyena_conv_bwd_long_ex.restype = ctypes.c_int
         L.hyena_conv_bwd_long_workspace.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int,
                                                     ctypes.POINTER(i64)]
         L.hyena_conv_bwd_long_workspace.restype = ctypes.c_int
@@ -320,11 +324,14 @@ def bwd_long_workspace_bytes(B: int, L: int, D: int, group_size: int, l_h: int,
 def conv_bwd_long(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Tensor,
                   dy: torch.Tensor, group_size: int, need_dq: bool = True, need_dkv: bool = True,
                   need_dh: bool = True, workspace: Optional[torch.Tensor] = None,
-                  stream: Optional[torch.cuda.Stream] = None):
+                  stream: Optional[torch.cuda.Stream] = None, reuse_spectra: bool = False):
     """Gradients (dq, dk, dv, dh) of the long-filter forward (FFT), any l_h.
 
     Same tensors and results as conv_bwd; parts not requested are None.
     ``workspace`` (uint8, on q's device) is allocated here if not given.
+    ``reuse_spectra``: the workspace already holds h's spectra from an
+    earlier conv_fwd_long or conv_bwd_long call on it with the same h and
+    sizes (hyena_conv_bwd_long_ex).
     """
     dt, dev = q.dtype, q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("h", h), ("dy", dy)):
@@ -342,6 +349,8 @@ def conv_bwd_long(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Te
     dv = torch.empty_like(q) if need_dkv else None
     dh = torch.empty((G, l_h), dtype=torch.float32, device=dev) if need_dh else None
     ws_n = bwd_long_workspace_bytes(B, L, D, group_size, l_h, code)
+    if reuse_spectra and workspace is None:
+        raise ValueError("reuse_spectra needs the workspace of an earlier call")
     if workspace is None:
         workspace = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
     elif workspace.device != dev or workspace.numel() * workspace.element_size() < ws_n:
@@ -351,14 +360,14 @@ def conv_bwd_long(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Te
     ptr = lambda t: t.data_ptr() if t is not None else None
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(), dy.data_ptr(), B, L, D,
             group_size, l_h, ptr(dq), ptr(dk), ptr(dv), ptr(dh), code, workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), stream.cuda_stream)
+            workspace.numel() * workspace.element_size(), int(bool(reuse_spectra)), stream.cuda_stream)
     if dev.index == torch.cuda.current_device():
-        st = lib().hyena_conv_bwd_long(*args)
+        st = lib().hyena_conv_bwd_long_ex(*args)
     else:
         with torch.cuda.device(dev):
-            st = lib().hyena_conv_bwd_long(*args)
+            st = lib().hyena_conv_bwd_long_ex(*args)
     if st != 0:
-        raise HyenaError(st, "hyena_conv_bwd_long")
+        raise HyenaError(st, "hyena_conv_bwd_long_ex")
     return dq, dk, dv, dh
 
 
@@ -388,13 +397,18 @@ class HyenaConvLong(torch.autograd.Function):
     """Autograd wrapper of the long-filter (FFT) path: y = HyenaConvLong.apply(q, k, v, h, group_size).
 
     Any filter length; the filter gradient comes back in h's dtype (fp32 sums).
+    The forward runs in a workspace of the backward's size, kept until the
+    backward, which then reuses the filter spectra the forward left in it.
     """
 
     @staticmethod
     def forward(ctx, q, k, v, h, group_size):
         ctx.save_for_backward(q, k, v, h)
         ctx.group_size = group_size
-        return conv_fwd_long(q, k, v, h, group_size)
+        B, L, D = q.shape
+        n = bwd_long_workspace_bytes(B, L, D, group_size, h.shape[1], _dtype_code(q.dtype))
+        ctx.workspace = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+        return conv_fwd_long(q, k, v, h, group_size, workspace=ctx.workspace)
 
     @staticmethod
     def backward(ctx, dy):
@@ -402,6 +416,8 @@ class HyenaConvLong(torch.autograd.Function):
         need = ctx.needs_input_grad
         dq, dk, dv, dh = conv_bwd_long(q, k, v, h, dy.contiguous(), ctx.group_size,
                                        need_dq=need[0], need_dkv=need[1] or need[2],
-                                       need_dh=need[3])
+                                       need_dh=need[3], workspace=ctx.workspace,
+                                       reuse_spectra=True)
+        ctx.workspace = None
         return (dq, dk if need[1] else None, dv if need[2] else None,
                 dh.to(h.dtype) if dh is not None else None, None)

@@ -1506,14 +1506,16 @@ int hyena_conv_bwd_long_workspace(int64_t B, int64_t L, int64_t D, int64_t group
     return HYENA_OK;
 }
 
-int hyena_conv_bwd_long(const void *q, const void *k, const void *v, const void *h, const void *dy, int64_t B,
-                        int64_t L, int64_t D, int64_t group_size, int64_t l_h, void *dq, void *dk, void *dv,
-                        float *dh, int dtype, void *workspace, int64_t workspace_bytes, void *stream) {
+int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const void *h, const void *dy, int64_t B,
+                           int64_t L, int64_t D, int64_t group_size, int64_t l_h, void *dq, void *dk, void *dv,
+                           float *dh, int dtype, void *workspace, int64_t workspace_bytes, int reuse_spectra,
+                           void *stream) {
     FftPlan pl;
     int st = fft_plan(B, L, D, group_size, l_h, dtype, &pl);
     if (st == HYENA_OK) st = fft_bwd_plan(B, D, group_size, &pl);
     if (st != HYENA_OK) return st;
-    if (!q || !k || !v || !h || !dy) return HYENA_ERR_NULL;
+    if (reuse_spectra != 0 && reuse_spectra != 1) return HYENA_ERR_SHAPE;
+    if (!q || !k || !v || (!h && !reuse_spectra) || !dy) return HYENA_ERR_NULL;
     if ((dk == nullptr) != (dv == nullptr)) return HYENA_ERR_NULL;
     const size_t eb = dtype == HYENA_DTYPE_F32 ? 4 : 2;
     uintptr_t mis = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)dy | (uintptr_t)workspace;
@@ -1524,7 +1526,7 @@ int hyena_conv_bwd_long(const void *q, const void *k, const void *v, const void 
     const int64_t G = D / group_size;
     const bool empty = B == 0 || L == 0 || D == 0;
     const size_t nbytes = (size_t)B * (size_t)L * (size_t)D * eb;
-    const size_t hbytes = (size_t)G * (size_t)l_h * eb;
+    const size_t hbytes = h ? (size_t)G * (size_t)l_h * eb : 0;
     const size_t dhbytes = (size_t)G * (size_t)l_h * sizeof(float);
     const size_t wbytes = empty ? 0 : (size_t)pl.bwd_ws_bytes;
     // every output and the workspace are disjoint from every input and from each other
@@ -1593,8 +1595,9 @@ int hyena_conv_bwd_long(const void *q, const void *k, const void *v, const void 
         return (const void *)fft_out_kernel<true, 2>;
     };
 
-    // filter spectra (the first work area serves as the filter pass's)
-    {
+    // filter spectra (the first work area serves as the filter pass's), or
+    // kept in the workspace by an earlier call
+    if (!reuse_spectra) {
         FftParams ph = p;
         ph.L = taps;
         ph.np = p.Gp / 2;
@@ -1666,6 +1669,13 @@ int hyena_conv_bwd_long(const void *q, const void *k, const void *v, const void 
     if (st != HYENA_OK) return st;
     if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
     return HYENA_OK;
+}
+
+int hyena_conv_bwd_long(const void *q, const void *k, const void *v, const void *h, const void *dy, int64_t B,
+                        int64_t L, int64_t D, int64_t group_size, int64_t l_h, void *dq, void *dk, void *dv,
+                        float *dh, int dtype, void *workspace, int64_t workspace_bytes, void *stream) {
+    return hyena_conv_bwd_long_ex(q, k, v, h, dy, B, L, D, group_size, l_h, dq, dk, dv, dh, dtype, workspace,
+                                  workspace_bytes, 0, stream);
 }
 
 }  // extern "C"

@@ -252,6 +252,26 @@ int hyena_conv_bwd_long(const void *q, const void *k, const void *v,
                         void *dk, void *dv, float *dh, int dtype,
                         void *workspace, int64_t workspace_bytes, void *stream);
 
+/* hyena_conv_bwd_long with the filter spectra kept in the workspace.  The
+ * backward's workspace begins with the same 8 N G' bytes of filter spectra
+ * as the forward's (they depend on L, l_h, D, group_size, dtype and the
+ * filter, not on B): a hyena_conv_fwd_long_ex or hyena_conv_bwd_long(_ex)
+ * call on this stream with the same h and sizes, given this workspace (at
+ * least hyena_conv_bwd_long_workspace bytes, which covers the forward's),
+ * leaves them there.  reuse_spectra = 0: compute them from h, as
+ * hyena_conv_bwd_long does; 1: reuse them, h is not read (it may be NULL).
+ * The results have the same bits either way; with a workspace that does not
+ * hold them they are meaningless (nothing is checked on the device).  Any
+ * other reuse_spectra value returns HYENA_ERR_SHAPE.  (For training: one
+ * workspace kept from the forward to the backward saves the backward's
+ * filter pass.) */
+int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v,
+                           const void *h, const void *dy, int64_t B, int64_t L,
+                           int64_t D, int64_t group_size, int64_t l_h, void *dq,
+                           void *dk, void *dv, float *dh, int dtype,
+                           void *workspace, int64_t workspace_bytes,
+                           int reuse_spectra, void *stream);
+
 /* Bytes of workspace hyena_conv_bwd_long needs (written to *bytes_out):
  * 8 N (G' + B D + B T S) with N the transform length, G' the filter count
  * rounded up to even and T S the column tiles times the group slots per

@@ -391,3 +391,15 @@ def test_long_filter_backward_workspace_size():
     assert hc.bwd_long_workspace_bytes(0, 8192, 4096, 16, 8192) == 0
     with pytest.raises(hc.HyenaError):
         hc.bwd_long_workspace_bytes(1, 100, 7, 1, 10)  # odd D
+
+
+def test_long_filter_backward_spectra_flag_is_checked_on_host():
+    lib = hc.lib()
+    a = dict(q=P["q"], k=P["k"], v=P["v"], h=P["h"], dy=P["out"] + (128 << 20), dq=P["out"],
+             dk=P["out"] + (1 << 20), dv=P["out"] + (2 << 20), dh=P["out"] + (3 << 20), ws=P["out"] + (64 << 20))
+    call = lambda h, flag: lib.hyena_conv_bwd_long_ex(a["q"], a["k"], a["v"], h, a["dy"], 1, 128, 64, 16, 1000,
+                                                      a["dq"], a["dk"], a["dv"], a["dh"], hc.DTYPE_BF16, a["ws"],
+                                                      1 << 10, flag, None)
+    assert call(a["h"], 2) == -2 and call(a["h"], -1) == -2
+    assert call(None, 0) == -1          # the spectra are computed from h
+    assert call(None, 1) == -10         # h is not needed with kept spectra; the workspace still is

@@ -243,3 +243,33 @@ def test_autograd_wrapper_matches_the_entry_point():
     assert torch.equal(y, hc.conv_fwd_long(q, k, v, h, gs))
     for leaf, w in zip(leaves, want):
         assert torch.equal(leaf.grad, w)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("L,D,gs,l_h", [(1000, 64, 16, 1000), (3000, 48, 3, 700), (300, 8, 1, 5000)])
+def test_kept_filter_spectra_give_the_same_bits(dt, L, D, gs, l_h):
+    """hyena_conv_bwd_long_ex with reuse_spectra: a forward on the backward's
+    workspace leaves the filter spectra there; a backward that reuses them
+    (h passed as NULL, the rest of the workspace filled with NaN) equals one
+    that computes them, bit for bit."""
+    dtype = DTYPES[dt]
+    log("long bwd kept spectra %s L=%d D=%d gs=%d l_h=%d" % (dt, L, D, gs, l_h))
+    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(2, L, D, gs, l_h, dtype, seed=L + 3))
+    dy = _dy(2, L, D, dtype, seed=L + 4).to(DEV)
+    code = hc.DTYPE_BF16 if dtype == torch.bfloat16 else hc.DTYPE_F32
+    n = hc.bwd_long_workspace_bytes(2, L, D, gs, l_h, code)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    hc.conv_fwd_long(q, k, v, h, gs, workspace=ws)
+    N = 1 << max(2, (L + min(l_h, L) - 2).bit_length())
+    G = D // gs
+    spectra = 8 * N * (G + (G & 1))
+    ws[spectra:].view(torch.float32).fill_(float("nan"))
+    outs = [torch.empty_like(q) for _ in range(3)] + [torch.empty(G, l_h, device=DEV)]
+    st = hc.lib().hyena_conv_bwd_long_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), None, dy.data_ptr(), 2, L, D, gs,
+                                         l_h, *[o.data_ptr() for o in outs], code, ws.data_ptr(), n, 1,
+                                         torch.cuda.current_stream().cuda_stream)
+    assert st == 0, hc.strerror(st)
+    fresh = hc.conv_bwd_long(q, k, v, h, dy, gs)
+    torch.cuda.synchronize()
+    for a, b in zip(outs, fresh):
+        assert torch.equal(a, b)

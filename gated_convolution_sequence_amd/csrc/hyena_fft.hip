@@ -82,6 +82,7 @@ struct FftParams {
     float2 *part;        // backward: filter-gradient spectral partial sums, or null
     int32_t nb;          // backward: batch rows (a work area holds nb N np values)
     int32_t pb_log, pb_tiles, n_slots;  // backward: pairs per column tile (log2), those tiles, group slots per tile
+    int32_t part_slot_major;  // backward: partials as part[b][tile][slot][f2][f1] (1) or [b][tile][f2][f1][slot] (0)
     int64_t L;           // rows of the input sequence (the filter pass: taps)
     int32_t D;           // channels (row pitch) of q, k, v, y
     int32_t np;          // channel pairs of this pass
@@ -673,7 +674,8 @@ __global__ __launch_bounds__(kFftThreads) void fft_col1_kernel(FftParams p) {
 //     channel 2j: (a_dz + m_dz) conj(a_x + m_x) / 4,
 //     channel 2j + 1: (a_dz - m_dz) conj(a_x - m_x) / 4,
 // summed over the tile's channels of each group into
-// part[b][f2][f1][tile][slot], slot = group - first group of the tile.
+// part[b][tile][f2][f1][slot], slot = group - first group of the tile
+// (the single-column form: part[b][tile][slot][f2][f1]).
 // LDS (dynamic): one buffer (in place) of 4 N1 P values -- element (t1, src, col,
 // pair) at ((2 t1 + src) 2 + col) P + pair -- the N1 inner twiddles and,
 // per column, the N1 inter-step twiddles W_N^(-t1 f2).
@@ -721,6 +723,8 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_cols_kernel(FftParams p) 
         const int g0 = c_lo / p.group_size;
         const int n_items = N1 * 2 * p.n_slots;
         for (int it = threadIdx.x; it < n_items; it += kFftThreads) {
+            // slot fastest: a wave's lanes read different pairs and store
+            // consecutive values of part
             const int slot = it % p.n_slots;
             const int col = (it / p.n_slots) & 1;
             const int f1 = it / (2 * p.n_slots);
@@ -748,7 +752,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_cols_kernel(FftParams p) 
                 acc.x += pr.x;
                 acc.y += pr.y;
             }
-            p.part[((((int64_t)b * M + f2) * N1 + f1) * p.n_tiles + tile) * p.n_slots + slot] =
+            p.part[((((int64_t)b * p.n_tiles + tile) * M + f2) * N1 + f1) * p.n_slots + slot] =
                 make_float2(0.25f * acc.x, 0.25f * acc.y);
         }
     }
@@ -886,8 +890,10 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) 
         const int g0 = c_lo / p.group_size;
         const int n_items = N1 * p.n_slots;
         for (int it = threadIdx.x; it < n_items; it += kFftThreads) {
-            const int slot = it % p.n_slots;
-            const int f1 = it / p.n_slots;
+            // f1 fastest: a wave's stores are consecutive values of part
+            // (slot-major layout), and its lanes read at rotated pairs
+            const int f1 = it % N1;
+            const int slot = it / N1;
             const int g = g0 + slot;
             const int lo = max(c_lo, g * p.group_size), hi = min(c_end, (g + 1) * p.group_size);
             if (lo >= hi) continue;
@@ -904,7 +910,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) 
                 acc.x += pr.x;
                 acc.y += pr.y;
             }
-            p.part[((((int64_t)b * M + f2) * N1 + f1) * p.n_tiles + tile) * p.n_slots + slot] = acc;
+            p.part[((((int64_t)b * p.n_tiles + tile) * p.n_slots + slot) * M + f2) * N1 + f1] = acc;
         }
     }
     if constexpr (kFftInPlace) __syncthreads();
@@ -938,9 +944,8 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) 
 // the twiddle W_N^(-t1 f2), stored as a one-row work area of Gp/2 pairs.
 // p.np = Gp/2 here; pb_log, pb_tiles and n_slots describe the backward
 // column tiles that wrote `part`.
-// LDS (dynamic): the sums (4 N1 P values: element (f1, col, group) at
-// (2 f1 + col) 2P + group), two buffers of 2 N1 P values, the N1 inner
-// twiddles and 2 N1 inter-step twiddles.
+// LDS (dynamic): the sums (N1 (4P + 1) values), two buffers of 2 N1 P
+// values, the N1 inner twiddles and 2 N1 inter-step twiddles.
 __global__ __launch_bounds__(kFftThreads) void fft_dh_cols_kernel(FftParams p) {
     extern __shared__ float2 lds[];
     const int item = xcd_item();
@@ -955,26 +960,36 @@ __global__ __launch_bounds__(kFftThreads) void fft_dh_cols_kernel(FftParams p) {
     const int fa = c, fb = (M - c) & (M - 1);
     const bool self = fa == fb;
     auto cpos = [&](int f) -> int64_t { return (int64_t)(f & (p.N3 - 1)) * p.N2 + (f >> p.log3); };
-    float2 *sums = lds, *bufA = lds + (N1 << lS), *bufB = bufA + (N1 << lQ), *tw = bufB + (N1 << lQ);
+    // sums of (f1, col, group) at f1 SP + (col << lG) + group: rows padded
+    // by one value, so the f1-fastest writes below spread over the banks
+    const int SP = (2 << lG) + 1;
+    auto sidx = [&](int f1, int col, int g) -> int { return f1 * SP + (col << lG) + g; };
+    float2 *sums = lds, *bufA = lds + N1 * SP, *bufB = bufA + (N1 << lQ), *tw = bufB + (N1 << lQ);
     float2 *wt[2] = {tw + N1, tw + 2 * N1};
     const int cpt = 2 << p.pb_log;      // channels per backward column tile
     for (int e = threadIdx.x; e < (N1 << lS); e += kFftThreads) {
-        const int f1 = e >> lS, col = (e >> lG) & 1;
-        const int g = (tile << lG) + (e & ((1 << lG) - 1));
+        // f1 fastest: a wave reads consecutive partials (slot-major layout)
+        // or partials n_slots apart, whose lines the workgroup's other
+        // groups read as well
+        const int f1 = e % N1, r = e / N1;
+        const int col = r >> lG, gl = r & ((1 << lG) - 1);
+        const int g = (tile << lG) + gl;
         float2 acc = make_float2(0.0f, 0.0f);
         if (g < p.G) {
             const int f2 = (self || !col) ? fa : fb;
             const int t_lo = (g * p.group_size) / cpt, t_hi = ((g + 1) * p.group_size - 1) / cpt;
             for (int b = 0; b < p.nb; ++b) {
-                const float2 *row = p.part + (((int64_t)b * M + f2) * N1 + f1) * p.pb_tiles * p.n_slots;
                 for (int t = t_lo; t <= t_hi; ++t) {
-                    const float2 v = row[(int64_t)t * p.n_slots + (g - (t * cpt) / p.group_size)];
+                    const int slot = g - (t * cpt) / p.group_size;
+                    const int64_t bt = (int64_t)b * p.pb_tiles + t;
+                    const float2 v = p.part_slot_major ? p.part[((bt * p.n_slots + slot) * M + f2) * N1 + f1]
+                                                       : p.part[((bt * M + f2) * N1 + f1) * p.n_slots + slot];
                     acc.x += v.x;
                     acc.y += v.y;
                 }
             }
         }
-        sums[e] = acc;
+        sums[sidx(f1, col, gl)] = acc;
     }
     fill_twiddles(tw, N1);
     for (int i = threadIdx.x; i < 2 * N1; i += kFftThreads) {
@@ -987,8 +1002,8 @@ __global__ __launch_bounds__(kFftThreads) void fft_dh_cols_kernel(FftParams p) {
         const int f1 = e >> lQ, col = (e >> logP) & 1, m = e & gmask;
         const int f2 = col ? fb : fa;
         const int f1m = (N1 - f1 - (f2 > 0 ? 1 : 0)) & (N1 - 1);
-        const int ia = (((f1 << 1) | col) << lG) + 2 * m;
-        const int ib = (((f1m << 1) | (col ^ 1)) << lG) + 2 * m;
+        const int ia = sidx(f1, col, 2 * m);
+        const int ib = sidx(f1m, col ^ 1, 2 * m);
         const float2 s0 = sums[ia], s1 = sums[ia + 1], r0 = sums[ib], r1 = sums[ib + 1];
         // H = (S[f] + conj(S[-f]))/2 for both groups, then H0 + i H1
         const float2 h0 = make_float2(0.5f * (s0.x + r0.x), 0.5f * (s0.y - r0.y));
@@ -1346,7 +1361,7 @@ int fft_bwd_plan(int64_t B, int64_t D, int64_t group_size, FftPlan *pl) {
         if ((int64_t)4 * pl->N1 * pl->P_bwd > kFftIpVals * kFftThreads) return HYENA_ERR_UNSUPPORTED;
     }
     pl->P_dh = pick_pairs(pl->N1, 8, Gp / 2, kFftColsBudget);
-    pl->lds_dh = (8 * pl->N1 * pl->P_dh + 3 * pl->N1) * (int)sizeof(float2);
+    pl->lds_dh = (8 * pl->N1 * pl->P_dh + 4 * pl->N1) * (int)sizeof(float2);
     if (pl->lds_bwd > kFftMaxLdsBytes || pl->lds_dh > kFftMaxLdsBytes) return HYENA_ERR_UNSUPPORTED;
     pl->pb_tiles = (pairs + pl->P_bwd - 1) / pl->P_bwd;
     // groups a tile of 2P channels can touch
@@ -1654,6 +1669,7 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
         while ((1 << pd.pb_log) < pl.P_bwd) ++pd.pb_log;
         pd.pb_tiles = (int32_t)pl.pb_tiles;
         pd.n_slots = (int32_t)pl.n_slots;
+        pd.part_slot_major = pl.bwd_col1 ? 1 : 0;
         st = launch((const void *)fft_dh_cols_kernel, pd, pl.P_dh, cols, 1, pl.lds_dh);
         pd.L = taps;
         pd.y = dh;

@@ -168,3 +168,89 @@ def check_long(y, q, k, v, h, gs, dtype, what=""):
     bad = np.argwhere(err > bound)
     assert bad.size == 0, "%s: FFT bound broken at %s" % (what, bad[0])
     return float(np.max(err)) / scale if scale else 0.0
+
+
+# ---- long-filter backward (FFT) ---------------------------------------------
+# Bars, per channel d of group g, batch row b and transform length N, with e
+# and r as for the forward: dq: r |ref| + |dy| 3 e sqrt(N) ||h_g|| ||x_bd||;
+# dk (dv): r |ref| + |v| (|k|) 3 e sqrt(N) ||h_g|| ||dz_bd||; dh: 3 e sqrt(N)
+# sum_{b, d in g} ||dz_bd|| ||x_bd||; gates 1e-2 (bf16) / 1e-5 (fp32) of
+# max|ref| for dq, dk, dv and 1e-5 for dh (fp32 output).
+
+def run_long_bwd(q, k, v, h, dy, gs, pad=16, **need):
+    """hyena_conv_bwd_long into NaN-filled outputs with canaries around each."""
+    B, L, D = q.shape
+    G, l_h = h.shape
+    n = q.numel()
+    bigs, outs = [], []
+    for shape, dt, cnt in (((B, L, D), q.dtype, n), ((B, L, D), q.dtype, n), ((B, L, D), q.dtype, n),
+                           ((G, l_h), torch.float32, G * l_h)):
+        big = torch.full((cnt + 2 * pad,), 7.0, dtype=dt, device=DEV)
+        out = big[pad:pad + cnt].view(shape)
+        out.fill_(float("nan"))
+        bigs.append(big)
+        outs.append(out)
+    want = [need.get("dq", True), need.get("dkv", True), need.get("dkv", True), need.get("dh", True)]
+    code = hc.DTYPE_BF16 if q.dtype == torch.bfloat16 else hc.DTYPE_F32
+    ws_n = hc.bwd_long_workspace_bytes(B, L, D, gs, l_h, code)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xff)  # contents need not be initialised
+    ptr = lambda t, w: t.data_ptr() if w else None
+    st = hc.lib().hyena_conv_bwd_long(q.data_ptr(), k.data_ptr(), v.data_ptr(), h.data_ptr(), dy.data_ptr(),
+                                      B, L, D, gs, l_h, *[ptr(o, w) for o, w in zip(outs, want)], code,
+                                      ws.data_ptr(), ws_n, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, hc.strerror(st)
+    torch.cuda.synchronize()
+    for big, cnt in zip(bigs, (n, n, n, G * l_h)):
+        assert torch.all(big[:pad] == 7.0) and torch.all(big[pad + cnt:] == 7.0), "write outside an output"
+    return [o if w else None for o, w in zip(outs, want)]
+
+
+def check_long_bwd(got, q, k, v, h, dy, gs, dtype, what=""):
+    """Gates and norm-wise FFT bounds of all four gradients against the fp64 oracle."""
+    qn, kn, vn, hn, dyn = (to_np(t) for t in (q, k, v, h, dy))
+    ref = oracle.conv_bwd_ref(qn, kn, vn, hn, dyn, gs)
+    B, L, D = qn.shape
+    N = transform_len(L, hn.shape[1])
+    e = (math.log2(N) + 2) * 7 * 2.0 ** -24
+    r = 2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -24
+    x = kn * vn
+    dz = dyn * qn
+    xn = np.sqrt(np.sum(x * x, axis=1))                    # [B, D]
+    zn = np.sqrt(np.sum(dz * dz, axis=1))                  # [B, D]
+    hnorm = np.sqrt(np.sum(hn * hn, axis=1))[np.arange(D) // gs]  # [D]
+    k3 = 3 * e * math.sqrt(N)
+    rel = {}
+    bounds = {
+        "dq": np.abs(dyn) * (k3 * hnorm[None, None, :] * xn[:, None, :]),
+        "dk": np.abs(vn) * (k3 * hnorm[None, None, :] * zn[:, None, :]),
+        "dv": np.abs(kn) * (k3 * hnorm[None, None, :] * zn[:, None, :]),
+    }
+    for i, name in enumerate(("dq", "dk", "dv")):
+        if got[i] is None:
+            continue
+        y = to_np(got[i])
+        assert np.all(np.isfinite(y)), "%s %s" % (what, name)
+        err = np.abs(y - ref[i])
+        scale = float(np.max(np.abs(ref[i]))) if ref[i].size else 0.0
+        gate = (1e-2 if dtype == torch.bfloat16 else 1e-5) * scale
+        assert float(np.max(err, initial=0.0)) <= gate, "%s %s: max err %.3e > gate %.3e" % (
+            what, name, np.max(err), gate)
+        bad = np.argwhere(err > r * np.abs(ref[i]) + bounds[name] + TINY)
+        assert bad.size == 0, "%s %s: FFT bound broken at %s" % (what, name, bad[0])
+        rel[name] = float(np.max(err, initial=0.0)) / scale if scale else 0.0
+    if got[3] is not None:
+        dh = to_np(got[3])
+        assert np.all(np.isfinite(dh)), "%s dh" % what
+        err = np.abs(dh - ref[3])
+        scale = float(np.max(np.abs(ref[3]))) if ref[3].size else 0.0
+        assert float(np.max(err, initial=0.0)) <= 1e-5 * scale + TINY, "%s dh: max err %.3e > gate %.3e" % (
+            what, np.max(err), 1e-5 * scale)
+        G = D // gs
+        terms = (zn * xn).sum(axis=0).reshape(G, gs).sum(axis=1)  # [G]
+        bad = np.argwhere(err > k3 * terms[:, None] + TINY)
+        assert bad.size == 0, "%s dh: FFT bound broken at %s" % (what, bad[0])
+        taps = min(hn.shape[1], L)
+        assert np.all(dh[:, taps:] == 0.0), "%s dh: taps past the sequence must be zero" % what
+        rel["dh"] = float(np.max(err, initial=0.0)) / scale if scale else 0.0
+    return rel

@@ -13,8 +13,8 @@ import pytest
 import torch
 
 import gated_convolution_sequence_amd as hc
-from gpu_util import (DEV, bwd_refs, bwd_rows, check, check_bwd, check_long, log, ref_and_envelope, run,
-                      run_long, to_np)
+from gpu_util import (DEV, bwd_refs, bwd_rows, check, check_bwd, check_long, check_long_bwd, log, ref_and_envelope,
+                      run, run_long, run_long_bwd, to_np)
 from workloads import gaussian_inputs, normal_activation
 
 pytestmark = pytest.mark.gpu
@@ -72,10 +72,12 @@ def _draw(kind, seed):
             l_h = int(rng.integers(1, 129))
             # (the span column carries the prefix length P)
             cases.append((dt, B, L, D, gs, l_h, int(rng.integers(0, 200))))
-        else:  # long filters
+        else:  # long filters (forward; "long_backward": shorter sequences)
             gs = int(rng.choice([1, 2, 3, 4, 8, 16]))
             D = int(np.lcm(gs, 2) * rng.integers(1, max(2, 48 // np.lcm(gs, 2)) + 1))
             l_h = int(rng.integers(1, 5000))
+            if kind == "long_backward":
+                L = min(L, 2000)
             cases.append((dt, B, L, D, gs, l_h, 0))
     return cases
 
@@ -90,6 +92,7 @@ BACKWARD = _draw("backward", 303)
 LONG = _draw("long", 404)
 BACKWARD_OFF = _draw("backward_off_tile", 505)
 HALO = _draw("halo", 606)
+LONG_BWD = _draw("long_backward", 707)
 
 
 @pytest.mark.parametrize("dt,B,L,D,gs,l_h,span", GROUPED, ids=_ids(GROUPED))
@@ -167,3 +170,14 @@ def test_random_history_prefix(dt, B, L, D, gs, l_h, P):
     torch.cuda.synchronize()
     ref, env = ref_and_envelope(q, k, v, h, gs)
     check(to_np(out), ref[:, P:], env[:, P:], l_h, dtype, "random prefix")
+
+
+@pytest.mark.parametrize("dt,B,L,D,gs,l_h,span", LONG_BWD, ids=_ids(LONG_BWD))
+def test_random_long_filter_backward(dt, B, L, D, gs, l_h, span):
+    """hyena_conv_bwd_long: all four gradients against the fp64 backward oracle."""
+    log("random long backward %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B * 7919 + L * 31 + D + 3 * l_h)
+    dy = normal_activation((B, L, D), dtype, "cpu", seed=L + 2 * l_h + 1)
+    got = run_long_bwd(*(t.to(DEV) for t in (q, k, v, h, dy)), gs)
+    check_long_bwd(got, q, k, v, h, dy, gs, dtype, "random long backward")

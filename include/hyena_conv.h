@@ -1,6 +1,7 @@
 /*
  * hyena_conv.h -- C ABI of the MI355X (gfx950) Hyena-SE / Hyena-MR operator
- * (forward, and its backward further down)
+ * (forward, its backward, and both for filters of any length through the
+ * FFT, further down)
  *
  *     y[b,t,d] = q[b,t,d] * sum_{s=0}^{min(t, l_h-1)} h[d / group_size, s] * k[b,t-s,d] * v[b,t-s,d]
  *

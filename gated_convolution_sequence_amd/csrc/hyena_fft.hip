@@ -437,7 +437,8 @@ __global__ __launch_bounds__(256) void fft_filter_transpose_kernel(const void *h
     for (int u = 0; u < 16; ++u) tile[ty + 4 * u][tx] = v[u];
     __syncthreads();
 #pragma unroll
-    for (int r = ty; r < 64; r += 4) {
+    for (int u = 0; u < 16; ++u) {
+        const int r = ty + 4 * u;
         const int t = t0 + r, g = g0 + tx;
         if (t < taps && g < Gp) hT[(size_t)t * Gp + g] = tile[tx][r];
     }

@@ -371,20 +371,31 @@ def conv_bwd_long(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, h: torch.Te
     return dq, dk, dv, dh
 
 
+MAX_DIRECT_TAPS = 2 * BLOCK_LEN  # longest filter of the chunked kernels (128)
+
+
 class HyenaConv(torch.autograd.Function):
     """Autograd wrapper: y = HyenaConv.apply(q, k, v, h, group_size).
 
-    The filter gradient comes back in h's dtype (accumulated in fp32).
+    Filters of up to MAX_DIRECT_TAPS taps run on the chunked kernels; longer
+    ones on the FFT path (as HyenaConvLong).  The filter gradient comes back
+    in h's dtype (accumulated in fp32).
     """
 
     @staticmethod
     def forward(ctx, q, k, v, h, group_size):
+        if h.dim() == 2 and h.shape[1] > MAX_DIRECT_TAPS:
+            ctx.long = True
+            return HyenaConvLong.forward(ctx, q, k, v, h, group_size)
+        ctx.long = False
         ctx.save_for_backward(q, k, v, h)
         ctx.group_size = group_size
         return conv_fwd(q, k, v, h, group_size)
 
     @staticmethod
     def backward(ctx, dy):
+        if ctx.long:
+            return HyenaConvLong.backward(ctx, dy)
         q, k, v, h = ctx.saved_tensors
         need = ctx.needs_input_grad
         dq, dk, dv, dh = conv_bwd(q, k, v, h, dy.contiguous(), ctx.group_size,

@@ -192,3 +192,20 @@ def test_kept_filter_spectra_give_the_same_bits(dt, L, D, gs, l_h):
     torch.cuda.synchronize()
     for a, b in zip(outs, fresh):
         assert torch.equal(a, b)
+
+
+def test_hyena_conv_routes_long_filters_to_the_fft_path():
+    """HyenaConv with a filter over 128 taps runs the FFT path: the same
+    output and gradients, bit for bit, as HyenaConvLong."""
+    B, L, D, gs, l_h = 1, 600, 32, 4, 700
+    q, k, v, h = (t.to(DEV) for t in gaussian_inputs(B, L, D, gs, l_h, torch.bfloat16, seed=71))
+    dy = _dy(B, L, D, torch.bfloat16, seed=72).to(DEV)
+    grads = []
+    for fn in (hc.HyenaConv, hc.HyenaConvLong):
+        leaves = [t.clone().requires_grad_(True) for t in (q, k, v, h)]
+        y = fn.apply(*leaves, gs)
+        y.backward(dy)
+        grads.append([y.detach()] + [t.grad for t in leaves])
+    torch.cuda.synchronize()
+    for a, b in zip(*grads):
+        assert torch.equal(a, b)

@@ -349,6 +349,94 @@ __device__ __forceinline__ float2 *lds_fft1(float2 *buf0, float2 *buf1, const fl
 }
 constexpr int kRowBufs = kFftInPlace ? 1 : 2;  // LDS buffers of the row-like kernels
 
+// Register-fed transforms.  With a full tile (M P = 16 kFftThreads values)
+// and a radix-16 first stage, that stage's butterfly of thread tid takes
+// x[tid + r kFftThreads], r < 16: the same 16 values the thread would stage
+// to LDS, so they go from the global loads straight into the butterfly.  The
+// last stage's results stay in registers too: with R its radix, U = 16 / R
+// and Ns = M / R, value e = u R + r of the thread is output f = j + r Ns of
+// pair tid mod P, where j = (tid + u kFftThreads) >> logP.  Only the stages
+// in between pass through LDS.  The butterflies and twiddles are those of
+// lds_fft_ip; results can differ from it in the last bit, since the compiler
+// contracts the complex products into fused multiply-adds differently.
+// The 16 outputs of a thread are, for every R, the inputs of its first
+// stage in the next transform of the same tile (f = tid >> logP + (M / 16) r'
+// with r' = u + r U), so a forward and an inverse transform chain in
+// registers (fft_reg_perm).
+constexpr int kFftRegVals = 16;
+static_assert(kFftIpVals >= kFftRegVals, "the in-place stages hold a full tile per thread");
+
+// (32 to 256 points: the first stage and the last, nothing in between)
+__device__ inline bool fft_reg_ok(int logM, int logP) {
+    return logM >= 5 && logM <= 8 && (1 << (logM + logP)) == kFftRegVals * kFftThreads;
+}
+// log2 of the last stage's radix: radix-16 stages while more than four bits remain
+__host__ __device__ inline int fft_last_log(int logM) { return logM - 4 * ((logM - 1) / 4); }
+// output index of value e of this thread after the last stage of radix 2^lr
+__device__ inline int fft_reg_out(int e, int lr, int logM, int logP) {
+    return ((threadIdx.x + (e >> lr) * kFftThreads) >> logP) + (e & ((1 << lr) - 1)) * (1 << (logM - lr));
+}
+
+// First stage (radix 16, no twiddles) from v[r] = x[tid + r kFftThreads];
+// writes its outputs to x.  The caller synchronises afterwards.
+template <bool INV>
+__device__ __forceinline__ void fft_reg_first(float2 *x, int logP, float2 (&v)[kFftRegVals]) {
+    dft<16, INV>(v);
+    const int j = threadIdx.x >> logP, p = threadIdx.x & ((1 << logP) - 1);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[((16 * j + r) << logP) + p] = v[r];
+}
+
+// The last stage of radix R (Ns = M / R) from x into v[u R + r].
+template <int R, bool INV>
+__device__ __forceinline__ void fft_reg_last(const float2 *x, const float2 *tw, int logP, int Ns,
+                                             float2 (&v)[kFftRegVals]) {
+    constexpr int U = kFftRegVals / R;
+    const int n = Ns << logP;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int i = threadIdx.x + u * kFftThreads;
+        const int j = i >> logP;  // < Ns: also the twiddle index
+        float2 t[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) t[r] = x[i + r * n];
+#pragma unroll
+        for (int r = 1; r < R; ++r) {
+            float2 w = tw[r * j];
+            if (INV) w.y = -w.y;
+            t[r] = cmul(t[r], w);
+        }
+        dft<R, INV>(t);
+#pragma unroll
+        for (int r = 0; r < R; ++r) v[u * R + r] = t[r];
+    }
+}
+
+// The second and last stage (x synchronised on entry; M = 16 2^lr) into v.
+// Returns without a barrier after its reads of x.
+template <bool INV>
+__device__ __forceinline__ void fft_reg_rest(float2 *x, const float2 *tw, int logM, int logP,
+                                             float2 (&v)[kFftRegVals]) {
+    const int lr = logM - 4;
+    if (lr == 4) fft_reg_last<16, INV>(x, tw, logP, 16, v);
+    else if (lr == 3) fft_reg_last<8, INV>(x, tw, logP, 16, v);
+    else if (lr == 2) fft_reg_last<4, INV>(x, tw, logP, 16, v);
+    else fft_reg_last<2, INV>(x, tw, logP, 16, v);
+}
+
+// Last-stage outputs (v[u R + r]) reordered as first-stage inputs of the
+// same tile (v[u + r U]).
+template <int R> __device__ __forceinline__ void fft_reg_perm(float2 (&v)[kFftRegVals]) {
+    constexpr int U = kFftRegVals / R;
+    float2 t[kFftRegVals];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r) t[u + r * U] = v[u * R + r];
+#pragma unroll
+    for (int e = 0; e < kFftRegVals; ++e) v[e] = t[e];
+}
+
 // Global -> LDS staging of n values, NB per thread at a time: the loads of a
 // batch are issued together (indices clamped into range, so none is
 // conditional) and waited for once.  Sixteen at a time when a thread stages
@@ -447,7 +535,7 @@ __global__ __launch_bounds__(256) void fft_filter_transpose_kernel(const void *h
 // Kernel 1: forward transform along t2 for one t1, then the twiddle.
 // LDS (dynamic): one buffer (in place) of N2 P values, the N2 inner twiddles and the
 // N2 inter-step twiddles W_N^(t1 f2) of this t1.
-template <bool F32, int SRC>
+template <bool F32, int SRC, bool REG>
 __global__ __launch_bounds__(kFftThreads) void fft_rows_kernel(FftParams p) {
     extern __shared__ float2 lds[];
     const int item = xcd_item();
@@ -458,6 +546,29 @@ __global__ __launch_bounds__(kFftThreads) void fft_rows_kernel(FftParams p) {
     const int NP = N2 << logP;
     const int64_t N = (int64_t)N1 * N2;
     float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + kRowBufs * NP, *wt = tw + N2;
+    if constexpr (REG) {
+        // full tile: loads into the first stage, the last stage into the stores
+        if (!fft_reg_ok(p.log2, logP)) return;  // the host launches this form only for full tiles
+        const int j = (tile << logP) + (threadIdx.x & pmask);
+        float2 v[kFftRegVals];
+#pragma unroll
+        for (int u = 0; u < kFftRegVals; ++u)
+            v[u] = load_pair<F32, SRC>(p, b, t1 + (int64_t)N1 * ((threadIdx.x + u * kFftThreads) >> logP), j);
+        fill_twiddles(tw, N2);
+        for (int f2 = threadIdx.x; f2 < N2; f2 += kFftThreads) wt[f2] = twiddle(((int64_t)t1 * f2) & (N - 1), N);
+        fft_reg_first<false>(buf0, logP, v);
+        __syncthreads();
+        fft_reg_rest<false>(buf0, tw, p.log2, logP, v);
+        if (j < p.np) {
+            const int lr = fft_last_log(p.log2);
+#pragma unroll
+            for (int e = 0; e < kFftRegVals; ++e) {
+                const int f2 = fft_reg_out(e, lr, p.log2, logP);
+                p.ws[(((int64_t)b * N2 + f2) * N1 + t1) * p.np + j] = cmul(v[e], wt[f2]);
+            }
+        }
+        return;
+    }
     stage_in(buf0, NP, [&](int i) {
         return load_pair<F32, SRC>(p, b, t1 + (int64_t)N1 * (i >> logP), (tile << logP) + (i & pmask));
     });
@@ -604,6 +715,8 @@ __global__ __launch_bounds__(kFftThreads) void fft_cols_kernel(FftParams p) {
 // point reads one filter spectrum value.
 // LDS (dynamic): one buffer (in place) of N1 P values, the N1 inner twiddles and the N1
 // inter-step twiddles.
+// LR > 0: the register-fed form for full tiles whose last stage has radix 2^LR.
+template <int LR>
 __global__ __launch_bounds__(kFftThreads) void fft_col1_kernel(FftParams p) {
     extern __shared__ float2 lds[];
     const int item = xcd_item();
@@ -624,6 +737,44 @@ __global__ __launch_bounds__(kFftThreads) void fft_col1_kernel(FftParams p) {
     const int my_j = (tile << logP) + (threadIdx.x & pmask);
     const int jc = min(my_j, p.np - 1);
     const float2 *hrow = p.hs + (size_t)f2 * N1 * p.Gp + (2 * jc) / p.group_size;
+    if constexpr (LR > 0) {
+        // full tile: loads into the forward's first stage, its last stage
+        // into the products and the inverse's first stage, the inverse's
+        // last stage into the stores
+        if (!fft_reg_ok(p.log1, logP) || fft_last_log(p.log1) != LR) return;  // the host's choice
+        const bool ok = my_j < p.np;
+        constexpr int lr = LR;
+        // the filter spectra of this thread's frequencies, in flight during the forward transform
+        float2 hr[kFftRegVals], v[kFftRegVals];
+#pragma unroll
+        for (int e = 0; e < kFftRegVals; ++e) hr[e] = hrow[(size_t)fft_reg_out(e, lr, p.log1, logP) * p.Gp];
+#pragma unroll
+        for (int u = 0; u < kFftRegVals; ++u) {
+            const float2 x = p.ws[(col0 + ((threadIdx.x + u * kFftThreads) >> logP)) * p.np + (ok ? my_j : 0)];
+            v[u] = ok ? x : make_float2(0.0f, 0.0f);
+        }
+        fill_twiddles(tw, N1);
+        for (int t1 = threadIdx.x; t1 < N1; t1 += kFftThreads)
+            wt[t1] = cconj(twiddle(((int64_t)t1 * f2) & (N - 1), N));
+        fft_reg_first<false>(bufA, logP, v);
+        __syncthreads();
+        fft_reg_last<1 << LR, false>(bufA, tw, logP, 16, v);
+#pragma unroll
+        for (int e = 0; e < kFftRegVals; ++e) v[e] = ok ? cmul(hr[e], v[e]) : make_float2(0.0f, 0.0f);
+        fft_reg_perm<1 << LR>(v);
+        __syncthreads();  // every thread's last-stage reads are done
+        fft_reg_first<true>(bufA, logP, v);
+        __syncthreads();
+        fft_reg_last<1 << LR, true>(bufA, tw, logP, 16, v);
+        if (ok) {
+#pragma unroll
+            for (int e = 0; e < kFftRegVals; ++e) {
+                const int t1 = fft_reg_out(e, lr, p.log1, logP);
+                p.ws[(col0 + t1) * p.np + my_j] = cmul(v[e], wt[t1]);
+            }
+        }
+        return;
+    }
     float2 hh[kFftIpVals];
 #pragma unroll
     for (int u = 0; u < kFftIpVals; ++u) {
@@ -1202,7 +1353,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_out3_kernel(FftParams p) {
 
 // Kernel 3: inverse transform along f2 for one t1, scale, gate, store.
 // LDS (dynamic): one buffer (in place) of N2 P values and the N2 inner twiddles.
-template <bool F32, int MODE>
+template <bool F32, int MODE, bool REG>
 __global__ __launch_bounds__(kFftThreads) void fft_out_kernel(FftParams p) {
     extern __shared__ float2 lds[];
     const int item = xcd_item();
@@ -1213,6 +1364,36 @@ __global__ __launch_bounds__(kFftThreads) void fft_out_kernel(FftParams p) {
     const int NP = N2 << logP;
     const float scale = 1.0f / ((float)N1 * (float)N2);
     float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + kRowBufs * NP;
+    if constexpr (REG) {
+        // full tile: loads into the first stage, the last stage into the stores
+        if (!fft_reg_ok(p.log2, logP)) return;  // the host launches this form only for full tiles
+        const int jj = (tile << logP) + (threadIdx.x & pmask);
+        const bool ok = jj < p.np;
+        const int lr = fft_last_log(p.log2);
+        Gates<F32, MODE> gr[kFftRegVals];
+#pragma unroll
+        for (int e = 0; e < kFftRegVals; ++e) {
+            const int64_t t = t1 + (int64_t)N1 * fft_reg_out(e, lr, p.log2, logP);
+            if (ok && t < p.L) load_gates<F32, MODE>(p, b, t, jj, gr[e]);
+        }
+        float2 v[kFftRegVals];
+#pragma unroll
+        for (int u = 0; u < kFftRegVals; ++u) {
+            const float2 x =
+                p.ws[(((int64_t)b * N2 + ((threadIdx.x + u * kFftThreads) >> logP)) * N1 + t1) * p.np + (ok ? jj : 0)];
+            v[u] = ok ? x : make_float2(0.0f, 0.0f);
+        }
+        fill_twiddles(tw, N2);
+        fft_reg_first<true>(buf0, logP, v);
+        __syncthreads();
+        fft_reg_rest<true>(buf0, tw, p.log2, logP, v);
+#pragma unroll
+        for (int e = 0; e < kFftRegVals; ++e) {
+            const int64_t t = t1 + (int64_t)N1 * fft_reg_out(e, lr, p.log2, logP);
+            if (ok && t < p.L) store_out<F32, MODE>(p, b, t, jj, v[e].x * scale, v[e].y * scale, gr[e]);
+        }
+        return;
+    }
     // output u of this thread: i = tid + u kFftThreads (NP <= kFftIpVals kFftThreads)
     Gates<F32, MODE> gv[kFftIpVals];
 #pragma unroll
@@ -1246,6 +1427,8 @@ struct FftPlan {
     bool three;                      // three-level split (N3 > 1)
     int P_rows, P_mid, P_cols, P_col1;          // pairs per workgroup: row (rows3/out3), middle,
     int lds_rows, lds_mid, lds_cols, lds_col1;  // column (paired, single) kernels; their LDS bytes
+    bool reg_rows, reg_col1;                    // full tiles: the register-fed forms of the row and
+                                                // output kernels (two-level) and of the single-column kernel
     // backward: column kernel (pairs per tile, tiles, group slots per tile),
     // filter-gradient column kernel (group pairs per tile), LDS, and the
     // workspace: spectra, two work areas, partial sums
@@ -1318,6 +1501,8 @@ int fft_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, i
     pl->lds_cols = (2 * kRowBufs * pl->N1 * pl->P_cols + 3 * pl->N1) * (int)sizeof(float2);
     pl->P_col1 = pick_pairs(pl->N1, kRowBufs, pairs);
     pl->lds_col1 = (kRowBufs * pl->N1 * pl->P_col1 + 2 * pl->N1) * (int)sizeof(float2);
+    pl->reg_rows = !pl->three && pl->log2 >= 5 && pl->log2 <= 8 && pl->N2 * pl->P_rows == kFftRegVals * kFftThreads;
+    pl->reg_col1 = pl->log1 >= 5 && pl->log1 <= 8 && pl->N1 * pl->P_col1 == kFftRegVals * kFftThreads;
     // the output kernels hold the gates of Mr P / kFftThreads outputs per
     // thread, the single-column kernel N1 P / kFftThreads filter-spectrum values
     if ((int64_t)Mr * pl->P_rows > kFftIpVals * kFftThreads ||
@@ -1387,6 +1572,31 @@ int transpose_filters(const void *h, bool f32, int64_t G, int64_t Gp, int64_t l_
                        dim3((unsigned)(gx * gy)), dim3(256), 0, s, h, (float *)hT, (int)G, (int)Gp, (int)l_h,
                        (int)taps, (int)gx);
     return hipGetLastError() == hipSuccess ? HYENA_OK : HYENA_ERR_LAUNCH;
+}
+
+// The row, output and single-column kernels for a plan: the register-fed
+// form for full tiles.
+template <int SRC> const void *rows_kernel(bool f32, bool reg) {
+    if (f32) return reg ? (const void *)fft_rows_kernel<true, SRC, true> : (const void *)fft_rows_kernel<true, SRC, false>;
+    return reg ? (const void *)fft_rows_kernel<false, SRC, true> : (const void *)fft_rows_kernel<false, SRC, false>;
+}
+template <int MODE> const void *out_kernel(bool f32, bool reg) {
+    if constexpr (MODE == 2) {  // the filter gradient: fp32 output
+        return reg ? (const void *)fft_out_kernel<true, 2, true> : (const void *)fft_out_kernel<true, 2, false>;
+    } else {
+        if (f32)
+            return reg ? (const void *)fft_out_kernel<true, MODE, true> : (const void *)fft_out_kernel<true, MODE, false>;
+        return reg ? (const void *)fft_out_kernel<false, MODE, true> : (const void *)fft_out_kernel<false, MODE, false>;
+    }
+}
+const void *col1_kernel(bool reg, int log1) {
+    if (!reg) return (const void *)fft_col1_kernel<0>;
+    switch (fft_last_log(log1)) {
+    case 1: return (const void *)fft_col1_kernel<1>;
+    case 2: return (const void *)fft_col1_kernel<2>;
+    case 3: return (const void *)fft_col1_kernel<3>;
+    default: return (const void *)fft_col1_kernel<4>;
+    }
 }
 
 // One launch: pair tile P, grid (batch rows x units x tiles), dynamic LDS.
@@ -1466,9 +1676,9 @@ int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v, const vo
         rows_flt = f32 ? (const void *)fft_rows3_kernel<true, 1> : (const void *)fft_rows3_kernel<false, 1>;
         out_fn = f32 ? (const void *)fft_out3_kernel<true, 0> : (const void *)fft_out3_kernel<false, 0>;
     } else {
-        rows_seq = f32 ? (const void *)fft_rows_kernel<true, 0> : (const void *)fft_rows_kernel<false, 0>;
-        rows_flt = f32 ? (const void *)fft_rows_kernel<true, 1> : (const void *)fft_rows_kernel<false, 1>;
-        out_fn = f32 ? (const void *)fft_out_kernel<true, 0> : (const void *)fft_out_kernel<false, 0>;
+        rows_seq = rows_kernel<0>(f32, pl.reg_rows);
+        rows_flt = rows_kernel<1>(f32, pl.reg_rows);
+        out_fn = out_kernel<0>(f32, pl.reg_rows);
     }
     // units per batch row of the row and output kernels: t1 (x t2 when three-level)
     const int64_t row_units = pl.three ? (int64_t)pl.N1 * pl.N2 : pl.N1;
@@ -1495,7 +1705,7 @@ int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v, const vo
         st = launch((const void *)fft_mid_kernel<false>, p, pl.P_mid, mid_units, B, pl.lds_mid);
     // channel pairs inside one group (even group size): single columns
     if (st == HYENA_OK)
-        st = group_size % 2 == 0 ? launch((const void *)fft_col1_kernel, p, pl.P_col1, M, B, pl.lds_col1)
+        st = group_size % 2 == 0 ? launch(col1_kernel(pl.reg_col1, pl.log1), p, pl.P_col1, M, B, pl.lds_col1)
                                  : launch((const void *)fft_cols_kernel<1>, p, pl.P_cols, cols, B, pl.lds_cols);
     if (st == HYENA_OK && pl.three)
         st = launch((const void *)fft_mid_kernel<true>, p, pl.P_mid, mid_units, B, pl.lds_mid);
@@ -1596,8 +1806,8 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
         rows_seq = f32 ? (const void *)fft_rows3_kernel<true, 0> : (const void *)fft_rows3_kernel<false, 0>;
         rows_flt = f32 ? (const void *)fft_rows3_kernel<true, 1> : (const void *)fft_rows3_kernel<false, 1>;
     } else {
-        rows_seq = f32 ? (const void *)fft_rows_kernel<true, 0> : (const void *)fft_rows_kernel<false, 0>;
-        rows_flt = f32 ? (const void *)fft_rows_kernel<true, 1> : (const void *)fft_rows_kernel<false, 1>;
+        rows_seq = rows_kernel<0>(f32, pl.reg_rows);
+        rows_flt = rows_kernel<1>(f32, pl.reg_rows);
     }
     // the last inverse pass with each output form
     auto out_fn = [&](int mode) -> const void * {
@@ -1606,9 +1816,9 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
             if (mode == 1) return f32 ? (const void *)fft_out3_kernel<true, 1> : (const void *)fft_out3_kernel<false, 1>;
             return (const void *)fft_out3_kernel<true, 2>;
         }
-        if (mode == 0) return f32 ? (const void *)fft_out_kernel<true, 0> : (const void *)fft_out_kernel<false, 0>;
-        if (mode == 1) return f32 ? (const void *)fft_out_kernel<true, 1> : (const void *)fft_out_kernel<false, 1>;
-        return (const void *)fft_out_kernel<true, 2>;
+        if (mode == 0) return out_kernel<0>(f32, pl.reg_rows);
+        if (mode == 1) return out_kernel<1>(f32, pl.reg_rows);
+        return out_kernel<2>(true, pl.reg_rows);
     };
 
     // filter spectra (the first work area serves as the filter pass's), or

@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import gated_convolution_sequence_amd as hc
-from gpu_util import DEV, check_long_bwd, log, run_long_bwd as _run
+from gpu_util import DEV, check_long_bwd, log, register_fed_forms, run_long_bwd as _run
 from workloads import gaussian_inputs
 
 pytestmark = pytest.mark.gpu
@@ -49,6 +49,32 @@ SHAPES = [
     (1, 8192, 16, 1, 8192),
     (1, 40000, 4, 2, 40000),     # N = 2^17: the three-level split
 ]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_register_fed_and_lds_forms_agree(dt):
+    """The backward's row and output passes with tiles of 4096 values
+    (register-fed first and last stages, D = 128) and with fewer channels
+    (every stage through LDS, the first 64 channels alone): dq, dk, dv of
+    those channels and dh of their groups agree within the FFT bars, and
+    each call matches the oracle."""
+    dtype = DTYPES[dt]
+    B, L, l_h, gs = 2, 2000, 2000, 2
+    assert register_fed_forms(L, 128, gs, l_h)[0] and not register_fed_forms(L, 64, gs, l_h)[0]
+    q, k, v, h = gaussian_inputs(B, L, 128, gs, l_h, dtype, seed=67)
+    dy = _dy(B, L, 128, dtype, seed=71)
+    log("long bwd register-fed vs LDS forms %s" % dt)
+    wide = [t.clone() for t in _run(*(t.to(DEV) for t in (q, k, v, h, dy)), gs)]
+    sub = [t[..., :64].contiguous() for t in (q, k, v)]
+    dys = dy[..., :64].contiguous()
+    narrow = _run(*(t.to(DEV) for t in (*sub, h[:32].contiguous(), dys)), gs)
+    for i, (a, b) in enumerate(zip(wide, narrow)):
+        a = a[..., :64] if i < 3 else a[:32]
+        scale = float(b.float().abs().max())
+        tol = (1e-2 if dtype == torch.bfloat16 and i < 3 else 1e-5) * scale
+        assert float((a.float() - b.float()).abs().max()) <= tol, "gradient %d" % i
+    check_long_bwd(wide, q, k, v, h, dy, gs, dtype, "register-fed")
+    check_long_bwd(narrow, *sub, h[:32].contiguous(), dys, gs, dtype, "LDS")
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])

@@ -24,7 +24,7 @@ import torch
 
 import gated_convolution_sequence_amd as hc
 import oracle
-from gpu_util import DEV, check_long, log, run_long, to_np
+from gpu_util import DEV, check_long, log, register_fed_forms, run_long, to_np
 from workloads import WORKLOADS, gaussian_inputs, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -130,6 +130,30 @@ def test_single_and_paired_column_kernels_agree(dt):
     assert float((y1.float() - y2.float()).abs().max()) <= tol
     check_long(y2, q, k, v, h2, 2, dtype, "single-column")
     check_long(y1, q, k, v, h1, 1, dtype, "paired")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_register_fed_and_lds_forms_agree(dt):
+    """With tiles of 4096 values the row, single-column and output kernels
+    keep a transform's first and last stages in registers; with fewer
+    channels they run every stage through LDS.  Channels do not interact, so
+    the first 64 channels of a D = 128 call (register-fed) and a D = 64 call
+    on them (LDS) compute the same convolution: they agree within the FFT
+    bar, and each matches the oracle."""
+    dtype = DTYPES[dt]
+    B, L, l_h, gs = 2, 2000, 2000, 2
+    assert register_fed_forms(L, 128, gs, l_h) == (True, True)
+    assert register_fed_forms(L, 64, gs, l_h) == (False, False)
+    q, k, v, h = gaussian_inputs(B, L, 128, gs, l_h, dtype, seed=61)
+    log("register-fed vs LDS forms %s" % dt)
+    yw = run_long(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), gs).clone()
+    sub = [t[..., :64].contiguous() for t in (q, k, v)]
+    yn = run_long(*(t.to(DEV) for t in sub), h[:32].contiguous().to(DEV), gs)
+    scale = float(yn.float().abs().max())
+    tol = (1e-2 if dtype == torch.bfloat16 else 1e-5) * scale
+    assert float((yw[..., :64].float() - yn.float()).abs().max()) <= tol
+    check_long(yw, q, k, v, h, gs, dtype, "register-fed")
+    check_long(yn, *sub, h[:32].contiguous(), gs, dtype, "LDS")
 
 
 def test_deterministic_and_workspace_reuse():

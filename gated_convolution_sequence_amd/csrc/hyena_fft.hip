@@ -990,6 +990,11 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_cols_kernel(FftParams p) 
 // LDS (dynamic): one buffer (in place) of 2 N1 P values -- element (t1, src, pair) at
 // (2 t1 + src) P + pair -- the N1 inner twiddles and the N1 inter-step
 // twiddles W_N^(-t1 f2).
+// LR > 0: the register-fed form for full tiles (2 N1 P = 4096 values, the 2P
+// sequences interleaved as above) whose last stage has radix 2^LR: a thread
+// keeps one source and pair, so its products need no other thread's values;
+// the forward's results go to LDS only for the partial sums.
+template <int LR>
 __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) {
     extern __shared__ float2 lds[];
     const int item = xcd_item();
@@ -1014,28 +1019,9 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) 
     const int jc = min(my_j, p.np - 1);
     const float2 *hrow = p.hs + (size_t)f2 * N1 * p.Gp + (2 * jc) / p.group_size;
     const int NP = N1 << logP;
-    float2 hh[kFftIpVals / 2];
-#pragma unroll
-    for (int u = 0; u < kFftIpVals / 2; ++u) {
-        const int i = threadIdx.x + u * kFftThreads;
-        if (i < NP) hh[u] = hrow[(size_t)(i >> logP) * p.Gp];
-    }
-    stage_in(bufA, NS, [&](int i) {
-        const int src = (i >> logP) & 1;
-        const int j = (tile << logP) + (i & pmask);
-        const bool ok = j < p.np;
-        const float2 v = p.ws[src * area + (col0 + (i >> lS)) * p.np + (ok ? j : 0)];
-        return ok ? v : make_float2(0.0f, 0.0f);
-    });
-    fill_twiddles(tw, N1);
-    for (int t1 = threadIdx.x; t1 < N1; t1 += kFftThreads)
-        wt[t1] = cconj(twiddle(((int64_t)t1 * f2) & (N - 1), N));
-    __syncthreads();
-    float2 *S = lds_fft1(bufA, bufB, tw, N1, p.log1, lS, false);
-    // products to the other buffer, or (in place) over S once the partial
-    // sums, which read other threads' values, are done
-    float2 *Z = kFftInPlace ? S : (S == bufA ? bufB : bufA);
-    if (p.part != nullptr) {
+    // the filter-gradient partial sums of this tile from the transformed
+    // columns S (x at (f1 << lS) + pair, dz sdz further)
+    auto partial_sums = [&](const float2 *S) {
         // one item per (f1, group slot): pairs lie inside one group
         const int c_lo = (tile << logP) * 2;
         const int c_end = min(c_lo + (2 << logP), 2 * p.np);
@@ -1064,7 +1050,75 @@ __global__ __launch_bounds__(kFftThreads) void fft_bwd_col1_kernel(FftParams p) 
             }
             p.part[((((int64_t)b * p.n_tiles + tile) * p.n_slots + slot) * M + f2) * N1 + f1] = acc;
         }
+    };
+    if constexpr (LR > 0) {
+        if (!fft_reg_ok(p.log1, lS) || fft_last_log(p.log1) != LR) return;  // the host's choice
+        constexpr int lr = LR;
+        const int src = (threadIdx.x >> logP) & 1;
+        const bool ok = my_j < p.np;
+        const int64_t base = src * area + col0 * p.np + (ok ? my_j : 0);
+        float2 hr[kFftRegVals], v[kFftRegVals];
+#pragma unroll
+        for (int e = 0; e < kFftRegVals; ++e) hr[e] = hrow[(size_t)fft_reg_out(e, lr, p.log1, lS) * p.Gp];
+#pragma unroll
+        for (int u = 0; u < kFftRegVals; ++u) {
+            const float2 x = p.ws[base + (int64_t)((threadIdx.x + u * kFftThreads) >> lS) * p.np];
+            v[u] = ok ? x : make_float2(0.0f, 0.0f);
+        }
+        fill_twiddles(tw, N1);
+        for (int t1 = threadIdx.x; t1 < N1; t1 += kFftThreads)
+            wt[t1] = cconj(twiddle(((int64_t)t1 * f2) & (N - 1), N));
+        fft_reg_first<false>(bufA, lS, v);
+        __syncthreads();
+        fft_reg_last<1 << LR, false>(bufA, tw, lS, 16, v);
+        if (p.part != nullptr) {
+            __syncthreads();  // every thread's last-stage reads are done
+#pragma unroll
+            for (int e = 0; e < kFftRegVals; ++e)
+                bufA[(fft_reg_out(e, lr, p.log1, lS) << lS) + (threadIdx.x & ((2 << logP) - 1))] = v[e];
+            __syncthreads();
+            partial_sums(bufA);
+        }
+#pragma unroll
+        for (int e = 0; e < kFftRegVals; ++e)
+            v[e] = ok ? cmul(src ? cconj(hr[e]) : hr[e], v[e]) : make_float2(0.0f, 0.0f);
+        fft_reg_perm<1 << LR>(v);
+        __syncthreads();  // the last-stage (or partial-sum) reads are done
+        fft_reg_first<true>(bufA, lS, v);
+        __syncthreads();
+        fft_reg_last<1 << LR, true>(bufA, tw, lS, 16, v);
+        if (ok) {
+            const int64_t obase = src * area + col0 * p.np + my_j;
+#pragma unroll
+            for (int e = 0; e < kFftRegVals; ++e) {
+                const int t1 = fft_reg_out(e, lr, p.log1, lS);
+                p.ws[obase + (int64_t)t1 * p.np] = cmul(v[e], wt[t1]);
+            }
+        }
+        return;
     }
+    float2 hh[kFftIpVals / 2];
+#pragma unroll
+    for (int u = 0; u < kFftIpVals / 2; ++u) {
+        const int i = threadIdx.x + u * kFftThreads;
+        if (i < NP) hh[u] = hrow[(size_t)(i >> logP) * p.Gp];
+    }
+    stage_in(bufA, NS, [&](int i) {
+        const int src = (i >> logP) & 1;
+        const int j = (tile << logP) + (i & pmask);
+        const bool ok = j < p.np;
+        const float2 v = p.ws[src * area + (col0 + (i >> lS)) * p.np + (ok ? j : 0)];
+        return ok ? v : make_float2(0.0f, 0.0f);
+    });
+    fill_twiddles(tw, N1);
+    for (int t1 = threadIdx.x; t1 < N1; t1 += kFftThreads)
+        wt[t1] = cconj(twiddle(((int64_t)t1 * f2) & (N - 1), N));
+    __syncthreads();
+    float2 *S = lds_fft1(bufA, bufB, tw, N1, p.log1, lS, false);
+    // products to the other buffer, or (in place) over S once the partial
+    // sums, which read other threads' values, are done
+    float2 *Z = kFftInPlace ? S : (S == bufA ? bufB : bufA);
+    if (p.part != nullptr) partial_sums(S);
     if constexpr (kFftInPlace) __syncthreads();
 #pragma unroll
     for (int u = 0; u < kFftIpVals / 2; ++u) {
@@ -1434,6 +1488,7 @@ struct FftPlan {
     // workspace: spectra, two work areas, partial sums
     int P_bwd, P_dh, lds_bwd, lds_dh;
     bool bwd_col1;                   // the backward's single-column form (even group sizes)
+    bool reg_bwd1;                   // ... in its register-fed form (full tiles)
     int64_t pb_tiles, n_slots, area_bytes, part_bytes, bwd_ws_bytes;
 };
 
@@ -1541,7 +1596,9 @@ int fft_bwd_plan(int64_t B, int64_t D, int64_t group_size, FftPlan *pl) {
         pl->P_bwd = pick_pairs(pl->N1, 2 * kRowBufs, pairs, kFftBwdBudget);
         pl->lds_bwd = (2 * kRowBufs * pl->N1 * pl->P_bwd + 2 * pl->N1) * (int)sizeof(float2);
         if ((int64_t)2 * pl->N1 * pl->P_bwd > kFftIpVals * kFftThreads) return HYENA_ERR_UNSUPPORTED;
+        pl->reg_bwd1 = pl->log1 >= 5 && pl->log1 <= 8 && 2 * pl->N1 * pl->P_bwd == kFftRegVals * kFftThreads;
     } else {
+        pl->reg_bwd1 = false;
         pl->P_bwd = pick_pairs(pl->N1, 4 * kRowBufs, pairs, kFftBwdBudget);
         pl->lds_bwd = (4 * kRowBufs * pl->N1 * pl->P_bwd + 3 * pl->N1) * (int)sizeof(float2);
         if ((int64_t)4 * pl->N1 * pl->P_bwd > kFftIpVals * kFftThreads) return HYENA_ERR_UNSUPPORTED;
@@ -1587,6 +1644,15 @@ template <int MODE> const void *out_kernel(bool f32, bool reg) {
         if (f32)
             return reg ? (const void *)fft_out_kernel<true, MODE, true> : (const void *)fft_out_kernel<true, MODE, false>;
         return reg ? (const void *)fft_out_kernel<false, MODE, true> : (const void *)fft_out_kernel<false, MODE, false>;
+    }
+}
+const void *bwd_col1_kernel(bool reg, int log1) {
+    if (!reg) return (const void *)fft_bwd_col1_kernel<0>;
+    switch (fft_last_log(log1)) {
+    case 1: return (const void *)fft_bwd_col1_kernel<1>;
+    case 2: return (const void *)fft_bwd_col1_kernel<2>;
+    case 3: return (const void *)fft_bwd_col1_kernel<3>;
+    default: return (const void *)fft_bwd_col1_kernel<4>;
     }
 }
 const void *col1_kernel(bool reg, int log1) {
@@ -1854,7 +1920,7 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
         pc.part = dh ? (float2 *)((char *)p.ws + 2 * pl.area_bytes) : nullptr;
         pc.n_slots = (int32_t)pl.n_slots;
         if (st == HYENA_OK)
-            st = pl.bwd_col1 ? launch((const void *)fft_bwd_col1_kernel, pc, pl.P_bwd, M, B, pl.lds_bwd)
+            st = pl.bwd_col1 ? launch(bwd_col1_kernel(pl.reg_bwd1, pl.log1), pc, pl.P_bwd, M, B, pl.lds_bwd)
                              : launch((const void *)fft_bwd_cols_kernel, pc, pl.P_bwd, cols, B, pl.lds_bwd);
     }
     if (st == HYENA_OK && pl.three && (dq || dk))

@@ -137,26 +137,28 @@ def transform_len(L, l_h):
 
 
 def register_fed_forms(L, D, gs, l_h):
-    """Which register-fed forms the long-filter plan takes, (rows and output,
-    single column): two-level transforms of 32 to 256 points whose pair tile
-    (at most 64 pairs, at most 4096 values, no wider than the pairs there are)
-    holds exactly 4096 values, so that each of 256 threads keeps 16."""
+    """Which register-fed forms the long-filter plan takes: (rows and output,
+    single column, the backward's single column).  Transforms of 32 to 256
+    points (two-level for the rows) whose tile of pairs (at most 64, at most
+    4096 values with the backward's two sequences per pair, no wider than the
+    pairs there are) holds exactly 4096 values, 16 for each of 256 threads."""
     N = transform_len(L, l_h)
     log_n = N.bit_length() - 1
     log1, log2 = (log_n + 1) // 2, log_n // 2
-    pairs = max(D // 2, (D // gs + 1) // 2)
 
-    def tile(m):
+    def tile(m, seqs, pairs):
         P = 64
-        while P > 1 and m * P > 4096:
+        while P > 1 and seqs * m * P > 4096:
             P //= 2
         while P > 1 and P // 2 >= pairs:
             P //= 2
-        return m * P
+        return seqs * m * P
 
-    rows = log_n <= 16 and 5 <= log2 <= 8 and tile(1 << log2) == 4096
-    col1 = 5 <= log1 <= 8 and tile(1 << log1) == 4096 and gs % 2 == 0
-    return rows, col1
+    pairs = max(D // 2, (D // gs + 1) // 2)
+    rows = log_n <= 16 and 5 <= log2 <= 8 and tile(1 << log2, 1, pairs) == 4096
+    col1 = 5 <= log1 <= 8 and tile(1 << log1, 1, pairs) == 4096 and gs % 2 == 0
+    bwd1 = 5 <= log1 <= 8 and tile(1 << log1, 2, D // 2) == 4096 and gs % 2 == 0
+    return rows, col1, bwd1
 
 
 def run_long(q, k, v, h, gs, pad=16):

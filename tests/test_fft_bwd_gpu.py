@@ -78,6 +78,27 @@ def test_register_fed_and_lds_forms_agree(dt):
     check_long_bwd(narrow, *sub, h[:16].contiguous(), dys, gs, dtype, "LDS")
 
 
+# every register-fed instance (64-, 128- and 256-point transforms), ragged
+# last tiles, two batch rows, different radices for rows and columns
+REGISTER_FED_SHAPES = [
+    # B, L, D, group_size, l_h
+    (2, 3000, 200, 2, 1000), (2, 5000, 136, 4, 3000), (1, 20000, 130, 2, 300), (1, 40000, 40, 8, 300),
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h", REGISTER_FED_SHAPES)
+def test_register_fed_shapes(dt, B, L, D, gs, l_h):
+    assert register_fed_forms(L, D, gs, l_h) == (True, True, True)
+    log("long bwd register-fed %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=2 * L + D + gs)
+    dy = _dy(B, L, D, dtype, seed=L + 11)
+    got = _run(*(t.to(DEV) for t in (q, k, v, h, dy)), gs)
+    rel = check_long_bwd(got, q, k, v, h, dy, gs, dtype, "long bwd register-fed")
+    log("  rel err %s" % ", ".join("%s %.2e" % kv for kv in rel.items()))
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("B,L,D,gs,l_h", SHAPES)
 def test_long_backward_gaussian(dt, B, L, D, gs, l_h):

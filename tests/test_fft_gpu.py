@@ -156,6 +156,30 @@ def test_register_fed_and_lds_forms_agree(dt):
     check_long(yn, *sub, h[:32].contiguous(), gs, dtype, "LDS")
 
 
+# shapes that reach every register-fed instance (last radix 4, 8 and 16:
+# 64-, 128- and 256-point transforms), with a ragged last pair tile, two
+# batch rows and a split with different radices for rows and columns
+REGISTER_FED_SHAPES = [
+    # B, L, D, group_size, l_h
+    (2, 3000, 200, 2, 1000),     # N = 2^12: 64 x 64, tiles of 64 pairs (64 + 36)
+    (2, 5000, 136, 4, 3000),     # N = 2^13: 128 columns, 64-point rows, 68 pairs
+    (1, 20000, 130, 2, 300),     # N = 2^15: 256 columns, 128-point rows, 65 pairs
+    (1, 40000, 40, 8, 300),      # N = 2^16: 256 x 256, tiles of 16 pairs (16 + 4)
+]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,D,gs,l_h", REGISTER_FED_SHAPES)
+def test_register_fed_shapes(dt, B, L, D, gs, l_h):
+    assert register_fed_forms(L, D, gs, l_h)[:2] == (True, True)
+    log("long register-fed %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=L + D + gs)
+    y = run_long(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), gs)
+    rel = check_long(y, q, k, v, h, gs, dtype, "long register-fed")
+    log("  rel err %.3e" % rel)
+
+
 def test_deterministic_and_workspace_reuse():
     B, L, D, gs, l_h = 1, 3000, 64, 2, 3000
     q, k, v, h = (t.to(DEV) for t in gaussian_inputs(B, L, D, gs, l_h, torch.bfloat16, seed=9))

@@ -1226,7 +1226,32 @@ __global__ __launch_bounds__(kFftThreads) void fft_dh_cols_kernel(FftParams p) {
     }
 }
 
-// Filter-gradient taps past the sequence (l_h > L: no row reaches them): zero.
+// The filter gradient from the last inverse pass's [taps][Gp] layout to
+// [G][l_h], zero for taps t >= taps (l_h > L: no row reaches them).  64 x 64
+// tiles through LDS: reads run along filters, writes along taps.
+__global__ __launch_bounds__(256) void fft_dh_transpose_kernel(const float *dhT, float *dh, int G, int Gp, int l_h,
+                                                              int taps, int n_tblk) {
+    __shared__ float tile[64][65];
+    const int t0 = (int)(blockIdx.x % n_tblk) * 64, g0 = (int)(blockIdx.x / n_tblk) * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    // all 16 loads of a thread in flight together
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int t = t0 + ty + 4 * u, g = g0 + tx;
+        v[u] = (t < taps && g < Gp) ? dhT[(size_t)t * Gp + g] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) tile[ty + 4 * u][tx] = v[u];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int g = g0 + ty + 4 * u, t = t0 + tx;
+        if (g < G && t < l_h) dh[(size_t)g * l_h + t] = tile[tx][ty + 4 * u];
+    }
+}
+
+// Filter-gradient taps from `from` on: zero (a call with no rows).
 __global__ __launch_bounds__(256) void fft_dh_tail_kernel(float *dh, int64_t G, int64_t l_h, int64_t from) {
     const int64_t w = l_h - from;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1236,7 +1261,9 @@ __global__ __launch_bounds__(256) void fft_dh_tail_kernel(float *dh, int64_t G, 
 // Output of the last inverse pass for channel pair j at row t (values
 // already scaled).  MODE 0: y = q z (the forward; the backward's dq with dy in
 // q's place).  MODE 1: the backward's dk = z v and dv = z k (z = dx).  MODE 2:
-// the filter gradient, fp32 [G][l_h], groups 2j and 2j + 1 at tap t.
+// the filter gradient transposed, fp32 [taps][Gp], groups 2j and 2j + 1 at
+// tap t (consecutive lanes write consecutive group pairs of one tap;
+// fft_dh_transpose_kernel then writes [G][l_h]).
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
     const __bf16 x = (__bf16)a, y = (__bf16)b;
     return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
@@ -1272,9 +1299,7 @@ template <bool F32, int MODE>
 __device__ inline void store_out(const FftParams &p, int b, int64_t t, int j, float z0, float z1,
                                  const Gates<F32, MODE> &g) {
     if constexpr (MODE == 2) {
-        float *dh = (float *)p.y;
-        dh[(size_t)(2 * j) * (size_t)p.l_h + (size_t)t] = z0;
-        if (2 * j + 1 < p.G) dh[(size_t)(2 * j + 1) * (size_t)p.l_h + (size_t)t] = z1;
+        *(float2 *)((float *)p.y + (size_t)t * (size_t)p.Gp + 2 * (size_t)j) = make_float2(z0, z1);
         return;
     }
     const size_t o = ((size_t)b * (size_t)p.L + (size_t)t) * (size_t)p.D + 2 * (size_t)j;
@@ -1835,7 +1860,9 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
     }
     hipStream_t s = (hipStream_t)stream;
     const int64_t taps = l_h < L ? l_h : L;
-    if (dh && (G * l_h + 255) / 256 > INT32_MAX) return HYENA_ERR_UNSUPPORTED;  // the zero-fill grid
+    // the zero-fill and transpose grids
+    if (dh && ((G * l_h + 255) / 256 > INT32_MAX || ((l_h + 63) / 64) * ((G + 63) / 64) > INT32_MAX))
+        return HYENA_ERR_UNSUPPORTED;
     if (empty || (!dq && !dk && !dh)) {
         // no rows: dh is zero (D == 0: dh has no elements)
         if (dh && G * l_h > 0) {
@@ -1937,7 +1964,9 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
     }
     if (st == HYENA_OK && dh) {
         // group spectra -> one-row work area of Gp/2 group pairs (the first
-        // work area, free once dq is out) -> inverse along f2 -> dh rows < taps
+        // work area, free once dq is out) -> inverse along f2 -> [taps][Gp]
+        // in the second work area (free once dk and dv are out; B N D / 2
+        // complex values >= taps Gp floats) -> dh [G][l_h]
         FftParams pd = p;
         pd.part = (float2 *)((char *)p.ws + 2 * pl.area_bytes);
         pd.np = p.Gp / 2;
@@ -1949,14 +1978,14 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
         pd.part_slot_major = pl.bwd_col1 ? 1 : 0;
         st = launch((const void *)fft_dh_cols_kernel, pd, pl.P_dh, cols, 1, pl.lds_dh);
         pd.L = taps;
-        pd.y = dh;
+        pd.y = area_dz;
         if (st == HYENA_OK && pl.three)
             st = launch((const void *)fft_mid_kernel<true>, pd, pl.P_mid, mid_units, 1, pl.lds_mid);
         if (st == HYENA_OK) st = launch(out_fn(2), pd, pl.P_rows, row_units, 1, pl.lds_rows);
-        if (st == HYENA_OK && l_h > taps) {
-            const int64_t n = G * (l_h - taps);
-            hipLaunchKernelGGL(fft_dh_tail_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dh, G, l_h,
-                               taps);
+        if (st == HYENA_OK) {
+            const int64_t n_tblk = (l_h + 63) / 64, n_gblk = (G + 63) / 64;
+            hipLaunchKernelGGL(fft_dh_transpose_kernel, dim3((unsigned)(n_tblk * n_gblk)), dim3(256), 0, s,
+                               (const float *)area_dz, dh, (int)G, (int)p.Gp, (int)l_h, (int)taps, (int)n_tblk);
         }
     }
     if (st != HYENA_OK) return st;

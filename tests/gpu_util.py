@@ -144,7 +144,11 @@ def register_fed_forms(L, D, gs, l_h):
     pairs there are) holds exactly 4096 values, 16 for each of 256 threads."""
     N = transform_len(L, l_h)
     log_n = N.bit_length() - 1
-    log1, log2 = (log_n + 1) // 2, log_n // 2
+    if log_n > 16:  # three-level split: N1 N2 N3, every transform at most 256 points
+        log1 = (log_n + 2) // 3
+        log2 = (log_n - log1 + 1) // 2
+    else:
+        log1, log2 = (log_n + 1) // 2, log_n // 2
 
     def tile(m, seqs, pairs):
         P = 64

@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import gated_convolution_sequence_amd as hc
-from gpu_util import DEV, check_long_bwd, log, register_fed_forms, run_long_bwd as _run
+from gpu_util import DEV, check_long_bwd, log, register_fed_forms, run_long_bwd as _run, transform_len
 from workloads import gaussian_inputs
 
 pytestmark = pytest.mark.gpu
@@ -83,13 +83,15 @@ def test_register_fed_and_lds_forms_agree(dt):
 REGISTER_FED_SHAPES = [
     # B, L, D, group_size, l_h
     (2, 3000, 200, 2, 1000), (2, 5000, 136, 4, 3000), (1, 20000, 130, 2, 300), (1, 40000, 40, 8, 300),
+    (1, 70000, 128, 2, 300),     # N = 2^17, three-level: register-fed 64-point columns
 ]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("B,L,D,gs,l_h", REGISTER_FED_SHAPES)
 def test_register_fed_shapes(dt, B, L, D, gs, l_h):
-    assert register_fed_forms(L, D, gs, l_h) == (True, True, True)
+    forms = register_fed_forms(L, D, gs, l_h)
+    assert forms[1] and forms[2] and (forms[0] or transform_len(L, l_h) > 1 << 16)
     log("long bwd register-fed %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
     dtype = DTYPES[dt]
     q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=2 * L + D + gs)

@@ -24,7 +24,7 @@ import torch
 
 import gated_convolution_sequence_amd as hc
 import oracle
-from gpu_util import DEV, check_long, log, register_fed_forms, run_long, to_np
+from gpu_util import DEV, check_long, log, register_fed_forms, run_long, to_np, transform_len
 from workloads import WORKLOADS, gaussian_inputs, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -165,13 +165,15 @@ REGISTER_FED_SHAPES = [
     (2, 5000, 136, 4, 3000),     # N = 2^13: 128 columns, 64-point rows, 68 pairs
     (1, 20000, 130, 2, 300),     # N = 2^15: 256 columns, 128-point rows, 65 pairs
     (1, 40000, 40, 8, 300),      # N = 2^16: 256 x 256, tiles of 16 pairs (16 + 4)
+    (1, 70000, 128, 2, 300),     # N = 2^17, three-level: register-fed 64-point columns
 ]
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("B,L,D,gs,l_h", REGISTER_FED_SHAPES)
 def test_register_fed_shapes(dt, B, L, D, gs, l_h):
-    assert register_fed_forms(L, D, gs, l_h)[:2] == (True, True)
+    forms = register_fed_forms(L, D, gs, l_h)
+    assert forms[1] and (forms[0] or transform_len(L, l_h) > 1 << 16)
     log("long register-fed %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
     dtype = DTYPES[dt]
     q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=L + D + gs)

@@ -1328,7 +1328,7 @@ __device__ inline void store_out(const FftParams &p, int b, int64_t t, int j, fl
 // and out3 (inverse N3-point FFT over f3, scale, gate, store).
 // LDS (dynamic) of either: one buffer (in place) of N3 P (N2 P) values, the inner
 // twiddles and the N3 (N2) inter-step twiddles.
-template <bool F32, int SRC>
+template <bool F32, int SRC, bool REG>
 __global__ __launch_bounds__(kFftThreads) void fft_rows3_kernel(FftParams p) {
     extern __shared__ float2 lds[];
     const int item = xcd_item();
@@ -1340,6 +1340,30 @@ __global__ __launch_bounds__(kFftThreads) void fft_rows3_kernel(FftParams p) {
     const int NP = N3 << logP;
     const int64_t M = (int64_t)N2 * N3;
     float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + kRowBufs * NP, *wt = tw + N3;
+    if constexpr (REG) {
+        // full tile: loads into the first stage, the last stage into the stores
+        if (!fft_reg_ok(p.log3, logP)) return;  // the host launches this form only for full tiles
+        const int j = (tile << logP) + (threadIdx.x & pmask);
+        float2 v[kFftRegVals];
+#pragma unroll
+        for (int u = 0; u < kFftRegVals; ++u)
+            v[u] = load_pair<F32, SRC>(
+                p, b, t1 + (int64_t)N1 * (t2 + (int64_t)N2 * ((threadIdx.x + u * kFftThreads) >> logP)), j);
+        fill_twiddles(tw, N3);
+        for (int f3 = threadIdx.x; f3 < N3; f3 += kFftThreads) wt[f3] = twiddle(((int64_t)t2 * f3) & (M - 1), M);
+        fft_reg_first<false>(buf0, logP, v);
+        __syncthreads();
+        fft_reg_rest<false>(buf0, tw, p.log3, logP, v);
+        if (j < p.np) {
+            const int lr = fft_last_log(p.log3);
+#pragma unroll
+            for (int e = 0; e < kFftRegVals; ++e) {
+                const int f3 = fft_reg_out(e, lr, p.log3, logP);
+                p.ws[(((int64_t)b * M + (int64_t)f3 * N2 + t2) * N1 + t1) * p.np + j] = cmul(v[e], wt[f3]);
+            }
+        }
+        return;
+    }
     stage_in(buf0, NP, [&](int i) {
         return load_pair<F32, SRC>(p, b, t1 + (int64_t)N1 * (t2 + (int64_t)N2 * (i >> logP)),
                                    (tile << logP) + (i & pmask));
@@ -1356,7 +1380,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_rows3_kernel(FftParams p) {
     }
 }
 
-template <bool INV>
+template <bool INV, bool REG>
 __global__ __launch_bounds__(kFftThreads) void fft_mid_kernel(FftParams p) {
     extern __shared__ float2 lds[];
     const int item = xcd_item();
@@ -1370,6 +1394,34 @@ __global__ __launch_bounds__(kFftThreads) void fft_mid_kernel(FftParams p) {
     const int64_t N = M * N1;
     float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + kRowBufs * NP, *wt = tw + N2;
     const int64_t row0 = (int64_t)b * M + (int64_t)f3 * N2;  // position of index 0 along t2 / f2
+    if constexpr (REG) {
+        // full tile: loads into the first stage, the last stage into the stores
+        if (!fft_reg_ok(p.log2, logP)) return;  // the host launches this form only for full tiles
+        const int j = (tile << logP) + (threadIdx.x & pmask);
+        const bool ok = j < p.np;
+        float2 v[kFftRegVals];
+#pragma unroll
+        for (int u = 0; u < kFftRegVals; ++u) {
+            const float2 x = p.ws[((row0 + ((threadIdx.x + u * kFftThreads) >> logP)) * N1 + t1) * p.np + (ok ? j : 0)];
+            v[u] = ok ? x : make_float2(0.0f, 0.0f);
+        }
+        fill_twiddles(tw, N2);
+        for (int u = threadIdx.x; u < N2; u += kFftThreads)
+            wt[u] = INV ? cconj(twiddle(((int64_t)u * f3) & (M - 1), M))
+                        : twiddle(((int64_t)t1 * (f3 + (int64_t)N3 * u)) & (N - 1), N);
+        fft_reg_first<INV>(buf0, logP, v);
+        __syncthreads();
+        fft_reg_rest<INV>(buf0, tw, p.log2, logP, v);
+        if (ok) {
+            const int lr = fft_last_log(p.log2);
+#pragma unroll
+            for (int e = 0; e < kFftRegVals; ++e) {
+                const int u = fft_reg_out(e, lr, p.log2, logP);
+                p.ws[((row0 + u) * N1 + t1) * p.np + j] = cmul(v[e], wt[u]);
+            }
+        }
+        return;
+    }
     stage_in(buf0, NP, [&](int i) {
         const int j = (tile << logP) + (i & pmask);
         const bool ok = j < p.np;
@@ -1390,7 +1442,7 @@ __global__ __launch_bounds__(kFftThreads) void fft_mid_kernel(FftParams p) {
     }
 }
 
-template <bool F32, int MODE>
+template <bool F32, int MODE, bool REG>
 __global__ __launch_bounds__(kFftThreads) void fft_out3_kernel(FftParams p) {
     extern __shared__ float2 lds[];
     const int item = xcd_item();
@@ -1403,6 +1455,36 @@ __global__ __launch_bounds__(kFftThreads) void fft_out3_kernel(FftParams p) {
     const int64_t M = (int64_t)N2 * N3;
     const float scale = 1.0f / ((float)N1 * (float)M);
     float2 *buf0 = lds, *buf1 = lds + NP, *tw = lds + kRowBufs * NP;
+    if constexpr (REG) {
+        // full tile: loads into the first stage, the last stage into the stores
+        if (!fft_reg_ok(p.log3, logP)) return;  // the host launches this form only for full tiles
+        const int jj = (tile << logP) + (threadIdx.x & pmask);
+        const bool ok = jj < p.np;
+        const int lr = fft_last_log(p.log3);
+        auto row_of = [&](int e) -> int64_t {
+            return t1 + (int64_t)N1 * (t2 + (int64_t)N2 * fft_reg_out(e, lr, p.log3, logP));
+        };
+        Gates<F32, MODE> gr[kFftRegVals];
+#pragma unroll
+        for (int e = 0; e < kFftRegVals; ++e)
+            if (ok && row_of(e) < p.L) load_gates<F32, MODE>(p, b, row_of(e), jj, gr[e]);
+        float2 v[kFftRegVals];
+#pragma unroll
+        for (int u = 0; u < kFftRegVals; ++u) {
+            const int f3 = (threadIdx.x + u * kFftThreads) >> logP;
+            const float2 x = p.ws[(((int64_t)b * M + (int64_t)f3 * N2 + t2) * N1 + t1) * p.np + (ok ? jj : 0)];
+            v[u] = ok ? x : make_float2(0.0f, 0.0f);
+        }
+        fill_twiddles(tw, N3);
+        fft_reg_first<true>(buf0, logP, v);
+        __syncthreads();
+        fft_reg_rest<true>(buf0, tw, p.log3, logP, v);
+#pragma unroll
+        for (int e = 0; e < kFftRegVals; ++e)
+            if (ok && row_of(e) < p.L)
+                store_out<F32, MODE>(p, b, row_of(e), jj, v[e].x * scale, v[e].y * scale, gr[e]);
+        return;
+    }
     // output u of this thread: i = tid + u kFftThreads (NP <= kFftIpVals kFftThreads)
     auto out_row = [&](int i) -> int64_t { return t1 + (int64_t)N1 * (t2 + (int64_t)N2 * (i >> logP)); };
     Gates<F32, MODE> gv[kFftIpVals];
@@ -1507,7 +1589,8 @@ struct FftPlan {
     int P_rows, P_mid, P_cols, P_col1;          // pairs per workgroup: row (rows3/out3), middle,
     int lds_rows, lds_mid, lds_cols, lds_col1;  // column (paired, single) kernels; their LDS bytes
     bool reg_rows, reg_col1;                    // full tiles: the register-fed forms of the row and
-                                                // output kernels (two-level) and of the single-column kernel
+                                                // output kernels (two-level) and of the single-column kernel,
+    bool reg_rows3, reg_mid;                    // and of the three-level row / output and middle kernels
     // backward: column kernel (pairs per tile, tiles, group slots per tile),
     // filter-gradient column kernel (group pairs per tile), LDS, and the
     // workspace: spectra, two work areas, partial sums
@@ -1583,6 +1666,8 @@ int fft_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, i
     pl->lds_col1 = (kRowBufs * pl->N1 * pl->P_col1 + 2 * pl->N1) * (int)sizeof(float2);
     pl->reg_rows = !pl->three && pl->log2 >= 5 && pl->log2 <= 8 && pl->N2 * pl->P_rows == kFftRegVals * kFftThreads;
     pl->reg_col1 = pl->log1 >= 5 && pl->log1 <= 8 && pl->N1 * pl->P_col1 == kFftRegVals * kFftThreads;
+    pl->reg_rows3 = pl->three && pl->log3 >= 5 && pl->log3 <= 8 && pl->N3 * pl->P_rows == kFftRegVals * kFftThreads;
+    pl->reg_mid = pl->three && pl->log2 >= 5 && pl->log2 <= 8 && pl->N2 * pl->P_mid == kFftRegVals * kFftThreads;
     // the output kernels hold the gates of Mr P / kFftThreads outputs per
     // thread, the single-column kernel N1 P / kFftThreads filter-spectrum values
     if ((int64_t)Mr * pl->P_rows > kFftIpVals * kFftThreads ||
@@ -1670,6 +1755,22 @@ template <int MODE> const void *out_kernel(bool f32, bool reg) {
             return reg ? (const void *)fft_out_kernel<true, MODE, true> : (const void *)fft_out_kernel<true, MODE, false>;
         return reg ? (const void *)fft_out_kernel<false, MODE, true> : (const void *)fft_out_kernel<false, MODE, false>;
     }
+}
+template <int SRC> const void *rows3_kernel(bool f32, bool reg) {
+    if (f32) return reg ? (const void *)fft_rows3_kernel<true, SRC, true> : (const void *)fft_rows3_kernel<true, SRC, false>;
+    return reg ? (const void *)fft_rows3_kernel<false, SRC, true> : (const void *)fft_rows3_kernel<false, SRC, false>;
+}
+template <int MODE> const void *out3_kernel(bool f32, bool reg) {
+    if constexpr (MODE == 2) {  // the filter gradient: fp32 output
+        return reg ? (const void *)fft_out3_kernel<true, 2, true> : (const void *)fft_out3_kernel<true, 2, false>;
+    } else {
+        if (f32)
+            return reg ? (const void *)fft_out3_kernel<true, MODE, true> : (const void *)fft_out3_kernel<true, MODE, false>;
+        return reg ? (const void *)fft_out3_kernel<false, MODE, true> : (const void *)fft_out3_kernel<false, MODE, false>;
+    }
+}
+template <bool INV> const void *mid_kernel(bool reg) {
+    return reg ? (const void *)fft_mid_kernel<INV, true> : (const void *)fft_mid_kernel<INV, false>;
 }
 const void *bwd_col1_kernel(bool reg, int log1) {
     if (!reg) return (const void *)fft_bwd_col1_kernel<0>;
@@ -1763,9 +1864,9 @@ int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v, const vo
     const int64_t cols = M / 2 + 1;
     const void *rows_seq, *rows_flt, *out_fn;
     if (pl.three) {
-        rows_seq = f32 ? (const void *)fft_rows3_kernel<true, 0> : (const void *)fft_rows3_kernel<false, 0>;
-        rows_flt = f32 ? (const void *)fft_rows3_kernel<true, 1> : (const void *)fft_rows3_kernel<false, 1>;
-        out_fn = f32 ? (const void *)fft_out3_kernel<true, 0> : (const void *)fft_out3_kernel<false, 0>;
+        rows_seq = rows3_kernel<0>(f32, pl.reg_rows3);
+        rows_flt = rows3_kernel<1>(f32, pl.reg_rows3);
+        out_fn = out3_kernel<0>(f32, pl.reg_rows3);
     } else {
         rows_seq = rows_kernel<0>(f32, pl.reg_rows);
         rows_flt = rows_kernel<1>(f32, pl.reg_rows);
@@ -1785,7 +1886,7 @@ int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v, const vo
         ph.h = p.hs;  // [taps][Gp] fp32, in the spectra's place until the column pass writes them
         if (st == HYENA_OK) st = launch(rows_flt, ph, pl.P_rows, row_units, 1, pl.lds_rows);
         if (st == HYENA_OK && pl.three)
-            st = launch((const void *)fft_mid_kernel<false>, ph, pl.P_mid, mid_units, 1, pl.lds_mid);
+            st = launch(mid_kernel<false>(pl.reg_mid), ph, pl.P_mid, mid_units, 1, pl.lds_mid);
         if (st == HYENA_OK) st = launch((const void *)fft_cols_kernel<0>, ph, pl.P_cols, cols, 1, pl.lds_cols);
     }
     // the sequence
@@ -1793,13 +1894,13 @@ int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v, const vo
     p.np = (int32_t)(D / 2);
     if (st == HYENA_OK) st = launch(rows_seq, p, pl.P_rows, row_units, B, pl.lds_rows);
     if (st == HYENA_OK && pl.three)
-        st = launch((const void *)fft_mid_kernel<false>, p, pl.P_mid, mid_units, B, pl.lds_mid);
+        st = launch(mid_kernel<false>(pl.reg_mid), p, pl.P_mid, mid_units, B, pl.lds_mid);
     // channel pairs inside one group (even group size): single columns
     if (st == HYENA_OK)
         st = group_size % 2 == 0 ? launch(col1_kernel(pl.reg_col1, pl.log1), p, pl.P_col1, M, B, pl.lds_col1)
                                  : launch((const void *)fft_cols_kernel<1>, p, pl.P_cols, cols, B, pl.lds_cols);
     if (st == HYENA_OK && pl.three)
-        st = launch((const void *)fft_mid_kernel<true>, p, pl.P_mid, mid_units, B, pl.lds_mid);
+        st = launch(mid_kernel<true>(pl.reg_mid), p, pl.P_mid, mid_units, B, pl.lds_mid);
     if (st == HYENA_OK) st = launch(out_fn, p, pl.P_rows, row_units, B, pl.lds_rows);
     if (st != HYENA_OK) return st;
     if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
@@ -1896,8 +1997,8 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
     const int64_t mid_units = (int64_t)pl.N1 * pl.N3;
     const void *rows_seq, *rows_flt;
     if (pl.three) {
-        rows_seq = f32 ? (const void *)fft_rows3_kernel<true, 0> : (const void *)fft_rows3_kernel<false, 0>;
-        rows_flt = f32 ? (const void *)fft_rows3_kernel<true, 1> : (const void *)fft_rows3_kernel<false, 1>;
+        rows_seq = rows3_kernel<0>(f32, pl.reg_rows3);
+        rows_flt = rows3_kernel<1>(f32, pl.reg_rows3);
     } else {
         rows_seq = rows_kernel<0>(f32, pl.reg_rows);
         rows_flt = rows_kernel<1>(f32, pl.reg_rows);
@@ -1905,9 +2006,9 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
     // the last inverse pass with each output form
     auto out_fn = [&](int mode) -> const void * {
         if (pl.three) {
-            if (mode == 0) return f32 ? (const void *)fft_out3_kernel<true, 0> : (const void *)fft_out3_kernel<false, 0>;
-            if (mode == 1) return f32 ? (const void *)fft_out3_kernel<true, 1> : (const void *)fft_out3_kernel<false, 1>;
-            return (const void *)fft_out3_kernel<true, 2>;
+            if (mode == 0) return out3_kernel<0>(f32, pl.reg_rows3);
+            if (mode == 1) return out3_kernel<1>(f32, pl.reg_rows3);
+            return out3_kernel<2>(true, pl.reg_rows3);
         }
         if (mode == 0) return out_kernel<0>(f32, pl.reg_rows);
         if (mode == 1) return out_kernel<1>(f32, pl.reg_rows);
@@ -1924,7 +2025,7 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
         ph.h = p.hs;  // [taps][Gp] fp32, in the spectra's place until the column pass writes them
         if (st == HYENA_OK) st = launch(rows_flt, ph, pl.P_rows, row_units, 1, pl.lds_rows);
         if (st == HYENA_OK && pl.three)
-            st = launch((const void *)fft_mid_kernel<false>, ph, pl.P_mid, mid_units, 1, pl.lds_mid);
+            st = launch(mid_kernel<false>(pl.reg_mid), ph, pl.P_mid, mid_units, 1, pl.lds_mid);
         if (st == HYENA_OK) st = launch((const void *)fft_cols_kernel<0>, ph, pl.P_cols, cols, 1, pl.lds_cols);
     }
     p.L = L;
@@ -1941,7 +2042,7 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
     }
     // the middle passes cover both work areas as 2B batch rows
     if (st == HYENA_OK && pl.three)
-        st = launch((const void *)fft_mid_kernel<false>, p, pl.P_mid, mid_units, 2 * B, pl.lds_mid);
+        st = launch(mid_kernel<false>(pl.reg_mid), p, pl.P_mid, mid_units, 2 * B, pl.lds_mid);
     {
         FftParams pc = p;
         pc.part = dh ? (float2 *)((char *)p.ws + 2 * pl.area_bytes) : nullptr;
@@ -1951,7 +2052,7 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
                              : launch((const void *)fft_bwd_cols_kernel, pc, pl.P_bwd, cols, B, pl.lds_bwd);
     }
     if (st == HYENA_OK && pl.three && (dq || dk))
-        st = launch((const void *)fft_mid_kernel<true>, p, pl.P_mid, mid_units, 2 * B, pl.lds_mid);
+        st = launch(mid_kernel<true>(pl.reg_mid), p, pl.P_mid, mid_units, 2 * B, pl.lds_mid);
     if (st == HYENA_OK && dq) {
         FftParams po = p;
         po.q = dy; po.y = dq;
@@ -1980,7 +2081,7 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
         pd.L = taps;
         pd.y = area_dz;
         if (st == HYENA_OK && pl.three)
-            st = launch((const void *)fft_mid_kernel<true>, pd, pl.P_mid, mid_units, 1, pl.lds_mid);
+            st = launch(mid_kernel<true>(pl.reg_mid), pd, pl.P_mid, mid_units, 1, pl.lds_mid);
         if (st == HYENA_OK) st = launch(out_fn(2), pd, pl.P_rows, row_units, 1, pl.lds_rows);
         if (st == HYENA_OK) {
             const int64_t n_tblk = (l_h + 63) / 64, n_gblk = (G + 63) / 64;

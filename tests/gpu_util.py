@@ -137,32 +137,39 @@ def transform_len(L, l_h):
 
 
 def register_fed_forms(L, D, gs, l_h):
-    """Which register-fed forms the long-filter plan takes: (rows and output,
-    single column, the backward's single column).  Transforms of 32 to 256
-    points (two-level for the rows) whose tile of pairs (at most 64, at most
-    4096 values with the backward's two sequences per pair, no wider than the
-    pairs there are) holds exactly 4096 values, 16 for each of 256 threads."""
+    """The register-fed forms the long-filter plan takes: "rows" (the row and
+    output kernels, rows3 and out3 under the three-level split), "mid" (the
+    three-level middle passes), "col1" (single column) and "bwd1" (the
+    backward's single column).  Each needs a transform of 32 to 256 points
+    whose tile of pairs (at most 64, at most 4096 values with the backward's
+    two sequences per pair, no wider than the pairs there are) holds exactly
+    4096 values, 16 for each of 256 threads."""
     N = transform_len(L, l_h)
     log_n = N.bit_length() - 1
-    if log_n > 16:  # three-level split: N1 N2 N3, every transform at most 256 points
+    three = log_n > 16
+    if three:  # N1 N2 N3, every transform at most 256 points
         log1 = (log_n + 2) // 3
         log2 = (log_n - log1 + 1) // 2
+        log3 = log_n - log1 - log2
     else:
-        log1, log2 = (log_n + 1) // 2, log_n // 2
+        log1, log2, log3 = (log_n + 1) // 2, log_n // 2, 0
 
-    def tile(m, seqs, pairs):
+    def full(log_m, seqs, pairs):
+        m = 1 << log_m
         P = 64
         while P > 1 and seqs * m * P > 4096:
             P //= 2
         while P > 1 and P // 2 >= pairs:
             P //= 2
-        return seqs * m * P
+        return 5 <= log_m <= 8 and seqs * m * P == 4096
 
     pairs = max(D // 2, (D // gs + 1) // 2)
-    rows = log_n <= 16 and 5 <= log2 <= 8 and tile(1 << log2, 1, pairs) == 4096
-    col1 = 5 <= log1 <= 8 and tile(1 << log1, 1, pairs) == 4096 and gs % 2 == 0
-    bwd1 = 5 <= log1 <= 8 and tile(1 << log1, 2, D // 2) == 4096 and gs % 2 == 0
-    return rows, col1, bwd1
+    return {
+        "rows": full(log3 if three else log2, 1, pairs),
+        "mid": three and full(log2, 1, pairs),
+        "col1": gs % 2 == 0 and full(log1, 1, pairs),
+        "bwd1": gs % 2 == 0 and full(log1, 2, D // 2),
+    }
 
 
 def run_long(q, k, v, h, gs, pad=16):

@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import gated_convolution_sequence_amd as hc
-from gpu_util import DEV, check_long_bwd, log, register_fed_forms, run_long_bwd as _run, transform_len
+from gpu_util import DEV, check_long_bwd, log, register_fed_forms, run_long_bwd as _run
 from workloads import gaussian_inputs
 
 pytestmark = pytest.mark.gpu
@@ -60,8 +60,8 @@ def test_register_fed_and_lds_forms_agree(dt):
     and each call matches the oracle."""
     dtype = DTYPES[dt]
     B, L, l_h, gs = 2, 2000, 2000, 2
-    assert register_fed_forms(L, 128, gs, l_h) == (True, True, True)
-    assert register_fed_forms(L, 32, gs, l_h) == (False, False, False)
+    wide, narrow = register_fed_forms(L, 128, gs, l_h), register_fed_forms(L, 32, gs, l_h)
+    assert wide["rows"] and wide["bwd1"] and not narrow["rows"] and not narrow["bwd1"]
     q, k, v, h = gaussian_inputs(B, L, 128, gs, l_h, dtype, seed=67)
     dy = _dy(B, L, 128, dtype, seed=71)
     log("long bwd register-fed vs LDS forms %s" % dt)
@@ -83,7 +83,8 @@ def test_register_fed_and_lds_forms_agree(dt):
 REGISTER_FED_SHAPES = [
     # B, L, D, group_size, l_h
     (2, 3000, 200, 2, 1000), (2, 5000, 136, 4, 3000), (1, 20000, 130, 2, 300), (1, 40000, 40, 8, 300),
-    (1, 70000, 128, 2, 300),     # N = 2^17, three-level: register-fed 64-point columns
+    (1, 70000, 128, 2, 300),     # N = 2^17, three-level: 64-point columns and middle passes
+    (1, 132000, 128, 2, 100),    # N = 2^18, three-level: 64 x 64 x 64, every pass register-fed
 ]
 
 
@@ -91,7 +92,7 @@ REGISTER_FED_SHAPES = [
 @pytest.mark.parametrize("B,L,D,gs,l_h", REGISTER_FED_SHAPES)
 def test_register_fed_shapes(dt, B, L, D, gs, l_h):
     forms = register_fed_forms(L, D, gs, l_h)
-    assert forms[1] and forms[2] and (forms[0] or transform_len(L, l_h) > 1 << 16)
+    assert forms["col1"] and forms["bwd1"] and (forms["rows"] or forms["mid"])
     log("long bwd register-fed %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
     dtype = DTYPES[dt]
     q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=2 * L + D + gs)

@@ -24,7 +24,7 @@ import torch
 
 import gated_convolution_sequence_amd as hc
 import oracle
-from gpu_util import DEV, check_long, log, register_fed_forms, run_long, to_np, transform_len
+from gpu_util import DEV, check_long, log, register_fed_forms, run_long, to_np
 from workloads import WORKLOADS, gaussian_inputs, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -142,8 +142,8 @@ def test_register_fed_and_lds_forms_agree(dt):
     bar, and each matches the oracle."""
     dtype = DTYPES[dt]
     B, L, l_h, gs = 2, 2000, 2000, 2
-    assert register_fed_forms(L, 128, gs, l_h)[:2] == (True, True)
-    assert register_fed_forms(L, 64, gs, l_h)[:2] == (False, False)
+    wide, narrow = register_fed_forms(L, 128, gs, l_h), register_fed_forms(L, 64, gs, l_h)
+    assert wide["rows"] and wide["col1"] and not narrow["rows"] and not narrow["col1"]
     q, k, v, h = gaussian_inputs(B, L, 128, gs, l_h, dtype, seed=61)
     log("register-fed vs LDS forms %s" % dt)
     yw = run_long(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), gs).clone()
@@ -165,7 +165,8 @@ REGISTER_FED_SHAPES = [
     (2, 5000, 136, 4, 3000),     # N = 2^13: 128 columns, 64-point rows, 68 pairs
     (1, 20000, 130, 2, 300),     # N = 2^15: 256 columns, 128-point rows, 65 pairs
     (1, 40000, 40, 8, 300),      # N = 2^16: 256 x 256, tiles of 16 pairs (16 + 4)
-    (1, 70000, 128, 2, 300),     # N = 2^17, three-level: register-fed 64-point columns
+    (1, 70000, 128, 2, 300),     # N = 2^17, three-level: 64-point columns and middle passes
+    (1, 132000, 128, 2, 100),    # N = 2^18, three-level: 64 x 64 x 64, every pass register-fed
 ]
 
 
@@ -173,7 +174,7 @@ REGISTER_FED_SHAPES = [
 @pytest.mark.parametrize("B,L,D,gs,l_h", REGISTER_FED_SHAPES)
 def test_register_fed_shapes(dt, B, L, D, gs, l_h):
     forms = register_fed_forms(L, D, gs, l_h)
-    assert forms[1] and (forms[0] or transform_len(L, l_h) > 1 << 16)
+    assert forms["col1"] and (forms["rows"] or forms["mid"])
     log("long register-fed %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
     dtype = DTYPES[dt]
     q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=L + D + gs)

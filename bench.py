@@ -769,8 +769,8 @@ def long_filter_rates(w, stream, reps):
            "us_spectra_kept": round(us_kept, 1), "kernels_spectra_kept": 3,
            "G_tok_ch_per_s_spectra_kept": round(lw.elems / (us_kept * 1e-6) / 1e9, 2),
            "backward": {"us": round(us_bwd, 1), "G_tok_ch_per_s": round(lw.elems / (us_bwd * 1e-6) / 1e9, 2),
-                        "workspace_bytes": ws_bwd, "kernels": 10,
-                        "us_spectra_kept": round(us_bwd_kept, 1), "kernels_spectra_kept": 7,
+                        "workspace_bytes": ws_bwd, "kernels": 11,
+                        "us_spectra_kept": round(us_bwd_kept, 1), "kernels_spectra_kept": 8,
                         "frac_of_peak_min_bytes": round(14 * lw.elems / (us_bwd * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
     del q, k, v, h, y, ws
     return res

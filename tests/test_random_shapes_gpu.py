@@ -14,7 +14,7 @@ import torch
 
 import gated_convolution_sequence_amd as hc
 from gpu_util import (DEV, bwd_refs, bwd_rows, check, check_bwd, check_long, check_long_bwd, log, ref_and_envelope,
-                      run, run_long, run_long_bwd, to_np)
+                      register_fed_forms, run, run_long, run_long_bwd, to_np)
 from workloads import gaussian_inputs, normal_activation
 
 pytestmark = pytest.mark.gpu
@@ -72,6 +72,15 @@ def _draw(kind, seed):
             l_h = int(rng.integers(1, 129))
             # (the span column carries the prefix length P)
             cases.append((dt, B, L, D, gs, l_h, int(rng.integers(0, 200))))
+        elif kind == "long_wide":
+            # widths whose pair tiles fill 4096 values: the register-fed forms
+            gs = int(rng.choice([2, 4, 8, 16]))
+            B = int(rng.integers(1, 3))
+            L = int(rng.integers(1000, 3001))
+            D = int(2 * rng.integers(64, 129))
+            D -= D % gs
+            l_h = int(rng.integers(1, 3001))
+            cases.append((dt, B, L, D, gs, l_h, 0))
         else:  # long filters (forward; "long_backward": shorter sequences)
             gs = int(rng.choice([1, 2, 3, 4, 8, 16]))
             D = int(np.lcm(gs, 2) * rng.integers(1, max(2, 48 // np.lcm(gs, 2)) + 1))
@@ -93,6 +102,14 @@ LONG = _draw("long", 404)
 BACKWARD_OFF = _draw("backward_off_tile", 505)
 HALO = _draw("halo", 606)
 LONG_BWD = _draw("long_backward", 707)
+LONG_WIDE = _draw("long_wide", 808)
+
+
+def test_wide_draw_reaches_the_register_fed_forms():
+    """Most wide long-filter cases take the register-fed row and column forms."""
+    forms = [register_fed_forms(L, D, gs, l_h) for _, _, L, D, gs, l_h, _ in LONG_WIDE]
+    assert sum(f["rows"] for f in forms) >= N_CASES // 2
+    assert sum(f["col1"] and f["bwd1"] for f in forms) >= N_CASES // 2
 
 
 @pytest.mark.parametrize("dt,B,L,D,gs,l_h,span", GROUPED, ids=_ids(GROUPED))
@@ -181,3 +198,17 @@ def test_random_long_filter_backward(dt, B, L, D, gs, l_h, span):
     dy = normal_activation((B, L, D), dtype, "cpu", seed=L + 2 * l_h + 1)
     got = run_long_bwd(*(t.to(DEV) for t in (q, k, v, h, dy)), gs)
     check_long_bwd(got, q, k, v, h, dy, gs, dtype, "random long backward")
+
+
+@pytest.mark.parametrize("dt,B,L,D,gs,l_h,span", LONG_WIDE, ids=_ids(LONG_WIDE))
+def test_random_long_filter_wide(dt, B, L, D, gs, l_h, span):
+    """Widths that fill the FFT tiles (register-fed forms), forward and backward."""
+    log("random wide long filter %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))
+    dtype = DTYPES[dt]
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=B * 6007 + L * 37 + D + 5 * l_h)
+    dy = normal_activation((B, L, D), dtype, "cpu", seed=L + 3 * l_h + 2)
+    qd, kd, vd, hd = (t.to(DEV) for t in (q, k, v, h))
+    y = run_long(qd, kd, vd, hd, gs)
+    check_long(y, q, k, v, h, gs, dtype, "random wide long filter")
+    got = run_long_bwd(qd, kd, vd, hd, dy.to(DEV), gs)
+    check_long_bwd(got, q, k, v, h, dy, gs, dtype, "random wide long backward")

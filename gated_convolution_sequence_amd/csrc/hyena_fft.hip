@@ -445,6 +445,13 @@ template <int R> __device__ __forceinline__ void fft_reg_perm(float2 (&v)[kFftRe
 #define HYENA_FFT_BATCH 8
 #endif
 constexpr int kBatch = HYENA_FFT_BATCH;  // also the batch of the filter-spectrum loads
+// Filter counts up to this read h [G][l_h] directly in the filter pass (one
+// element per filter row; the rows are shared through L2); more filters are
+// first transposed to fp32 [taps][G'], so each pair is one 8-byte read.
+#ifndef HYENA_FFT_DIRECT_FILTERS
+#define HYENA_FFT_DIRECT_FILTERS 512
+#endif
+constexpr int64_t kFftDirectFilters = HYENA_FFT_DIRECT_FILTERS;
 template <int NB, typename Load>
 __device__ inline void stage_in_nb(float2 *dst, int n, Load load) {
     for (int base = 0; base < n; base += NB * kFftThreads) {
@@ -468,9 +475,10 @@ __device__ inline void stage_in(float2 *dst, int n, Load load) {
 
 // Input pair j at row t, zero past the end of the sequence or the pairs:
 // (x[2j], x[2j+1]) with x = k v (SRC = 0, batch row b), or (h[2j][t],
-// h[2j+1][t]) (SRC = 1, the filters; zero for a filter past the last).  The
-// loads always go to a valid address (row 0, pair 0 when out of range) and
-// the value is then replaced by zero.
+// h[2j+1][t]) (the filters; zero for a filter past the last) from the
+// transposed fp32 copy (SRC = 1) or from h [G][l_h] itself (SRC = 2: one
+// element per filter row).  The loads always go to a valid address (row 0,
+// pair 0 when out of range) and the value is then replaced by zero.
 template <bool F32, int SRC>
 __device__ inline float2 load_pair(const FftParams &p, int b, int64_t t, int j) {
     const bool ok = t < p.L && j < p.np;
@@ -490,11 +498,23 @@ __device__ inline float2 load_pair(const FftParams &p, int b, int64_t t, int j) 
             a = __uint_as_float(kk << 16) * __uint_as_float(vv << 16);
             c = __uint_as_float(kk & 0xffff0000u) * __uint_as_float(vv & 0xffff0000u);
         }
-    } else {
+    } else if constexpr (SRC == 1) {
         // the filters transposed to fp32 [taps][Gp] (fft_filter_transpose_kernel)
         const float2 hh = *(const float2 *)((const float *)p.h + (size_t)tc * p.Gp + 2 * (size_t)jc);
         a = hh.x;
         c = hh.y;
+    } else {
+        // the filters as given, [G][l_h]; filter 2j + 1 = G (odd G) is zero
+        const bool two = 2 * jc + 1 < p.G;
+        const size_t o0 = (size_t)(2 * jc) * (size_t)p.l_h + (size_t)tc, o1 = two ? o0 + (size_t)p.l_h : o0;
+        if constexpr (F32) {
+            a = ((const float *)p.h)[o0];
+            c = ((const float *)p.h)[o1];
+        } else {
+            a = __uint_as_float((uint32_t)((const uint16_t *)p.h)[o0] << 16);
+            c = __uint_as_float((uint32_t)((const uint16_t *)p.h)[o1] << 16);
+        }
+        c = two ? c : 0.0f;
     }
     return ok ? make_float2(a, c) : make_float2(0.0f, 0.0f);
 }
@@ -1863,13 +1883,14 @@ int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v, const vo
     const int64_t M = (int64_t)pl.N2 * pl.N3;  // columns
     const int64_t cols = M / 2 + 1;
     const void *rows_seq, *rows_flt, *out_fn;
+    const bool direct_filters = G <= kFftDirectFilters;
     if (pl.three) {
         rows_seq = rows3_kernel<0>(f32, pl.reg_rows3);
-        rows_flt = rows3_kernel<1>(f32, pl.reg_rows3);
+        rows_flt = direct_filters ? rows3_kernel<2>(f32, pl.reg_rows3) : rows3_kernel<1>(f32, pl.reg_rows3);
         out_fn = out3_kernel<0>(f32, pl.reg_rows3);
     } else {
         rows_seq = rows_kernel<0>(f32, pl.reg_rows);
-        rows_flt = rows_kernel<1>(f32, pl.reg_rows);
+        rows_flt = direct_filters ? rows_kernel<2>(f32, pl.reg_rows) : rows_kernel<1>(f32, pl.reg_rows);
         out_fn = out_kernel<0>(f32, pl.reg_rows);
     }
     // units per batch row of the row and output kernels: t1 (x t2 when three-level)
@@ -1882,8 +1903,10 @@ int hyena_conv_fwd_long_ex(const void *q, const void *k, const void *v, const vo
         FftParams ph = p;
         ph.L = l_h < L ? l_h : L;
         ph.np = p.Gp / 2;
-        st = transpose_filters(h, f32, p.G, p.Gp, l_h, ph.L, p.hs, s);
-        ph.h = p.hs;  // [taps][Gp] fp32, in the spectra's place until the column pass writes them
+        if (!direct_filters) {
+            st = transpose_filters(h, f32, p.G, p.Gp, l_h, ph.L, p.hs, s);
+            ph.h = p.hs;  // [taps][Gp] fp32, in the spectra's place until the column pass writes them
+        }
         if (st == HYENA_OK) st = launch(rows_flt, ph, pl.P_rows, row_units, 1, pl.lds_rows);
         if (st == HYENA_OK && pl.three)
             st = launch(mid_kernel<false>(pl.reg_mid), ph, pl.P_mid, mid_units, 1, pl.lds_mid);
@@ -1996,12 +2019,13 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
     const int64_t row_units = pl.three ? (int64_t)pl.N1 * pl.N2 : pl.N1;
     const int64_t mid_units = (int64_t)pl.N1 * pl.N3;
     const void *rows_seq, *rows_flt;
+    const bool direct_filters = G <= kFftDirectFilters;
     if (pl.three) {
         rows_seq = rows3_kernel<0>(f32, pl.reg_rows3);
-        rows_flt = rows3_kernel<1>(f32, pl.reg_rows3);
+        rows_flt = direct_filters ? rows3_kernel<2>(f32, pl.reg_rows3) : rows3_kernel<1>(f32, pl.reg_rows3);
     } else {
         rows_seq = rows_kernel<0>(f32, pl.reg_rows);
-        rows_flt = rows_kernel<1>(f32, pl.reg_rows);
+        rows_flt = direct_filters ? rows_kernel<2>(f32, pl.reg_rows) : rows_kernel<1>(f32, pl.reg_rows);
     }
     // the last inverse pass with each output form
     auto out_fn = [&](int mode) -> const void * {
@@ -2021,8 +2045,10 @@ int hyena_conv_bwd_long_ex(const void *q, const void *k, const void *v, const vo
         FftParams ph = p;
         ph.L = taps;
         ph.np = p.Gp / 2;
-        st = transpose_filters(h, f32, p.G, p.Gp, l_h, taps, p.hs, s);
-        ph.h = p.hs;  // [taps][Gp] fp32, in the spectra's place until the column pass writes them
+        if (!direct_filters) {
+            st = transpose_filters(h, f32, p.G, p.Gp, l_h, taps, p.hs, s);
+            ph.h = p.hs;  // [taps][Gp] fp32, in the spectra's place until the column pass writes them
+        }
         if (st == HYENA_OK) st = launch(rows_flt, ph, pl.P_rows, row_units, 1, pl.lds_rows);
         if (st == HYENA_OK && pl.three)
             st = launch(mid_kernel<false>(pl.reg_mid), ph, pl.P_mid, mid_units, 1, pl.lds_mid);

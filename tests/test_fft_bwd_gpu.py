@@ -103,6 +103,19 @@ def test_register_fed_shapes(dt, B, L, D, gs, l_h):
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_many_filters(dt):
+    """Over 512 filters (G = 1040, group size 2) the filter pass transposes
+    them first; all four gradients against the oracle."""
+    dtype = DTYPES[dt]
+    B, L, D, gs, l_h = 1, 1500, 2080, 2, 1500
+    log("long bwd many filters %s" % dt)
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=89)
+    dy = _dy(B, L, D, dtype, seed=97)
+    got = _run(*(t.to(DEV) for t in (q, k, v, h, dy)), gs)
+    check_long_bwd(got, q, k, v, h, dy, gs, dtype, "long bwd many filters")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("B,L,D,gs,l_h", SHAPES)
 def test_long_backward_gaussian(dt, B, L, D, gs, l_h):
     log("long bwd %s B=%d L=%d D=%d gs=%d l_h=%d" % (dt, B, L, D, gs, l_h))

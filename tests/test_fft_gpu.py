@@ -183,6 +183,19 @@ def test_register_fed_shapes(dt, B, L, D, gs, l_h):
     log("  rel err %.3e" % rel)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_many_filters(dt):
+    """Over 512 filters the filter pass first transposes them to fp32
+    [taps][G'] (fewer are read from h [G][l_h] directly): G = 1024 here, one
+    filter per channel, against the oracle."""
+    dtype = DTYPES[dt]
+    B, L, D, gs, l_h = 1, 2000, 1024, 1, 2000
+    log("long many filters %s" % dt)
+    q, k, v, h = gaussian_inputs(B, L, D, gs, l_h, dtype, seed=83)
+    y = run_long(q.to(DEV), k.to(DEV), v.to(DEV), h.to(DEV), gs)
+    check_long(y, q, k, v, h, gs, dtype, "many filters")
+
+
 def test_deterministic_and_workspace_reuse():
     B, L, D, gs, l_h = 1, 3000, 64, 2, 3000
     q, k, v, h = (t.to(DEV) for t in gaussian_inputs(B, L, D, gs, l_h, torch.bfloat16, seed=9))

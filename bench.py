@@ -341,15 +341,15 @@ def main():
 
     # ---- one filter per channel (chunk-direction kernel), same layers -------
     if not args.skip_chunk_direction:
-        out["chunk_direction"] = chunk_direction_rates(layers, sets, stream, max(10, K // 4))
+        out["chunk_direction"] = chunk_direction_rates(layers, sets, stream, max(MIN_EVENT_STEPS, K))
 
     # ---- a long filter (FFT convolution path), at the first layer's shape --
     if not args.skip_long_filter:
-        out["long_filter"] = long_filter_rates(layers[0], stream, max(5, K // 20))
+        out["long_filter"] = long_filter_rates(layers[0], stream, max(MIN_EVENT_STEPS, K))
 
     # ---- backward of each layer (outside the forward step's timed region)
     if not args.skip_backward:
-        out["backward"] = backward_rates(layers, sets, stream, max(5, K // 8))
+        out["backward"] = backward_rates(layers, sets, stream, max(MIN_EVENT_STEPS, K))
 
     if args.halo:
         out["halo_shard"] = halo_shard_rate(layers[-1], sets[-1], stream, max(20, K // 4))
@@ -380,7 +380,7 @@ def main():
         torch.cuda.empty_cache()
         out["extra_shapes"] = {
             "mr_b4": batched_mr_rate(stream, max(MIN_EVENT_STEPS, K)),
-            "long_stripe": long_stripe_rate(stream, max(10, K // 2)),
+            "long_stripe": long_stripe_rate(stream, max(MIN_EVENT_STEPS, K)),
         }
     print(json.dumps(out), flush=True)
 
@@ -761,15 +761,17 @@ def long_filter_rates(w, stream, reps):
     ws_bwd = ws_b.numel()
     del dy, ws_b
     moved = 40 * lw.elems
+    # the filter pass reads h directly up to 512 filters, else transposes it first
+    n_filter = 2 if lw.D // lw.group_size <= 512 else 3
     res = {"B": lw.B, "L": lw.L, "D": lw.D, "group_size": lw.group_size, "l_h": lw.l_h,
            "us": round(us, 1), "G_tok_ch_per_s": round(lw.elems / (us * 1e-6) / 1e9, 2),
            "moved_bytes_model": moved, "GBs_moved": round(moved / (us * 1e-6) / 1e9, 1),
            "frac_of_peak_moved": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-           "workspace_bytes": ws_n, "kernels": 6,
+           "workspace_bytes": ws_n, "kernels": 3 + n_filter, "calls_averaged": reps,
            "us_spectra_kept": round(us_kept, 1), "kernels_spectra_kept": 3,
            "G_tok_ch_per_s_spectra_kept": round(lw.elems / (us_kept * 1e-6) / 1e9, 2),
            "backward": {"us": round(us_bwd, 1), "G_tok_ch_per_s": round(lw.elems / (us_bwd * 1e-6) / 1e9, 2),
-                        "workspace_bytes": ws_bwd, "kernels": 11,
+                        "workspace_bytes": ws_bwd, "kernels": 8 + n_filter,
                         "us_spectra_kept": round(us_bwd_kept, 1), "kernels_spectra_kept": 8,
                         "frac_of_peak_min_bytes": round(14 * lw.elems / (us_bwd * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}}
     del q, k, v, h, y, ws

@@ -1689,10 +1689,15 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
             xoff[ks] = (int)((((r / T::VEC) ^ (unsigned)(w & 7))) << 4) + (int)(r % T::VEC) * T::EB;
         }
         __syncthreads();
+        // The wave's channels are one 16-byte row segment and the host keeps
+        // D a whole number of segments, so they lie all inside D or all past
+        // it: one wave-uniform test, and no branch between channels (their
+        // reads and matrix-core chains overlap).
+        const bool wave_in = (int)__builtin_amdgcn_readfirstlane(c_begin + w * T::CPW) < p.D;
 #pragma unroll
         for (int cl = 0; cl < T::CPW; ++cl) {
+            if (!wave_in) break;
             const int dl = w * T::CPW + cl;
-            if (c_begin + dl >= p.D) break;
             const unsigned char *xrow = xr + dl * T::RING_B;
             const uint32_t *ptr = pt + dl * PTN;  // reversed tap table of this channel
             f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};

@@ -163,9 +163,11 @@ def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cop
            "layers": layers,
            "commands": [
                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o run -- "
-               "python3 bench.py --steps 8 --warmup 2 --skip-cpu-baseline --skip-naive --skip-extra-shapes",
+               "python3 bench.py --steps 8 --warmup 2 --skip-cpu-baseline --skip-naive --skip-extra-shapes "
+               "--skip-stream-reference",
                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o run -- "
-               "python3 bench.py --steps 8 --warmup 2 --skip-cpu-baseline --skip-naive --skip-extra-shapes",
+               "python3 bench.py --steps 8 --warmup 2 --skip-cpu-baseline --skip-naive --skip-extra-shapes "
+               "--skip-stream-reference",
                "rocprofv3 --pmc FETCH_SIZE ... -- python3 bench.py --calibrate-copy-mib %d" % copy_mib,
                "rocprofv3 --pmc WRITE_SIZE ... -- python3 bench.py --calibrate-copy-mib %d" % copy_mib]}
     with open(TRAFFIC_FILE, "w") as f:
@@ -187,8 +189,16 @@ def calibrate_copy(mib: int, reps: int = 10):
 
 
 def source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 of the kernel source's code: comments, blank lines and trailing
+    spaces removed, so that a comment edit keeps the counters current while any
+    change to the code itself makes them stale."""
+    import re
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.rstrip() for line in text.split("\n") if line.strip())
+    return hashlib.sha256(code.encode("utf-8")).hexdigest()
 
 
 def measured_traffic(layer: str):

@@ -44,6 +44,11 @@
 //   * The epilogue stages the fp32 accumulators (4 consecutive channels per
 //     lane) through a swizzled LDS tile, reads them row-major, multiplies by
 //     q, rounds to bf16 and writes 16 bytes per lane.
+//   * The 16-wave form for filters over 33 taps has no registers to keep
+//     the B fragments or earlier chunks' fragments: it builds each B
+//     fragment from a table of tap pairs in LDS right before the MFMAs that
+//     use it, walks odd spans backwards in time, and gates its accumulators
+//     in the MFMA layout (q read from LDS) before staging bf16 y.
 //   * Buffer resources bound every access: rows before the batch start or
 //     past the span, and channels past D, read as zero and are never
 //     written.  That supplies X_{-1} = 0, ragged last chunks and partial slabs.

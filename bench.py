@@ -22,7 +22,7 @@ Reported (one JSON line):
                region; the timed region itself carries events in every 5th
                step, reported beside), against the 8 TB/s HBM3E peak; `traffic` is the
                measured HBM bytes per launch from the committed rocprofv3
-               counter summary, or null if the kernel source changed since;
+               counter summary, or null if the kernel code changed since;
   layers       the same figures for each layer's kernel;
   chunk_direction  each layer with one filter per channel: the direct kernel
                (8 taps or fewer; with its backward) or the chunk-direction

@@ -1366,11 +1366,23 @@ __global__ __launch_bounds__(256) void hyena_bwd_dh_reduce_kernel(const float *w
     const int idx = blockIdx.x * 256 + threadIdx.x;
     if (idx >= G * l_h) return;
     const int g = idx / l_h, s = idx % l_h;
+    // term n = r * tiles_per_group + t (partial row r, tile t of the group),
+    // added in that order; eight loads in flight before their adds
+    const int n_terms = rows * tiles_per_group;
+    auto term = [&](int n) -> float {
+        const int r = n / tiles_per_group, t = n % tiles_per_group;
+        return ws[((size_t)r * tiles + (size_t)g * tiles_per_group + t) * l_h + s];
+    };
     float acc = 0.0f;
-    for (int r = 0; r < rows; ++r) {
-        const float *row = ws + (size_t)r * tiles * l_h;
-        for (int t = 0; t < tiles_per_group; ++t) acc += row[(size_t)(g * tiles_per_group + t) * l_h + s];
+    int n = 0;
+    for (; n + 8 <= n_terms; n += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = term(n + u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
     }
+    for (; n < n_terms; ++n) acc += term(n);
     dh[idx] = acc;
 }
 

@@ -2344,6 +2344,186 @@ __global__ __launch_bounds__(512) void hyena_bwd_dh_lag_kernel(DhParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same partial filter gradients in bf16 on the matrix cores.  For one
+// channel, with dz = dy q and x = k v each rounded once to bf16 (the
+// grouped kernels' dh operands), take an input step of 32 rows from t0 and
+//     D[i][j] = sum_{k<32} x[t0 - 8 i + k] * dz[t0 + j + k],
+// the product of A[i][k] = x[t0 - 8 i + k] (16 x 32) and B[k][j] =
+// dz[t0 + j + k] (32 x 16), i.e. v_mfma_f32_16x16x32_bf16.  Every term of
+// D[i][j] pairs dz at time t with x at t - s for the one lag s = 8 i + j, so
+// the columns j < 8 give each lag s < 128 once (the columns j >= 8 are not
+// used), and steps t0 = S0 - 32, S0, ..., 32 apart, with dz zero outside the
+// span's rows [S0, S1), sum every term of the span exactly once.  One MFMA
+// per channel and 32 rows replaces 32 * 128 fp32 multiply-adds, and each
+// accumulator element already holds one lag: no diagonal sums.
+//
+// A workgroup owns kLagCh channels and a span (as the fp32 kernel), walked
+// in 128-row blocks; wave w takes channels 8 w .. 8 w + 7.  In LDS each
+// channel has a time ring of x (512 rows, 16-byte aligned runs of 8 times,
+// so an A operand is one 16-byte read) and two rings of dz as dword pairs,
+// (dz[2m], dz[2m+1]) and (dz[2m+1], dz[2m+2]), so that a B operand, which
+// starts at any time, is four dwords of one of them; four dwords past each
+// dz ring's end repeat its first four, so those four never wrap.  Rings are
+// rotated by 16 bytes per channel segment (channel / 8) so that one staging
+// write of a wave (8 segments x 8 row pairs) covers the banks evenly.  A
+// thread loads two consecutive rows of one 16-byte channel segment; the
+// next block's rows are loaded while this block's steps run.
+// ---------------------------------------------------------------------------
+constexpr int kLmBlock = 128;       // rows per block
+constexpr int kLmXRing = 512;       // x ring, times per channel
+constexpr int kLmZDw = 128;         // dz ring, dwords per copy (256 times)
+constexpr int kLmZPitch = 2 * (kLmZDw + 4);  // dz dwords per channel (two copies, each with 4 repeated)
+
+__global__ __launch_bounds__(512) void hyena_bwd_dh_lag_mfma_kernel(DhParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t xr[kLagCh * kLmXRing];
+    __shared__ __attribute__((aligned(16))) uint32_t zr[kLagCh * kLmZPitch];
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int n16 = l & 15, q4 = l >> 4;
+    int bid = blockIdx.x;
+    const int slab = bid % p.n_slabs;
+    bid /= p.n_slabs;
+    const int spn = bid % p.n_spans;
+    const int b = bid / p.n_spans;
+    const int64_t S0 = (int64_t)spn * p.span_rows;
+    const int64_t S1 = min(p.L, S0 + (int64_t)p.span_rows);
+    const int nblk = (int)((S1 - S0 + kLmBlock - 1) / kLmBlock);
+    const int c_begin = slab * kLagCh;
+    const int row_bytes = p.D * 2;
+    const size_t batch_off = (size_t)b * (size_t)p.L * (size_t)row_bytes + (size_t)c_begin * 2;
+
+    // loader role: rows 2 rg, 2 rg + 1 of a block, channels 8 sg .. 8 sg + 7
+    const int sg = tid & 7, rg = tid >> 3;
+    const bool seg_ok = c_begin + sg * 8 < p.D;
+    // rows [r_lo, r_hi) of a tensor (0 <= r_lo <= r_hi <= L): this thread's
+    // rows r0 + 2 rg and r0 + 2 rg + 1, zero outside the window
+    auto load2 = [&](const void *base, int64_t r0, int64_t r_lo, int64_t r_hi, u32x4_t *dst, auto pol_tag) {
+        constexpr int pol = decltype(pol_tag)::value;
+        const int n = (int)(r_hi - r_lo) * row_bytes - c_begin * 2;
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc((const char *)base + batch_off + (size_t)r_lo * (size_t)row_bytes, (uint32_t)(n > 0 ? n : 0));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int64_t r = r0 + 2 * rg + u;
+            const uint32_t o = (seg_ok && r >= r_lo && r < r_hi) ? (uint32_t)((r - r_lo) * row_bytes + sg * 16) : kOOB;
+            dst[u] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, o, 0, pol));
+        }
+    };
+    const std::integral_constant<int, 0> kAlloc;              // L2-allocating loads
+    const std::integral_constant<int, kLoadPolicy> kStream;   // streaming loads
+    // bf16 (round to nearest even) of the fp32 product of channel e of a, c
+    auto prod = [](const u32x4_t &a, const u32x4_t &c, int e) -> uint32_t {
+        const float f = (e & 1) ? bf_hi(a[e >> 1]) * bf_hi(c[e >> 1]) : bf_lo(a[e >> 1]) * bf_lo(c[e >> 1]);
+        return pack_bf16(f, 0.0f) & 0xffffu;
+    };
+    // x of times t, t + 1 (t even) for this thread's 8 channels -> x ring
+    auto put_x = [&](int64_t t, const u32x4_t *kk, const u32x4_t *vv) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int ch = sg * 8 + e;
+            const uint32_t d = prod(kk[0], vv[0], e) | (prod(kk[1], vv[1], e) << 16);
+            const int pe = (int)((t + 8 * sg) & (kLmXRing - 1));
+            *(uint32_t *)(&xr[ch * kLmXRing + pe]) = d;
+        }
+    };
+    // dz of times t, t + 1 (t even) -> both dz rings (and their repeats)
+    auto put_z = [&](int64_t t, const u32x4_t *dd, const u32x4_t *qq) {
+        const int m = (int)(t >> 1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int ch = sg * 8 + e;
+            const uint32_t z0 = prod(dd[0], qq[0], e), z1 = prod(dd[1], qq[1], e);
+            uint32_t *z = zr + ch * kLmZPitch;
+            const int p0 = (m + 4 * sg) & (kLmZDw - 1);        // copy 0: (dz[t], dz[t+1])
+            z[p0] = z0 | (z1 << 16);
+            if (p0 < 4) z[kLmZDw + p0] = z0 | (z1 << 16);
+            uint16_t *z1h = (uint16_t *)(z + kLmZDw + 4);       // copy 1: (dz[2m'+1], dz[2m'+2])
+            const int ph = (m - 1 + 4 * sg) & (kLmZDw - 1);      // dz[t]: upper half of pair t/2 - 1
+            const int pl = (m + 4 * sg) & (kLmZDw - 1);          // dz[t+1]: lower half of pair t/2
+            z1h[2 * ph + 1] = (uint16_t)z0;
+            if (ph < 4) z1h[2 * (kLmZDw + ph) + 1] = (uint16_t)z0;
+            z1h[2 * pl] = (uint16_t)z1;
+            if (pl < 4) z1h[2 * (kLmZDw + pl)] = (uint16_t)z1;
+        }
+    };
+
+    // dz rings start at zero (times before the span read as zero); the 160
+    // rows of x before the span (zero before row 0)
+    for (int i = tid; i < kLagCh * kLmZPitch; i += 512) zr[i] = 0u;
+    {
+        u32x4_t kk[2], vv[2];
+        const int64_t lo = max((int64_t)0, S0 - 160);
+        load2(p.k, S0 - 128, lo, S0, kk, kAlloc);
+        load2(p.v, S0 - 128, lo, S0, vv, kAlloc);
+        put_x(S0 - 128 + 2 * rg, kk, vv);
+        if (rg < 16) {
+            load2(p.k, S0 - 160, lo, S0, kk, kAlloc);
+            load2(p.v, S0 - 160, lo, S0, vv, kAlloc);
+            put_x(S0 - 160 + 2 * rg, kk, vv);
+        }
+    }
+    u32x4_t dy_r[2], q_r[2], k_r[2], v_r[2];
+    auto load_blk = [&](int blk) {
+        const int64_t r0 = S0 + (int64_t)blk * kLmBlock;
+        load2(p.dy, r0, S0, S1, dy_r, kStream);
+        load2(p.q, r0, S0, S1, q_r, kStream);
+        // k and v allocate in L2: the next span reads its last rows as history
+        load2(p.k, r0, S0, S1, k_r, kAlloc);
+        load2(p.v, r0, S0, S1, v_r, kAlloc);
+    };
+    load_blk(0);
+    __syncthreads();  // the dz rings are zero before any block writes them
+
+    // the wave's channels lie all inside D or all past it (D is a whole
+    // number of 8-channel segments)
+    const int ch0 = w * 8;
+    const bool wave_in = (int)__builtin_amdgcn_readfirstlane(c_begin + ch0) < p.D;
+    f32x4_t acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int rot = 8 * (ch0 >> 3);  // the wave's channels share one segment (rotation)
+    for (int blk = 0; blk <= nblk; ++blk) {
+        const int64_t bs = S0 + (int64_t)blk * kLmBlock;
+        // this block's rows (past the span, or the block after the last: zeros)
+        put_x(bs + 2 * rg, k_r, v_r);
+        put_z(bs + 2 * rg, dy_r, q_r);
+        if (blk < nblk) load_blk(blk + 1);  // the block after the last: an empty window
+        __syncthreads();
+        const int nk = blk < nblk ? kLmBlock / 32 : 1;
+        if (wave_in) {
+            for (int ks = 0; ks < nk; ++ks) {
+                const int64_t t0 = bs - 32 + 32 * ks;
+                // A: x[t0 - 8 n16 + 8 q4 .. + 7]; B: dz[t0 + n16 + 8 q4 .. + 7]
+                const int pa = (int)((t0 - 8 * n16 + 8 * q4 + rot) & (kLmXRing - 1));
+                const int64_t e0 = t0 + n16 + 8 * q4;
+                const int par = (int)(e0 & 1);
+                const int pb = par * (kLmZDw + 4) + (int)(((e0 - par) / 2 + 4 * (ch0 >> 3)) & (kLmZDw - 1));
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const u32x4_t av = *(const u32x4_t *)(&xr[(ch0 + c) * kLmXRing + pa]);
+                    const uint32_t *zb = zr + (ch0 + c) * kLmZPitch + pb;
+                    const u32x4_t bv = {zb[0], zb[1], zb[2], zb[3]};
+                    acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                                     __builtin_bit_cast(bf16x8_t, bv), acc[c], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();  // the rings' oldest entries are rewritten next
+    }
+    // lane (n16, q4), element r: lag 8 (4 q4 + r) + n16 (columns n16 < 8)
+    if (wave_in && n16 < 8) {
+        float *ws = p.ws + ((size_t)(b * p.n_spans + spn) * p.D + c_begin + ch0) * p.l_h;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = 8 * (4 * q4 + r) + n16;
+                if (s < p.l_h) ws[(size_t)c * p.l_h + s] = acc[c][r];
+            }
+    }
+}
+
 // Kernel families and their compiled span counts (indices into kSpans).
 enum Family { kFwd = 0, kRevDual = 1, kDh = 2, kCd = 3, kDqDh = 4, kBwd = 5, kCdRevDual = 6 };
 // (the chunk-direction kernel takes its span at run time: one entry)
@@ -2590,12 +2770,17 @@ template <bool F32> DhFn pick_lag(int ng2) {
 // kLagCh channels and kLagSpanRows rows (fewer for a shorter sequence) per
 // workgroup; `kh` holds the tap groups of 16 the kernel sums (a power of 2,
 // NG2) and `span` the span in 64-row chunks.
-int lag_plan(int64_t B, int64_t L, int64_t D, int64_t l_h, Plan *pl) {
+int lag_plan(int64_t B, int64_t L, int64_t D, int64_t l_h, int dtype, Plan *pl) {
     if (D > INT32_MAX / 16) return HYENA_ERR_UNSUPPORTED;
     const int ng = (int)((l_h + 15) / 16);
     pl->kh = ng <= 1 ? 1 : ng <= 2 ? 2 : ng <= 4 ? 4 : 8;
     pl->n_chunks = (L + kChunk - 1) / kChunk;
-    const int64_t rows = min((int64_t)kLagSpanRows, pl->n_chunks * kChunk);
+    // a span's byte window (its rows, or the 160 rows of history before it)
+    // is addressed with 32-bit offsets: shorter spans for very wide rows
+    const int64_t row_bytes = D * (dtype == HYENA_DTYPE_F32 ? 4 : 2);
+    const int64_t fit = ((kMaxWindowBytes - 1) / row_bytes - 160) / kChunk * kChunk;
+    if (fit < kChunk) return HYENA_ERR_UNSUPPORTED;
+    const int64_t rows = min(min((int64_t)kLagSpanRows, fit), pl->n_chunks * kChunk);
     pl->span_index = 0;
     pl->span = rows / kChunk;
     pl->n_spans = (L + rows - 1) / rows;
@@ -2753,7 +2938,7 @@ static int fwd_launch(const void *q, const void *k, const void *v, const void *h
 static int dh_plan(int64_t B, int64_t L, int64_t D, int64_t group_size, int64_t l_h, int dtype,
                    Plan *pl, int64_t *ws_bytes) {
     if (group_size % kTile != 0) {
-        int st = l_h <= kDirTaps ? dir_plan(B, L, D, l_h, dtype, 0, pl) : lag_plan(B, L, D, l_h, pl);
+        int st = l_h <= kDirTaps ? dir_plan(B, L, D, l_h, dtype, 0, pl) : lag_plan(B, L, D, l_h, dtype, pl);
         if (st != HYENA_OK) return st;
         if ((D * (dtype == HYENA_DTYPE_F32 ? 4 : 2)) % 16 != 0) return HYENA_ERR_UNSUPPORTED;
         *ws_bytes = B * pl->n_spans * D * l_h * (int64_t)sizeof(float);
@@ -2897,7 +3082,7 @@ static int bwd_entry(const void *q, const void *k, const void *v, const void *h,
             p.n_slabs = (int32_t)dpl.n_slabs;
             p.group_size = (int32_t)group_size;
             p.span_rows = (int32_t)(dpl.span * kChunk);
-            DhFn fn = f32 ? pick_lag<true>(dpl.kh) : pick_lag<false>(dpl.kh);
+            DhFn fn = f32 ? pick_lag<true>(dpl.kh) : hyena_bwd_dh_lag_mfma_kernel;
             hipLaunchKernelGGL(fn, dim3((unsigned)dpl.workgroups), dim3(512), 0, (hipStream_t)stream, p);
             if (hipGetLastError() != hipSuccess) return HYENA_ERR_LAUNCH;
             const int G = (int)(D / group_size);

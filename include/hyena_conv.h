@@ -143,8 +143,9 @@ int hyena_conv_fwd_halo(const void *q, const void *k, const void *v,
  * reports (16-byte aligned, contents need not be initialised); it is
  * overwritten.  Outputs and workspace must not overlap the inputs or each
  * other.  bf16 precision as the forward: dz and x are rounded once to bf16
- * as matrix-core operands, sums are fp32, outputs rounded once.  Results are
- * the same run to run.  In bf16 a call with all four outputs reads q, k, v
+ * as matrix-core operands (off the 16-channel grouping with at most 8 taps,
+ * the direct sums keep them in fp32), sums are fp32, outputs rounded once.
+ * Results are the same run to run.  In bf16 a call with all four outputs reads q, k, v
  * and dy once; a call with fewer takes other kernels, whose fp32 sums may
  * group the same terms differently (dq, dh: last-place differences; fp32
  * calls give the same bits either way). */

@@ -278,6 +278,14 @@ def test_backward_workspace_size():
         assert hc.bwd_workspace_bytes(B, L, D, gs, l_h) == B * (-(-L // 1024)) * D * l_h * 4
     with pytest.raises(hc.HyenaError):
         hc.bwd_workspace_bytes(1, 8192, 12, 3, 9)
+    # very wide rows: the lag-product pass addresses a span's rows, and the
+    # 160 rows of history before it, with 32-bit byte offsets, so its spans
+    # shrink in 64-row chunks to keep that window below 2^31 bytes
+    D = 1 << 20
+    for code, eb in ((hc.DTYPE_BF16, 2), (hc.DTYPE_F32, 4)):
+        rows = ((2 ** 31 - 1) // (eb * D) - 160) // 64 * 64
+        assert rows in (832, 320)
+        assert hc.bwd_workspace_bytes(1, 8192, D, 8, 100, code) == (-(-8192 // rows)) * D * 100 * 4
 
 
 def _long(q=P["q"], k=P["k"], v=P["v"], h=P["h"], B=1, L=128, D=64, gs=16, l_h=1000,

@@ -25,8 +25,8 @@ Reported (one JSON line):
                counter summary, or null if the kernel code changed since;
   layers       the same figures for each layer's kernel;
   chunk_direction  each layer with one filter per channel: the direct kernel
-               (8 taps or fewer; with its backward) or the chunk-direction
-               GEMM kernel;
+               (8 taps or fewer) or the chunk-direction GEMM kernel, each
+               with its backward;
   long_filter  a filter as long as the sequence (the FFT path), with the
                filter spectra computed per call and kept across calls, and
                its backward (dq, dk, dv, dh);
@@ -668,14 +668,16 @@ def chunk_direction_rates(layers, sets, stream, reps):
                                 "hbm_frac": round(alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                                 "span_chunks": span, "workgroups": wgs,
                                 "kernel": ("hyena_fwd_direct_kernel" if w.l_h <= 8 else "hyena_fwd_cd_kernel")}
-        if w.l_h <= 8:
-            res[w.name + "_gs1"]["backward"] = _direct_backward_rate(w, per, h1, stream, reps)
+        res[w.name + "_gs1"]["backward"] = _gs1_backward_rate(w, per, h1, stream, reps)
     return res
 
 
-def _direct_backward_rate(w, per, h1, stream, reps):
-    """dq, dk, dv, dh with one filter per channel (the direct kernels): one
-    walk backwards in time over q, k, v, dy and the per-group reduction."""
+def _gs1_backward_rate(w, per, h1, stream, reps):
+    """dq, dk, dv, dh with one filter per channel.  Up to 8 taps (the direct
+    kernels): one walk backwards in time over q, k, v, dy and the per-group
+    reduction.  Longer filters: the chunk-direction kernel for dq, the same
+    walked backwards with two gates for dk and dv, the lag products of dh on
+    the matrix cores (bf16) and the reduction."""
     import torch
     import gated_convolution_sequence_amd as hc
     from workloads import normal_activation
@@ -706,13 +708,16 @@ def _direct_backward_rate(w, per, h1, stream, reps):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
     eb = 2 if w.dtype == "bf16" else 4
-    # q, k, v, dy read once, dq, dk, dv written once: 7 element accesses per
-    # token*channel (plus the l_h - 1 rows each span reads on either side)
-    moved = 7 * eb * w.elems
+    # direct: q, k, v, dy read once, dq, dk, dv written once, 7 element
+    # accesses per token*channel (plus the l_h - 1 rows each span reads on
+    # either side); longer filters: dq pass 4 (k, v, dy; dq), dk/dv pass 6
+    # (dy, q, k, v; dk, dv), lag pass 4 (dy, q, k, v): 14
+    direct = w.l_h <= 8
+    moved = (7 if direct else 14) * eb * w.elems
     del dys
     return {"us": round(us, 2), "G_tok_ch_per_s": round(w.elems / (us * 1e-6) / 1e9, 2),
             "moved_bytes": moved, "GBs_moved": round(moved / (us * 1e-6) / 1e9, 1),
-            "kernels": 2, "workspace_bytes": ws_n}
+            "kernels": 2 if direct else 4, "workspace_bytes": ws_n}
 
 
 def long_filter_rates(w, stream, reps):

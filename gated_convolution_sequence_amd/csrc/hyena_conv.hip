@@ -2373,7 +2373,10 @@ __global__ __launch_bounds__(512) void hyena_bwd_dh_lag_kernel(DhParams p) {
 constexpr int kLmBlock = 128;       // rows per block
 constexpr int kLmXRing = 512;       // x ring, times per channel
 constexpr int kLmZDw = 128;         // dz ring, dwords per copy (256 times)
-constexpr int kLmZPitch = 2 * (kLmZDw + 4);  // dz dwords per channel (two copies, each with 4 repeated)
+// the second dz copy starts 144 dwords (16 banks) after the first, so the
+// two copies' dwords that one 16-lane group of a B read takes use disjoint banks
+constexpr int kLmZCopy = kLmZDw + 16;
+constexpr int kLmZPitch = 2 * kLmZCopy;  // dz dwords per channel (two copies, each with 4 repeated)
 
 __global__ __launch_bounds__(512) void hyena_bwd_dh_lag_mfma_kernel(DhParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t xr[kLagCh * kLmXRing];
@@ -2438,7 +2441,7 @@ __global__ __launch_bounds__(512) void hyena_bwd_dh_lag_mfma_kernel(DhParams p) 
             const int p0 = (m + 4 * sg) & (kLmZDw - 1);        // copy 0: (dz[t], dz[t+1])
             z[p0] = z0 | (z1 << 16);
             if (p0 < 4) z[kLmZDw + p0] = z0 | (z1 << 16);
-            uint16_t *z1h = (uint16_t *)(z + kLmZDw + 4);       // copy 1: (dz[2m'+1], dz[2m'+2])
+            uint16_t *z1h = (uint16_t *)(z + kLmZCopy);         // copy 1: (dz[2m'+1], dz[2m'+2])
             const int ph = (m - 1 + 4 * sg) & (kLmZDw - 1);      // dz[t]: upper half of pair t/2 - 1
             const int pl = (m + 4 * sg) & (kLmZDw - 1);          // dz[t+1]: lower half of pair t/2
             z1h[2 * ph + 1] = (uint16_t)z0;
@@ -2498,7 +2501,7 @@ __global__ __launch_bounds__(512) void hyena_bwd_dh_lag_mfma_kernel(DhParams p) 
                 const int pa = (int)((t0 - 8 * n16 + 8 * q4 + rot) & (kLmXRing - 1));
                 const int64_t e0 = t0 + n16 + 8 * q4;
                 const int par = (int)(e0 & 1);
-                const int pb = par * (kLmZDw + 4) + (int)(((e0 - par) / 2 + 4 * (ch0 >> 3)) & (kLmZDw - 1));
+                const int pb = par * kLmZCopy + (int)(((e0 - par) / 2 + 4 * (ch0 >> 3)) & (kLmZDw - 1));
 #pragma unroll
                 for (int c = 0; c < 8; ++c) {
                     const u32x4_t av = *(const u32x4_t *)(&xr[(ch0 + c) * kLmXRing + pa]);

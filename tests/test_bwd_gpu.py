@@ -335,6 +335,35 @@ def test_backward_off_tile_one_filter_per_channel_medium():
     _check_all(grads, ref, env, l_h, torch.bfloat16, _direct_rows(B, L, D, gs, l_h, torch.bfloat16), "bwd cd medium")
 
 
+
+@pytest.mark.parametrize("name", ["se", "mr"])
+def test_backward_one_filter_per_channel_full_sampled(name):
+    """The layer at its full size (B=1, L=8192, D=4096) with one filter per
+    channel (each channel its group's taps, as the benchmark times it): SE
+    through the direct kernels, MR through the chunk-direction passes and
+    the matrix-core lag products.  Every output element must be finite, and
+    all four gradients of eight whole channels (first, last and six seeded)
+    are compared with the oracle run on those channels alone (with one
+    filter per channel the operator is separable by channel)."""
+    w = WORKLOADS[name]
+    log("bwd %s group_size 1 full: generate" % name)
+    q, k, v, h = make_inputs(w, DEV)
+    h1 = torch.repeat_interleave(h, w.group_size, dim=0).contiguous()
+    dy = normal_activation((w.B, w.L, w.D), w.torch_dtype, DEV, seed=w.seed + 9)
+    dq, dk, dv, dh = _bwd_gpu(q, k, v, h1, dy, 1)
+    for nm, g in (("dq", dq), ("dk", dk), ("dv", dv), ("dh", dh)):
+        assert bool(torch.isfinite(g).all()), "%s %s: non-finite output" % (name, nm)
+    rows = _direct_rows(w.B, w.L, w.D, 1, w.l_h, w.torch_dtype)
+    rng = np.random.default_rng(w.seed)
+    chans = sorted({0, w.D - 1, *rng.choice(w.D, size=6, replace=False).tolist()})
+    for c in chans:
+        log("  channel %d" % c)
+        sl = lambda a: a[:, :, c:c + 1].contiguous()
+        ref, env = _refs(sl(q), sl(k), sl(v), h1[c:c + 1], sl(dy), 1)
+        for nm, g, r, en in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, env):
+            check(to_np(sl(g)), r, en, w.l_h, w.torch_dtype, "%s gs1 %s channel %d" % (name, nm, c))
+        check_dh(dh[c:c + 1], ref[3], env[3], w.torch_dtype, rows, "%s gs1 dh channel %d" % (name, c))
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("B,L,gs,l_h", [(0, 64, 16, 7), (2, 0, 16, 128), (1, 0, 1, 7)])
 def test_backward_without_rows_zeroes_dh(dt, B, L, gs, l_h):

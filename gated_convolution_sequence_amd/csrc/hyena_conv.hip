@@ -304,24 +304,7 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     const __amdgpu_buffer_rsrc_t rkp = make_rsrc(p.P > 0 ? (const char *)p.kp + pre_off : (const char *)p.k, nrec_p);
     const __amdgpu_buffer_rsrc_t rvp = make_rsrc(p.P > 0 ? (const char *)p.vp + pre_off : (const char *)p.v, nrec_p);
 
-    // ---- stage this wave's filter (zero outside [0, l_h)) -----------------
     const bool tile_ok = c_begin + w * kTile < p.D;
-    {
-        const int g = tile_ok ? (c_begin + w * kTile) / p.group_size : 0;
-        for (int i = l; i < kHLen; i += 64) {
-            const int tap = i - kHOff;
-            if constexpr (F32) {
-                float hv = 0.0f;
-                if (tile_ok && tap >= 0 && tap < p.l_h) hv = ((const float *)p.h)[(size_t)g * p.l_h + tap];
-                hs[w][i] = hv;
-            } else {
-                const uint16_t *hg = (const uint16_t *)p.h + (size_t)g * p.l_h;
-                const uint32_t lo = tile_ok && tap >= 0 && tap < p.l_h ? hg[tap] : 0u;
-                const uint32_t hi = tile_ok && tap >= 1 && tap <= p.l_h ? hg[tap - 1] : 0u;
-                hs[w][kHLen - 1 - i] = lo | (hi << 16);
-            }
-        }
-    }
 
     // ---- cooperative row-major access: thread -> (row, 16-byte segment) ----
     // q, k, v and y all use it: 16 bytes per lane, whole 256-byte rows.
@@ -416,6 +399,46 @@ __global__ __launch_bounds__(64 * NW) void hyena_fwd_kernel(Params p) {
     for (int s = 0; s < PF; ++s) {
         load_kv(s < NI ? ld_chunk(s) : S, s < NI, kr[s], vr[s]);
         load_q(s < S ? cp_chunk(s) : S, s < S, qr[s]);
+    }
+
+    // ---- stage this wave's filter (zero outside [0, l_h)), after the first
+    // chunks' loads are issued so that the two latencies overlap.  Every tap
+    // load is issued unconditionally (an index outside the filter reads the
+    // row's first tap, which is then replaced by zero), so all are in flight
+    // together.
+    {
+        const int g = tile_ok ? (c_begin + w * kTile) / p.group_size : 0;
+        const size_t hrow = (size_t)g * p.l_h;
+        constexpr int NTL = kHLen / 64;  // staged entries per lane
+        if constexpr (F32) {
+            float hv[NTL];
+#pragma unroll
+            for (int j = 0; j < NTL; ++j) {
+                const int tap = l + 64 * j - kHOff;
+                hv[j] = ((const float *)p.h)[hrow + (tile_ok && tap >= 0 && tap < p.l_h ? tap : 0)];
+            }
+#pragma unroll
+            for (int j = 0; j < NTL; ++j) {
+                const int tap = l + 64 * j - kHOff;
+                hs[w][l + 64 * j] = tile_ok && tap >= 0 && tap < p.l_h ? hv[j] : 0.0f;
+            }
+        } else {
+            const uint16_t *hg = (const uint16_t *)p.h + hrow;
+            uint32_t lo[NTL], hi[NTL];
+#pragma unroll
+            for (int j = 0; j < NTL; ++j) {
+                const int tap = l + 64 * j - kHOff;
+                lo[j] = hg[tile_ok && tap >= 0 && tap < p.l_h ? tap : 0];
+                hi[j] = hg[tile_ok && tap >= 1 && tap <= p.l_h ? tap - 1 : 0];
+            }
+#pragma unroll
+            for (int j = 0; j < NTL; ++j) {
+                const int tap = l + 64 * j - kHOff;
+                const uint32_t a = tile_ok && tap >= 0 && tap < p.l_h ? lo[j] : 0u;
+                const uint32_t b = tile_ok && tap >= 1 && tap <= p.l_h ? hi[j] : 0u;
+                hs[w][kHLen - 1 - (l + 64 * j)] = a | (b << 16);
+            }
+        }
     }
 
     __syncthreads();  // filters staged
@@ -1050,17 +1073,7 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
     const int row0 = (int)(t_begin - base_row);
     const int rowf = (int)(t_fut - 1 - t_begin);  // (DKV) offset rows of walk row t_begin
 
-    // ---- stage this wave's filter (zero outside [0, l_h)) -----------------
     const bool tile_ok = c_begin + w * kTile < p.D;
-    {
-        const int g = tile_ok ? (c_begin + w * kTile) / p.group_size : 0;
-        for (int i = l; i < kHLen; i += 64) {
-            const int tap = i - kHOff;
-            float hv = 0.0f;
-            if (tile_ok && tap >= 0 && tap < p.l_h) hv = bf_lo(((const uint16_t *)p.h)[(size_t)g * p.l_h + tap]);
-            hsw[i] = hv;
-        }
-    }
 
     const int ld_row = tid / T::TPR;
     const int ld_seg = tid % T::TPR;
@@ -1148,6 +1161,25 @@ __global__ __launch_bounds__(kThreads) void hyena_bwd_dq_dh_kernel(DhParams p) {
 
 #pragma unroll
     for (int s = 0; s < PF; ++s) load(-H + s, s);
+    // ---- stage this wave's filter (zero outside [0, l_h)), after the first
+    // chunks' loads are issued; every tap load unconditional (an index
+    // outside the filter reads the row's first tap, then replaced by zero)
+    {
+        const int g = tile_ok ? (c_begin + w * kTile) / p.group_size : 0;
+        const uint16_t *hg = (const uint16_t *)p.h + (size_t)g * p.l_h;
+        constexpr int NTL = kHLen / 64;
+        uint32_t hv[NTL];
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) {
+            const int tap = l + 64 * j - kHOff;
+            hv[j] = hg[tile_ok && tap >= 0 && tap < p.l_h ? tap : 0];
+        }
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) {
+            const int tap = l + 64 * j - kHOff;
+            hsw[l + 64 * j] = tile_ok && tap >= 0 && tap < p.l_h ? bf_lo(hv[j]) : 0.0f;
+        }
+    }
     __syncthreads();  // filters staged
 
     // Toeplitz operand fragments (B = H^T), as in the forward kernel.

@@ -1967,33 +1967,6 @@ __global__ __launch_bounds__(64) void hyena_fwd_direct_kernel(Params p) {
     // row, row -j sits in xw[j - 1] (the first row's shift moves it to xw[j]).
     // History rows (read by the previous span too) use the default,
     // L2-allocating policy; rows before row 0 come from the prefix, if any.
-    float xw[LH][kDirCh];
-#pragma unroll
-    for (int s = 0; s < LH; ++s)
-#pragma unroll
-        for (int c = 0; c < kDirCh; ++c) xw[s][c] = 0.0f;
-#pragma unroll
-    for (int j = 1; j < LH; ++j) {
-        seg_t kk, vv;
-        bool have = false;
-        if (wk.t0 - j >= 0) {
-            kk = W::template load<0>(rk, wk.off(-j));
-            vv = W::template load<0>(rv, wk.off(-j));
-            have = true;
-        } else if (!REV && p.P > 0 && p.P + wk.t0 - j >= 0) {
-            const size_t pb = (size_t)wk.b * (size_t)p.P * (size_t)wk.row_bytes;
-            const __amdgpu_buffer_rsrc_t rkp = make_rsrc((const char *)p.kp + pb, (uint32_t)(p.P * wk.row_bytes));
-            const __amdgpu_buffer_rsrc_t rvp = make_rsrc((const char *)p.vp + pb, (uint32_t)(p.P * wk.row_bytes));
-            const uint32_t o = wk.ok ? (uint32_t)((p.P + (int)wk.t0 - j) * wk.row_bytes + wk.c0 * W::EB) : kOOB;
-            kk = W::template load<0>(rkp, o);
-            vv = W::template load<0>(rvp, o);
-            have = true;
-        }
-        if (have) {
-#pragma unroll
-            for (int c = 0; c < kDirCh; ++c) xw[j - 1][c] = W::elem(kk, c) * W::elem(vv, c);
-        }
-    }
     seg_t kb[2][kDirBatch], vb[2][kDirBatch], qb[2][kDirBatch], gb[2][DUAL ? kDirBatch : 1];
     auto load_batch = [&](int i0, int sl) {
 #pragma unroll
@@ -2005,7 +1978,35 @@ __global__ __launch_bounds__(64) void hyena_fwd_direct_kernel(Params p) {
             if constexpr (DUAL) gb[sl][u] = W::template load<kLoadPolicy>(rg, o);
         }
     };
+    // The history rows' loads are all issued, then the first batch's, before
+    // any is used (a row in neither the sequence nor the prefix reads as
+    // zero: an offset outside the window); the walk-row selection is uniform
+    // per workgroup, so picking the sequence or the prefix is a scalar select.
+    const size_t pb = (size_t)wk.b * (size_t)p.P * (size_t)wk.row_bytes;
+    const bool has_pre = !REV && p.P > 0;
+    const __amdgpu_buffer_rsrc_t rkp =
+        make_rsrc(has_pre ? (const char *)p.kp + pb : (const char *)p.k, has_pre ? (uint32_t)(p.P * wk.row_bytes) : 0u);
+    const __amdgpu_buffer_rsrc_t rvp =
+        make_rsrc(has_pre ? (const char *)p.vp + pb : (const char *)p.v, has_pre ? (uint32_t)(p.P * wk.row_bytes) : 0u);
+    seg_t hk[LH > 1 ? LH - 1 : 1], hvv[LH > 1 ? LH - 1 : 1];
+#pragma unroll
+    for (int j = 1; j < LH; ++j) {
+        const bool in_seq = wk.t0 - j >= 0;
+        const bool in_pre = !in_seq && has_pre && p.P + wk.t0 - j >= 0;
+        const uint32_t o = in_seq ? wk.off(-j)
+                           : (in_pre && wk.ok) ? (uint32_t)((p.P + (int)wk.t0 - j) * wk.row_bytes + wk.c0 * W::EB)
+                                               : kOOB;
+        hk[j - 1] = W::template load<0>(in_seq ? rk : rkp, o);
+        hvv[j - 1] = W::template load<0>(in_seq ? rv : rvp, o);
+    }
     load_batch(0, 0);
+    float xw[LH][kDirCh];
+#pragma unroll
+    for (int c = 0; c < kDirCh; ++c) xw[LH - 1][c] = 0.0f;
+#pragma unroll
+    for (int j = 1; j < LH; ++j)
+#pragma unroll
+        for (int c = 0; c < kDirCh; ++c) xw[j - 1][c] = W::elem(hk[j - 1], c) * W::elem(hvv[j - 1], c);
     for (int i = 0; i < wk.nrows; i += 2 * kDirBatch) {
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {

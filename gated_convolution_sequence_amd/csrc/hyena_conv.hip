@@ -2486,19 +2486,15 @@ __global__ __launch_bounds__(512) void hyena_bwd_dh_lag_mfma_kernel(DhParams p) 
 
     // dz rings start at zero (times before the span read as zero); the 160
     // rows of x before the span (zero before row 0)
-    for (int i = tid; i < kLagCh * kLmZPitch; i += 512) zr[i] = 0u;
-    {
-        u32x4_t kk[2], vv[2];
-        const int64_t lo = max((int64_t)0, S0 - 160);
-        load2(p.k, S0 - 128, lo, S0, kk, kAlloc);
-        load2(p.v, S0 - 128, lo, S0, vv, kAlloc);
-        put_x(S0 - 128 + 2 * rg, kk, vv);
-        if (rg < 16) {
-            load2(p.k, S0 - 160, lo, S0, kk, kAlloc);
-            load2(p.v, S0 - 160, lo, S0, vv, kAlloc);
-            put_x(S0 - 160 + 2 * rg, kk, vv);
-        }
-    }
+    // every load of the history rows and of the first block is issued
+    // before any is used (the second history pass: 32 rows, threads rg < 16)
+    u32x4_t kk[2], vv[2], kk2[2], vv2[2];
+    const int64_t hlo = max((int64_t)0, S0 - 160);
+    load2(p.k, S0 - 128, hlo, S0, kk, kAlloc);
+    load2(p.v, S0 - 128, hlo, S0, vv, kAlloc);
+    const int64_t h2 = rg < 16 ? S0 - 160 : S0;  // threads rg >= 16: rows at S0 and past, outside the window
+    load2(p.k, h2, hlo, S0, kk2, kAlloc);
+    load2(p.v, h2, hlo, S0, vv2, kAlloc);
     u32x4_t dy_r[2], q_r[2], k_r[2], v_r[2];
     auto load_blk = [&](int blk) {
         const int64_t r0 = S0 + (int64_t)blk * kLmBlock;
@@ -2509,6 +2505,9 @@ __global__ __launch_bounds__(512) void hyena_bwd_dh_lag_mfma_kernel(DhParams p) 
         load2(p.v, r0, S0, S1, v_r, kAlloc);
     };
     load_blk(0);
+    for (int i = tid; i < kLagCh * kLmZPitch; i += 512) zr[i] = 0u;
+    put_x(S0 - 128 + 2 * rg, kk, vv);
+    if (rg < 16) put_x(S0 - 160 + 2 * rg, kk2, vv2);
     __syncthreads();  // the dz rings are zero before any block writes them
 
     // the wave's channels lie all inside D or all past it (D is a whole

@@ -1619,29 +1619,37 @@ __global__ __launch_bounds__(kCdThreads) void hyena_fwd_cd_kernel(Params p) {
     // Every tap load is issued unconditionally (an index outside the filter
     // reads element 0 and is then replaced by zero), so all of them are in
     // flight together.
+    // (one filter per channel, the filter row is the channel: no division)
     uint32_t tap_lo[NPT], tap_hi[NPT];
+    auto load_taps = [&](auto gs1_tag) {
+        constexpr bool GS1 = decltype(gs1_tag)::value;
 #pragma unroll
-    for (int j = 0; j < NPT; ++j) {
-        const int i = tid + j * kCdThreads;
-        const int dl = i / PTN, m = i % PTN - kCdTapOff;
-        const int ch = c_begin + dl;
-        const bool chok = i < SLAB * PTN && ch < p.D;
-        const size_t hrow = chok ? (size_t)(ch / p.group_size) * p.l_h : 0;
-        const bool lo_ok = chok && m >= 0 && m < p.l_h;
-        const size_t ilo = lo_ok ? hrow + m : 0;
-        if constexpr (F32) {
-            const uint32_t vlo = ((const uint32_t *)p.h)[ilo];
-            tap_lo[j] = lo_ok ? vlo : 0u;
-            tap_hi[j] = 0u;
-        } else {
-            const bool hi_ok = chok && m >= 1 && m <= p.l_h;
-            const size_t ihi = hi_ok ? hrow + m - 1 : 0;
-            const uint32_t vlo = ((const uint16_t *)p.h)[ilo];
-            const uint32_t vhi = ((const uint16_t *)p.h)[ihi];
-            tap_lo[j] = lo_ok ? vlo : 0u;
-            tap_hi[j] = hi_ok ? vhi : 0u;
+        for (int j = 0; j < NPT; ++j) {
+            const int i = tid + j * kCdThreads;
+            const int dl = i / PTN, m = i % PTN - kCdTapOff;
+            const int ch = c_begin + dl;
+            const bool chok = i < SLAB * PTN && ch < p.D;
+            const size_t hrow = chok ? (size_t)(GS1 ? ch : ch / p.group_size) * p.l_h : 0;
+            const bool lo_ok = chok && m >= 0 && m < p.l_h;
+            const size_t ilo = lo_ok ? hrow + m : 0;
+            if constexpr (F32) {
+                const uint32_t vlo = ((const uint32_t *)p.h)[ilo];
+                tap_lo[j] = lo_ok ? vlo : 0u;
+                tap_hi[j] = 0u;
+            } else {
+                const bool hi_ok = chok && m >= 1 && m <= p.l_h;
+                const size_t ihi = hi_ok ? hrow + m - 1 : 0;
+                const uint32_t vlo = ((const uint16_t *)p.h)[ilo];
+                const uint32_t vhi = ((const uint16_t *)p.h)[ihi];
+                tap_lo[j] = lo_ok ? vlo : 0u;
+                tap_hi[j] = hi_ok ? vhi : 0u;
+            }
         }
-    }
+    };
+    if (p.group_size == 1)
+        load_taps(std::true_type{});
+    else
+        load_taps(std::false_type{});
     // stored reversed (entry e of a channel at PTN - 1 - e), so the entries
     // one MFMA operand takes, e, e - 2, e - 4, e - 6, lie at rising addresses
 #pragma unroll

@@ -94,6 +94,29 @@ def test_paired_filters_match_the_grouped_path(dt):
     assert torch.equal(y8, y16)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("l_h", [4, 9, 65, 128])
+def test_one_filter_per_channel_matches_repeated_pairs(dt, l_h):
+    """group_size 1 with each group_size 2 filter given to both of its channels
+    is the same problem: each channel's sums are taken on their own, in the same
+    order, whatever row the taps come from, so y, dq, dk and dv agree bit for
+    bit on any inputs (dh sums a group's channels and is not compared here)."""
+    dtype = DTYPES[dt]
+    B, L, D = 2, 1000, 264
+    q, k, v, h2 = gaussian_inputs(B, L, D, 2, l_h, dtype, seed=300 + l_h)
+    dy = gaussian_inputs(B, L, D, 2, 1, dtype, seed=400 + l_h)[0]
+    h1 = torch.repeat_interleave(h2, 2, dim=0).contiguous()
+    q, k, v, dy, h1, h2 = (t.to(DEV) for t in (q, k, v, dy, h1, h2))
+    log("repeated pairs %s l_h=%d: forward" % (dt, l_h))
+    assert torch.equal(hc.conv_fwd(q, k, v, h1, 1), hc.conv_fwd(q, k, v, h2, 2))
+    log("repeated pairs %s l_h=%d: backward" % (dt, l_h))
+    g1 = hc.conv_bwd(q, k, v, h1, dy, 1)
+    g2 = hc.conv_bwd(q, k, v, h2, dy, 2)
+    for name, a, b in zip(("dq", "dk", "dv"), g1[:3], g2[:3]):
+        assert torch.equal(a, b), name
+    assert bool(torch.isfinite(g1[3]).all())
+
+
 @pytest.mark.parametrize("l_h", [1, 16, 17, 33, 64, 65, 128])
 def test_impulses_on_block_and_sub_chunk_seams_reproduce_the_filter(l_h):
     L, D = 1100, 64

@@ -328,3 +328,26 @@ def test_long_stripe_sampled():
         log("%s: sampled checks" % w.name)
         _sampled_checks(w, q, k, v, h, y, n_groups=6, seed=5)
         del q, k, v, h, y
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("l_h", [7, 33, 128])
+def test_wider_group_matches_repeated_filters(dt, l_h):
+    """group_size 32 is group_size 16 with each filter given to both of its
+    16-channel tiles: a tile's Toeplitz products read only its own filter row,
+    so y, dq, dk and dv agree bit for bit on any inputs (dh sums a group's
+    channels and is not compared here)."""
+    dtype = DTYPES[dt]
+    B, L, D = 2, 1000, 256
+    q, k, v, h32 = gaussian_inputs(B, L, D, 32, l_h, dtype, seed=500 + l_h)
+    dy = gaussian_inputs(B, L, D, 32, 1, dtype, seed=600 + l_h)[0]
+    h16 = torch.repeat_interleave(h32, 2, dim=0).contiguous()
+    q, k, v, dy, h16, h32 = (t.to(DEV) for t in (q, k, v, dy, h16, h32))
+    log("wider group %s l_h=%d: forward" % (dt, l_h))
+    assert torch.equal(hc.conv_fwd(q, k, v, h32, 32), hc.conv_fwd(q, k, v, h16, 16))
+    log("wider group %s l_h=%d: backward" % (dt, l_h))
+    g32 = hc.conv_bwd(q, k, v, h32, dy, 32)
+    g16 = hc.conv_bwd(q, k, v, h16, dy, 16)
+    for name, a, b in zip(("dq", "dk", "dv"), g32[:3], g16[:3]):
+        assert torch.equal(a, b), name
+    assert bool(torch.isfinite(g32[3]).all())
